@@ -1,0 +1,386 @@
+// Host side of the C ABI: argument validation (before any launch), workspace
+// layout, launch plans and the round's entry points.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "eagle_internal.h"
+
+namespace eg {
+
+static thread_local char g_err[512] = "";
+
+static int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+size_t elem_size(const eagle_dims& d) { return d.dtype == EAGLE_BF16 ? 2 : 4; }
+
+// Workgroups a weight-streaming launch aims for: two per compute unit (eight
+// waves) keeps enough 16-byte loads in flight to cover HBM latency.
+static constexpr int TARGET_WG = 512;
+
+GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
+  GemmPlan p{};
+  p.M = M;
+  p.nw = 1;
+  switch (op) {
+    case OP_FC: p.N = d.d; p.K = 2 * d.d; break;
+    case OP_QKV: p.N = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim; p.K = d.d; break;
+    case OP_O: p.N = d.d; p.K = d.n_heads * d.head_dim; break;
+    case OP_GATEUP: p.N = d.ffn; p.K = d.d; p.nw = 2; break;
+    default: p.N = d.d; p.K = d.ffn; break;
+  }
+  p.mt = std::min(4, cdiv(std::min(M, 64), 16));
+  p.zg = cdiv(M, 64);
+  p.nblk = cdiv(p.N, 64);
+  const int ks = d.dtype == EAGLE_BF16 ? 32 : 16;
+  const int base = p.nblk * p.zg;
+  int S = std::max(1, cdiv(TARGET_WG, base));
+  S = std::min(S, std::max(1, p.K / (4 * ks)));
+  int Kc = cdiv(cdiv(p.K, S), ks) * ks;
+  S = cdiv(p.K, Kc);
+  p.S = S;
+  p.Kc = Kc;
+  p.part_floats = S > 1 ? (size_t)p.nblk * p.zg * S * 4 * p.nw * p.mt * 256 : 0;
+  return p;
+}
+
+LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
+  LmPlan p{};
+  p.M = M;
+  p.mt = std::min(4, cdiv(std::min(M, 64), 16));
+  p.zg = cdiv(M, 64);
+  p.nblk = cdiv(d.vocab, 64);
+  p.rec = 2 + 2 * topk;
+  p.part_floats = (size_t)M * p.nblk * p.rec;
+  return p;
+}
+
+AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& c, int nseq) {
+  AttnPlan p{};
+  p.RS = RS;
+  p.g = d.n_heads / d.n_kv_heads;
+  p.nq = RS * p.g;
+  p.QT = 32;
+  p.nqt = cdiv(p.nq, p.QT);
+  const int nwg = nseq * d.n_kv_heads * p.nqt;
+  const int maxP = c.max_prefix;
+  const int nps_t = std::max(1, cdiv(1024, nwg));
+  p.KCH = std::max(32, cdiv(cdiv(maxP, nps_t), 32) * 32);
+  p.nps = cdiv(maxP, p.KCH);
+  p.nsplit = p.nps + (mode == MODE_LEVEL ? 1 : 0);
+  p.part_floats = (size_t)nwg * p.nsplit * p.QT * (d.head_dim + 2);
+  return p;
+}
+
+WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
+  WsLayout L{};
+  const size_t es = elem_size(d);
+  const int B = c.batch, k = c.topk, D = c.depth, m = c.m;
+  const int rows_lv = B * k, rows_ex = B * m;
+  L.rows_max = std::max(std::max(rows_lv, rows_ex), B);
+  L.pool_n = k + (D - 1) * k * k;
+  const size_t R = L.rows_max, HD = (size_t)d.n_heads * d.head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.err = take(16);
+  L.cnt = take((size_t)NCNT * 4);
+  L.pool = take((size_t)B * L.pool_n * sizeof(eagle_pool_entry));
+  L.frontier = take((size_t)(D + 1) * B * k * sizeof(eagle_frontier_node));
+  L.feat = take((size_t)D * B * k * d.d * es);
+  const size_t kvt = (size_t)B * D * k * d.n_kv_heads * d.head_dim * es;
+  L.tk = take(kvt);
+  L.tv = take(kvt);
+  L.ext_h = take((size_t)B * m * d.d * es);
+  L.x0f = take(R * d.d * 4);
+  L.x0b = take(R * d.d * es);
+  L.q = take(R * HD * 4);
+  L.attn = take(R * HD * es);
+  L.yf = take(R * d.d * 4);
+  L.yg = take(R * d.d * es);
+  L.rstd = take(R * 4);
+  L.ssq = take((size_t)cdiv(d.d, 64) * R * 4);
+  L.act = take(R * d.ffn * es);
+  size_t gp = 0;
+  for (int op = OP_FC; op <= OP_DOWN; ++op)
+    for (int M : {rows_lv, rows_ex}) gp = std::max(gp, plan_gemm(op, M, d).part_floats);
+  L.gpart = take(gp * 4);
+  const size_t lp = std::max(plan_lm(B, d, k).part_floats, plan_lm(rows_lv, d, k).part_floats);
+  L.lmpart = take(lp * 4);
+  L.lmres = take((size_t)std::max(B, rows_lv) * 2 * k * 4);
+  const size_t ap = std::max(plan_attn(MODE_LEVEL, k, d, c, B).part_floats,
+                             plan_attn(MODE_EXTEND, m, d, c, B).part_floats);
+  L.apart = take(ap * 4);
+  L.total = off;
+  return L;
+}
+
+// ------------------------------------------------------------------ validation
+
+static int check_dims(const eagle_dims* d) {
+  if (!d) return fail(EAGLE_ERR_ARG, "dims is NULL");
+  if (d->dtype != EAGLE_F32 && d->dtype != EAGLE_BF16) return fail(EAGLE_ERR_ARG, "dtype %d", d->dtype);
+  if (d->d <= 0 || d->n_heads <= 0 || d->n_kv_heads <= 0 || d->head_dim <= 0 || d->ffn <= 0 || d->vocab <= 0)
+    return fail(EAGLE_ERR_SHAPE, "non-positive dimension");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(EAGLE_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
+  if (d->d != d->n_heads * d->head_dim)
+    return fail(EAGLE_ERR_SHAPE, "d %d != n_heads %d * head_dim %d", d->d, d->n_heads, d->head_dim);
+  if (d->n_heads % d->n_kv_heads) return fail(EAGLE_ERR_SHAPE, "n_heads %% n_kv_heads != 0");
+  if (d->ffn % 8) return fail(EAGLE_ERR_UNSUPPORTED, "ffn %d not a multiple of 8", d->ffn);
+  if (d->vocab > 64 * 4096) return fail(EAGLE_ERR_UNSUPPORTED, "vocab %d > 262144", d->vocab);
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f)) return fail(EAGLE_ERR_ARG, "rms_eps / rope_theta");
+  return EAGLE_OK;
+}
+
+static int check_cfg(const eagle_dims* d, const eagle_tree_cfg* c) {
+  if (!c) return fail(EAGLE_ERR_ARG, "cfg is NULL");
+  if (c->batch < 1) return fail(EAGLE_ERR_SHAPE, "batch %d", c->batch);
+  if (c->depth < 2 || c->depth > EAGLE_MAX_DEPTH) return fail(EAGLE_ERR_UNSUPPORTED, "depth %d (2..16)", c->depth);
+  if (c->topk < 1 || c->topk > EAGLE_MAX_TOPK) return fail(EAGLE_ERR_UNSUPPORTED, "topk %d (1..16)", c->topk);
+  if (d && c->topk > d->vocab) return fail(EAGLE_ERR_SHAPE, "topk %d > vocab %d", c->topk, d->vocab);
+  if (c->m < 2 || c->m > EAGLE_MAX_TREE) return fail(EAGLE_ERR_UNSUPPORTED, "m %d (2..64)", c->m);
+  const long pool = (long)c->topk + (long)(c->depth - 1) * c->topk * c->topk;
+  if (c->m - 1 > pool) return fail(EAGLE_ERR_SHAPE, "m-1 = %d > pool %ld", c->m - 1, pool);
+  if (c->max_prefix < c->m + 1) return fail(EAGLE_ERR_SHAPE, "max_prefix %d < m+1", c->max_prefix);
+  if (d) {
+    const AttnPlan pa = plan_attn(MODE_EXTEND, c->m, *d, *c, c->batch);
+    const long wg = (long)c->batch * d->n_kv_heads * pa.nqt;
+    if (wg >= GRID_CNT) return fail(EAGLE_ERR_UNSUPPORTED, "attention grid %ld too large", wg);
+    const long blocks = (long)cdiv(d->ffn, 64) * cdiv(c->batch * c->m, 64);
+    if (blocks >= GRID_CNT || (long)c->batch * c->m > 4096)
+      return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", c->batch * c->m);
+  }
+  return EAGLE_OK;
+}
+
+static int check_ws(const eagle_dims* d, const eagle_tree_cfg* c, const void* ws, size_t ws_bytes) {
+  if (!ws) return fail(EAGLE_ERR_ARG, "workspace is NULL");
+  if ((uintptr_t)ws % 256) return fail(EAGLE_ERR_ARG, "workspace not 256-byte aligned");
+  const size_t need = plan_ws(*d, *c).total;
+  if (ws_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return EAGLE_OK;
+}
+
+static int check_weights(const eagle_weights* w, bool tail_only) {
+  if (!w) return fail(EAGLE_ERR_ARG, "weights is NULL");
+  if (!w->lm_head) return fail(EAGLE_ERR_ARG, "weight lm_head is NULL");
+  if (tail_only) return EAGLE_OK;
+  const void* need[] = {w->fc_w, w->fc_b, w->wq, w->wk, w->wv, w->wo, w->post_norm,
+                        w->w_gate, w->w_up, w->w_down, w->embed};
+  const char* names[] = {"fc_w", "fc_b", "wq", "wk", "wv", "wo", "post_norm",
+                         "w_gate", "w_up", "w_down", "embed"};
+  for (int i = 0; i < 11; ++i)
+    if (!need[i]) return fail(EAGLE_ERR_ARG, "weight %s is NULL", names[i]);
+  return EAGLE_OK;
+}
+
+static int check_state(const eagle_seq_state* s) {
+  if (!s) return fail(EAGLE_ERR_ARG, "state is NULL");
+  if (!s->k_cache || !s->v_cache || !s->prefix_len || !s->root_feat || !s->root_token)
+    return fail(EAGLE_ERR_ARG, "state has a NULL pointer");
+  return EAGLE_OK;
+}
+
+static RoundArgs make_args(const eagle_dims& d, const eagle_tree_cfg& c, const eagle_weights* w,
+                           const eagle_seq_state* st, void* ws) {
+  RoundArgs a{};
+  a.dtype = d.dtype;
+  a.B = c.batch; a.d = d.d; a.H = d.n_heads; a.Hkv = d.n_kv_heads; a.hd = d.head_dim;
+  a.F = d.ffn; a.V = d.vocab; a.D = c.depth; a.k = c.topk; a.m = c.m; a.max_prefix = c.max_prefix;
+  a.eps = d.rms_eps; a.theta = d.rope_theta;
+  if (w) {
+    a.fc_w = w->fc_w; a.fc_b = w->fc_b; a.wq = w->wq; a.wk = w->wk; a.wv = w->wv; a.wo = w->wo;
+    a.post_norm = w->post_norm; a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
+    a.embed = w->embed; a.lm_head = w->lm_head;
+  }
+  if (st) {
+    a.k_cache = st->k_cache; a.v_cache = st->v_cache; a.prefix_len = st->prefix_len;
+    a.root_feat = st->root_feat; a.root_token = st->root_token;
+  }
+  const WsLayout L = plan_ws(d, c);
+  char* base = (char*)ws;
+  a.err = (int*)(base + L.err);
+  a.cnt = (int*)(base + L.cnt);
+  a.pool = (eagle_pool_entry*)(base + L.pool);
+  a.frontier = (eagle_frontier_node*)(base + L.frontier);
+  a.feat = base + L.feat; a.tk = base + L.tk; a.tv = base + L.tv; a.ext_h = base + L.ext_h;
+  a.x0f = (float*)(base + L.x0f); a.x0b = base + L.x0b; a.q = (float*)(base + L.q);
+  a.attn = base + L.attn; a.yf = (float*)(base + L.yf); a.yg = base + L.yg;
+  a.rstd = (float*)(base + L.rstd); a.ssq = (float*)(base + L.ssq); a.act = base + L.act;
+  a.gpart = (float*)(base + L.gpart); a.lmpart = (float*)(base + L.lmpart);
+  a.lmres = (float*)(base + L.lmres); a.apart = (float*)(base + L.apart);
+  a.pool_n = L.pool_n;
+  return a;
+}
+
+static int hip_ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(EAGLE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return EAGLE_OK;
+}
+
+// draft layer over `rows` rows (frontier or extend): FC, QKV+RoPE+KV, attention,
+// O+residual+norm stats, gate/up+SwiGLU, down+residual
+static int run_layer(RoundArgs a, const eagle_dims& d, const eagle_tree_cfg& c, hipStream_t s) {
+  static const char* names[] = {"fc", "qkv", "o", "gateup", "down"};
+  for (int op = OP_FC; op <= OP_DOWN; ++op) {
+    if (op == OP_O) {
+      const AttnPlan pa = plan_attn(a.mode, a.RS, d, c, a.B);
+      int r = hip_ok(launch_attn(a, pa, s), "attention launch");
+      if (r) return r;
+    }
+    const GemmPlan p = plan_gemm(op, a.rows, d);
+    int r = hip_ok(launch_gemm(op, a, p, s), names[op]);
+    if (r) return r;
+  }
+  return EAGLE_OK;
+}
+
+}  // namespace eg
+
+using namespace eg;
+
+extern "C" {
+
+const char* eagle_status_str(int status) {
+  switch (status) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_ERR_ARG: return "invalid argument";
+    case EAGLE_ERR_SHAPE: return "inconsistent shape";
+    case EAGLE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case EAGLE_ERR_WORKSPACE: return "workspace too small";
+    case EAGLE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* eagle_last_error(void) { return g_err; }
+
+size_t eagle_workspace_bytes(const eagle_dims* dims, const eagle_tree_cfg* cfg) {
+  if (check_dims(dims) || check_cfg(dims, cfg)) return 0;
+  return plan_ws(*dims, *cfg).total;
+}
+
+int eagle_workspace_init(const eagle_dims* dims, const eagle_tree_cfg* cfg, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
+    return r;
+  return hip_ok(launch_zero(ws, plan_ws(*dims, *cfg).total, (hipStream_t)stream), "zero fill");
+}
+
+int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
+                      const eagle_seq_state* state, int32_t level, int32_t flags, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
+    return r;
+  if (flags != EAGLE_LEVEL_FULL && flags != EAGLE_LEVEL_TAIL_ONLY)
+    return fail(EAGLE_ERR_ARG, "flags %d", flags);
+  if (level < 1 || level > cfg->depth) return fail(EAGLE_ERR_ARG, "level %d (1..%d)", level, cfg->depth);
+  const bool tail_only = level == 1 || flags == EAGLE_LEVEL_TAIL_ONLY;
+  if ((r = check_weights(w, tail_only)) || (r = check_state(state))) return r;
+  const hipStream_t s = (hipStream_t)stream;
+  RoundArgs a = make_args(*dims, *cfg, w, state, ws);
+  if (level == 1) {
+    a.rows = cfg->batch;
+    return hip_ok(launch_lmhead(a, plan_lm(cfg->batch, *dims, cfg->topk), 1, s), "lm head");
+  }
+  a.mode = MODE_LEVEL;
+  a.depth = level - 1;
+  a.rows = cfg->batch * cfg->topk;
+  a.RS = cfg->topk;
+  if (!tail_only && (r = run_layer(a, *dims, *cfg, s))) return r;
+  return hip_ok(launch_lmhead(a, plan_lm(a.rows, *dims, cfg->topk), level, s), "lm head");
+}
+
+int eagle_rerank_build_tree(const eagle_dims* dims, const eagle_tree_cfg* cfg,
+                            const eagle_seq_state* state, void* ws, size_t ws_bytes, int32_t* tokens,
+                            int32_t* parents, int32_t* depth, int32_t* positions, uint8_t* mask,
+                            float* node_logscore, void* stream) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
+    return r;
+  if ((r = check_state(state))) return r;
+  if (!tokens || !parents) return fail(EAGLE_ERR_ARG, "tokens/parents is NULL");
+  RoundArgs a = make_args(*dims, *cfg, nullptr, state, ws);
+  return hip_ok(launch_rerank(a, tokens, parents, depth, positions, mask, node_logscore,
+                              (hipStream_t)stream),
+                "rerank");
+}
+
+int eagle_verify_greedy(const eagle_tree_cfg* cfg, int32_t vocab, const float* target_logits,
+                        const int32_t* tokens, const int32_t* parents, int32_t* accept_len,
+                        int32_t* accept_path, int32_t* bonus, void* stream) {
+  int r;
+  if ((r = check_cfg(nullptr, cfg))) return r;
+  if (vocab < 1) return fail(EAGLE_ERR_SHAPE, "vocab %d", vocab);
+  if (!target_logits || !tokens || !parents || !accept_len || !accept_path || !bonus)
+    return fail(EAGLE_ERR_ARG, "verify: NULL pointer");
+  return hip_ok(launch_verify(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, tokens, parents,
+                              accept_len, accept_path, bonus, (hipStream_t)stream),
+                "verify");
+}
+
+int eagle_draft_extend(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
+                       const eagle_seq_state* state, const void* true_feat, const int32_t* tokens,
+                       const int32_t* accept_len, const int32_t* accept_path, const int32_t* bonus,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
+    return r;
+  if ((r = check_weights(w, false)) || (r = check_state(state))) return r;
+  if (!true_feat || !tokens || !accept_len || !accept_path || !bonus)
+    return fail(EAGLE_ERR_ARG, "extend: NULL pointer");
+  RoundArgs a = make_args(*dims, *cfg, w, state, ws);
+  a.mode = MODE_EXTEND;
+  a.depth = 0;
+  a.rows = cfg->batch * cfg->m;
+  a.RS = cfg->m;
+  a.true_feat = true_feat;
+  a.tokens = tokens;
+  a.accept_len = accept_len;
+  a.accept_path = accept_path;
+  a.bonus = bonus;
+  return run_layer(a, *dims, *cfg, (hipStream_t)stream);
+}
+
+int eagle_ws_view(const eagle_dims* dims, const eagle_tree_cfg* cfg, const void* ws, int32_t what,
+                  void** ptr, size_t* bytes) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg))) return r;
+  if (!ws || !ptr || !bytes) return fail(EAGLE_ERR_ARG, "ws_view: NULL pointer");
+  const WsLayout L = plan_ws(*dims, *cfg);
+  const size_t es = elem_size(*dims);
+  const size_t B = cfg->batch, k = cfg->topk, D = cfg->depth, m = cfg->m;
+  size_t off, n;
+  switch (what) {
+    case EAGLE_WS_ERROR: off = L.err; n = 16; break;
+    case EAGLE_WS_POOL: off = L.pool; n = B * L.pool_n * sizeof(eagle_pool_entry); break;
+    case EAGLE_WS_FRONTIER: off = L.frontier; n = (D + 1) * B * k * sizeof(eagle_frontier_node); break;
+    case EAGLE_WS_FEAT: off = L.feat; n = D * B * k * dims->d * es; break;
+    case EAGLE_WS_TREE_K: off = L.tk; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
+    case EAGLE_WS_TREE_V: off = L.tv; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
+    case EAGLE_WS_EXT_H: off = L.ext_h; n = B * m * dims->d * es; break;
+    default: return fail(EAGLE_ERR_ARG, "ws_view: region %d", what);
+  }
+  *ptr = (char*)ws + off;
+  *bytes = n;
+  return EAGLE_OK;
+}
+
+}  // extern "C"

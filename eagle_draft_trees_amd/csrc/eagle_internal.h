@@ -1,0 +1,207 @@
+// Internal declarations of the gfx950 EAGLE-2 draft-round library: element
+// types, MFMA wrappers, wave reductions, the workspace layout and launch plans.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "eagle_mi355x.h"
+
+namespace eg {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+constexpr int BLOCK = 256;       // four waves
+constexpr int NCNT = 1 << 16;    // last-block counters in the workspace
+constexpr int GRID_CNT = NCNT - 1;
+
+enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
+enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1 };
+enum ErrBits { ERR_TOKEN = 1, ERR_PREFIX = 2 };
+
+// ------------------------------------------------------------------ elements
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+// round to nearest, ties to even (finite inputs)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename T> struct El;
+template <> struct El<float> {
+  static constexpr int KSTEP = 16;  // k covered by one 16-byte-per-lane fragment across a wave
+  static constexpr int PER16 = 4;   // elements per 16 bytes
+  __device__ static __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct El<bf16_t> {
+  static constexpr int KSTEP = 32;
+  static constexpr int PER16 = 8;
+  __device__ static __forceinline__ float ld(const bf16_t* p, size_t i) { return bf2f(p[i]); }
+  __device__ static __forceinline__ void st(bf16_t* p, size_t i, float v) { p[i] = (bf16_t)f2bf(v); }
+};
+
+// 16x16 output tile, 16 bytes of A (rows) and 16 bytes of B (columns) per lane.
+// Lane l supplies A[l%16][kslot(l/16)] and B[kslot(l/16)][l%16]; it receives
+// D[4*(l/16)+r][l%16], r = 0..3.  Both operands use the same k permutation,
+// so any assignment of k to (lane group, element) contracts correctly.
+__device__ __forceinline__ f32x4_t mma16(uint4 a, uint4 b, f32x4_t c, bf16_t) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(uint4 a, uint4 b, f32x4_t c, float) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  return c;
+}
+
+// ------------------------------------------------------------------ wave reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+// butterfly sum; every lane takes lane 0's total so all lanes agree bit for bit
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return __shfl(v, 0);
+}
+// (value desc, id asc) winner across the wave; every lane gets the result
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o);
+    int oi = __shfl_xor(id, o);
+    if (ov > v || (ov == v && oi < id)) { v = ov; id = oi; }
+  }
+}
+
+// ------------------------------------------------------------------ workspace
+
+struct WsLayout {
+  size_t err, cnt, pool, frontier, feat, tk, tv, ext_h;
+  size_t x0f, x0b, q, attn, yf, yg, rstd, ssq, act;
+  size_t gpart, lmpart, lmres, apart;
+  size_t total;
+  int rows_max, pool_n;
+};
+
+struct GemmPlan {
+  int M, N, K, nw, mt, zg, nblk, S, Kc;
+  size_t part_floats;  // split-K partial floats (0 when S == 1)
+};
+
+struct LmPlan {
+  int M, mt, zg, nblk, rec;  // rec = floats per (row, block) partial
+  size_t part_floats;
+};
+
+struct AttnPlan {
+  int RS, g, nq, QT, nqt, KCH, nps, nsplit;  // nsplit = prefix splits (+1 in-tree split)
+  size_t part_floats;
+};
+
+GemmPlan plan_gemm(int op, int M, const eagle_dims& d);
+LmPlan plan_lm(int M, const eagle_dims& d, int topk);
+AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& c, int nseq);
+WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c);
+size_t elem_size(const eagle_dims& d);
+
+// ------------------------------------------------------------------ kernel argument blocks
+
+struct RoundArgs {
+  // shapes
+  int dtype;  // eagle_dtype
+  int B, d, H, Hkv, hd, F, V, D, k, m, max_prefix;
+  float eps, theta;
+  int mode, depth;  // depth = depth of the rows being forwarded (level - 1)
+  int rows, RS;     // total rows, rows per sequence
+  // weights
+  const void *fc_w, *fc_b, *wq, *wk, *wv, *wo, *post_norm, *w_gate, *w_up, *w_down, *embed, *lm_head;
+  // state
+  void *k_cache, *v_cache;
+  int* prefix_len;
+  void* root_feat;
+  int* root_token;
+  // extend inputs
+  const void* true_feat;
+  const int *tokens, *accept_len, *accept_path, *bonus;
+  // workspace
+  int* err;
+  int* cnt;
+  eagle_pool_entry* pool;
+  eagle_frontier_node* frontier;  // [D+1][B][k]
+  void *feat, *tk, *tv, *ext_h;
+  float* x0f;
+  void* x0b;
+  float* q;
+  void* attn;
+  float* yf;
+  void* yg;
+  float *rstd, *ssq;
+  void* act;
+  float *gpart, *lmpart, *lmres, *apart;
+  int pool_n;
+};
+
+// ------------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ int clamp_tok(int t, int V, int* err) {
+  if (t < 0 || t >= V) {
+    atomicOr(err, ERR_TOKEN);
+    t = t < 0 ? 0 : V - 1;
+  }
+  return t;
+}
+
+__device__ __forceinline__ int clamp_prefix(int P, const RoundArgs& a) {
+  const int hi = a.max_prefix - a.m;
+  if (P < 1 || P > hi) {
+    atomicOr(a.err, ERR_PREFIX);
+    P = P < 1 ? 1 : hi;
+  }
+  return P;
+}
+
+__device__ __forceinline__ int clamp_slot(int s, int k) { return s < 0 ? 0 : (s >= k ? k - 1 : s); }
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
+
+// last-block election: every thread fences its own stores, one thread bumps the
+// counter; returns true in the block that arrived last (counter reset to 0)
+__device__ __forceinline__ bool arrive_last(int* cnt, int total) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(cnt, 1);
+    s_last = (prev == total - 1);
+    if (s_last) atomicExch(cnt, 0);
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// launchers (return a hipError_t)
+hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
+hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
+hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
+                         int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);
+hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
+                         const int32_t* parents, int32_t* alen, int32_t* apath, int32_t* bonus,
+                         hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace eg

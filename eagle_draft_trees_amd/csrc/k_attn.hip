@@ -1,0 +1,202 @@
+// Tree-masked attention of the draft decoder layer.
+//
+// Levels: a frontier row at depth L sits at position P-1+L and sees every
+// prefix row plus the in-tree K/V of its ancestors and itself, never a sibling
+// or cousin ([P1] "EAGLE 推测解码为什么比 Medusa 快？（含 EAGLE-2 动态草稿树）"
+// §12 item 5: the mask looks only at ancestors; [P4] "投机解码：从eagle1到dflash"
+// EAGLE-2 diagram: tree causal mask).  Extend: row i sees the prefix and
+// extend rows 0..i, which the QKV epilogue has already appended to the cache
+// ([P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里").
+//
+// All rows of a sequence share its prefix, so one workgroup takes one
+// (sequence, KV head, query tile) and one slice of the prefix: the K/V tiles of
+// that slice are staged in LDS once and used by every query row and every
+// query head of the GQA group.  Each slice writes (max, sum, unnormalised
+// output) partials; a separate slice handles the per-row in-tree keys; the
+// last workgroup to finish a (sequence, KV head, query tile) merges the slices
+// in slice order (deterministic).  Scores 1/sqrt(hd) * q.k in fp32.
+#include "eagle_internal.h"
+
+namespace eg {
+
+constexpr int AT_QT = 32;  // queries per workgroup
+constexpr int AT_KT = 32;  // keys per LDS tile
+
+template <typename T>
+__global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
+  __shared__ float sQ[AT_QT][129];
+  __shared__ float sK[AT_KT][129];
+  __shared__ float sV[AT_KT][128];
+  __shared__ float sS[AT_QT][AT_KT + 1];
+  __shared__ float sM[AT_QT], sL[AT_QT], sScale[AT_QT];
+  __shared__ int sLim[AT_QT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wg = blockIdx.x, split = blockIdx.y;
+  const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int hd = a.hd, g = p.g;
+  const int q0 = qt * AT_QT;
+  const int nq = min(AT_QT, p.nq - q0);
+  const int P = clamp_prefix(a.prefix_len[b], a);
+  const float scale = rsqrtf((float)hd);
+  const int HD = a.H * hd;
+
+  // queries: qi -> (row within sequence, head)
+  for (int idx = tid; idx < nq * hd; idx += BLOCK) {
+    const int qi = idx / hd, dd = idx % hd, gq = q0 + qi;
+    const int row = b * p.RS + gq / g, head = kvh * g + gq % g;
+    sQ[qi][dd] = a.q[(size_t)row * HD + head * hd + dd] * scale;
+  }
+  if (tid < AT_QT) {
+    const int gq = q0 + tid;
+    sLim[tid] = (a.mode == MODE_LEVEL) ? P : P + gq / g + 1;
+    sM[tid] = -INFINITY;
+    sL[tid] = 0.f;
+  }
+  __syncthreads();
+
+  const size_t prec = (size_t)hd + 2;
+  float* part = a.apart + ((size_t)wg * p.nsplit + split) * AT_QT * prec;
+  const int qg_pv = BLOCK / hd;    // query groups in the P.V step
+  const int dpv = tid % hd, qpv = tid / hd;
+  float acc[AT_QT / 2];
+#pragma unroll
+  for (int i = 0; i < AT_QT / 2; ++i) acc[i] = 0.f;
+
+  if (split < p.nps) {
+    int maxlim = 0;
+    for (int qi = 0; qi < nq; ++qi) maxlim = max(maxlim, sLim[qi]);
+    const int klo = split * p.KCH;
+    const int khi = min(maxlim, klo + p.KCH);
+    const T* Kb = (const T*)a.k_cache + ((size_t)b * a.max_prefix * a.Hkv + kvh) * hd;
+    const T* Vb = (const T*)a.v_cache + ((size_t)b * a.max_prefix * a.Hkv + kvh) * hd;
+    const size_t rstride = (size_t)a.Hkv * hd;
+    for (int kt0 = klo; kt0 < khi; kt0 += AT_KT) {
+      const int nk = min(AT_KT, khi - kt0);
+      for (int idx = tid; idx < AT_KT * hd; idx += BLOCK) {
+        const int kr = idx / hd, dd = idx % hd;
+        float kv = 0.f, vv = 0.f;
+        if (kr < nk) {
+          kv = El<T>::ld(Kb, (size_t)(kt0 + kr) * rstride + dd);
+          vv = El<T>::ld(Vb, (size_t)(kt0 + kr) * rstride + dd);
+        }
+        sK[kr][dd] = kv;
+        sV[kr][dd] = vv;
+      }
+      __syncthreads();
+      {
+        const int kr = tid % AT_KT;
+        for (int qi = tid / AT_KT; qi < nq; qi += BLOCK / AT_KT) {
+          float s = 0.f;
+          for (int dd = 0; dd < hd; ++dd) s += sQ[qi][dd] * sK[kr][dd];
+          sS[qi][kr] = (kr < nk && kt0 + kr < sLim[qi]) ? s : -INFINITY;
+        }
+      }
+      __syncthreads();
+      {
+        const int half = lane >> 5, kr = lane & 31;
+        for (int qi = wave * 2 + half; qi < nq; qi += 8) {
+          const float x = sS[qi][kr];
+          float t = x;
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) t = fmaxf(t, __shfl_xor(t, o));
+          const float mold = sM[qi];
+          const float mnew = fmaxf(mold, t);
+          const float pr = (mnew == -INFINITY || x == -INFINITY) ? 0.f : expf(x - mnew);
+          float ps = pr;
+#pragma unroll
+          for (int o = 16; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
+          ps = __shfl(ps, half * 32);
+          sS[qi][kr] = pr;
+          if (kr == 0) {
+            const float sc = (mold == -INFINITY) ? (mnew == -INFINITY ? 1.f : 0.f) : expf(mold - mnew);
+            sScale[qi] = sc;
+            sL[qi] = sL[qi] * sc + ps;
+            sM[qi] = mnew;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < AT_QT / 2; ++i) {
+        const int qi = qpv + i * qg_pv;
+        if (qi < nq) {
+          float s = acc[i] * sScale[qi];
+          for (int kr = 0; kr < nk; ++kr) s += sS[qi][kr] * sV[kr][dpv];
+          acc[i] = s;
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < AT_QT / 2; ++i) {
+      const int qi = qpv + i * qg_pv;
+      if (qi < nq) part[qi * prec + 2 + dpv] = acc[i];
+    }
+    if (tid < nq) {
+      part[tid * prec] = sM[tid];
+      part[tid * prec + 1] = sL[tid];
+    }
+  } else {
+    // in-tree keys of a level row: its ancestors' slots and its own
+    for (int qi = wave; qi < nq; qi += 4) {
+      const int gq = q0 + qi, j = gq / g;
+      const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
+      float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+      const float qa = sQ[qi][lane], qb = (lane + 64 < hd) ? sQ[qi][lane + 64] : 0.f;
+      for (int dep = 1; dep <= a.depth; ++dep) {
+        const size_t off =
+            ((((size_t)b * a.D + dep) * a.k + clamp_slot(nd.anc[dep - 1], a.k)) * a.Hkv + kvh) * hd;
+        const T* kp = (const T*)a.tk + off;
+        const T* vp = (const T*)a.tv + off;
+        const float kb2 = (lane + 64 < hd) ? El<T>::ld(kp, lane + 64) : 0.f;
+        const float s = wave_sum(qa * El<T>::ld(kp, lane) + qb * kb2);
+        const float mnew = fmaxf(m, s);
+        const float sc = (m == -INFINITY) ? 0.f : expf(m - mnew);
+        const float pr = expf(s - mnew);
+        l = l * sc + pr;
+        o0 = o0 * sc + pr * El<T>::ld(vp, lane);
+        if (lane + 64 < hd) o1 = o1 * sc + pr * El<T>::ld(vp, lane + 64);
+        m = mnew;
+      }
+      part[qi * prec + 2 + lane] = o0;
+      if (lane + 64 < hd) part[qi * prec + 2 + lane + 64] = o1;
+      if (lane == 0) {
+        part[qi * prec] = m;
+        part[qi * prec + 1] = l;
+      }
+    }
+  }
+
+  if (!arrive_last(a.cnt + wg, p.nsplit)) return;
+
+  for (int idx = tid; idx < nq * hd; idx += BLOCK) {
+    const int qi = idx / hd, dd = idx % hd, gq = q0 + qi;
+    const float* base = a.apart + (size_t)wg * p.nsplit * AT_QT * prec + qi * prec;
+    float M = -INFINITY;
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float* ps = base + (size_t)s * AT_QT * prec;
+      if (ps[1] > 0.f) M = fmaxf(M, ps[0]);
+    }
+    float L = 0.f, O = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float* ps = base + (size_t)s * AT_QT * prec;
+      if (ps[1] > 0.f) {
+        const float w = expf(ps[0] - M);
+        L += ps[1] * w;
+        O += ps[2 + dd] * w;
+      }
+    }
+    const int row = b * p.RS + gq / g, head = kvh * g + gq % g;
+    El<T>::st((T*)a.attn, (size_t)row * HD + head * hd + dd, O / L);
+  }
+}
+
+hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
+  const dim3 grid(a.B * a.Hkv * p.nqt, p.nsplit), block(BLOCK);
+  if (a.dtype == EAGLE_BF16) hipLaunchKernelGGL((k_attn<bf16_t>), grid, block, 0, s, a, p);
+  else hipLaunchKernelGGL((k_attn<float>), grid, block, 0, s, a, p);
+  return hipGetLastError();
+}
+
+}  // namespace eg

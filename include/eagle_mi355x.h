@@ -1,0 +1,232 @@
+/*
+ * eagle_mi355x.h -- C ABI of the MI355X (gfx950) EAGLE-2 draft-round library.
+ *
+ * One round of EAGLE feature-level drafting with EAGLE-2 dynamic draft trees:
+ *   eagle_draft_level(level = 1)          LM-head tail on the root's draft feature
+ *   eagle_draft_level(level = 2..depth)   draft forward on the k frontier nodes,
+ *                                         LM head, softmax, top-k, k*k -> k select
+ *   eagle_rerank_build_tree               top m-1 of every candidate + the root,
+ *                                         flattened, ancestor-only mask, positions
+ *   eagle_verify_greedy                   greedy longest-accepted-path walk
+ *   eagle_draft_extend                    draft forward over the accepted path with
+ *                                         the target's true features, KV append
+ *
+ * Sources, cited by title and section:
+ *   [P1] "EAGLE 推测解码为什么比 Medusa 快？（含 EAGLE-2 动态草稿树）" (study notes)
+ *   [P2] "(EAGLE 1)EAGLE: Speculative Sampling Requires Rethinking Feature Uncertainty"
+ *   [P3] Medusa -> EAGLE -> EAGLE-2 notes, zdszero.github.io "spec_medusa_eagle"
+ *   [P4] "投机解码：从eagle1到dflash" (EAGLE-2 flow diagram)
+ *
+ * Conventions shared by every entry point
+ *   Ownership  Every pointer is a device buffer owned by the caller (weights,
+ *              state, outputs, workspace).  The library allocates no device
+ *              memory and keeps no state between calls except a thread-local
+ *              error string.
+ *   Execution  Calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *              default stream) and never synchronise.  A round's calls must be
+ *              issued in round order on one stream; `ws` carries the round's
+ *              state (frontier, candidate pool, draft features, in-tree KV)
+ *              between calls and must not be used by two rounds at once.
+ *              Nothing in a round waits on the host, so a whole round can be
+ *              captured into one HIP graph.
+ *   Errors     0 = OK, negative = eagle_status.  Every shape, pointer and size
+ *              check runs on the host before any launch; a failing call
+ *              launches nothing.  Launch failures return EAGLE_ERR_HIP.  The
+ *              reason is in eagle_last_error().  Bad data found on the device
+ *              (a token id outside [0, vocab), a prefix length outside
+ *              [1, max_prefix - m]) is clamped and recorded in the workspace
+ *              error word (eagle_ws_view(EAGLE_WS_ERROR)); it never traps.
+ *   Types      dims.dtype applies to weights, features, K/V and the workspace
+ *              feature/KV regions.  Logits, scores and log-probabilities are
+ *              fp32; indices are int32; the tree mask is uint8.  All matrices
+ *              are row-major.
+ */
+#ifndef EAGLE_MI355X_H
+#define EAGLE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EAGLE_OK = 0,
+    EAGLE_ERR_ARG = -1,          /* null pointer, bad enum, level out of range   */
+    EAGLE_ERR_SHAPE = -2,        /* dims / tree config inconsistent              */
+    EAGLE_ERR_UNSUPPORTED = -3,  /* valid but outside what the kernels cover     */
+    EAGLE_ERR_WORKSPACE = -4,    /* ws_bytes < eagle_workspace_bytes()           */
+    EAGLE_ERR_HIP = -5           /* a HIP launch failed                          */
+} eagle_status;
+
+typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
+
+#define EAGLE_MAX_DEPTH 16
+#define EAGLE_MAX_TOPK 16
+#define EAGLE_MAX_TREE 64
+
+/* Model shapes.  d == n_heads * head_dim; n_heads % n_kv_heads == 0 (GQA when
+ * n_kv_heads < n_heads); head_dim in {64, 128}; ffn % 8 == 0.  The draft head
+ * is FC(2d -> d, bias) + one Llama decoder layer whose first input norm is the
+ * identity and which has no final norm ([P3] "在 SGLang 里"); embedding and LM
+ * head are the target's ([P1] §4.1 components).  rms_eps (e.g. 1e-6) is the
+ * post-attention RMSNorm epsilon; rope_theta (e.g. 1e4) the rotary base. */
+typedef struct {
+    int32_t d, n_heads, n_kv_heads, head_dim, ffn, vocab;
+    int32_t dtype;               /* eagle_dtype */
+    float rms_eps, rope_theta;
+} eagle_dims;
+
+/* Draft-head weights (all dims.dtype, row-major, Linear convention [out][in]):
+ *   fc_w [d][2d]   columns 0..d-1 take the feature, d..2d-1 the token embedding
+ *                  ([P1] §4.1 input = [f_j || e(t_{j+1})]);
+ *   fc_b [d];  wq [H*hd][d];  wk, wv [Hkv*hd][d];  wo [d][H*hd];
+ *   post_norm [d] (RMSNorm gain);  w_gate, w_up [ffn][d];  w_down [d][ffn];
+ *   embed [vocab][d] and lm_head [vocab][d]: the target's, shared and frozen. */
+typedef struct {
+    const void *fc_w, *fc_b, *wq, *wk, *wv, *wo, *post_norm, *w_gate, *w_up, *w_down;
+    const void *embed, *lm_head;
+} eagle_weights;
+
+/* Tree shape: (depth, topk, m) = SGLang's (num-steps, eagle-topk,
+ * num-draft-tokens) ([P3] "在 SGLang 里"); m counts the root.
+ * 1 <= batch; 2 <= depth <= 16; 1 <= topk <= 16; 2 <= m <= 64;
+ * m - 1 <= topk + (depth - 1) * topk^2; max_prefix = rows of the KV cache. */
+typedef struct {
+    int32_t batch, depth, topk, m, max_prefix;
+} eagle_tree_cfg;
+
+/* Per-sequence decoding state, owned by the caller and updated by the extend.
+ *   k_cache, v_cache [batch][max_prefix][Hkv][hd] (dtype): the draft's KV for
+ *       the accepted prefix, keys stored after RoPE.  Rows 0..prefix_len-1 are
+ *       valid; the last of them is the root row.
+ *   prefix_len [batch] int32; needs 1 <= prefix_len <= max_prefix - m.
+ *   root_feat [batch][d] (dtype): the draft feature predicted at the root row,
+ *       whose LM head gives level 1 (written by the previous extend).
+ *   root_token [batch] int32: the root token (the previous round's bonus). */
+typedef struct {
+    void *k_cache, *v_cache;
+    int32_t *prefix_len;
+    void *root_feat;
+    int32_t *root_token;
+} eagle_seq_state;
+
+/* Workspace records (readable through eagle_ws_view). */
+typedef struct {
+    float score;      /* sum of draft log-probabilities along the root path     */
+    float logp;       /* this node's own draft log-probability                  */
+    int32_t token;
+    int32_t parent;   /* pool index of the parent; -1 for children of the root  */
+    int32_t depth;    /* 1..depth                                               */
+    int32_t pslot;    /* frontier slot of the parent at its level; -1: the root */
+} eagle_pool_entry;   /* pool of a sequence: [topk + (depth-1)*topk^2] entries  */
+
+typedef struct {
+    int32_t token;
+    float score;
+    int32_t pool_idx;
+    int32_t pslot;                   /* frontier slot of the parent (-1: root)  */
+    int32_t anc[EAGLE_MAX_DEPTH];    /* anc[i] = frontier slot of the ancestor  */
+                                     /* at depth i+1 (the last one is itself)   */
+} eagle_frontier_node;
+
+/* Bytes of workspace for (dims, cfg); 0 if they are invalid. */
+size_t eagle_workspace_bytes(const eagle_dims *dims, const eagle_tree_cfg *cfg);
+
+/* Zero the workspace (counters and error word must start at zero).  Call once
+ * after allocating it; every kernel leaves its counters at zero again. */
+int eagle_workspace_init(const eagle_dims *dims, const eagle_tree_cfg *cfg, void *ws,
+                         size_t ws_bytes, void *stream);
+
+#define EAGLE_LEVEL_FULL 0
+#define EAGLE_LEVEL_TAIL_ONLY 1   /* level >= 2: skip the forward and run the LM-head
+                                     tail + select on the features already in the
+                                     workspace (EAGLE_WS_FEAT, depth level-1) */
+
+/* One tree level ([P1] §10.3 expansion; [P3] select_top_k_tokens).
+ * level 1: LM head + softmax + top-k on root_feat; the k children of each
+ *   root enter the pool and form frontier depth 1.  The first level's top-k
+ *   comes from the previous round's extend ([P3] "在 SGLang 里").
+ * level L >= 2: for each node x of frontier depth L-1 the row
+ *   [feature of x's parent || embed[token(x)]] goes through FC + bias, q/k/v,
+ *   RoPE at position prefix_len-1+(L-1), attention over all prefix rows plus
+ *   the in-tree K/V of x's ancestors and x itself (ancestor-only mask,
+ *   [P1] §12 item 5), o-projection + residual, RMSNorm, SwiGLU + residual
+ *   ([P1] §4.1; [P2] Core Idea; [P3]).  The predicted features go to
+ *   EAGLE_WS_FEAT depth L-1 and the row's K/V to the in-tree slots.  Then LM
+ *   head, softmax, top-k per row; child score = parent score + log p (the
+ *   path product of [P1] §10.3 in the log domain); all k*k children join the
+ *   pool in (frontier slot, rank) order, and the best k by (score desc, pool
+ *   index asc) form frontier depth L.
+ * Levels must run 1, 2, ..., depth in order within a round. */
+int eagle_draft_level(const eagle_dims *dims, const eagle_weights *w,
+                      const eagle_tree_cfg *cfg, const eagle_seq_state *state,
+                      int32_t level, int32_t flags, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Rerank and build ([P1] §10.3 rerank; [P3] organize_draft_results and
+ * build_tree_kernel_efficient; [P4] EAGLE-2 diagram).  Per sequence: the best
+ * m-1 pool entries by (score desc, depth asc, pool index asc) plus the root;
+ * flattened root first, then depth-major, then by parent's flat index, then
+ * by child rank.  Outputs (device, [batch][m] unless noted):
+ *   tokens, parents (flat index, -1 for the root), depth, positions
+ *   (prefix_len-1+depth), mask [batch][m][m] uint8 (1 iff column is an
+ *   ancestor of the row or the row itself), node_logscore (0 for the root).
+ * Any output pointer except tokens and parents may be NULL. */
+int eagle_rerank_build_tree(const eagle_dims *dims, const eagle_tree_cfg *cfg,
+                            const eagle_seq_state *state, void *ws, size_t ws_bytes,
+                            int32_t *tokens, int32_t *parents, int32_t *depth,
+                            int32_t *positions, uint8_t *mask, float *node_logscore,
+                            void *stream);
+
+/* Greedy verification ([P4] EAGLE-2 diagram: accept the longest consistent
+ * path, back off to the last accepted node).  target_logits [batch][m][vocab]
+ * fp32 are the target's logits at each flat tree node.  From the root: t* =
+ * argmax of the current node's row (lowest id on exact ties); if a child has
+ * token t*, descend, else stop.  Outputs: accept_len [batch] = nodes on the
+ * path including the root (accepted drafts + 1); accept_path [batch][depth+1]
+ * flat indices, -1 after the end; bonus [batch] = t* at the stop. */
+int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
+                        const int32_t *tokens, const int32_t *parents, int32_t *accept_len,
+                        int32_t *accept_path, int32_t *bonus, void *stream);
+
+/* Draft extend ([P3] "在 SGLang 里": rerun the draft over the accepted
+ * positions with the target's true hidden states, take row accept_len-1 as
+ * the next start; [P2] Core Idea; [P1] §12 item 3).  Row i < accept_len
+ * carries [true_feat[path_i] || embed[token of path_{i+1}, or the bonus for
+ * the last row]] at position prefix_len+i and attends the prefix plus extend
+ * rows 0..i.  Rows are padded to m per sequence (padding rows are computed
+ * and ignored).  Updates the state: K/V rows prefix_len..prefix_len+m-1
+ * written (the first accept_len are valid), prefix_len += accept_len,
+ * root_feat = feature of row accept_len-1, root_token = bonus.
+ * true_feat [batch][m][d] (dtype) are the target's features at each flat
+ * tree node; tokens [batch][m], accept_len, accept_path, bonus as produced
+ * by the calls above. */
+int eagle_draft_extend(const eagle_dims *dims, const eagle_weights *w,
+                       const eagle_tree_cfg *cfg, const eagle_seq_state *state,
+                       const void *true_feat, const int32_t *tokens, const int32_t *accept_len,
+                       const int32_t *accept_path, const int32_t *bonus, void *ws,
+                       size_t ws_bytes, void *stream);
+
+const char *eagle_status_str(int status);
+const char *eagle_last_error(void);   /* thread-local text of the last failure */
+
+/* Workspace regions, for tests and debugging. */
+typedef enum {
+    EAGLE_WS_ERROR = 0,     /* int32[4]; [0] bit 0: token id clamped, bit 1: prefix_len clamped */
+    EAGLE_WS_POOL = 1,      /* eagle_pool_entry [batch][pool]                        */
+    EAGLE_WS_FRONTIER = 2,  /* eagle_frontier_node [depth+1][batch][topk] (by depth)  */
+    EAGLE_WS_FEAT = 3,      /* dtype [depth][batch][topk][d]: features of frontier nodes */
+    EAGLE_WS_TREE_K = 4,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree keys (post-RoPE) */
+    EAGLE_WS_TREE_V = 5,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree values    */
+    EAGLE_WS_EXT_H = 6      /* dtype [batch][m][d]: extend output features per row     */
+} eagle_ws_region;
+
+int eagle_ws_view(const eagle_dims *dims, const eagle_tree_cfg *cfg, const void *ws,
+                  int32_t what, void **ptr, size_t *bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_MI355X_H */

@@ -60,8 +60,8 @@ class TreeConfig:
 
     @property
     def max_prefix(self) -> int:
-        # room for the draft extend, which appends up to m rows
-        return self.P_hi + self.m
+        # room for three draft extends, each appending up to m rows
+        return self.P_hi + 3 * self.m
 
     @property
     def pool_size(self) -> int:

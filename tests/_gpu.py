@@ -1,0 +1,192 @@
+"""Helpers of the GPU parity tests.
+
+Stage-isolated parity: every stage's inputs are produced by the oracle (or
+the seeded generator), rounded to the GPU's storage types, written into the
+GPU workspace, and fed to both sides.  No oracle input comes from the HIP
+path.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import eagle_oracle as O
+
+try:
+    import torch
+    HAVE_GPU = torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    HAVE_GPU = False
+
+NEAR = O.NEAR_TIE
+FEAT_TOL = {"f32": 1e-4, "bf16": 2e-2}   # relative L2 of feature rows
+PROB_TOL = 1e-3                           # |delta| of top-k child probabilities
+SCORE_TOL = 1e-3                          # |delta| of node log-scores
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def quant(x: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 value of x after rounding to the GPU storage type."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "bf16":
+        return O.widen(synth.bf16_bits(x.astype(np.float32)), "bf16")
+    return x.astype(np.float32).astype(np.float64)
+
+
+def store(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage bytes of x in the GPU type (uint16 bf16 bits or float32)."""
+    x = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return synth.bf16_bits(x) if dtype == "bf16" else x
+
+
+def rel_l2(g: np.ndarray, o: np.ndarray) -> float:
+    g = np.asarray(g, np.float64).reshape(-1)
+    o = np.asarray(o, np.float64).reshape(-1)
+    return float(np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-30))
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().double().cpu().numpy()
+    return t.cpu().numpy()
+
+
+class OracleSeqs:
+    """Oracle state per sequence, advanced level by level."""
+
+    def __init__(self, cfg, inp, seqs: Optional[Sequence[int]] = None):
+        self.cfg, self.inp = cfg, inp
+        self.model = O.Model(cfg, inp)
+        self.seqs = list(range(cfg.B)) if seqs is None else list(seqs)
+        W = lambda a: O.widen(a, cfg.dtype)
+        self.st = {b: O.SeqState(W(inp["k_cache"][b]), W(inp["v_cache"][b]),
+                                 int(inp["prefix_len"][b]), W(inp["root_feat"][b]),
+                                 int(inp["root_token"][b])) for b in self.seqs}
+        self.pool: Dict[int, List[O.PoolEntry]] = {b: [] for b in self.seqs}
+        self.F: Dict[int, List[List[O.FrontierNode]]] = {b: [] for b in self.seqs}
+        self.feats: Dict[int, dict] = {b: {} for b in self.seqs}
+        self.intree: Dict[int, dict] = {b: {} for b in self.seqs}
+        self.tail_margin: Dict[int, List[float]] = {b: [] for b in self.seqs}
+        self.sel_margin: Dict[int, List[float]] = {b: [] for b in self.seqs}
+
+    def level1(self):
+        for b in self.seqs:
+            pool, F, mg = O.level_one(self.model, self.st[b], self.cfg.k)
+            self.pool[b], self.F[b] = pool, [F]
+            self.tail_margin[b] += mg["tail"]
+
+    def forward(self, level: int) -> Dict[int, np.ndarray]:
+        return {b: O.level_step_forward(self.model, self.st[b], level, self.F[b][-1],
+                                        self.feats[b], self.intree[b]) for b in self.seqs}
+
+    def tail(self, level: int, h: Dict[int, np.ndarray]):
+        for b in self.seqs:
+            F, tails, sm = O.level_step_tail(self.model, level, self.F[b][-1], h[b], self.pool[b],
+                                             self.cfg.k)
+            self.F[b].append(F)
+            self.tail_margin[b] += tails
+            self.sel_margin[b].append(sm)
+
+    def quantize_state(self, depth: int):
+        """Round features and in-tree K/V of `depth` (and scores of frontier
+        `depth`) to the GPU storage types, as the GPU would hold them."""
+        dt = self.cfg.dtype
+        for b in self.seqs:
+            for key in list(self.feats[b]):
+                if key[0] == depth:
+                    self.feats[b][key] = quant(self.feats[b][key], dt)
+            for key in list(self.intree[b]):
+                if key[0] == depth:
+                    kk, vv = self.intree[b][key]
+                    self.intree[b][key] = (quant(kk, dt), quant(vv, dt))
+
+    def quantize_scores(self):
+        for b in self.seqs:
+            for e in self.pool[b]:
+                e.score = float(np.float32(e.score))
+                e.logp = float(np.float32(e.logp))
+            for F in self.F[b]:
+                for x in F:
+                    x.score = float(np.float32(x.score))
+
+
+def frontier_records(cfg, nodes: List[O.FrontierNode]) -> np.ndarray:
+    from eagle_draft_trees_amd import _lib as L
+    rec = np.zeros(len(nodes), dtype=L.FRONTIER_DTYPE)
+    for j, x in enumerate(nodes):
+        rec[j]["token"], rec[j]["score"] = x.token, np.float32(x.score)
+        rec[j]["pool_idx"], rec[j]["pslot"] = x.pool_idx, x.pslot
+        rec[j]["anc"][:len(x.anc)] = x.anc
+    return rec
+
+
+def pool_records(pool: List[O.PoolEntry]) -> np.ndarray:
+    from eagle_draft_trees_amd import _lib as L
+    rec = np.zeros(len(pool), dtype=L.POOL_DTYPE)
+    for i, e in enumerate(pool):
+        rec[i] = (np.float32(e.score), np.float32(e.logp), e.token, e.parent, e.depth, e.pslot)
+    return rec
+
+
+def seed_workspace(r, orc: OracleSeqs, upto_depth: int, with_pool: bool = True):
+    """Write the oracle's frontiers 1..upto_depth, features and in-tree K/V of
+    depths 1..upto_depth-1 and the pool into the GPU workspace."""
+    from eagle_draft_trees_amd import _lib as L
+    cfg = r.cfg
+    B, k, d, D = cfg.B, cfg.k, cfg.d, cfg.D
+    es = 2 if cfg.dtype == "bf16" else 4
+    fsz = L.FRONTIER_DTYPE.itemsize
+    kvrow = cfg.Hkv * cfg.hd
+    for b in orc.seqs:
+        for depth in range(1, upto_depth + 1):
+            rec = frontier_records(cfg, orc.F[b][depth - 1])
+            r.ws_write(L.WS_FRONTIER, rec, ((depth * B + b) * k) * fsz)
+        for (depth, slot), h in orc.feats[b].items():
+            if depth < upto_depth:
+                r.ws_write(L.WS_FEAT, store(h, cfg.dtype), (((depth * B) + b) * k + slot) * d * es)
+        for (depth, slot), (kk, vv) in orc.intree[b].items():
+            if depth < upto_depth:
+                off = (((b * D) + depth) * k + slot) * kvrow * es
+                r.ws_write(L.WS_TREE_K, store(kk.reshape(-1), cfg.dtype), off)
+                r.ws_write(L.WS_TREE_V, store(vv.reshape(-1), cfg.dtype), off)
+        if with_pool and orc.pool[b]:
+            r.ws_write(L.WS_POOL, pool_records(orc.pool[b]),
+                       b * cfg.pool_size * L.POOL_DTYPE.itemsize)
+
+
+def gpu_frontier(r, depth: int) -> np.ndarray:
+    from eagle_draft_trees_amd import _lib as L
+    cfg = r.cfg
+    rec = r.ws_records(L.WS_FRONTIER)
+    return rec.reshape(cfg.D + 1, cfg.B, cfg.k)[depth]
+
+
+def gpu_pool(r) -> np.ndarray:
+    from eagle_draft_trees_amd import _lib as L
+    return r.ws_records(L.WS_POOL).reshape(r.cfg.B, r.cfg.pool_size)
+
+
+def gpu_feats(r, depth: int) -> np.ndarray:
+    from eagle_draft_trees_amd import _lib as L
+    cfg = r.cfg
+    t = r.ws_typed(L.WS_FEAT).view(cfg.D, cfg.B, cfg.k, cfg.d)[depth]
+    return to_host(t)
+
+
+def gpu_tree_kv(r):
+    from eagle_draft_trees_amd import _lib as L
+    cfg = r.cfg
+    shp = (cfg.B, cfg.D, cfg.k, cfg.Hkv, cfg.hd)
+    return (to_host(r.ws_typed(L.WS_TREE_K).view(*shp)),
+            to_host(r.ws_typed(L.WS_TREE_V).view(*shp)))

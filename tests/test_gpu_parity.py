@@ -1,0 +1,466 @@
+"""GPU parity of the HIP draft round against the fp64 oracle, through the C ABI.
+
+Gate (stage-isolated): each stage's inputs come from the generator or from
+the oracle's earlier stages, rounded to the GPU's storage types and written
+into the GPU workspace; both sides then compute that stage.
+  * features, in-tree K/V, extend rows: relative L2 <= 1e-4 (fp32), 2e-2 (bf16)
+  * top-k child probabilities |delta| <= 1e-3; node log-scores |delta| <= 1e-3
+  * token ids, parents, frontier, pool, tree, mask, positions, accept length,
+    path, bonus: bit-exact wherever the oracle's selection margins exceed
+    1e-3 (log domain); rows below are counted as near-tie and reported.
+End-to-end (gated for fp32 shapes, reported for bf16): whole rounds from the
+generated inputs, three rounds in a row.
+"""
+from __future__ import annotations
+
+import gc
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import eagle_oracle as O
+from tests._gpu import (FEAT_TOL, HAVE_GPU, NEAR, PROB_TOL, SCORE_TOL, OracleSeqs, gpu_feats,
+                        gpu_frontier, gpu_pool, gpu_tree_kv, pool_records, quant, rel_l2,
+                        say, seed_workspace, store, to_host)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not HAVE_GPU, reason="needs a GPU")]
+
+FAST = ["tiny", "tiny_bf16", "ragged_f32", "ragged_bf16", "hd128_bf16", "chain_small", "wide_bf16"]
+FULL = ["7b", "13b", "70b", "chain"]
+# sequences the oracle checks at full size (the GPU runs the whole batch)
+SAMPLE = {"13b": [0, 7, 15], "70b": [0, 3], "chain": [0, 31, 63]}
+
+_CACHE: dict = {}
+
+
+def get(name):
+    import torch
+    from eagle_draft_trees_amd.round import DraftRound
+    if name not in _CACHE:
+        _CACHE.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+        cfg = synth.config_by_name(name)
+        say(f"  generating inputs for {name}")
+        inp = synth.make_inputs(cfg, seed=11)
+        r = DraftRound(cfg, inp)
+        _CACHE[name] = (cfg, inp, r, O.Model(cfg, inp), SAMPLE.get(name))
+    cfg, inp, r, model, seqs = _CACHE[name]
+    r.reset_state(inp)
+    torch.cuda.synchronize()
+    return cfg, inp, r, model, seqs
+
+
+def oracle_for(cfg, inp, model, seqs):
+    o = OracleSeqs.__new__(OracleSeqs)
+    OracleSeqs.__init__(o, cfg, inp, seqs)
+    o.model = model
+    return o
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _check_children(cfg, gp_seq, o_entries, base, tails, strict):
+    """Pool entries of one sequence's level: probabilities and scores within
+    tolerance always; ids bit-exact where the row's tail margin is clear."""
+    k = cfg.k
+    g = gp_seq[base:base + len(o_entries)]
+    n_rows = len(o_entries) // k
+    near_rows = 0
+    for j in range(n_rows):
+        og = o_entries[j * k:(j + 1) * k]
+        gg = g[j * k:(j + 1) * k]
+        assert np.allclose(np.exp(gg["logp"]), [math.exp(e.logp) for e in og], atol=PROB_TOL, rtol=0)
+        assert np.allclose(gg["score"], [e.score for e in og], atol=SCORE_TOL, rtol=0)
+        if tails[j] > NEAR:
+            assert list(gg["token"]) == [e.token for e in og], f"row {j} ids"
+            assert list(gg["parent"]) == [e.parent for e in og]
+            assert list(gg["depth"]) == [e.depth for e in og]
+            assert list(gg["pslot"]) == [e.pslot for e in og]
+        else:
+            near_rows += 1
+    return near_rows
+
+
+def _check_frontier(gf_seq, o_front):
+    assert list(gf_seq["token"][:len(o_front)]) == [x.token for x in o_front]
+    assert list(gf_seq["pool_idx"][:len(o_front)]) == [x.pool_idx for x in o_front]
+    assert list(gf_seq["pslot"][:len(o_front)]) == [x.pslot for x in o_front]
+    for j, x in enumerate(o_front):
+        assert list(gf_seq[j]["anc"][:len(x.anc)]) == list(x.anc)
+
+
+# ------------------------------------------------------------------ level 1
+
+@pytest.mark.parametrize("name", FAST + FULL)
+def test_level1_tail(name):
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[level1 tail] {name}")
+    orc = oracle_for(cfg, inp, model, seqs)
+    r.level(1)
+    sync()
+    orc.level1()
+    gp, gf = gpu_pool(r), gpu_frontier(r, 1)
+    near = 0
+    for b in orc.seqs:
+        n = _check_children(cfg, gp[b], orc.pool[b], 0, orc.tail_margin[b], True)
+        near += n
+        if n == 0:
+            _check_frontier(gf[b], orc.F[b][0])
+    say(f"  level1 {name}: {len(orc.seqs)} sequences, {near} near-tie rows")
+
+
+# ------------------------------------------------------------------ levels >= 2
+
+def _levels_for(name):
+    cfg = synth.config_by_name(name)
+    if name in FULL:
+        return [2] + ([3] if name in ("7b", "chain") else [])
+    return list(range(2, cfg.D + 1))
+
+
+@pytest.mark.parametrize("name,level", [(n, L) for n in FAST + FULL for L in _levels_for(n)])
+def test_level_forward_then_tail(name, level):
+    import torch
+    from eagle_draft_trees_amd import _lib as L
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[level {level}] {name}")
+    orc = oracle_for(cfg, inp, model, seqs)
+    orc.level1()
+    for lv in range(2, level):
+        h = orc.forward(lv)
+        orc.tail(lv, h)
+    for dep in range(1, level - 1):
+        orc.quantize_state(dep)
+    orc.quantize_scores()
+    seed_workspace(r, orc, upto_depth=level - 1)
+    sync()
+    r.level(level, L.EAGLE_LEVEL_FULL)
+    sync()
+    h_o = orc.forward(level)  # the same (rounded) stage inputs
+    depth = level - 1
+    gfeat = gpu_feats(r, depth)
+    gtk, gtv = gpu_tree_kv(r)
+    tol = FEAT_TOL[cfg.dtype]
+    worst = 0.0
+    for b in orc.seqs:
+        for j in range(cfg.k):
+            e = rel_l2(gfeat[b, j], h_o[b][j])
+            worst = max(worst, e)
+            assert e <= tol, (b, j, e)
+            ok, ov = orc.intree[b][(depth, j)]
+            assert rel_l2(gtk[b, depth, j], ok) <= tol
+            assert rel_l2(gtv[b, depth, j], ov) <= tol
+    say(f"  forward {name} level {level}: worst feature rel L2 {worst:.2e} (tol {tol})")
+
+    # tail-only stage on the oracle's features, rounded as the GPU stores them
+    orc.quantize_state(depth)
+    es = 2 if cfg.dtype == "bf16" else 4
+    for b in orc.seqs:
+        for j in range(cfg.k):
+            r.ws_write(L.WS_FEAT, store(orc.feats[b][(depth, j)], cfg.dtype),
+                       (((depth * cfg.B) + b) * cfg.k + j) * cfg.d * es)
+    sync()
+    r.level(level, L.EAGLE_LEVEL_TAIL_ONLY)
+    sync()
+    hq = {b: np.stack([orc.feats[b][(depth, j)] for j in range(cfg.k)]) for b in orc.seqs}
+    orc.tail(level, hq)
+    gp, gf = gpu_pool(r), gpu_frontier(r, level)
+    base = cfg.k + (level - 2) * cfg.k * cfg.k
+    near = 0
+    for b in orc.seqs:
+        tails = orc.tail_margin[b][-cfg.k:]
+        n = _check_children(cfg, gp[b], orc.pool[b][base:base + cfg.k * cfg.k], base, tails, True)
+        near += n
+        if n == 0 and orc.sel_margin[b][-1] > NEAR:
+            _check_frontier(gf[b], orc.F[b][-1])
+            assert np.allclose(gf[b]["score"][:cfg.k], [x.score for x in orc.F[b][-1]],
+                               atol=SCORE_TOL, rtol=0)
+    say(f"  tail {name} level {level}: {near} near-tie rows")
+
+
+# ------------------------------------------------------------------ rerank, verify, extend
+
+def _oracle_pool(cfg, inp, model, seqs, seed=5):
+    """A full-depth candidate pool from the oracle (tails on random features)."""
+    orc = oracle_for(cfg, inp, model, seqs)
+    orc.level1()
+    rng = np.random.default_rng(seed)
+    for lv in range(2, cfg.D + 1):
+        h = {b: rng.normal(size=(cfg.k, cfg.d)) for b in orc.seqs}
+        orc.tail(lv, h)
+    orc.quantize_scores()
+    return orc
+
+
+def _trees(cfg, orc):
+    out = {}
+    for b in orc.seqs:
+        sel, margin = O.rerank(orc.pool[b], cfg.m)
+        out[b] = (O.build_tree(orc.pool[b], sel, orc.st[b].root_token, orc.st[b].P), margin)
+    return out
+
+
+@pytest.mark.parametrize("name", FAST + FULL)
+def test_rerank_build(name):
+    from eagle_draft_trees_amd import _lib as L
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[rerank/build] {name}")
+    orc = _oracle_pool(cfg, inp, model, seqs)
+    for b in orc.seqs:
+        r.ws_write(L.WS_POOL, pool_records(orc.pool[b]), b * cfg.pool_size * L.POOL_DTYPE.itemsize)
+    sync()
+    r.rerank()
+    sync()
+    trees = _trees(cfg, orc)
+    for name_, t in (("tokens", r.tokens), ("parents", r.parents), ("depth", r.depth),
+                     ("positions", r.positions)):
+        g = t.cpu().numpy()
+        for b in orc.seqs:
+            want = getattr(trees[b][0], name_)
+            assert list(g[b]) == list(want), (name_, b)
+    gm, gs = r.mask.cpu().numpy(), r.logscore.cpu().numpy()
+    for b in orc.seqs:
+        tr = trees[b][0]
+        assert np.array_equal(gm[b], tr.mask)
+        assert np.array_equal(gs[b], tr.logscore.astype(np.float32))
+    say(f"  rerank {name}: min margin {min(m for _, m in trees.values()):.2e} (exact on equal keys)")
+
+
+def _plant(cfg, inp, trees, seqs, seed=3, p=0.8):
+    """Target logits with planted accepted paths: along a random root-to-leaf
+    walk, each step's child token gets the row's top logit with prob p."""
+    TL = inp["target_logits"].copy()
+    rng = np.random.default_rng(seed)
+    for b in seqs:
+        tr = trees[b][0]
+        node = 0
+        while True:
+            kids = [c for c in range(cfg.m) if tr.parents[c] == node]
+            if not kids or rng.random() > p:
+                break
+            c = kids[rng.integers(len(kids))]
+            TL[b, node, tr.tokens[c]] = TL[b, node].max() + 1.0
+            node = c
+    return TL
+
+
+def _upload_tree(r, trees, seqs):
+    import torch
+    tok, par = r.tokens.cpu().numpy(), r.parents.cpu().numpy()
+    for b in seqs:
+        tok[b], par[b] = trees[b][0].tokens, trees[b][0].parents
+    r.tokens.copy_(torch.from_numpy(tok))
+    r.parents.copy_(torch.from_numpy(par))
+
+
+@pytest.mark.parametrize("name", FAST + FULL)
+def test_verify_walk(name):
+    import torch
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[verify] {name}")
+    orc = _oracle_pool(cfg, inp, model, seqs)
+    trees = _trees(cfg, orc)
+    TL = _plant(cfg, inp, trees, orc.seqs)
+    _upload_tree(r, trees, orc.seqs)
+    r.target_logits.copy_(torch.from_numpy(TL))
+    sync()
+    r.verify()
+    sync()
+    al, ap, bo = r.accept_len.cpu().numpy(), r.accept_path.cpu().numpy(), r.bonus.cpu().numpy()
+    near, lens = 0, []
+    for b in orc.seqs:
+        tr = trees[b][0]
+        path, alen, bonus, wm = O.verify_greedy(TL[b].astype(np.float64), tr.tokens, tr.parents)
+        if min(wm) <= NEAR:
+            near += 1
+            continue
+        assert al[b] == alen and bo[b] == bonus, (b, al[b], alen, bo[b], bonus)
+        assert list(ap[b][:alen]) == path and all(x == -1 for x in ap[b][alen:])
+        lens.append(alen)
+    say(f"  verify {name}: accept lengths {lens}, near-tie {near}")
+
+
+@pytest.mark.parametrize("name", FAST + FULL)
+def test_extend(name):
+    import torch
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[extend] {name}")
+    orc = _oracle_pool(cfg, inp, model, seqs)
+    trees = _trees(cfg, orc)
+    TL = _plant(cfg, inp, trees, orc.seqs, p=0.9)
+    _upload_tree(r, trees, orc.seqs)
+    al, ap, bo = (r.accept_len.cpu().numpy(), r.accept_path.cpu().numpy(), r.bonus.cpu().numpy())
+    ores = {}
+    for b in orc.seqs:
+        tr = trees[b][0]
+        path, alen, bonus, _ = O.verify_greedy(TL[b].astype(np.float64), tr.tokens, tr.parents)
+        al[b], bo[b] = alen, bonus
+        ap[b] = path + [-1] * (cfg.D + 1 - alen)
+        ores[b] = (path, alen, bonus)
+    r.accept_len.copy_(torch.from_numpy(al))
+    r.accept_path.copy_(torch.from_numpy(ap))
+    r.bonus.copy_(torch.from_numpy(bo))
+    P0 = inp["prefix_len"].copy()
+    sync()
+    r.extend()
+    sync()
+    tol = FEAT_TOL[cfg.dtype]
+    tf = O.widen(inp["true_feat"], cfg.dtype)
+    g_root = to_host(r.root_feat)
+    g_ext = to_host(r.ws_typed(6).view(cfg.B, cfg.m, cfg.d))
+    g_k, g_v = to_host(r.k_cache), to_host(r.v_cache)
+    g_plen, g_rtok = r.prefix_len.cpu().numpy(), r.root_token.cpu().numpy()
+    worst, lens = 0.0, []
+    for b in orc.seqs:
+        path, alen, bonus = ores[b]
+        st = orc.st[b]
+        h, kn, vn = O.draft_extend(model, st, tf[b], trees[b][0].tokens, path, bonus)
+        lens.append(alen)
+        assert g_plen[b] == P0[b] + alen and g_rtok[b] == bonus
+        for i in range(alen):
+            e = rel_l2(g_ext[b, i], h[i])
+            worst = max(worst, e)
+            assert e <= tol, (b, i, e)
+            assert rel_l2(g_k[b, P0[b] + i], kn[i]) <= tol
+            assert rel_l2(g_v[b, P0[b] + i], vn[i]) <= tol
+        assert rel_l2(g_root[b], h[alen - 1]) <= tol
+    say(f"  extend {name}: accept lengths {lens}, worst rel L2 {worst:.2e} (tol {tol})")
+
+
+# ------------------------------------------------------------------ whole rounds
+
+def _oracle_draft(model, st, cfg):
+    k, D = cfg.k, cfg.D
+    pool, F, mg = O.level_one(model, st, k)
+    margins = list(mg["tail"])
+    feats, intree = {}, {}
+    for level in range(2, D + 1):
+        h = O.level_step_forward(model, st, level, F, feats, intree)
+        F, tails, sm = O.level_step_tail(model, level, F, h, pool, k)
+        margins += tails + [sm]
+    sel, rm = O.rerank(pool, cfg.m)
+    margins.append(rm)
+    return O.build_tree(pool, sel, st.root_token, st.P), min(margins)
+
+
+def _run_rounds(name, rounds, gate):
+    import torch
+    cfg, inp, r, model, seqs = get(name)
+    seqs = list(range(cfg.B)) if seqs is None else seqs
+    W = lambda a: O.widen(a, cfg.dtype)
+    states = {b: O.SeqState(W(inp["k_cache"][b]), W(inp["v_cache"][b]), int(inp["prefix_len"][b]),
+                            W(inp["root_feat"][b]), int(inp["root_token"][b])) for b in seqs}
+    tf = W(inp["true_feat"])
+    alive = set(seqs)
+    stats = {"match": 0, "compared": 0, "near": 0, "feat": []}
+    rng = np.random.default_rng(99)
+    for rd in range(rounds):
+        trees = {}
+        for b in sorted(alive):
+            tr, mmin = _oracle_draft(model, states[b], cfg)
+            trees[b] = (tr, mmin)
+        TL = inp["target_logits"].copy()
+        for b in sorted(alive):   # plant a path so that accept lengths vary
+            tr = trees[b][0]
+            node = 0
+            while rng.random() < 0.85:
+                kids = [c for c in range(cfg.m) if tr.parents[c] == node]
+                if not kids:
+                    break
+                c = kids[rng.integers(len(kids))]
+                TL[b, node, tr.tokens[c]] = TL[b, node].max() + 1.0
+                node = c
+        r.target_logits.copy_(torch.from_numpy(TL))
+        r.run_round()
+        sync()
+        err = int(r.ws_region(0).view(torch.int32)[0].item())
+        assert err == 0, f"device error word {err:#x} after round {rd}"
+        g_tok, g_par = r.tokens.cpu().numpy(), r.parents.cpu().numpy()
+        g_mask, g_pos = r.mask.cpu().numpy(), r.positions.cpu().numpy()
+        g_al, g_bo = r.accept_len.cpu().numpy(), r.bonus.cpu().numpy()
+        g_root = to_host(r.root_feat)
+        g_plen = r.prefix_len.cpu().numpy()
+        for b in sorted(alive):
+            tr, mmin = trees[b]
+            P0 = states[b].P
+            path, alen, bonus, wm = O.verify_greedy(TL[b].astype(np.float64), tr.tokens, tr.parents)
+            O.draft_extend(model, states[b], tf[b], tr.tokens, path, bonus)
+            if min(mmin, min(wm)) <= NEAR:
+                stats["near"] += 1
+                alive.discard(b)
+                continue
+            stats["compared"] += 1
+            diff = [f for f, ok in (
+                ("tokens", list(g_tok[b]) == list(tr.tokens)),
+                ("parents", list(g_par[b]) == list(tr.parents)),
+                ("mask", np.array_equal(g_mask[b], tr.mask)),
+                ("positions", list(g_pos[b]) == list(tr.positions)),
+                ("accept_len", g_al[b] == alen), ("bonus", g_bo[b] == bonus),
+                ("prefix_len", g_plen[b] == P0 + alen)) if not ok]
+            same = not diff
+            fe = rel_l2(g_root[b], states[b].root_feat)
+            stats["feat"].append(fe)
+            if gate:
+                assert same, (name, rd, b, diff, list(g_tok[b]), list(tr.tokens))
+                assert fe <= FEAT_TOL[cfg.dtype], (name, rd, b, fe)
+            if same:
+                stats["match"] += 1
+            else:
+                alive.discard(b)  # the states have diverged
+    return stats
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_f32", "chain_small"])
+def test_round_end_to_end_fp32(name):
+    say(f"[end-to-end fp32] {name}")
+    s = _run_rounds(name, 3, gate=True)
+    say(f"  {name}: {s['match']}/{s['compared']} sequence-rounds identical, {s['near']} near-tie, "
+        f"worst root feature rel L2 {max(s['feat'], default=0):.2e}")
+    assert s["compared"] > 0
+
+
+@pytest.mark.parametrize("name", ["tiny_bf16", "ragged_bf16", "hd128_bf16", "wide_bf16", "7b"])
+def test_round_end_to_end_bf16_reported(name):
+    say(f"[end-to-end bf16, reported] {name}")
+    s = _run_rounds(name, 2, gate=False)
+    say(f"  {name}: {s['match']}/{s['compared']} sequence-rounds identical to the oracle, "
+        f"{s['near']} near-tie, root feature rel L2 max {max(s['feat'], default=0):.2e}")
+    assert all(f <= FEAT_TOL["bf16"] for f in s["feat"][:1]) or s["compared"] == 0
+
+
+# ------------------------------------------------------------------ determinism, data errors
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "7b"])
+def test_repeat_runs_are_bit_identical(name):
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[determinism] {name}")
+    outs = []
+    for rep in range(2):
+        r.reset_state(inp)
+        r.run_round()
+        sync()
+        outs.append([t.cpu().numpy().copy() for t in (r.tokens, r.parents, r.mask, r.logscore,
+                                                      r.accept_len, r.bonus, r.prefix_len)]
+                    + [to_host(r.root_feat).copy(), r.ws.cpu().numpy().copy()])
+    for a, b in zip(*outs[:2]):
+        assert np.array_equal(a, b)
+
+
+def test_out_of_range_token_is_clamped_and_flagged():
+    import torch
+    cfg, inp, r, model, seqs = get("ragged_f32")
+    say("[data errors] ragged_f32")
+    r.root_token[1] = cfg.V + 5
+    sync()
+    r.run_round()
+    sync()
+    err = r.ws_region(0).view(torch.int32)[0].item()
+    assert err & 1, err
+    assert int(r.tokens[1, 0]) == cfg.V - 1

@@ -44,10 +44,12 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   p.zg = cdiv(M, 64);
   p.nblk = cdiv(p.N, 64);
   const int ks = d.dtype == EAGLE_BF16 ? 32 : 16;
+  // a split's K range is whole pipeline iterations (8 k-steps)
+  const int unit = 8 * ks;
   const int base = p.nblk * p.zg;
-  int S = std::max(1, cdiv(TARGET_WG, base));
-  S = std::min(S, std::max(1, p.K / (4 * ks)));
-  int Kc = cdiv(cdiv(p.K, S), ks) * ks;
+  int S = std::min(cdiv(TARGET_WG, base), std::max(1, p.K / unit));
+  S = std::max(1, std::min(S, GEMM_MAXS));
+  const int Kc = cdiv(cdiv(p.K, S), unit) * unit;
   S = cdiv(p.K, Kc);
   p.S = S;
   p.Kc = Kc;
@@ -62,6 +64,7 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
   p.zg = cdiv(M, 64);
   p.nblk = cdiv(d.vocab, 64);
   p.rec = 2 + 2 * topk;
+  p.G = std::max(1, std::min(p.nblk, 8192 / topk));
   p.part_floats = (size_t)M * p.nblk * p.rec;
   return p;
 }
@@ -75,8 +78,10 @@ AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& 
   p.nqt = cdiv(p.nq, p.QT);
   const int nwg = nseq * d.n_kv_heads * p.nqt;
   const int maxP = c.max_prefix;
-  const int nps_t = std::max(1, cdiv(1024, nwg));
-  p.KCH = std::max(32, cdiv(cdiv(maxP, nps_t), 32) * 32);
+  // about 512 workgroups in all, slices of at least 64 keys, at most 128 slices
+  const int nps_t = std::max(1, cdiv(512, nwg));
+  p.KCH = std::max(std::max(64, cdiv(maxP, 127)), cdiv(cdiv(maxP, nps_t), 32) * 32);
+  p.KCH = cdiv(p.KCH, 32) * 32;
   p.nps = cdiv(maxP, p.KCH);
   p.nsplit = p.nps + (mode == MODE_LEVEL ? 1 : 0);
   p.part_floats = (size_t)nwg * p.nsplit * p.QT * (d.head_dim + 2);
@@ -159,8 +164,15 @@ static int check_cfg(const eagle_dims* d, const eagle_tree_cfg* c) {
   if (c->max_prefix < c->m + 1) return fail(EAGLE_ERR_SHAPE, "max_prefix %d < m+1", c->max_prefix);
   if (d) {
     const AttnPlan pa = plan_attn(MODE_EXTEND, c->m, *d, *c, c->batch);
+    const AttnPlan pl = plan_attn(MODE_LEVEL, c->topk, *d, *c, c->batch);
+    if (pa.nsplit > 128 || pl.nsplit > 128)
+      return fail(EAGLE_ERR_UNSUPPORTED, "attention split count too large");
     const long wg = (long)c->batch * d->n_kv_heads * pa.nqt;
     if (wg >= GRID_CNT) return fail(EAGLE_ERR_UNSUPPORTED, "attention grid %ld too large", wg);
+    for (int op = OP_FC; op <= OP_DOWN; ++op)
+      for (int M : {c->batch * c->topk, c->batch * c->m})
+        if (plan_gemm(op, M, *d).S > GEMM_MAXS)
+          return fail(EAGLE_ERR_UNSUPPORTED, "K too long for %d split-K ways", GEMM_MAXS);
     const long blocks = (long)cdiv(d->ffn, 64) * cdiv(c->batch * c->m, 64);
     if (blocks >= GRID_CNT || (long)c->batch * c->m > 4096)
       return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", c->batch * c->m);
@@ -298,14 +310,18 @@ int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagl
   RoundArgs a = make_args(*dims, *cfg, w, state, ws);
   if (level == 1) {
     a.rows = cfg->batch;
-    return hip_ok(launch_lmhead(a, plan_lm(cfg->batch, *dims, cfg->topk), 1, s), "lm head");
+    const LmPlan pl = plan_lm(cfg->batch, *dims, cfg->topk);
+    if ((r = hip_ok(launch_lmhead(a, pl, 1, s), "lm head"))) return r;
+    return hip_ok(launch_lmmerge(a, pl, 1, s), "lm merge");
   }
   a.mode = MODE_LEVEL;
   a.depth = level - 1;
   a.rows = cfg->batch * cfg->topk;
   a.RS = cfg->topk;
   if (!tail_only && (r = run_layer(a, *dims, *cfg, s))) return r;
-  return hip_ok(launch_lmhead(a, plan_lm(a.rows, *dims, cfg->topk), level, s), "lm head");
+  const LmPlan pl = plan_lm(a.rows, *dims, cfg->topk);
+  if ((r = hip_ok(launch_lmhead(a, pl, level, s), "lm head"))) return r;
+  return hip_ok(launch_lmmerge(a, pl, level, s), "lm merge");
 }
 
 int eagle_rerank_build_tree(const eagle_dims* dims, const eagle_tree_cfg* cfg,

@@ -17,6 +17,7 @@ constexpr int WAVE = 64;
 constexpr int BLOCK = 256;       // four waves
 constexpr int NCNT = 1 << 16;    // last-block counters in the workspace
 constexpr int GRID_CNT = NCNT - 1;
+constexpr int GEMM_MAXS = 16;    // split-K ways at most
 
 enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
 enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1 };
@@ -102,6 +103,7 @@ struct GemmPlan {
 
 struct LmPlan {
   int M, mt, zg, nblk, rec;  // rec = floats per (row, block) partial
+  int G;                     // slab lists merged per LDS pass in the merge kernel
   size_t part_floats;
 };
 
@@ -176,26 +178,48 @@ __device__ __forceinline__ int clamp_slot(int s, int k) { return s < 0 ? 0 : (s 
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
 
-// last-block election: every thread fences its own stores, one thread bumps the
-// counter; returns true in the block that arrived last (counter reset to 0)
+// Last-block election across workgroups (possibly on different XCDs, whose L2s
+// are not coherent with each other).  Every thread waits until its own global
+// stores are complete (a workgroup-scope fence does not wait for them), the
+// block synchronises, and one thread alone releases at agent scope (one L2
+// write-back per block instead of one per wave) and bumps the counter.  The
+// block that arrives last acquires at agent scope (one L2 invalidate) and
+// resets the counter.  Returns true in that block only.
 __device__ __forceinline__ bool arrive_last(int* cnt, int total) {
   __shared__ int s_last;
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int prev = atomicAdd(cnt, 1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == total - 1);
-    if (s_last) atomicExch(cnt, 0);
+    if (s_last) {
+      __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
   }
   __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
+  return s_last != 0;
+}
+
+// block-wide (value desc, id asc) argmax of 256 threads; result in every thread
+__device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* si) {
+  wave_argmax(v, id);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) { sv[wave] = v; si[wave] = id; }
+  __syncthreads();
+  v = sv[0];
+  id = si[0];
+#pragma unroll
+  for (int w = 1; w < BLOCK / WAVE; ++w)
+    if (sv[w] > v || (sv[w] == v && si[w] < id)) { v = sv[w]; id = si[w]; }
 }
 
 // launchers (return a hipError_t)
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
+hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
 hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
                          int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);

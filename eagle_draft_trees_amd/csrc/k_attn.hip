@@ -21,6 +21,7 @@ namespace eg {
 
 constexpr int AT_QT = 32;  // queries per workgroup
 constexpr int AT_KT = 32;  // keys per LDS tile
+constexpr int AT_MAXSPLIT = 128;  // merge weights and maxima reuse the K/V tiles' LDS
 
 template <typename T>
 __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
@@ -73,15 +74,25 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
     const size_t rstride = (size_t)a.Hkv * hd;
     for (int kt0 = klo; kt0 < khi; kt0 += AT_KT) {
       const int nk = min(AT_KT, khi - kt0);
-      for (int idx = tid; idx < AT_KT * hd; idx += BLOCK) {
-        const int kr = idx / hd, dd = idx % hd;
-        float kv = 0.f, vv = 0.f;
-        if (kr < nk) {
-          kv = El<T>::ld(Kb, (size_t)(kt0 + kr) * rstride + dd);
-          vv = El<T>::ld(Vb, (size_t)(kt0 + kr) * rstride + dd);
+      {
+        // 16-byte loads: PER elements of one key row per thread and chunk
+        constexpr int PER = El<T>::PER16;
+        const int cpr = hd / PER;  // chunks per key row
+        for (int idx = tid; idx < AT_KT * cpr; idx += BLOCK) {
+          const int kr = idx / cpr, d0 = (idx % cpr) * PER;
+          uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
+          if (kr < nk) {
+            kv = ld16(Kb + (size_t)(kt0 + kr) * rstride + d0);
+            vv = ld16(Vb + (size_t)(kt0 + kr) * rstride + d0);
+          }
+          const T* ke = (const T*)&kv;
+          const T* ve = (const T*)&vv;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            sK[kr][d0 + e] = El<T>::ld(ke, e);
+            sV[kr][d0 + e] = El<T>::ld(ve, e);
+          }
         }
-        sK[kr][dd] = kv;
-        sV[kr][dd] = vv;
       }
       __syncthreads();
       {
@@ -144,20 +155,36 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
       const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
       float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
       const float qa = sQ[qi][lane], qb = (lane + 64 < hd) ? sQ[qi][lane + 64] : 0.f;
-      for (int dep = 1; dep <= a.depth; ++dep) {
-        const size_t off =
-            ((((size_t)b * a.D + dep) * a.k + clamp_slot(nd.anc[dep - 1], a.k)) * a.Hkv + kvh) * hd;
-        const T* kp = (const T*)a.tk + off;
-        const T* vp = (const T*)a.tv + off;
-        const float kb2 = (lane + 64 < hd) ? El<T>::ld(kp, lane + 64) : 0.f;
-        const float s = wave_sum(qa * El<T>::ld(kp, lane) + qb * kb2);
-        const float mnew = fmaxf(m, s);
-        const float sc = (m == -INFINITY) ? 0.f : expf(m - mnew);
-        const float pr = expf(s - mnew);
-        l = l * sc + pr;
-        o0 = o0 * sc + pr * El<T>::ld(vp, lane);
-        if (lane + 64 < hd) o1 = o1 * sc + pr * El<T>::ld(vp, lane + 64);
-        m = mnew;
+      // every ancestor's K/V is loaded up front so the loads overlap
+      float ka[EAGLE_MAX_DEPTH], kb[EAGLE_MAX_DEPTH], va[EAGLE_MAX_DEPTH], vb[EAGLE_MAX_DEPTH];
+#pragma unroll
+      for (int dep = 1; dep <= EAGLE_MAX_DEPTH; ++dep) {
+        ka[dep - 1] = kb[dep - 1] = va[dep - 1] = vb[dep - 1] = 0.f;
+        if (dep <= a.depth) {
+          const size_t off =
+              ((((size_t)b * a.D + dep) * a.k + clamp_slot(nd.anc[dep - 1], a.k)) * a.Hkv + kvh) * hd;
+          const T* kp = (const T*)a.tk + off;
+          const T* vp = (const T*)a.tv + off;
+          ka[dep - 1] = El<T>::ld(kp, lane);
+          va[dep - 1] = El<T>::ld(vp, lane);
+          if (lane + 64 < hd) {
+            kb[dep - 1] = El<T>::ld(kp, lane + 64);
+            vb[dep - 1] = El<T>::ld(vp, lane + 64);
+          }
+        }
+      }
+#pragma unroll
+      for (int dep = 1; dep <= EAGLE_MAX_DEPTH; ++dep) {
+        if (dep <= a.depth) {
+          const float s = wave_sum(qa * ka[dep - 1] + qb * kb[dep - 1]);
+          const float mnew = fmaxf(m, s);
+          const float sc = (m == -INFINITY) ? 0.f : expf(m - mnew);
+          const float pr = expf(s - mnew);
+          l = l * sc + pr;
+          o0 = o0 * sc + pr * va[dep - 1];
+          o1 = o1 * sc + pr * vb[dep - 1];
+          m = mnew;
+        }
       }
       part[qi * prec + 2 + lane] = o0;
       if (lane + 64 < hd) part[qi * prec + 2 + lane + 64] = o1;
@@ -170,25 +197,40 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
 
   if (!arrive_last(a.cnt + wg, p.nsplit)) return;
 
+  // merge the slices in slice order: per-query weights first (LDS), then the
+  // weighted sum of each slice's unnormalised output
+  float* sw = &sK[0][0];  // [nq][nsplit] slice sums, then weights; nq * nsplit <= 32 * 128
+  float* smx = &sV[0][0];  // [nq][nsplit] slice maxima
+  const float* wbase = a.apart + (size_t)wg * p.nsplit * AT_QT * prec;
+  for (int idx = tid; idx < nq * p.nsplit; idx += BLOCK) {
+    const int qi = idx / p.nsplit, s = idx % p.nsplit;
+    const float* ps = wbase + ((size_t)s * AT_QT + qi) * prec;
+    smx[idx] = ps[0];
+    sw[idx] = ps[1];
+  }
+  __syncthreads();
+  if (tid < nq) {
+    float M = -INFINITY;
+    for (int s = 0; s < p.nsplit; ++s)
+      if (sw[tid * p.nsplit + s] > 0.f) M = fmaxf(M, smx[tid * p.nsplit + s]);
+    float L = 0.f;
+    for (int s = 0; s < p.nsplit; ++s) {
+      const float ls = sw[tid * p.nsplit + s];
+      const float w = ls > 0.f ? expf(smx[tid * p.nsplit + s] - M) : 0.f;
+      sw[tid * p.nsplit + s] = w;
+      L += ls * w;
+    }
+    sScale[tid] = 1.0f / L;
+  }
+  __syncthreads();
   for (int idx = tid; idx < nq * hd; idx += BLOCK) {
     const int qi = idx / hd, dd = idx % hd, gq = q0 + qi;
-    const float* base = a.apart + (size_t)wg * p.nsplit * AT_QT * prec + qi * prec;
-    float M = -INFINITY;
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float* ps = base + (size_t)s * AT_QT * prec;
-      if (ps[1] > 0.f) M = fmaxf(M, ps[0]);
-    }
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float* ps = base + (size_t)s * AT_QT * prec;
-      if (ps[1] > 0.f) {
-        const float w = expf(ps[0] - M);
-        L += ps[1] * w;
-        O += ps[2 + dd] * w;
-      }
-    }
+    float O = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < p.nsplit; ++s)
+      O += sw[qi * p.nsplit + s] * wbase[((size_t)s * AT_QT + qi) * prec + 2 + dd];
     const int row = b * p.RS + gq / g, head = kvh * g + gq % g;
-    El<T>::st((T*)a.attn, (size_t)row * HD + head * hd + dd, O / L);
+    El<T>::st((T*)a.attn, (size_t)row * HD + head * hd + dd, O * sScale[qi]);
   }
 }
 

@@ -4,15 +4,16 @@
 //   Y[M][N] = X[M][K] * W[N][K]^T,  M = frontier rows (B*k) or extend rows (B*m)
 //
 // At drafting shapes M is 1..64 while W is megabytes, so every kernel here is
-// bound by streaming W from HBM once.  A wave owns 16 output columns and one
-// K range; each k-step it issues one 16-byte load per lane of W (16 rows x 64
-// contiguous bytes per wave instruction) and one of X, and feeds them to a
-// 16x16 MFMA (bf16: v_mfma_f32_16x16x32_bf16; fp32: four 16x16x4 steps).  A
-// workgroup is four waves = 64 adjacent columns.  When the grid would be too
-// small to keep HBM busy, K is split across workgroups; each split writes fp32
-// partials and the last workgroup to arrive (counter in the workspace) sums
-// them in split order -- deterministic, no float atomics -- and runs the
-// epilogue.
+// bound by streaming W from HBM once.  A workgroup is four waves = 64 adjacent
+// output columns over one K range.  It stages the X rows of that K range in
+// LDS chunk by chunk (shared by the four waves), so the only global loads in
+// the main loop are W's: one 16-byte load per lane per k-step (16 rows x 64
+// contiguous bytes per wave instruction), eight k-steps in flight, each fed to
+// a 16x16 MFMA (bf16: v_mfma_f32_16x16x32_bf16; fp32: four 16x16x4 steps)
+// with its A operand read from LDS.  When the grid would be too small to keep
+// HBM busy, K is split across workgroups; each split writes fp32 partials and
+// the last workgroup to arrive (counter in the workspace) sums them in split
+// order -- deterministic, no float atomics -- and runs the epilogue.
 //
 // Fused steps (draft head of [P1] "EAGLE 推测解码为什么比 Medusa 快？" §4.1 and
 // [P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里"):
@@ -44,8 +45,13 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
+  constexpr int ES = (int)sizeof(T);
   constexpr int ROWS = MT * 16;
-  __shared__ float tile[NW][ROWS][65];
+  constexpr int XRB = (4096 / MT) & ~15;  // bytes of X per row in LDS per staged chunk
+  constexpr int XST = XRB + 16;   // LDS row stride: 16 rows of one m-tile hit disjoint banks
+  static_assert(NW * ROWS * 65 * 4 <= ROWS * XST, "epilogue tile aliases the X tile");
+  __shared__ __attribute__((aligned(16))) unsigned char xs[ROWS * XST];
+  __shared__ const T* rsrc[2][ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x, split = blockIdx.y, zg = blockIdx.z;
@@ -73,54 +79,58 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
     if (OP == OP_DOWN) wr[0] = (const T*)a.w_down + off;
   }
 
-  // ---- this lane's X rows (one per m-tile); FC gathers two sources
-  const T* xa[MT];
-  const T* xb[MT];
-  bool rv[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = zg * 64 + mt * 16 + (lane & 15);
-    rv[mt] = row < p.M;
-    const int r = rv[mt] ? row : 0;
-    xb[mt] = (const T*)a.embed;  // second source, read only by the FC (k >= d)
-    if (OP == OP_FC) {
-      int tok;
-      if (a.mode == MODE_LEVEL) {
-        const int b = r / a.k, j = r % a.k;
-        const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
-        tok = nd.token;
-        if (a.depth == 1) xa[mt] = (const T*)a.root_feat + (size_t)b * a.d;
-        else xa[mt] = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
-      } else {
-        const int b = r / a.m, i = r % a.m;
-        int alen = a.accept_len[b];
-        alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-        const int last = alen - 1, ii = i < last ? i : last;
-        const int* path = a.accept_path + (size_t)b * (a.D + 1);
-        int pi = path[ii];
-        pi = pi < 0 ? 0 : (pi >= a.m ? a.m - 1 : pi);
-        xa[mt] = (const T*)a.true_feat + ((size_t)b * a.m + pi) * a.d;
-        if (i < last) {
-          int pn = path[i + 1];
-          pn = pn < 0 ? 0 : (pn >= a.m ? a.m - 1 : pn);
-          tok = a.tokens[(size_t)b * a.m + pn];
+  // ---- X rows of this z-group; the FC gathers [parent feature || embed[token]]
+  if (tid < ROWS) {
+    const int row = zg * 64 + tid;
+    const T* s0 = nullptr;
+    const T* s1 = (const T*)a.embed;
+    if (row < p.M) {
+      if (OP == OP_FC) {
+        int tok;
+        if (a.mode == MODE_LEVEL) {
+          const int b = row / a.k, j = row % a.k;
+          const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
+          tok = nd.token;
+          if (a.depth == 1) s0 = (const T*)a.root_feat + (size_t)b * a.d;
+          else s0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
         } else {
-          tok = a.bonus[b];
+          const int b = row / a.m, i = row % a.m;
+          int alen = a.accept_len[b];
+          alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
+          const int last = alen - 1, ii = i < last ? i : last;
+          const int* path = a.accept_path + (size_t)b * (a.D + 1);
+          int pi = path[ii];
+          pi = pi < 0 ? 0 : (pi >= a.m ? a.m - 1 : pi);
+          s0 = (const T*)a.true_feat + ((size_t)b * a.m + pi) * a.d;
+          if (i < last) {
+            int pn = path[i + 1];
+            pn = pn < 0 ? 0 : (pn >= a.m ? a.m - 1 : pn);
+            tok = a.tokens[(size_t)b * a.m + pn];
+          } else {
+            tok = a.bonus[b];
+          }
         }
+        tok = clamp_tok(tok, a.V, a.err);
+        s1 = (const T*)a.embed + (size_t)tok * a.d;  // read with k - d
+      } else if (OP == OP_QKV) {
+        s0 = (const T*)a.x0b + (size_t)row * K;
+      } else if (OP == OP_O) {
+        s0 = (const T*)a.attn + (size_t)row * K;
+      } else if (OP == OP_GATEUP) {
+        s0 = (const T*)a.yg + (size_t)row * K;
+      } else {
+        s0 = (const T*)a.act + (size_t)row * K;
       }
-      tok = clamp_tok(tok, a.V, a.err);
-      xb[mt] = (const T*)a.embed + (size_t)tok * a.d;  // indexed with k - d
-    } else if (OP == OP_QKV) {
-      xa[mt] = (const T*)a.x0b + (size_t)r * K;
-    } else if (OP == OP_O) {
-      xa[mt] = (const T*)a.attn + (size_t)r * K;
-    } else if (OP == OP_GATEUP) {
-      xa[mt] = (const T*)a.yg + (size_t)r * K;
-    } else {
-      xa[mt] = (const T*)a.act + (size_t)r * K;
     }
+    rsrc[0][tid] = s0;
+    rsrc[1][tid] = s1;
   }
   const int kswitch = (OP == OP_FC) ? a.d : K;
+  const int k0 = split * p.Kc;
+  const int k1 = min(K, k0 + p.Kc);
+  const int kn = k1 - k0;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  __syncthreads();
 
   f32x4_t acc[NW][MT];
 #pragma unroll
@@ -128,43 +138,60 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int kq = (lane >> 4) * PER;
-  const int k0 = split * p.Kc;
-  const int k1 = min(K, k0 + p.Kc);
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  int k = k0;
-  constexpr int U = 4;
-  for (; k + U * KS <= k1; k += U * KS) {
-    uint4 wf[U][NW];
+  const int kq = (lane >> 4) * PER;          // this lane group's k offset in a k-step
+  const unsigned char* xl = xs + (lane & 15) * XST + (lane >> 4) * 16;
+  // software pipeline: the next U k-steps' weights are in flight while the
+  // current U k-steps run on the MFMA units.  X is staged in LDS one chunk of
+  // KCH elements at a time (shared by the four waves).
+  constexpr int U = (MT * NW > 4) ? 4 : 8;
+  constexpr int KCH = (XRB / ES) / (U * KS) * (U * KS);
+  static_assert(KCH > 0, "X chunk");
+  const int nit = (kn + U * KS - 1) / (U * KS);
+  uint4 wc[U][NW], wn[U][NW];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const int k = u * KS + kq;
+      wc[u][w] = (nv && k < kn) ? ld16(wr[w] + k0 + k) : zero;
+    }
+  for (int it = 0; it < nit; ++it) {
+    const int kb = it * U * KS;
+    const int kc = kb - kb % KCH;
+    if (kb == kc) {
+      __syncthreads();
+      const int nch = min(KCH, kn - kc) / PER;
+      for (int idx = tid; idx < ROWS * nch; idx += BLOCK) {
+        const int r = idx / nch, c = idx - r * nch, k = k0 + kc + c * PER;
+        const T* s0 = rsrc[0][r];
+        uint4* dst = (uint4*)(xs + r * XST + c * 16);
+        if (s0) *dst = ld16(k < kswitch ? s0 + k : rsrc[1][r] + (k - kswitch));
+        else *dst = make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) wf[u][w] = nv ? ld16(wr[w] + k + u * KS + kq) : zero;
+      for (int w = 0; w < NW; ++w) {
+        const int k = kb + U * KS + u * KS + kq;
+        wn[u][w] = (nv && k < kn) ? ld16(wr[w] + k0 + k) : zero;
+      }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kk = k + u * KS + kq;
+      const int k = kb + u * KS;
+      const bool kin = k + kq < kn;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const T* src = (kk < kswitch) ? xa[mt] + kk : xb[mt] + (kk - kswitch);
-        const uint4 xf = rv[mt] ? ld16(src) : zero;
+        const uint4 xf = kin ? *(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES) : zero;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wf[u][w], acc[w][mt], T());
+        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wc[u][w], acc[w][mt], T());
       }
     }
-  }
-  for (; k < k1; k += KS) {
-    const int kk = k + kq;
-    const bool kin = kk < k1;
-    uint4 wf[NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) wf[w] = (nv && kin) ? ld16(wr[w] + kk) : zero;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const T* src = (kk < kswitch) ? xa[mt] + kk : xb[mt] + (kk - kswitch);
-      const uint4 xf = (rv[mt] && kin) ? ld16(src) : zero;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wf[w], acc[w][mt], T());
-    }
+      for (int w = 0; w < NW; ++w) wc[u][w] = wn[u][w];
   }
 
   // ---- split-K: partials, last block reduces in split order
@@ -181,21 +208,35 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
     for (int w = 0; w < NW; ++w)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.S; ++s) {
-      const float* ps = a.gpart + ((((size_t)bid * p.S + s) * 4 + wave) * (NW * MT) * 64) * 4;
+    // splits' loads issued eight at a time, summed in split order
+    for (int s0 = 0; s0 < p.S; s0 += 8) {
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[w][mt] += *(const f32x4_t*)(ps + ((size_t)(w * MT + mt) * 64 + lane) * 4);
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x4_t v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float* ps =
+                a.gpart + ((((size_t)bid * p.S + s0 + u) * 4 + wave) * (NW * MT) * 64) * 4;
+            v[u] = s0 + u < p.S ? *(const f32x4_t*)(ps + ((size_t)(w * MT + mt) * 64 + lane) * 4)
+                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc[w][mt] += v[u];
+        }
     }
   }
+  // the epilogue tile reuses the X tile's LDS
+  __syncthreads();
+  float* tile = (float*)xs;  // [NW][ROWS][65]
+#define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
 #pragma unroll
   for (int w = 0; w < NW; ++w)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tile[w][mt * 16 + (lane >> 4) * 4 + r][cl] = acc[w][mt][r];
+      for (int r = 0; r < 4; ++r) TILE(w, mt * 16 + (lane >> 4) * 4 + r, cl) = acc[w][mt][r];
   __syncthreads();
 
   // ---- epilogues
@@ -204,7 +245,7 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
     for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
-      const float v = tile[0][mr][c] + El<T>::ld((const T*)a.fc_b, nn);
+      const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
       a.x0f[(size_t)row * a.d + nn] = v;
       El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
     }
@@ -214,7 +255,7 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
     for (int idx = tid; idx < rows_here * 32; idx += BLOCK) {
       const int mr = idx >> 5, c = idx & 31, row = zg * 64 + mr;
       const int fi = 32 * jj + c;  // frequency index within the half
-      float lo = tile[0][mr][c], hi = tile[0][mr][c + 32];
+      float lo = TILE(0, mr, c), hi = TILE(0, mr, c + 32);
       int b, slot, pos;
       if (a.mode == MODE_LEVEL) {
         b = row / a.k;
@@ -257,22 +298,29 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
   } else if (OP == OP_O) {
     for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
-      if (nn >= p.N) { tile[0][mr][c] = 0.f; continue; }
-      const float y = tile[0][mr][c] + a.x0f[(size_t)row * a.d + nn];
-      tile[0][mr][c] = y;
+      if (nn >= p.N) { TILE(0, mr, c) = 0.f; continue; }
+      const float y = TILE(0, mr, c) + a.x0f[(size_t)row * a.d + nn];
+      TILE(0, mr, c) = y;
       a.yf[(size_t)row * a.d + nn] = y;
       El<T>::st((T*)a.yg, (size_t)row * a.d + nn, y * El<T>::ld((const T*)a.post_norm, nn));
     }
     __syncthreads();
     if (tid < rows_here) {
       float s = 0.f;
-      for (int c = 0; c < 64; ++c) s += tile[0][tid][c] * tile[0][tid][c];
+      for (int c = 0; c < 64; ++c) s += TILE(0, tid, c) * TILE(0, tid, c);
       a.ssq[(size_t)blk * a.rows + zg * 64 + tid] = s;
     }
     if (arrive_last(a.cnt + GRID_CNT, p.nblk * p.zg)) {
       for (int row = tid; row < p.M; row += BLOCK) {
         float s = 0.f;
-        for (int bb = 0; bb < p.nblk; ++bb) s += a.ssq[(size_t)bb * a.rows + row];
+        for (int b0 = 0; b0 < p.nblk; b0 += 16) {
+          float v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            v[u] = b0 + u < p.nblk ? a.ssq[(size_t)(b0 + u) * a.rows + row] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) s += v[u];
+        }
         a.rstd[row] = 1.0f / sqrtf(s / (float)a.d + a.eps);
       }
     }
@@ -281,14 +329,14 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float r = a.rstd[row];
-      const float g = tile[0][mr][c] * r, u = tile[NW - 1][mr][c] * r;
+      const float g = TILE(0, mr, c) * r, u = TILE(NW - 1, mr, c) * r;
       El<T>::st((T*)a.act, (size_t)row * a.F + nn, g / (1.0f + expf(-g)) * u);
     }
   } else {  // OP_DOWN
     for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
-      const float h = tile[0][mr][c] + a.yf[(size_t)row * a.d + nn];
+      const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
       if (a.mode == MODE_LEVEL) {
         El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + nn, h);
       } else {
@@ -308,6 +356,7 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
       }
     }
   }
+#undef TILE
 }
 
 template <typename T, int OP>

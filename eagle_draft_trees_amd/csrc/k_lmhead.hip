@@ -1,4 +1,4 @@
-// Frozen LM head + softmax + top-k + EAGLE-2 expansion, in one launch.
+// Frozen LM head + softmax + top-k + EAGLE-2 expansion.
 //
 // [P1] "EAGLE 推测解码为什么比 Medusa 快？（含 EAGLE-2 动态草稿树）" §4.1: the draft
 // distribution is softmax(LM_Head(f-hat)); §10.3: a node's value is the product
@@ -7,32 +7,38 @@
 // multiplies the running score by this level's top-k probabilities and keeps
 // the best topk of topk^2.  Scores are kept as sums of log-probabilities.
 //
-// Phase 1 (every workgroup): four waves each stream 16 vocabulary rows of the
-// LM head (the same MFMA weight-streaming loop as the draft GEMMs) against the
-// M feature rows; the 64-column logit tile goes to LDS.  Per row, one wave
-// reduces its 64 columns to (max, sum exp) and the slab's top-k (logit desc,
-// id asc).  Logits never leave the chip.
-// Phase 2 (the grid's last workgroup): per row, combine the slabs' (max, sum)
-// into log-sum-exp and merge the sorted slab lists by a tournament; log p =
-// logit - lse.  Then per sequence: level 1 puts the root's k children into the
-// pool and frontier; level L >= 2 scores the k*k children (parent score +
-// log p), appends all of them to the pool in (frontier slot, rank) order and
-// keeps the best k by (score desc, pool index asc) as the next frontier.
+// k_lmhead (one launch over the vocabulary): four waves per workgroup each
+// stream 16 LM-head rows against the M feature rows (MFMA, A operand from
+// LDS, X staged in K chunks, the next weight loads issued before the current
+// MFMAs); the 64-column logit tile goes to LDS and each row's slab is reduced
+// to (max, sum exp) and its top-k (logit desc, id asc).  Logits never leave
+// the chip.
+// k_lmmerge (one workgroup per row): combines the slabs' (max, sum) into a
+// log-sum-exp, merges the sorted slab lists in LDS by block-wide argmax rounds
+// and writes (id, log p = logit - lse).  Then per sequence: level 1 puts the
+// root's k children into the pool and frontier; for level L >= 2 the last row
+// of a sequence to finish scores the k*k children (parent score + log p),
+// appends all of them to the pool in (frontier slot, rank) order and keeps the
+// best k by (score desc, pool index asc) as the next frontier.
 #include <float.h>
 
 #include "eagle_internal.h"
 
 namespace eg {
 
-constexpr int LM_MAXBLK = 4096;  // vocab <= 262144
-
 template <typename T, int MT>
 __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int level) {
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
+  constexpr int ES = (int)sizeof(T);
   constexpr int ROWS = MT * 16;
-  __shared__ float tile[ROWS][65];
-  __shared__ unsigned char heads[4][LM_MAXBLK];
+  constexpr int U = MT == 1 ? 8 : 4;  // weight k-steps in flight (more m-tiles: more MFMA per load)
+  constexpr int XRB = (4096 / MT) & ~15;
+  constexpr int XST = XRB + 16;
+  constexpr int KCH = (XRB / ES) / (U * KS) * (U * KS);  // elements per staged X chunk
+  static_assert(KCH > 0, "chunk");
+  static_assert(ROWS * 65 * 4 <= ROWS * XST, "logit tile aliases the X tile");
+  __shared__ __attribute__((aligned(16))) unsigned char xs[ROWS * XST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x, zg = blockIdx.z;
@@ -41,58 +47,70 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   const int n = blk * 64 + cl;
   const bool nv = n < a.V;
   const T* wr = (const T*)a.lm_head + (size_t)(nv ? n : 0) * K;
-
-  const T* xr[MT];
-  bool rv[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int row = zg * 64 + mt * 16 + (lane & 15);
-    rv[mt] = row < p.M;
-    const int r = rv[mt] ? row : 0;
-    xr[mt] = (level == 1) ? (const T*)a.root_feat + (size_t)r * K
-                          : (const T*)a.feat + ((size_t)(level - 1) * a.B * kk_ + r) * K;
-  }
+  const T* xbase = (level == 1) ? (const T*)a.root_feat
+                                : (const T*)a.feat + (size_t)(level - 1) * a.B * kk_ * K;
+  const int rows_here = min(ROWS, p.M - zg * 64);
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  const int kq = (lane >> 4) * PER;
+  const unsigned char* xl = xs + (lane & 15) * XST + (lane >> 4) * 16;
 
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int kq = (lane >> 4) * PER;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  constexpr int U = 4;
-  int k = 0;
-  for (; k + U * KS <= K; k += U * KS) {
-    uint4 wf[U];
+
+  const int nit = (K + U * KS - 1) / (U * KS);
+  uint4 wc[U], wn[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wf[u] = nv ? ld16(wr + k + u * KS + kq) : zero;
+  for (int u = 0; u < U; ++u) {
+    const int k = u * KS + kq;
+    wc[u] = (nv && k < K) ? ld16(wr + k) : zero;
+  }
+  for (int it = 0; it < nit; ++it) {
+    const int kb = it * U * KS;
+    const int kc = kb - kb % KCH;  // start of the staged chunk holding this iteration
+    if (kb == kc) {
+      __syncthreads();
+      const int kn = min(KCH, K - kc), nch = kn / PER;
+      for (int idx = tid; idx < ROWS * nch; idx += BLOCK) {
+        const int r = idx / nch, c = idx - r * nch;
+        uint4* dst = (uint4*)(xs + r * XST + c * 16);
+        if (r < rows_here) *dst = ld16(xbase + (size_t)(zg * 64 + r) * K + kc + c * PER);
+        else *dst = make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+    }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {  // next iteration's weights (beyond K: not loaded)
+      const int k = kb + U * KS + u * KS + kq;
+      wn[u] = (nv && k < K) ? ld16(wr + k) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kb + u * KS;
+      const bool kin = k + kq < K;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xf = rv[mt] ? ld16(xr[mt] + k + u * KS + kq) : zero;
-        acc[mt] = mma16(xf, wf[u], acc[mt], T());
+        const uint4 xf = kin ? *(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES) : zero;
+        acc[mt] = mma16(xf, wc[u], acc[mt], T());
       }
-  }
-  for (; k < K; k += KS) {
-    const int kk = k + kq;
-    const bool kin = kk < K;
-    const uint4 wf = (nv && kin) ? ld16(wr + kk) : zero;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint4 xf = (rv[mt] && kin) ? ld16(xr[mt] + kk) : zero;
-      acc[mt] = mma16(xf, wf, acc[mt], T());
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) wc[u] = wn[u];
   }
+
+  __syncthreads();
+  float* tile = (float*)xs;  // [ROWS][65] logits
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) tile[mt * 16 + (lane >> 4) * 4 + r][cl] = nv ? acc[mt][r] : -INFINITY;
+    for (int r = 0; r < 4; ++r)
+      tile[(mt * 16 + (lane >> 4) * 4 + r) * 65 + cl] = nv ? acc[mt][r] : -INFINITY;
   __syncthreads();
 
-  // ---- per-row slab partials: (max, sum exp, top-k logits, top-k ids)
-  const int rows_here = min(ROWS, p.M - zg * 64);
+  // per-row slab partials: (max, sum exp, top-k logits, top-k ids)
   for (int mr = wave; mr < rows_here; mr += 4) {
     const int row = zg * 64 + mr;
-    float x = tile[mr][lane];
+    float x = tile[mr * 65 + lane];
     const int id0 = blk * 64 + lane;
     const float mx = wave_max(x);
     const float s = wave_sum(x == -INFINITY ? 0.f : expf(x - mx));
@@ -109,125 +127,198 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
       if (id == id0) x = -INFINITY;
     }
   }
+}
 
-  if (!arrive_last(a.cnt + GRID_CNT, p.nblk * p.zg)) return;
+constexpr int LM_CAND = 8192;  // (logit, id) candidates held in LDS by the merge
 
-  // ---- phase 2a: per row, log-sum-exp and the global top-k
-  for (int row = wave; row < p.M; row += 4) {
-    const float* base = a.lmpart + (size_t)row * p.nblk * p.rec;
-    float M = -INFINITY, S = 0.f;
-    for (int bb = lane; bb < p.nblk; bb += 64) {
-      const float mb = base[(size_t)bb * p.rec], sb = base[(size_t)bb * p.rec + 1];
-      if (mb == -INFINITY) continue;
-      const float nm = fmaxf(M, mb);
-      S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + sb * expf(mb - nm);
+__global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int level) {
+  __shared__ float cv[LM_CAND + EAGLE_MAX_TOPK];
+  __shared__ int ci[LM_CAND + EAGLE_MAX_TOPK];
+  __shared__ float rv[EAGLE_MAX_TOPK];
+  __shared__ int ri[EAGLE_MAX_TOPK];
+  __shared__ float redv[BLOCK / WAVE];
+  __shared__ int redi[BLOCK / WAVE];
+  __shared__ float redm[BLOCK / WAVE], reds[BLOCK / WAVE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x, kk_ = a.k;
+  const float* base = a.lmpart + (size_t)row * p.nblk * p.rec;
+
+  // log-sum-exp over the slabs, combined in a fixed order
+  float M = -INFINITY, S = 0.f;
+  for (int bb = tid; bb < p.nblk; bb += BLOCK) {
+    const float mb = base[(size_t)bb * p.rec], sb = base[(size_t)bb * p.rec + 1];
+    if (mb == -INFINITY) continue;
+    const float nm = fmaxf(M, mb);
+    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + sb * expf(mb - nm);
+    M = nm;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float oM = __shfl_xor(M, o), oS = __shfl_xor(S, o);
+    const float nm = fmaxf(M, oM);
+    if (nm != -INFINITY) {
+      S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + (oM == -INFINITY ? 0.f : oS * expf(oM - nm));
       M = nm;
     }
+  }
+  if (lane == 0) { redm[wave] = M; reds[wave] = S; }
+  __syncthreads();
+  if (tid == 0) {
+    float m0 = redm[0], s0 = reds[0];
+    for (int w = 1; w < BLOCK / WAVE; ++w) {
+      const float nm = fmaxf(m0, redm[w]);
+      s0 = (m0 == -INFINITY ? 0.f : s0 * expf(m0 - nm)) +
+           (redm[w] == -INFINITY ? 0.f : reds[w] * expf(redm[w] - nm));
+      m0 = nm;
+    }
+    redm[0] = m0 + logf(s0);
+  }
+  __syncthreads();
+  const float lse = redm[0];
+
+  // top-k: merge the sorted slab lists, p.G slabs per LDS pass, plus the running list
+  int nr = 0;
+  for (int g0 = 0; g0 < p.nblk; g0 += p.G) {
+    const int gn = min(p.G, p.nblk - g0);
+    const int nc = gn * kk_;
+    // candidate loads are issued eight at a time per thread so their latencies overlap
+    for (int i0 = tid; i0 < nc; i0 += 8 * BLOCK) {
+      float vv[8];
+      int ii[8];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float oM = __shfl_xor(M, o), oS = __shfl_xor(S, o);
-      const float nm = fmaxf(M, oM);
-      if (nm != -INFINITY) {
-        S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + (oM == -INFINITY ? 0.f : oS * expf(oM - nm));
-        M = nm;
+      for (int u = 0; u < 8; ++u) {
+        const int idx = i0 + u * BLOCK;
+        vv[u] = -INFINITY;
+        ii[u] = -1;
+        if (idx < nc) {
+          const float* rec = base + (size_t)(g0 + idx / kk_) * p.rec;
+          const int j = idx % kk_;
+          vv[u] = rec[2 + j];
+          ii[u] = __float_as_int(rec[2 + kk_ + j]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = i0 + u * BLOCK;
+        if (idx < nc) {
+          cv[idx] = ii[u] < 0 ? -INFINITY : vv[u];
+          ci[idx] = ii[u] < 0 ? INT_MAX : ii[u];
+        }
       }
     }
-    M = __shfl(M, 0);
-    S = __shfl(S, 0);
-    const float lse = M + logf(S);
-
-    for (int bb = lane; bb < p.nblk; bb += 64) heads[wave][bb] = 0;
-    float* res = a.lmres + (size_t)row * 2 * kk_;
+    if (tid < nr) { cv[nc + tid] = rv[tid]; ci[nc + tid] = ri[tid]; }
+    __syncthreads();
+    const int ntot = nc + nr;
     for (int r = 0; r < kk_; ++r) {
       float v = -INFINITY;
       int id = INT_MAX;
-      for (int bb = lane; bb < p.nblk; bb += 64) {
-        const int h = heads[wave][bb];
-        if (h >= kk_) continue;
-        const float cv = base[(size_t)bb * p.rec + 2 + h];
-        const int ci = __float_as_int(base[(size_t)bb * p.rec + 2 + kk_ + h]);
-        if (ci < 0) continue;
-        if (cv > v || (cv == v && ci < id)) { v = cv; id = ci; }
-      }
-      wave_argmax(v, id);
-      if (id != INT_MAX && ((id >> 6) & 63) == lane) heads[wave][id >> 6]++;
-      if (lane == 0) {
-        res[r] = __int_as_float(id == INT_MAX ? 0 : id);
-        res[kk_ + r] = v - lse;
-      }
+      for (int c = tid; c < ntot; c += BLOCK)
+        if (cv[c] > v || (cv[c] == v && ci[c] < id)) { v = cv[c]; id = ci[c]; }
+      block_argmax(v, id, redv, redi);
+      for (int c = tid; c < ntot; c += BLOCK)
+        if (ci[c] == id) cv[c] = -INFINITY, ci[c] = INT_MAX;
+      if (tid == 0) { rv[r] = v; ri[r] = id; }
+      __syncthreads();
     }
+    nr = kk_;
+  }
+  float* res = a.lmres + (size_t)row * 2 * kk_;
+  if (tid < kk_) {
+    res[tid] = __int_as_float(ri[tid] == INT_MAX ? 0 : ri[tid]);
+    res[kk_ + tid] = rv[tid] - lse;
+  }
+
+  // ---- expansion and select
+  const int pn = a.pool_n;
+  if (level == 1) {
+    const int b = row;
+    eagle_pool_entry* pool = a.pool + (size_t)b * pn;
+    eagle_frontier_node* fnew = a.frontier + ((size_t)1 * a.B + b) * kk_;
+    if (tid < kk_) {
+      const int id = ri[tid] == INT_MAX ? 0 : ri[tid];
+      const float lp = rv[tid] - lse;
+      pool[tid] = eagle_pool_entry{lp, lp, id, -1, 1, -1};
+      eagle_frontier_node nd;
+      nd.token = id;
+      nd.score = lp;
+      nd.pool_idx = tid;
+      nd.pslot = -1;
+      for (int i = 0; i < EAGLE_MAX_DEPTH; ++i) nd.anc[i] = 0;
+      nd.anc[0] = tid;
+      fnew[tid] = nd;
+    }
+    return;
+  }
+  const int b = row / kk_;
+  if (!arrive_last(a.cnt + b, kk_)) return;
+  // stage the parent frontier and every row's (id, log p) in LDS with one
+  // parallel pass, so the select below touches no global memory in its rounds
+  const eagle_frontier_node* fprev = a.frontier + ((size_t)(level - 1) * a.B + b) * kk_;
+  float* sres = cv;                          // [k][2k] (reuses the candidate buffer)
+  int* sanc = ci;                            // [k][EAGLE_MAX_DEPTH]
+  float* psc = cv + EAGLE_MAX_TOPK * 2 * EAGLE_MAX_TOPK;
+  int* ppi = ci + EAGLE_MAX_TOPK * EAGLE_MAX_DEPTH;
+  for (int idx = tid; idx < kk_ * 2 * kk_; idx += BLOCK)
+    sres[idx] = a.lmres[(size_t)b * kk_ * 2 * kk_ + idx];
+  for (int idx = tid; idx < kk_ * EAGLE_MAX_DEPTH; idx += BLOCK)
+    sanc[idx] = fprev[idx / EAGLE_MAX_DEPTH].anc[idx % EAGLE_MAX_DEPTH];
+  if (tid < kk_) {
+    psc[tid] = fprev[tid].score;
+    ppi[tid] = fprev[tid].pool_idx;
   }
   __syncthreads();
-
-  // ---- phase 2b: expansion and select per sequence
-  const int pn = a.pool_n;
-  for (int b = wave; b < a.B; b += 4) {
-    eagle_pool_entry* pool = a.pool + (size_t)b * pn;
-    eagle_frontier_node* fnew = a.frontier + ((size_t)level * a.B + b) * kk_;
-    if (level == 1) {
-      const float* res = a.lmres + (size_t)b * 2 * kk_;
-      if (lane < kk_) {
-        const int id = __float_as_int(res[lane]);
-        const float lp = res[kk_ + lane];
-        pool[lane] = eagle_pool_entry{lp, lp, id, -1, 1, -1};
-        eagle_frontier_node nd;
-        nd.token = id;
-        nd.score = lp;
-        nd.pool_idx = lane;
-        nd.pslot = -1;
-        for (int i = 0; i < EAGLE_MAX_DEPTH; ++i) nd.anc[i] = 0;
-        nd.anc[0] = lane;
-        fnew[lane] = nd;
-      }
-      continue;
+  if (wave != 0) return;
+  eagle_pool_entry* pool = a.pool + (size_t)b * pn;
+  eagle_frontier_node* fnew = a.frontier + ((size_t)level * a.B + b) * kk_;
+  const int pbase = kk_ + (level - 2) * kk_ * kk_;
+  const int nc = kk_ * kk_;
+  float sc[4];
+  int tk[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int c = lane + 64 * t;
+    sc[t] = -INFINITY;
+    tk[t] = 0;
+    if (c < nc) {
+      const int j = c / kk_, r = c % kk_;
+      const float* rr = sres + j * 2 * kk_;
+      const int id = __float_as_int(rr[r]);
+      const float lp = rr[kk_ + r];
+      const float s = psc[j] + lp;
+      sc[t] = s;
+      tk[t] = id;
+      pool[pbase + c] = eagle_pool_entry{s, lp, id, ppi[j], level, j};
     }
-    const eagle_frontier_node* fprev = a.frontier + ((size_t)(level - 1) * a.B + b) * kk_;
-    const int base = kk_ + (level - 2) * kk_ * kk_;
-    const int nc = kk_ * kk_;
-    float sc[4];
+  }
+  for (int jn = 0; jn < kk_; ++jn) {
+    float v = -INFINITY;
+    int id = INT_MAX;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int c = lane + 64 * t;
-      sc[t] = -INFINITY;
-      if (c < nc) {
-        const int j = c / kk_, r = c % kk_;
-        const float* res = a.lmres + ((size_t)b * kk_ + j) * 2 * kk_;
-        const int id = __float_as_int(res[r]);
-        const float lp = res[kk_ + r];
-        const float s = fprev[j].score + lp;
-        sc[t] = s;
-        pool[base + c] = eagle_pool_entry{s, lp, id, fprev[j].pool_idx, level, j};
-      }
+      if (c < nc && (sc[t] > v || (sc[t] == v && c < id))) { v = sc[t]; id = c; }
     }
-    for (int jn = 0; jn < kk_; ++jn) {
-      float v = -INFINITY;
-      int id = INT_MAX;
+    wave_argmax(v, id);
+    // the owner of candidate `id` holds its token
+    int own = 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = lane + 64 * t;
-        if (c < nc && (sc[t] > v || (sc[t] == v && c < id))) { v = sc[t]; id = c; }
-      }
-      wave_argmax(v, id);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        if (lane + 64 * t == id) sc[t] = -INFINITY;
-      if (id == INT_MAX) continue;  // fewer than k candidates (cannot happen with k*k >= k)
-      const int j = id / kk_;
-      const eagle_frontier_node& par = fprev[j];
-      // the winner's pool record was written by this wave above
-      const float* res = a.lmres + ((size_t)b * kk_ + j) * 2 * kk_;
-      const int tok = __float_as_int(res[id % kk_]);
-      if (lane < EAGLE_MAX_DEPTH) {
-        int av = (lane < level - 1) ? par.anc[lane] : 0;
-        if (lane == level - 1) av = jn;
-        fnew[jn].anc[lane] = av;
-      }
-      if (lane == 0) {
-        fnew[jn].token = tok;
-        fnew[jn].score = v;
-        fnew[jn].pool_idx = base + id;
-        fnew[jn].pslot = j;
-      }
+    for (int t = 0; t < 4; ++t)
+      if (lane + 64 * t == id) { own = tk[t]; sc[t] = -INFINITY; }
+    const int owner = id < INT_MAX ? (id & 63) : 0;
+    own = __shfl(own, owner);
+    if (id == INT_MAX) continue;  // fewer than k candidates (cannot happen: k*k >= k)
+    const int j = id / kk_;
+    if (lane < EAGLE_MAX_DEPTH) {
+      int av = (lane < level - 1) ? sanc[j * EAGLE_MAX_DEPTH + lane] : 0;
+      if (lane == level - 1) av = jn;
+      fnew[jn].anc[lane] = av;
+    }
+    if (lane == 0) {
+      fnew[jn].token = own;
+      fnew[jn].score = v;
+      fnew[jn].pool_idx = pbase + id;
+      fnew[jn].pslot = j;
     }
   }
 }
@@ -247,6 +338,11 @@ static hipError_t launch_lm_t(const RoundArgs& a, const LmPlan& p, int level, hi
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
   return a.dtype == EAGLE_BF16 ? launch_lm_t<bf16_t>(a, p, level, s)
                                : launch_lm_t<float>(a, p, level, s);
+}
+
+hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
+  hipLaunchKernelGGL(k_lmmerge, dim3(p.M), dim3(BLOCK), 0, s, a, p, level);
+  return hipGetLastError();
 }
 
 }  // namespace eg

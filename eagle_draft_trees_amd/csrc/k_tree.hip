@@ -42,10 +42,19 @@ __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, 
     flat_of[e] = -1;
   }
   __syncthreads();
+  // rank = number of better keys; reads are batched 16 at a time so that the
+  // LDS latency is paid once per batch, and counting stops once the entry
+  // cannot make the cut
   for (int e = tid; e < n; e += BLOCK) {
     const unsigned long long ke = key[e];
     int c = 0;
-    for (int j = 0; j < n && c < ns; ++j) c += key[j] > ke;
+    for (int j0 = 0; j0 < n && c < ns; j0 += 16) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int j = j0 + u;
+        c += (j < n && key[j] > ke) ? 1 : 0;
+      }
+    }
     if (c < ns) sel[c] = e;
   }
   __syncthreads();
@@ -70,10 +79,14 @@ __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, 
     }
     __syncthreads();
     int cnt = 0, rank = 0;
-    for (int j = 0; j < ns; ++j) {
-      if (sdep[j] != dd) continue;
-      ++cnt;
-      if (tid < ns && dep == dd && sk2[j] < sk2[tid]) ++rank;
+    const bool mine = tid < ns && dep == dd;
+    const unsigned k2 = mine ? sk2[tid] : 0u;
+#pragma unroll 16
+    for (int j = 0; j < EAGLE_MAX_TREE; ++j) {
+      if (j < ns && sdep[j] == dd) {
+        ++cnt;
+        rank += (mine && sk2[j] < k2) ? 1 : 0;
+      }
     }
     if (tid < ns && dep == dd) flat_of[e] = (short)(base + rank);
     base += cnt;
@@ -133,9 +146,16 @@ __global__ void __launch_bounds__(1024) k_verify(int m, int D, int V, const floa
     const float* row = tl + ((size_t)b * m + node) * V;
     float v = -INFINITY;
     int id = INT_MAX;
-    for (int i = tid; i < V; i += 1024) {
-      const float x = row[i];
-      if (x > v) { v = x; id = i; }  // per thread indices increase: first max wins
+    for (int i0 = tid; i0 < V; i0 += 1024 * 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * 1024;
+        x[u] = i < V ? row[i] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)  // this thread's indices increase: the first max wins
+        if (x[u] > v) { v = x[u]; id = i0 + u * 1024; }
     }
     wave_argmax(v, id);
     if (lane == 0) { wv[wave] = v; wi[wave] = id; }

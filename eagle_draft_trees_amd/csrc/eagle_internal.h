@@ -76,6 +76,74 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return __shfl(v, 0);
 }
+// ------------------------------------------------------------------ DPP reductions
+// Cross-lane steps on the DPP path (a VALU operand modifier, no LDS round trip):
+// xor 1 and xor 2 within quads, then half-row and row mirrors; after those every
+// lane of a 16-lane row holds the row's result, and the four rows are combined
+// from lanes 15, 31, 47, 63.  The step order is fixed, so float results are
+// deterministic.
+
+__device__ __forceinline__ unsigned dpp_u32(unsigned x, int ctrl_sel) {
+  switch (ctrl_sel) {
+    case 0: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad xor 1
+    case 1: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad xor 2
+    case 2: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);  // half-row mirror
+    default: return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false); // row mirror
+  }
+}
+
+// Order-preserving 64-bit key of (value desc, id asc): larger key = better.
+__device__ __forceinline__ unsigned long long argkey(float v, int id) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ float argkey_value(unsigned long long k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ int argkey_id(unsigned long long k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+// maximum 64-bit key over the wave; every lane gets it
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const unsigned hi = dpp_u32((unsigned)(k >> 32), s), lo = dpp_u32((unsigned)k, s);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    k = o > k ? o : k;
+  }
+  unsigned long long r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(k >> 32), row * 16 + 15);
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)k, row * 16 + 15);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    r = o > r ? o : r;
+  }
+  return r;
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v += __uint_as_float(dpp_u32(__float_as_uint(v), s));
+  float r = 0.f;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) r += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), row * 16 + 15));
+  return r;
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v = fmaxf(v, __uint_as_float(dpp_u32(__float_as_uint(v), s)));
+  float r = -INFINITY;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) r = fmaxf(r, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), row * 16 + 15)));
+  return r;
+}
+
 // (value desc, id asc) winner across the wave; every lane gets the result
 __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 #pragma unroll

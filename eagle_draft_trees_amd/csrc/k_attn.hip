@@ -23,7 +23,7 @@ constexpr int AT_QT = 32;  // queries per workgroup
 constexpr int AT_KT = 32;  // keys per LDS tile
 constexpr int AT_MAXSPLIT = 128;  // merge weights and maxima reuse the K/V tiles' LDS
 
-template <typename T>
+template <typename T, int HDIM>
 __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
   __shared__ float sQ[AT_QT][129];
   __shared__ float sK[AT_KT][129];
@@ -35,7 +35,8 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wg = blockIdx.x, split = blockIdx.y;
   const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
-  const int hd = a.hd, g = p.g;
+  constexpr int hd = HDIM;
+  const int g = p.g;
   const int q0 = qt * AT_QT;
   const int nq = min(AT_QT, p.nq - q0);
   const int P = clamp_prefix(a.prefix_len[b], a);
@@ -58,7 +59,7 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
 
   const size_t prec = (size_t)hd + 2;
   float* part = a.apart + ((size_t)wg * p.nsplit + split) * AT_QT * prec;
-  const int qg_pv = BLOCK / hd;    // query groups in the P.V step
+  constexpr int qg_pv = BLOCK / hd;  // query groups in the P.V step
   const int dpv = tid % hd, qpv = tid / hd;
   float acc[AT_QT / 2];
 #pragma unroll
@@ -98,8 +99,15 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
       {
         const int kr = tid % AT_KT;
         for (int qi = tid / AT_KT; qi < nq; qi += BLOCK / AT_KT) {
-          float s = 0.f;
-          for (int dd = 0; dd < hd; ++dd) s += sQ[qi][dd] * sK[kr][dd];
+          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+          for (int dd = 0; dd < hd; dd += 4) {
+            s0 += sQ[qi][dd] * sK[kr][dd];
+            s1 += sQ[qi][dd + 1] * sK[kr][dd + 1];
+            s2 += sQ[qi][dd + 2] * sK[kr][dd + 2];
+            s3 += sQ[qi][dd + 3] * sK[kr][dd + 3];
+          }
+          const float s = (s0 + s1) + (s2 + s3);
           sS[qi][kr] = (kr < nk && kt0 + kr < sLim[qi]) ? s : -INFINITY;
         }
       }
@@ -132,9 +140,13 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
       for (int i = 0; i < AT_QT / 2; ++i) {
         const int qi = qpv + i * qg_pv;
         if (qi < nq) {
-          float s = acc[i] * sScale[qi];
-          for (int kr = 0; kr < nk; ++kr) s += sS[qi][kr] * sV[kr][dpv];
-          acc[i] = s;
+          float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+          for (int kr = 0; kr < AT_KT; kr += 2) {  // keys >= nk have weight 0 and value 0
+            s0 += sS[qi][kr] * sV[kr][dpv];
+            s1 += sS[qi][kr + 1] * sV[kr + 1][dpv];
+          }
+          acc[i] = acc[i] * sScale[qi] + (s0 + s1);
         }
       }
       __syncthreads();
@@ -236,8 +248,13 @@ __global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
 
 hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
   const dim3 grid(a.B * a.Hkv * p.nqt, p.nsplit), block(BLOCK);
-  if (a.dtype == EAGLE_BF16) hipLaunchKernelGGL((k_attn<bf16_t>), grid, block, 0, s, a, p);
-  else hipLaunchKernelGGL((k_attn<float>), grid, block, 0, s, a, p);
+  if (a.dtype == EAGLE_BF16) {
+    if (a.hd == 128) hipLaunchKernelGGL((k_attn<bf16_t, 128>), grid, block, 0, s, a, p);
+    else hipLaunchKernelGGL((k_attn<bf16_t, 64>), grid, block, 0, s, a, p);
+  } else {
+    if (a.hd == 128) hipLaunchKernelGGL((k_attn<float, 128>), grid, block, 0, s, a, p);
+    else hipLaunchKernelGGL((k_attn<float, 64>), grid, block, 0, s, a, p);
+  }
   return hipGetLastError();
 }
 

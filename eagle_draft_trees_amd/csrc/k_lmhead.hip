@@ -107,38 +107,55 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
       tile[(mt * 16 + (lane >> 4) * 4 + r) * 65 + cl] = nv ? acc[mt][r] : -INFINITY;
   __syncthreads();
 
-  // per-row slab partials: (max, sum exp, top-k logits, top-k ids)
+  // per-row slab partials: (max, sum exp, top-k logits, top-k ids).  Each lane
+  // ranks its column against the row's 64 columns in LDS (value desc, id asc:
+  // ranks are unique); the lanes ranked below k write the slab's sorted list.
   for (int mr = wave; mr < rows_here; mr += 4) {
     const int row = zg * 64 + mr;
-    float x = tile[mr * 65 + lane];
-    const int id0 = blk * 64 + lane;
-    const float mx = wave_max(x);
-    const float s = wave_sum(x == -INFINITY ? 0.f : expf(x - mx));
+    const float* trow = tile + mr * 65;
+    const float x = trow[lane];
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const float y = trow[j];
+      rank += (y > x || (y == x && j < lane)) ? 1 : 0;
+    }
+    const float mx = wave_max_dpp(x);
+    const float s = wave_sum_dpp(x == -INFINITY ? 0.f : expf(x - mx));
     float* rec = a.lmpart + ((size_t)row * p.nblk + blk) * p.rec;
     if (lane == 0) { rec[0] = mx; rec[1] = s; }
-    for (int r = 0; r < kk_; ++r) {
-      float v = x;
-      int id = (x == -INFINITY) ? INT_MAX : id0;
-      wave_argmax(v, id);
-      if (lane == 0) {
-        rec[2 + r] = v;
-        rec[2 + kk_ + r] = __int_as_float(id == INT_MAX ? -1 : id);
-      }
-      if (id == id0) x = -INFINITY;
+    if (rank < kk_) {
+      rec[2 + rank] = x;
+      rec[2 + kk_ + rank] = __int_as_float(x == -INFINITY ? -1 : blk * 64 + lane);
     }
   }
 }
 
 constexpr int LM_CAND = 8192;  // (logit, id) candidates held in LDS by the merge
 
+// maximum over the block of a 64-bit key; `slot` alternates between calls so a
+// single barrier per call suffices
+__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long k,
+                                                            unsigned long long* red, int slot) {
+  k = wave_max_u64(k);
+  if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = k;
+  __syncthreads();
+  unsigned long long r = red[slot * 4];
+#pragma unroll
+  for (int w = 1; w < BLOCK / WAVE; ++w) r = red[slot * 4 + w] > r ? red[slot * 4 + w] : r;
+  return r;
+}
+
 __global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int level) {
-  __shared__ float cv[LM_CAND + EAGLE_MAX_TOPK];
-  __shared__ int ci[LM_CAND + EAGLE_MAX_TOPK];
-  __shared__ float rv[EAGLE_MAX_TOPK];
-  __shared__ int ri[EAGLE_MAX_TOPK];
-  __shared__ float redv[BLOCK / WAVE];
-  __shared__ int redi[BLOCK / WAVE];
+  __shared__ unsigned long long ck[LM_CAND + EAGLE_MAX_TOPK];  // slab lists as keys
+  __shared__ unsigned short head[LM_CAND + 1];                 // next entry of each list
+  __shared__ unsigned long long rk[EAGLE_MAX_TOPK];            // running top-k
+  __shared__ unsigned long long red[8];
   __shared__ float redm[BLOCK / WAVE], reds[BLOCK / WAVE];
+  __shared__ float sres[EAGLE_MAX_TOPK * 2 * EAGLE_MAX_TOPK];
+  __shared__ int sanc[EAGLE_MAX_TOPK * EAGLE_MAX_DEPTH];
+  __shared__ float psc[EAGLE_MAX_TOPK];
+  __shared__ int ppi[EAGLE_MAX_TOPK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x, kk_ = a.k;
@@ -177,12 +194,12 @@ __global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int le
   __syncthreads();
   const float lse = redm[0];
 
-  // top-k: merge the sorted slab lists, p.G slabs per LDS pass, plus the running list
-  int nr = 0;
+  // top-k: the slab lists are sorted, so each round only compares list heads;
+  // p.G lists per LDS pass, the running list joins each pass as one more list
+  int nr = 0, slot = 0;
   for (int g0 = 0; g0 < p.nblk; g0 += p.G) {
     const int gn = min(p.G, p.nblk - g0);
     const int nc = gn * kk_;
-    // candidate loads are issued eight at a time per thread so their latencies overlap
     for (int i0 = tid; i0 < nc; i0 += 8 * BLOCK) {
       float vv[8];
       int ii[8];
@@ -201,28 +218,39 @@ __global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int le
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int idx = i0 + u * BLOCK;
-        if (idx < nc) {
-          cv[idx] = ii[u] < 0 ? -INFINITY : vv[u];
-          ci[idx] = ii[u] < 0 ? INT_MAX : ii[u];
-        }
+        if (idx < nc) ck[idx] = ii[u] < 0 ? 0ull : argkey(vv[u], ii[u]);
       }
     }
-    if (tid < nr) { cv[nc + tid] = rv[tid]; ci[nc + tid] = ri[tid]; }
+    const int nl = gn + (nr ? 1 : 0);  // lists in this pass
+    if (tid < nr) ck[nc + tid] = rk[tid];
+    for (int l = tid; l < nl; l += BLOCK) head[l] = 0;
     __syncthreads();
-    const int ntot = nc + nr;
     for (int r = 0; r < kk_; ++r) {
-      float v = -INFINITY;
-      int id = INT_MAX;
-      for (int c = tid; c < ntot; c += BLOCK)
-        if (cv[c] > v || (cv[c] == v && ci[c] < id)) { v = cv[c]; id = ci[c]; }
-      block_argmax(v, id, redv, redi);
-      for (int c = tid; c < ntot; c += BLOCK)
-        if (ci[c] == id) cv[c] = -INFINITY, ci[c] = INT_MAX;
-      if (tid == 0) { rv[r] = v; ri[r] = id; }
-      __syncthreads();
+      unsigned long long best = 0;
+      int bl = -1;
+      for (int l = tid; l < nl; l += BLOCK) {
+        const int h = head[l];
+        if (h < kk_) {
+          const unsigned long long kv = ck[l * kk_ + h];
+          if (kv > best) { best = kv; bl = l; }
+        }
+      }
+      const unsigned long long win = block_max_u64(best, red, slot);
+      slot ^= 1;
+      if (bl >= 0 && best == win && win != 0ull) head[bl]++;  // keys are unique: one owner
+      if (tid == 0) rk[r] = win;
     }
     nr = kk_;
+    __syncthreads();
   }
+  __shared__ float rv[EAGLE_MAX_TOPK];
+  __shared__ int ri[EAGLE_MAX_TOPK];
+  if (tid < kk_) {
+    const unsigned long long w = rk[tid];
+    rv[tid] = w ? argkey_value(w) : -INFINITY;
+    ri[tid] = w ? argkey_id(w) : INT_MAX;
+  }
+  __syncthreads();
   float* res = a.lmres + (size_t)row * 2 * kk_;
   if (tid < kk_) {
     res[tid] = __int_as_float(ri[tid] == INT_MAX ? 0 : ri[tid]);
@@ -255,10 +283,6 @@ __global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int le
   // stage the parent frontier and every row's (id, log p) in LDS with one
   // parallel pass, so the select below touches no global memory in its rounds
   const eagle_frontier_node* fprev = a.frontier + ((size_t)(level - 1) * a.B + b) * kk_;
-  float* sres = cv;                          // [k][2k] (reuses the candidate buffer)
-  int* sanc = ci;                            // [k][EAGLE_MAX_DEPTH]
-  float* psc = cv + EAGLE_MAX_TOPK * 2 * EAGLE_MAX_TOPK;
-  int* ppi = ci + EAGLE_MAX_TOPK * EAGLE_MAX_DEPTH;
   for (int idx = tid; idx < kk_ * 2 * kk_; idx += BLOCK)
     sres[idx] = a.lmres[(size_t)b * kk_ * 2 * kk_ + idx];
   for (int idx = tid; idx < kk_ * EAGLE_MAX_DEPTH; idx += BLOCK)
@@ -292,22 +316,24 @@ __global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int le
     }
   }
   for (int jn = 0; jn < kk_; ++jn) {
-    float v = -INFINITY;
-    int id = INT_MAX;
+    unsigned long long best = 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int c = lane + 64 * t;
-      if (c < nc && (sc[t] > v || (sc[t] == v && c < id))) { v = sc[t]; id = c; }
+      if (c < nc) {
+        const unsigned long long kv = sc[t] == -INFINITY ? 0ull : argkey(sc[t], c);
+        best = kv > best ? kv : best;
+      }
     }
-    wave_argmax(v, id);
-    // the owner of candidate `id` holds its token
+    const unsigned long long win = wave_max_u64(best);  // (score desc, pool index asc)
+    if (win == 0ull) continue;  // fewer than k candidates (cannot happen: k*k >= k)
+    const float v = argkey_value(win);
+    const int id = argkey_id(win);
     int own = 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       if (lane + 64 * t == id) { own = tk[t]; sc[t] = -INFINITY; }
-    const int owner = id < INT_MAX ? (id & 63) : 0;
-    own = __shfl(own, owner);
-    if (id == INT_MAX) continue;  // fewer than k candidates (cannot happen: k*k >= k)
+    own = __shfl(own, id & 63);
     const int j = id / kk_;
     if (lane < EAGLE_MAX_DEPTH) {
       int av = (lane < level - 1) ? sanc[j * EAGLE_MAX_DEPTH + lane] : 0;

@@ -4,6 +4,8 @@
 namespace eg {
 
 constexpr int MAX_POOL = EAGLE_MAX_TOPK + (EAGLE_MAX_DEPTH - 1) * EAGLE_MAX_TOPK * EAGLE_MAX_TOPK;
+constexpr int MAX_POOL_P2 = 4096;  // next power of two
+static_assert(MAX_POOL <= MAX_POOL_P2, "pool");
 
 // Rerank and build, one workgroup per sequence.
 // [P1] "EAGLE 推测解码为什么比 Medusa 快？（含 EAGLE-2 动态草稿树）" §10.3: after the
@@ -15,13 +17,13 @@ constexpr int MAX_POOL = EAGLE_MAX_TOPK + (EAGLE_MAX_DEPTH - 1) * EAGLE_MAX_TOPK
 // x1, x2, x3, x1a, x1b, ... ; 0/1 ancestor mask; per-level positions.
 //
 // Selection: one 64-bit key per pool entry = (score desc, depth asc, index asc)
-// as an unsigned integer; an entry is kept when fewer than m-1 keys beat it,
-// and that count is its rank.  Flattening: depth by depth, each kept node's
-// rank among its depth by (parent's flat index, pool index).
+// as an unsigned integer; a bitonic sort in LDS orders them and the first m-1
+// are kept.  Flattening: depth by depth, each kept node's rank among its depth
+// by (parent's flat index, pool index).
 __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, int32_t* parents,
                                                   int32_t* depth, int32_t* positions, uint8_t* mask,
                                                   float* logscore) {
-  __shared__ unsigned long long key[MAX_POOL];
+  __shared__ unsigned long long key[MAX_POOL_P2];
   __shared__ short flat_of[MAX_POOL];
   __shared__ int sel[EAGLE_MAX_TREE];
   __shared__ unsigned sk2[EAGLE_MAX_TREE];
@@ -32,31 +34,36 @@ __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, 
   const int tid = threadIdx.x, b = blockIdx.x;
   const int n = a.pool_n, m = a.m, ns = m - 1;
   const eagle_pool_entry* pool = a.pool + (size_t)b * n;
+  int np = 1;
+  while (np < n) np <<= 1;  // <= MAX_POOL_P2
 
-  for (int e = tid; e < n; e += BLOCK) {
-    const eagle_pool_entry pe = pool[e];
-    uint32_t u = __float_as_uint(pe.score);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving for floats
-    key[e] = ((unsigned long long)u << 32) | ((unsigned long long)(255 - pe.depth) << 24) |
-             (unsigned long long)(0xFFFFFF - e);
-    flat_of[e] = -1;
-  }
-  __syncthreads();
-  // rank = number of better keys; reads are batched 16 at a time so that the
-  // LDS latency is paid once per batch, and counting stops once the entry
-  // cannot make the cut
-  for (int e = tid; e < n; e += BLOCK) {
-    const unsigned long long ke = key[e];
-    int c = 0;
-    for (int j0 = 0; j0 < n && c < ns; j0 += 16) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = j0 + u;
-        c += (j < n && key[j] > ke) ? 1 : 0;
-      }
+  for (int e = tid; e < np; e += BLOCK) {
+    unsigned long long kv = 0ull;  // padding sorts last
+    if (e < n) {
+      const eagle_pool_entry pe = pool[e];
+      uint32_t u = __float_as_uint(pe.score);
+      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // order-preserving for floats
+      kv = ((unsigned long long)u << 32) | ((unsigned long long)(255 - (pe.depth & 255)) << 24) |
+           (unsigned long long)(0xFFFFFF - e);
+      flat_of[e] = -1;
     }
-    if (c < ns) sel[c] = e;
+    key[e] = kv;
   }
+  if (tid < EAGLE_MAX_TREE) sk2[tid] = 0xFFFFFFFFu;
+  __syncthreads();
+  // bitonic sort, best key first
+  for (int size = 2; size <= np; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (np >> 1); i += BLOCK) {
+        const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const unsigned long long x = key[lo], y = key[hi];
+        if ((x < y) == desc) { key[lo] = y; key[hi] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < ns) sel[tid] = 0xFFFFFF - (int)(key[tid] & 0xFFFFFFull);
   __syncthreads();
 
   // pool records are device data: keep depth in 1..D and parents inside the pool
@@ -66,32 +73,36 @@ __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, 
     dep = min(max(pool[e].depth, 1), a.D);
     par = pool[e].parent;
     if (par < 0 || par >= n) par = -1;
+    sdep[tid] = dep;
   }
   if (tid < EAGLE_MAX_TREE) {
     fpar[tid] = 0;
     fdep[tid] = 0;
+    if (tid >= ns) sdep[tid] = 0;
   }
+  __syncthreads();
+  // flatten depth by depth: rank among the same depth by (parent's flat index, pool index)
   int base = 1;
   for (int dd = 1; dd <= a.D; ++dd) {
-    if (tid < ns) {
-      sdep[tid] = dep;
-      if (dep == dd) sk2[tid] = ((unsigned)(par < 0 ? 0 : (int)flat_of[par] & 0xFFFF) << 16) | (unsigned)e;
+    const bool mine = tid < ns && dep == dd;
+    unsigned k2 = 0xFFFFFFFFu;
+    if (mine) {
+      k2 = ((unsigned)(par < 0 ? 0 : (int)flat_of[par] & 0xFFFF) << 16) | (unsigned)e;
+      sk2[tid] = k2;
     }
     __syncthreads();
     int cnt = 0, rank = 0;
-    const bool mine = tid < ns && dep == dd;
-    const unsigned k2 = mine ? sk2[tid] : 0u;
-#pragma unroll 16
+#pragma unroll
     for (int j = 0; j < EAGLE_MAX_TREE; ++j) {
-      if (j < ns && sdep[j] == dd) {
-        ++cnt;
-        rank += (mine && sk2[j] < k2) ? 1 : 0;
-      }
+      cnt += sdep[j] == dd ? 1 : 0;
+      rank += sk2[j] < k2 ? 1 : 0;
     }
-    if (tid < ns && dep == dd) flat_of[e] = (short)(base + rank);
+    if (mine) flat_of[e] = (short)(base + rank);
     base += cnt;
     __syncthreads();
+    if (mine) sk2[tid] = 0xFFFFFFFFu;
   }
+  __syncthreads();
 
   int P = clamp_prefix(a.prefix_len[b], a);
   int32_t* tk = tokens + (size_t)b * m;

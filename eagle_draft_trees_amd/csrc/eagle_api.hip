@@ -57,6 +57,25 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   return p;
 }
 
+// Level GEMMs (at most 16 rows): about one workgroup per compute unit, each
+// with up to 16 waves that split K; column tiles per workgroup grow with N.
+SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
+  SkPlan p{};
+  const GemmPlan g = plan_gemm(op, M, d);
+  p.M = M;
+  p.N = g.N;
+  p.K = g.K;
+  p.ntile = cdiv(p.N, 16);
+  p.CT = std::max(1, std::min(SK_MAXW, cdiv(p.ntile, 256)));
+  const int nks = cdiv(p.K, d.dtype == EAGLE_BF16 ? 32 : 16);
+  p.KSW = std::max(1, std::min(SK_MAXW / p.CT, nks / 8));
+  p.nwg = cdiv(p.ntile, p.CT);
+  p.nps = 0;
+  return p;
+}
+
+static inline bool use_skinny(int mode, int rows) { return mode == MODE_LEVEL && rows <= 16; }
+
 LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
   LmPlan p{};
   p.M = M;
@@ -118,7 +137,7 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   L.yf = take(R * d.d * 4);
   L.yg = take(R * d.d * es);
   L.rstd = take(R * 4);
-  L.ssq = take((size_t)cdiv(d.d, 64) * R * 4);
+  L.ssq = take((size_t)cdiv(d.d, 16) * R * 4);
   L.act = take(R * d.ffn * es);
   size_t gp = 0;
   for (int op = OP_FC; op <= OP_DOWN; ++op)
@@ -255,8 +274,14 @@ static int run_layer(RoundArgs a, const eagle_dims& d, const eagle_tree_cfg& c, 
       int r = hip_ok(launch_attn(a, pa, s), "attention launch");
       if (r) return r;
     }
-    const GemmPlan p = plan_gemm(op, a.rows, d);
-    int r = hip_ok(launch_gemm(op, a, p, s), names[op]);
+    int r;
+    if (use_skinny(a.mode, a.rows)) {
+      SkPlan p = plan_skinny(op, a.rows, d);
+      if (op == OP_GATEUP) p.nps = plan_skinny(OP_O, a.rows, d).nwg;
+      r = hip_ok(launch_skinny(op, a, p, s), names[op]);
+    } else {
+      r = hip_ok(launch_gemm(op, a, plan_gemm(op, a.rows, d), s), names[op]);
+    }
     if (r) return r;
   }
   return EAGLE_OK;

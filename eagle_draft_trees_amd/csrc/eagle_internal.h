@@ -169,6 +169,14 @@ struct GemmPlan {
   size_t part_floats;  // split-K partial floats (0 when S == 1)
 };
 
+// Level GEMM with at most 16 rows: CT column tiles of 16 per workgroup, K split
+// over KSW waves per tile (CT * KSW <= SK_MAXW waves), nwg workgroups.
+constexpr int SK_MAXW = 16;
+struct SkPlan {
+  int M, N, K, ntile, CT, KSW, nwg;
+  int nps;  // gate/up: RMSNorm partial sums per row written by the O launch
+};
+
 struct LmPlan {
   int M, mt, zg, nblk, rec;  // rec = floats per (row, block) partial
   int G;                     // slab lists merged per LDS pass in the merge kernel
@@ -181,6 +189,7 @@ struct AttnPlan {
 };
 
 GemmPlan plan_gemm(int op, int M, const eagle_dims& d);
+SkPlan plan_skinny(int op, int M, const eagle_dims& d);
 LmPlan plan_lm(int M, const eagle_dims& d, int topk);
 AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& c, int nseq);
 WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c);
@@ -225,6 +234,13 @@ struct RoundArgs {
 
 // ------------------------------------------------------------------ device helpers
 
+// v if keep, else all-zero bits (a bitwise mask, never a select between
+// memory locations).
+__device__ __forceinline__ uint4 mask4(uint4 v, bool keep) {
+  const unsigned m = keep ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 __device__ __forceinline__ int clamp_tok(int t, int V, int* err) {
   if (t < 0 || t >= V) {
     atomicOr(err, ERR_TOKEN);
@@ -245,6 +261,13 @@ __device__ __forceinline__ int clamp_prefix(int P, const RoundArgs& a) {
 __device__ __forceinline__ int clamp_slot(int s, int k) { return s < 0 ? 0 : (s >= k ? k - 1 : s); }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
+// 16-byte load from a pointer known to be global memory (for pointers that
+// were themselves read from LDS, whose address space the compiler cannot infer)
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16g(const void* p) {
+  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Last-block election across workgroups (possibly on different XCDs, whose L2s
 // are not coherent with each other).  Every thread waits until its own global
@@ -286,6 +309,7 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 
 // launchers (return a hipError_t)
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
+hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
 hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
 hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s);

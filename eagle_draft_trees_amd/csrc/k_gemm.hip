@@ -129,7 +129,6 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
   const int k0 = split * p.Kc;
   const int k1 = min(K, k0 + p.Kc);
   const int kn = k1 - k0;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   f32x4_t acc[NW][MT];
@@ -144,54 +143,112 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
   // current U k-steps run on the MFMA units.  X is staged in LDS one chunk of
   // KCH elements at a time (shared by the four waves).
   constexpr int U = (MT * NW > 4) ? 4 : 8;
-  constexpr int KCH = (XRB / ES) / (U * KS) * (U * KS);
+  constexpr int KCH = (XRB / ES) / (2 * U * KS) * (2 * U * KS);
   static_assert(KCH > 0, "X chunk");
   const int nit = (kn + U * KS - 1) / (U * KS);
-  uint4 wc[U][NW], wn[U][NW];
+  // X staging: a chunk is at most CPR 16-byte pieces per row, SB per thread,
+  // loaded SBB at a time (all of a batch before any is stored, so that their
+  // latencies overlap; smaller batches where registers are scarce).  Every
+  // slot loads and stores unconditionally: when the split needs fewer pieces
+  // than there are slots, the extra slots repeat real pieces (same address,
+  // same value, same LDS location), and rows past M read row 0 and store
+  // zeros, so no load is left in flight on any path.
+  constexpr int CPR = KCH / PER;
+  constexpr int SB = ROWS * CPR / BLOCK;
+  static_assert(SB * BLOCK == ROWS * CPR, "staging covers a chunk exactly");
+  constexpr int SBB = (MT * NW >= 3 && SB > 8) ? SB / 2 : SB;
+  static_assert(SB % SBB == 0, "staging batches");
+  uint4 xv[SBB];
+  int xo[SBB];
+  auto stage_load = [&](int kc, int b0) __attribute__((always_inline)) {
+    const int nch = max(min(KCH, kn - kc), PER) / PER, tot = ROWS * nch;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+    for (int u = 0; u < SBB; ++u) {
+      const int idx = (tid + (b0 + u) * BLOCK) % tot;
+      const int r = idx / nch, c = idx - r * nch;
+      const int k = min(k0 + kc + c * PER, K - PER);
+      const T* s0 = rsrc[0][r];
+      const bool ok = s0 != nullptr && kc + c * PER < kn;
+      const int rr = s0 != nullptr ? r : 0;  // row 0 of the group always exists
+      const T* base = k < kswitch ? rsrc[0][rr] : rsrc[1][rr];
+      xv[u] = mask4(ld16g(base + (k < kswitch ? k : k - kswitch)), ok);
+      xo[u] = r * XST + c * 16;
+    }
+  };
+  auto stage_store = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int k = u * KS + kq;
-      wc[u][w] = (nv && k < kn) ? ld16(wr[w] + k0 + k) : zero;
-    }
-  for (int it = 0; it < nit; ++it) {
-    const int kb = it * U * KS;
-    const int kc = kb - kb % KCH;
-    if (kb == kc) {
-      __syncthreads();
-      const int nch = min(KCH, kn - kc) / PER;
-      for (int idx = tid; idx < ROWS * nch; idx += BLOCK) {
-        const int r = idx / nch, c = idx - r * nch, k = k0 + kc + c * PER;
-        const T* s0 = rsrc[0][r];
-        uint4* dst = (uint4*)(xs + r * XST + c * 16);
-        if (s0) *dst = ld16(k < kswitch ? s0 + k : rsrc[1][r] + (k - kswitch));
-        else *dst = make_uint4(0, 0, 0, 0);
-      }
-      __syncthreads();
-    }
+    for (int u = 0; u < SBB; ++u) *(uint4*)(xs + xo[u]) = xv[u];
+  };
+  // Weight loads are unconditional from a clamped in-row address (k beyond
+  // this split reads valid memory whose product is masked to zero at use), so
+  // that the compiler can keep a precise count of loads in flight.  Two
+  // register buffers alternate (ping-pong): the loads of iteration it+1 are in
+  // flight while iteration it runs, and no register copy at the loop edge
+  // forces them to complete early.
+  const int klast = K - PER;
+  auto wload = [&](uint4 (&buf)[U][NW], int it) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int k = kb + U * KS + u * KS + kq;
-        wn[u][w] = (nv && k < kn) ? ld16(wr[w] + k0 + k) : zero;
-      }
+      for (int w = 0; w < NW; ++w)
+        buf[u][w] = ld16(wr[w] + min(k0 + it * U * KS + u * KS + kq, klast));
+  };
+  auto compute = [&](const uint4 (&buf)[U][NW], int it, int kc) __attribute__((always_inline)) {
+    const int kb = it * U * KS;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = kb + u * KS;
       const bool kin = k + kq < kn;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xf = kin ? *(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES) : zero;
+        const uint4 xf = mask4(*(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES), kin);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wc[u][w], acc[w][mt], T());
+        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, buf[u][w], acc[w][mt], T());
       }
     }
+  };
+  uint4 wa[U][NW], wb[U][NW];
+  // first chunk's X loads go out before the first weight loads; both are in
+  // flight together
+  stage_load(0, 0);
+  wload(wa, 0);
+  stage_store();
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+  for (int b0 = SBB; b0 < SB; b0 += SBB) {
+    stage_load(0, b0);
+    stage_store();
+  }
+  __syncthreads();
+  // Chunks hold an even number of iterations (KCH is a multiple of 2*U*KS),
+  // so each chunk starts on buffer wa.  The loads of the iteration after the
+  // last may be issued too (clamped, in bounds, unused).
+  int it = 0;
+  for (int kc = 0; kc < kn; kc += KCH) {
+    if (kc > 0) {  // all of this split's X for the chunk; drains the pipeline once per chunk
+      __syncthreads();
 #pragma unroll
-      for (int w = 0; w < NW; ++w) wc[u][w] = wn[u][w];
+      for (int b0 = 0; b0 < SB; b0 += SBB) {
+        stage_load(kc, b0);
+        stage_store();
+      }
+      __syncthreads();
+    }
+    const int itend = min(nit, (kc + KCH) / (U * KS));
+    // The scheduling barriers keep each batch of loads ahead of the MFMAs on
+    // the other buffer (the compiler would otherwise sink them and wait early);
+    // the loop body is one straight block so that its wait counts stay exact.
+    for (; it + 1 < itend; it += 2) {
+      wload(wb, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wa, it, kc);
+      wload(wa, it + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wb, it + 1, kc);
+    }
+    if (it < itend) {  // odd count: last chunk only
+      compute(wa, it, kc);
+      ++it;
+    }
   }
 
   // ---- split-K: partials, last block reduces in split order

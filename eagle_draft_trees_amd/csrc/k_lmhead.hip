@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   constexpr int U = MT == 1 ? 8 : 4;  // weight k-steps in flight (more m-tiles: more MFMA per load)
   constexpr int XRB = (4096 / MT) & ~15;
   constexpr int XST = XRB + 16;
-  constexpr int KCH = (XRB / ES) / (U * KS) * (U * KS);  // elements per staged X chunk
+  constexpr int KCH = (XRB / ES) / (2 * U * KS) * (2 * U * KS);  // elements per staged X chunk
   static_assert(KCH > 0, "chunk");
   static_assert(ROWS * 65 * 4 <= ROWS * XST, "logit tile aliases the X tile");
   __shared__ __attribute__((aligned(16))) unsigned char xs[ROWS * XST];
@@ -50,7 +50,6 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   const T* xbase = (level == 1) ? (const T*)a.root_feat
                                 : (const T*)a.feat + (size_t)(level - 1) * a.B * kk_ * K;
   const int rows_here = min(ROWS, p.M - zg * 64);
-  const uint4 zero = make_uint4(0, 0, 0, 0);
   const int kq = (lane >> 4) * PER;
   const unsigned char* xl = xs + (lane & 15) * XST + (lane >> 4) * 16;
 
@@ -59,43 +58,78 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nit = (K + U * KS - 1) / (U * KS);
-  uint4 wc[U], wn[U];
+  // X staging: a chunk is CPR 16-byte pieces per row, SB per thread, all
+  // loaded before any is stored so that their latencies overlap.  Loads are
+  // unconditional (a piece beyond K or the rows reads a valid piece of row 0
+  // and is masked to zero) so that no load is left in flight on any path.
+  constexpr int CPR = KCH / PER;
+  constexpr int SB = ROWS * CPR / BLOCK;
+  static_assert(SB * BLOCK == ROWS * CPR, "staging covers a chunk exactly");
+  uint4 xv[SB];
+  auto stage_load = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int k = u * KS + kq;
-    wc[u] = (nv && k < K) ? ld16(wr + k) : zero;
-  }
-  for (int it = 0; it < nit; ++it) {
+    for (int u = 0; u < SB; ++u) {
+      const int idx = tid + u * BLOCK;
+      const int r = idx / CPR, c = idx % CPR, k = kc + c * PER;
+      const bool ok = k < K && r < rows_here;  // else: row 0's piece (valid), stored as zeros
+      xv[u] = mask4(ld16(xbase + (size_t)(zg * 64 + (r < rows_here ? r : 0)) * K + min(k, K - PER)), ok);
+    }
+  };
+  auto stage_store = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int idx = tid + u * BLOCK;
+      *(uint4*)(xs + (idx / CPR) * XST + (idx % CPR) * 16) = xv[u];
+    }
+  };
+  // Weight loads are unconditional from a clamped in-row address (a product
+  // beyond K is masked to zero at use), and two register buffers alternate, so
+  // the loads of iteration it+1 stay in flight while iteration it runs (see the
+  // layer GEMMs for the same structure).
+  const int klast = K - PER;
+  auto wload = [&](uint4 (&buf)[U], int it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) buf[u] = ld16(wr + min(it * U * KS + u * KS + kq, klast));
+  };
+  auto compute = [&](const uint4 (&buf)[U], int it, int kc) __attribute__((always_inline)) {
     const int kb = it * U * KS;
-    const int kc = kb - kb % KCH;  // start of the staged chunk holding this iteration
-    if (kb == kc) {
-      __syncthreads();
-      const int kn = min(KCH, K - kc), nch = kn / PER;
-      for (int idx = tid; idx < ROWS * nch; idx += BLOCK) {
-        const int r = idx / nch, c = idx - r * nch;
-        uint4* dst = (uint4*)(xs + r * XST + c * 16);
-        if (r < rows_here) *dst = ld16(xbase + (size_t)(zg * 64 + r) * K + kc + c * PER);
-        else *dst = make_uint4(0, 0, 0, 0);
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {  // next iteration's weights (beyond K: not loaded)
-      const int k = kb + U * KS + u * KS + kq;
-      wn[u] = (nv && k < K) ? ld16(wr + k) : zero;
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = kb + u * KS;
       const bool kin = k + kq < K;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xf = kin ? *(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES) : zero;
-        acc[mt] = mma16(xf, wc[u], acc[mt], T());
+        const uint4 xf = mask4(*(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES), kin);
+        acc[mt] = mma16(xf, buf[u], acc[mt], T());
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) wc[u] = wn[u];
+  };
+  uint4 wa[U], wb[U];
+  stage_load(0);  // the first chunk's X and the first weights are in flight together
+  wload(wa, 0);
+  stage_store();
+  __syncthreads();
+  int it = 0;
+  for (int kc = 0; kc < K; kc += KCH) {
+    if (kc > 0) {  // next X chunk: drains the pipeline once per chunk
+      __syncthreads();
+      stage_load(kc);
+      stage_store();
+      __syncthreads();
+    }
+    const int itend = min(nit, (kc + KCH) / (U * KS));
+    for (; it + 1 < itend; it += 2) {
+      wload(wb, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wa, it, kc);
+      wload(wa, it + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wb, it + 1, kc);
+    }
+    if (it < itend) {  // odd count: last chunk only
+      compute(wa, it, kc);
+      ++it;
+    }
   }
 
   __syncthreads();

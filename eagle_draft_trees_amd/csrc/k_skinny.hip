@@ -1,0 +1,317 @@
+// Weight-streaming GEMMs of the draft layer for the drafting levels, where the
+// frontier has at most 16 rows:
+//
+//   Y[M][N] = X[M][K] * W[N][K]^T,  M <= 16
+//
+// At this shape every byte of W is used once, so the kernel is bound by
+// streaming W from HBM; what limits a simple design is latency, not
+// arithmetic: a few serialized memory round trips per workgroup (staging,
+// cross-workgroup split-K hand-off) cost more than the streaming itself.  So:
+//
+//  * one workgroup holds CT column tiles of 16 columns and splits K over KSW
+//    waves per tile (CT * KSW <= 16 waves); the K partial sums meet in LDS
+//    and one wave per tile finishes them in slice order (deterministic), so
+//    there is no cross-workgroup hand-off at all;
+//  * each lane loads its 16 bytes of W (16 columns x 64 bytes per wave
+//    instruction) and its 16 bytes of X (the same k range of its row, an L2
+//    hit) straight into registers, BU k-steps per batch, two batches in
+//    flight (ping-pong buffers); loads are unconditional from clamped
+//    in-bounds addresses, and products past the slice are masked to zero;
+//  * the layer's elementwise work is fused into the epilogue (bias, RoPE and
+//    the in-tree KV write, residuals, the SwiGLU), and the RMSNorm statistic
+//    is finished where it is consumed: the O epilogue writes per-workgroup
+//    row sums of squares, and every gate/up workgroup reduces them itself.
+//
+// Draft layer of [P1] "EAGLE 推测解码为什么比 Medusa 快？" §4.1 and [P3]
+// zdszero.github.io spec_medusa_eagle, "在 SGLang 里"; tree positions of the
+// RoPE step per [P1] §12 item 5 (positions shared per level).
+#include "eagle_internal.h"
+
+namespace eg {
+
+// column of lane column c (0..15) of tile t; a q/k/v tile holds 8 rotation
+// pairs (i, i + hd/2) of one head so that the RoPE epilogue is lane-local
+__device__ __forceinline__ int sk_col(int op, int t, int c, int hd) {
+  if (op == OP_QKV) {
+    const int per = hd / 16, head = t / per, j = t - head * per;
+    return head * hd + (c < 8 ? 8 * j + c : hd / 2 + 8 * j + (c - 8));
+  }
+  return t * 16 + c;
+}
+
+template <typename T, int OP>
+__global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p) {
+  constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;  // weight streams per wave (gate and up)
+  constexpr int KS = El<T>::KSTEP;
+  constexpr int PER = El<T>::PER16;
+  constexpr int BU = (NW == 2) ? 3 : 4;  // k-steps per load batch
+  __shared__ f32x4_t red[SK_MAXW][NW][WAVE];
+  __shared__ float s_ssq[SK_MAXW][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ct = wave % p.CT, ks = wave / p.CT;
+  const int t = blockIdx.x * p.CT + ct;
+  const int c = lane & 15, g = lane >> 4;
+  const bool tv = t < p.ntile;
+  const int n = sk_col(OP, tv ? t : 0, c, a.hd);
+  const bool nv = tv && n < p.N;
+  const int K = p.K;
+
+  // ---- this lane's weight rows (columns past N read row 0, discarded)
+  const T* wr[NW];
+  {
+    const int nn = nv ? n : 0;
+    if (OP == OP_QKV) {
+      const int hq = a.H * a.hd, hk = a.Hkv * a.hd;
+      if (nn < hq) wr[0] = (const T*)a.wq + (size_t)nn * K;
+      else if (nn < hq + hk) wr[0] = (const T*)a.wk + (size_t)(nn - hq) * K;
+      else wr[0] = (const T*)a.wv + (size_t)(nn - hq - hk) * K;
+    } else {
+      const size_t off = (size_t)nn * K;
+      if (OP == OP_FC) wr[0] = (const T*)a.fc_w + off;
+      if (OP == OP_O) wr[0] = (const T*)a.wo + off;
+      if (OP == OP_GATEUP) { wr[0] = (const T*)a.w_gate + off; wr[NW - 1] = (const T*)a.w_up + off; }
+      if (OP == OP_DOWN) wr[0] = (const T*)a.w_down + off;
+    }
+  }
+
+  // ---- this lane's X row: row c (rows past M repeat row 0; discarded).  The
+  // FC gathers [parent feature || embed[token]] without a concatenated copy.
+  const int xr = c < p.M ? c : 0;
+  const T* x0;
+  const T* x1;
+  int kswitch = K;
+  if (OP == OP_FC) {
+    const int b = xr / a.k, j = xr - b * a.k;
+    const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
+    const int tok = clamp_tok(nd.token, a.V, a.err);
+    if (a.depth == 1) x0 = (const T*)a.root_feat + (size_t)b * a.d;
+    else x0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
+    x1 = (const T*)a.embed + (size_t)tok * a.d;
+    kswitch = a.d;
+  } else {
+    const T* xb = (OP == OP_QKV) ? (const T*)a.x0b
+                : (OP == OP_O) ? (const T*)a.attn
+                : (OP == OP_GATEUP) ? (const T*)a.yg : (const T*)a.act;
+    x0 = xb + (size_t)xr * K;
+    x1 = x0;
+  }
+
+  // ---- gate/up: prefetch this thread's share of the O epilogue's RMSNorm
+  // partials (row tid%16, partials tid/16 + j*QJ); they are summed after the
+  // main loop, so their latency hides behind the weight stream
+  constexpr int SQ = 8;
+  float sqv[SQ];
+  const int qrow = tid & 15, qj = tid >> 4, QJ = (int)(blockDim.x >> 4);
+  if (OP == OP_GATEUP) {
+#pragma unroll
+    for (int u = 0; u < SQ; ++u)
+      sqv[u] = a.ssq[(size_t)min(qj + u * QJ, p.nps - 1) * a.rows + min(qrow, p.M - 1)];
+  }
+
+  // ---- this wave's K slice: k-steps [s0k, s1k), elements [.., kend)
+  const int nks = (K + KS - 1) / KS;
+  const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
+  const int kend = min(K, s1k * KS);
+  const int nb = (s1k - s0k + BU - 1) / BU;
+  const int klast = K - PER;
+
+  f32x4_t acc[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](uint4 (&wb)[BU][NW], uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int kc = min((s0k + b * BU + u) * KS + g * PER, klast);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + kc);
+      xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
+    }
+  };
+  auto comp = [&](const uint4 (&wb)[BU][NW], const uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int k = (s0k + b * BU + u) * KS + g * PER;
+      const uint4 xf = mask4(xb[u], k < kend);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc[w] = mma16(xf, wb[u][w], acc[w], T());
+    }
+  };
+
+  // Two batches in flight: the scheduling barriers keep each batch of loads
+  // ahead of the MFMAs on the other buffer; the loop body is one straight
+  // block, so the compiler's wait counts stay exact, and the last one to
+  // three batches are peeled so that no load is issued past the slice.
+  uint4 wa[BU][NW], xa[BU], wbf[BU][NW], xbf[BU];
+  load(wa, xa, 0);
+  int b = 0;
+  for (; b + 3 < nb; b += 2) {
+    load(wbf, xbf, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, xa, b);
+    load(wa, xa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbf, xbf, b + 1);
+  }
+  const int rem = nb - b;
+  if (rem == 1) {
+    comp(wa, xa, b);
+  } else if (rem == 2) {
+    load(wbf, xbf, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, xa, b);
+    comp(wbf, xbf, b + 1);
+  } else if (rem == 3) {
+    load(wbf, xbf, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, xa, b);
+    load(wa, xa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbf, xbf, b + 1);
+    comp(wa, xa, b + 2);
+  }
+
+  // ---- K slices meet in LDS; wave (ct, slice 0) sums them in slice order
+#pragma unroll
+  for (int w = 0; w < NW; ++w) red[wave][w][lane] = acc[w];
+  if (OP == OP_GATEUP) {  // RMSNorm sums: this thread's partials, then the wave's 4 per row
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < SQ; ++u)
+      if (qj + u * QJ < p.nps) s += sqv[u];
+    for (int q = qj + SQ * QJ; q < p.nps; q += QJ) s += a.ssq[(size_t)q * a.rows + min(qrow, p.M - 1)];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (lane < 16) s_ssq[wave][lane] = s;
+  }
+  __syncthreads();
+  const bool fin = ks == 0;
+  f32x4_t v[NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) v[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if (fin)
+    for (int s = 0; s < p.KSW; ++s)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v[w] += red[s * p.CT + ct][w][lane];
+
+  // ---- epilogues; lane holds rows 4g..4g+3 of column n
+  if (OP == OP_FC) {
+    if (fin && nv) {
+      const float bias = El<T>::ld((const T*)a.fc_b, n);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row >= p.M) continue;
+        const float x = v[0][r] + bias;
+        a.x0f[(size_t)row * a.d + n] = x;
+        El<T>::st((T*)a.x0b, (size_t)row * a.d + n, x);
+      }
+    }
+  } else if (OP == OP_QKV) {
+    if (fin) {
+      const int per = a.hd / 16, head = t / per, j = t - head * per, half = a.hd / 2;
+      const bool low = c < 8;
+      const int fi = 8 * j + (low ? c : c - 8);  // frequency index within the half
+      const bool rot = head < a.H + a.Hkv;
+      const double inv = pow((double)a.theta, -2.0 * (double)fi / (double)a.hd);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float own = v[0][r];
+        const float other = __shfl_xor(own, 8);
+        const int row = 4 * g + r;
+        if (!tv || row >= p.M) continue;
+        float lo = low ? own : other, hi = low ? other : own;
+        const int bb = row / a.k, slot = row - bb * a.k;
+        if (rot) {
+          const int pos = clamp_prefix(a.prefix_len[bb], a) - 1 + a.depth;
+          double sd, cd;
+          sincos((double)pos * inv, &sd, &cd);
+          const float cs = (float)cd, sn = (float)sd;
+          const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;
+          lo = nlo;
+          hi = nhi;
+        }
+        const float val = low ? lo : hi;
+        const int idx = low ? fi : fi + half;
+        if (head < a.H) {
+          a.q[(size_t)row * (a.H * a.hd) + head * a.hd + idx] = val;
+        } else {
+          const bool isk = head < a.H + a.Hkv;
+          const int kvh = isk ? head - a.H : head - a.H - a.Hkv;
+          T* base = (T*)(isk ? a.tk : a.tv);
+          El<T>::st(base, ((((size_t)bb * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd + idx, val);
+        }
+      }
+    }
+  } else if (OP == OP_O) {
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
+    if (fin) {
+      const float gain = nv ? El<T>::ld((const T*)a.post_norm, n) : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (!nv || row >= p.M) continue;
+        const float y = v[0][r] + a.x0f[(size_t)row * a.d + n];
+        a.yf[(size_t)row * a.d + n] = y;
+        El<T>::st((T*)a.yg, (size_t)row * a.d + n, y * gain);
+        sq[r] = y * y;
+      }
+      // sum over the tile's 16 columns (the 16 lanes of one DPP row)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) sq[r] += __uint_as_float(dpp_u32(__float_as_uint(sq[r]), st));
+        if (c == 0) s_ssq[ct][4 * g + r] = sq[r];
+      }
+    }
+    __syncthreads();
+    if (tid < p.M) {
+      float s = 0.f;
+      for (int q = 0; q < p.CT; ++q) s += s_ssq[q][tid];
+      a.ssq[(size_t)blockIdx.x * a.rows + tid] = s;
+    }
+  } else if (OP == OP_GATEUP) {
+    if (fin && nv) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row >= p.M) continue;
+        float ss = 0.f;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) ss += s_ssq[w][row];
+        const float rs = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+        const float gg = v[0][r] * rs, uu = v[NW - 1][r] * rs;
+        El<T>::st((T*)a.act, (size_t)row * a.F + n, gg / (1.0f + expf(-gg)) * uu);
+      }
+    }
+  } else {  // OP_DOWN: predicted feature of the level (no final norm)
+    if (fin && nv) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (row >= p.M) continue;
+        const float h = v[0][r] + a.yf[(size_t)row * a.d + n];
+        El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + n, h);
+      }
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_sk_t(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s) {
+  const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
+  switch (op) {
+    case OP_FC: hipLaunchKernelGGL((k_skinny<T, OP_FC>), grid, block, 0, s, a, p); break;
+    case OP_QKV: hipLaunchKernelGGL((k_skinny<T, OP_QKV>), grid, block, 0, s, a, p); break;
+    case OP_O: hipLaunchKernelGGL((k_skinny<T, OP_O>), grid, block, 0, s, a, p); break;
+    case OP_GATEUP: hipLaunchKernelGGL((k_skinny<T, OP_GATEUP>), grid, block, 0, s, a, p); break;
+    default: hipLaunchKernelGGL((k_skinny<T, OP_DOWN>), grid, block, 0, s, a, p); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s) {
+  return a.dtype == EAGLE_BF16 ? launch_sk_t<bf16_t>(op, a, p, s) : launch_sk_t<float>(op, a, p, s);
+}
+
+}  // namespace eg

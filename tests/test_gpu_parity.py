@@ -359,7 +359,7 @@ def _run_rounds(name, rounds, gate):
                             W(inp["root_feat"][b]), int(inp["root_token"][b])) for b in seqs}
     tf = W(inp["true_feat"])
     alive = set(seqs)
-    stats = {"match": 0, "compared": 0, "near": 0, "feat": []}
+    stats = {"match": 0, "compared": 0, "near": 0, "feat": [], "path_differs": 0, "diffs": []}
     rng = np.random.default_rng(99)
     for rd in range(rounds):
         trees = {}
@@ -385,6 +385,7 @@ def _run_rounds(name, rounds, gate):
         g_tok, g_par = r.tokens.cpu().numpy(), r.parents.cpu().numpy()
         g_mask, g_pos = r.mask.cpu().numpy(), r.positions.cpu().numpy()
         g_al, g_bo = r.accept_len.cpu().numpy(), r.bonus.cpu().numpy()
+        g_path = r.accept_path.cpu().numpy()
         g_root = to_host(r.root_feat)
         g_plen = r.prefix_len.cpu().numpy()
         for b in sorted(alive):
@@ -405,8 +406,17 @@ def _run_rounds(name, rounds, gate):
                 ("accept_len", g_al[b] == alen), ("bonus", g_bo[b] == bonus),
                 ("prefix_len", g_plen[b] == P0 + alen)) if not ok]
             same = not diff
+            # the next root feature is comparable only when the extend consumed the
+            # same accepted nodes (indices and tokens) and bonus as the oracle's
+            path_same = (g_al[b] == alen and g_bo[b] == bonus
+                         and list(g_path[b][:alen]) == list(path[:alen])
+                         and all(g_tok[b][i] == tr.tokens[i] for i in path[:alen]))
             fe = rel_l2(g_root[b], states[b].root_feat)
-            stats["feat"].append(fe)
+            if path_same:
+                stats["feat"].append(fe)
+            else:
+                stats["path_differs"] += 1
+            stats["diffs"].append(diff)
             if gate:
                 assert same, (name, rd, b, diff, list(g_tok[b]), list(tr.tokens))
                 assert fe <= FEAT_TOL[cfg.dtype], (name, rd, b, fe)
@@ -431,8 +441,13 @@ def test_round_end_to_end_bf16_reported(name):
     say(f"[end-to-end bf16, reported] {name}")
     s = _run_rounds(name, 2, gate=False)
     say(f"  {name}: {s['match']}/{s['compared']} sequence-rounds identical to the oracle, "
-        f"{s['near']} near-tie, root feature rel L2 max {max(s['feat'], default=0):.2e}")
-    assert all(f <= FEAT_TOL["bf16"] for f in s["feat"][:1]) or s["compared"] == 0
+        f"{s['near']} near-tie, {s['path_differs']} with another accepted path, "
+        f"root feature rel L2 max {max(s['feat'], default=0):.2e} (same path), "
+        f"fields differing: {s['diffs']}")
+    # bf16 storage moves logits by more than the oracle's near-tie margin, so the
+    # drafted tree may differ from the fp64 one; where the accepted path is the
+    # same, the extend's next root feature must still agree
+    assert all(f <= FEAT_TOL["bf16"] for f in s["feat"])
 
 
 # ------------------------------------------------------------------ determinism, data errors

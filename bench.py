@@ -58,16 +58,24 @@ LMHEAD_SOURCES = ("k_lmhead.hip", "eagle_internal.h")
 
 
 def stored_traffic(workload: str):
-    """HBM bytes per LM-head launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, "lmhead_7b_pmc.json")
+    """HBM bytes per LM-head launch from the committed counter summary (its
+    `key: value` lines), if it was taken on the current kernel source and the
+    same workload; else None."""
+    path = os.path.join(PROFILES, "k_lmhead_7b_counters.md")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                rec[k.strip()] = v.strip().strip("`")
     if rec.get("source_hash") != source_hash(*LMHEAD_SOURCES) or rec.get("workload") != workload:
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, inp, budget_s: float) -> dict:
@@ -152,7 +160,7 @@ def main() -> int:
         with torch.cuda.stream(stream):
             r.level(1, stream=stream)
             for _ in range(args.lmhead_only):
-                r.level(2, L.EAGLE_LEVEL_TAIL_ONLY, stream=stream)
+                r.level(2, L.EAGLE_LEVEL_LMHEAD_ONLY, stream=stream)
         torch.cuda.synchronize()
         print(json.dumps({"lmhead_only": args.lmhead_only, "copy_bytes": src.numel()}))
         return 0
@@ -189,16 +197,25 @@ def main() -> int:
     ms = el * 1e3 / args.steps
     rounds_s = args.steps / el
 
-    # dominant kernel (LM head + softmax + top-k + select), timed live with HIP
-    # events on the stream it runs on: one launch per tail-only level call
+    # dominant kernel (the LM-head GEMM with its fused per-slab softmax and
+    # top-k), timed live with HIP events on the stream it runs on: a
+    # LMHEAD_ONLY level call launches exactly that one kernel
+    # Between launches a 512 MiB read (a reduction, outside the events) evicts
+    # the 256 MB memory-side Infinity Cache, which would otherwise keep part of
+    # the 262 MB LM head warm across back-to-back launches; inside a round the
+    # layer weights stream through it in between.  A read, not a copy: a
+    # copy's dirty lines would be written back during the timed launch.
+    scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
     evs = []
     with torch.cuda.stream(stream):
         for it in range(max(5, args.steps // 5)):
             for level in range(2, cfg.D + 1):
+                torch.sum(scrub, dim=0, out=scrub_out)
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                r.level(level, L.EAGLE_LEVEL_TAIL_ONLY, stream=stream)
+                r.level(level, L.EAGLE_LEVEL_LMHEAD_ONLY, stream=stream)
                 e1.record(stream)
                 evs.append((e0, e1))
     torch.cuda.synchronize()
@@ -228,7 +245,7 @@ def main() -> int:
         "tree_tokens_per_s": round(rounds_s * cfg.B * cfg.m, 1),
         "round_hbm": {"algorithmic_bytes": int(round_bytes), "achieved": round(round_gbps, 1),
                       "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(round_gbps / HBM_PEAK_GBPS, 4)},
-        "roofline": {"kernel": "k_lmhead (LM head + softmax + top-k + k*k->k select)",
+        "roofline": {"kernel": "k_lmhead (LM-head GEMM + per-slab softmax/top-k)",
                      "bound": "hbm", "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
                      "avg_launch_us": round(lm_ms * 1e3, 2),

@@ -25,6 +25,7 @@ EAGLE_F32 = 0
 EAGLE_BF16 = 1
 EAGLE_LEVEL_FULL = 0
 EAGLE_LEVEL_TAIL_ONLY = 1
+EAGLE_LEVEL_LMHEAD_ONLY = 2
 EAGLE_MAX_DEPTH = 16
 
 WS_ERROR, WS_POOL, WS_FRONTIER, WS_FEAT, WS_TREE_K, WS_TREE_V, WS_EXT_H = range(7)

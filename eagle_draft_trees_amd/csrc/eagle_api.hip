@@ -326,10 +326,11 @@ int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagl
   int r;
   if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
     return r;
-  if (flags != EAGLE_LEVEL_FULL && flags != EAGLE_LEVEL_TAIL_ONLY)
+  if (flags != EAGLE_LEVEL_FULL && flags != EAGLE_LEVEL_TAIL_ONLY && flags != EAGLE_LEVEL_LMHEAD_ONLY)
     return fail(EAGLE_ERR_ARG, "flags %d", flags);
   if (level < 1 || level > cfg->depth) return fail(EAGLE_ERR_ARG, "level %d (1..%d)", level, cfg->depth);
-  const bool tail_only = level == 1 || flags == EAGLE_LEVEL_TAIL_ONLY;
+  const bool lm_only = flags == EAGLE_LEVEL_LMHEAD_ONLY;
+  const bool tail_only = level == 1 || flags != EAGLE_LEVEL_FULL;
   if ((r = check_weights(w, tail_only)) || (r = check_state(state))) return r;
   const hipStream_t s = (hipStream_t)stream;
   RoundArgs a = make_args(*dims, *cfg, w, state, ws);
@@ -337,6 +338,7 @@ int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagl
     a.rows = cfg->batch;
     const LmPlan pl = plan_lm(cfg->batch, *dims, cfg->topk);
     if ((r = hip_ok(launch_lmhead(a, pl, 1, s), "lm head"))) return r;
+    if (lm_only) return EAGLE_OK;
     return hip_ok(launch_lmmerge(a, pl, 1, s), "lm merge");
   }
   a.mode = MODE_LEVEL;
@@ -346,6 +348,7 @@ int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagl
   if (!tail_only && (r = run_layer(a, *dims, *cfg, s))) return r;
   const LmPlan pl = plan_lm(a.rows, *dims, cfg->topk);
   if ((r = hip_ok(launch_lmhead(a, pl, level, s), "lm head"))) return r;
+  if (lm_only) return EAGLE_OK;
   return hip_ok(launch_lmmerge(a, pl, level, s), "lm merge");
 }
 

@@ -143,6 +143,12 @@ int eagle_workspace_init(const eagle_dims *dims, const eagle_tree_cfg *cfg, void
 #define EAGLE_LEVEL_TAIL_ONLY 1   /* level >= 2: skip the forward and run the LM-head
                                      tail + select on the features already in the
                                      workspace (EAGLE_WS_FEAT, depth level-1) */
+#define EAGLE_LEVEL_LMHEAD_ONLY 2 /* timing and counter runs: launch only the LM-head
+                                     GEMM stage of the tail (per-slab softmax and
+                                     top-k partials in the workspace); the pool and
+                                     frontier are NOT updated, so a level run this way
+                                     must be run again with FULL or TAIL_ONLY before
+                                     the round continues */
 
 /* One tree level ([P1] §10.3 expansion; [P3] select_top_k_tokens).
  * level 1: LM head + softmax + top-k on root_feat; the k children of each

@@ -88,22 +88,20 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
   return p;
 }
 
+// Attention: one workgroup per (sequence, KV head, 16-query tile); when those
+// are fewer than about 256 the keys are split further (at least 4 chunks of 16
+// keys per split) so that every compute unit streams part of the KV.
 AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& c, int nseq) {
   AttnPlan p{};
   p.RS = RS;
   p.g = d.n_heads / d.n_kv_heads;
   p.nq = RS * p.g;
-  p.QT = 32;
-  p.nqt = cdiv(p.nq, p.QT);
-  const int nwg = nseq * d.n_kv_heads * p.nqt;
-  const int maxP = c.max_prefix;
-  // about 512 workgroups in all, slices of at least 64 keys, at most 128 slices
-  const int nps_t = std::max(1, cdiv(512, nwg));
-  p.KCH = std::max(std::max(64, cdiv(maxP, 127)), cdiv(cdiv(maxP, nps_t), 32) * 32);
-  p.KCH = cdiv(p.KCH, 32) * 32;
-  p.nps = cdiv(maxP, p.KCH);
-  p.nsplit = p.nps + (mode == MODE_LEVEL ? 1 : 0);
-  p.part_floats = (size_t)nwg * p.nsplit * p.QT * (d.head_dim + 2);
+  p.nqt = cdiv(p.nq, 16);
+  const int tiles = nseq * d.n_kv_heads * p.nqt;
+  const int keys = c.max_prefix + (mode == MODE_LEVEL ? c.depth * c.topk : 0);
+  const int chunks = cdiv(keys, 16);
+  p.nsplit = std::max(1, std::min({8, cdiv(256, tiles), std::max(1, chunks / 4)}));
+  p.part_floats = p.nsplit > 1 ? (size_t)tiles * p.nsplit * 16 * (d.head_dim + 2) : 0;
   return p;
 }
 
@@ -183,11 +181,8 @@ static int check_cfg(const eagle_dims* d, const eagle_tree_cfg* c) {
   if (c->max_prefix < c->m + 1) return fail(EAGLE_ERR_SHAPE, "max_prefix %d < m+1", c->max_prefix);
   if (d) {
     const AttnPlan pa = plan_attn(MODE_EXTEND, c->m, *d, *c, c->batch);
-    const AttnPlan pl = plan_attn(MODE_LEVEL, c->topk, *d, *c, c->batch);
-    if (pa.nsplit > 128 || pl.nsplit > 128)
-      return fail(EAGLE_ERR_UNSUPPORTED, "attention split count too large");
     const long wg = (long)c->batch * d->n_kv_heads * pa.nqt;
-    if (wg >= GRID_CNT) return fail(EAGLE_ERR_UNSUPPORTED, "attention grid %ld too large", wg);
+    if (wg > (1L << 30)) return fail(EAGLE_ERR_UNSUPPORTED, "attention grid %ld too large", wg);
     for (int op = OP_FC; op <= OP_DOWN; ++op)
       for (int M : {c->batch * c->topk, c->batch * c->m})
         if (plan_gemm(op, M, *d).S > GEMM_MAXS)

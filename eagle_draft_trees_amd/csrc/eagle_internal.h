@@ -184,8 +184,9 @@ struct LmPlan {
 };
 
 struct AttnPlan {
-  int RS, g, nq, QT, nqt, KCH, nps, nsplit;  // nsplit = prefix splits (+1 in-tree split)
-  size_t part_floats;
+  int RS, g, nq, nqt;  // rows per sequence, GQA group, queries per KV head, 16-query tiles
+  int nsplit;          // key splits per tile (partials merged by a second kernel when > 1)
+  size_t part_floats;  // split partials
 };
 
 GemmPlan plan_gemm(int op, int M, const eagle_dims& d);

@@ -8,254 +8,401 @@
 // extend rows 0..i, which the QKV epilogue has already appended to the cache
 // ([P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里").
 //
-// All rows of a sequence share its prefix, so one workgroup takes one
-// (sequence, KV head, query tile) and one slice of the prefix: the K/V tiles of
-// that slice are staged in LDS once and used by every query row and every
-// query head of the GQA group.  Each slice writes (max, sum, unnormalised
-// output) partials; a separate slice handles the per-row in-tree keys; the
-// last workgroup to finish a (sequence, KV head, query tile) merges the slices
-// in slice order (deterministic).  Scores 1/sqrt(hd) * q.k in fp32.
+// One workgroup per (sequence, KV head, tile of 16 queries); the queries of a
+// tile are (row, head of the GQA group) pairs.  Its eight waves split the keys
+// in chunks of 16: the prefix rows first, then (levels) every in-tree slot of
+// depths 1..L as extra keys, masked per query to that query's ancestors and
+// itself.  Per chunk a wave
+//   * computes the 16x16 score tile S^T = K Q^T on MFMA (bf16: q split into a
+//     high and a low bf16 part, so the scores keep about 16 mantissa bits;
+//     fp32: the fp32 MFMA), lane (g, q) holding keys 4g..4g+3 of query q;
+//   * updates each query's running max and sum (online softmax);
+//   * accumulates P V on the vector ALUs in fp32, each lane owning hd/64
+//     output dimensions, with every V row read as one coalesced row.
+// The next chunk's K and V loads are in flight while a chunk computes.  The
+// waves' partial (max, sum, output) meet in LDS and are combined in wave order
+// (deterministic); there is no cross-workgroup step.  Scores 1/sqrt(hd) q.k.
 #include "eagle_internal.h"
 
 namespace eg {
 
-constexpr int AT_QT = 32;  // queries per workgroup
-constexpr int AT_KT = 32;  // keys per LDS tile
-constexpr int AT_MAXSPLIT = 128;  // merge weights and maxima reuse the K/V tiles' LDS
+constexpr int AT_W = 8;       // waves per workgroup
+constexpr int AT_Q = 16;      // queries per workgroup (one MFMA tile)
+constexpr int AT_C = 16;      // keys per chunk
+constexpr int AT_MAXS = 8;    // key splits of one query tile at most
 
-template <typename T, int HDIM>
-__global__ void __launch_bounds__(BLOCK) k_attn(RoundArgs a, AttnPlan p) {
-  __shared__ float sQ[AT_QT][129];
-  __shared__ float sK[AT_KT][129];
-  __shared__ float sV[AT_KT][128];
-  __shared__ float sS[AT_QT][AT_KT + 1];
-  __shared__ float sM[AT_QT], sL[AT_QT], sScale[AT_QT];
-  __shared__ int sLim[AT_QT];
+template <typename T, int HD> struct AtVec;  // this lane's HD/64 elements of a V row
+template <> struct AtVec<bf16_t, 128> {
+  typedef uint32_t raw;
+  __device__ static raw ld(const bf16_t* row, int lane) { return *(const uint32_t*)(row + 2 * lane); }
+  __device__ static void cvt(raw r, float* v) { v[0] = bf2f(r & 0xFFFFu); v[1] = bf2f(r >> 16); }
+};
+template <> struct AtVec<bf16_t, 64> {
+  typedef uint32_t raw;
+  __device__ static raw ld(const bf16_t* row, int lane) { return row[lane]; }
+  __device__ static void cvt(raw r, float* v) { v[0] = bf2f(r & 0xFFFFu); }
+};
+template <> struct AtVec<float, 128> {
+  typedef float2 raw;
+  __device__ static raw ld(const float* row, int lane) { return *(const float2*)(row + 2 * lane); }
+  __device__ static void cvt(raw r, float* v) { v[0] = r.x; v[1] = r.y; }
+};
+template <> struct AtVec<float, 64> {
+  typedef float raw;
+  __device__ static raw ld(const float* row, int lane) { return row[lane]; }
+  __device__ static void cvt(raw r, float* v) { v[0] = r; }
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <typename T, int HD>
+__global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
+  constexpr int KS = El<T>::KSTEP;
+  constexpr int PER = El<T>::PER16;
+  constexpr int NKS = HD / KS;   // MFMA k-steps over the head dimension
+  constexpr int DPL = HD / 64;   // output dimensions per lane in the P.V step
+  typedef AtVec<T, HD> VV;
+  __shared__ __attribute__((aligned(16))) float sP[AT_W][AT_Q][AT_C];  // this chunk's probabilities, per wave
+  __shared__ float sAl[AT_W][AT_Q];            // this chunk's rescale of the running output
+  __shared__ float sM[AT_W][AT_Q], sL[AT_W][AT_Q];
+  __shared__ float sO[AT_W][AT_Q][HD];
+  __shared__ int sLim[AT_Q];
+  __shared__ int sAnc[AT_Q][EAGLE_MAX_DEPTH];
+  __shared__ float sWt[AT_W][AT_Q], sInvL[AT_Q];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int q = lane & 15, g = lane >> 4;
   const int wg = blockIdx.x, split = blockIdx.y;
   const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
-  constexpr int hd = HDIM;
-  const int g = p.g;
-  const int q0 = qt * AT_QT;
-  const int nq = min(AT_QT, p.nq - q0);
+  const int q0 = qt * AT_Q;
   const int P = clamp_prefix(a.prefix_len[b], a);
-  const float scale = rsqrtf((float)hd);
-  const int HD = a.H * hd;
+  const bool level = a.mode == MODE_LEVEL;
+  const int HDq = a.H * HD;
 
-  // queries: qi -> (row within sequence, head)
-  for (int idx = tid; idx < nq * hd; idx += BLOCK) {
-    const int qi = idx / hd, dd = idx % hd, gq = q0 + qi;
-    const int row = b * p.RS + gq / g, head = kvh * g + gq % g;
-    sQ[qi][dd] = a.q[(size_t)row * HD + head * hd + dd] * scale;
-  }
-  if (tid < AT_QT) {
+  // ---- per-query visibility: prefix limit and (levels) ancestor slots
+  if (tid < AT_Q) {
     const int gq = q0 + tid;
-    sLim[tid] = (a.mode == MODE_LEVEL) ? P : P + gq / g + 1;
-    sM[tid] = -INFINITY;
-    sL[tid] = 0.f;
+    const int row = min(gq, p.nq - 1) / p.g;
+    sLim[tid] = gq >= p.nq ? 0 : (level ? P : P + row + 1);
+    if (level) {  // the record's 16 ancestor slots in four 16-byte loads (all in flight together)
+      const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + row];
+      uint4 an[EAGLE_MAX_DEPTH / 4];
+#pragma unroll
+      for (int u = 0; u < EAGLE_MAX_DEPTH / 4; ++u) an[u] = ld16(&nd.anc[4 * u]);
+#pragma unroll
+      for (int dd = 0; dd < EAGLE_MAX_DEPTH; ++dd) {
+        const uint4 v = an[dd / 4];
+        const int s_ = (int)((dd & 3) == 0 ? v.x : (dd & 3) == 1 ? v.y : (dd & 3) == 2 ? v.z : v.w);
+        sAnc[tid][dd] = (gq < p.nq && dd < a.depth) ? clamp_slot(s_, a.k) : -1;
+      }
+    }
+  }
+  // keys: Pv prefix rows (the widest limit in the tile), then ntree in-tree slots
+  // (all wave-uniform; said so explicitly so that chunk indices and branches stay scalar)
+  const int lastrow = (min(q0 + AT_Q, p.nq) - 1) / p.g;
+  const int Pv = __builtin_amdgcn_readfirstlane(level ? P : min(P + lastrow + 1, a.max_prefix));
+  const int ntree = __builtin_amdgcn_readfirstlane(level ? a.depth * a.k : 0);
+  const int cp = (Pv + AT_C - 1) / AT_C;
+  const int nch = cp + (ntree + AT_C - 1) / AT_C;
+  // this split's chunks [c0, c1) (splits of one tile merge in k_attn_merge)
+  const int cps = (nch + p.nsplit - 1) / p.nsplit;
+  const int c0 = split * cps, c1 = min(nch, c0 + cps);
+  const size_t rs = (size_t)a.Hkv * HD;  // stride between key rows of the cache
+  const T* Kp = (const T*)a.k_cache + ((size_t)b * a.max_prefix * a.Hkv + kvh) * HD;
+  const T* Vp = (const T*)a.v_cache + ((size_t)b * a.max_prefix * a.Hkv + kvh) * HD;
+  const T* Kt = (const T*)a.tk;
+  const T* Vt = (const T*)a.tv;
+  // row of key i of chunk c (clamped to a valid row; masked later)
+  auto krow = [&](const T* prefix, const T* tree, int c, int i) __attribute__((always_inline)) -> const T* {
+    if (c < cp) return prefix + (size_t)min(c * AT_C + i, Pv - 1) * rs;
+    int t = (c - cp) * AT_C + i;
+    t = t < ntree ? t : 0;
+    const int dep = t / a.k + 1, slot = t - (dep - 1) * a.k;
+    return tree + ((((size_t)b * a.D + dep) * a.k + slot) * a.Hkv + kvh) * HD;
+  };
+
+  // the first chunk's K/V loads go out now, ahead of the query setup
+  typedef typename VV::raw vraw;
+  auto load = [&](uint4 (&kr)[NKS], vraw (&vr)[AT_C], int c) __attribute__((always_inline)) {
+    c = min(c, c1 - 1);  // past the split's last chunk: repeat it (unused)
+    if (c < cp) {  // consecutive prefix rows; the last chunk's tail repeats row Pv-1
+      const int r0 = c * AT_C, rmax = Pv - 1 - r0;
+      const T* kp = Kp + (size_t)(r0 + min(q, rmax)) * rs;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) kr[s] = ld16(kp + s * KS + g * PER);
+#pragma unroll
+      for (int j = 0; j < AT_C; ++j) vr[j] = VV::ld(Vp + (size_t)(r0 + min(j, rmax)) * rs, lane);
+    } else {
+      const T* kp = krow(Kp, Kt, c, q);
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) kr[s] = ld16(kp + s * KS + g * PER);
+#pragma unroll
+      for (int j = 0; j < AT_C; ++j) vr[j] = VV::ld(krow(Vp, Vt, c, j), lane);
+    }
+  };
+
+  uint4 ka[NKS], kb[NKS];
+  vraw va[AT_C], vb[AT_C];
+  const bool busy = c0 + w < c1;
+  if (busy) load(ka, va, c0 + w);
+
+  // ---- this lane's query operand (query q0+q, dims of k-step s for lane group g),
+  // pre-scaled by 1/sqrt(hd); bf16 keeps a high and a low part
+  const float scale = rsqrtf((float)HD);
+  uint4 qh[NKS], ql[NKS];
+  {
+    const int gq = min(q0 + q, p.nq - 1);
+    const bool qv = q0 + q < p.nq;
+    const int row = b * p.RS + gq / p.g, head = kvh * p.g + gq % p.g;
+    const float* qp = a.q + ((size_t)row * a.H + head) * HD;
+    const float qs = qv ? scale : 0.f;  // padding queries: zero (their rows are never written)
+    float4 qx[NKS][PER / 4];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int u = 0; u < PER / 4; ++u) qx[s][u] = *(const float4*)(qp + s * KS + g * PER + 4 * u);
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      float x[PER];
+#pragma unroll
+      for (int u = 0; u < PER / 4; ++u) {
+        x[4 * u] = qx[s][u].x * qs;
+        x[4 * u + 1] = qx[s][u].y * qs;
+        x[4 * u + 2] = qx[s][u].z * qs;
+        x[4 * u + 3] = qx[s][u].w * qs;
+      }
+      if constexpr (sizeof(T) == 2) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
+          const uint32_t l0 = f2bf(x[2 * e] - bf2f(h0)), l1 = f2bf(x[2 * e + 1] - bf2f(h1));
+          hw[e] = h0 | (h1 << 16);
+          lw[e] = l0 | (l1 << 16);
+        }
+        qh[s] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        ql[s] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      } else {
+        qh[s] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                           __float_as_uint(x[3]));
+        ql[s] = make_uint4(0, 0, 0, 0);
+      }
+    }
   }
   __syncthreads();
 
-  const size_t prec = (size_t)hd + 2;
-  float* part = a.apart + ((size_t)wg * p.nsplit + split) * AT_QT * prec;
-  constexpr int qg_pv = BLOCK / hd;  // query groups in the P.V step
-  const int dpv = tid % hd, qpv = tid / hd;
-  float acc[AT_QT / 2];
+  // running softmax state of query q (replicated over the lane groups) and
+  // this lane's output dimensions for all 16 queries
+  float m = -INFINITY, l = 0.f;
+  float acc[AT_Q][DPL];
 #pragma unroll
-  for (int i = 0; i < AT_QT / 2; ++i) acc[i] = 0.f;
+  for (int i = 0; i < AT_Q; ++i)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
 
-  if (split < p.nps) {
-    int maxlim = 0;
-    for (int qi = 0; qi < nq; ++qi) maxlim = max(maxlim, sLim[qi]);
-    const int klo = split * p.KCH;
-    const int khi = min(maxlim, klo + p.KCH);
-    const T* Kb = (const T*)a.k_cache + ((size_t)b * a.max_prefix * a.Hkv + kvh) * hd;
-    const T* Vb = (const T*)a.v_cache + ((size_t)b * a.max_prefix * a.Hkv + kvh) * hd;
-    const size_t rstride = (size_t)a.Hkv * hd;
-    for (int kt0 = klo; kt0 < khi; kt0 += AT_KT) {
-      const int nk = min(AT_KT, khi - kt0);
-      {
-        // 16-byte loads: PER elements of one key row per thread and chunk
-        constexpr int PER = El<T>::PER16;
-        const int cpr = hd / PER;  // chunks per key row
-        for (int idx = tid; idx < AT_KT * cpr; idx += BLOCK) {
-          const int kr = idx / cpr, d0 = (idx % cpr) * PER;
-          uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
-          if (kr < nk) {
-            kv = ld16(Kb + (size_t)(kt0 + kr) * rstride + d0);
-            vv = ld16(Vb + (size_t)(kt0 + kr) * rstride + d0);
-          }
-          const T* ke = (const T*)&kv;
-          const T* ve = (const T*)&vv;
+  auto chunk = [&](const uint4 (&kr)[NKS], const vraw (&vr)[AT_C], int c) __attribute__((always_inline)) {
+    // scores: lane (g, q) gets S^T[4g + r][q], r = 0..3
+    f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            sK[kr][d0 + e] = El<T>::ld(ke, e);
-            sV[kr][d0 + e] = El<T>::ld(ve, e);
-          }
-        }
-      }
-      __syncthreads();
-      {
-        const int kr = tid % AT_KT;
-        for (int qi = tid / AT_KT; qi < nq; qi += BLOCK / AT_KT) {
-          float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-          for (int dd = 0; dd < hd; dd += 4) {
-            s0 += sQ[qi][dd] * sK[kr][dd];
-            s1 += sQ[qi][dd + 1] * sK[kr][dd + 1];
-            s2 += sQ[qi][dd + 2] * sK[kr][dd + 2];
-            s3 += sQ[qi][dd + 3] * sK[kr][dd + 3];
-          }
-          const float s = (s0 + s1) + (s2 + s3);
-          sS[qi][kr] = (kr < nk && kt0 + kr < sLim[qi]) ? s : -INFINITY;
-        }
-      }
-      __syncthreads();
-      {
-        const int half = lane >> 5, kr = lane & 31;
-        for (int qi = wave * 2 + half; qi < nq; qi += 8) {
-          const float x = sS[qi][kr];
-          float t = x;
-#pragma unroll
-          for (int o = 16; o > 0; o >>= 1) t = fmaxf(t, __shfl_xor(t, o));
-          const float mold = sM[qi];
-          const float mnew = fmaxf(mold, t);
-          const float pr = (mnew == -INFINITY || x == -INFINITY) ? 0.f : expf(x - mnew);
-          float ps = pr;
-#pragma unroll
-          for (int o = 16; o > 0; o >>= 1) ps += __shfl_xor(ps, o);
-          ps = __shfl(ps, half * 32);
-          sS[qi][kr] = pr;
-          if (kr == 0) {
-            const float sc = (mold == -INFINITY) ? (mnew == -INFINITY ? 1.f : 0.f) : expf(mold - mnew);
-            sScale[qi] = sc;
-            sL[qi] = sL[qi] * sc + ps;
-            sM[qi] = mnew;
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < AT_QT / 2; ++i) {
-        const int qi = qpv + i * qg_pv;
-        if (qi < nq) {
-          float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-          for (int kr = 0; kr < AT_KT; kr += 2) {  // keys >= nk have weight 0 and value 0
-            s0 += sS[qi][kr] * sV[kr][dpv];
-            s1 += sS[qi][kr + 1] * sV[kr + 1][dpv];
-          }
-          acc[i] = acc[i] * sScale[qi] + (s0 + s1);
-        }
-      }
-      __syncthreads();
+    for (int s = 0; s < NKS; ++s) {
+      st = mma16(kr[s], qh[s], st, T());
+      if constexpr (sizeof(T) == 2) st = mma16(kr[s], ql[s], st, T());
     }
+    float sc[4];
+    float cmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < AT_QT / 2; ++i) {
-      const int qi = qpv + i * qg_pv;
-      if (qi < nq) part[qi * prec + 2 + dpv] = acc[i];
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      bool vis;
+      if (c < cp) {
+        vis = c * AT_C + i < sLim[q];
+      } else {
+        const int t = (c - cp) * AT_C + i;
+        const int dep = min(t / a.k + 1, EAGLE_MAX_DEPTH), slot = t - (dep - 1) * a.k;
+        vis = t < ntree && q0 + q < p.nq && sAnc[q][dep - 1] == slot;
+      }
+      sc[r] = vis ? st[r] : -INFINITY;
+      cmax = fmaxf(cmax, sc[r]);
     }
-    if (tid < nq) {
-      part[tid * prec] = sM[tid];
-      part[tid * prec + 1] = sL[tid];
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float mnew = fmaxf(m, cmax);
+    const float al = (m == -INFINITY) ? 0.f : expf(m - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = sc[r] == -INFINITY ? 0.f : expf(sc[r] - mnew);
+      sP[w][q][4 * g + r] = pr;
+      ps += pr;
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * al + ps;
+    m = mnew;
+    if (g == 0) sAl[w][q] = al;
+    __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads
+    // P.V: this lane's output dimensions, every query of the tile
+    float v[AT_C][DPL];
+#pragma unroll
+    for (int j = 0; j < AT_C; ++j) VV::cvt(vr[j], v[j]);
+#pragma unroll
+    for (int i = 0; i < AT_Q; ++i) {
+      const float ai = sAl[w][i];
+      float pr[AT_C];  // the query's 16 probabilities: four aligned 16-byte broadcast reads
+#pragma unroll
+      for (int u = 0; u < AT_C / 4; ++u) {
+        const float4 f = *(const float4*)&sP[w][i][4 * u];
+        pr[4 * u] = f.x;
+        pr[4 * u + 1] = f.y;
+        pr[4 * u + 2] = f.z;
+        pr[4 * u + 3] = f.w;
+      }
+      float o[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = acc[i][e] * ai;
+#pragma unroll
+      for (int j = 0; j < AT_C; ++j)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] += pr[j] * v[j][e];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[i][e] = o[e];
+    }
+    __builtin_amdgcn_wave_barrier();  // reads done before the next chunk's writes
+  };
+
+  // chunks w, w+AT_W, ...; two in flight (ping-pong register sets; a load
+  // past the last chunk repeats it and is unused)
+  if (busy) {
+    for (int c = c0 + w;; c += 2 * AT_W) {
+      load(kb, vb, c + AT_W);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(ka, va, c);
+      if (c + AT_W >= c1) break;
+      load(ka, va, c + 2 * AT_W);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(kb, vb, c + AT_W);
+      if (c + 2 * AT_W >= c1) break;
+    }
+  }
+
+  // ---- combine the waves' partial results in wave order
+  if (g == 0) {
+    sM[w][q] = m;
+    sL[w][q] = l;
+  }
+#pragma unroll
+  for (int i = 0; i < AT_Q; ++i)
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) sO[w][i][lane * DPL + e] = acc[i][e];
+  __syncthreads();
+  if (tid < AT_Q) {
+    float M = -INFINITY;
+    for (int ww = 0; ww < AT_W; ++ww)
+      if (sL[ww][tid] > 0.f) M = fmaxf(M, sM[ww][tid]);
+    float L = 0.f;
+    for (int ww = 0; ww < AT_W; ++ww) {
+      const float wt = sL[ww][tid] > 0.f ? expf(sM[ww][tid] - M) : 0.f;
+      sWt[ww][tid] = wt;
+      L += sL[ww][tid] * wt;
+    }
+    sInvL[tid] = L > 0.f ? 1.0f / L : 0.f;
+  }
+  __syncthreads();
+  if (p.nsplit == 1) {
+    for (int idx = tid; idx < AT_Q * HD; idx += AT_W * WAVE) {
+      const int i = idx / HD, dd = idx - i * HD, gq = q0 + i;
+      if (gq >= p.nq) continue;
+      float O = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < AT_W; ++ww) O += sWt[ww][i] * sO[ww][i][dd];
+      const int row = b * p.RS + gq / p.g, head = kvh * p.g + gq % p.g;
+      El<T>::st((T*)a.attn, (size_t)row * HDq + head * HD + dd, O * sInvL[i]);
     }
   } else {
-    // in-tree keys of a level row: its ancestors' slots and its own
-    for (int qi = wave; qi < nq; qi += 4) {
-      const int gq = q0 + qi, j = gq / g;
-      const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
-      float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-      const float qa = sQ[qi][lane], qb = (lane + 64 < hd) ? sQ[qi][lane + 64] : 0.f;
-      // every ancestor's K/V is loaded up front so the loads overlap
-      float ka[EAGLE_MAX_DEPTH], kb[EAGLE_MAX_DEPTH], va[EAGLE_MAX_DEPTH], vb[EAGLE_MAX_DEPTH];
+    // partial of this split: [max, sum, unnormalised output] per query
+    float* part = a.apart + ((size_t)wg * p.nsplit + split) * AT_Q * (HD + 2);
+    for (int idx = tid; idx < AT_Q * HD; idx += AT_W * WAVE) {
+      const int i = idx / HD, dd = idx - i * HD;
+      float O = 0.f;
 #pragma unroll
-      for (int dep = 1; dep <= EAGLE_MAX_DEPTH; ++dep) {
-        ka[dep - 1] = kb[dep - 1] = va[dep - 1] = vb[dep - 1] = 0.f;
-        if (dep <= a.depth) {
-          const size_t off =
-              ((((size_t)b * a.D + dep) * a.k + clamp_slot(nd.anc[dep - 1], a.k)) * a.Hkv + kvh) * hd;
-          const T* kp = (const T*)a.tk + off;
-          const T* vp = (const T*)a.tv + off;
-          ka[dep - 1] = El<T>::ld(kp, lane);
-          va[dep - 1] = El<T>::ld(vp, lane);
-          if (lane + 64 < hd) {
-            kb[dep - 1] = El<T>::ld(kp, lane + 64);
-            vb[dep - 1] = El<T>::ld(vp, lane + 64);
-          }
-        }
-      }
-#pragma unroll
-      for (int dep = 1; dep <= EAGLE_MAX_DEPTH; ++dep) {
-        if (dep <= a.depth) {
-          const float s = wave_sum(qa * ka[dep - 1] + qb * kb[dep - 1]);
-          const float mnew = fmaxf(m, s);
-          const float sc = (m == -INFINITY) ? 0.f : expf(m - mnew);
-          const float pr = expf(s - mnew);
-          l = l * sc + pr;
-          o0 = o0 * sc + pr * va[dep - 1];
-          o1 = o1 * sc + pr * vb[dep - 1];
-          m = mnew;
-        }
-      }
-      part[qi * prec + 2 + lane] = o0;
-      if (lane + 64 < hd) part[qi * prec + 2 + lane + 64] = o1;
-      if (lane == 0) {
-        part[qi * prec] = m;
-        part[qi * prec + 1] = l;
-      }
+      for (int ww = 0; ww < AT_W; ++ww) O += sWt[ww][i] * sO[ww][i][dd];
+      part[i * (HD + 2) + 2 + dd] = O;
     }
-  }
-
-  if (!arrive_last(a.cnt + wg, p.nsplit)) return;
-
-  // merge the slices in slice order: per-query weights first (LDS), then the
-  // weighted sum of each slice's unnormalised output
-  float* sw = &sK[0][0];  // [nq][nsplit] slice sums, then weights; nq * nsplit <= 32 * 128
-  float* smx = &sV[0][0];  // [nq][nsplit] slice maxima
-  const float* wbase = a.apart + (size_t)wg * p.nsplit * AT_QT * prec;
-  for (int idx = tid; idx < nq * p.nsplit; idx += BLOCK) {
-    const int qi = idx / p.nsplit, s = idx % p.nsplit;
-    const float* ps = wbase + ((size_t)s * AT_QT + qi) * prec;
-    smx[idx] = ps[0];
-    sw[idx] = ps[1];
-  }
-  __syncthreads();
-  if (tid < nq) {
-    float M = -INFINITY;
-    for (int s = 0; s < p.nsplit; ++s)
-      if (sw[tid * p.nsplit + s] > 0.f) M = fmaxf(M, smx[tid * p.nsplit + s]);
-    float L = 0.f;
-    for (int s = 0; s < p.nsplit; ++s) {
-      const float ls = sw[tid * p.nsplit + s];
-      const float w = ls > 0.f ? expf(smx[tid * p.nsplit + s] - M) : 0.f;
-      sw[tid * p.nsplit + s] = w;
-      L += ls * w;
+    if (tid < AT_Q) {
+      float M = -INFINITY, L = 0.f;
+      for (int ww = 0; ww < AT_W; ++ww)
+        if (sL[ww][tid] > 0.f) M = fmaxf(M, sM[ww][tid]);
+      for (int ww = 0; ww < AT_W; ++ww) L += sL[ww][tid] * sWt[ww][tid];
+      part[tid * (HD + 2)] = M;
+      part[tid * (HD + 2) + 1] = L;
     }
-    sScale[tid] = 1.0f / L;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nq * hd; idx += BLOCK) {
-    const int qi = idx / hd, dd = idx % hd, gq = q0 + qi;
-    float O = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < p.nsplit; ++s)
-      O += sw[qi * p.nsplit + s] * wbase[((size_t)s * AT_QT + qi) * prec + 2 + dd];
-    const int row = b * p.RS + gq / g, head = kvh * g + gq % g;
-    El<T>::st((T*)a.attn, (size_t)row * HD + head * hd + dd, O * sScale[qi]);
   }
 }
 
-hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
-  const dim3 grid(a.B * a.Hkv * p.nqt, p.nsplit), block(BLOCK);
-  if (a.dtype == EAGLE_BF16) {
-    if (a.hd == 128) hipLaunchKernelGGL((k_attn<bf16_t, 128>), grid, block, 0, s, a, p);
-    else hipLaunchKernelGGL((k_attn<bf16_t, 64>), grid, block, 0, s, a, p);
-  } else {
-    if (a.hd == 128) hipLaunchKernelGGL((k_attn<float, 128>), grid, block, 0, s, a, p);
-    else hipLaunchKernelGGL((k_attn<float, 64>), grid, block, 0, s, a, p);
+// Combine the key splits of each (sequence, KV head, query tile) in split
+// order: softmax-weighted sum of the splits' unnormalised outputs.  Every load
+// is issued up front (clamped, masked), so the kernel waits once.
+template <typename T, int HD>
+__global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPlan p) {
+  constexpr int PT = AT_Q * HD / (AT_W * WAVE);  // outputs per thread
+  __shared__ float sW[AT_MAXS][AT_Q], sInv[AT_Q];
+  const int tid = threadIdx.x, wg = blockIdx.x;
+  const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int q0 = qt * AT_Q;
+  const int ns = p.nsplit;
+  const float* part = a.apart + (size_t)wg * ns * AT_Q * (HD + 2);
+  float ov[PT][AT_MAXS];
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int idx = tid + u * AT_W * WAVE, i = idx / HD, dd = idx - i * HD;
+#pragma unroll
+    for (int s = 0; s < AT_MAXS; ++s)
+      ov[u][s] = part[((size_t)min(s, ns - 1) * AT_Q + i) * (HD + 2) + 2 + dd];
   }
+  if (tid < AT_Q) {
+    float mm[AT_MAXS], ll[AT_MAXS];
+#pragma unroll
+    for (int s = 0; s < AT_MAXS; ++s) {
+      const float* ps = part + ((size_t)min(s, ns - 1) * AT_Q + tid) * (HD + 2);
+      mm[s] = ps[0];
+      ll[s] = s < ns ? ps[1] : 0.f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < AT_MAXS; ++s)
+      if (ll[s] > 0.f) M = fmaxf(M, mm[s]);
+    float L = 0.f;
+#pragma unroll
+    for (int s = 0; s < AT_MAXS; ++s) {
+      const float wt = ll[s] > 0.f ? expf(mm[s] - M) : 0.f;
+      sW[s][tid] = wt;
+      L += ll[s] * wt;
+    }
+    sInv[tid] = L > 0.f ? 1.0f / L : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int idx = tid + u * AT_W * WAVE, i = idx / HD, dd = idx - i * HD, gq = q0 + i;
+    float O = 0.f;
+#pragma unroll
+    for (int s = 0; s < AT_MAXS; ++s) O += sW[s][i] * ov[u][s];  // weight 0 past ns
+    if (gq >= p.nq) continue;
+    const int row = b * p.RS + gq / p.g, head = kvh * p.g + gq % p.g;
+    El<T>::st((T*)a.attn, (size_t)row * (a.H * HD) + head * HD + dd, O * sInv[i]);
+  }
+}
+
+template <typename T, int HD>
+static hipError_t launch_attn_t(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
+  const int tiles = a.B * a.Hkv * p.nqt;
+  hipLaunchKernelGGL((k_attn<T, HD>), dim3(tiles, p.nsplit), dim3(AT_W * WAVE), 0, s, a, p);
+  if (p.nsplit > 1) hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(tiles), dim3(AT_W * WAVE), 0, s, a, p);
   return hipGetLastError();
+}
+
+hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
+  if (a.dtype == EAGLE_BF16) return a.hd == 128 ? launch_attn_t<bf16_t, 128>(a, p, s) : launch_attn_t<bf16_t, 64>(a, p, s);
+  return a.hd == 128 ? launch_attn_t<float, 128>(a, p, s) : launch_attn_t<float, 64>(a, p, s);
 }
 
 }  // namespace eg

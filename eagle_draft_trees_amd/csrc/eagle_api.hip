@@ -57,6 +57,8 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   return p;
 }
 
+static constexpr size_t SK_XLDS_MAX = 140 * 1024;  // LDS for a staged X tile (of 160 KB per CU)
+
 // Level GEMMs (at most 16 rows): about one workgroup per compute unit, each
 // with up to 16 waves that split K; column tiles per workgroup grow with N.
 SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
@@ -68,9 +70,16 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   p.ntile = cdiv(p.N, 16);
   p.CT = std::max(1, std::min(SK_MAXW, cdiv(p.ntile, 256)));
   const int nks = cdiv(p.K, d.dtype == EAGLE_BF16 ? 32 : 16);
-  p.KSW = std::max(1, std::min(SK_MAXW / p.CT, nks / 8));
+  const int nw = op == OP_GATEUP ? 2 : 1;
+  // one column tile per workgroup: all 16 waves split K (every CU busy);
+  // several tiles: fewer, longer K slices (at least 32 k-steps) stream better
+  p.KSW = p.CT == 1 ? std::max(1, std::min(SK_MAXW, nks / 8))
+                    : std::max(1, std::min(SK_MAXW / p.CT, nks / 32));
   p.nwg = cdiv(p.ntile, p.CT);
   p.nps = 0;
+  // the X tile is staged in LDS when it fits and is shared by at least two
+  // weight streams (with one, staging costs as much as it saves)
+  p.xlds = p.CT * nw >= 2 && (size_t)16 * (p.K * elem_size(d) + 16) <= SK_XLDS_MAX;
   return p;
 }
 

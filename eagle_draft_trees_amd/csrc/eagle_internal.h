@@ -174,7 +174,8 @@ struct GemmPlan {
 constexpr int SK_MAXW = 16;
 struct SkPlan {
   int M, N, K, ntile, CT, KSW, nwg;
-  int nps;  // gate/up: RMSNorm partial sums per row written by the O launch
+  int nps;   // gate/up: RMSNorm partial sums per row written by the O launch
+  int xlds;  // X staged in LDS (its 16 rows fit)
 };
 
 struct LmPlan {

@@ -13,10 +13,14 @@
 //    and one wave per tile finishes them in slice order (deterministic), so
 //    there is no cross-workgroup hand-off at all;
 //  * each lane loads its 16 bytes of W (16 columns x 64 bytes per wave
-//    instruction) and its 16 bytes of X (the same k range of its row, an L2
-//    hit) straight into registers, BU k-steps per batch, two batches in
-//    flight (ping-pong buffers); loads are unconditional from clamped
+//    instruction) straight into registers, BU k-steps per batch, two batches
+//    in flight (ping-pong buffers); loads are unconditional from clamped
 //    in-bounds addresses, and products past the slice are masked to zero;
+//  * X comes from an LDS copy of its 16 rows staged once per workgroup when
+//    that fits (K <= 4096 bf16); otherwise each lane also loads its 16 bytes
+//    of X (an L2 hit) per k-step.  X loads share the memory queue with the
+//    weight loads and cost about a quarter of the streaming rate, so the LDS
+//    copy is preferred;
 //  * the layer's elementwise work is fused into the epilogue (bias, RoPE and
 //    the in-tree KV write, residuals, the SwiGLU), and the RMSNorm statistic
 //    is finished where it is consumed: the O epilogue writes per-workgroup
@@ -39,13 +43,20 @@ __device__ __forceinline__ int sk_col(int op, int t, int c, int hd) {
   return t * 16 + c;
 }
 
-template <typename T, int OP>
+// XL: X staged once in LDS (when its 16 rows fit) instead of loaded from L2
+// at every k-step; the weight loop then issues only weight loads.
+template <typename T, int OP, bool XL>
 __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;  // weight streams per wave (gate and up)
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
+  constexpr int ES = (int)sizeof(T);
   constexpr int BU = (NW == 2) ? 3 : 4;  // k-steps per load batch
-  __shared__ f32x4_t red[SK_MAXW][NW][WAVE];
+  // dynamic LDS: the X tile [16][K] (row stride K*ES + 16 bytes, so the 16
+  // rows of one read fall in different banks), then reused for the K-slice
+  // partial sums [wave][NW][64] once every wave is done with X
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  f32x4_t* red = (f32x4_t*)dyn;
   __shared__ float s_ssq[SK_MAXW][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,20 +131,23 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
 #pragma unroll
   for (int w = 0; w < NW; ++w) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  const int XST = K * ES + 16;  // LDS row stride of the X tile (XL)
+  const unsigned char* xrow = dyn + c * XST;
   auto load = [&](uint4 (&wb)[BU][NW], uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int kc = min((s0k + b * BU + u) * KS + g * PER, klast);
 #pragma unroll
       for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + kc);
-      xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
+      if (!XL) xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
     }
   };
   auto comp = [&](const uint4 (&wb)[BU][NW], const uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int k = (s0k + b * BU + u) * KS + g * PER;
-      const uint4 xf = mask4(xb[u], k < kend);
+      const uint4 xv = XL ? *(const uint4*)(xrow + min(k, klast) * ES) : xb[u];
+      const uint4 xf = mask4(xv, k < kend);
 #pragma unroll
       for (int w = 0; w < NW; ++w) acc[w] = mma16(xf, wb[u][w], acc[w], T());
     }
@@ -145,6 +159,26 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   // three batches are peeled so that no load is issued past the slice.
   uint4 wa[BU][NW], xa[BU], wbf[BU][NW], xbf[BU];
   load(wa, xa, 0);
+  if (XL) {
+    // stage X: the threads of lane column c (4 per wave) copy row c, all of a
+    // thread's pieces loaded before any is stored (loads clamped, stores guarded)
+    constexpr int SPT = 9;
+    const int npc = K / PER, tix = wave * 4 + g, nth = (int)(blockDim.x >> 4);
+    for (int i0 = tix; i0 < npc; i0 += nth * SPT) {
+      uint4 v[SPT];
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const int k = min(i0 + u * nth, npc - 1) * PER;
+        v[u] = ld16(k < kswitch ? x0 + k : x1 + (k - kswitch));
+      }
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const int i = i0 + u * nth;
+        if (i < npc) *(uint4*)(dyn + c * XST + i * 16) = v[u];
+      }
+    }
+    __syncthreads();
+  }
   int b = 0;
   for (; b + 3 < nb; b += 2) {
     load(wbf, xbf, b + 1);
@@ -173,8 +207,9 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   }
 
   // ---- K slices meet in LDS; wave (ct, slice 0) sums them in slice order
+  if (XL) __syncthreads();  // every wave is done reading the X tile it overwrites
 #pragma unroll
-  for (int w = 0; w < NW; ++w) red[wave][w][lane] = acc[w];
+  for (int w = 0; w < NW; ++w) red[(wave * NW + w) * WAVE + lane] = acc[w];
   if (OP == OP_GATEUP) {  // RMSNorm sums: this thread's partials, then the wave's 4 per row
     float s = 0.f;
 #pragma unroll
@@ -193,7 +228,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   if (fin)
     for (int s = 0; s < p.KSW; ++s)
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v[w] += red[s * p.CT + ct][w][lane];
+      for (int w = 0; w < NW; ++w) v[w] += red[((s * p.CT + ct) * NW + w) * WAVE + lane];
 
   // ---- epilogues; lane holds rows 4g..4g+3 of column n
   if (OP == OP_FC) {
@@ -297,15 +332,27 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   }
 }
 
+template <typename T, int OP>
+static void launch_sk_op(const RoundArgs& a, const SkPlan& p, hipStream_t s) {
+  constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
+  const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
+  const size_t red = (size_t)WAVE * p.CT * p.KSW * NW * sizeof(f32x4_t);
+  if (p.xlds) {
+    const size_t xb = (size_t)16 * (p.K * sizeof(T) + 16);
+    hipLaunchKernelGGL((k_skinny<T, OP, true>), grid, block, xb > red ? xb : red, s, a, p);
+  } else {
+    hipLaunchKernelGGL((k_skinny<T, OP, false>), grid, block, red, s, a, p);
+  }
+}
+
 template <typename T>
 static hipError_t launch_sk_t(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s) {
-  const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
   switch (op) {
-    case OP_FC: hipLaunchKernelGGL((k_skinny<T, OP_FC>), grid, block, 0, s, a, p); break;
-    case OP_QKV: hipLaunchKernelGGL((k_skinny<T, OP_QKV>), grid, block, 0, s, a, p); break;
-    case OP_O: hipLaunchKernelGGL((k_skinny<T, OP_O>), grid, block, 0, s, a, p); break;
-    case OP_GATEUP: hipLaunchKernelGGL((k_skinny<T, OP_GATEUP>), grid, block, 0, s, a, p); break;
-    default: hipLaunchKernelGGL((k_skinny<T, OP_DOWN>), grid, block, 0, s, a, p); break;
+    case OP_FC: launch_sk_op<T, OP_FC>(a, p, s); break;
+    case OP_QKV: launch_sk_op<T, OP_QKV>(a, p, s); break;
+    case OP_O: launch_sk_op<T, OP_O>(a, p, s); break;
+    case OP_GATEUP: launch_sk_op<T, OP_GATEUP>(a, p, s); break;
+    default: launch_sk_op<T, OP_DOWN>(a, p, s); break;
   }
   return hipGetLastError();
 }

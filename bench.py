@@ -54,7 +54,7 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-LMHEAD_SOURCES = ("k_lmhead.hip", "eagle_internal.h")
+LMHEAD_SOURCES = ("k_lmhead.hip", "skinny_core.h", "eagle_internal.h")
 
 
 def stored_traffic(workload: str):
@@ -245,7 +245,7 @@ def main() -> int:
         "tree_tokens_per_s": round(rounds_s * cfg.B * cfg.m, 1),
         "round_hbm": {"algorithmic_bytes": int(round_bytes), "achieved": round(round_gbps, 1),
                       "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(round_gbps / HBM_PEAK_GBPS, 4)},
-        "roofline": {"kernel": "k_lmhead (LM-head GEMM + per-slab softmax/top-k)",
+        "roofline": {"kernel": "k_lmskinny (LM-head GEMM + per-slab softmax/top-k)",
                      "bound": "hbm", "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
                      "avg_launch_us": round(lm_ms * 1e3, 2),

@@ -6,7 +6,7 @@
 
 #include <algorithm>
 
-#include "eagle_internal.h"
+#include "skinny_core.h"
 
 namespace eg {
 
@@ -24,6 +24,8 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 size_t elem_size(const eagle_dims& d) { return d.dtype == EAGLE_BF16 ? 2 : 4; }
+
+static constexpr size_t SK_XLDS_MAX = 140 * 1024;  // LDS for a staged X tile (of 160 KB per CU)
 
 // Workgroups a weight-streaming launch aims for: two per compute unit (eight
 // waves) keeps enough 16-byte loads in flight to cover HBM latency.
@@ -57,8 +59,6 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   return p;
 }
 
-static constexpr size_t SK_XLDS_MAX = 140 * 1024;  // LDS for a staged X tile (of 160 KB per CU)
-
 // Level GEMMs (at most 16 rows): about one workgroup per compute unit, each
 // with up to 16 waves that split K; column tiles per workgroup grow with N.
 SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
@@ -79,7 +79,8 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   p.nps = 0;
   // the X tile is staged in LDS when it fits and is shared by at least two
   // weight streams (with one, staging costs as much as it saves)
-  p.xlds = p.CT * nw >= 2 && (size_t)16 * (p.K * elem_size(d) + 16) <= SK_XLDS_MAX;
+  // (not the FC, whose X rows are gathered from two sources)
+  p.xlds = op != OP_FC && p.CT * nw >= 2 && sk_xtile_bytes(p.K, (int)elem_size(d)) <= SK_XLDS_MAX;
   return p;
 }
 
@@ -90,7 +91,17 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
   p.M = M;
   p.mt = std::min(4, cdiv(std::min(M, 64), 16));
   p.zg = cdiv(M, 64);
-  p.nblk = cdiv(d.vocab, 64);
+  p.sk = M <= 16;
+  if (p.sk) {  // slabs of CT*16 columns, about one workgroup per compute unit
+    const int ntile = cdiv(d.vocab, 16);
+    const int nks = cdiv(d.d, d.dtype == EAGLE_BF16 ? 32 : 16);
+    p.CT = std::max(1, std::min(SK_MAXW, cdiv(ntile, 256)));
+    p.KSW = std::max(1, std::min(SK_MAXW / p.CT, nks / 32));
+    p.nblk = cdiv(ntile, p.CT);
+    p.xlds = p.CT >= 2 && sk_xtile_bytes(d.d, (int)elem_size(d)) <= SK_XLDS_MAX;
+  } else {
+    p.nblk = cdiv(d.vocab, 64);
+  }
   p.rec = 2 + 2 * topk;
   p.G = std::max(1, std::min(p.nblk, 8192 / topk));
   p.part_floats = (size_t)M * p.nblk * p.rec;

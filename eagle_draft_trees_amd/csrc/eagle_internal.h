@@ -179,8 +179,9 @@ struct SkPlan {
 };
 
 struct LmPlan {
-  int M, mt, zg, nblk, rec;  // rec = floats per (row, block) partial
+  int M, mt, zg, nblk, rec;  // rec = floats per (row, slab) partial; nblk = slabs
   int G;                     // slab lists merged per LDS pass in the merge kernel
+  int sk, CT, KSW, xlds;     // sk: streaming-core kernel (M <= 16), CT tiles x KSW waves
   size_t part_floats;
 };
 

@@ -22,7 +22,7 @@
 // best k by (score desc, pool index asc) as the next frontier.
 #include <float.h>
 
-#include "eagle_internal.h"
+#include "skinny_core.h"
 
 namespace eg {
 
@@ -161,6 +161,90 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
     if (rank < kk_) {
       rec[2 + rank] = x;
       rec[2 + kk_ + rank] = __int_as_float(x == -INFINITY ? -1 : blk * 64 + lane);
+    }
+  }
+}
+
+// LM head for at most 16 rows (drafting levels and level 1): the level GEMMs'
+// streaming core over 16-column tiles of the vocabulary.  A workgroup holds CT
+// tiles (one slab of CT*16 columns) and splits K over KSW waves per tile; X
+// (the rows' features) is staged in LDS when it fits.  The slab's logits meet
+// in LDS and one wave per row reduces them to the slab record (max, sum exp,
+// top-k by (logit desc, id asc) from k rounds of a 64-bit key argmax).
+template <typename T, bool XL>
+__global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan p, int level) {
+  constexpr int KS = El<T>::KSTEP;
+  constexpr int BU = 4;
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwv = (int)(blockDim.x >> 6);
+  const int ct = wave % p.CT, ks = wave / p.CT;
+  const int t = blockIdx.x * p.CT + ct;
+  const int c = lane & 15, g = lane >> 4;
+  const int K = a.d, kk_ = a.k;
+  const int n = t * 16 + c;
+  const bool nv = n < a.V;
+  const T* const wr[1] = {(const T*)a.lm_head + (size_t)(nv ? n : 0) * K};
+  const T* xbase = (level == 1) ? (const T*)a.root_feat
+                                : (const T*)a.feat + (size_t)(level - 1) * a.B * kk_ * K;
+  const T* x0 = xbase + (size_t)(c < p.M ? c : 0) * K;  // rows past M repeat row 0 (discarded)
+  const int nks = (K + KS - 1) / KS;
+  const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
+  f32x4_t acc[1];
+  sk_stream<T, 1, BU, XL>(wr, x0, x0, K, K, s0k, s1k, dyn, acc, xbase, p.M);
+
+  // K slices meet in LDS (over the X tile, once every wave is done with it),
+  // then the slab's logits [16 rows][CT*16 columns]
+  if (XL) __syncthreads();
+  f32x4_t* red = (f32x4_t*)dyn;
+  float* lg = (float*)(dyn + (size_t)nwv * WAVE * sizeof(f32x4_t));
+  const int ncol = p.CT * 16, LW = ncol + 1;
+  red[wave * WAVE + lane] = acc[0];
+  __syncthreads();
+  if (ks == 0) {
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.KSW; ++s) v += red[(s * p.CT + ct) * WAVE + lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lg[(4 * g + r) * LW + ct * 16 + c] = nv ? v[r] : -INFINITY;
+  }
+  __syncthreads();
+
+  // one wave per row: up to four columns per lane
+  const int col0 = blockIdx.x * ncol;
+  for (int row = wave; row < p.M; row += nwv) {
+    float x[4];
+    unsigned long long key[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = lane + 64 * u;
+      x[u] = j < ncol ? lg[row * LW + j] : -INFINITY;
+      key[u] = x[u] == -INFINITY ? 0ull : argkey(x[u], col0 + j);
+      mx = fmaxf(mx, x[u]);
+    }
+    mx = wave_max_dpp(mx);
+    float se = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) se += x[u] == -INFINITY ? 0.f : expf(x[u] - mx);
+    se = wave_sum_dpp(se);
+    float* rec = a.lmpart + ((size_t)row * p.nblk + blockIdx.x) * p.rec;
+    if (lane == 0) {
+      rec[0] = mx;
+      rec[1] = se;
+    }
+    for (int r = 0; r < kk_; ++r) {
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) best = key[u] > best ? key[u] : best;
+      const unsigned long long win = wave_max_u64(best);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (key[u] == win) key[u] = 0ull;  // keys are unique: one owner
+      if (lane == 0) {
+        rec[2 + r] = win ? argkey_value(win) : -INFINITY;
+        rec[2 + kk_ + r] = __int_as_float(win ? argkey_id(win) : -1);
+      }
     }
   }
 }
@@ -395,7 +479,21 @@ static hipError_t launch_lm_t(const RoundArgs& a, const LmPlan& p, int level, hi
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_lmsk_t(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
+  const int nwv = p.CT * p.KSW;
+  const size_t epi = (size_t)nwv * WAVE * sizeof(f32x4_t) + (size_t)16 * (p.CT * 16 + 1) * sizeof(float);
+  if (p.xlds) {
+    const size_t xb = sk_xtile_bytes(a.d, (int)sizeof(T));
+    hipLaunchKernelGGL((k_lmskinny<T, true>), dim3(p.nblk), dim3(nwv * WAVE), xb > epi ? xb : epi, s, a, p, level);
+  } else {
+    hipLaunchKernelGGL((k_lmskinny<T, false>), dim3(p.nblk), dim3(nwv * WAVE), epi, s, a, p, level);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
+  if (p.sk) return a.dtype == EAGLE_BF16 ? launch_lmsk_t<bf16_t>(a, p, level, s) : launch_lmsk_t<float>(a, p, level, s);
   return a.dtype == EAGLE_BF16 ? launch_lm_t<bf16_t>(a, p, level, s)
                                : launch_lm_t<float>(a, p, level, s);
 }

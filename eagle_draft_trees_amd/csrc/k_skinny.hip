@@ -29,7 +29,7 @@
 // Draft layer of [P1] "EAGLE 推测解码为什么比 Medusa 快？" §4.1 and [P3]
 // zdszero.github.io spec_medusa_eagle, "在 SGLang 里"; tree positions of the
 // RoPE step per [P1] §12 item 5 (positions shared per level).
-#include "eagle_internal.h"
+#include "skinny_core.h"
 
 namespace eg {
 
@@ -49,8 +49,6 @@ template <typename T, int OP, bool XL>
 __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;  // weight streams per wave (gate and up)
   constexpr int KS = El<T>::KSTEP;
-  constexpr int PER = El<T>::PER16;
-  constexpr int ES = (int)sizeof(T);
   constexpr int BU = (NW == 2) ? 3 : 4;  // k-steps per load batch
   // dynamic LDS: the X tile [16][K] (row stride K*ES + 16 bytes, so the 16
   // rows of one read fall in different banks), then reused for the K-slice
@@ -120,91 +118,11 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
       sqv[u] = a.ssq[(size_t)min(qj + u * QJ, p.nps - 1) * a.rows + min(qrow, p.M - 1)];
   }
 
-  // ---- this wave's K slice: k-steps [s0k, s1k), elements [.., kend)
+  // ---- this wave's K slice: k-steps [s0k, s1k)
   const int nks = (K + KS - 1) / KS;
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
-  const int kend = min(K, s1k * KS);
-  const int nb = (s1k - s0k + BU - 1) / BU;
-  const int klast = K - PER;
-
   f32x4_t acc[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int XST = K * ES + 16;  // LDS row stride of the X tile (XL)
-  const unsigned char* xrow = dyn + c * XST;
-  auto load = [&](uint4 (&wb)[BU][NW], uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int kc = min((s0k + b * BU + u) * KS + g * PER, klast);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + kc);
-      if (!XL) xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
-    }
-  };
-  auto comp = [&](const uint4 (&wb)[BU][NW], const uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int k = (s0k + b * BU + u) * KS + g * PER;
-      const uint4 xv = XL ? *(const uint4*)(xrow + min(k, klast) * ES) : xb[u];
-      const uint4 xf = mask4(xv, k < kend);
-#pragma unroll
-      for (int w = 0; w < NW; ++w) acc[w] = mma16(xf, wb[u][w], acc[w], T());
-    }
-  };
-
-  // Two batches in flight: the scheduling barriers keep each batch of loads
-  // ahead of the MFMAs on the other buffer; the loop body is one straight
-  // block, so the compiler's wait counts stay exact, and the last one to
-  // three batches are peeled so that no load is issued past the slice.
-  uint4 wa[BU][NW], xa[BU], wbf[BU][NW], xbf[BU];
-  load(wa, xa, 0);
-  if (XL) {
-    // stage X: the threads of lane column c (4 per wave) copy row c, all of a
-    // thread's pieces loaded before any is stored (loads clamped, stores guarded)
-    constexpr int SPT = 9;
-    const int npc = K / PER, tix = wave * 4 + g, nth = (int)(blockDim.x >> 4);
-    for (int i0 = tix; i0 < npc; i0 += nth * SPT) {
-      uint4 v[SPT];
-#pragma unroll
-      for (int u = 0; u < SPT; ++u) {
-        const int k = min(i0 + u * nth, npc - 1) * PER;
-        v[u] = ld16(k < kswitch ? x0 + k : x1 + (k - kswitch));
-      }
-#pragma unroll
-      for (int u = 0; u < SPT; ++u) {
-        const int i = i0 + u * nth;
-        if (i < npc) *(uint4*)(dyn + c * XST + i * 16) = v[u];
-      }
-    }
-    __syncthreads();
-  }
-  int b = 0;
-  for (; b + 3 < nb; b += 2) {
-    load(wbf, xbf, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, xa, b);
-    load(wa, xa, b + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wbf, xbf, b + 1);
-  }
-  const int rem = nb - b;
-  if (rem == 1) {
-    comp(wa, xa, b);
-  } else if (rem == 2) {
-    load(wbf, xbf, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, xa, b);
-    comp(wbf, xbf, b + 1);
-  } else if (rem == 3) {
-    load(wbf, xbf, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, xa, b);
-    load(wa, xa, b + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wbf, xbf, b + 1);
-    comp(wa, xa, b + 2);
-  }
+  sk_stream<T, NW, BU, XL>(wr, x0, x1, kswitch, K, s0k, s1k, dyn, acc, x0 - (size_t)xr * K, p.M);
 
   // ---- K slices meet in LDS; wave (ct, slice 0) sums them in slice order
   if (XL) __syncthreads();  // every wave is done reading the X tile it overwrites
@@ -338,7 +256,7 @@ static void launch_sk_op(const RoundArgs& a, const SkPlan& p, hipStream_t s) {
   const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
   const size_t red = (size_t)WAVE * p.CT * p.KSW * NW * sizeof(f32x4_t);
   if (p.xlds) {
-    const size_t xb = (size_t)16 * (p.K * sizeof(T) + 16);
+    const size_t xb = sk_xtile_bytes(p.K, (int)sizeof(T));
     hipLaunchKernelGGL((k_skinny<T, OP, true>), grid, block, xb > red ? xb : red, s, a, p);
   } else {
     hipLaunchKernelGGL((k_skinny<T, OP, false>), grid, block, red, s, a, p);

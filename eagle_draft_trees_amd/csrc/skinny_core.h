@@ -1,0 +1,120 @@
+// Weight-streaming core shared by the level GEMMs (k_skinny.hip) and the
+// LM head (k_lmhead.hip) at drafting shapes, where at most 16 rows of X meet
+// a weight matrix that is read exactly once.
+//
+// One wave streams NW weight-row tiles (16 rows = 16 output columns each,
+// 16 rows x 64 contiguous bytes per wave load instruction) over its K slice,
+// k-steps [s0k, s1k), into 16x16 MFMA accumulators.  BU k-steps form a load
+// batch and two batches are in flight (ping-pong register sets).  Loads are
+// unconditional from clamped in-bounds addresses (products past the slice are
+// masked to zero), the steady-state loop body is one straight block, and the
+// last one to three batches are peeled: all so that the compiler's wait
+// counts stay exact and no load waits behind a needless drain.
+//
+// X is either staged once in LDS (XL: its 16 rows, row stride K*ES + 16 so
+// that the rows of one read fall in different banks; staged while the first
+// weight batch is in flight) or loaded per k-step from L2.  X loads share the
+// memory queue with the weight loads and cost a quarter to a third of the
+// streaming rate, so the LDS copy is used wherever it fits and is shared.
+#pragma once
+#include "eagle_internal.h"
+
+namespace eg {
+
+// Row c of X (c = lane % 16) is x0[k] for k < kswitch and x1[k - kswitch]
+// beyond (the FC's gathered [feature || embedding] input); callers with one
+// source pass x1 = x0 and kswitch = K.  With XL, X must be M contiguous rows
+// of stride K starting at xs (only those rows are staged: LDS rows past M
+// keep stale values, which reach only the discarded output rows past M), and
+// every thread of the block must call this (it stages X and synchronises).
+template <typename T, int NW, int BU, bool XL>
+__device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0, const T* x1, int kswitch,
+                                          int K, int s0k, int s1k, unsigned char* dyn,
+                                          f32x4_t (&acc)[NW], const T* xs = nullptr, int M = 16) {
+  constexpr int KS = El<T>::KSTEP;
+  constexpr int PER = El<T>::PER16;
+  constexpr int ES = (int)sizeof(T);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int kend = min(K, s1k * KS);
+  const int nb = (s1k - s0k + BU - 1) / BU;
+  const int klast = K - PER;
+  const int XST = K * ES + 16;
+  const unsigned char* xrow = dyn + c * XST;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto load = [&](uint4 (&wb)[BU][NW], uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int kc = min((s0k + b * BU + u) * KS + g * PER, klast);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + kc);
+      if (!XL) xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
+    }
+  };
+  auto comp = [&](const uint4 (&wb)[BU][NW], const uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int k = (s0k + b * BU + u) * KS + g * PER;
+      const uint4 xv = XL ? *(const uint4*)(xrow + min(k, klast) * ES) : xb[u];
+      const uint4 xf = mask4(xv, k < kend);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc[w] = mma16(xf, wb[u][w], acc[w], T());
+    }
+  };
+
+  uint4 wa[BU][NW], xa[BU], wbf[BU][NW], xbf[BU];
+  load(wa, xa, 0);
+  if (XL) {
+    // the M real rows, piece by piece over all threads; all of a thread's
+    // pieces are loaded before any is stored (loads clamped, stores guarded)
+    constexpr int SPT = 9;
+    const int npc = K / PER, tot = M * npc;
+    for (int i0 = (int)threadIdx.x; i0 < tot; i0 += (int)blockDim.x * SPT) {
+      uint4 v[SPT];
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const int i = min(i0 + u * (int)blockDim.x, tot - 1);
+        v[u] = ld16(xs + (size_t)(i / npc) * K + (i % npc) * PER);
+      }
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {
+        const int i = i0 + u * (int)blockDim.x;
+        if (i < tot) *(uint4*)(dyn + (i / npc) * XST + (i % npc) * 16) = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  int b = 0;
+  for (; b + 3 < nb; b += 2) {
+    load(wbf, xbf, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, xa, b);
+    load(wa, xa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbf, xbf, b + 1);
+  }
+  const int rem = nb - b;
+  if (rem == 1) {
+    comp(wa, xa, b);
+  } else if (rem == 2) {
+    load(wbf, xbf, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, xa, b);
+    comp(wbf, xbf, b + 1);
+  } else if (rem == 3) {
+    load(wbf, xbf, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, xa, b);
+    load(wa, xa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbf, xbf, b + 1);
+    comp(wa, xa, b + 2);
+  }
+}
+
+// Bytes of X tile staged by sk_stream<XL = true>.
+__host__ __device__ inline size_t sk_xtile_bytes(int K, int es) { return (size_t)16 * ((size_t)K * es + 16); }
+
+}  // namespace eg

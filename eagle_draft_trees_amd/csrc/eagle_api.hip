@@ -103,7 +103,6 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
     p.nblk = cdiv(d.vocab, 64);
   }
   p.rec = 2 + 2 * topk;
-  p.G = std::max(1, std::min(p.nblk, 8192 / topk));
   p.part_floats = (size_t)M * p.nblk * p.rec;
   return p;
 }

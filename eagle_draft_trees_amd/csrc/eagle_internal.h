@@ -126,6 +126,24 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
   return r;
 }
 
+// maximum over the wave of unsigned 32-bit values (0 is the identity); every lane gets it
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) v = max(v, dpp_u32(v, s));
+  unsigned r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) r = max(r, (unsigned)__builtin_amdgcn_readlane(v, row * 16 + 15));
+  return r;
+}
+// the same maximum as wave_max_u64, from two 32-bit reductions: the high
+// words, then the low words of the lanes that hold the highest high word
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  const unsigned hi = (unsigned)(k >> 32);
+  const unsigned mh = wave_max_u32(hi);
+  const unsigned ml = wave_max_u32(hi == mh ? (unsigned)k : 0u);
+  return ((unsigned long long)mh << 32) | ml;
+}
+
 __device__ __forceinline__ float wave_sum_dpp(float v) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) v += __uint_as_float(dpp_u32(__float_as_uint(v), s));
@@ -180,7 +198,6 @@ struct SkPlan {
 
 struct LmPlan {
   int M, mt, zg, nblk, rec;  // rec = floats per (row, slab) partial; nblk = slabs
-  int G;                     // slab lists merged per LDS pass in the merge kernel
   int sk, CT, KSW, xlds;     // sk: streaming-core kernel (M <= 16), CT tiles x KSW waves
   size_t part_floats;
 };

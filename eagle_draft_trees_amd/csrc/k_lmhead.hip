@@ -1,11 +1,9 @@
-// Frozen LM head + softmax + top-k + EAGLE-2 expansion.
+// Frozen LM head + softmax + top-k, per vocabulary slab.
 //
 // [P1] "EAGLE 推测解码为什么比 Medusa 快？（含 EAGLE-2 动态草稿树）" §4.1: the draft
-// distribution is softmax(LM_Head(f-hat)); §10.3: a node's value is the product
-// of confidences on its root path, each level expands the best k nodes.
-// [P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里": select_top_k_tokens
-// multiplies the running score by this level's top-k probabilities and keeps
-// the best topk of topk^2.  Scores are kept as sums of log-probabilities.
+// distribution is softmax(LM_Head(f-hat)), and each level keeps the top-k
+// tokens of every expanded node.  The slab records written here are merged
+// into the rows' log-sum-exp and top-k by k_lmmerge.
 //
 // k_lmhead (one launch over the vocabulary): four waves per workgroup each
 // stream 16 LM-head rows against the M feature rows (MFMA, A operand from
@@ -13,13 +11,6 @@
 // MFMAs); the 64-column logit tile goes to LDS and each row's slab is reduced
 // to (max, sum exp) and its top-k (logit desc, id asc).  Logits never leave
 // the chip.
-// k_lmmerge (one workgroup per row): combines the slabs' (max, sum) into a
-// log-sum-exp, merges the sorted slab lists in LDS by block-wide argmax rounds
-// and writes (id, log p = logit - lse).  Then per sequence: level 1 puts the
-// root's k children into the pool and frontier; for level L >= 2 the last row
-// of a sequence to finish scores the k*k children (parent score + log p),
-// appends all of them to the pool in (frontier slot, rank) order and keeps the
-// best k by (score desc, pool index asc) as the next frontier.
 #include <float.h>
 
 #include "skinny_core.h"
@@ -237,7 +228,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
       unsigned long long best = 0ull;
 #pragma unroll
       for (int u = 0; u < 4; ++u) best = key[u] > best ? key[u] : best;
-      const unsigned long long win = wave_max_u64(best);
+      const unsigned long long win = wave_max_key(best);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (key[u] == win) key[u] = 0ull;  // keys are unique: one owner
@@ -245,224 +236,6 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
         rec[2 + r] = win ? argkey_value(win) : -INFINITY;
         rec[2 + kk_ + r] = __int_as_float(win ? argkey_id(win) : -1);
       }
-    }
-  }
-}
-
-constexpr int LM_CAND = 8192;  // (logit, id) candidates held in LDS by the merge
-
-// maximum over the block of a 64-bit key; `slot` alternates between calls so a
-// single barrier per call suffices
-__device__ __forceinline__ unsigned long long block_max_u64(unsigned long long k,
-                                                            unsigned long long* red, int slot) {
-  k = wave_max_u64(k);
-  if ((threadIdx.x & 63) == 0) red[slot * 4 + (threadIdx.x >> 6)] = k;
-  __syncthreads();
-  unsigned long long r = red[slot * 4];
-#pragma unroll
-  for (int w = 1; w < BLOCK / WAVE; ++w) r = red[slot * 4 + w] > r ? red[slot * 4 + w] : r;
-  return r;
-}
-
-__global__ void __launch_bounds__(BLOCK) k_lmmerge(RoundArgs a, LmPlan p, int level) {
-  __shared__ unsigned long long ck[LM_CAND + EAGLE_MAX_TOPK];  // slab lists as keys
-  __shared__ unsigned short head[LM_CAND + 1];                 // next entry of each list
-  __shared__ unsigned long long rk[EAGLE_MAX_TOPK];            // running top-k
-  __shared__ unsigned long long red[8];
-  __shared__ float redm[BLOCK / WAVE], reds[BLOCK / WAVE];
-  __shared__ float sres[EAGLE_MAX_TOPK * 2 * EAGLE_MAX_TOPK];
-  __shared__ int sanc[EAGLE_MAX_TOPK * EAGLE_MAX_DEPTH];
-  __shared__ float psc[EAGLE_MAX_TOPK];
-  __shared__ int ppi[EAGLE_MAX_TOPK];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = blockIdx.x, kk_ = a.k;
-  const float* base = a.lmpart + (size_t)row * p.nblk * p.rec;
-
-  // log-sum-exp over the slabs, combined in a fixed order
-  float M = -INFINITY, S = 0.f;
-  for (int bb = tid; bb < p.nblk; bb += BLOCK) {
-    const float mb = base[(size_t)bb * p.rec], sb = base[(size_t)bb * p.rec + 1];
-    if (mb == -INFINITY) continue;
-    const float nm = fmaxf(M, mb);
-    S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + sb * expf(mb - nm);
-    M = nm;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float oM = __shfl_xor(M, o), oS = __shfl_xor(S, o);
-    const float nm = fmaxf(M, oM);
-    if (nm != -INFINITY) {
-      S = (M == -INFINITY ? 0.f : S * expf(M - nm)) + (oM == -INFINITY ? 0.f : oS * expf(oM - nm));
-      M = nm;
-    }
-  }
-  if (lane == 0) { redm[wave] = M; reds[wave] = S; }
-  __syncthreads();
-  if (tid == 0) {
-    float m0 = redm[0], s0 = reds[0];
-    for (int w = 1; w < BLOCK / WAVE; ++w) {
-      const float nm = fmaxf(m0, redm[w]);
-      s0 = (m0 == -INFINITY ? 0.f : s0 * expf(m0 - nm)) +
-           (redm[w] == -INFINITY ? 0.f : reds[w] * expf(redm[w] - nm));
-      m0 = nm;
-    }
-    redm[0] = m0 + logf(s0);
-  }
-  __syncthreads();
-  const float lse = redm[0];
-
-  // top-k: the slab lists are sorted, so each round only compares list heads;
-  // p.G lists per LDS pass, the running list joins each pass as one more list
-  int nr = 0, slot = 0;
-  for (int g0 = 0; g0 < p.nblk; g0 += p.G) {
-    const int gn = min(p.G, p.nblk - g0);
-    const int nc = gn * kk_;
-    for (int i0 = tid; i0 < nc; i0 += 8 * BLOCK) {
-      float vv[8];
-      int ii[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = i0 + u * BLOCK;
-        vv[u] = -INFINITY;
-        ii[u] = -1;
-        if (idx < nc) {
-          const float* rec = base + (size_t)(g0 + idx / kk_) * p.rec;
-          const int j = idx % kk_;
-          vv[u] = rec[2 + j];
-          ii[u] = __float_as_int(rec[2 + kk_ + j]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = i0 + u * BLOCK;
-        if (idx < nc) ck[idx] = ii[u] < 0 ? 0ull : argkey(vv[u], ii[u]);
-      }
-    }
-    const int nl = gn + (nr ? 1 : 0);  // lists in this pass
-    if (tid < nr) ck[nc + tid] = rk[tid];
-    for (int l = tid; l < nl; l += BLOCK) head[l] = 0;
-    __syncthreads();
-    for (int r = 0; r < kk_; ++r) {
-      unsigned long long best = 0;
-      int bl = -1;
-      for (int l = tid; l < nl; l += BLOCK) {
-        const int h = head[l];
-        if (h < kk_) {
-          const unsigned long long kv = ck[l * kk_ + h];
-          if (kv > best) { best = kv; bl = l; }
-        }
-      }
-      const unsigned long long win = block_max_u64(best, red, slot);
-      slot ^= 1;
-      if (bl >= 0 && best == win && win != 0ull) head[bl]++;  // keys are unique: one owner
-      if (tid == 0) rk[r] = win;
-    }
-    nr = kk_;
-    __syncthreads();
-  }
-  __shared__ float rv[EAGLE_MAX_TOPK];
-  __shared__ int ri[EAGLE_MAX_TOPK];
-  if (tid < kk_) {
-    const unsigned long long w = rk[tid];
-    rv[tid] = w ? argkey_value(w) : -INFINITY;
-    ri[tid] = w ? argkey_id(w) : INT_MAX;
-  }
-  __syncthreads();
-  float* res = a.lmres + (size_t)row * 2 * kk_;
-  if (tid < kk_) {
-    res[tid] = __int_as_float(ri[tid] == INT_MAX ? 0 : ri[tid]);
-    res[kk_ + tid] = rv[tid] - lse;
-  }
-
-  // ---- expansion and select
-  const int pn = a.pool_n;
-  if (level == 1) {
-    const int b = row;
-    eagle_pool_entry* pool = a.pool + (size_t)b * pn;
-    eagle_frontier_node* fnew = a.frontier + ((size_t)1 * a.B + b) * kk_;
-    if (tid < kk_) {
-      const int id = ri[tid] == INT_MAX ? 0 : ri[tid];
-      const float lp = rv[tid] - lse;
-      pool[tid] = eagle_pool_entry{lp, lp, id, -1, 1, -1};
-      eagle_frontier_node nd;
-      nd.token = id;
-      nd.score = lp;
-      nd.pool_idx = tid;
-      nd.pslot = -1;
-      for (int i = 0; i < EAGLE_MAX_DEPTH; ++i) nd.anc[i] = 0;
-      nd.anc[0] = tid;
-      fnew[tid] = nd;
-    }
-    return;
-  }
-  const int b = row / kk_;
-  if (!arrive_last(a.cnt + b, kk_)) return;
-  // stage the parent frontier and every row's (id, log p) in LDS with one
-  // parallel pass, so the select below touches no global memory in its rounds
-  const eagle_frontier_node* fprev = a.frontier + ((size_t)(level - 1) * a.B + b) * kk_;
-  for (int idx = tid; idx < kk_ * 2 * kk_; idx += BLOCK)
-    sres[idx] = a.lmres[(size_t)b * kk_ * 2 * kk_ + idx];
-  for (int idx = tid; idx < kk_ * EAGLE_MAX_DEPTH; idx += BLOCK)
-    sanc[idx] = fprev[idx / EAGLE_MAX_DEPTH].anc[idx % EAGLE_MAX_DEPTH];
-  if (tid < kk_) {
-    psc[tid] = fprev[tid].score;
-    ppi[tid] = fprev[tid].pool_idx;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  eagle_pool_entry* pool = a.pool + (size_t)b * pn;
-  eagle_frontier_node* fnew = a.frontier + ((size_t)level * a.B + b) * kk_;
-  const int pbase = kk_ + (level - 2) * kk_ * kk_;
-  const int nc = kk_ * kk_;
-  float sc[4];
-  int tk[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int c = lane + 64 * t;
-    sc[t] = -INFINITY;
-    tk[t] = 0;
-    if (c < nc) {
-      const int j = c / kk_, r = c % kk_;
-      const float* rr = sres + j * 2 * kk_;
-      const int id = __float_as_int(rr[r]);
-      const float lp = rr[kk_ + r];
-      const float s = psc[j] + lp;
-      sc[t] = s;
-      tk[t] = id;
-      pool[pbase + c] = eagle_pool_entry{s, lp, id, ppi[j], level, j};
-    }
-  }
-  for (int jn = 0; jn < kk_; ++jn) {
-    unsigned long long best = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int c = lane + 64 * t;
-      if (c < nc) {
-        const unsigned long long kv = sc[t] == -INFINITY ? 0ull : argkey(sc[t], c);
-        best = kv > best ? kv : best;
-      }
-    }
-    const unsigned long long win = wave_max_u64(best);  // (score desc, pool index asc)
-    if (win == 0ull) continue;  // fewer than k candidates (cannot happen: k*k >= k)
-    const float v = argkey_value(win);
-    const int id = argkey_id(win);
-    int own = 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (lane + 64 * t == id) { own = tk[t]; sc[t] = -INFINITY; }
-    own = __shfl(own, id & 63);
-    const int j = id / kk_;
-    if (lane < EAGLE_MAX_DEPTH) {
-      int av = (lane < level - 1) ? sanc[j * EAGLE_MAX_DEPTH + lane] : 0;
-      if (lane == level - 1) av = jn;
-      fnew[jn].anc[lane] = av;
-    }
-    if (lane == 0) {
-      fnew[jn].token = own;
-      fnew[jn].score = v;
-      fnew[jn].pool_idx = pbase + id;
-      fnew[jn].pslot = j;
     }
   }
 }
@@ -496,11 +269,6 @@ hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStre
   if (p.sk) return a.dtype == EAGLE_BF16 ? launch_lmsk_t<bf16_t>(a, p, level, s) : launch_lmsk_t<float>(a, p, level, s);
   return a.dtype == EAGLE_BF16 ? launch_lm_t<bf16_t>(a, p, level, s)
                                : launch_lm_t<float>(a, p, level, s);
-}
-
-hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
-  hipLaunchKernelGGL(k_lmmerge, dim3(p.M), dim3(BLOCK), 0, s, a, p, level);
-  return hipGetLastError();
 }
 
 }  // namespace eg

@@ -27,10 +27,9 @@ size_t elem_size(const eagle_dims& d) { return d.dtype == EAGLE_BF16 ? 2 : 4; }
 
 static constexpr size_t SK_XLDS_MAX = 140 * 1024;  // LDS for a staged X tile (of 160 KB per CU)
 
-// Workgroups a weight-streaming launch aims for: two per compute unit (eight
-// waves) keeps enough 16-byte loads in flight to cover HBM latency.
-static constexpr int TARGET_WG = 512;
-
+// Layer GEMMs at more than 16 rows (the extend, wide frontiers): 64 output
+// columns per workgroup, K split so that a split's X rows fit in LDS and the
+// grid covers the compute units.
 GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   GemmPlan p{};
   p.M = M;
@@ -46,16 +45,17 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   p.zg = cdiv(M, 64);
   p.nblk = cdiv(p.N, 64);
   const int ks = d.dtype == EAGLE_BF16 ? 32 : 16;
-  // a split's K range is whole pipeline iterations (8 k-steps)
-  const int unit = 8 * ks;
+  const int es = (int)elem_size(d);
+  // a split's K range is staged in LDS whole: at most GW_XPIECES 16-byte pieces
+  const int kcmax = std::max(ks, GW_XPIECES * 16 / (p.mt * 16 * es) / ks * ks);
   const int base = p.nblk * p.zg;
-  int S = std::min(cdiv(TARGET_WG, base), std::max(1, p.K / unit));
-  S = std::max(1, std::min(S, GEMM_MAXS));
-  const int Kc = cdiv(cdiv(p.K, S), unit) * unit;
-  S = cdiv(p.K, Kc);
-  p.S = S;
-  p.Kc = Kc;
-  p.part_floats = S > 1 ? (size_t)p.nblk * p.zg * S * 4 * p.nw * p.mt * 256 : 0;
+  int S = cdiv(p.K, kcmax);
+  // about one workgroup per compute unit at least (every K slice keeps a k-step)
+  S = std::max(S, std::min(cdiv(256, base), std::max(1, p.K / (4 * ks))));
+  p.Kc = cdiv(cdiv(p.K, S), ks) * ks;
+  p.S = cdiv(p.K, p.Kc);
+  p.nps = op == OP_GATEUP ? cdiv(d.d, 64) : 0;
+  p.part_floats = p.S > 1 ? (size_t)p.nblk * p.zg * p.S * 4 * p.nw * p.mt * 256 : 0;
   return p;
 }
 
@@ -206,7 +206,9 @@ static int check_cfg(const eagle_dims* d, const eagle_tree_cfg* c) {
       for (int M : {c->batch * c->topk, c->batch * c->m})
         if (plan_gemm(op, M, *d).S > GEMM_MAXS)
           return fail(EAGLE_ERR_UNSUPPORTED, "K too long for %d split-K ways", GEMM_MAXS);
-    const long blocks = (long)cdiv(d->ffn, 64) * cdiv(c->batch * c->m, 64);
+    long blocks = 0;
+    for (int op = OP_FC; op <= OP_DOWN; ++op)
+      blocks = std::max(blocks, (long)plan_gemm(op, c->batch * c->m, *d).nblk * cdiv(c->batch * c->m, 64));
     if (blocks >= GRID_CNT || (long)c->batch * c->m > 4096)
       return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", c->batch * c->m);
   }

@@ -17,7 +17,9 @@ constexpr int WAVE = 64;
 constexpr int BLOCK = 256;       // four waves
 constexpr int NCNT = 1 << 16;    // last-block counters in the workspace
 constexpr int GRID_CNT = NCNT - 1;
-constexpr int GEMM_MAXS = 16;    // split-K ways at most
+constexpr int GEMM_MAXS = 64;    // split-K ways at most
+constexpr int GW_THREADS = 1024;  // layer GEMM workgroup: 4 column tiles x 4 K slices
+constexpr int GW_XPIECES = 8192;  // 16-byte X pieces a layer GEMM workgroup stages at most
 
 enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
 enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1 };
@@ -184,8 +186,18 @@ struct WsLayout {
 
 struct GemmPlan {
   int M, N, K, nw, mt, zg, nblk, S, Kc;
+  int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
   size_t part_floats;  // split-K partial floats (0 when S == 1)
 };
+// dynamic LDS of a layer GEMM workgroup: the X tile, then the K-slice
+// partials, then the output tile and the RMSNorm partials
+inline size_t gemm_lds_bytes(const GemmPlan& p, int es) {
+  const size_t rows = (size_t)p.mt * 16;
+  const size_t xt = rows * ((size_t)p.Kc * es + 16);
+  const size_t red = (size_t)12 * p.nw * p.mt * 64 * 16;
+  const size_t tile = (size_t)p.nw * rows * 65 * 4 + rows * 16 * 4;
+  return xt > red ? (xt > tile ? xt : tile) : (red > tile ? red : tile);
+}
 
 // Level GEMM with at most 16 rows: CT column tiles of 16 per workgroup, K split
 // over KSW waves per tile (CT * KSW <= SK_MAXW waves), nwg workgroups.

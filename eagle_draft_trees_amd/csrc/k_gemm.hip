@@ -41,42 +41,74 @@ __device__ __forceinline__ int qkv_col(int blk, int c, int hd) {
 }
 
 template <typename T, int OP, int MT>
-__global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
+__global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
   constexpr int ES = (int)sizeof(T);
   constexpr int ROWS = MT * 16;
-  constexpr int XRB = (4096 / MT) & ~15;  // bytes of X per row in LDS per staged chunk
-  constexpr int XST = XRB + 16;   // LDS row stride: 16 rows of one m-tile hit disjoint banks
-  static_assert(NW * ROWS * 65 * 4 <= ROWS * XST, "epilogue tile aliases the X tile");
-  __shared__ __attribute__((aligned(16))) unsigned char xs[ROWS * XST];
+  constexpr int BU = NW == 2 ? 2 : 4;  // k-steps per weight load batch
+  constexpr int SPT = GW_XPIECES / GW_THREADS;
+  // X tile [ROWS][Kc] (row stride Kc*ES + 16 bytes: the 16 rows of an m-tile
+  // fall on different banks); then the K-slice partials; then the output tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
   __shared__ const T* rsrc[2][ROWS];
+  __shared__ float s_rstd[ROWS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ct = wave & 3, ks = wave >> 2;  // column tile, K slice
+  const int c = lane & 15, g = lane >> 4;
   const int blk = blockIdx.x, split = blockIdx.y, zg = blockIdx.z;
-  const int cl = wave * 16 + (lane & 15);
+  const int cl = ct * 16 + c;
   const int K = p.K;
 
   // ---- this lane's output column and weight rows
   int n;
-  bool nv;
   const T* wr[NW];
   if (OP == OP_QKV) {
     n = qkv_col(blk, cl, a.hd);
-    nv = true;
     const int hq = a.H * a.hd, hk = a.Hkv * a.hd;
     if (n < hq) wr[0] = (const T*)a.wq + (size_t)n * K;
     else if (n < hq + hk) wr[0] = (const T*)a.wk + (size_t)(n - hq) * K;
     else wr[0] = (const T*)a.wv + (size_t)(n - hq - hk) * K;
   } else {
     n = blk * 64 + cl;
-    nv = n < p.N;
-    const size_t off = (size_t)(nv ? n : 0) * K;
+    const size_t off = (size_t)(n < p.N ? n : 0) * K;
     if (OP == OP_FC) wr[0] = (const T*)a.fc_w + off;
     if (OP == OP_O) wr[0] = (const T*)a.wo + off;
     if (OP == OP_GATEUP) { wr[0] = (const T*)a.w_gate + off; wr[NW - 1] = (const T*)a.w_up + off; }
     if (OP == OP_DOWN) wr[0] = (const T*)a.w_down + off;
+  }
+
+  // gate/up: the RMSNorm statistic of this z-group's rows is the sum of the O
+  // launch's per-workgroup row partials; 16 threads per row each sum every
+  // 16th partial (loads issued now, used by the epilogue)
+  float ssq_part = 0.f;
+  if (OP == OP_GATEUP) {
+    const int r = tid >> 4, j = tid & 15, row = zg * 64 + r;
+    if (r < ROWS && row < p.M) {
+      for (int q0 = j; q0 < p.nps; q0 += 64) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int q = q0 + 16 * u;
+          v[u] = q < p.nps ? a.ssq[(size_t)q * a.rows + row] : 0.f;
+        }
+        ssq_part += (v[0] + v[1]) + (v[2] + v[3]);
+      }
+    }
+  }
+  // down, extend: the sequence state advances here (the prefix grows by the
+  // accepted length, the bonus token becomes the next root).  Nothing in this
+  // launch reads either field, so one workgroup does it without an election.
+  if (OP == OP_DOWN && a.mode == MODE_EXTEND && blk == 0 && split == 0 && zg == 0) {
+    for (int b = tid; b < a.B; b += GW_THREADS) {
+      int alen = a.accept_len[b];
+      alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
+      a.prefix_len[b] = clamp_prefix(a.prefix_len[b], a) + alen;
+      a.root_token[b] = clamp_tok(a.bonus[b], a.V, a.err);
+    }
   }
 
   // ---- X rows of this z-group; the FC gathers [parent feature || embed[token]]
@@ -127,8 +159,14 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
   }
   const int kswitch = (OP == OP_FC) ? a.d : K;
   const int k0 = split * p.Kc;
-  const int k1 = min(K, k0 + p.Kc);
-  const int kn = k1 - k0;
+  const int kn = min(K, k0 + p.Kc) - k0;  // this split's K range [k0, k0 + kn)
+  const int XST = p.Kc * ES + 16;
+  // this wave's k-steps [s0k, s1k) of the split (four K slices)
+  const int nks = (kn + KS - 1) / KS;
+  const int s0k = ks * nks / 4, s1k = (ks + 1) * nks / 4;
+  const int nb = (s1k - s0k + BU - 1) / BU;
+  const int kend = min(kn, s1k * KS);
+  const int klast = K - PER;
   __syncthreads();
 
   f32x4_t acc[NW][MT];
@@ -137,169 +175,174 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int kq = (lane >> 4) * PER;          // this lane group's k offset in a k-step
-  const unsigned char* xl = xs + (lane & 15) * XST + (lane >> 4) * 16;
-  // software pipeline: the next U k-steps' weights are in flight while the
-  // current U k-steps run on the MFMA units.  X is staged in LDS one chunk of
-  // KCH elements at a time (shared by the four waves).
-  constexpr int U = (MT * NW > 4) ? 4 : 8;
-  constexpr int KCH = (XRB / ES) / (2 * U * KS) * (2 * U * KS);
-  static_assert(KCH > 0, "X chunk");
-  const int nit = (kn + U * KS - 1) / (U * KS);
-  // X staging: a chunk is at most CPR 16-byte pieces per row, SB per thread,
-  // loaded SBB at a time (all of a batch before any is stored, so that their
-  // latencies overlap; smaller batches where registers are scarce).  Every
-  // slot loads and stores unconditionally: when the split needs fewer pieces
-  // than there are slots, the extra slots repeat real pieces (same address,
-  // same value, same LDS location), and rows past M read row 0 and store
-  // zeros, so no load is left in flight on any path.
-  constexpr int CPR = KCH / PER;
-  constexpr int SB = ROWS * CPR / BLOCK;
-  static_assert(SB * BLOCK == ROWS * CPR, "staging covers a chunk exactly");
-  constexpr int SBB = (MT * NW >= 3 && SB > 8) ? SB / 2 : SB;
-  static_assert(SB % SBB == 0, "staging batches");
-  uint4 xv[SBB];
-  int xo[SBB];
-  auto stage_load = [&](int kc, int b0) __attribute__((always_inline)) {
-    const int nch = max(min(KCH, kn - kc), PER) / PER, tot = ROWS * nch;
+  // Weight loads are unconditional from a clamped in-row address (a k-step
+  // beyond the slice reads valid memory whose product is masked to zero), so
+  // that the compiler keeps an exact count of loads in flight; two register
+  // buffers alternate, so the next batch is in flight while this one runs.
+  auto wload = [&](uint4 (&buf)[BU][NW], int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < SBB; ++u) {
-      const int idx = (tid + (b0 + u) * BLOCK) % tot;
-      const int r = idx / nch, c = idx - r * nch;
-      const int k = min(k0 + kc + c * PER, K - PER);
-      const T* s0 = rsrc[0][r];
-      const bool ok = s0 != nullptr && kc + c * PER < kn;
-      const int rr = s0 != nullptr ? r : 0;  // row 0 of the group always exists
-      const T* base = k < kswitch ? rsrc[0][rr] : rsrc[1][rr];
-      xv[u] = mask4(ld16g(base + (k < kswitch ? k : k - kswitch)), ok);
-      xo[u] = r * XST + c * 16;
-    }
-  };
-  auto stage_store = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < SBB; ++u) *(uint4*)(xs + xo[u]) = xv[u];
-  };
-  // Weight loads are unconditional from a clamped in-row address (k beyond
-  // this split reads valid memory whose product is masked to zero at use), so
-  // that the compiler can keep a precise count of loads in flight.  Two
-  // register buffers alternate (ping-pong): the loads of iteration it+1 are in
-  // flight while iteration it runs, and no register copy at the loop edge
-  // forces them to complete early.
-  const int klast = K - PER;
-  auto wload = [&](uint4 (&buf)[U][NW], int it) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < BU; ++u)
 #pragma unroll
       for (int w = 0; w < NW; ++w)
-        buf[u][w] = ld16(wr[w] + min(k0 + it * U * KS + u * KS + kq, klast));
+        buf[u][w] = ld16(wr[w] + min(k0 + (s0k + b * BU + u) * KS + g * PER, klast));
   };
-  auto compute = [&](const uint4 (&buf)[U][NW], int it, int kc) __attribute__((always_inline)) {
-    const int kb = it * U * KS;
+  const unsigned char* xl = xs + c * XST;
+  auto comp = [&](const uint4 (&buf)[BU][NW], int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kb + u * KS;
-      const bool kin = k + kq < kn;
+    for (int u = 0; u < BU; ++u) {
+      const int kk = (s0k + b * BU + u) * KS + g * PER;
+      const bool kin = kk < kend;
+      const int kx = min(kk, kn - PER) * ES;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xf = mask4(*(const uint4*)(xl + mt * 16 * XST + (k - kc) * ES), kin);
+        const uint4 xf = mask4(*(const uint4*)(xl + mt * 16 * XST + kx), kin);
 #pragma unroll
         for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, buf[u][w], acc[w][mt], T());
       }
     }
   };
-  uint4 wa[U][NW], wb[U][NW];
-  // first chunk's X loads go out before the first weight loads; both are in
-  // flight together
-  stage_load(0, 0);
-  wload(wa, 0);
-  stage_store();
+
+  // ---- X tile: the split's K range of every row, SPT 16-byte pieces per
+  // thread, all loaded before any is stored (rows past M are zeros); the
+  // first weight batch is issued behind them
+  uint4 wa[BU][NW], wb[BU][NW];
+  {
+    const int npc = kn / PER, tot = ROWS * npc;
+    uint4 v[SPT];
+    int o[SPT];
 #pragma unroll
-  for (int b0 = SBB; b0 < SB; b0 += SBB) {
-    stage_load(0, b0);
-    stage_store();
+    for (int u = 0; u < SPT; ++u) {
+      const int i = min(tid + u * GW_THREADS, tot - 1);
+      const int r = i / npc, pc = i - r * npc;
+      const int k = k0 + pc * PER;
+      const T* s0 = rsrc[0][r];
+      const int rr = s0 != nullptr ? r : 0;  // row 0 of the group always exists
+      const T* src = k < kswitch ? rsrc[0][rr] + k : rsrc[1][rr] + (k - kswitch);
+      v[u] = mask4(ld16g(src), s0 != nullptr);
+      o[u] = r * XST + pc * 16;
+    }
+    wload(wa, 0);
+#pragma unroll
+    for (int u = 0; u < SPT; ++u)
+      if (tid + u * GW_THREADS < tot) *(uint4*)(xs + o[u]) = v[u];
   }
   __syncthreads();
-  // Chunks hold an even number of iterations (KCH is a multiple of 2*U*KS),
-  // so each chunk starts on buffer wa.  The loads of the iteration after the
-  // last may be issued too (clamped, in bounds, unused).
-  int it = 0;
-  for (int kc = 0; kc < kn; kc += KCH) {
-    if (kc > 0) {  // all of this split's X for the chunk; drains the pipeline once per chunk
-      __syncthreads();
-#pragma unroll
-      for (int b0 = 0; b0 < SB; b0 += SBB) {
-        stage_load(kc, b0);
-        stage_store();
-      }
-      __syncthreads();
-    }
-    const int itend = min(nit, (kc + KCH) / (U * KS));
-    // The scheduling barriers keep each batch of loads ahead of the MFMAs on
-    // the other buffer (the compiler would otherwise sink them and wait early);
-    // the loop body is one straight block so that its wait counts stay exact.
-    for (; it + 1 < itend; it += 2) {
-      wload(wb, it + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wa, it, kc);
-      wload(wa, it + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(wb, it + 1, kc);
-    }
-    if (it < itend) {  // odd count: last chunk only
-      compute(wa, it, kc);
-      ++it;
-    }
+
+  int b = 0;
+  for (; b + 3 < nb; b += 2) {
+    wload(wb, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, b);
+    wload(wa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wb, b + 1);
+  }
+  const int rem = nb - b;
+  if (rem == 1) {
+    comp(wa, b);
+  } else if (rem == 2) {
+    wload(wb, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, b);
+    comp(wb, b + 1);
+  } else if (rem == 3) {
+    wload(wb, b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, b);
+    wload(wa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wb, b + 1);
+    comp(wa, b + 2);
   }
 
-  // ---- split-K: partials, last block reduces in split order
-  const int bid = zg * p.nblk + blk;
-  if (p.S > 1) {
-    float* part = a.gpart + ((((size_t)bid * p.S + split) * 4 + wave) * (NW * MT) * 64) * 4;
+  // ---- the four K slices meet in LDS (over the X tile); slice 0's waves sum
+  // them in slice order
+  __syncthreads();
+  f32x4_t* red = (f32x4_t*)xs;  // [slice 1..3][column tile][NW * MT][64]
+  if (ks != 0) {
 #pragma unroll
     for (int w = 0; w < NW; ++w)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        *(f32x4_t*)(part + ((size_t)(w * MT + mt) * 64 + lane) * 4) = acc[w][mt];
-    if (!arrive_last(a.cnt + bid, p.S)) return;
+        red[(((ks - 1) * 4 + ct) * (NW * MT) + w * MT + mt) * WAVE + lane] = acc[w][mt];
+  }
+  __syncthreads();
+  const bool fin = ks == 0;
+  if (fin) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // splits' loads issued eight at a time, summed in split order
-    for (int s0 = 0; s0 < p.S; s0 += 8) {
+    for (int s = 0; s < 3; ++s)
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          f32x4_t v[8];
+        for (int mt = 0; mt < MT; ++mt) acc[w][mt] += red[((s * 4 + ct) * (NW * MT) + w * MT + mt) * WAVE + lane];
+  }
+
+  // ---- split-K: partials; the last workgroup of the column block sums them
+  // in split order
+  const int bid = zg * p.nblk + blk;
+  if (p.S > 1) {
+    if (fin) {
+      float* part = a.gpart + ((((size_t)bid * p.S + split) * 4 + ct) * (NW * MT) * 64) * 4;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float* ps =
-                a.gpart + ((((size_t)bid * p.S + s0 + u) * 4 + wave) * (NW * MT) * 64) * 4;
-            v[u] = s0 + u < p.S ? *(const f32x4_t*)(ps + ((size_t)(w * MT + mt) * 64 + lane) * 4)
-                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *(f32x4_t*)(part + ((size_t)(w * MT + mt) * 64 + lane) * 4) = acc[w][mt];
+    }
+    if (!arrive_last(a.cnt + bid, p.S)) return;
+    if (fin) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // splits' loads issued eight at a time, summed in split order
+      for (int s0 = 0; s0 < p.S; s0 += 8) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x4_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const float* ps = a.gpart + ((((size_t)bid * p.S + s0 + u) * 4 + ct) * (NW * MT) * 64) * 4;
+              v[u] = s0 + u < p.S ? *(const f32x4_t*)(ps + ((size_t)(w * MT + mt) * 64 + lane) * 4)
+                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[w][mt] += v[u];
           }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) acc[w][mt] += v[u];
-        }
+      }
     }
   }
-  // the epilogue tile reuses the X tile's LDS
+  // the epilogue tile reuses the LDS
   __syncthreads();
   float* tile = (float*)xs;  // [NW][ROWS][65]
 #define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
+  if (fin) {
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
+    for (int w = 0; w < NW; ++w)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) TILE(w, mt * 16 + (lane >> 4) * 4 + r, cl) = acc[w][mt][r];
+        for (int r = 0; r < 4; ++r) TILE(w, mt * 16 + g * 4 + r, cl) = acc[w][mt][r];
+  }
+  if (OP == OP_GATEUP) {  // 1 / rms per row from its 16 partial sums
+    float* sq = tile + NW * ROWS * 65;
+    if (tid < ROWS * 16) sq[tid] = ssq_part;
+    __syncthreads();
+    if (tid < ROWS) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc += sq[tid * 16 + j];
+      s_rstd[tid] = 1.0f / sqrtf(sacc / (float)a.d + a.eps);
+    }
+  }
   __syncthreads();
 
   // ---- epilogues
   const int rows_here = min(ROWS, p.M - zg * 64);
   if (OP == OP_FC) {
-    for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
@@ -309,7 +352,7 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
   } else if (OP == OP_QKV) {
     const int per = a.hd / 64, head = blk / per, jj = blk % per, half = a.hd / 2;
     const int hq = a.H, hk = a.Hkv;
-    for (int idx = tid; idx < rows_here * 32; idx += BLOCK) {
+    for (int idx = tid; idx < rows_here * 32; idx += GW_THREADS) {
       const int mr = idx >> 5, c = idx & 31, row = zg * 64 + mr;
       const int fi = 32 * jj + c;  // frequency index within the half
       float lo = TILE(0, mr, c), hi = TILE(0, mr, c + 32);
@@ -353,7 +396,7 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
       }
     }
   } else if (OP == OP_O) {
-    for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) { TILE(0, mr, c) = 0.f; continue; }
       const float y = TILE(0, mr, c) + a.x0f[(size_t)row * a.d + nn];
@@ -362,35 +405,21 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
       El<T>::st((T*)a.yg, (size_t)row * a.d + nn, y * El<T>::ld((const T*)a.post_norm, nn));
     }
     __syncthreads();
-    if (tid < rows_here) {
+    if (tid < rows_here) {  // this workgroup's share of each row's sum of squares
       float s = 0.f;
       for (int c = 0; c < 64; ++c) s += TILE(0, tid, c) * TILE(0, tid, c);
       a.ssq[(size_t)blk * a.rows + zg * 64 + tid] = s;
     }
-    if (arrive_last(a.cnt + GRID_CNT, p.nblk * p.zg)) {
-      for (int row = tid; row < p.M; row += BLOCK) {
-        float s = 0.f;
-        for (int b0 = 0; b0 < p.nblk; b0 += 16) {
-          float v[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u)
-            v[u] = b0 + u < p.nblk ? a.ssq[(size_t)(b0 + u) * a.rows + row] : 0.f;
-#pragma unroll
-          for (int u = 0; u < 16; ++u) s += v[u];
-        }
-        a.rstd[row] = 1.0f / sqrtf(s / (float)a.d + a.eps);
-      }
-    }
   } else if (OP == OP_GATEUP) {
-    for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
-      const float r = a.rstd[row];
+      const float r = s_rstd[mr];
       const float g = TILE(0, mr, c) * r, u = TILE(NW - 1, mr, c) * r;
       El<T>::st((T*)a.act, (size_t)row * a.F + nn, g / (1.0f + expf(-g)) * u);
     }
   } else {  // OP_DOWN
-    for (int idx = tid; idx < rows_here * 64; idx += BLOCK) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
@@ -404,26 +433,19 @@ __global__ void __launch_bounds__(BLOCK) k_gemm(RoundArgs a, GemmPlan p) {
         if (i == alen - 1) El<T>::st((T*)a.root_feat, (size_t)b * a.d + nn, h);
       }
     }
-    if (a.mode == MODE_EXTEND && arrive_last(a.cnt + GRID_CNT, p.nblk * p.zg)) {
-      for (int b = tid; b < a.B; b += BLOCK) {
-        int alen = a.accept_len[b];
-        alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-        a.prefix_len[b] = clamp_prefix(a.prefix_len[b], a) + alen;
-        a.root_token[b] = clamp_tok(a.bonus[b], a.V, a.err);
-      }
-    }
   }
 #undef TILE
 }
 
 template <typename T, int OP>
 static hipError_t launch_op(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
-  const dim3 grid(p.nblk, p.S, p.zg), block(BLOCK);
+  const dim3 grid(p.nblk, p.S, p.zg), block(GW_THREADS);
+  const size_t lds = gemm_lds_bytes(p, (int)sizeof(T));
   switch (p.mt) {
-    case 1: hipLaunchKernelGGL((k_gemm<T, OP, 1>), grid, block, 0, s, a, p); break;
-    case 2: hipLaunchKernelGGL((k_gemm<T, OP, 2>), grid, block, 0, s, a, p); break;
-    case 3: hipLaunchKernelGGL((k_gemm<T, OP, 3>), grid, block, 0, s, a, p); break;
-    default: hipLaunchKernelGGL((k_gemm<T, OP, 4>), grid, block, 0, s, a, p); break;
+    case 1: hipLaunchKernelGGL((k_gemm<T, OP, 1>), grid, block, lds, s, a, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm<T, OP, 2>), grid, block, lds, s, a, p); break;
+    case 3: hipLaunchKernelGGL((k_gemm<T, OP, 3>), grid, block, lds, s, a, p); break;
+    default: hipLaunchKernelGGL((k_gemm<T, OP, 4>), grid, block, lds, s, a, p); break;
   }
   return hipGetLastError();
 }

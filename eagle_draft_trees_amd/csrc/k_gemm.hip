@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   // X tile [ROWS][Kc] (row stride Kc*ES + 16 bytes: the 16 rows of an m-tile
   // fall on different banks); then the K-slice partials; then the output tile
   extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
-  __shared__ const T* rsrc[2][ROWS];
+  __shared__ const T* rsrc[2][ROWS];  // FC: the two sources of each row
   __shared__ float s_rstd[ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -111,51 +111,40 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
     }
   }
 
-  // ---- X rows of this z-group; the FC gathers [parent feature || embed[token]]
-  if (tid < ROWS) {
-    const int row = zg * 64 + tid;
-    const T* s0 = nullptr;
-    const T* s1 = (const T*)a.embed;
-    if (row < p.M) {
-      if (OP == OP_FC) {
-        int tok;
-        if (a.mode == MODE_LEVEL) {
-          const int b = row / a.k, j = row % a.k;
-          const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
-          tok = nd.token;
-          if (a.depth == 1) s0 = (const T*)a.root_feat + (size_t)b * a.d;
-          else s0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
-        } else {
-          const int b = row / a.m, i = row % a.m;
-          int alen = a.accept_len[b];
-          alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-          const int last = alen - 1, ii = i < last ? i : last;
-          const int* path = a.accept_path + (size_t)b * (a.D + 1);
-          int pi = path[ii];
-          pi = pi < 0 ? 0 : (pi >= a.m ? a.m - 1 : pi);
-          s0 = (const T*)a.true_feat + ((size_t)b * a.m + pi) * a.d;
-          if (i < last) {
-            int pn = path[i + 1];
-            pn = pn < 0 ? 0 : (pn >= a.m ? a.m - 1 : pn);
-            tok = a.tokens[(size_t)b * a.m + pn];
-          } else {
-            tok = a.bonus[b];
-          }
-        }
-        tok = clamp_tok(tok, a.V, a.err);
-        s1 = (const T*)a.embed + (size_t)tok * a.d;  // read with k - d
-      } else if (OP == OP_QKV) {
-        s0 = (const T*)a.x0b + (size_t)row * K;
-      } else if (OP == OP_O) {
-        s0 = (const T*)a.attn + (size_t)row * K;
-      } else if (OP == OP_GATEUP) {
-        s0 = (const T*)a.yg + (size_t)row * K;
+  // ---- FC rows: [parent feature || embed[token]] gathered on the fly; rows
+  // past M take row 0's sources
+  if (OP == OP_FC && tid < ROWS) {
+    const int row0 = zg * 64 + tid;
+    const bool ok = row0 < p.M;
+    const int row = ok ? row0 : zg * 64;  // row 0 of the group always exists
+    const T* s0;
+    int tok;
+    if (a.mode == MODE_LEVEL) {
+      const int b = row / a.k, j = row % a.k;
+      const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
+      tok = nd.token;
+      if (a.depth == 1) s0 = (const T*)a.root_feat + (size_t)b * a.d;
+      else s0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
+    } else {
+      const int b = row / a.m, i = row % a.m;
+      int alen = a.accept_len[b];
+      alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
+      const int last = alen - 1, ii = i < last ? i : last;
+      const int* path = a.accept_path + (size_t)b * (a.D + 1);
+      int pi = path[ii];
+      pi = pi < 0 ? 0 : (pi >= a.m ? a.m - 1 : pi);
+      s0 = (const T*)a.true_feat + ((size_t)b * a.m + pi) * a.d;
+      if (i < last) {
+        int pn = path[i + 1];
+        pn = pn < 0 ? 0 : (pn >= a.m ? a.m - 1 : pn);
+        tok = a.tokens[(size_t)b * a.m + pn];
       } else {
-        s0 = (const T*)a.act + (size_t)row * K;
+        tok = a.bonus[b];
       }
     }
+    tok = clamp_tok(tok, a.V, a.err);
     rsrc[0][tid] = s0;
-    rsrc[1][tid] = s1;
+    rsrc[1][tid] = (const T*)a.embed + (size_t)tok * a.d;  // read with k - d
   }
   const int kswitch = (OP == OP_FC) ? a.d : K;
   const int k0 = split * p.Kc;
@@ -203,57 +192,59 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   };
 
   // ---- X tile: the split's K range of every row, SPT 16-byte pieces per
-  // thread, all loaded before any is stored (rows past M are zeros); the
-  // first weight batch is issued behind them
+  // thread, all loaded before any is stored; the first two weight batches
+  // are issued behind them
   uint4 wa[BU][NW], wb[BU][NW];
   {
-    const int npc = kn / PER, tot = ROWS * npc;
+    const unsigned npc = (unsigned)(kn / PER), tot = ROWS * npc;
+    // non-FC rows are rows of one activation matrix; the FC's row pointers
+    // come from LDS.  Rows past M read row 0 of the group: every
+    // MFMA output row depends on its own X row only, and the epilogues store
+    // rows below M only, so those rows need no masking.
+    const T* xsrc = OP == OP_QKV ? (const T*)a.x0b
+                  : OP == OP_O ? (const T*)a.attn
+                  : OP == OP_GATEUP ? (const T*)a.yg : (const T*)a.act;
     uint4 v[SPT];
     int o[SPT];
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
-      const int i = min(tid + u * GW_THREADS, tot - 1);
-      const int r = i / npc, pc = i - r * npc;
-      const int k = k0 + pc * PER;
-      const T* s0 = rsrc[0][r];
-      const int rr = s0 != nullptr ? r : 0;  // row 0 of the group always exists
-      const T* src = k < kswitch ? rsrc[0][rr] + k : rsrc[1][rr] + (k - kswitch);
-      v[u] = mask4(ld16g(src), s0 != nullptr);
-      o[u] = r * XST + pc * 16;
+      const unsigned i = min((unsigned)(tid + u * GW_THREADS), tot - 1);
+      const unsigned r = i / npc, pc = i - r * npc;
+      const int k = k0 + (int)pc * PER;
+      const T* src;
+      if (OP == OP_FC) {
+        const bool lo = k < kswitch;
+        src = rsrc[lo ? 0 : 1][r] + (lo ? k : k - kswitch);  // one LDS read, index selected
+      } else {
+        const int row = zg * 64 + (int)r;
+        src = xsrc + (size_t)(row < p.M ? row : zg * 64) * K + k;
+      }
+      v[u] = ld16g(src);
+      o[u] = (int)(r * XST + pc * 16);
     }
     wload(wa, 0);
+    wload(wb, 1);
+    // unconditional: a slot past the tile repeats the last piece (same value,
+    // same place), so no load is sunk into a branch of its own
 #pragma unroll
-    for (int u = 0; u < SPT; ++u)
-      if (tid + u * GW_THREADS < tot) *(uint4*)(xs + o[u]) = v[u];
+    for (int u = 0; u < SPT; ++u) *(uint4*)(xs + o[u]) = v[u];
   }
   __syncthreads();
 
+  // both buffers are in flight from here on: each batch's MFMAs are followed
+  // by the load two batches ahead into the same buffer (clamped in-row
+  // addresses past the slice are cache hits, their products unused)
   int b = 0;
-  for (; b + 3 < nb; b += 2) {
-    wload(wb, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; b + 2 < nb; b += 2) {
     comp(wa, b);
     wload(wa, b + 2);
     __builtin_amdgcn_sched_barrier(0);
     comp(wb, b + 1);
+    wload(wb, b + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const int rem = nb - b;
-  if (rem == 1) {
-    comp(wa, b);
-  } else if (rem == 2) {
-    wload(wb, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, b);
-    comp(wb, b + 1);
-  } else if (rem == 3) {
-    wload(wb, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, b);
-    wload(wa, b + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wb, b + 1);
-    comp(wa, b + 2);
-  }
+  if (b < nb) comp(wa, b);
+  if (b + 1 < nb) comp(wb, b + 1);
 
   // ---- the four K slices meet in LDS (over the X tile); slice 0's waves sum
   // them in slice order
@@ -278,8 +269,11 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   }
 
   // ---- split-K: partials; the last workgroup of the column block sums them
-  // in split order
+  // in split order, one (column tile, m-tile, lane) per thread with every
+  // split's loads in flight together
   const int bid = zg * p.nblk + blk;
+  float* tile = (float*)xs;  // [NW][ROWS][65], over the LDS once the slices are summed
+#define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
   if (p.S > 1) {
     if (fin) {
       float* part = a.gpart + ((((size_t)bid * p.S + split) * 4 + ct) * (NW * MT) * 64) * 4;
@@ -290,41 +284,41 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
           *(f32x4_t*)(part + ((size_t)(w * MT + mt) * 64 + lane) * 4) = acc[w][mt];
     }
     if (!arrive_last(a.cnt + bid, p.S)) return;
+    if (tid < 4 * MT * WAVE) {
+      const int ct_ = tid / (MT * WAVE), mt_ = (tid / WAVE) % MT;
+      f32x4_t sum[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < p.S; s0 += 8) {
+        f32x4_t v[8][NW];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sp = min(s0 + u, p.S - 1);
+          const float* ps = a.gpart + ((((size_t)bid * p.S + sp) * 4 + ct_) * (NW * MT) * 64) * 4;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) v[u][w] = *(const f32x4_t*)(ps + ((size_t)(w * MT + mt_) * 64 + lane) * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int w = 0; w < NW; ++w)
+            if (s0 + u < p.S) sum[w] += v[u][w];
+      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) TILE(w, mt_ * 16 + g * 4 + r, ct_ * 16 + c) = sum[w][r];
+    }
+  } else {
+    __syncthreads();  // the tile is over the slice partials
     if (fin) {
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      // splits' loads issued eight at a time, summed in split order
-      for (int s0 = 0; s0 < p.S; s0 += 8) {
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int w = 0; w < NW; ++w)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            f32x4_t v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const float* ps = a.gpart + ((((size_t)bid * p.S + s0 + u) * 4 + ct) * (NW * MT) * 64) * 4;
-              v[u] = s0 + u < p.S ? *(const f32x4_t*)(ps + ((size_t)(w * MT + mt) * 64 + lane) * 4)
-                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) acc[w][mt] += v[u];
-          }
-      }
+          for (int r = 0; r < 4; ++r) TILE(w, mt * 16 + g * 4 + r, cl) = acc[w][mt][r];
     }
-  }
-  // the epilogue tile reuses the LDS
-  __syncthreads();
-  float* tile = (float*)xs;  // [NW][ROWS][65]
-#define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
-  if (fin) {
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) TILE(w, mt * 16 + g * 4 + r, cl) = acc[w][mt][r];
   }
   if (OP == OP_GATEUP) {  // 1 / rms per row from its 16 partial sums
     float* sq = tile + NW * ROWS * 65;

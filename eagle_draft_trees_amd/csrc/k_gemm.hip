@@ -40,6 +40,143 @@ __device__ __forceinline__ int qkv_col(int blk, int c, int hd) {
   return head * hd + off;
 }
 
+// gate/up: the RMSNorm statistic of a row is the sum of the O launch's
+// per-workgroup row partials; 16 threads per row each sum every 16th partial
+// (loads issued here, the sums used after the GEMM)
+__device__ __forceinline__ float ssq_prefetch(const RoundArgs& a, const GemmPlan& p, int zg, int tid, int rows) {
+  float s = 0.f;
+  const int r = tid >> 4, j = tid & 15, row = zg * 64 + r;
+  if (r < rows && row < p.M) {
+    for (int q0 = j; q0 < p.nps; q0 += 64) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + 16 * u;
+        v[u] = q < p.nps ? a.ssq[(size_t)q * a.rows + row] : 0.f;
+      }
+      s += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+  }
+  return s;
+}
+// 1 / rms per row from the 16 partial sums of ssq_prefetch (sq: ROWS*16 floats of LDS)
+template <int ROWS>
+__device__ __forceinline__ void rstd_finish(const RoundArgs& a, float* sq, float ssq_part, float* s_rstd, int tid) {
+  if (tid < ROWS * 16) sq[tid] = ssq_part;
+  __syncthreads();
+  if (tid < ROWS) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sacc += sq[tid * 16 + j];
+    s_rstd[tid] = 1.0f / sqrtf(sacc / (float)a.d + a.eps);
+  }
+}
+
+// The ops' epilogues on one 64-column block of one z-group; tile[NW][ROWS][65]
+// in LDS holds the block's sums (all threads of the workgroup call this).
+template <typename T, int OP, int MT>
+__device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan& p, float* tile,
+                                              const float* s_rstd, int blk, int zg, int tid) {
+  constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
+  constexpr int ROWS = MT * 16;
+#define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
+  const int rows_here = min(ROWS, p.M - zg * 64);
+  if (OP == OP_FC) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+      if (nn >= p.N) continue;
+      const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
+      a.x0f[(size_t)row * a.d + nn] = v;
+      El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
+    }
+  } else if (OP == OP_QKV) {
+    const int per = a.hd / 64, head = blk / per, jj = blk % per, half = a.hd / 2;
+    const int hq = a.H, hk = a.Hkv;
+    for (int idx = tid; idx < rows_here * 32; idx += GW_THREADS) {
+      const int mr = idx >> 5, c = idx & 31, row = zg * 64 + mr;
+      const int fi = 32 * jj + c;  // frequency index within the half
+      float lo = TILE(0, mr, c), hi = TILE(0, mr, c + 32);
+      int b, slot, pos;
+      if (a.mode == MODE_LEVEL) {
+        b = row / a.k;
+        slot = row % a.k;
+        pos = clamp_prefix(a.prefix_len[b], a) - 1 + a.depth;
+      } else {
+        b = row / a.m;
+        slot = row % a.m;
+        pos = clamp_prefix(a.prefix_len[b], a) + slot;
+      }
+      if (head < hq + hk) {  // q or k: rotate the (fi, fi+half) pair
+        const double inv = pow((double)a.theta, -2.0 * (double)fi / (double)a.hd);
+        double sd, cd;
+        sincos((double)pos * inv, &sd, &cd);
+        const float cs = (float)cd, sn = (float)sd;
+        const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;
+        lo = nlo;
+        hi = nhi;
+      }
+      if (head < hq) {
+        float* qr = a.q + (size_t)row * (a.H * a.hd) + head * a.hd;
+        qr[fi] = lo;
+        qr[fi + half] = hi;
+      } else {
+        const bool isk = head < hq + hk;
+        const int kvh = isk ? head - hq : head - hq - hk;
+        T* dst;
+        if (a.mode == MODE_LEVEL) {
+          T* base = (T*)(isk ? a.tk : a.tv);
+          dst = base + ((((size_t)b * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd;
+        } else {
+          T* base = (T*)(isk ? a.k_cache : a.v_cache);
+          const int P = clamp_prefix(a.prefix_len[b], a);
+          dst = base + (((size_t)b * a.max_prefix + P + slot) * a.Hkv + kvh) * a.hd;
+        }
+        El<T>::st(dst, fi, lo);
+        El<T>::st(dst, fi + half, hi);
+      }
+    }
+  } else if (OP == OP_O) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+      if (nn >= p.N) { TILE(0, mr, c) = 0.f; continue; }
+      const float y = TILE(0, mr, c) + a.x0f[(size_t)row * a.d + nn];
+      TILE(0, mr, c) = y;
+      a.yf[(size_t)row * a.d + nn] = y;
+      El<T>::st((T*)a.yg, (size_t)row * a.d + nn, y * El<T>::ld((const T*)a.post_norm, nn));
+    }
+    __syncthreads();
+    if (tid < rows_here) {  // this workgroup's share of each row's sum of squares
+      float s = 0.f;
+      for (int c = 0; c < 64; ++c) s += TILE(0, tid, c) * TILE(0, tid, c);
+      a.ssq[(size_t)blk * a.rows + zg * 64 + tid] = s;
+    }
+  } else if (OP == OP_GATEUP) {
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+      if (nn >= p.N) continue;
+      const float r = s_rstd[mr];
+      const float g = TILE(0, mr, c) * r, u = TILE(NW - 1, mr, c) * r;
+      El<T>::st((T*)a.act, (size_t)row * a.F + nn, g / (1.0f + expf(-g)) * u);
+    }
+  } else {  // OP_DOWN
+    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+      if (nn >= p.N) continue;
+      const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
+      if (a.mode == MODE_LEVEL) {
+        El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + nn, h);
+      } else {
+        El<T>::st((T*)a.ext_h, (size_t)row * a.d + nn, h);
+        const int b = row / a.m, i = row % a.m;
+        int alen = a.accept_len[b];
+        alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
+        if (i == alen - 1) El<T>::st((T*)a.root_feat, (size_t)b * a.d + nn, h);
+      }
+    }
+  }
+#undef TILE
+}
+
 template <typename T, int OP, int MT>
 __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
@@ -81,24 +218,8 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
     if (OP == OP_DOWN) wr[0] = (const T*)a.w_down + off;
   }
 
-  // gate/up: the RMSNorm statistic of this z-group's rows is the sum of the O
-  // launch's per-workgroup row partials; 16 threads per row each sum every
-  // 16th partial (loads issued now, used by the epilogue)
-  float ssq_part = 0.f;
-  if (OP == OP_GATEUP) {
-    const int r = tid >> 4, j = tid & 15, row = zg * 64 + r;
-    if (r < ROWS && row < p.M) {
-      for (int q0 = j; q0 < p.nps; q0 += 64) {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int q = q0 + 16 * u;
-          v[u] = q < p.nps ? a.ssq[(size_t)q * a.rows + row] : 0.f;
-        }
-        ssq_part += (v[0] + v[1]) + (v[2] + v[3]);
-      }
-    }
-  }
+  // gate/up: the RMSNorm statistic of this z-group's rows (loads issued now)
+  const float ssq_part = OP == OP_GATEUP && p.S == 1 ? ssq_prefetch(a, p, zg, tid, ROWS) : 0.f;
   // down, extend: the sequence state advances here (the prefix grows by the
   // accepted length, the bonus token becomes the next root).  Nothing in this
   // launch reads either field, so one workgroup does it without an election.
@@ -268,178 +389,93 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
         for (int mt = 0; mt < MT; ++mt) acc[w][mt] += red[((s * 4 + ct) * (NW * MT) + w * MT + mt) * WAVE + lane];
   }
 
-  // ---- split-K: partials; the last workgroup of the column block sums them
-  // in split order, one (column tile, m-tile, lane) per thread with every
-  // split's loads in flight together
-  const int bid = zg * p.nblk + blk;
-  float* tile = (float*)xs;  // [NW][ROWS][65], over the LDS once the slices are summed
-#define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
+  // ---- split K: the partials go to the workspace and k_gemm_fin sums them
   if (p.S > 1) {
     if (fin) {
-      float* part = a.gpart + ((((size_t)bid * p.S + split) * 4 + ct) * (NW * MT) * 64) * 4;
+      float* part = a.gpart + (((((size_t)zg * p.nblk + blk) * p.S + split) * 4 + ct) * (NW * MT) * 64) * 4;
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           *(f32x4_t*)(part + ((size_t)(w * MT + mt) * 64 + lane) * 4) = acc[w][mt];
     }
-    if (!arrive_last(a.cnt + bid, p.S)) return;
-    if (tid < 4 * MT * WAVE) {
-      const int ct_ = tid / (MT * WAVE), mt_ = (tid / WAVE) % MT;
-      f32x4_t sum[NW];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) sum[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < p.S; s0 += 8) {
-        f32x4_t v[8][NW];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int sp = min(s0 + u, p.S - 1);
-          const float* ps = a.gpart + ((((size_t)bid * p.S + sp) * 4 + ct_) * (NW * MT) * 64) * 4;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) v[u][w] = *(const f32x4_t*)(ps + ((size_t)(w * MT + mt_) * 64 + lane) * 4);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int w = 0; w < NW; ++w)
-            if (s0 + u < p.S) sum[w] += v[u][w];
-      }
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) TILE(w, mt_ * 16 + g * 4 + r, ct_ * 16 + c) = sum[w][r];
-    }
-  } else {
-    __syncthreads();  // the tile is over the slice partials
-    if (fin) {
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) TILE(w, mt * 16 + g * 4 + r, cl) = acc[w][mt][r];
-    }
+    return;
   }
-  if (OP == OP_GATEUP) {  // 1 / rms per row from its 16 partial sums
-    float* sq = tile + NW * ROWS * 65;
-    if (tid < ROWS * 16) sq[tid] = ssq_part;
-    __syncthreads();
-    if (tid < ROWS) {
-      float sacc = 0.f;
+  __syncthreads();  // the output tile is over the slice partials
+  float* tile = (float*)xs;  // [NW][ROWS][65]
+  if (fin) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sacc += sq[tid * 16 + j];
-      s_rstd[tid] = 1.0f / sqrtf(sacc / (float)a.d + a.eps);
-    }
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tile[(w * ROWS + mt * 16 + g * 4 + r) * 65 + cl] = acc[w][mt][r];
   }
+  if (OP == OP_GATEUP) rstd_finish<ROWS>(a, tile + NW * ROWS * 65, ssq_part, s_rstd, tid);
   __syncthreads();
+  gemm_epilogue<T, OP, MT>(a, p, tile, s_rstd, blk, zg, tid);
+}
 
-  // ---- epilogues
-  const int rows_here = min(ROWS, p.M - zg * 64);
-  if (OP == OP_FC) {
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
-      if (nn >= p.N) continue;
-      const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
-      a.x0f[(size_t)row * a.d + nn] = v;
-      El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
-    }
-  } else if (OP == OP_QKV) {
-    const int per = a.hd / 64, head = blk / per, jj = blk % per, half = a.hd / 2;
-    const int hq = a.H, hk = a.Hkv;
-    for (int idx = tid; idx < rows_here * 32; idx += GW_THREADS) {
-      const int mr = idx >> 5, c = idx & 31, row = zg * 64 + mr;
-      const int fi = 32 * jj + c;  // frequency index within the half
-      float lo = TILE(0, mr, c), hi = TILE(0, mr, c + 32);
-      int b, slot, pos;
-      if (a.mode == MODE_LEVEL) {
-        b = row / a.k;
-        slot = row % a.k;
-        pos = clamp_prefix(a.prefix_len[b], a) - 1 + a.depth;
-      } else {
-        b = row / a.m;
-        slot = row % a.m;
-        pos = clamp_prefix(a.prefix_len[b], a) + slot;
+// Sum of a split GEMM's partials for one 64-column block of one z-group, in
+// split order (one (column tile, m-tile, lane) per thread, every split's
+// loads in flight together), then the op's epilogue.
+template <typename T, int OP, int MT>
+__global__ void __launch_bounds__(GW_THREADS) k_gemm_fin(RoundArgs a, GemmPlan p) {
+  constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
+  constexpr int ROWS = MT * 16;
+  __shared__ float tile[NW * ROWS * 65 + ROWS * 16];
+  __shared__ float s_rstd[ROWS];
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 15, g = lane >> 4;
+  const int blk = blockIdx.x, zg = blockIdx.z;
+  const float ssq_part = OP == OP_GATEUP ? ssq_prefetch(a, p, zg, tid, ROWS) : 0.f;
+  if (tid < 4 * MT * WAVE) {
+    const int ct = tid / (MT * WAVE), mt = (tid / WAVE) % MT;
+    const float* base = a.gpart + ((size_t)zg * p.nblk + blk) * p.S * 4 * (NW * MT) * 64 * 4;
+    f32x4_t sum[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < p.S; s0 += 8) {
+      f32x4_t v[8][NW];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float* ps = base + (((size_t)min(s0 + u, p.S - 1) * 4 + ct) * (NW * MT) * 64) * 4;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v[u][w] = *(const f32x4_t*)(ps + ((size_t)(w * MT + mt) * 64 + lane) * 4);
       }
-      if (head < hq + hk) {  // q or k: rotate the (fi, fi+half) pair
-        const double inv = pow((double)a.theta, -2.0 * (double)fi / (double)a.hd);
-        double sd, cd;
-        sincos((double)pos * inv, &sd, &cd);
-        const float cs = (float)cd, sn = (float)sd;
-        const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;
-        lo = nlo;
-        hi = nhi;
-      }
-      if (head < hq) {
-        float* qr = a.q + (size_t)row * (a.H * a.hd) + head * a.hd;
-        qr[fi] = lo;
-        qr[fi + half] = hi;
-      } else {
-        const bool isk = head < hq + hk;
-        const int kvh = isk ? head - hq : head - hq - hk;
-        T* dst;
-        if (a.mode == MODE_LEVEL) {
-          T* base = (T*)(isk ? a.tk : a.tv);
-          dst = base + ((((size_t)b * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd;
-        } else {
-          T* base = (T*)(isk ? a.k_cache : a.v_cache);
-          const int P = clamp_prefix(a.prefix_len[b], a);
-          dst = base + (((size_t)b * a.max_prefix + P + slot) * a.Hkv + kvh) * a.hd;
-        }
-        El<T>::st(dst, fi, lo);
-        El<T>::st(dst, fi + half, hi);
-      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+          if (s0 + u < p.S) sum[w] += v[u][w];
     }
-  } else if (OP == OP_O) {
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
-      if (nn >= p.N) { TILE(0, mr, c) = 0.f; continue; }
-      const float y = TILE(0, mr, c) + a.x0f[(size_t)row * a.d + nn];
-      TILE(0, mr, c) = y;
-      a.yf[(size_t)row * a.d + nn] = y;
-      El<T>::st((T*)a.yg, (size_t)row * a.d + nn, y * El<T>::ld((const T*)a.post_norm, nn));
-    }
-    __syncthreads();
-    if (tid < rows_here) {  // this workgroup's share of each row's sum of squares
-      float s = 0.f;
-      for (int c = 0; c < 64; ++c) s += TILE(0, tid, c) * TILE(0, tid, c);
-      a.ssq[(size_t)blk * a.rows + zg * 64 + tid] = s;
-    }
-  } else if (OP == OP_GATEUP) {
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
-      if (nn >= p.N) continue;
-      const float r = s_rstd[mr];
-      const float g = TILE(0, mr, c) * r, u = TILE(NW - 1, mr, c) * r;
-      El<T>::st((T*)a.act, (size_t)row * a.F + nn, g / (1.0f + expf(-g)) * u);
-    }
-  } else {  // OP_DOWN
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
-      if (nn >= p.N) continue;
-      const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
-      if (a.mode == MODE_LEVEL) {
-        El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + nn, h);
-      } else {
-        El<T>::st((T*)a.ext_h, (size_t)row * a.d + nn, h);
-        const int b = row / a.m, i = row % a.m;
-        int alen = a.accept_len[b];
-        alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-        if (i == alen - 1) El<T>::st((T*)a.root_feat, (size_t)b * a.d + nn, h);
-      }
-    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tile[(w * ROWS + mt * 16 + g * 4 + r) * 65 + ct * 16 + c] = sum[w][r];
   }
-#undef TILE
+  if (OP == OP_GATEUP) rstd_finish<ROWS>(a, tile + NW * ROWS * 65, ssq_part, s_rstd, tid);
+  __syncthreads();
+  gemm_epilogue<T, OP, MT>(a, p, tile, s_rstd, blk, zg, tid);
 }
 
 template <typename T, int OP>
 static hipError_t launch_op(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(p.nblk, p.S, p.zg), block(GW_THREADS);
   const size_t lds = gemm_lds_bytes(p, (int)sizeof(T));
+  const dim3 fgrid(p.nblk, 1, p.zg);
   switch (p.mt) {
     case 1: hipLaunchKernelGGL((k_gemm<T, OP, 1>), grid, block, lds, s, a, p); break;
     case 2: hipLaunchKernelGGL((k_gemm<T, OP, 2>), grid, block, lds, s, a, p); break;
     case 3: hipLaunchKernelGGL((k_gemm<T, OP, 3>), grid, block, lds, s, a, p); break;
     default: hipLaunchKernelGGL((k_gemm<T, OP, 4>), grid, block, lds, s, a, p); break;
+  }
+  if (p.S > 1) {
+    switch (p.mt) {
+      case 1: hipLaunchKernelGGL((k_gemm_fin<T, OP, 1>), fgrid, block, 0, s, a, p); break;
+      case 2: hipLaunchKernelGGL((k_gemm_fin<T, OP, 2>), fgrid, block, 0, s, a, p); break;
+      case 3: hipLaunchKernelGGL((k_gemm_fin<T, OP, 3>), fgrid, block, 0, s, a, p); break;
+      default: hipLaunchKernelGGL((k_gemm_fin<T, OP, 4>), fgrid, block, 0, s, a, p); break;
+    }
   }
   return hipGetLastError();
 }

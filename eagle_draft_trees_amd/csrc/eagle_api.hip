@@ -28,8 +28,8 @@ size_t elem_size(const eagle_dims& d) { return d.dtype == EAGLE_BF16 ? 2 : 4; }
 static constexpr size_t SK_XLDS_MAX = 140 * 1024;  // LDS for a staged X tile (of 160 KB per CU)
 
 // Layer GEMMs at more than 16 rows (the extend, wide frontiers): 64 output
-// columns per workgroup, K split so that a split's X rows fit in LDS and the
-// grid covers the compute units.
+// columns per workgroup over its whole K range (X streamed through LDS in
+// chunks); K is split across workgroups only to cover the compute units.
 GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   GemmPlan p{};
   p.M = M;
@@ -44,15 +44,13 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   p.mt = std::min(4, cdiv(std::min(M, 64), 16));
   p.zg = cdiv(M, 64);
   p.nblk = cdiv(p.N, 64);
-  const int ks = d.dtype == EAGLE_BF16 ? 32 : 16;
-  const int es = (int)elem_size(d);
-  // a split's K range is staged in LDS whole: at most GW_XPIECES 16-byte pieces
-  const int kcmax = std::max(ks, GW_XPIECES * 16 / (p.mt * 16 * es) / ks * ks);
+  const int kc = gemm_kc(p.nw, (int)elem_size(d));
+  // K is split across workgroups only when the column blocks alone leave
+  // more than half of the compute units idle; a split keeps two chunks or more
   const int base = p.nblk * p.zg;
-  int S = cdiv(p.K, kcmax);
-  // about one workgroup per compute unit at least (every K slice keeps a k-step)
-  S = std::max(S, std::min(cdiv(256, base), std::max(1, p.K / (4 * ks))));
-  p.Kc = cdiv(cdiv(p.K, S), ks) * ks;
+  int S = 1;
+  if (base < 128) S = std::max(1, std::min(cdiv(256, base), cdiv(p.K, 2 * kc)));
+  p.Kc = cdiv(cdiv(p.K, S), kc) * kc;
   p.S = cdiv(p.K, p.Kc);
   p.nps = op == OP_GATEUP ? cdiv(d.d, 64) : 0;
   p.part_floats = p.S > 1 ? (size_t)p.nblk * p.zg * p.S * 4 * p.nw * p.mt * 256 : 0;

@@ -18,8 +18,11 @@ constexpr int BLOCK = 256;       // four waves
 constexpr int NCNT = 1 << 16;    // last-block counters in the workspace
 constexpr int GRID_CNT = NCNT - 1;
 constexpr int GEMM_MAXS = 64;    // split-K ways at most
-constexpr int GW_THREADS = 1024;  // layer GEMM workgroup: 4 column tiles x 4 K slices
-constexpr int GW_XPIECES = 8192;  // 16-byte X pieces a layer GEMM workgroup stages at most
+constexpr int GW_KSW = 4;                   // layer GEMM workgroup: 4 column tiles x GW_KSW K slices
+constexpr int GW_THREADS = 4 * GW_KSW * 64;
+// k-steps per wave per X chunk: four with one weight stream, two with two
+__host__ __device__ constexpr int gw_bu(int nw) { return nw == 2 ? 2 : 4; }
+constexpr int GW_FIN_THREADS = 1024;        // split-sum workgroup: one (column tile, m-tile, lane) per thread
 
 enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
 enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1 };
@@ -189,12 +192,14 @@ struct GemmPlan {
   int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
   size_t part_floats;  // split-K partial floats (0 when S == 1)
 };
-// dynamic LDS of a layer GEMM workgroup: the X tile, then the K-slice
+// K elements of one X chunk of a layer GEMM (the GW_KSW slices' k-steps)
+inline int gemm_kc(int nw, int es) { return GW_KSW * gw_bu(nw) * (es == 2 ? 32 : 16); }
+// dynamic LDS of a layer GEMM workgroup: two X chunks, then the K-slice
 // partials, then the output tile and the RMSNorm partials
 inline size_t gemm_lds_bytes(const GemmPlan& p, int es) {
   const size_t rows = (size_t)p.mt * 16;
-  const size_t xt = rows * ((size_t)p.Kc * es + 16);
-  const size_t red = (size_t)12 * p.nw * p.mt * 64 * 16;
+  const size_t xt = 2 * rows * ((size_t)gemm_kc(p.nw, es) * es + 16);
+  const size_t red = (size_t)(GW_KSW - 1) * 4 * p.nw * p.mt * 64 * 16;
   const size_t tile = (size_t)p.nw * rows * 65 * 4 + rows * 16 * 4;
   return xt > red ? (xt > tile ? xt : tile) : (red > tile ? red : tile);
 }

@@ -41,17 +41,19 @@ __device__ __forceinline__ int qkv_col(int blk, int c, int hd) {
 }
 
 // gate/up: the RMSNorm statistic of a row is the sum of the O launch's
-// per-workgroup row partials; 16 threads per row each sum every 16th partial
-// (loads issued here, the sums used after the GEMM)
+// per-workgroup row partials; tpr = blockDim / rows (at most 16) threads per
+// row each sum every tpr-th partial (loads issued here, the sums used after
+// the GEMM)
 __device__ __forceinline__ float ssq_prefetch(const RoundArgs& a, const GemmPlan& p, int zg, int tid, int rows) {
+  const int tpr = min(16, (int)blockDim.x / rows);
   float s = 0.f;
-  const int r = tid >> 4, j = tid & 15, row = zg * 64 + r;
+  const int r = tid / tpr, j = tid - r * tpr, row = zg * 64 + r;
   if (r < rows && row < p.M) {
-    for (int q0 = j; q0 < p.nps; q0 += 64) {
+    for (int q0 = j; q0 < p.nps; q0 += 4 * tpr) {
       float v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int q = q0 + 16 * u;
+        const int q = q0 + tpr * u;
         v[u] = q < p.nps ? a.ssq[(size_t)q * a.rows + row] : 0.f;
       }
       s += (v[0] + v[1]) + (v[2] + v[3]);
@@ -59,15 +61,15 @@ __device__ __forceinline__ float ssq_prefetch(const RoundArgs& a, const GemmPlan
   }
   return s;
 }
-// 1 / rms per row from the 16 partial sums of ssq_prefetch (sq: ROWS*16 floats of LDS)
+// 1 / rms per row from the tpr partial sums of ssq_prefetch (sq: ROWS*16 floats of LDS)
 template <int ROWS>
 __device__ __forceinline__ void rstd_finish(const RoundArgs& a, float* sq, float ssq_part, float* s_rstd, int tid) {
-  if (tid < ROWS * 16) sq[tid] = ssq_part;
+  const int tpr = min(16, (int)blockDim.x / ROWS);
+  if (tid < ROWS * tpr) sq[tid] = ssq_part;
   __syncthreads();
   if (tid < ROWS) {
     float sacc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) sacc += sq[tid * 16 + j];
+    for (int j = 0; j < tpr; ++j) sacc += sq[tid * tpr + j];
     s_rstd[tid] = 1.0f / sqrtf(sacc / (float)a.d + a.eps);
   }
 }
@@ -82,7 +84,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
 #define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
   const int rows_here = min(ROWS, p.M - zg * 64);
   if (OP == OP_FC) {
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
@@ -92,7 +94,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
   } else if (OP == OP_QKV) {
     const int per = a.hd / 64, head = blk / per, jj = blk % per, half = a.hd / 2;
     const int hq = a.H, hk = a.Hkv;
-    for (int idx = tid; idx < rows_here * 32; idx += GW_THREADS) {
+    for (int idx = tid; idx < rows_here * 32; idx += (int)blockDim.x) {
       const int mr = idx >> 5, c = idx & 31, row = zg * 64 + mr;
       const int fi = 32 * jj + c;  // frequency index within the half
       float lo = TILE(0, mr, c), hi = TILE(0, mr, c + 32);
@@ -136,7 +138,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       }
     }
   } else if (OP == OP_O) {
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) { TILE(0, mr, c) = 0.f; continue; }
       const float y = TILE(0, mr, c) + a.x0f[(size_t)row * a.d + nn];
@@ -151,7 +153,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       a.ssq[(size_t)blk * a.rows + zg * 64 + tid] = s;
     }
   } else if (OP == OP_GATEUP) {
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float r = s_rstd[mr];
@@ -159,7 +161,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       El<T>::st((T*)a.act, (size_t)row * a.F + nn, g / (1.0f + expf(-g)) * u);
     }
   } else {  // OP_DOWN
-    for (int idx = tid; idx < rows_here * 64; idx += GW_THREADS) {
+    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
       const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
@@ -184,17 +186,21 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   constexpr int PER = El<T>::PER16;
   constexpr int ES = (int)sizeof(T);
   constexpr int ROWS = MT * 16;
-  constexpr int BU = NW == 2 ? 2 : 4;  // k-steps per weight load batch
-  constexpr int SPT = GW_XPIECES / GW_THREADS;
-  // X tile [ROWS][Kc] (row stride Kc*ES + 16 bytes: the 16 rows of an m-tile
-  // fall on different banks); then the K-slice partials; then the output tile
+  constexpr int BU = gw_bu(NW);              // k-steps per wave per chunk
+  constexpr int KC = GW_KSW * BU * KS;       // chunk of K: every slice's k-steps
+  constexpr int XST = KC * ES + 16;          // LDS row stride: an m-tile's 16 rows on different banks
+  constexpr int XBUF = ROWS * XST;           // one X chunk
+  constexpr int NPC = KC / PER;              // 16-byte pieces per row of a chunk
+  constexpr int XP = (ROWS * NPC + GW_THREADS - 1) / GW_THREADS;  // pieces per thread
+  // two X chunks [ROWS][KC] (double buffer); then the K-slice partials; then
+  // the output tile
   extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
   __shared__ const T* rsrc[2][ROWS];  // FC: the two sources of each row
   __shared__ float s_rstd[ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ct = wave & 3, ks = wave >> 2;  // column tile, K slice
+  const int ct = wave & 3, ks = wave >> 2;  // column tile, K slice (of GW_KSW)
   const int c = lane & 15, g = lane >> 4;
   const int blk = blockIdx.x, split = blockIdx.y, zg = blockIdx.z;
   const int cl = ct * 16 + c;
@@ -270,12 +276,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   const int kswitch = (OP == OP_FC) ? a.d : K;
   const int k0 = split * p.Kc;
   const int kn = min(K, k0 + p.Kc) - k0;  // this split's K range [k0, k0 + kn)
-  const int XST = p.Kc * ES + 16;
-  // this wave's k-steps [s0k, s1k) of the split (four K slices)
-  const int nks = (kn + KS - 1) / KS;
-  const int s0k = ks * nks / 4, s1k = (ks + 1) * nks / 4;
-  const int nb = (s1k - s0k + BU - 1) / BU;
-  const int kend = min(kn, s1k * KS);
+  const int nb = (kn + KC - 1) / KC;      // its chunks
   const int klast = K - PER;
   __syncthreads();
 
@@ -285,92 +286,114 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[w][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Weight loads are unconditional from a clamped in-row address (a k-step
-  // beyond the slice reads valid memory whose product is masked to zero), so
-  // that the compiler keeps an exact count of loads in flight; two register
-  // buffers alternate, so the next batch is in flight while this one runs.
+  // Weights of chunk b: this wave's BU k-steps of its slice.  Loads are
+  // unconditional from clamped in-row addresses (k past the split is masked
+  // at use), so that the compiler keeps an exact count of loads in flight.
   auto wload = [&](uint4 (&buf)[BU][NW], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BU; ++u)
 #pragma unroll
       for (int w = 0; w < NW; ++w)
-        buf[u][w] = ld16(wr[w] + min(k0 + (s0k + b * BU + u) * KS + g * PER, klast));
+        buf[u][w] = ld16(wr[w] + min(k0 + b * KC + (ks * BU + u) * KS + g * PER, klast));
   };
-  const unsigned char* xl = xs + c * XST;
-  auto comp = [&](const uint4 (&buf)[BU][NW], int b) __attribute__((always_inline)) {
+  // X chunk b: XP 16-byte pieces per thread into registers, then into LDS.
+  // Non-FC rows are rows of one activation matrix; the FC's row pointers come
+  // from LDS.  Rows past M read row 0 of the group and k past K reads the
+  // row's last piece: every MFMA output row depends on its own X row only,
+  // products past the split are masked, and the epilogues store rows below M.
+  const T* xsrc = OP == OP_QKV ? (const T*)a.x0b
+                : OP == OP_O ? (const T*)a.attn
+                : OP == OP_GATEUP ? (const T*)a.yg : (const T*)a.act;
+  auto xload = [&](uint4 (&xr)[XP], int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < BU; ++u) {
-      const int kk = (s0k + b * BU + u) * KS + g * PER;
-      const bool kin = kk < kend;
-      const int kx = min(kk, kn - PER) * ES;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xf = mask4(*(const uint4*)(xl + mt * 16 * XST + kx), kin);
-#pragma unroll
-        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, buf[u][w], acc[w][mt], T());
-      }
-    }
-  };
-
-  // ---- X tile: the split's K range of every row, SPT 16-byte pieces per
-  // thread, all loaded before any is stored; the first two weight batches
-  // are issued behind them
-  uint4 wa[BU][NW], wb[BU][NW];
-  {
-    const unsigned npc = (unsigned)(kn / PER), tot = ROWS * npc;
-    // non-FC rows are rows of one activation matrix; the FC's row pointers
-    // come from LDS.  Rows past M read row 0 of the group: every
-    // MFMA output row depends on its own X row only, and the epilogues store
-    // rows below M only, so those rows need no masking.
-    const T* xsrc = OP == OP_QKV ? (const T*)a.x0b
-                  : OP == OP_O ? (const T*)a.attn
-                  : OP == OP_GATEUP ? (const T*)a.yg : (const T*)a.act;
-    uint4 v[SPT];
-    int o[SPT];
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const unsigned i = min((unsigned)(tid + u * GW_THREADS), tot - 1);
-      const unsigned r = i / npc, pc = i - r * npc;
-      const int k = k0 + (int)pc * PER;
+    for (int q = 0; q < XP; ++q) {
+      const int i = min(tid + q * GW_THREADS, ROWS * NPC - 1);
+      const int r = i / NPC, pc = i % NPC;
+      const int k = min(k0 + b * KC + pc * PER, klast);
       const T* src;
       if (OP == OP_FC) {
         const bool lo = k < kswitch;
         src = rsrc[lo ? 0 : 1][r] + (lo ? k : k - kswitch);  // one LDS read, index selected
       } else {
-        const int row = zg * 64 + (int)r;
+        const int row = zg * 64 + r;
         src = xsrc + (size_t)(row < p.M ? row : zg * 64) * K + k;
       }
-      v[u] = ld16g(src);
-      o[u] = (int)(r * XST + pc * 16);
+      xr[q] = ld16g(src);
     }
-    wload(wa, 0);
-    wload(wb, 1);
-    // unconditional: a slot past the tile repeats the last piece (same value,
-    // same place), so no load is sunk into a branch of its own
+  };
+  // unconditional stores: a slot past the chunk repeats the last piece (same
+  // value, same place), so no load is sunk into a branch of its own
+  auto xstore = [&](const uint4 (&xr)[XP], int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) *(uint4*)(xs + o[u]) = v[u];
-  }
-  __syncthreads();
+    for (int q = 0; q < XP; ++q) {
+      const int i = min(tid + q * GW_THREADS, ROWS * NPC - 1);
+      const int r = i / NPC, pc = i % NPC;
+      *(uint4*)(xs + buf * XBUF + r * XST + pc * 16) = xr[q];
+    }
+  };
+  auto comp = [&](const uint4 (&wbuf)[BU][NW], int b, int buf) __attribute__((always_inline)) {
+    const unsigned char* xrow = xs + buf * XBUF + c * XST;
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int kc = (ks * BU + u) * KS + g * PER;  // offset in the chunk
+      const bool kin = b * KC + kc < kn;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint4 xf = mask4(*(const uint4*)(xrow + mt * 16 * XST + kc * ES), kin);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wbuf[u][w], acc[w][mt], T());
+      }
+    }
+  };
 
-  // both buffers are in flight from here on: each batch's MFMAs are followed
-  // by the load two batches ahead into the same buffer (clamped in-row
-  // addresses past the slice are cache hits, their products unused)
+  // ---- pipeline over the split's chunks: chunk b is computed from X buffer
+  // b % 2 and weight buffer b % 2 while chunk b+1's X (registers, then the
+  // other LDS buffer) and weights are in flight; chunk b+2's loads are issued
+  // after chunk b's MFMAs, and one barrier per chunk hands the X buffers over.
+  // Loads past the last chunk read clamped in-range addresses and are unused.
+  uint4 xr[XP];
+  uint4 wa[BU][NW], wb[BU][NW];
+  // (scheduling barriers keep the prologue's loads in the loop's order: X
+  // chunk, then that chunk's weights)
+  xload(xr, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  wload(wa, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  xstore(xr, 0);
+  xload(xr, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  wload(wb, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  // the loop body is one straight block (two chunks) and the last one or two
+  // chunks are peeled, so that every entry sees the same loads in flight and
+  // the compiler's wait counts stay exact
   int b = 0;
   for (; b + 2 < nb; b += 2) {
-    comp(wa, b);
+    comp(wa, b, 0);
+    xstore(xr, 1);
+    xload(xr, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
     wload(wa, b + 2);
+    __syncthreads();
+    comp(wb, b + 1, 1);
+    xstore(xr, 0);
+    xload(xr, b + 3);
     __builtin_amdgcn_sched_barrier(0);
-    comp(wb, b + 1);
     wload(wb, b + 3);
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   }
-  if (b < nb) comp(wa, b);
-  if (b + 1 < nb) comp(wb, b + 1);
+  if (b < nb) comp(wa, b, 0);
+  if (b + 1 < nb) {
+    xstore(xr, 1);
+    __syncthreads();
+    comp(wb, b + 1, 1);
+  }
+  __syncthreads();  // every wave is done with the X buffers
 
-  // ---- the four K slices meet in LDS (over the X tile); slice 0's waves sum
+  // ---- the K slices meet in LDS (over the X buffers); slice 0's waves sum
   // them in slice order
-  __syncthreads();
-  f32x4_t* red = (f32x4_t*)xs;  // [slice 1..3][column tile][NW * MT][64]
+  f32x4_t* red = (f32x4_t*)xs;  // [slice 1..GW_KSW-1][column tile][NW * MT][64]
   if (ks != 0) {
 #pragma unroll
     for (int w = 0; w < NW; ++w)
@@ -382,7 +405,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   const bool fin = ks == 0;
   if (fin) {
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
+    for (int s = 0; s < GW_KSW - 1; ++s)
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
@@ -420,7 +443,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
 // split order (one (column tile, m-tile, lane) per thread, every split's
 // loads in flight together), then the op's epilogue.
 template <typename T, int OP, int MT>
-__global__ void __launch_bounds__(GW_THREADS) k_gemm_fin(RoundArgs a, GemmPlan p) {
+__global__ void __launch_bounds__(GW_FIN_THREADS) k_gemm_fin(RoundArgs a, GemmPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
   constexpr int ROWS = MT * 16;
   __shared__ float tile[NW * ROWS * 65 + ROWS * 16];
@@ -471,10 +494,10 @@ static hipError_t launch_op(const RoundArgs& a, const GemmPlan& p, hipStream_t s
   }
   if (p.S > 1) {
     switch (p.mt) {
-      case 1: hipLaunchKernelGGL((k_gemm_fin<T, OP, 1>), fgrid, block, 0, s, a, p); break;
-      case 2: hipLaunchKernelGGL((k_gemm_fin<T, OP, 2>), fgrid, block, 0, s, a, p); break;
-      case 3: hipLaunchKernelGGL((k_gemm_fin<T, OP, 3>), fgrid, block, 0, s, a, p); break;
-      default: hipLaunchKernelGGL((k_gemm_fin<T, OP, 4>), fgrid, block, 0, s, a, p); break;
+      case 1: hipLaunchKernelGGL((k_gemm_fin<T, OP, 1>), fgrid, dim3(GW_FIN_THREADS), 0, s, a, p); break;
+      case 2: hipLaunchKernelGGL((k_gemm_fin<T, OP, 2>), fgrid, dim3(GW_FIN_THREADS), 0, s, a, p); break;
+      case 3: hipLaunchKernelGGL((k_gemm_fin<T, OP, 3>), fgrid, dim3(GW_FIN_THREADS), 0, s, a, p); break;
+      default: hipLaunchKernelGGL((k_gemm_fin<T, OP, 4>), fgrid, dim3(GW_FIN_THREADS), 0, s, a, p); break;
     }
   }
   return hipGetLastError();

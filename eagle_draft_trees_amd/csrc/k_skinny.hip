@@ -49,7 +49,7 @@ template <typename T, int OP, bool XL>
 __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;  // weight streams per wave (gate and up)
   constexpr int KS = El<T>::KSTEP;
-  constexpr int BU = (NW == 2) ? 3 : 4;  // k-steps per load batch
+  constexpr int BU = (NW == 2) ? (XL ? 3 : 2) : 4;  // k-steps per load batch (registers permitting)
   // dynamic LDS: the X tile [16][K] (row stride K*ES + 16 bytes, so the 16
   // rows of one read fall in different banks), then reused for the K-slice
   // partial sums [wave][NW][64] once every wave is done with X

@@ -8,12 +8,12 @@
 // batch and two batches are in flight (ping-pong register sets).  Loads are
 // unconditional from clamped in-bounds addresses (products past the slice are
 // masked to zero), the steady-state loop body is one straight block, and the
-// last one to three batches are peeled: all so that the compiler's wait
-// counts stay exact and no load waits behind a needless drain.
+// last one or two batches are peeled: all so that the compiler's wait counts
+// stay exact and no load waits behind a needless drain.
 //
-// X is either staged once in LDS (XL: its 16 rows, row stride K*ES + 16 so
-// that the rows of one read fall in different banks; staged while the first
-// weight batch is in flight) or loaded per k-step from L2.  X loads share the
+// X is either staged once in LDS (XL: its rows, row stride K*ES + 16 so that
+// the rows of one read fall in different banks; staged while the first two
+// weight batches are in flight) or loaded per k-step from L2.  X loads share the
 // memory queue with the weight loads and cost a quarter to a third of the
 // streaming rate, so the LDS copy is used wherever it fits and is shared.
 #pragma once
@@ -65,53 +65,62 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
   };
 
   uint4 wa[BU][NW], xa[BU], wbf[BU][NW], xbf[BU];
-  load(wa, xa, 0);
   if (XL) {
-    // the M real rows, piece by piece over all threads; all of a thread's
-    // pieces are loaded before any is stored (loads clamped, stores guarded)
-    constexpr int SPT = 9;
-    const int npc = K / PER, tot = M * npc;
-    for (int i0 = (int)threadIdx.x; i0 < tot; i0 += (int)blockDim.x * SPT) {
-      uint4 v[SPT];
+    // The M real rows, piece by piece over all threads.  A thread's first SPT
+    // pieces are loaded first, then both weight batches, then the pieces are
+    // stored: the stores wait for X alone and the weights stay in flight
+    // across the barrier.  Stores are unconditional (a slot past the end
+    // repeats the last piece: same value, same place), so no load is sunk
+    // into a branch of its own.
+    constexpr int SPT = NW == 2 ? 6 : 9;  // with two weight streams, registers are scarcer
+    const int npc = K / PER, tot = M * npc, nt = (int)blockDim.x;
+    uint4 v[SPT];
+    auto xload = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < SPT; ++u) {
-        const int i = min(i0 + u * (int)blockDim.x, tot - 1);
+        const int i = min(i0 + u * nt, tot - 1);
         v[u] = ld16(xs + (size_t)(i / npc) * K + (i % npc) * PER);
       }
+    };
+    auto xstore = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < SPT; ++u) {
-        const int i = i0 + u * (int)blockDim.x;
-        if (i < tot) *(uint4*)(dyn + (i / npc) * XST + (i % npc) * 16) = v[u];
+        const int i = min(i0 + u * nt, tot - 1);
+        *(uint4*)(dyn + (i / npc) * XST + (i % npc) * 16) = v[u];
       }
+    };
+    xload((int)threadIdx.x);
+    __builtin_amdgcn_sched_barrier(0);
+    load(wa, xa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(wbf, xbf, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    xstore((int)threadIdx.x);
+    for (int i0 = (int)threadIdx.x + nt * SPT; i0 < tot; i0 += nt * SPT) {  // rows longer than one pass
+      xload(i0);
+      xstore(i0);
     }
     __syncthreads();
+  } else {
+    load(wa, xa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(wbf, xbf, 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // Both buffers stay in flight: each batch's MFMAs are followed by the load
+  // two batches ahead into the same buffer (loads past the slice read clamped
+  // in-row addresses and are unused); the last one or two batches are peeled.
   int b = 0;
-  for (; b + 3 < nb; b += 2) {
-    load(wbf, xbf, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; b + 2 < nb; b += 2) {
     comp(wa, xa, b);
     load(wa, xa, b + 2);
     __builtin_amdgcn_sched_barrier(0);
     comp(wbf, xbf, b + 1);
+    load(wbf, xbf, b + 3);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const int rem = nb - b;
-  if (rem == 1) {
-    comp(wa, xa, b);
-  } else if (rem == 2) {
-    load(wbf, xbf, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, xa, b);
-    comp(wbf, xbf, b + 1);
-  } else if (rem == 3) {
-    load(wbf, xbf, b + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, xa, b);
-    load(wa, xa, b + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wbf, xbf, b + 1);
-    comp(wa, xa, b + 2);
-  }
+  if (b < nb) comp(wa, xa, b);
+  if (b + 1 < nb) comp(wbf, xbf, b + 1);
 }
 
 // Bytes of X tile staged by sk_stream<XL = true>.

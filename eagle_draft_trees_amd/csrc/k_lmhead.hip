@@ -183,7 +183,8 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
   const int nks = (K + KS - 1) / KS;
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[1];
-  sk_stream<T, 1, BU, XL>(wr, x0, x0, K, K, s0k, s1k, dyn, acc, xbase, p.M);
+  const int nbu = ((nks + p.KSW - 1) / p.KSW + BU - 1) / BU;
+  sk_stream<T, 1, BU, XL>(wr, x0, x0, K, K, s0k, s1k, nbu, dyn, acc, xbase, p.M);
 
   // K slices meet in LDS (over the X tile, once every wave is done with it),
   // then the slab's logits [16 rows][CT*16 columns]

@@ -122,7 +122,8 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   const int nks = (K + KS - 1) / KS;
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[NW];
-  sk_stream<T, NW, BU, XL>(wr, x0, x1, kswitch, K, s0k, s1k, dyn, acc, x0 - (size_t)xr * K, p.M);
+  const int nbu = ((nks + p.KSW - 1) / p.KSW + BU - 1) / BU;
+  sk_stream<T, NW, BU, XL>(wr, x0, x1, kswitch, K, s0k, s1k, nbu, dyn, acc, x0 - (size_t)xr * K, p.M);
 
   // ---- K slices meet in LDS; wave (ct, slice 0) sums them in slice order
   if (XL) __syncthreads();  // every wave is done reading the X tile it overwrites

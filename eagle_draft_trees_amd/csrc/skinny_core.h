@@ -23,13 +23,15 @@ namespace eg {
 
 // Row c of X (c = lane % 16) is x0[k] for k < kswitch and x1[k - kswitch]
 // beyond (the FC's gathered [feature || embedding] input); callers with one
-// source pass x1 = x0 and kswitch = K.  With XL, X must be M contiguous rows
+// source pass x1 = x0 and kswitch = K.  nbu is the number of BU-k-step
+// batches of the longest slice in the block, the same for every wave (a wave
+// with a shorter slice runs masked batches), since the loop holds barriers.  With XL, X must be M contiguous rows
 // of stride K starting at xs (only those rows are staged: LDS rows past M
 // keep stale values, which reach only the discarded output rows past M), and
 // every thread of the block must call this (it stages X and synchronises).
 template <typename T, int NW, int BU, bool XL>
 __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0, const T* x1, int kswitch,
-                                          int K, int s0k, int s1k, unsigned char* dyn,
+                                          int K, int s0k, int s1k, int nbu, unsigned char* dyn,
                                           f32x4_t (&acc)[NW], const T* xs = nullptr, int M = 16) {
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
@@ -37,7 +39,7 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int kend = min(K, s1k * KS);
-  const int nb = (s1k - s0k + BU - 1) / BU;
+  const int nb = nbu;  // the same in every wave of the block (the loop's barriers)
   const int klast = K - PER;
   const int XST = K * ES + 16;
   const unsigned char* xrow = dyn + c * XST;
@@ -118,6 +120,10 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
     comp(wbf, xbf, b + 1);
     load(wbf, xbf, b + 3);
     __builtin_amdgcn_sched_barrier(0);
+    // keep the waves of the block in step: the memory system serves older
+    // waves first, and waves that finish early leave the compute unit with
+    // fewer loads in flight for the rest of the stream
+    __builtin_amdgcn_s_barrier();
   }
   if (b < nb) comp(wa, xa, b);
   if (b + 1 < nb) comp(wbf, xbf, b + 1);

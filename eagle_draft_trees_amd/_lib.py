@@ -27,6 +27,7 @@ EAGLE_LEVEL_FULL = 0
 EAGLE_LEVEL_TAIL_ONLY = 1
 EAGLE_LEVEL_LMHEAD_ONLY = 2
 EAGLE_MAX_DEPTH = 16
+EAGLE_PACKED_WEIGHTS = 0x45505731
 
 WS_ERROR, WS_POOL, WS_FRONTIER, WS_FEAT, WS_TREE_K, WS_TREE_V, WS_EXT_H = range(7)
 
@@ -48,7 +49,7 @@ WEIGHT_NAMES = ("fc_w", "fc_b", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "
 
 
 class EagleWeights(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in WEIGHT_NAMES]
+    _fields_ = [(n, c_void_p) for n in WEIGHT_NAMES] + [("packed", c_int32)]
 
 
 class EagleTreeCfg(ctypes.Structure):
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
         P = POINTER
         sig = {
             "eagle_workspace_bytes": (c_size_t, [P(EagleDims), P(EagleTreeCfg)]),
+            "eagle_packed_weights_bytes": (c_size_t, [P(EagleDims)]),
+            "eagle_pack_weights": (c_int32, [P(EagleDims), P(EagleWeights), c_void_p, c_size_t,
+                                             P(EagleWeights), c_void_p]),
             "eagle_workspace_init": (c_int32, [P(EagleDims), P(EagleTreeCfg), c_void_p, c_size_t,
                                                c_void_p]),
             "eagle_draft_level": (c_int32, [P(EagleDims), P(EagleWeights), P(EagleTreeCfg),
@@ -146,6 +150,19 @@ def _nbytes(t) -> int:
 
 
 # ------------------------------------------------------------------ entry points
+
+def eagle_packed_weights_bytes(dims: EagleDims) -> int:
+    return int(lib().eagle_packed_weights_bytes(ctypes.byref(dims)))
+
+
+def eagle_pack_weights(dims, src: EagleWeights, dst, stream=None) -> EagleWeights:
+    """Packs the row-major weights of `src` into the device buffer `dst`;
+    returns the weights struct the drafting calls take."""
+    out = EagleWeights()
+    _check(lib().eagle_pack_weights(ctypes.byref(dims), ctypes.byref(src), _ptr(dst), _nbytes(dst),
+                                    ctypes.byref(out), _stream(stream)), "eagle_pack_weights")
+    return out
+
 
 def eagle_workspace_bytes(dims: EagleDims, cfg: EagleTreeCfg) -> int:
     return int(lib().eagle_workspace_bytes(ctypes.byref(dims), ctypes.byref(cfg)))

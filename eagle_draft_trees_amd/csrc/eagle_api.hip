@@ -221,8 +221,33 @@ static int check_ws(const eagle_dims* d, const eagle_tree_cfg* c, const void* ws
   return EAGLE_OK;
 }
 
+// the nine streamed matrices: rows N, inputs K, q/k/v pair grouping
+struct PackMat {
+  const void* eagle_weights::*field;
+  const char* name;
+  int N, K, pair_hd;
+};
+static void pack_mats(const eagle_dims& d, PackMat (&m)[9]) {
+  const int hq = d.n_heads * d.head_dim, hk = d.n_kv_heads * d.head_dim;
+  m[0] = {&eagle_weights::fc_w, "fc_w", d.d, 2 * d.d, 0};
+  m[1] = {&eagle_weights::wq, "wq", hq, d.d, d.head_dim};
+  m[2] = {&eagle_weights::wk, "wk", hk, d.d, d.head_dim};
+  m[3] = {&eagle_weights::wv, "wv", hk, d.d, d.head_dim};
+  m[4] = {&eagle_weights::wo, "wo", d.d, hq, 0};
+  m[5] = {&eagle_weights::w_gate, "w_gate", d.ffn, d.d, 0};
+  m[6] = {&eagle_weights::w_up, "w_up", d.ffn, d.d, 0};
+  m[7] = {&eagle_weights::w_down, "w_down", d.d, d.ffn, 0};
+  m[8] = {&eagle_weights::lm_head, "lm_head", d.vocab, d.d, 0};
+}
+static size_t packed_mat_bytes(int N, int K, int es) {
+  const int ks = es == 2 ? 32 : 16;
+  return (size_t)cdiv(N, 16) * 16 * ((size_t)cdiv(K, ks) * ks) * es;
+}
+
 static int check_weights(const eagle_weights* w, bool tail_only) {
   if (!w) return fail(EAGLE_ERR_ARG, "weights is NULL");
+  if (w->packed != EAGLE_PACKED_WEIGHTS)
+    return fail(EAGLE_ERR_ARG, "weights are not packed (pack them once with eagle_pack_weights)");
   if (!w->lm_head) return fail(EAGLE_ERR_ARG, "weight lm_head is NULL");
   if (tail_only) return EAGLE_OK;
   const void* need[] = {w->fc_w, w->fc_b, w->wq, w->wk, w->wv, w->wo, w->post_norm,
@@ -324,6 +349,47 @@ const char* eagle_last_error(void) { return g_err; }
 size_t eagle_workspace_bytes(const eagle_dims* dims, const eagle_tree_cfg* cfg) {
   if (check_dims(dims) || check_cfg(dims, cfg)) return 0;
   return plan_ws(*dims, *cfg).total;
+}
+
+size_t eagle_packed_weights_bytes(const eagle_dims* dims) {
+  if (check_dims(dims)) return 0;
+  PackMat m[9];
+  pack_mats(*dims, m);
+  size_t total = 0;
+  for (const PackMat& x : m) total += align256(packed_mat_bytes(x.N, x.K, (int)elem_size(*dims)));
+  return total;
+}
+
+int eagle_pack_weights(const eagle_dims* dims, const eagle_weights* src, void* dst, size_t dst_bytes,
+                       eagle_weights* out, void* stream) {
+  int r;
+  if ((r = check_dims(dims))) return r;
+  if (!src || !dst || !out) return fail(EAGLE_ERR_ARG, "src, dst or out is NULL");
+  if (src->packed) return fail(EAGLE_ERR_ARG, "src is already packed");
+  if ((uintptr_t)dst % 256) return fail(EAGLE_ERR_ARG, "dst not 256-byte aligned");
+  const size_t need = eagle_packed_weights_bytes(dims);
+  if (dst_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "dst %zu < %zu bytes", dst_bytes, need);
+  PackMat m[9];
+  pack_mats(*dims, m);
+  for (const PackMat& x : m) {
+    const void* p = src->*(x.field);
+    if (!p) return fail(EAGLE_ERR_ARG, "weight %s is NULL", x.name);
+    if ((uintptr_t)p % 16) return fail(EAGLE_ERR_ARG, "weight %s not 16-byte aligned", x.name);
+  }
+  if (!src->fc_b || !src->post_norm || !src->embed) return fail(EAGLE_ERR_ARG, "fc_b, post_norm or embed is NULL");
+  const int es = (int)elem_size(*dims);
+  eagle_weights o = *src;
+  size_t off = 0;
+  for (const PackMat& x : m) {
+    unsigned char* d = (unsigned char*)dst + off;
+    if ((r = hip_ok(launch_pack(src->*(x.field), d, x.N, x.K, es, x.pair_hd, (hipStream_t)stream), "pack")))
+      return r;
+    o.*(x.field) = d;
+    off += align256(packed_mat_bytes(x.N, x.K, es));
+  }
+  o.packed = EAGLE_PACKED_WEIGHTS;
+  *out = o;
+  return EAGLE_OK;
 }
 
 int eagle_workspace_init(const eagle_dims* dims, const eagle_tree_cfg* cfg, void* ws, size_t ws_bytes,

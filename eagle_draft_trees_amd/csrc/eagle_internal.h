@@ -278,6 +278,33 @@ __device__ __forceinline__ uint4 mask4(uint4 v, bool keep) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
+// ------------------------------------------------------------------ packed weights
+// A streamed matrix W [N][K] is stored as tiles of 16 output rows x KSTEP
+// inputs (one kilobyte, the B operand of one 16x16 MFMA step) in the order a
+// wave loads them: lane l's 16 bytes at l * PER16 elements; tile (t, s) at
+// (t * nks + s) * 16 * KSTEP, nks = ceil(K / KSTEP).  Rows and K are padded
+// with zeros to whole tiles.
+
+// elements of one tile
+template <typename T> __host__ __device__ constexpr int wtile_elems() { return 16 * El<T>::KSTEP; }
+
+// lane `lane`'s piece of tile (t, 0); k-step s adds s * wtile_elems<T>()
+template <typename T>
+__device__ __forceinline__ const T* wtile_base(const void* w, int nks, int t, int lane) {
+  return (const T*)w + (size_t)t * nks * wtile_elems<T>() + lane * El<T>::PER16;
+}
+
+// q/k/v tiles are numbered over the heads in the order [q heads | k heads |
+// v heads], hd/16 tiles per head; tile j of a head holds its rows 8j..8j+7
+// and hd/2+8j..hd/2+8j+7 (8 rotation pairs)
+template <typename T>
+__device__ __forceinline__ const T* qkv_tile(const RoundArgs& a, int t, int nks, int lane) {
+  const int per = a.hd / 16, head = t / per;
+  if (head < a.H) return wtile_base<T>(a.wq, nks, t, lane);
+  if (head < a.H + a.Hkv) return wtile_base<T>(a.wk, nks, t - a.H * per, lane);
+  return wtile_base<T>(a.wv, nks, t - (a.H + a.Hkv) * per, lane);
+}
+
 __device__ __forceinline__ int clamp_tok(int t, int V, int* err) {
   if (t < 0 || t >= V) {
     atomicOr(err, ERR_TOKEN);
@@ -356,5 +383,8 @@ hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int3
                          const int32_t* parents, int32_t* alen, int32_t* apath, int32_t* bonus,
                          hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// one matrix W [N][K] (row-major) into the packed tile layout; pair_hd > 0:
+// q/k/v row grouping of rotation pairs for head_dim pair_hd
+hipError_t launch_pack(const void* src, void* dst, int N, int K, int es, int pair_hd, hipStream_t s);
 
 }  // namespace eg

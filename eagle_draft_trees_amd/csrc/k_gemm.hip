@@ -34,11 +34,6 @@
 
 namespace eg {
 
-__device__ __forceinline__ int qkv_col(int blk, int c, int hd) {
-  const int per = hd / 64, head = blk / per, j = blk % per, half = hd / 2;
-  const int off = (c < 32) ? (32 * j + c) : (half + 32 * j + (c - 32));
-  return head * hd + off;
-}
 
 // gate/up: the RMSNorm statistic of a row is the sum of the O launch's
 // per-workgroup row partials; tpr = blockDim / rows (at most 16) threads per
@@ -92,12 +87,15 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
     }
   } else if (OP == OP_QKV) {
-    const int per = a.hd / 64, head = blk / per, jj = blk % per, half = a.hd / 2;
+    // the block's four tiles are tiles 4*blk .. 4*blk+3 of one head (hd/16
+    // tiles per head); tile j holds the rotation pairs (8j+e, hd/2+8j+e),
+    // e < 8, in its columns e and 8+e
+    const int per = a.hd / 16, head = (4 * blk) / per, j0 = (4 * blk) % per, half = a.hd / 2;
     const int hq = a.H, hk = a.Hkv;
     for (int idx = tid; idx < rows_here * 32; idx += (int)blockDim.x) {
-      const int mr = idx >> 5, c = idx & 31, row = zg * 64 + mr;
-      const int fi = 32 * jj + c;  // frequency index within the half
-      float lo = TILE(0, mr, c), hi = TILE(0, mr, c + 32);
+      const int mr = idx >> 5, pr = idx & 31, ct = pr >> 3, e = pr & 7, row = zg * 64 + mr;
+      const int fi = 8 * (j0 + ct) + e;  // frequency index within the half
+      float lo = TILE(0, mr, ct * 16 + e), hi = TILE(0, mr, ct * 16 + 8 + e);
       int b, slot, pos;
       if (a.mode == MODE_LEVEL) {
         b = row / a.k;
@@ -206,22 +204,20 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   const int cl = ct * 16 + c;
   const int K = p.K;
 
-  // ---- this lane's output column and weight rows
-  int n;
+  // ---- this lane's packed weight tile, 4*blk + ct (a tile past the last
+  // reads tile 0, discarded; rows past N within a tile are zero)
+  const int nks = (K + KS - 1) / KS;
   const T* wr[NW];
-  if (OP == OP_QKV) {
-    n = qkv_col(blk, cl, a.hd);
-    const int hq = a.H * a.hd, hk = a.Hkv * a.hd;
-    if (n < hq) wr[0] = (const T*)a.wq + (size_t)n * K;
-    else if (n < hq + hk) wr[0] = (const T*)a.wk + (size_t)(n - hq) * K;
-    else wr[0] = (const T*)a.wv + (size_t)(n - hq - hk) * K;
-  } else {
-    n = blk * 64 + cl;
-    const size_t off = (size_t)(n < p.N ? n : 0) * K;
-    if (OP == OP_FC) wr[0] = (const T*)a.fc_w + off;
-    if (OP == OP_O) wr[0] = (const T*)a.wo + off;
-    if (OP == OP_GATEUP) { wr[0] = (const T*)a.w_gate + off; wr[NW - 1] = (const T*)a.w_up + off; }
-    if (OP == OP_DOWN) wr[0] = (const T*)a.w_down + off;
+  {
+    const int t = 4 * blk + ct, tt = t < (p.N + 15) / 16 ? t : 0;
+    if (OP == OP_QKV) wr[0] = qkv_tile<T>(a, tt, nks, lane);
+    if (OP == OP_FC) wr[0] = wtile_base<T>(a.fc_w, nks, tt, lane);
+    if (OP == OP_O) wr[0] = wtile_base<T>(a.wo, nks, tt, lane);
+    if (OP == OP_GATEUP) {
+      wr[0] = wtile_base<T>(a.w_gate, nks, tt, lane);
+      wr[NW - 1] = wtile_base<T>(a.w_up, nks, tt, lane);
+    }
+    if (OP == OP_DOWN) wr[0] = wtile_base<T>(a.w_down, nks, tt, lane);
   }
 
   // gate/up: the RMSNorm statistic of this z-group's rows (loads issued now)
@@ -294,7 +290,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
     for (int u = 0; u < BU; ++u)
 #pragma unroll
       for (int w = 0; w < NW; ++w)
-        buf[u][w] = ld16(wr[w] + min(k0 + b * KC + (ks * BU + u) * KS + g * PER, klast));
+        buf[u][w] = ld16(wr[w] + (size_t)min((k0 + b * KC) / KS + ks * BU + u, nks - 1) * wtile_elems<T>());
   };
   // X chunk b: XP 16-byte pieces per thread into registers, then into LDS.
   // Non-FC rows are rows of one activation matrix; the FC's row pointers come

@@ -37,7 +37,9 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   const int cl = wave * 16 + (lane & 15);
   const int n = blk * 64 + cl;
   const bool nv = n < a.V;
-  const T* wr = (const T*)a.lm_head + (size_t)(nv ? n : 0) * K;
+  const int nkt = (K + KS - 1) / KS;
+  const int ntl = (a.V + 15) / 16;
+  const T* wr = wtile_base<T>(a.lm_head, nkt, min(blk * 4 + wave, ntl - 1), lane);  // packed tile
   const T* xbase = (level == 1) ? (const T*)a.root_feat
                                 : (const T*)a.feat + (size_t)(level - 1) * a.B * kk_ * K;
   const int rows_here = min(ROWS, p.M - zg * 64);
@@ -80,7 +82,7 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   const int klast = K - PER;
   auto wload = [&](uint4 (&buf)[U], int it) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) buf[u] = ld16(wr + min(it * U * KS + u * KS + kq, klast));
+    for (int u = 0; u < U; ++u) buf[u] = ld16(wr + (size_t)min(it * U + u, nkt - 1) * wtile_elems<T>());
   };
   auto compute = [&](const uint4 (&buf)[U], int it, int kc) __attribute__((always_inline)) {
     const int kb = it * U * KS;
@@ -176,11 +178,12 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
   const int K = a.d, kk_ = a.k;
   const int n = t * 16 + c;
   const bool nv = n < a.V;
-  const T* const wr[1] = {(const T*)a.lm_head + (size_t)(nv ? n : 0) * K};
+  const int nks = (K + KS - 1) / KS;
+  // the packed tile (a tile past the last reads tile 0, discarded)
+  const T* const wr[1] = {wtile_base<T>(a.lm_head, nks, t < (a.V + 15) / 16 ? t : 0, lane)};
   const T* xbase = (level == 1) ? (const T*)a.root_feat
                                 : (const T*)a.feat + (size_t)(level - 1) * a.B * kk_ * K;
   const T* x0 = xbase + (size_t)(c < p.M ? c : 0) * K;  // rows past M repeat row 0 (discarded)
-  const int nks = (K + KS - 1) / KS;
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[1];
   const int nbu = ((nks + p.KSW - 1) / p.KSW + BU - 1) / BU;

@@ -66,22 +66,20 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   const bool nv = tv && n < p.N;
   const int K = p.K;
 
-  // ---- this lane's weight rows (columns past N read row 0, discarded)
+  // ---- this lane's packed weight tile (a tile past the last reads tile 0,
+  // discarded; rows past N within a tile are zero)
+  const int nks = (K + KS - 1) / KS;
   const T* wr[NW];
   {
-    const int nn = nv ? n : 0;
-    if (OP == OP_QKV) {
-      const int hq = a.H * a.hd, hk = a.Hkv * a.hd;
-      if (nn < hq) wr[0] = (const T*)a.wq + (size_t)nn * K;
-      else if (nn < hq + hk) wr[0] = (const T*)a.wk + (size_t)(nn - hq) * K;
-      else wr[0] = (const T*)a.wv + (size_t)(nn - hq - hk) * K;
-    } else {
-      const size_t off = (size_t)nn * K;
-      if (OP == OP_FC) wr[0] = (const T*)a.fc_w + off;
-      if (OP == OP_O) wr[0] = (const T*)a.wo + off;
-      if (OP == OP_GATEUP) { wr[0] = (const T*)a.w_gate + off; wr[NW - 1] = (const T*)a.w_up + off; }
-      if (OP == OP_DOWN) wr[0] = (const T*)a.w_down + off;
+    const int tt = tv ? t : 0;
+    if (OP == OP_QKV) wr[0] = qkv_tile<T>(a, tt, nks, lane);
+    if (OP == OP_FC) wr[0] = wtile_base<T>(a.fc_w, nks, tt, lane);
+    if (OP == OP_O) wr[0] = wtile_base<T>(a.wo, nks, tt, lane);
+    if (OP == OP_GATEUP) {
+      wr[0] = wtile_base<T>(a.w_gate, nks, tt, lane);
+      wr[NW - 1] = wtile_base<T>(a.w_up, nks, tt, lane);
     }
+    if (OP == OP_DOWN) wr[0] = wtile_base<T>(a.w_down, nks, tt, lane);
   }
 
   // ---- this lane's X row: row c (rows past M repeat row 0; discarded).  The
@@ -119,7 +117,6 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   }
 
   // ---- this wave's K slice: k-steps [s0k, s1k)
-  const int nks = (K + KS - 1) / KS;
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[NW];
   const int nbu = ((nks + p.KSW - 1) / p.KSW + BU - 1) / BU;

@@ -2,8 +2,8 @@
 // LM head (k_lmhead.hip) at drafting shapes, where at most 16 rows of X meet
 // a weight matrix that is read exactly once.
 //
-// One wave streams NW weight-row tiles (16 rows = 16 output columns each,
-// 16 rows x 64 contiguous bytes per wave load instruction) over its K slice,
+// One wave streams NW packed weight tiles (16 output columns each, one
+// contiguous kilobyte per k-step and wave load instruction) over its K slice,
 // k-steps [s0k, s1k), into 16x16 MFMA accumulators.  BU k-steps form a load
 // batch and two batches are in flight (ping-pong register sets).  Loads are
 // unconditional from clamped in-bounds addresses (products past the slice are
@@ -21,6 +21,7 @@
 
 namespace eg {
 
+// wr[w]: this lane's piece of k-step 0 of its packed tile (wtile_base).
 // Row c of X (c = lane % 16) is x0[k] for k < kswitch and x1[k - kswitch]
 // beyond (the FC's gathered [feature || embedding] input); callers with one
 // source pass x1 = x0 and kswitch = K.  nbu is the number of BU-k-step
@@ -46,12 +47,14 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
 #pragma unroll
   for (int w = 0; w < NW; ++w) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  const int nkt = (K + KS - 1) / KS;  // k-step tiles of a packed row block
   auto load = [&](uint4 (&wb)[BU][NW], uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
-      const int kc = min((s0k + b * BU + u) * KS + g * PER, klast);
+      const int st = min(s0k + b * BU + u, nkt - 1);
+      const int kc = min(st * KS + g * PER, klast);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + kc);
+      for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + (size_t)st * wtile_elems<T>());
       if (!XL) xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
     }
   };

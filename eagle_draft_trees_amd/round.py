@@ -25,6 +25,9 @@ def to_device(a, dtype: str, device) -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+PACKED_NAMES = ("fc_w", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "lm_head")
+
+
 class DraftRound:
     """Owns the device state of one configuration and runs rounds."""
 
@@ -55,7 +58,13 @@ class DraftRound:
         self.bonus = torch.zeros(B, **i32)
         self.dims = L.make_dims(cfg)
         self.tcfg = L.make_tree_cfg(cfg)
-        self.wts = L.make_weights(self.w)
+        # the streamed matrices go to the packed tile layout once; the
+        # row-major copies of those are released
+        self.wpack = torch.empty(L.eagle_packed_weights_bytes(self.dims), dtype=torch.uint8, device=dev)
+        self.wts = L.eagle_pack_weights(self.dims, L.make_weights(self.w), self.wpack)
+        torch.cuda.synchronize(dev)
+        for n in PACKED_NAMES:
+            del self.w[n]
         self.state = L.make_state(self.k_cache, self.v_cache, self.prefix_len, self.root_feat,
                                   self.root_token)
         nbytes = L.eagle_workspace_bytes(self.dims, self.tcfg)

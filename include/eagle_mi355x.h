@@ -78,16 +78,24 @@ typedef struct {
     float rms_eps, rope_theta;
 } eagle_dims;
 
-/* Draft-head weights (all dims.dtype, row-major, Linear convention [out][in]):
+/* Draft-head weights (all dims.dtype).  As the caller holds them (row-major,
+ * Linear convention [out][in]):
  *   fc_w [d][2d]   columns 0..d-1 take the feature, d..2d-1 the token embedding
  *                  ([P1] §4.1 input = [f_j || e(t_{j+1})]);
  *   fc_b [d];  wq [H*hd][d];  wk, wv [Hkv*hd][d];  wo [d][H*hd];
  *   post_norm [d] (RMSNorm gain);  w_gate, w_up [ffn][d];  w_down [d][ffn];
- *   embed [vocab][d] and lm_head [vocab][d]: the target's, shared and frozen. */
+ *   embed [vocab][d] and lm_head [vocab][d]: the target's, shared and frozen.
+ * The drafting calls stream the nine matrices fc_w, wq, wk, wv, wo, w_gate,
+ * w_up, w_down and lm_head once per pass and take them in the packed layout
+ * that eagle_pack_weights writes (packed == EAGLE_PACKED_WEIGHTS); fc_b,
+ * post_norm and embed stay row-major.  `packed` is 0 for row-major sources. */
 typedef struct {
     const void *fc_w, *fc_b, *wq, *wk, *wv, *wo, *post_norm, *w_gate, *w_up, *w_down;
     const void *embed, *lm_head;
+    int32_t packed;
 } eagle_weights;
+
+#define EAGLE_PACKED_WEIGHTS 0x45505731  /* marks a struct filled by eagle_pack_weights */
 
 /* Tree shape: (depth, topk, m) = SGLang's (num-steps, eagle-topk,
  * num-draft-tokens) ([P3] "在 SGLang 里"); m counts the root.
@@ -131,6 +139,29 @@ typedef struct {
                                      /* at depth i+1 (the last one is itself)   */
 } eagle_frontier_node;
 
+/* Packed weights (one-time set-up, like loading a checkpoint).  Each streamed
+ * matrix W [N][K] becomes tiles of 16 output rows x KS inputs (KS = 32 for
+ * bf16, 16 for fp32): one kilobyte, the operand of one 16x16 MFMA step, stored
+ * in the order the 64 lanes of a wave load it (lane l = 16g + c holds row c,
+ * inputs g*16/elem .. of the tile), tiles of one row block consecutive along K
+ * (tile (t, s) at ((t * ceil(K/KS)) + s) * 16 * KS elements).  A wave's load
+ * is then one contiguous kilobyte instead of 16 rows of 64 bytes.  Rows and K
+ * are padded with zeros to whole tiles.  wq, wk, wv tiles hold 8 RoPE pairs of
+ * one head: tile j of a head holds its rows 8j..8j+7 and hd/2+8j..hd/2+8j+7,
+ * so that the rotation stays within a lane's columns; every other matrix's
+ * tile t holds rows 16t..16t+15.
+ * eagle_packed_weights_bytes: bytes of the packed buffer (each matrix at a
+ * 256-byte-aligned offset); 0 if dims are invalid.
+ * eagle_pack_weights: src holds the row-major matrices (src->packed == 0);
+ * dst is device memory of at least that many bytes, 256-byte aligned, owned
+ * by the caller and left untouched by the drafting calls.  Fills *out with
+ * pointers into dst (and src's fc_b, post_norm, embed) and sets out->packed.
+ * Returns EAGLE_ERR_ARG on NULL pointers or a misaligned dst,
+ * EAGLE_ERR_WORKSPACE if dst_bytes is too small; launches on `stream`. */
+size_t eagle_packed_weights_bytes(const eagle_dims *dims);
+int eagle_pack_weights(const eagle_dims *dims, const eagle_weights *src, void *dst, size_t dst_bytes,
+                       eagle_weights *out, void *stream);
+
 /* Bytes of workspace for (dims, cfg); 0 if they are invalid. */
 size_t eagle_workspace_bytes(const eagle_dims *dims, const eagle_tree_cfg *cfg);
 
@@ -165,7 +196,8 @@ int eagle_workspace_init(const eagle_dims *dims, const eagle_tree_cfg *cfg, void
  *   path product of [P1] §10.3 in the log domain); all k*k children join the
  *   pool in (frontier slot, rank) order, and the best k by (score desc, pool
  *   index asc) form frontier depth L.
- * Levels must run 1, 2, ..., depth in order within a round. */
+ * Levels must run 1, 2, ..., depth in order within a round.  w: packed
+ * weights (eagle_pack_weights; EAGLE_ERR_ARG otherwise). */
 int eagle_draft_level(const eagle_dims *dims, const eagle_weights *w,
                       const eagle_tree_cfg *cfg, const eagle_seq_state *state,
                       int32_t level, int32_t flags, void *ws, size_t ws_bytes,
@@ -208,7 +240,7 @@ int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *t
  * root_feat = feature of row accept_len-1, root_token = bonus.
  * true_feat [batch][m][d] (dtype) are the target's features at each flat
  * tree node; tokens [batch][m], accept_len, accept_path, bonus as produced
- * by the calls above. */
+ * by the calls above.  w: packed weights, as for eagle_draft_level. */
 int eagle_draft_extend(const eagle_dims *dims, const eagle_weights *w,
                        const eagle_tree_cfg *cfg, const eagle_seq_state *state,
                        const void *true_feat, const int32_t *tokens, const int32_t *accept_len,

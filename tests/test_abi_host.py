@@ -62,7 +62,7 @@ def test_entry_points_reject_bad_arguments_before_launch():
     n = L.eagle_workspace_bytes(dims, tc)
     fake = 1 << 40  # never dereferenced: validation fails first
     ws = ctypes.c_void_p(fake)
-    w = L.EagleWeights(*([fake] * 12))
+    w = L.EagleWeights(*([fake] * 12), L.EAGLE_PACKED_WEIGHTS)
     st = L.EagleSeqState(fake, fake, fake, fake, fake)
     lib = L.lib()
 
@@ -77,7 +77,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     _expect(L.EAGLE_ERR_ARG, lambda: level(level=0))
     _expect(L.EAGLE_ERR_ARG, lambda: level(level=4))
     _expect(L.EAGLE_ERR_ARG, lambda: level(flags=5))
-    _expect(L.EAGLE_ERR_ARG, lambda: level(weights=L.EagleWeights(*([fake] * 11 + [0]))))
+    _expect(L.EAGLE_ERR_ARG, lambda: level(weights=L.EagleWeights(*([fake] * 11 + [0]), L.EAGLE_PACKED_WEIGHTS)))
+    _expect(L.EAGLE_ERR_ARG, lambda: level(weights=L.EagleWeights(*([fake] * 12))))  # row-major
+    assert "not packed" in L.eagle_last_error()
     _expect(L.EAGLE_ERR_ARG, lambda: level(state=L.EagleSeqState(fake, 0, fake, fake, fake)))
     d_bad, _ = _cfg(d=320)
     _expect(L.EAGLE_ERR_SHAPE, lambda: level(dims_=d_bad))
@@ -113,3 +115,37 @@ def test_ws_view_regions_are_inside_the_workspace():
     spans.sort()
     assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))  # regions do not overlap
     assert L.POOL_DTYPE.itemsize == 24 and L.FRONTIER_DTYPE.itemsize == 80
+
+
+def _packed_bytes_formula(d, H, Hkv, hd, F, V, es):
+    ks = 32 if es == 2 else 16
+    cd = lambda a, b: -(-a // b)
+    mats = [(d, 2 * d), (H * hd, d), (Hkv * hd, d), (Hkv * hd, d), (d, H * hd), (F, d), (F, d), (d, F), (V, d)]
+    return sum(cd(cd(n, 16) * 16 * cd(k, ks) * ks * es, 256) * 256 for n, k in mats)
+
+
+def test_packed_weights_bytes_and_pack_validation():
+    for dt, es in ((L.EAGLE_BF16, 2), (L.EAGLE_F32, 4)):
+        dims, _ = _cfg(d=192, H=3, Hkv=1, F=400, V=1003)
+        dims.dtype = dt
+        assert L.eagle_packed_weights_bytes(dims) == _packed_bytes_formula(192, 3, 1, 64, 400, 1003, es)
+    dims, _ = _cfg()
+    need = L.eagle_packed_weights_bytes(dims)
+    assert need > 0
+    fake = 1 << 40
+    src = L.EagleWeights(*([fake] * 12))
+    out = L.EagleWeights()
+    lib = L.lib()
+
+    def pack(src_=src, dst=fake, n=need):
+        return L._check(lib.eagle_pack_weights(ctypes.byref(dims), ctypes.byref(src_), dst, n,
+                                                ctypes.byref(out), None), "pack")
+
+    _expect(L.EAGLE_ERR_ARG, lambda: pack(dst=None))
+    _expect(L.EAGLE_ERR_ARG, lambda: pack(dst=fake + 16))               # misaligned
+    _expect(L.EAGLE_ERR_WORKSPACE, lambda: pack(n=need - 1))
+    _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 12), L.EAGLE_PACKED_WEIGHTS)))
+    _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 2 + [0] + [fake] * 9))))
+    assert "wq" in L.eagle_last_error()
+    _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 2 + [fake + 8] + [fake] * 9))))
+    assert "aligned" in L.eagle_last_error()

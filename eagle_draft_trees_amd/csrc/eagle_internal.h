@@ -332,6 +332,13 @@ __device__ __forceinline__ uint4 ld16g(const void* p) {
   const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// 16-byte load of a packed weight piece, non-temporal: the weight stream is
+// read once per pass and should not evict what the next kernels reuse (the
+// KV cache, activations, partial records)
+__device__ __forceinline__ uint4 ld16w(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4_t*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Last-block election across workgroups (possibly on different XCDs, whose L2s
 // are not coherent with each other).  Every thread waits until its own global

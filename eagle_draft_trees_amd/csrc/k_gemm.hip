@@ -290,7 +290,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
     for (int u = 0; u < BU; ++u)
 #pragma unroll
       for (int w = 0; w < NW; ++w)
-        buf[u][w] = ld16(wr[w] + (size_t)min((k0 + b * KC) / KS + ks * BU + u, nks - 1) * wtile_elems<T>());
+        buf[u][w] = ld16w(wr[w] + (size_t)min((k0 + b * KC) / KS + ks * BU + u, nks - 1) * wtile_elems<T>());
   };
   // X chunk b: XP 16-byte pieces per thread into registers, then into LDS.
   // Non-FC rows are rows of one activation matrix; the FC's row pointers come

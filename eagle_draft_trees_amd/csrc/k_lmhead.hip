@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   const int klast = K - PER;
   auto wload = [&](uint4 (&buf)[U], int it) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) buf[u] = ld16(wr + (size_t)min(it * U + u, nkt - 1) * wtile_elems<T>());
+    for (int u = 0; u < U; ++u) buf[u] = ld16w(wr + (size_t)min(it * U + u, nkt - 1) * wtile_elems<T>());
   };
   auto compute = [&](const uint4 (&buf)[U], int it, int kc) __attribute__((always_inline)) {
     const int kb = it * U * KS;

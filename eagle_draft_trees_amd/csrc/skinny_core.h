@@ -54,7 +54,7 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
       const int st = min(s0k + b * BU + u, nkt - 1);
       const int kc = min(st * KS + g * PER, klast);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) wb[u][w] = ld16(wr[w] + (size_t)st * wtile_elems<T>());
+      for (int w = 0; w < NW; ++w) wb[u][w] = ld16w(wr[w] + (size_t)st * wtile_elems<T>());
       if (!XL) xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
     }
   };

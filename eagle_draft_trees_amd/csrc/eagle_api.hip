@@ -78,7 +78,9 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   // the X tile is staged in LDS when it fits and is shared by at least two
   // weight streams (with one, staging costs as much as it saves)
   // (not the FC, whose X rows are gathered from two sources)
-  p.xlds = op != OP_FC && p.CT * nw >= 2 && sk_xtile_bytes(p.K, (int)elem_size(d)) <= SK_XLDS_MAX;
+  // (not the down projection either: its X, the SwiGLU activations, is stored
+  // packed, one contiguous kilobyte per k-step, and is read from L2 directly)
+  p.xlds = op != OP_FC && op != OP_DOWN && p.CT * nw >= 2 && sk_xtile_bytes(p.K, (int)elem_size(d)) <= SK_XLDS_MAX;
   return p;
 }
 
@@ -153,7 +155,7 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   L.yg = take(R * d.d * es);
   L.rstd = take(R * 4);
   L.ssq = take((size_t)cdiv(d.d, 16) * R * 4);
-  L.act = take(R * d.ffn * es);
+  L.act = take((size_t)cdiv((int)R, 16) * 16 * cdiv(d.ffn, es == 2 ? 32 : 16) * (es == 2 ? 32 : 16) * es);  // packed
   size_t gp = 0;
   for (int op = OP_FC; op <= OP_DOWN; ++op)
     for (int M : {rows_lv, rows_ex}) gp = std::max(gp, plan_gemm(op, M, d).part_floats);

@@ -294,6 +294,18 @@ __device__ __forceinline__ const T* wtile_base(const void* w, int nks, int t, in
   return (const T*)w + (size_t)t * nks * wtile_elems<T>() + lane * El<T>::PER16;
 }
 
+// The SwiGLU activations (the down projection's X) are stored in the same
+// lane order as the A operand: rows in groups of 16, element (r, k) of the
+// [rows][K] matrix at (((r/16) * nks + k/KSTEP) * 64 + 16 * g + r%16) * PER16
+// + k%PER16 with g = (k%KSTEP)/PER16, so that one 16-row k-step of X is one
+// contiguous kilobyte.
+template <typename T>
+__host__ __device__ __forceinline__ size_t xpk_index(int r, int k, int nks) {
+  constexpr int KS = El<T>::KSTEP, PER = El<T>::PER16;
+  const int s = k / KS, kk = k - s * KS, g = kk / PER, e = kk - g * PER;
+  return (((size_t)(r >> 4) * nks + s) * 64 + g * 16 + (r & 15)) * PER + e;
+}
+
 // q/k/v tiles are numbered over the heads in the order [q heads | k heads |
 // v heads], hd/16 tiles per head; tile j of a head holds its rows 8j..8j+7
 // and hd/2+8j..hd/2+8j+7 (8 rotation pairs)

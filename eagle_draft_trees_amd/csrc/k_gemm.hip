@@ -156,7 +156,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       if (nn >= p.N) continue;
       const float r = s_rstd[mr];
       const float g = TILE(0, mr, c) * r, u = TILE(NW - 1, mr, c) * r;
-      El<T>::st((T*)a.act, (size_t)row * a.F + nn, g / (1.0f + expf(-g)) * u);
+      El<T>::st((T*)a.act, xpk_index<T>(row, nn, (a.F + El<T>::KSTEP - 1) / El<T>::KSTEP), g / (1.0f + expf(-g)) * u);
     }
   } else {  // OP_DOWN
     for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
@@ -297,19 +297,36 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   // from LDS.  Rows past M read row 0 of the group and k past K reads the
   // row's last piece: every MFMA output row depends on its own X row only,
   // products past the split are masked, and the epilogues store rows below M.
-  const T* xsrc = OP == OP_QKV ? (const T*)a.x0b
-                : OP == OP_O ? (const T*)a.attn
-                : OP == OP_GATEUP ? (const T*)a.yg : (const T*)a.act;
+  const T* xsrc = OP == OP_QKV ? (const T*)a.x0b : OP == OP_O ? (const T*)a.attn : (const T*)a.yg;
+  // The down projection's X (the SwiGLU activations) is stored packed: its
+  // pieces are walked in packed order (16-row group, k-step, lane), so that
+  // consecutive threads read consecutive 16 bytes; a row group past M reads
+  // the group's first row group instead (its rows are never stored).
+  auto xpiece = [&](int q, int& r, int& pc) __attribute__((always_inline)) {
+    const int i = min(tid + q * GW_THREADS, ROWS * NPC - 1);
+    if (OP == OP_DOWN) {
+      constexpr int SPC = KC / KS;  // k-steps per chunk
+      const int z = i / (SPC * 64), rem = i - z * (SPC * 64), sl = rem >> 6, l = rem & 63;
+      r = 16 * z + (l & 15);
+      pc = sl * (KS / PER) + (l >> 4);
+    } else {
+      r = i / NPC;
+      pc = i % NPC;
+    }
+  };
   auto xload = [&](uint4 (&xr)[XP], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < XP; ++q) {
-      const int i = min(tid + q * GW_THREADS, ROWS * NPC - 1);
-      const int r = i / NPC, pc = i % NPC;
+      int r, pc;
+      xpiece(q, r, pc);
       const int k = min(k0 + b * KC + pc * PER, klast);
       const T* src;
       if (OP == OP_FC) {
         const bool lo = k < kswitch;
         src = rsrc[lo ? 0 : 1][r] + (lo ? k : k - kswitch);  // one LDS read, index selected
+      } else if (OP == OP_DOWN) {
+        const int row = zg * 64 + r;
+        src = (const T*)a.act + xpk_index<T>(row < ((p.M + 15) & ~15) ? row : zg * 64 + (r & 15), k, nks);
       } else {
         const int row = zg * 64 + r;
         src = xsrc + (size_t)(row < p.M ? row : zg * 64) * K + k;
@@ -322,8 +339,8 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   auto xstore = [&](const uint4 (&xr)[XP], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < XP; ++q) {
-      const int i = min(tid + q * GW_THREADS, ROWS * NPC - 1);
-      const int r = i / NPC, pc = i % NPC;
+      int r, pc;
+      xpiece(q, r, pc);
       *(uint4*)(xs + buf * XBUF + r * XST + pc * 16) = xr[q];
     }
   };

@@ -96,10 +96,11 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
     else x0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
     x1 = (const T*)a.embed + (size_t)tok * a.d;
     kswitch = a.d;
+  } else if (OP == OP_DOWN) {  // packed activations: this lane's piece of k-step 0 (row c)
+    x0 = (const T*)a.act + lane * El<T>::PER16;
+    x1 = x0;
   } else {
-    const T* xb = (OP == OP_QKV) ? (const T*)a.x0b
-                : (OP == OP_O) ? (const T*)a.attn
-                : (OP == OP_GATEUP) ? (const T*)a.yg : (const T*)a.act;
+    const T* xb = (OP == OP_QKV) ? (const T*)a.x0b : (OP == OP_O) ? (const T*)a.attn : (const T*)a.yg;
     x0 = xb + (size_t)xr * K;
     x1 = x0;
   }
@@ -120,7 +121,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[NW];
   const int nbu = ((nks + p.KSW - 1) / p.KSW + BU - 1) / BU;
-  sk_stream<T, NW, BU, XL>(wr, x0, x1, kswitch, K, s0k, s1k, nbu, dyn, acc, x0 - (size_t)xr * K, p.M);
+  sk_stream<T, NW, BU, XL, OP == OP_DOWN>(wr, x0, x1, kswitch, K, s0k, s1k, nbu, dyn, acc, x0 - (size_t)xr * K, p.M);
 
   // ---- K slices meet in LDS; wave (ct, slice 0) sums them in slice order
   if (XL) __syncthreads();  // every wave is done reading the X tile it overwrites
@@ -232,7 +233,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
         for (int w = 0; w < (int)(blockDim.x >> 6); ++w) ss += s_ssq[w][row];
         const float rs = 1.0f / sqrtf(ss / (float)a.d + a.eps);
         const float gg = v[0][r] * rs, uu = v[NW - 1][r] * rs;
-        El<T>::st((T*)a.act, (size_t)row * a.F + n, gg / (1.0f + expf(-gg)) * uu);
+        El<T>::st((T*)a.act, xpk_index<T>(row, n, (a.F + KS - 1) / KS), gg / (1.0f + expf(-gg)) * uu);
       }
     }
   } else {  // OP_DOWN: predicted feature of the level (no final norm)
@@ -253,9 +254,9 @@ static void launch_sk_op(const RoundArgs& a, const SkPlan& p, hipStream_t s) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
   const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
   const size_t red = (size_t)WAVE * p.CT * p.KSW * NW * sizeof(f32x4_t);
-  if (p.xlds) {
+  if (p.xlds && OP != OP_DOWN) {  // the down projection's X is packed, never staged
     const size_t xb = sk_xtile_bytes(p.K, (int)sizeof(T));
-    hipLaunchKernelGGL((k_skinny<T, OP, true>), grid, block, xb > red ? xb : red, s, a, p);
+    hipLaunchKernelGGL((k_skinny<T, OP, OP != OP_DOWN>), grid, block, xb > red ? xb : red, s, a, p);
   } else {
     hipLaunchKernelGGL((k_skinny<T, OP, false>), grid, block, red, s, a, p);
   }

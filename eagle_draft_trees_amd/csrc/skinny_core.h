@@ -22,6 +22,8 @@
 namespace eg {
 
 // wr[w]: this lane's piece of k-step 0 of its packed tile (wtile_base).
+// XP: X is stored packed (16 rows x one k-step per kilobyte, xpk_index) and
+// x0 is this lane's piece of k-step 0; otherwise X is row-major:
 // Row c of X (c = lane % 16) is x0[k] for k < kswitch and x1[k - kswitch]
 // beyond (the FC's gathered [feature || embedding] input); callers with one
 // source pass x1 = x0 and kswitch = K.  nbu is the number of BU-k-step
@@ -30,7 +32,7 @@ namespace eg {
 // of stride K starting at xs (only those rows are staged: LDS rows past M
 // keep stale values, which reach only the discarded output rows past M), and
 // every thread of the block must call this (it stages X and synchronises).
-template <typename T, int NW, int BU, bool XL>
+template <typename T, int NW, int BU, bool XL, bool XP = false>
 __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0, const T* x1, int kswitch,
                                           int K, int s0k, int s1k, int nbu, unsigned char* dyn,
                                           f32x4_t (&acc)[NW], const T* xs = nullptr, int M = 16) {
@@ -55,7 +57,7 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
       const int kc = min(st * KS + g * PER, klast);
 #pragma unroll
       for (int w = 0; w < NW; ++w) wb[u][w] = ld16w(wr[w] + (size_t)st * wtile_elems<T>());
-      if (!XL) xb[u] = ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
+      if (!XL) xb[u] = XP ? ld16(x0 + (size_t)st * wtile_elems<T>()) : ld16(kc < kswitch ? x0 + kc : x1 + (kc - kswitch));
     }
   };
   auto comp = [&](const uint4 (&wb)[BU][NW], const uint4 (&xb)[BU], int b) __attribute__((always_inline)) {

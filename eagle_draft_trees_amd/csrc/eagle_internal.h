@@ -85,8 +85,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Cross-lane steps on the DPP path (a VALU operand modifier, no LDS round trip):
 // xor 1 and xor 2 within quads, then half-row and row mirrors; after those every
 // lane of a 16-lane row holds the row's result, and the four rows are combined
-// from lanes 15, 31, 47, 63.  The step order is fixed, so float results are
-// deterministic.
+// with row broadcasts into lane 63 (see wave_max_u32).  The step order is
+// fixed, so float results are deterministic.
 
 __device__ __forceinline__ unsigned dpp_u32(unsigned x, int ctrl_sel) {
   switch (ctrl_sel) {
@@ -112,36 +112,29 @@ __device__ __forceinline__ int argkey_id(unsigned long long k) {
   return (int)(0xFFFFFFFFu - (uint32_t)k);
 }
 
-// maximum 64-bit key over the wave; every lane gets it
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const unsigned hi = dpp_u32((unsigned)(k >> 32), s), lo = dpp_u32((unsigned)k, s);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    k = o > k ? o : k;
-  }
-  unsigned long long r = 0;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) {
-    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(k >> 32), row * 16 + 15);
-    const unsigned lo = __builtin_amdgcn_readlane((unsigned)k, row * 16 + 15);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    r = o > r ? o : r;
-  }
-  return r;
-}
 
 // maximum over the wave of unsigned 32-bit values (0 is the identity); every lane gets it
+// Cross-row finish of a DPP reduction with the GFX9 row broadcasts: after the
+// four intra-row steps every lane of a 16-lane row holds the row's result;
+// row_bcast:15 folds row 0 into row 1 and row 2 into row 3, row_bcast:31 folds
+// lane 31 into rows 2 and 3, so lane 63 holds the wave's result and one
+// readlane broadcasts it (no scalar-unit work per row).
+__device__ __forceinline__ unsigned dpp_bcast15(unsigned x, unsigned id) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xA, 0xF, false);
+}
+__device__ __forceinline__ unsigned dpp_bcast31(unsigned x, unsigned id) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xC, 0xF, false);
+}
 __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) v = max(v, dpp_u32(v, s));
-  unsigned r = 0;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) r = max(r, (unsigned)__builtin_amdgcn_readlane(v, row * 16 + 15));
-  return r;
+  v = max(v, dpp_bcast15(v, 0u));
+  v = max(v, dpp_bcast31(v, 0u));
+  return (unsigned)__builtin_amdgcn_readlane(v, 63);
 }
-// the same maximum as wave_max_u64, from two 32-bit reductions: the high
-// words, then the low words of the lanes that hold the highest high word
+// maximum 64-bit key over the wave (every lane gets it), from two 32-bit
+// reductions: the high words, then the low words of the lanes that hold the
+// highest high word
 __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
   const unsigned hi = (unsigned)(k >> 32);
   const unsigned mh = wave_max_u32(hi);
@@ -152,19 +145,18 @@ __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k)
 __device__ __forceinline__ float wave_sum_dpp(float v) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) v += __uint_as_float(dpp_u32(__float_as_uint(v), s));
-  float r = 0.f;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) r += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), row * 16 + 15));
-  return r;
+  v += __uint_as_float(dpp_bcast15(__float_as_uint(v), 0u));
+  v += __uint_as_float(dpp_bcast31(__float_as_uint(v), 0u));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
 __device__ __forceinline__ float wave_max_dpp(float v) {
+  const unsigned ninf = __float_as_uint(-INFINITY);
 #pragma unroll
   for (int s = 0; s < 4; ++s) v = fmaxf(v, __uint_as_float(dpp_u32(__float_as_uint(v), s)));
-  float r = -INFINITY;
-#pragma unroll
-  for (int row = 0; row < 4; ++row) r = fmaxf(r, __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), row * 16 + 15)));
-  return r;
+  v = fmaxf(v, __uint_as_float(dpp_bcast15(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_bcast31(__float_as_uint(v), ninf)));
+  return __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 63));
 }
 
 // (value desc, id asc) winner across the wave; every lane gets the result

@@ -228,6 +228,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
       rec[0] = mx;
       rec[1] = se;
     }
+    unsigned long long mine = 0ull;  // lane r: the r-th entry
     for (int r = 0; r < kk_; ++r) {
       unsigned long long best = 0ull;
 #pragma unroll
@@ -236,10 +237,11 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (key[u] == win) key[u] = 0ull;  // keys are unique: one owner
-      if (lane == 0) {
-        rec[2 + r] = win ? argkey_value(win) : -INFINITY;
-        rec[2 + kk_ + r] = __int_as_float(win ? argkey_id(win) : -1);
-      }
+      if (lane == r) mine = win;
+    }
+    if (lane < kk_) {
+      rec[2 + lane] = mine ? argkey_value(mine) : -INFINITY;
+      rec[2 + kk_ + lane] = __int_as_float(mine ? argkey_id(mine) : -1);
     }
   }
 }

@@ -198,8 +198,11 @@ def main() -> int:
     rounds_s = args.steps / el
 
     # dominant kernel (the LM-head GEMM with its fused per-slab softmax and
-    # top-k), timed live with HIP events on the stream it runs on: a
-    # LMHEAD_ONLY level call launches exactly that one kernel
+    # top-k), timed live on the stream it runs on: a LMHEAD_ONLY level call
+    # launches exactly that one kernel, and the timed variant has the kernel's
+    # own dispatch stamp a pair of HIP events at its start and end.  A second
+    # pair of ordinary events, queued around the same call, shows what queue
+    # markers add.
     # Between launches a 512 MiB read (a reduction, outside the events) evicts
     # the 256 MB memory-side Infinity Cache, which would otherwise keep part of
     # the 262 MB LM head warm across back-to-back launches; inside a round the
@@ -207,19 +210,22 @@ def main() -> int:
     # copy's dirty lines would be written back during the timed launch.
     scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     scrub_out = torch.empty((), dtype=torch.float32, device=dev)
-    evs = []
+    n_lm = max(5, args.steps // 5) * (cfg.D - 1)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_lm)]
     with torch.cuda.stream(stream):
-        for it in range(max(5, args.steps // 5)):
-            for level in range(2, cfg.D + 1):
-                torch.sum(scrub, dim=0, out=scrub_out)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                r.level(level, L.EAGLE_LEVEL_LMHEAD_ONLY, stream=stream)
-                e1.record(stream)
-                evs.append((e0, e1))
+        for q in ev:            # torch creates events on their first record
+            for e in q:
+                e.record(stream)
     torch.cuda.synchronize()
-    lm_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    with torch.cuda.stream(stream):
+        for i, (m0, k0, k1, m1) in enumerate(ev):
+            torch.sum(scrub, dim=0, out=scrub_out)
+            m0.record(stream)
+            r.level_timed(2 + i % (cfg.D - 1), L.EAGLE_LEVEL_LMHEAD_ONLY, k0, k1, stream=stream)
+            m1.record(stream)
+    torch.cuda.synchronize()
+    lm_ms = float(np.mean([k0.elapsed_time(k1) for _, k0, k1, _ in ev]))
+    lm_marker_ms = float(np.mean([m0.elapsed_time(m1) for m0, _, _, m1 in ev]))
     ab = algorithmic_bytes(cfg)
     lm_gbps = ab["lm_head_per_launch"] / (lm_ms * 1e-3) / 1e9
     traffic = stored_traffic(workload)
@@ -249,6 +255,9 @@ def main() -> int:
                      "bound": "hbm", "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
                      "avg_launch_us": round(lm_ms * 1e3, 2),
+                     "timing": f"{n_lm} launches, HIP events stamped by the kernel's dispatch "
+                               f"(hipExtLaunchKernel); queued marker events around the same "
+                               f"launches: {lm_marker_ms * 1e3:.2f} us",
                      "bytes_per_launch": int(ab["lm_head_per_launch"]),
                      "traffic": traffic},
     }

@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
             "eagle_draft_level": (c_int32, [P(EagleDims), P(EagleWeights), P(EagleTreeCfg),
                                             P(EagleSeqState), c_int32, c_int32, c_void_p, c_size_t,
                                             c_void_p]),
+            "eagle_draft_level_timed": (c_int32, [P(EagleDims), P(EagleWeights), P(EagleTreeCfg),
+                                                  P(EagleSeqState), c_int32, c_int32, c_void_p,
+                                                  c_size_t, c_void_p, c_void_p, c_void_p]),
             "eagle_rerank_build_tree": (c_int32, [P(EagleDims), P(EagleTreeCfg), P(EagleSeqState),
                                                   c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                                   c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -177,6 +180,21 @@ def eagle_draft_level(dims, weights, cfg, state, level, flags, ws, stream=None) 
     _check(lib().eagle_draft_level(ctypes.byref(dims), ctypes.byref(weights), ctypes.byref(cfg),
                                    ctypes.byref(state), level, flags, _ptr(ws), _nbytes(ws),
                                    _stream(stream)), f"eagle_draft_level({level})")
+
+
+def _event(e) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (which must have been recorded once,
+    since torch creates the event lazily) or an int handle."""
+    return e if isinstance(e, int) else e.cuda_event
+
+
+def eagle_draft_level_timed(dims, weights, cfg, state, level, flags, ws, start_event, stop_event,
+                            stream=None) -> None:
+    _check(lib().eagle_draft_level_timed(ctypes.byref(dims), ctypes.byref(weights),
+                                         ctypes.byref(cfg), ctypes.byref(state), level, flags,
+                                         _ptr(ws), _nbytes(ws), _event(start_event),
+                                         _event(stop_event), _stream(stream)),
+           f"eagle_draft_level_timed({level})")
 
 
 def eagle_rerank_build_tree(dims, cfg, state, ws, tokens, parents, depth=None, positions=None,

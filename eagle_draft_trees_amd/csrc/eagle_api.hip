@@ -402,9 +402,9 @@ int eagle_workspace_init(const eagle_dims* dims, const eagle_tree_cfg* cfg, void
   return hip_ok(launch_zero(ws, plan_ws(*dims, *cfg).total, (hipStream_t)stream), "zero fill");
 }
 
-int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
-                      const eagle_seq_state* state, int32_t level, int32_t flags, void* ws,
-                      size_t ws_bytes, void* stream) {
+static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
+                       const eagle_seq_state* state, int32_t level, int32_t flags, void* ws,
+                       size_t ws_bytes, hipEvent_t e0, hipEvent_t e1, void* stream) {
   int r;
   if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
     return r;
@@ -419,7 +419,7 @@ int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagl
   if (level == 1) {
     a.rows = cfg->batch;
     const LmPlan pl = plan_lm(cfg->batch, *dims, cfg->topk);
-    if ((r = hip_ok(launch_lmhead(a, pl, 1, s), "lm head"))) return r;
+    if ((r = hip_ok(launch_lmhead(a, pl, 1, s, e0, e1), "lm head"))) return r;
     if (lm_only) return EAGLE_OK;
     return hip_ok(launch_lmmerge(a, pl, 1, s), "lm merge");
   }
@@ -429,9 +429,23 @@ int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagl
   a.RS = cfg->topk;
   if (!tail_only && (r = run_layer(a, *dims, *cfg, s))) return r;
   const LmPlan pl = plan_lm(a.rows, *dims, cfg->topk);
-  if ((r = hip_ok(launch_lmhead(a, pl, level, s), "lm head"))) return r;
+  if ((r = hip_ok(launch_lmhead(a, pl, level, s, e0, e1), "lm head"))) return r;
   if (lm_only) return EAGLE_OK;
   return hip_ok(launch_lmmerge(a, pl, level, s), "lm merge");
+}
+
+int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
+                      const eagle_seq_state* state, int32_t level, int32_t flags, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return draft_level(dims, w, cfg, state, level, flags, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+int eagle_draft_level_timed(const eagle_dims* dims, const eagle_weights* w,
+                            const eagle_tree_cfg* cfg, const eagle_seq_state* state, int32_t level,
+                            int32_t flags, void* ws, size_t ws_bytes, void* start_event,
+                            void* stop_event, void* stream) {
+  return draft_level(dims, w, cfg, state, level, flags, ws, ws_bytes, (hipEvent_t)start_event,
+                     (hipEvent_t)stop_event, stream);
 }
 
 int eagle_rerank_build_tree(const eagle_dims* dims, const eagle_tree_cfg* cfg,

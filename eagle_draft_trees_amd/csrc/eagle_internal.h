@@ -385,7 +385,9 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 // launchers (return a hipError_t)
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
-hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
+// e0/e1 (may be null): events stamped at the LM-head kernel's own start and end
+hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
+                         hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
 hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,

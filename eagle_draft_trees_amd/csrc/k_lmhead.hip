@@ -11,6 +11,7 @@
 // MFMAs); the 64-column logit tile goes to LDS and each row's slab is reduced
 // to (max, sum exp) and its top-k (logit desc, id asc).  Logits never leave
 // the chip.
+#include <hip/hip_ext.h>
 #include <float.h>
 
 #include "skinny_core.h"
@@ -246,35 +247,52 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
   }
 }
 
+// Launch through hipExtLaunchKernel when events are given (they then mark the
+// kernel's own start and end), through the plain launch otherwise.
+template <typename... A>
+static void lm_launch(void (*k)(A...), dim3 g, dim3 b, size_t sh, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1, A... args) {
+  if (e0 || e1)
+    hipExtLaunchKernelGGL(k, g, b, (uint32_t)sh, s, e0, e1, 0u, args...);
+  else
+    hipLaunchKernelGGL(k, g, b, sh, s, args...);
+}
+
 template <typename T>
-static hipError_t launch_lm_t(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
+static hipError_t launch_lm_t(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
+                              hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(p.nblk, 1, p.zg), block(BLOCK);
   switch (p.mt) {
-    case 1: hipLaunchKernelGGL((k_lmhead<T, 1>), grid, block, 0, s, a, p, level); break;
-    case 2: hipLaunchKernelGGL((k_lmhead<T, 2>), grid, block, 0, s, a, p, level); break;
-    case 3: hipLaunchKernelGGL((k_lmhead<T, 3>), grid, block, 0, s, a, p, level); break;
-    default: hipLaunchKernelGGL((k_lmhead<T, 4>), grid, block, 0, s, a, p, level); break;
+    case 1: lm_launch(k_lmhead<T, 1>, grid, block, 0, s, e0, e1, a, p, level); break;
+    case 2: lm_launch(k_lmhead<T, 2>, grid, block, 0, s, e0, e1, a, p, level); break;
+    case 3: lm_launch(k_lmhead<T, 3>, grid, block, 0, s, e0, e1, a, p, level); break;
+    default: lm_launch(k_lmhead<T, 4>, grid, block, 0, s, e0, e1, a, p, level); break;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t launch_lmsk_t(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
+static hipError_t launch_lmsk_t(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
+                                hipEvent_t e0, hipEvent_t e1) {
   const int nwv = p.CT * p.KSW;
   const size_t epi = (size_t)nwv * WAVE * sizeof(f32x4_t) + (size_t)16 * (p.CT * 16 + 1) * sizeof(float);
+  const dim3 grid(p.nblk), block(nwv * WAVE);
   if (p.xlds) {
     const size_t xb = sk_xtile_bytes(a.d, (int)sizeof(T));
-    hipLaunchKernelGGL((k_lmskinny<T, true>), dim3(p.nblk), dim3(nwv * WAVE), xb > epi ? xb : epi, s, a, p, level);
+    lm_launch(k_lmskinny<T, true>, grid, block, xb > epi ? xb : epi, s, e0, e1, a, p, level);
   } else {
-    hipLaunchKernelGGL((k_lmskinny<T, false>), dim3(p.nblk), dim3(nwv * WAVE), epi, s, a, p, level);
+    lm_launch(k_lmskinny<T, false>, grid, block, epi, s, e0, e1, a, p, level);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
-  if (p.sk) return a.dtype == EAGLE_BF16 ? launch_lmsk_t<bf16_t>(a, p, level, s) : launch_lmsk_t<float>(a, p, level, s);
-  return a.dtype == EAGLE_BF16 ? launch_lm_t<bf16_t>(a, p, level, s)
-                               : launch_lm_t<float>(a, p, level, s);
+hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
+                         hipEvent_t e0, hipEvent_t e1) {
+  if (p.sk)
+    return a.dtype == EAGLE_BF16 ? launch_lmsk_t<bf16_t>(a, p, level, s, e0, e1)
+                                 : launch_lmsk_t<float>(a, p, level, s, e0, e1);
+  return a.dtype == EAGLE_BF16 ? launch_lm_t<bf16_t>(a, p, level, s, e0, e1)
+                               : launch_lm_t<float>(a, p, level, s, e0, e1);
 }
 
 }  // namespace eg

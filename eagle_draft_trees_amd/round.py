@@ -92,6 +92,10 @@ class DraftRound:
         L.eagle_draft_level(self.dims, self.wts, self.tcfg, self.state, level, flags, self.ws,
                             stream)
 
+    def level_timed(self, level: int, flags: int, start_event, stop_event, stream=None) -> None:
+        L.eagle_draft_level_timed(self.dims, self.wts, self.tcfg, self.state, level, flags,
+                                  self.ws, start_event, stop_event, stream)
+
     def rerank(self, stream=None) -> None:
         L.eagle_rerank_build_tree(self.dims, self.tcfg, self.state, self.ws, self.tokens,
                                   self.parents, self.depth, self.positions, self.mask,

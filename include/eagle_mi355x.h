@@ -203,6 +203,18 @@ int eagle_draft_level(const eagle_dims *dims, const eagle_weights *w,
                       int32_t level, int32_t flags, void *ws, size_t ws_bytes,
                       void *stream);
 
+/* eagle_draft_level, with the LM-head GEMM kernel of the call launched so that
+ * start_event and stop_event (hipEvent_t, created by the caller with timing
+ * enabled; either may be NULL) are stamped when that one kernel starts and
+ * when it ends (hipExtLaunchKernel), rather than where the events would sit
+ * in the stream's queue: it times the kernel alone, with no queue overhead.
+ * Same arguments, outputs and errors as eagle_draft_level otherwise.  For
+ * timing runs; not meant for graph capture. */
+int eagle_draft_level_timed(const eagle_dims *dims, const eagle_weights *w,
+                            const eagle_tree_cfg *cfg, const eagle_seq_state *state,
+                            int32_t level, int32_t flags, void *ws, size_t ws_bytes,
+                            void *start_event, void *stop_event, void *stream);
+
 /* Rerank and build ([P1] §10.3 rerank; [P3] organize_draft_results and
  * build_tree_kernel_efficient; [P4] EAGLE-2 diagram).  Per sequence: the best
  * m-1 pool entries by (score desc, depth asc, pool index asc) plus the root;

@@ -468,6 +468,39 @@ def test_repeat_runs_are_bit_identical(name):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["ragged_bf16", "7b"])
+def test_timed_level_matches_plain(name):
+    """eagle_draft_level_timed drafts the same tree as eagle_draft_level, and the
+    events it hands to the LM-head launch bracket a positive time that lies
+    inside ordinary events queued around the same call."""
+    import torch
+    from eagle_draft_trees_amd import _lib as L
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[timed level] {name}")
+    outs = lambda: [t.cpu().numpy().copy() for t in (r.tokens, r.parents, r.mask, r.logscore)]
+    r.draft()
+    sync()
+    ref = outs()
+    r.reset_state(inp)
+    ev = []
+    for level in range(1, cfg.D + 1):
+        q = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in q:          # torch creates an event on its first record
+            e.record()
+        sync()
+        q[0].record()
+        r.level_timed(level, L.EAGLE_LEVEL_FULL, q[1], q[2])
+        q[3].record()
+        ev.append(q)
+    r.rerank()
+    sync()
+    for a, b in zip(ref, outs()):
+        assert np.array_equal(a, b)
+    for m0, k0, k1, m1 in ev:
+        assert k0.elapsed_time(k1) > 0
+        assert m0.elapsed_time(k0) >= -1e-3 and k1.elapsed_time(m1) >= -1e-3
+
+
 def test_out_of_range_token_is_clamped_and_flagged():
     import torch
     cfg, inp, r, model, seqs = get("ragged_f32")

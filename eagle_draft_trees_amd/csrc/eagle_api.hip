@@ -120,7 +120,7 @@ AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& 
   const int keys = c.max_prefix + (mode == MODE_LEVEL ? c.depth * c.topk : 0);
   const int chunks = cdiv(keys, 16);
   p.nsplit = std::max(1, std::min({8, cdiv(256, tiles), std::max(1, chunks / 4)}));
-  p.part_floats = p.nsplit > 1 ? (size_t)tiles * p.nsplit * 16 * (d.head_dim + 2) : 0;
+  p.part_floats = p.nsplit > 1 ? (size_t)tiles * p.nsplit * 16 * (d.head_dim + 4) : 0;
   return p;
 }
 

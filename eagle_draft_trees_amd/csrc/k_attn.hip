@@ -17,8 +17,9 @@
 //     high and a low bf16 part, so the scores keep about 16 mantissa bits;
 //     fp32: the fp32 MFMA), lane (g, q) holding keys 4g..4g+3 of query q;
 //   * updates each query's running max and sum (online softmax);
-//   * accumulates P V on the vector ALUs in fp32, each lane owning hd/64
-//     output dimensions, with every V row read as one coalesced row.
+//   * accumulates P V: bf16 on MFMA (16x16x16, keys as the contraction),
+//     with the probabilities split into a high and a low bf16 part; fp32 on
+//     the vector ALUs, each lane owning hd/64 output dimensions.
 // The next chunk's K and V loads are in flight while a chunk computes.  The
 // waves' partial (max, sum, output) meet in LDS and are combined in wave order
 // (deterministic); there is no cross-workgroup step.  Scores 1/sqrt(hd) q.k.
@@ -31,47 +32,88 @@ constexpr int AT_Q = 16;      // queries per workgroup (one MFMA tile)
 constexpr int AT_C = 16;      // keys per chunk
 constexpr int AT_MAXS = 8;    // key splits of one query tile at most
 
-template <typename T, int HD> struct AtVec;  // this lane's HD/64 elements of a V row
-template <> struct AtVec<bf16_t, 128> {
-  typedef uint32_t raw;
-  __device__ static raw ld(const bf16_t* row, int lane) { return *(const uint32_t*)(row + 2 * lane); }
-  __device__ static void cvt(raw r, float* v) { v[0] = bf2f(r & 0xFFFFu); v[1] = bf2f(r >> 16); }
+// What a lane loads of a chunk's 16 V rows: N loads, load u from key row
+// key(u, g) at column col(lane).
+//  * bf16 (P V on MFMA): lane (g, i) loads keys 4g..4g+3, each at the NT = hd/16
+//    consecutive columns NT*i .. NT*i+NT-1.  Tile t of the product then takes
+//    hd column NT*i + t as its row i, so element t of the four loads is the
+//    lane's A operand for tile t, and the result row 4g+r of tile t is hd
+//    column NT*(4g+r) + t: each lane ends with NT*4 consecutive columns.
+//  * fp32 (P V on the vector ALUs): lane loads every key row at its hd/64
+//    columns DPL*lane ...
+template <typename T, int HD> struct AtV;
+template <> struct AtV<bf16_t, 128> {
+  static constexpr int N = 4;
+  typedef uint4 raw;
+  __device__ static int key(int u, int g) { return 4 * g + u; }
+  __device__ static int col(int lane) { return 8 * (lane & 15); }
+  __device__ static raw ld(const bf16_t* p) { return *(const uint4*)p; }
+  __device__ static uint32_t el(raw v, int t) {  // 16-bit element t (t compile-time)
+    const uint32_t d = (t >> 1) == 0 ? v.x : (t >> 1) == 1 ? v.y : (t >> 1) == 2 ? v.z : v.w;
+    return (t & 1) ? d >> 16 : d & 0xFFFFu;
+  }
 };
-template <> struct AtVec<bf16_t, 64> {
-  typedef uint32_t raw;
-  __device__ static raw ld(const bf16_t* row, int lane) { return row[lane]; }
-  __device__ static void cvt(raw r, float* v) { v[0] = bf2f(r & 0xFFFFu); }
+template <> struct AtV<bf16_t, 64> {
+  static constexpr int N = 4;
+  typedef uint2 raw;
+  __device__ static int key(int u, int g) { return 4 * g + u; }
+  __device__ static int col(int lane) { return 4 * (lane & 15); }
+  __device__ static raw ld(const bf16_t* p) { return *(const uint2*)p; }
+  __device__ static uint32_t el(raw v, int t) {
+    const uint32_t d = (t >> 1) == 0 ? v.x : v.y;
+    return (t & 1) ? d >> 16 : d & 0xFFFFu;
+  }
 };
-template <> struct AtVec<float, 128> {
+template <> struct AtV<float, 128> {
+  static constexpr int N = AT_C;
   typedef float2 raw;
-  __device__ static raw ld(const float* row, int lane) { return *(const float2*)(row + 2 * lane); }
+  __device__ static int key(int u, int) { return u; }
+  __device__ static int col(int lane) { return 2 * lane; }
+  __device__ static raw ld(const float* p) { return *(const float2*)p; }
   __device__ static void cvt(raw r, float* v) { v[0] = r.x; v[1] = r.y; }
 };
-template <> struct AtVec<float, 64> {
+template <> struct AtV<float, 64> {
+  static constexpr int N = AT_C;
   typedef float raw;
-  __device__ static raw ld(const float* row, int lane) { return row[lane]; }
+  __device__ static int key(int u, int) { return u; }
+  __device__ static int col(int lane) { return lane; }
+  __device__ static raw ld(const float* p) { return *p; }
   __device__ static void cvt(raw r, float* v) { v[0] = r; }
 };
+
+// 16x16x16 bf16 product: lane (g, i) supplies A[i][4g..4g+3] and
+// B[4g..4g+3][i] (four bf16 in two words), receives D[4g+r][i].
+__device__ __forceinline__ f32x4_t mma16k16(uint2 a, uint2 b, f32x4_t c) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
 
 template <typename T, int HD>
 __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
   constexpr int NKS = HD / KS;   // MFMA k-steps over the head dimension
-  constexpr int DPL = HD / 64;   // output dimensions per lane in the P.V step
-  typedef AtVec<T, HD> VV;
-  __shared__ __attribute__((aligned(16))) float sP[AT_W][AT_Q][AT_C];  // this chunk's probabilities, per wave
-  __shared__ float sAl[AT_W][AT_Q];            // this chunk's rescale of the running output
+  constexpr int DPL = HD / 64;   // output dimensions per lane in the fp32 P.V step
+  constexpr bool MFPV = sizeof(T) == 2;  // P.V on MFMA
+  constexpr int NT = HD / 16;    // MFMA tiles over the head dimension
+  constexpr int OP = HD + 4;     // padded LDS row of a wave's partial output
+  typedef AtV<T, HD> VV;
+  constexpr int NV = VV::N;
+  __shared__ __attribute__((aligned(16))) float sP[AT_W][AT_Q][AT_C];  // fp32: this chunk's probabilities, per wave
+  __shared__ float sAl[AT_W][AT_Q];            // fp32: this chunk's rescale of the running output
   __shared__ float sM[AT_W][AT_Q], sL[AT_W][AT_Q];
-  __shared__ float sO[AT_W][AT_Q][HD];
+  __shared__ __attribute__((aligned(16))) float sO[AT_W][AT_Q][OP];
   __shared__ int sLim[AT_Q];
   __shared__ int sAnc[AT_Q][EAGLE_MAX_DEPTH];
-  __shared__ float sWt[AT_W][AT_Q], sInvL[AT_Q];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int q = lane & 15, g = lane >> 4;
-  const int wg = blockIdx.x, split = blockIdx.y;
+  // split-major block order: consecutive blocks (which land on different
+  // XCDs) take the splits of one tile, so each XCD reads whole cache rows
+  // (every head of a row range) instead of one head's 256-byte slice of rows
+  const int split = blockIdx.x % p.nsplit, wg = blockIdx.x / p.nsplit;
   const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
   const int q0 = qt * AT_Q;
   const int P = clamp_prefix(a.prefix_len[b], a);
@@ -122,7 +164,8 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
 
   // the first chunk's K/V loads go out now, ahead of the query setup
   typedef typename VV::raw vraw;
-  auto load = [&](uint4 (&kr)[NKS], vraw (&vr)[AT_C], int c) __attribute__((always_inline)) {
+  const int vcol = VV::col(lane);
+  auto load = [&](uint4 (&kr)[NKS], vraw (&vr)[NV], int c) __attribute__((always_inline)) {
     c = min(c, c1 - 1);  // past the split's last chunk: repeat it (unused)
     if (c < cp) {  // consecutive prefix rows; the last chunk's tail repeats row Pv-1
       const int r0 = c * AT_C, rmax = Pv - 1 - r0;
@@ -130,20 +173,22 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
 #pragma unroll
       for (int s = 0; s < NKS; ++s) kr[s] = ld16(kp + s * KS + g * PER);
 #pragma unroll
-      for (int j = 0; j < AT_C; ++j) vr[j] = VV::ld(Vp + (size_t)(r0 + min(j, rmax)) * rs, lane);
+      for (int u = 0; u < NV; ++u) vr[u] = VV::ld(Vp + (size_t)(r0 + min(VV::key(u, g), rmax)) * rs + vcol);
     } else {
       const T* kp = krow(Kp, Kt, c, q);
 #pragma unroll
       for (int s = 0; s < NKS; ++s) kr[s] = ld16(kp + s * KS + g * PER);
 #pragma unroll
-      for (int j = 0; j < AT_C; ++j) vr[j] = VV::ld(krow(Vp, Vt, c, j), lane);
+      for (int u = 0; u < NV; ++u) vr[u] = VV::ld(krow(Vp, Vt, c, VV::key(u, g)) + vcol);
     }
   };
 
+  // this wave's chunks: c0+w, c0+w+AT_W, ... below c1 (a wave-uniform count);
+  // the first is in flight before the query setup
   uint4 ka[NKS], kb[NKS];
-  vraw va[AT_C], vb[AT_C];
-  const bool busy = c0 + w < c1;
-  if (busy) load(ka, va, c0 + w);
+  vraw va[NV], vb[NV];
+  const int nmine = __builtin_amdgcn_readfirstlane(c0 + w < c1 ? (c1 - 1 - c0 - w) / AT_W + 1 : 0);
+  if (nmine >= 1) load(ka, va, c0 + w);
 
   // ---- this lane's query operand (query q0+q, dims of k-step s for lane group g),
   // pre-scaled by 1/sqrt(hd); bf16 keeps a high and a low part
@@ -193,13 +238,18 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   // running softmax state of query q (replicated over the lane groups) and
   // this lane's output dimensions for all 16 queries
   float m = -INFINITY, l = 0.f;
-  float acc[AT_Q][DPL];
+  // bf16: query q's output at columns NT*(4g+r)+t in accm[t][r];
+  // fp32: this lane's DPL columns of every query in acc
+  f32x4_t accm[MFPV ? NT : 1];
+  float acc[MFPV ? 1 : AT_Q][DPL];
 #pragma unroll
-  for (int i = 0; i < AT_Q; ++i)
+  for (int t = 0; t < (MFPV ? NT : 1); ++t) accm[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < (MFPV ? 1 : AT_Q); ++i)
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
 
-  auto chunk = [&](const uint4 (&kr)[NKS], const vraw (&vr)[AT_C], int c) __attribute__((always_inline)) {
+  auto chunk = [&](const uint4 (&kr)[NKS], const vraw (&vr)[NV], int c) __attribute__((always_inline)) {
     // scores: lane (g, q) gets S^T[4g + r][q], r = 0..3
     f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -227,51 +277,77 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float mnew = fmaxf(m, cmax);
     const float al = (m == -INFINITY) ? 0.f : expf(m - mnew);
-    float ps = 0.f;
+    float pr4[4], ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float pr = sc[r] == -INFINITY ? 0.f : expf(sc[r] - mnew);
-      sP[w][q][4 * g + r] = pr;
-      ps += pr;
+      pr4[r] = sc[r] == -INFINITY ? 0.f : expf(sc[r] - mnew);
+      ps += pr4[r];
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l = l * al + ps;
     m = mnew;
-    if (g == 0) sAl[w][q] = al;
-    __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads
-    // P.V: this lane's output dimensions, every query of the tile
-    float v[AT_C][DPL];
+    if constexpr (MFPV) {
+      // lane (g, q) holds query q's probabilities of keys 4g..4g+3: the B
+      // operand of the 16x16x16 product as it stands.  A high and a low bf16
+      // part keep about 16 bits of each probability; V is exact in bf16.
+      uint32_t h[4], lo[4];
 #pragma unroll
-    for (int j = 0; j < AT_C; ++j) VV::cvt(vr[j], v[j]);
-#pragma unroll
-    for (int i = 0; i < AT_Q; ++i) {
-      const float ai = sAl[w][i];
-      float pr[AT_C];  // the query's 16 probabilities: four aligned 16-byte broadcast reads
-#pragma unroll
-      for (int u = 0; u < AT_C / 4; ++u) {
-        const float4 f = *(const float4*)&sP[w][i][4 * u];
-        pr[4 * u] = f.x;
-        pr[4 * u + 1] = f.y;
-        pr[4 * u + 2] = f.z;
-        pr[4 * u + 3] = f.w;
+      for (int r = 0; r < 4; ++r) {
+        h[r] = f2bf(pr4[r]);
+        lo[r] = f2bf(pr4[r] - bf2f(h[r]));
       }
-      float o[DPL];
+      const uint2 bh = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      const uint2 bl = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = acc[i][e] * ai;
+      for (int t = 0; t < NT; ++t) {
+        const uint2 av = make_uint2(VV::el(vr[0], t) | (VV::el(vr[1], t) << 16),
+                                    VV::el(vr[2], t) | (VV::el(vr[3], t) << 16));
+        f32x4_t o = accm[t] * al;
+        o = mma16k16(av, bh, o);
+        accm[t] = mma16k16(av, bl, o);
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < AT_C; ++j)
+      for (int r = 0; r < 4; ++r) sP[w][q][4 * g + r] = pr4[r];
+      if (g == 0) sAl[w][q] = al;
+      __builtin_amdgcn_wave_barrier();  // the wave's LDS writes before its reads
+      // P.V: this lane's output dimensions, every query of the tile
+      float v[AT_C][DPL];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] += pr[j] * v[j][e];
+      for (int j = 0; j < AT_C; ++j) VV::cvt(vr[j], v[j]);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[i][e] = o[e];
+      for (int i = 0; i < AT_Q; ++i) {
+        const float ai = sAl[w][i];
+        float pr[AT_C];  // the query's 16 probabilities: four aligned 16-byte broadcast reads
+#pragma unroll
+        for (int u = 0; u < AT_C / 4; ++u) {
+          const float4 f = *(const float4*)&sP[w][i][4 * u];
+          pr[4 * u] = f.x;
+          pr[4 * u + 1] = f.y;
+          pr[4 * u + 2] = f.z;
+          pr[4 * u + 3] = f.w;
+        }
+        float o[DPL];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = acc[i][e] * ai;
+#pragma unroll
+        for (int j = 0; j < AT_C; ++j)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[e] += pr[j] * v[j][e];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[i][e] = o[e];
+      }
+      __builtin_amdgcn_wave_barrier();  // reads done before the next chunk's writes
     }
-    __builtin_amdgcn_wave_barrier();  // reads done before the next chunk's writes
   };
 
-  // chunks w, w+AT_W, ...; two in flight (ping-pong register sets; a load
-  // past the last chunk repeats it and is unused)
-  if (busy) {
+  if (nmine == 1) {
+    // a single chunk (short prefixes, or many key splits): nothing to prefetch
+    chunk(ka, va, c0 + w);
+  } else if (nmine > 1) {
+    // two in flight (ping-pong register sets; a load past the wave's last
+    // chunk repeats the split's last chunk and is unused)
     for (int c = c0 + w;; c += 2 * AT_W) {
       load(kb, vb, c + AT_W);
       __builtin_amdgcn_sched_barrier(0);
@@ -289,51 +365,59 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     sM[w][q] = m;
     sL[w][q] = l;
   }
+  if constexpr (MFPV) {
 #pragma unroll
-  for (int i = 0; i < AT_Q; ++i)
+    for (int r = 0; r < 4; ++r) {  // NT consecutive columns per r
+      float* dst = &sO[w][q][NT * (4 * g + r)];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) sO[w][i][lane * DPL + e] = acc[i][e];
-  __syncthreads();
-  if (tid < AT_Q) {
-    float M = -INFINITY;
-    for (int ww = 0; ww < AT_W; ++ww)
-      if (sL[ww][tid] > 0.f) M = fmaxf(M, sM[ww][tid]);
-    float L = 0.f;
-    for (int ww = 0; ww < AT_W; ++ww) {
-      const float wt = sL[ww][tid] > 0.f ? expf(sM[ww][tid] - M) : 0.f;
-      sWt[ww][tid] = wt;
-      L += sL[ww][tid] * wt;
-    }
-    sInvL[tid] = L > 0.f ? 1.0f / L : 0.f;
-  }
-  __syncthreads();
-  if (p.nsplit == 1) {
-    for (int idx = tid; idx < AT_Q * HD; idx += AT_W * WAVE) {
-      const int i = idx / HD, dd = idx - i * HD, gq = q0 + i;
-      if (gq >= p.nq) continue;
-      float O = 0.f;
-#pragma unroll
-      for (int ww = 0; ww < AT_W; ++ww) O += sWt[ww][i] * sO[ww][i][dd];
-      const int row = b * p.RS + gq / p.g, head = kvh * p.g + gq % p.g;
-      El<T>::st((T*)a.attn, (size_t)row * HDq + head * HD + dd, O * sInvL[i]);
+      for (int t = 0; t < NT; t += 4)
+        *(float4*)(dst + t) = make_float4(accm[t][r], accm[t + 1][r], accm[t + 2][r], accm[t + 3][r]);
     }
   } else {
-    // partial of this split: [max, sum, unnormalised output] per query
-    float* part = a.apart + ((size_t)wg * p.nsplit + split) * AT_Q * (HD + 2);
-    for (int idx = tid; idx < AT_Q * HD; idx += AT_W * WAVE) {
-      const int i = idx / HD, dd = idx - i * HD;
-      float O = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < AT_W; ++ww) O += sWt[ww][i] * sO[ww][i][dd];
-      part[i * (HD + 2) + 2 + dd] = O;
+    for (int i = 0; i < AT_Q; ++i)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sO[w][i][lane * DPL + e] = acc[i][e];
+  }
+  __syncthreads();
+  {
+    // 32 threads per query: each weighs the waves itself (max over waves that
+    // saw a key, then exp(m_w - M)) and sums its DPT columns in wave order
+    constexpr int TPQ = AT_W * WAVE / AT_Q;
+    constexpr int DPT = HD / TPQ;
+    const int i = tid / TPQ, d0 = (tid % TPQ) * DPT, gq = q0 + i;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < AT_W; ++ww)
+      if (sL[ww][i] > 0.f) M = fmaxf(M, sM[ww][i]);
+    float L = 0.f, O[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) O[e] = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < AT_W; ++ww) {
+      const float lw = sL[ww][i];
+      const float wt = lw > 0.f ? expf(sM[ww][i] - M) : 0.f;
+      L += lw * wt;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) O[e] += wt * sO[ww][i][d0 + e];
     }
-    if (tid < AT_Q) {
-      float M = -INFINITY, L = 0.f;
-      for (int ww = 0; ww < AT_W; ++ww)
-        if (sL[ww][tid] > 0.f) M = fmaxf(M, sM[ww][tid]);
-      for (int ww = 0; ww < AT_W; ++ww) L += sL[ww][tid] * sWt[ww][tid];
-      part[tid * (HD + 2)] = M;
-      part[tid * (HD + 2) + 1] = L;
+    if (p.nsplit == 1) {
+      if (gq < p.nq) {
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+        const int row = b * p.RS + gq / p.g, head = kvh * p.g + gq % p.g;
+        const size_t o = (size_t)row * HDq + head * HD + d0;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) El<T>::st((T*)a.attn, o + e, O[e] * inv);
+      }
+    } else {
+      // partial of this split, per query: unnormalised output, then max and sum
+      float* part = a.apart + (((size_t)wg * p.nsplit + split) * AT_Q + i) * (HD + 4);
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) part[d0 + e] = O[e];
+      if (tid % TPQ == 0) {
+        part[HD] = M;
+        part[HD + 1] = L;
+      }
     }
   }
 }
@@ -349,22 +433,22 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPla
   const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
   const int q0 = qt * AT_Q;
   const int ns = p.nsplit;
-  const float* part = a.apart + (size_t)wg * ns * AT_Q * (HD + 2);
+  const float* part = a.apart + (size_t)wg * ns * AT_Q * (HD + 4);
   float ov[PT][AT_MAXS];
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
     const int idx = tid + u * AT_W * WAVE, i = idx / HD, dd = idx - i * HD;
 #pragma unroll
     for (int s = 0; s < AT_MAXS; ++s)
-      ov[u][s] = part[((size_t)min(s, ns - 1) * AT_Q + i) * (HD + 2) + 2 + dd];
+      ov[u][s] = part[((size_t)min(s, ns - 1) * AT_Q + i) * (HD + 4) + dd];
   }
   if (tid < AT_Q) {
     float mm[AT_MAXS], ll[AT_MAXS];
 #pragma unroll
     for (int s = 0; s < AT_MAXS; ++s) {
-      const float* ps = part + ((size_t)min(s, ns - 1) * AT_Q + tid) * (HD + 2);
-      mm[s] = ps[0];
-      ll[s] = s < ns ? ps[1] : 0.f;
+      const float* ps = part + ((size_t)min(s, ns - 1) * AT_Q + tid) * (HD + 4);
+      mm[s] = ps[HD];
+      ll[s] = s < ns ? ps[HD + 1] : 0.f;
     }
     float M = -INFINITY;
 #pragma unroll
@@ -395,7 +479,7 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPla
 template <typename T, int HD>
 static hipError_t launch_attn_t(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
   const int tiles = a.B * a.Hkv * p.nqt;
-  hipLaunchKernelGGL((k_attn<T, HD>), dim3(tiles, p.nsplit), dim3(AT_W * WAVE), 0, s, a, p);
+  hipLaunchKernelGGL((k_attn<T, HD>), dim3(tiles * p.nsplit), dim3(AT_W * WAVE), 0, s, a, p);
   if (p.nsplit > 1) hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(tiles), dim3(AT_W * WAVE), 0, s, a, p);
   return hipGetLastError();
 }

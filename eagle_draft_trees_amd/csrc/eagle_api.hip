@@ -43,13 +43,26 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   }
   p.mt = std::min(4, cdiv(std::min(M, 64), 16));
   p.zg = cdiv(M, 64);
+  p.ct = 4;
   p.nblk = cdiv(p.N, 64);
   const int kc = gemm_kc(p.nw, (int)elem_size(d));
   // K is split across workgroups only when the column blocks alone leave
   // more than half of the compute units idle; a split keeps two chunks or more
   const int base = p.nblk * p.zg;
   int S = 1;
-  if (base < 128) S = std::max(1, std::min(cdiv(256, base), cdiv(p.K, 2 * kc)));
+  if (base < 128) {
+    S = std::max(1, std::min(cdiv(256, base), cdiv(p.K, 2 * kc)));
+  } else if (op != OP_O) {
+    // unsplit: three column tiles per workgroup when that leaves fewer of the
+    // 256 compute units idle in the launch's last round of workgroups (the O
+    // launch keeps four: its blocks define the RMSNorm partials gate/up reads)
+    auto idle = [](int wgs) { return cdiv(wgs, 256) * 256 - wgs; };
+    const int n3 = cdiv(cdiv(p.N, 16), 3);
+    if (cdiv(n3 * p.zg, 256) <= cdiv(base, 256) && idle(n3 * p.zg) < idle(base)) {
+      p.ct = 3;
+      p.nblk = n3;
+    }
+  }
   p.Kc = cdiv(cdiv(p.K, S), kc) * kc;
   p.S = cdiv(p.K, p.Kc);
   p.nps = op == OP_GATEUP ? cdiv(d.d, 64) : 0;

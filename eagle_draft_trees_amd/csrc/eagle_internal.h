@@ -181,6 +181,7 @@ struct WsLayout {
 
 struct GemmPlan {
   int M, N, K, nw, mt, zg, nblk, S, Kc;
+  int ct;              // column tiles per workgroup (3 or 4; 4 whenever K is split)
   int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
   size_t part_floats;  // split-K partial floats (0 when S == 1)
 };
@@ -386,6 +387,13 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
 // e0/e1 (may be null): events stamped at the LM-head kernel's own start and end
+// Slab records of the LM head, field-major per row: field f (0 max, 1 sum of
+// exp, 2..k+1 the slab's top-k logits, k+2..2k+1 their token ids) of slab blk
+// of row `row` at lmpart[(row * rec + f) * nblk + blk], so a pass over one
+// field of every slab is contiguous.  Returns the address of field 0.
+__device__ __forceinline__ float* slab_field(float* lmpart, int row, int blk, const LmPlan& p) {
+  return lmpart + (size_t)row * p.rec * p.nblk + blk;
+}
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);

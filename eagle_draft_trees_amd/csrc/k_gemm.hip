@@ -4,15 +4,16 @@
 //   Y[M][N] = X[M][K] * W[N][K]^T,  M = frontier rows (B*k) or extend rows (B*m)
 //
 // At drafting shapes M is 1..64 while W is megabytes, so every kernel here is
-// bound by streaming W from HBM once.  A workgroup is four waves = 64 adjacent
-// output columns over one K range.  It stages the X rows of that K range in
-// LDS chunk by chunk (shared by the four waves), so the only global loads in
-// the main loop are W's: one 16-byte load per lane per k-step (16 rows x 64
-// contiguous bytes per wave instruction), eight k-steps in flight, each fed to
-// a 16x16 MFMA (bf16: v_mfma_f32_16x16x32_bf16; fp32: four 16x16x4 steps)
-// with its A operand read from LDS.  When the grid would be too small to keep
-// HBM busy, K is split across workgroups; each split writes fp32 partials and
-// the last workgroup to arrive (counter in the workspace) sums them in split
+// bound by streaming W from HBM once.  A workgroup holds CTW adjacent 16-column
+// tiles (four, or three where that leaves fewer compute units idle) times four
+// K slices, one wave each, over one K range.  It stages the X rows of that K
+// range in LDS chunk by chunk (shared by its waves), so the only global loads
+// in the main loop are W's: one 16-byte load per lane per k-step (one
+// contiguous kilobyte of the packed tile per wave instruction), each fed to a
+// 16x16 MFMA per m-tile (bf16: v_mfma_f32_16x16x32_bf16; fp32: four 16x16x4
+// steps) with its A operand read from LDS.  When the column blocks would leave
+// most compute units idle, K is split across workgroups (four-tile blocks
+// only); each split writes fp32 partials and k_gemm_fin sums them in split
 // order -- deterministic, no float atomics -- and runs the epilogue.
 //
 // Fused steps (draft head of [P1] "EAGLE 推测解码为什么比 Medusa 快？" §4.1 and
@@ -71,30 +72,35 @@ __device__ __forceinline__ void rstd_finish(const RoundArgs& a, float* sq, float
 
 // The ops' epilogues on one 64-column block of one z-group; tile[NW][ROWS][65]
 // in LDS holds the block's sums (all threads of the workgroup call this).
-template <typename T, int OP, int MT>
+template <typename T, int OP, int MT, int CTW>
 __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan& p, float* tile,
                                               const float* s_rstd, int blk, int zg, int tid) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
   constexpr int ROWS = MT * 16;
+  constexpr int BW = CTW * 16;  // columns of the block
+  static_assert(OP != OP_O || CTW == 4, "the O launch keeps 64-column blocks");
 #define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
   const int rows_here = min(ROWS, p.M - zg * 64);
   if (OP == OP_FC) {
-    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+    for (int idx = tid; idx < rows_here * BW; idx += (int)blockDim.x) {
+      const int mr = idx / BW, c = idx % BW, nn = blk * BW + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
       a.x0f[(size_t)row * a.d + nn] = v;
       El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
     }
   } else if (OP == OP_QKV) {
-    // the block's four tiles are tiles 4*blk .. 4*blk+3 of one head (hd/16
-    // tiles per head); tile j holds the rotation pairs (8j+e, hd/2+8j+e),
+    // the block's tiles are tiles CTW*blk .. CTW*blk+CTW-1 (hd/16 tiles per
+    // head); tile j of a head holds the rotation pairs (8j+e, hd/2+8j+e),
     // e < 8, in its columns e and 8+e
-    const int per = a.hd / 16, head = (4 * blk) / per, j0 = (4 * blk) % per, half = a.hd / 2;
+    const int per = a.hd / 16, half = a.hd / 2, ntile = (p.N + 15) / 16;
     const int hq = a.H, hk = a.Hkv;
-    for (int idx = tid; idx < rows_here * 32; idx += (int)blockDim.x) {
-      const int mr = idx >> 5, pr = idx & 31, ct = pr >> 3, e = pr & 7, row = zg * 64 + mr;
-      const int fi = 8 * (j0 + ct) + e;  // frequency index within the half
+    for (int idx = tid; idx < rows_here * CTW * 8; idx += (int)blockDim.x) {
+      const int mr = idx / (CTW * 8), pr = idx % (CTW * 8), ct = pr >> 3, e = pr & 7, row = zg * 64 + mr;
+      const int t = CTW * blk + ct;
+      if (t >= ntile) continue;
+      const int head = t / per;
+      const int fi = 8 * (t % per) + e;  // frequency index within the half
       float lo = TILE(0, mr, ct * 16 + e), hi = TILE(0, mr, ct * 16 + 8 + e);
       int b, slot, pos;
       if (a.mode == MODE_LEVEL) {
@@ -151,16 +157,16 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       a.ssq[(size_t)blk * a.rows + zg * 64 + tid] = s;
     }
   } else if (OP == OP_GATEUP) {
-    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+    for (int idx = tid; idx < rows_here * BW; idx += (int)blockDim.x) {
+      const int mr = idx / BW, c = idx % BW, nn = blk * BW + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float r = s_rstd[mr];
       const float g = TILE(0, mr, c) * r, u = TILE(NW - 1, mr, c) * r;
       El<T>::st((T*)a.act, xpk_index<T>(row, nn, (a.F + El<T>::KSTEP - 1) / El<T>::KSTEP), g / (1.0f + expf(-g)) * u);
     }
   } else {  // OP_DOWN
-    for (int idx = tid; idx < rows_here * 64; idx += (int)blockDim.x) {
-      const int mr = idx >> 6, c = idx & 63, nn = blk * 64 + c, row = zg * 64 + mr;
+    for (int idx = tid; idx < rows_here * BW; idx += (int)blockDim.x) {
+      const int mr = idx / BW, c = idx % BW, nn = blk * BW + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
       if (a.mode == MODE_LEVEL) {
@@ -177,8 +183,9 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
 #undef TILE
 }
 
-template <typename T, int OP, int MT>
-__global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
+template <typename T, int OP, int MT, int CTW>
+__global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPlan p) {
+  constexpr int THREADS = CTW * GW_KSW * 64;  // CTW column tiles x GW_KSW K slices
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
@@ -189,7 +196,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   constexpr int XST = KC * ES + 16;          // LDS row stride: an m-tile's 16 rows on different banks
   constexpr int XBUF = ROWS * XST;           // one X chunk
   constexpr int NPC = KC / PER;              // 16-byte pieces per row of a chunk
-  constexpr int XP = (ROWS * NPC + GW_THREADS - 1) / GW_THREADS;  // pieces per thread
+  constexpr int XP = (ROWS * NPC + THREADS - 1) / THREADS;  // pieces per thread
   // two X chunks [ROWS][KC] (double buffer); then the K-slice partials; then
   // the output tile
   extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
@@ -198,18 +205,18 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ct = wave & 3, ks = wave >> 2;  // column tile, K slice (of GW_KSW)
+  const int ct = wave % CTW, ks = wave / CTW;  // column tile, K slice (of GW_KSW)
   const int c = lane & 15, g = lane >> 4;
   const int blk = blockIdx.x, split = blockIdx.y, zg = blockIdx.z;
   const int cl = ct * 16 + c;
   const int K = p.K;
 
-  // ---- this lane's packed weight tile, 4*blk + ct (a tile past the last
+  // ---- this lane's packed weight tile, CTW*blk + ct (a tile past the last
   // reads tile 0, discarded; rows past N within a tile are zero)
   const int nks = (K + KS - 1) / KS;
   const T* wr[NW];
   {
-    const int t = 4 * blk + ct, tt = t < (p.N + 15) / 16 ? t : 0;
+    const int t = CTW * blk + ct, tt = t < (p.N + 15) / 16 ? t : 0;
     if (OP == OP_QKV) wr[0] = qkv_tile<T>(a, tt, nks, lane);
     if (OP == OP_FC) wr[0] = wtile_base<T>(a.fc_w, nks, tt, lane);
     if (OP == OP_O) wr[0] = wtile_base<T>(a.wo, nks, tt, lane);
@@ -226,7 +233,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   // accepted length, the bonus token becomes the next root).  Nothing in this
   // launch reads either field, so one workgroup does it without an election.
   if (OP == OP_DOWN && a.mode == MODE_EXTEND && blk == 0 && split == 0 && zg == 0) {
-    for (int b = tid; b < a.B; b += GW_THREADS) {
+    for (int b = tid; b < a.B; b += THREADS) {
       int alen = a.accept_len[b];
       alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
       a.prefix_len[b] = clamp_prefix(a.prefix_len[b], a) + alen;
@@ -303,7 +310,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   // consecutive threads read consecutive 16 bytes; a row group past M reads
   // the group's first row group instead (its rows are never stored).
   auto xpiece = [&](int q, int& r, int& pc) __attribute__((always_inline)) {
-    const int i = min(tid + q * GW_THREADS, ROWS * NPC - 1);
+    const int i = min(tid + q * THREADS, ROWS * NPC - 1);
     if (OP == OP_DOWN) {
       constexpr int SPC = KC / KS;  // k-steps per chunk
       const int z = i / (SPC * 64), rem = i - z * (SPC * 64), sl = rem >> 6, l = rem & 63;
@@ -412,7 +419,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
     for (int w = 0; w < NW; ++w)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        red[(((ks - 1) * 4 + ct) * (NW * MT) + w * MT + mt) * WAVE + lane] = acc[w][mt];
+        red[(((ks - 1) * CTW + ct) * (NW * MT) + w * MT + mt) * WAVE + lane] = acc[w][mt];
   }
   __syncthreads();
   const bool fin = ks == 0;
@@ -422,13 +429,13 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[w][mt] += red[((s * 4 + ct) * (NW * MT) + w * MT + mt) * WAVE + lane];
+        for (int mt = 0; mt < MT; ++mt) acc[w][mt] += red[((s * CTW + ct) * (NW * MT) + w * MT + mt) * WAVE + lane];
   }
 
   // ---- split K: the partials go to the workspace and k_gemm_fin sums them
   if (p.S > 1) {
     if (fin) {
-      float* part = a.gpart + (((((size_t)zg * p.nblk + blk) * p.S + split) * 4 + ct) * (NW * MT) * 64) * 4;
+      float* part = a.gpart + (((((size_t)zg * p.nblk + blk) * p.S + split) * CTW + ct) * (NW * MT) * 64) * 4;
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
@@ -449,7 +456,7 @@ __global__ void __launch_bounds__(GW_THREADS) k_gemm(RoundArgs a, GemmPlan p) {
   }
   if (OP == OP_GATEUP) rstd_finish<ROWS>(a, tile + NW * ROWS * 65, ssq_part, s_rstd, tid);
   __syncthreads();
-  gemm_epilogue<T, OP, MT>(a, p, tile, s_rstd, blk, zg, tid);
+  gemm_epilogue<T, OP, MT, CTW>(a, p, tile, s_rstd, blk, zg, tid);
 }
 
 // Sum of a split GEMM's partials for one 64-column block of one z-group, in
@@ -491,21 +498,34 @@ __global__ void __launch_bounds__(GW_FIN_THREADS) k_gemm_fin(RoundArgs a, GemmPl
   }
   if (OP == OP_GATEUP) rstd_finish<ROWS>(a, tile + NW * ROWS * 65, ssq_part, s_rstd, tid);
   __syncthreads();
-  gemm_epilogue<T, OP, MT>(a, p, tile, s_rstd, blk, zg, tid);
+  gemm_epilogue<T, OP, MT, 4>(a, p, tile, s_rstd, blk, zg, tid);
+}
+
+template <typename T, int OP, int CTW>
+static void launch_main(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
+  const dim3 grid(p.nblk, p.S, p.zg), block(CTW * GW_KSW * 64);
+  const size_t lds = gemm_lds_bytes(p, (int)sizeof(T));
+  switch (p.mt) {
+    case 1: hipLaunchKernelGGL((k_gemm<T, OP, 1, CTW>), grid, block, lds, s, a, p); break;
+    case 2: hipLaunchKernelGGL((k_gemm<T, OP, 2, CTW>), grid, block, lds, s, a, p); break;
+    case 3: hipLaunchKernelGGL((k_gemm<T, OP, 3, CTW>), grid, block, lds, s, a, p); break;
+    default: hipLaunchKernelGGL((k_gemm<T, OP, 4, CTW>), grid, block, lds, s, a, p); break;
+  }
 }
 
 template <typename T, int OP>
 static hipError_t launch_op(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
-  const dim3 grid(p.nblk, p.S, p.zg), block(GW_THREADS);
-  const size_t lds = gemm_lds_bytes(p, (int)sizeof(T));
-  const dim3 fgrid(p.nblk, 1, p.zg);
-  switch (p.mt) {
-    case 1: hipLaunchKernelGGL((k_gemm<T, OP, 1>), grid, block, lds, s, a, p); break;
-    case 2: hipLaunchKernelGGL((k_gemm<T, OP, 2>), grid, block, lds, s, a, p); break;
-    case 3: hipLaunchKernelGGL((k_gemm<T, OP, 3>), grid, block, lds, s, a, p); break;
-    default: hipLaunchKernelGGL((k_gemm<T, OP, 4>), grid, block, lds, s, a, p); break;
+  if constexpr (OP != OP_O) {
+    if (p.ct == 3) {
+      if (p.S != 1) return hipErrorInvalidValue;  // three-tile blocks are never split
+      launch_main<T, OP, 3>(a, p, s);
+      return hipGetLastError();
+    }
   }
+  if (p.ct != 4) return hipErrorInvalidValue;
+  launch_main<T, OP, 4>(a, p, s);
   if (p.S > 1) {
+    const dim3 fgrid(p.nblk, 1, p.zg);
     switch (p.mt) {
       case 1: hipLaunchKernelGGL((k_gemm_fin<T, OP, 1>), fgrid, dim3(GW_FIN_THREADS), 0, s, a, p); break;
       case 2: hipLaunchKernelGGL((k_gemm_fin<T, OP, 2>), fgrid, dim3(GW_FIN_THREADS), 0, s, a, p); break;

@@ -150,11 +150,11 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
     }
     const float mx = wave_max_dpp(x);
     const float s = wave_sum_dpp(x == -INFINITY ? 0.f : expf(x - mx));
-    float* rec = a.lmpart + ((size_t)row * p.nblk + blk) * p.rec;
-    if (lane == 0) { rec[0] = mx; rec[1] = s; }
+    float* rec = slab_field(a.lmpart, row, blk, p);  // field f at rec[f * nblk]
+    if (lane == 0) { rec[0] = mx; rec[p.nblk] = s; }
     if (rank < kk_) {
-      rec[2 + rank] = x;
-      rec[2 + kk_ + rank] = __int_as_float(x == -INFINITY ? -1 : blk * 64 + lane);
+      rec[(2 + rank) * p.nblk] = x;
+      rec[(2 + kk_ + rank) * p.nblk] = __int_as_float(x == -INFINITY ? -1 : blk * 64 + lane);
     }
   }
 }
@@ -224,10 +224,10 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
 #pragma unroll
     for (int u = 0; u < 4; ++u) se += x[u] == -INFINITY ? 0.f : expf(x[u] - mx);
     se = wave_sum_dpp(se);
-    float* rec = a.lmpart + ((size_t)row * p.nblk + blockIdx.x) * p.rec;
+    float* rec = slab_field(a.lmpart, row, blockIdx.x, p);  // field f at rec[f * nblk]
     if (lane == 0) {
       rec[0] = mx;
-      rec[1] = se;
+      rec[p.nblk] = se;
     }
     unsigned long long mine = 0ull;  // lane r: the r-th entry
     for (int r = 0; r < kk_; ++r) {
@@ -241,8 +241,8 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
       if (lane == r) mine = win;
     }
     if (lane < kk_) {
-      rec[2 + lane] = mine ? argkey_value(mine) : -INFINITY;
-      rec[2 + kk_ + lane] = __int_as_float(mine ? argkey_id(mine) : -1);
+      rec[(2 + lane) * p.nblk] = mine ? argkey_value(mine) : -INFINITY;
+      rec[(2 + kk_ + lane) * p.nblk] = __int_as_float(mine ? argkey_id(mine) : -1);
     }
   }
 }

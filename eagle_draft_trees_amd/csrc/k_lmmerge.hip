@@ -83,11 +83,11 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
       int hi[NL];
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
-        const float* rc = base + (size_t)min(bb0 + lane + WAVE * u, nblk - 1) * rec;
+        const float* rc = base + min(bb0 + lane + WAVE * u, nblk - 1);  // field f at rc[f * nblk]
         mv[u] = rc[0];
-        sv[u] = rc[1];
-        hv[u] = rc[2];
-        hi[u] = __float_as_int(rc[2 + kk_]);
+        sv[u] = rc[nblk];
+        hv[u] = rc[2 * nblk];
+        hi[u] = __float_as_int(rc[(2 + kk_) * nblk]);
       }
 #pragma unroll
       for (int u = 0; u < NL; ++u) {
@@ -140,11 +140,11 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
     for (int t = 0; t < 4; ++t) {
       const int c = lane + WAVE * t, j = c / kk_, e = c - j * kk_;
       const int sl = __shfl(mysel, j < WAVE ? j : 0);
-      const float* rc = base + (size_t)sl * rec;
+      const float* rc = base + sl;
       key[t] = 0ull;
       if (c < nsel * kk_) {
-        const int id = __float_as_int(rc[2 + kk_ + e]);
-        key[t] = id < 0 ? 0ull : argkey(rc[2 + e], id);
+        const int id = __float_as_int(rc[(2 + kk_ + e) * nblk]);
+        key[t] = id < 0 ? 0ull : argkey(rc[(2 + e) * nblk], id);
       }
     }
     unsigned long long mine = 0ull;  // lane q: the row's q-th entry

@@ -140,6 +140,177 @@ __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, 
   }
 }
 
+// Bitonic sort, descending, of a wave's 64*KPL keys held in registers:
+// element i = lane*KPL + j is key[j] of lane `lane`.  A compare-exchange at
+// stride below KPL is inside a lane's registers; a larger one pairs lane with
+// lane ^ (stride/KPL) through lane shuffles.  No LDS and no barriers.
+template <int KPL>
+__device__ __forceinline__ void wave_sort_desc(unsigned long long (&key)[KPL], int lane) {
+  constexpr int N = 64 * KPL;
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= KPL) {
+        const int lm = stride / KPL;
+        const bool lo = (lane & lm) == 0;  // the lower element of its pair
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const bool desc = ((lane * KPL + j) & size) == 0;
+          const unsigned long long x = key[j];
+          const unsigned long long y =
+              ((unsigned long long)(unsigned)__shfl_xor((int)(unsigned)(x >> 32), lm) << 32) |
+              (unsigned long long)(unsigned)__shfl_xor((int)(unsigned)x, lm);
+          key[j] = (x > y) == (lo == desc) ? x : y;  // a descending pair's lower element keeps the max
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          if (j & stride) continue;
+          const int jj = j | stride;
+          const bool desc = ((lane * KPL + j) & size) == 0;
+          const unsigned long long x = key[j], y = key[jj];
+          const bool sw = (x < y) == desc;
+          key[j] = sw ? y : x;
+          key[jj] = sw ? x : y;
+        }
+      }
+    }
+  }
+}
+
+// The same rerank and build in one wave per sequence, for pools of at most
+// 64*KPL entries: the pool is copied to LDS once, its keys are sorted in
+// registers (wave_sort_desc), and one lane per kept node does the flatten
+// (depth by depth, its rank among the kept nodes of its depth by (parent's
+// flat index, pool index)) and its mask row.  Results are those of k_rerank.
+template <int KPL>
+__global__ void __launch_bounds__(WAVE) k_rerank_wave(RoundArgs a, int32_t* tokens, int32_t* parents,
+                                                      int32_t* depth, int32_t* positions, uint8_t* mask,
+                                                      float* logscore) {
+  constexpr int NMAX = 64 * KPL;
+  constexpr int QPL = NMAX * 3 / 64;  // 8-byte pieces of the pool per lane (3 per entry)
+  __shared__ eagle_pool_entry sp[NMAX];
+  __shared__ short flat_of[NMAX];
+  __shared__ int sel[EAGLE_MAX_TREE];
+  __shared__ __attribute__((aligned(16))) unsigned sk2[WAVE];
+  __shared__ int fpar[EAGLE_MAX_TREE], fdep[EAGLE_MAX_TREE];
+  __shared__ unsigned long long fanc[EAGLE_MAX_TREE];
+
+  const int lane = threadIdx.x, b = blockIdx.x;
+  const int n = a.pool_n, m = a.m, ns = m - 1;
+  {  // the pool into LDS, every load issued before any store
+    const unsigned long long* src = (const unsigned long long*)(a.pool + (size_t)b * n);
+    unsigned long long* dst = (unsigned long long*)sp;
+    const int nq = n * 3;
+    unsigned long long v[QPL];
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) v[u] = src[min(lane + WAVE * u, nq - 1)];
+#pragma unroll
+    for (int u = 0; u < QPL; ++u)
+      if (lane + WAVE * u < nq) dst[lane + WAVE * u] = v[u];
+    for (int e = lane; e < n; e += WAVE) flat_of[e] = -1;
+  }
+  __syncthreads();
+
+  // keys (score desc, depth asc, index asc) as unsigned integers; padding is 0
+  unsigned long long key[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = lane * KPL + j;
+    key[j] = 0ull;
+    if (e < n) {
+      uint32_t u = __float_as_uint(sp[e].score);
+      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      key[j] = ((unsigned long long)u << 32) | ((unsigned long long)(255 - (sp[e].depth & 255)) << 24) |
+               (unsigned long long)(0xFFFFFF - e);
+    }
+  }
+  wave_sort_desc<KPL>(key, lane);
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int i = lane * KPL + j;
+    if (i < ns) sel[i] = 0xFFFFFF - (int)(key[j] & 0xFFFFFFull);
+  }
+  __syncthreads();
+
+  // pool records are device data: keep depth in 1..D and parents inside the pool
+  const bool act = lane < ns;
+  int e = 0, dep = 0, par = -1;
+  if (act) {
+    e = sel[lane];
+    dep = min(max(sp[e].depth, 1), a.D);
+    par = sp[e].parent;
+    if (par < 0 || par >= n) par = -1;
+  }
+  int base = 1;
+  for (int dd = 1; dd <= a.D; ++dd) {
+    const bool mine = act && dep == dd;
+    const unsigned k2 =
+        mine ? (((unsigned)(par < 0 ? 0 : (int)flat_of[par] & 0xFFFF) << 16) | (unsigned)e) : 0xFFFFFFFFu;
+    sk2[lane] = k2;
+    __syncthreads();
+    int rank = 0;
+#pragma unroll
+    for (int u = 0; u < WAVE; u += 4) {
+      const uint4 q = *(const uint4*)&sk2[u];
+      rank += (q.x < k2 ? 1 : 0) + (q.y < k2 ? 1 : 0) + (q.z < k2 ? 1 : 0) + (q.w < k2 ? 1 : 0);
+    }
+    if (mine) flat_of[e] = (short)(base + rank);
+    base += __popcll(__ballot(mine));
+    __syncthreads();
+  }
+
+  const int P = clamp_prefix(a.prefix_len[b], a);
+  int32_t* tk = tokens + (size_t)b * m;
+  int32_t* pa = parents + (size_t)b * m;
+  fpar[lane] = lane == 0 ? -1 : 0;
+  fdep[lane] = 0;
+  if (lane == 0) {
+    tk[0] = clamp_tok(a.root_token[b], a.V, a.err);
+    pa[0] = -1;
+    if (depth) depth[(size_t)b * m] = 0;
+    if (positions) positions[(size_t)b * m] = P - 1;
+    if (logscore) logscore[(size_t)b * m] = 0.f;
+  }
+  __syncthreads();
+  if (act && flat_of[e] >= 1 && flat_of[e] < m) {
+    const int f = flat_of[e];
+    const int pf = (par < 0 || flat_of[par] < 0) ? 0 : flat_of[par];
+    tk[f] = sp[e].token;
+    pa[f] = pf;
+    if (depth) depth[(size_t)b * m + f] = dep;
+    if (positions) positions[(size_t)b * m + f] = P - 1 + dep;
+    if (logscore) logscore[(size_t)b * m + f] = sp[e].score;
+    fpar[f] = pf;
+    fdep[f] = dep;
+  }
+  // ancestor bitmasks, depth by depth (a parent precedes its children); lane f
+  // holds flat node f's
+  unsigned long long anc = lane == 0 ? 1ull : 0ull;
+  fanc[lane] = anc;
+  __syncthreads();
+  const int myd = fdep[lane], myp = fpar[lane];
+  for (int dd = 1; dd <= a.D; ++dd) {
+    if (lane > 0 && lane < m && myd == dd && myp < lane) {
+      anc = fanc[myp] | (1ull << lane);
+      fanc[lane] = anc;
+    }
+    __syncthreads();
+  }
+  if (mask && lane < m) {  // lane f writes mask row f
+    uint8_t* row = mask + ((size_t)b * m + lane) * m;
+    if ((m & 3) == 0 && ((uintptr_t)mask & 3) == 0) {
+      for (int c = 0; c < m; c += 4) {
+        const unsigned x = (unsigned)(anc >> c) & 0xFu;
+        ((unsigned*)row)[c >> 2] = (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+      }
+    } else {
+      for (int c = 0; c < m; ++c) row[c] = (uint8_t)((anc >> c) & 1ull);
+    }
+  }
+}
+
 // Greedy verify, one workgroup (16 waves) per sequence.  [P4] EAGLE-2 diagram:
 // accept the longest consistent path from the root and back off to the last
 // accepted node; the target's choice there is the bonus token.
@@ -209,8 +380,17 @@ __global__ void k_zero(uint4* p, size_t n16) {
 
 hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
                          int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s) {
-  hipLaunchKernelGGL(k_rerank, dim3(a.B), dim3(BLOCK), 0, s, a, tokens, parents, depth, positions,
-                     mask, logscore);
+  int np = 1;
+  while (np < a.pool_n) np <<= 1;
+  if (np <= 64 * 8)
+    hipLaunchKernelGGL(k_rerank_wave<8>, dim3(a.B), dim3(WAVE), 0, s, a, tokens, parents, depth, positions,
+                       mask, logscore);
+  else if (np <= 64 * 16)
+    hipLaunchKernelGGL(k_rerank_wave<16>, dim3(a.B), dim3(WAVE), 0, s, a, tokens, parents, depth, positions,
+                       mask, logscore);
+  else
+    hipLaunchKernelGGL(k_rerank, dim3(a.B), dim3(BLOCK), 0, s, a, tokens, parents, depth, positions,
+                       mask, logscore);
   return hipGetLastError();
 }
 

@@ -96,6 +96,9 @@ _add(TreeConfig("hd128_bf16", 13, "bf16", 2, 256, 2, 2, 128, 264, 777, 3, 100, 5
 _add(TreeConfig("chain_small", 14, "f32", 5, 128, 2, 2, 64, 256, 515, 7, 70, 6, 1, 6))
 _add(TreeConfig("wide_bf16", 15, "bf16", 2, 256, 4, 2, 64, 512, 2048, 20, 90, 4, 16, 64,
                 norm_gain_noise=True))
+# a pool above 1024 entries (16 + 4*256): the rerank's LDS-sort path
+_add(TreeConfig("deep_bf16", 16, "bf16", 2, 256, 4, 2, 64, 512, 2048, 20, 90, 5, 16, 64,
+                norm_gain_noise=True))
 
 
 def config_by_name(name: str) -> TreeConfig:

@@ -470,6 +470,37 @@ def test_repeat_runs_are_bit_identical(name):
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "7b"])
+def test_graph_replay_matches_eager(name):
+    """A round captured in a HIP graph and replayed several times, each replay
+    after the state is reloaded eagerly, gives the eager round's results bit
+    for bit every time."""
+    import torch
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[graph replay] {name}")
+    snap = lambda: ([t.cpu().numpy().copy() for t in (r.tokens, r.parents, r.mask, r.logscore,
+                                                       r.accept_len, r.bonus, r.prefix_len,
+                                                       r.root_token)]
+                    + [to_host(r.root_feat).copy()])
+    r.run_round()
+    sync()
+    ref = snap()
+    stream = torch.cuda.Stream()
+    r.reset_state(inp)
+    sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        r.run_round(stream=stream)
+    sync()
+    for rep in range(3):
+        r.reset_state(inp)
+        sync()
+        g.replay()
+        sync()
+        for a_, b_ in zip(ref, snap()):
+            assert np.array_equal(a_, b_), f"replay {rep}"
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "7b"])
 def test_timed_level_matches_plain(name):
     """eagle_draft_level_timed drafts the same tree as eagle_draft_level, and the
     events it hands to the LM-head launch bracket a positive time that lies

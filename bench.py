@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -115,6 +116,56 @@ def cpu_baseline(cfg, inp, budget_s: float) -> dict:
                       f"{el:.1f} s, fp64 NumPy"}
 
 
+def batched_lmhead(torch, L, dev, stream, rows=512, vocab=128256, d=4096, reps=10) -> dict:
+    """The LM-head GEMM batched over `rows` rows at the large-vocabulary chain
+    workload's shape (vocab 128256, d 4096; 512 = its batch x tree rows): a
+    level-1 LM-head-only call on a batch of `rows` sequences (the same kernel a
+    level with more than 16 rows runs, logits reduced to slab records on chip),
+    timed with kernel-stamped HIP events.  MFMA utilisation = 2*rows*vocab*d
+    FLOP per launch over the dense bf16 MFMA peak."""
+    import numpy as np
+    H, hd, F = 32, 128, 14336
+    dims = L.EagleDims(d, H, H, hd, F, vocab, L.EAGLE_BF16, 1e-6, 1e4)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    shapes = {"fc_w": (d, 2 * d), "fc_b": (d,), "wq": (H * hd, d), "wk": (H * hd, d),
+              "wv": (H * hd, d), "wo": (d, H * hd), "post_norm": (d,), "w_gate": (F, d),
+              "w_up": (F, d), "w_down": (d, F), "embed": (vocab, d)}
+    w = {n: torch.zeros(sh, **bf) for n, sh in shapes.items()}  # not read by an LM-head-only call
+    w["lm_head"] = torch.randn(vocab, d, generator=gen, **bf) * (3.0 / d ** 0.5)
+    wpack = torch.empty(L.eagle_packed_weights_bytes(dims), dtype=torch.uint8, device=dev)
+    wts = L.eagle_pack_weights(dims, L.make_weights(w), wpack)
+    tcfg = L.EagleTreeCfg(rows, 2, 1, 2, 4)
+    kc = torch.zeros(rows, 4, H, hd, **bf)
+    vc = torch.zeros(rows, 4, H, hd, **bf)
+    plen = torch.full((rows,), 2, dtype=torch.int32, device=dev)
+    feat = torch.randn(rows, d, generator=gen, **bf)
+    tok = torch.zeros(rows, dtype=torch.int32, device=dev)
+    state = L.make_state(kc, vc, plen, feat, tok)
+    ws = torch.empty(L.eagle_workspace_bytes(dims, tcfg), dtype=torch.uint8, device=dev)
+    L.eagle_workspace_init(dims, tcfg, ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        for q in ev:  # torch creates events on their first record
+            for e in q:
+                e.record(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        L.eagle_draft_level(dims, wts, tcfg, state, 1, L.EAGLE_LEVEL_LMHEAD_ONLY, ws, stream)
+        for e0, e1 in ev:
+            L.eagle_draft_level_timed(dims, wts, tcfg, state, 1, L.EAGLE_LEVEL_LMHEAD_ONLY, ws,
+                                      e0, e1, stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    tflops = 2.0 * rows * vocab * d / (ms * 1e-3) / 1e12
+    return {"kernel": "k_lmhead (LM-head GEMM + per-slab softmax/top-k, rows > 16)",
+            "rows": rows, "vocab": vocab, "d": d, "bound": "mfma",
+            "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(ms * 1e3, 1),
+            "launches": reps}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +176,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the batched LM-head GEMM measurement")
     ap.add_argument("--lmhead-only", type=int, default=0,
                     help="only launch the LM-head kernel this many times (counter runs)")
     args = ap.parse_args()
@@ -267,6 +320,8 @@ def main() -> int:
                      "bytes_per_launch": int(ab["lm_head_per_launch"]),
                      "traffic": traffic},
     }
+    if not args.no_batched:
+        out["mfma_batched_lmhead"] = batched_lmhead(torch, L, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)

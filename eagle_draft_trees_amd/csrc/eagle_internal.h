@@ -209,6 +209,7 @@ struct SkPlan {
 struct LmPlan {
   int M, mt, zg, nblk, rec;  // rec = floats per (row, slab) partial; nblk = slabs
   int sk, CT, KSW, xlds;     // sk: streaming-core kernel (M <= 16), CT tiles x KSW waves
+  int big;                   // bf16 and more than 64 rows: the tiled GEMM (k_lmgemm), zg groups of 512 rows
   size_t part_floats;
 };
 
@@ -386,6 +387,8 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 // launchers (return a hipError_t)
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
+hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1);
 // e0/e1 (may be null): events stamped at the LM-head kernel's own start and end
 // Slab records of the LM head, field-major per row: field f (0 max, 1 sum of
 // exp, 2..k+1 the slab's top-k logits, k+2..2k+1 their token ids) of slab blk

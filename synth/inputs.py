@@ -99,6 +99,9 @@ _add(TreeConfig("wide_bf16", 15, "bf16", 2, 256, 4, 2, 64, 512, 2048, 20, 90, 4,
 # a pool above 1024 entries (16 + 4*256): the rerank's LDS-sort path
 _add(TreeConfig("deep_bf16", 16, "bf16", 2, 256, 4, 2, 64, 512, 2048, 20, 90, 5, 16, 64,
                 norm_gain_noise=True))
+# more than 64 LM-head rows (80 at level 1, 160 after): the tiled batched
+# LM-head GEMM; a vocabulary that ends inside a 128-column block
+_add(TreeConfig("batch_bf16", 17, "bf16", 80, 256, 4, 2, 64, 512, 3000, 8, 40, 3, 2, 6))
 
 
 def config_by_name(name: str) -> TreeConfig:

@@ -62,6 +62,10 @@ Readings of what the pages leave open (each also listed in the design doc):
       this is the E[N] = 1 + ... convention of [P1] §8.
   R12 greedy verification (argmax, lowest id on exact ties).
   R13 exactly one decoder layer.
+  R14 target-side tree verify (the next step after the round, [P1] §6.2,
+      [P4] EAGLE-2 diagram stage two): the tree tokens' keys and values sit in
+      the target's cache right after the prefix, in flat order; query i sees
+      every prefix row and tree row j iff mask[i, j] is set.
 
 Parity pins: every function below is pinned by a CPU test (tests/
 test_oracle_*.py) against brute force, closed forms, special cases or the
@@ -82,7 +86,7 @@ __all__ = [
     "widen", "Model", "SeqState", "PoolEntry", "FrontierNode", "rope", "rms_norm", "silu",
     "attend_row", "draft_rows", "finish_rows", "lm_logits", "lm_tail", "level_one",
     "level_step_forward", "level_step_tail", "rerank", "build_tree", "verify_greedy",
-    "draft_extend", "run_round", "RoundResult", "NEAR_TIE",
+    "draft_extend", "run_round", "RoundResult", "NEAR_TIE", "tree_verify_attention",
 ]
 
 NEAR_TIE = 1e-3  # a selection whose margin (log domain) is below this is "near-tie"
@@ -437,6 +441,22 @@ def verify_greedy(target_logits: np.ndarray, tokens: np.ndarray, parents: np.nda
             return path, len(path), best, margins
         node = child[0]
         path.append(node)
+
+
+def tree_verify_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, P: int,
+                          mask: np.ndarray) -> np.ndarray:
+    """Target-side tree-verify attention of one sequence ([P1] §6.2: the target
+    scores every tree node in one forward with tree attention; [P4] EAGLE-2
+    diagram, stage two: a node sees only its ancestors and itself; R14).
+    q [m, H, hd] post-RoPE; k_cache/v_cache [>= P+m, Hkv, hd] with the prefix
+    in rows 0..P-1 and the flat tree nodes in rows P..P+m-1; mask [m, m]
+    (nonzero: visible).  Returns [m, H*hd]."""
+    m = q.shape[0]
+    out = np.empty((m, q.shape[1] * q.shape[2]), dtype=np.float64)
+    for i in range(m):
+        rows = list(range(P)) + [P + j for j in range(m) if mask[i, j]]
+        out[i] = attend_row(q[i], k_cache[rows], v_cache[rows])
+    return out
 
 
 # --------------------------------------------------------------------------- extend

@@ -166,6 +166,47 @@ def batched_lmhead(torch, L, dev, stream, rows=512, vocab=128256, d=4096, reps=1
             "launches": reps}
 
 
+def tree_verify(torch, L, r, cfg, stream, reps=50) -> dict:
+    """Target-side tree-verify attention at the round's shape: the m flattened
+    tree tokens of each sequence attend to its prefix and, through the mask the
+    round just built, to their ancestors' rows (appended after the prefix).
+    Timed with HIP events around a graph of `reps` back-to-back calls
+    (attention and its split merge); bytes = the K/V rows read plus q, mask and
+    output."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    gen = torch.Generator(device=r.device)
+    gen.manual_seed(1)
+    q = torch.randn(cfg.B, cfg.m, cfg.H, cfg.hd, generator=gen, device=r.device, dtype=torch.float32)
+    out = torch.empty(cfg.B, cfg.m, cfg.H * cfg.hd, device=r.device,
+                      dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
+    call = lambda: L.eagle_tree_verify_attention(r.dims, r.tcfg, q, r.k_cache, r.v_cache, r.prefix_len,
+                                                 r.mask, out, r.ws, stream)
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()  # launched as the round is: from a graph
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            call()
+    torch.cuda.synchronize()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    P = (cfg.P_lo + cfg.P_hi) / 2.0
+    nbytes = cfg.B * ((P + cfg.m) * cfg.Hkv * cfg.hd * 2 * es + cfg.m * cfg.H * cfg.hd * (4 + es)
+                      + cfg.m * cfg.m)
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "k_attn + k_attn_merge (tree verify mode)", "bound": "hbm",
+            "us_per_call": round(us, 2), "bytes_per_call": int(nbytes), "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "timing": f"HIP events around a graph of {reps} back-to-back calls"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -320,6 +361,7 @@ def main() -> int:
                      "bytes_per_launch": int(ab["lm_head_per_launch"]),
                      "traffic": traffic},
     }
+    out["tree_verify_attention"] = tree_verify(torch, L, r, cfg, stream)
     if not args.no_batched:
         out["mfma_batched_lmhead"] = batched_lmhead(torch, L, dev, stream)
     if not args.no_cpu_baseline:

@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
             "eagle_draft_level_timed": (c_int32, [P(EagleDims), P(EagleWeights), P(EagleTreeCfg),
                                                   P(EagleSeqState), c_int32, c_int32, c_void_p,
                                                   c_size_t, c_void_p, c_void_p, c_void_p]),
+            "eagle_tree_verify_attention": (c_int32, [P(EagleDims), P(EagleTreeCfg), c_void_p,
+                                                      c_void_p, c_void_p, c_void_p, c_void_p,
+                                                      c_void_p, c_void_p, c_size_t, c_void_p]),
             "eagle_rerank_build_tree": (c_int32, [P(EagleDims), P(EagleTreeCfg), P(EagleSeqState),
                                                   c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                                   c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -195,6 +198,14 @@ def eagle_draft_level_timed(dims, weights, cfg, state, level, flags, ws, start_e
                                          _ptr(ws), _nbytes(ws), _event(start_event),
                                          _event(stop_event), _stream(stream)),
            f"eagle_draft_level_timed({level})")
+
+
+def eagle_tree_verify_attention(dims, cfg, q, k_cache, v_cache, prefix_len, mask, out, ws,
+                                stream=None) -> None:
+    _check(lib().eagle_tree_verify_attention(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+                                             _ptr(mask), _ptr(out), _ptr(ws), _nbytes(ws),
+                                             _stream(stream)), "eagle_tree_verify_attention")
 
 
 def eagle_rerank_build_tree(dims, cfg, state, ws, tokens, parents, depth=None, positions=None,

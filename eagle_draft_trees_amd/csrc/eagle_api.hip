@@ -463,6 +463,28 @@ int eagle_draft_level_timed(const eagle_dims* dims, const eagle_weights* w,
                      (hipEvent_t)stop_event, stream);
 }
 
+int eagle_tree_verify_attention(const eagle_dims* dims, const eagle_tree_cfg* cfg, const float* q,
+                                const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+                                const uint8_t* mask, void* out, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
+    return r;
+  if (!q || !k_cache || !v_cache || !prefix_len || !mask || !out)
+    return fail(EAGLE_ERR_ARG, "q, k_cache, v_cache, prefix_len, mask or out is NULL");
+  RoundArgs a = make_args(*dims, *cfg, nullptr, nullptr, ws);
+  a.mode = MODE_VERIFY;
+  a.RS = cfg->m;
+  a.rows = cfg->batch * cfg->m;
+  a.q = (float*)q;
+  a.k_cache = (void*)k_cache;
+  a.v_cache = (void*)v_cache;
+  a.prefix_len = (int32_t*)prefix_len;
+  a.vmask = mask;
+  a.attn = out;
+  const AttnPlan pa = plan_attn(MODE_EXTEND, cfg->m, *dims, *cfg, cfg->batch);
+  return hip_ok(launch_attn(a, pa, (hipStream_t)stream), "tree verify attention");
+}
+
 int eagle_rerank_build_tree(const eagle_dims* dims, const eagle_tree_cfg* cfg,
                             const eagle_seq_state* state, void* ws, size_t ws_bytes, int32_t* tokens,
                             int32_t* parents, int32_t* depth, int32_t* positions, uint8_t* mask,

@@ -25,7 +25,7 @@ __host__ __device__ constexpr int gw_bu(int nw) { return nw == 2 ? 2 : 4; }
 constexpr int GW_FIN_THREADS = 1024;        // split-sum workgroup: one (column tile, m-tile, lane) per thread
 
 enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
-enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1 };
+enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1, MODE_VERIFY = 2 };  // verify: target-side tree attention
 enum ErrBits { ERR_TOKEN = 1, ERR_PREFIX = 2 };
 
 // ------------------------------------------------------------------ elements
@@ -255,6 +255,7 @@ struct RoundArgs {
   void* x0b;
   float* q;
   void* attn;
+  const uint8_t* vmask;  // tree verify: the [B][m][m] ancestor-or-self mask
   float* yf;
   void* yg;
   float *rstd, *ssq;

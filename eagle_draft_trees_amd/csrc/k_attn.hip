@@ -6,7 +6,12 @@
 // §12 item 5: the mask looks only at ancestors; [P4] "投机解码：从eagle1到dflash"
 // EAGLE-2 diagram: tree causal mask).  Extend: row i sees the prefix and
 // extend rows 0..i, which the QKV epilogue has already appended to the cache
-// ([P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里").
+// ([P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里").  Tree verify (the
+// target model's attention over the flattened tree, [P1] §6.2: one target
+// forward with tree attention scores every node; [P4] EAGLE-2 diagram, stage
+// two: a node sees only its ancestors and itself): the tree rows sit in the
+// cache right after the prefix, and query i sees every prefix row plus tree
+// row j iff mask[i][j] is set.
 //
 // One workgroup per (sequence, KV head, tile of 16 queries); the queries of a
 // tile are (row, head of the GQA group) pairs.  Its eight waves split the keys
@@ -106,6 +111,7 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   __shared__ __attribute__((aligned(16))) float sO[AT_W][AT_Q][OP];
   __shared__ int sLim[AT_Q];
   __shared__ int sAnc[AT_Q][EAGLE_MAX_DEPTH];
+  __shared__ uint8_t sMb[AT_Q][EAGLE_MAX_TREE];  // tree verify: the queries' mask rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -117,14 +123,14 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
   const int q0 = qt * AT_Q;
   const int P = clamp_prefix(a.prefix_len[b], a);
-  const bool level = a.mode == MODE_LEVEL;
+  const bool level = a.mode == MODE_LEVEL, verify = a.mode == MODE_VERIFY;
   const int HDq = a.H * HD;
 
   // ---- per-query visibility: prefix limit and (levels) ancestor slots
   if (tid < AT_Q) {
     const int gq = q0 + tid;
     const int row = min(gq, p.nq - 1) / p.g;
-    sLim[tid] = gq >= p.nq ? 0 : (level ? P : P + row + 1);
+    sLim[tid] = gq >= p.nq ? 0 : ((level || verify) ? P : P + row + 1);
     if (level) {  // the record's 16 ancestor slots in four 16-byte loads (all in flight together)
       const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + row];
       uint4 an[EAGLE_MAX_DEPTH / 4];
@@ -141,7 +147,8 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   // keys: Pv prefix rows (the widest limit in the tile), then ntree in-tree slots
   // (all wave-uniform; said so explicitly so that chunk indices and branches stay scalar)
   const int lastrow = (min(q0 + AT_Q, p.nq) - 1) / p.g;
-  const int Pv = __builtin_amdgcn_readfirstlane(level ? P : min(P + lastrow + 1, a.max_prefix));
+  const int Pv = __builtin_amdgcn_readfirstlane(
+      level ? P : verify ? min(P + a.m, a.max_prefix) : min(P + lastrow + 1, a.max_prefix));
   const int ntree = __builtin_amdgcn_readfirstlane(level ? a.depth * a.k : 0);
   const int cp = (Pv + AT_C - 1) / AT_C;
   const int nch = cp + (ntree + AT_C - 1) / AT_C;
@@ -233,6 +240,15 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
       }
     }
   }
+  // tree verify: the tile's mask rows, one byte per thread (padding queries
+  // see no tree row)
+  if (verify) {
+    for (int idx = tid; idx < AT_Q * a.m; idx += AT_W * WAVE) {
+      const int qq = idx / a.m, j = idx - qq * a.m, gq = q0 + qq;
+      const int row = min(gq, p.nq - 1) / p.g;
+      sMb[qq][j] = gq < p.nq ? a.vmask[((size_t)b * a.m + row) * a.m + j] : (uint8_t)0;
+    }
+  }
   __syncthreads();
 
   // running softmax state of query q (replicated over the lane groups) and
@@ -264,7 +280,12 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
       const int i = 4 * g + r;
       bool vis;
       if (c < cp) {
-        vis = c * AT_C + i < sLim[q];
+        const int key = c * AT_C + i;
+        vis = key < sLim[q];
+        if (verify) {  // a tree row: its entry in the query's mask row
+          const unsigned j = (unsigned)(key - P);
+          vis = vis || (j < (unsigned)a.m && sMb[q][j] != 0);
+        }
       } else {
         const int t = (c - cp) * AT_C + i;
         const int dep = min(t / a.k + 1, EAGLE_MAX_DEPTH), slot = t - (dep - 1) * a.k;

@@ -215,6 +215,30 @@ int eagle_draft_level_timed(const eagle_dims *dims, const eagle_weights *w,
                             int32_t level, int32_t flags, void *ws, size_t ws_bytes,
                             void *start_event, void *stop_event, void *stream);
 
+/* Target-side tree-verify attention ([P1] §6.2: the target scores every tree
+ * node in one forward with tree attention; [P4] EAGLE-2 diagram, stage two: the
+ * flattened tree is fed with the ancestor-only mask and per-node positions).
+ * The target's attention over the m flattened tree tokens of each sequence:
+ *   q        device fp32 [batch][m][n_heads][head_dim], post-RoPE at the node
+ *            positions (prefix_len-1+depth), row i = flat node i;
+ *   k_cache, v_cache  device dtype [batch][max_prefix][n_kv_heads][head_dim]:
+ *            rows 0..prefix_len-1 hold the prefix, rows prefix_len..prefix_len+m-1
+ *            the tree tokens' keys and values (flat order, post-RoPE);
+ *   prefix_len  device int32 [batch] (clamped to 1..max_prefix-m and flagged in
+ *            the workspace error word, as everywhere);
+ *   mask     device uint8 [batch][m][m], as eagle_rerank_build_tree writes it
+ *            (nonzero: the column node is an ancestor of the row node or itself);
+ *   out      device dtype [batch][m][n_heads*head_dim].
+ * Query (i, head h) attends, scaled by 1/sqrt(head_dim), to every prefix row and
+ * to tree row j iff mask[i][j] != 0, with KV head h*n_kv_heads/n_heads.  Uses
+ * the workspace of (dims, cfg) for split partials; depth and topk of cfg are
+ * validated but not used.  Errors: EAGLE_ERR_ARG for NULL pointers, the usual
+ * shape/workspace errors, EAGLE_ERR_HIP if the launch fails. */
+int eagle_tree_verify_attention(const eagle_dims *dims, const eagle_tree_cfg *cfg, const float *q,
+                                const void *k_cache, const void *v_cache, const int32_t *prefix_len,
+                                const uint8_t *mask, void *out, void *ws, size_t ws_bytes,
+                                void *stream);
+
 /* Rerank and build ([P1] §10.3 rerank; [P3] organize_draft_results and
  * build_tree_kernel_efficient; [P4] EAGLE-2 diagram).  Per sequence: the best
  * m-1 pool entries by (score desc, depth asc, pool index asc) plus the root;

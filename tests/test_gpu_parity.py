@@ -469,6 +469,56 @@ def test_repeat_runs_are_bit_identical(name):
         assert np.array_equal(a, b)
 
 
+def _random_tree_mask(rng, m):
+    """Ancestor-or-self mask of a random tree in flat order (parent before child)."""
+    parent = [-1] + [int(rng.integers(0, i)) for i in range(1, m)]
+    mask = np.zeros((m, m), dtype=np.uint8)
+    for i in range(m):
+        j = i
+        while j >= 0:
+            mask[i, j] = 1
+            j = parent[j]
+    return mask
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_bf16", "hd128_bf16", "wide_bf16", "7b", "70b"])
+def test_tree_verify_attention(name):
+    """Target-side tree-verify attention through the C ABI against the oracle:
+    seeded post-RoPE queries, the tree rows' K/V written right after each
+    prefix, ancestor masks of random trees; relative L2 per sequence."""
+    import torch
+    from eagle_draft_trees_amd import _lib as L
+    from eagle_draft_trees_amd.round import to_device
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[tree verify attention] {name}")
+    dt = cfg.dtype
+    rng = np.random.default_rng(1000 + cfg.uid)
+    B, m, H, Hkv, hd = cfg.B, cfg.m, cfg.H, cfg.Hkv, cfg.hd
+    q = rng.normal(size=(B, m, H, hd)).astype(np.float32)
+    kc = np.array(inp["k_cache"], copy=True)
+    vc = np.array(inp["v_cache"], copy=True)
+    P = np.asarray(inp["prefix_len"], np.int32)
+    for b in range(B):
+        kc[b, P[b]:P[b] + m] = store(rng.normal(size=(m, Hkv, hd)), dt)
+        vc[b, P[b]:P[b] + m] = store(rng.normal(size=(m, Hkv, hd)), dt)
+    mask = np.stack([_random_tree_mask(rng, m) for _ in range(B)])
+    out = torch.zeros(B, m, H * hd, dtype=torch.bfloat16 if dt == "bf16" else torch.float32,
+                      device="cuda")
+    L.eagle_tree_verify_attention(r.dims, r.tcfg, torch.from_numpy(q).cuda(), to_device(kc, dt, "cuda"),
+                                  to_device(vc, dt, "cuda"), to_device(P, dt, "cuda"),
+                                  torch.from_numpy(mask).cuda(), out, r.ws)
+    sync()
+    got = to_host(out)
+    worst = 0.0
+    for b in (seqs if seqs is not None else range(B)):
+        o = O.tree_verify_attention(q[b].astype(np.float64), O.widen(kc[b], dt), O.widen(vc[b], dt),
+                                    int(P[b]), mask[b])
+        e = rel_l2(got[b], o)
+        worst = max(worst, e)
+        assert e <= FEAT_TOL[dt], (b, e)
+    say(f"  tree verify attention {name}: worst rel L2 {worst:.2e} (tol {FEAT_TOL[dt]})")
+
+
 @pytest.mark.parametrize("name", ["ragged_bf16", "7b"])
 def test_graph_replay_matches_eager(name):
     """A round captured in a HIP graph and replayed several times, each replay

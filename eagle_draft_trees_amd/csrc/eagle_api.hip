@@ -97,7 +97,9 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   return p;
 }
 
-static inline bool use_skinny(int mode, int rows) { return mode == MODE_LEVEL && rows <= 16; }
+static inline bool use_skinny(int mode, int rows) {
+  return (mode == MODE_LEVEL || mode == MODE_EXTEND) && rows <= 16;
+}
 
 LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
   LmPlan p{};
@@ -143,7 +145,7 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   WsLayout L{};
   const size_t es = elem_size(d);
   const int B = c.batch, k = c.topk, D = c.depth, m = c.m;
-  const int rows_lv = B * k, rows_ex = B * m;
+  const int re = ext_rows(m, D), rows_lv = B * k, rows_ex = B * re;
   L.rows_max = std::max(std::max(rows_lv, rows_ex), B);
   L.pool_n = k + (D - 1) * k * k;
   const size_t R = L.rows_max, HD = (size_t)d.n_heads * d.head_dim;
@@ -161,7 +163,7 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   const size_t kvt = (size_t)B * D * k * d.n_kv_heads * d.head_dim * es;
   L.tk = take(kvt);
   L.tv = take(kvt);
-  L.ext_h = take((size_t)B * m * d.d * es);
+  L.ext_h = take((size_t)rows_ex * d.d * es);
   L.x0f = take(R * d.d * 4);
   L.x0b = take(R * d.d * es);
   L.q = take(R * HD * 4);
@@ -178,8 +180,10 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   const size_t lp = std::max(plan_lm(B, d, k).part_floats, plan_lm(rows_lv, d, k).part_floats);
   L.lmpart = take(lp * 4);
   L.lmres = take((size_t)std::max(B, rows_lv) * 2 * k * 4);
-  const size_t ap = std::max(plan_attn(MODE_LEVEL, k, d, c, B).part_floats,
-                             plan_attn(MODE_EXTEND, m, d, c, B).part_floats);
+  // (tree verify: m rows per sequence)
+  const size_t ap = std::max({plan_attn(MODE_LEVEL, k, d, c, B).part_floats,
+                              plan_attn(MODE_EXTEND, re, d, c, B).part_floats,
+                              plan_attn(MODE_EXTEND, m, d, c, B).part_floats});
   L.apart = take(ap * 4);
   L.total = off;
   return L;
@@ -217,13 +221,14 @@ static int check_cfg(const eagle_dims* d, const eagle_tree_cfg* c) {
     const AttnPlan pa = plan_attn(MODE_EXTEND, c->m, *d, *c, c->batch);
     const long wg = (long)c->batch * d->n_kv_heads * pa.nqt;
     if (wg > (1L << 30)) return fail(EAGLE_ERR_UNSUPPORTED, "attention grid %ld too large", wg);
+    const int rows_ex = c->batch * ext_rows(c->m, c->depth);
     for (int op = OP_FC; op <= OP_DOWN; ++op)
-      for (int M : {c->batch * c->topk, c->batch * c->m})
+      for (int M : {c->batch * c->topk, rows_ex})
         if (plan_gemm(op, M, *d).S > GEMM_MAXS)
           return fail(EAGLE_ERR_UNSUPPORTED, "K too long for %d split-K ways", GEMM_MAXS);
     long blocks = 0;
     for (int op = OP_FC; op <= OP_DOWN; ++op)
-      blocks = std::max(blocks, (long)plan_gemm(op, c->batch * c->m, *d).nblk * cdiv(c->batch * c->m, 64));
+      blocks = std::max(blocks, (long)plan_gemm(op, rows_ex, *d).nblk * cdiv(rows_ex, 64));
     if (blocks >= GRID_CNT || (long)c->batch * c->m > 4096)
       return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", c->batch * c->m);
   }
@@ -526,8 +531,8 @@ int eagle_draft_extend(const eagle_dims* dims, const eagle_weights* w, const eag
   RoundArgs a = make_args(*dims, *cfg, w, state, ws);
   a.mode = MODE_EXTEND;
   a.depth = 0;
-  a.rows = cfg->batch * cfg->m;
-  a.RS = cfg->m;
+  a.RS = ext_rows(cfg->m, cfg->depth);  // an accepted path's longest length
+  a.rows = cfg->batch * a.RS;
   a.true_feat = true_feat;
   a.tokens = tokens;
   a.accept_len = accept_len;
@@ -552,7 +557,7 @@ int eagle_ws_view(const eagle_dims* dims, const eagle_tree_cfg* cfg, const void*
     case EAGLE_WS_FEAT: off = L.feat; n = D * B * k * dims->d * es; break;
     case EAGLE_WS_TREE_K: off = L.tk; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
     case EAGLE_WS_TREE_V: off = L.tv; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
-    case EAGLE_WS_EXT_H: off = L.ext_h; n = B * m * dims->d * es; break;
+    case EAGLE_WS_EXT_H: off = L.ext_h; n = B * ext_rows((int)m, (int)D) * dims->d * es; break;
     default: return fail(EAGLE_ERR_ARG, "ws_view: region %d", what);
   }
   *ptr = (char*)ws + off;

@@ -331,6 +331,42 @@ __device__ __forceinline__ int clamp_prefix(int P, const RoundArgs& a) {
 
 __device__ __forceinline__ int clamp_slot(int s, int k) { return s < 0 ? 0 : (s >= k ? k - 1 : s); }
 
+// Rows per sequence of the extend: an accepted path holds the root and at
+// most one node per level, and no more nodes than the tree, so min(m, D+1)
+// rows cover every accepted length.
+__host__ __device__ inline int ext_rows(int m, int D) { return m < D + 1 ? m : D + 1; }
+
+// accept_len of sequence b, clamped to 1..(extend rows per sequence)
+__device__ __forceinline__ int ext_alen(const RoundArgs& a, int b) {
+  const int l = a.accept_len[b];
+  return l < 1 ? 1 : (l > a.RS ? a.RS : l);
+}
+
+// Sources of extend row `row` (sequence row / RS, row i within it): the
+// target's feature at path node min(i, alen-1) and the token of path node
+// i+1, or the bonus for row alen-1 (rows past it repeat that row's feature
+// and carry the next path entry's token or the bonus; they are computed and
+// ignored).  Flat tree indices are clamped into the tree.
+template <typename T>
+__device__ __forceinline__ void ext_row_src(const RoundArgs& a, int row, const T*& feat, int& tok) {
+  const int b = row / a.RS, i = row - b * a.RS;
+  const int last = ext_alen(a, b) - 1, ii = i < last ? i : last;
+  const int* path = a.accept_path + (size_t)b * (a.D + 1);
+  const int pi = clamp_slot(path[ii], a.m);
+  feat = (const T*)a.true_feat + ((size_t)b * a.m + pi) * a.d;
+  tok = i < last ? a.tokens[(size_t)b * a.m + clamp_slot(path[i + 1], a.m)] : a.bonus[b];
+}
+
+// Extend: the sequence state advances (the prefix grows by the accepted
+// length, the bonus becomes the next root token).  Called by one workgroup
+// of a launch that reads neither field.
+__device__ __forceinline__ void ext_advance_state(const RoundArgs& a, int tid, int nthreads) {
+  for (int b = tid; b < a.B; b += nthreads) {
+    a.prefix_len[b] = clamp_prefix(a.prefix_len[b], a) + ext_alen(a, b);
+    a.root_token[b] = clamp_tok(a.bonus[b], a.V, a.err);
+  }
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
 // 16-byte load from a pointer known to be global memory (for pointers that
 // were themselves read from LDS, whose address space the compiler cannot infer)

@@ -1,7 +1,7 @@
 // Skinny weight-streaming GEMMs of the draft layer on MFMA, with the layer's
 // elementwise work fused into the loaders and epilogues.
 //
-//   Y[M][N] = X[M][K] * W[N][K]^T,  M = frontier rows (B*k) or extend rows (B*m)
+//   Y[M][N] = X[M][K] * W[N][K]^T,  M = frontier rows (B*k) or extend rows (B*min(m, D+1))
 //
 // At drafting shapes M is 1..64 while W is megabytes, so every kernel here is
 // bound by streaming W from HBM once.  A workgroup holds CTW adjacent 16-column
@@ -24,13 +24,13 @@
 //           ([P1] §12 item 5: positions shared per level) and writes k, v
 //           straight into the in-tree slot (levels) or the prefix cache (extend)
 //   O       epilogue adds the residual x0, keeps y, emits y*gain for the MLP
-//           and per-block sums of squares; the grid's last block turns them
-//           into the RMSNorm 1/rms per row
+//           and per-block sums of squares (each gate/up workgroup sums them
+//           into the RMSNorm 1/rms of its rows)
 //   GATEUP  two weight streams per wave (gate and up rows of the same 16
 //           columns); epilogue silu(g/rms) * (u/rms)
 //   DOWN    epilogue adds the residual y -> predicted feature (no final norm);
-//           the extend also writes the next root feature and advances the
-//           sequence state in the grid's last block
+//           the extend also writes the next root feature, and its first
+//           workgroup advances the sequence state
 #include "eagle_internal.h"
 
 namespace eg {
@@ -108,8 +108,8 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
         slot = row % a.k;
         pos = clamp_prefix(a.prefix_len[b], a) - 1 + a.depth;
       } else {
-        b = row / a.m;
-        slot = row % a.m;
+        b = row / a.RS;
+        slot = row % a.RS;
         pos = clamp_prefix(a.prefix_len[b], a) + slot;
       }
       if (head < hq + hk) {  // q or k: rotate the (fi, fi+half) pair
@@ -173,10 +173,8 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
         El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + nn, h);
       } else {
         El<T>::st((T*)a.ext_h, (size_t)row * a.d + nn, h);
-        const int b = row / a.m, i = row % a.m;
-        int alen = a.accept_len[b];
-        alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-        if (i == alen - 1) El<T>::st((T*)a.root_feat, (size_t)b * a.d + nn, h);
+        const int b = row / a.RS, i = row % a.RS;
+        if (i == ext_alen(a, b) - 1) El<T>::st((T*)a.root_feat, (size_t)b * a.d + nn, h);
       }
     }
   }
@@ -232,14 +230,8 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
   // down, extend: the sequence state advances here (the prefix grows by the
   // accepted length, the bonus token becomes the next root).  Nothing in this
   // launch reads either field, so one workgroup does it without an election.
-  if (OP == OP_DOWN && a.mode == MODE_EXTEND && blk == 0 && split == 0 && zg == 0) {
-    for (int b = tid; b < a.B; b += THREADS) {
-      int alen = a.accept_len[b];
-      alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-      a.prefix_len[b] = clamp_prefix(a.prefix_len[b], a) + alen;
-      a.root_token[b] = clamp_tok(a.bonus[b], a.V, a.err);
-    }
-  }
+  if (OP == OP_DOWN && a.mode == MODE_EXTEND && blk == 0 && split == 0 && zg == 0)
+    ext_advance_state(a, tid, THREADS);
 
   // ---- FC rows: [parent feature || embed[token]] gathered on the fly; rows
   // past M take row 0's sources
@@ -256,21 +248,7 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
       if (a.depth == 1) s0 = (const T*)a.root_feat + (size_t)b * a.d;
       else s0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
     } else {
-      const int b = row / a.m, i = row % a.m;
-      int alen = a.accept_len[b];
-      alen = alen < 1 ? 1 : (alen > a.D + 1 ? a.D + 1 : alen);
-      const int last = alen - 1, ii = i < last ? i : last;
-      const int* path = a.accept_path + (size_t)b * (a.D + 1);
-      int pi = path[ii];
-      pi = pi < 0 ? 0 : (pi >= a.m ? a.m - 1 : pi);
-      s0 = (const T*)a.true_feat + ((size_t)b * a.m + pi) * a.d;
-      if (i < last) {
-        int pn = path[i + 1];
-        pn = pn < 0 ? 0 : (pn >= a.m ? a.m - 1 : pn);
-        tok = a.tokens[(size_t)b * a.m + pn];
-      } else {
-        tok = a.bonus[b];
-      }
+      ext_row_src<T>(a, row, s0, tok);
     }
     tok = clamp_tok(tok, a.V, a.err);
     rsrc[0][tid] = s0;

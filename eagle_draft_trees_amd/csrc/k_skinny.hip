@@ -1,5 +1,5 @@
-// Weight-streaming GEMMs of the draft layer for the drafting levels, where the
-// frontier has at most 16 rows:
+// Weight-streaming GEMMs of the draft layer where at most 16 rows are
+// forwarded (a drafting level's frontier, or the extend's accepted paths):
 //
 //   Y[M][N] = X[M][K] * W[N][K]^T,  M <= 16
 //
@@ -89,12 +89,17 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   const T* x1;
   int kswitch = K;
   if (OP == OP_FC) {
-    const int b = xr / a.k, j = xr - b * a.k;
-    const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
-    const int tok = clamp_tok(nd.token, a.V, a.err);
-    if (a.depth == 1) x0 = (const T*)a.root_feat + (size_t)b * a.d;
-    else x0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
-    x1 = (const T*)a.embed + (size_t)tok * a.d;
+    int tok;
+    if (a.mode == MODE_LEVEL) {
+      const int b = xr / a.k, j = xr - b * a.k;
+      const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
+      tok = nd.token;
+      if (a.depth == 1) x0 = (const T*)a.root_feat + (size_t)b * a.d;
+      else x0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
+    } else {  // extend: [true feature of the path node || embedding of the next token]
+      ext_row_src<T>(a, xr, x0, tok);
+    }
+    x1 = (const T*)a.embed + (size_t)clamp_tok(tok, a.V, a.err) * a.d;
     kswitch = a.d;
   } else if (OP == OP_DOWN) {  // packed activations: this lane's piece of k-step 0 (row c)
     x0 = (const T*)a.act + lane * El<T>::PER16;
@@ -174,9 +179,13 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
         const int row = 4 * g + r;
         if (!tv || row >= p.M) continue;
         float lo = low ? own : other, hi = low ? other : own;
-        const int bb = row / a.k, slot = row - bb * a.k;
+        // levels: a frontier slot at tree position P-1+depth; extend: row i of
+        // the sequence at position P+i, appended to the prefix cache
+        const bool lv = a.mode == MODE_LEVEL;
+        const int bb = row / a.RS, slot = row - bb * a.RS;
+        const int P = clamp_prefix(a.prefix_len[bb], a);
         if (rot) {
-          const int pos = clamp_prefix(a.prefix_len[bb], a) - 1 + a.depth;
+          const int pos = lv ? P - 1 + a.depth : P + slot;
           double sd, cd;
           sincos((double)pos * inv, &sd, &cd);
           const float cs = (float)cd, sn = (float)sd;
@@ -191,8 +200,10 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
         } else {
           const bool isk = head < a.H + a.Hkv;
           const int kvh = isk ? head - a.H : head - a.H - a.Hkv;
-          T* base = (T*)(isk ? a.tk : a.tv);
-          El<T>::st(base, ((((size_t)bb * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd + idx, val);
+          if (lv)
+            El<T>::st((T*)(isk ? a.tk : a.tv), ((((size_t)bb * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd + idx, val);
+          else
+            El<T>::st((T*)(isk ? a.k_cache : a.v_cache), (((size_t)bb * a.max_prefix + P + slot) * a.Hkv + kvh) * a.hd + idx, val);
         }
       }
     }
@@ -236,16 +247,24 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
         El<T>::st((T*)a.act, xpk_index<T>(row, n, (a.F + KS - 1) / KS), gg / (1.0f + expf(-gg)) * uu);
       }
     }
-  } else {  // OP_DOWN: predicted feature of the level (no final norm)
+  } else {  // OP_DOWN: predicted feature of the level or extend row (no final norm)
     if (fin && nv) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
         if (row >= p.M) continue;
         const float h = v[0][r] + a.yf[(size_t)row * a.d + n];
-        El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + n, h);
+        if (a.mode == MODE_LEVEL) {
+          El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + n, h);
+        } else {  // extend: row alen-1 of a sequence is its next root feature
+          El<T>::st((T*)a.ext_h, (size_t)row * a.d + n, h);
+          const int bb = row / a.RS, i = row - bb * a.RS;
+          if (i == ext_alen(a, bb) - 1) El<T>::st((T*)a.root_feat, (size_t)bb * a.d + n, h);
+        }
       }
     }
+    // nothing in this launch reads prefix_len or root_token
+    if (a.mode == MODE_EXTEND && blockIdx.x == 0) ext_advance_state(a, tid, (int)blockDim.x);
   }
 }
 

@@ -270,10 +270,12 @@ int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *t
  * the next start; [P2] Core Idea; [P1] §12 item 3).  Row i < accept_len
  * carries [true_feat[path_i] || embed[token of path_{i+1}, or the bonus for
  * the last row]] at position prefix_len+i and attends the prefix plus extend
- * rows 0..i.  Rows are padded to m per sequence (padding rows are computed
- * and ignored).  Updates the state: K/V rows prefix_len..prefix_len+m-1
- * written (the first accept_len are valid), prefix_len += accept_len,
- * root_feat = feature of row accept_len-1, root_token = bonus.
+ * rows 0..i.  An accepted path has at most min(m, depth+1) nodes, so each
+ * sequence forwards re = min(m, depth+1) rows (rows past accept_len are
+ * computed and ignored).  Updates the state: K/V rows
+ * prefix_len..prefix_len+re-1 written (the first accept_len are valid),
+ * prefix_len += accept_len, root_feat = feature of row accept_len-1,
+ * root_token = bonus.  accept_len is clamped to 1..re.
  * true_feat [batch][m][d] (dtype) are the target's features at each flat
  * tree node; tokens [batch][m], accept_len, accept_path, bonus as produced
  * by the calls above.  w: packed weights, as for eagle_draft_level. */
@@ -294,7 +296,7 @@ typedef enum {
     EAGLE_WS_FEAT = 3,      /* dtype [depth][batch][topk][d]: features of frontier nodes */
     EAGLE_WS_TREE_K = 4,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree keys (post-RoPE) */
     EAGLE_WS_TREE_V = 5,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree values    */
-    EAGLE_WS_EXT_H = 6      /* dtype [batch][m][d]: extend output features per row     */
+    EAGLE_WS_EXT_H = 6      /* dtype [batch][min(m, depth+1)][d]: extend output features */
 } eagle_ws_region;
 
 int eagle_ws_view(const eagle_dims *dims, const eagle_tree_cfg *cfg, const void *ws,

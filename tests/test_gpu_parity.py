@@ -315,7 +315,7 @@ def test_extend(name):
     tol = FEAT_TOL[cfg.dtype]
     tf = O.widen(inp["true_feat"], cfg.dtype)
     g_root = to_host(r.root_feat)
-    g_ext = to_host(r.ws_typed(6).view(cfg.B, cfg.m, cfg.d))
+    g_ext = to_host(r.ws_typed(6).view(cfg.B, min(cfg.m, cfg.D + 1), cfg.d))
     g_k, g_v = to_host(r.k_cache), to_host(r.v_cache)
     g_plen, g_rtok = r.prefix_len.cpu().numpy(), r.root_token.cpu().numpy()
     worst, lens = 0.0, []

@@ -66,6 +66,17 @@ Readings of what the pages leave open (each also listed in the design doc):
       [P4] EAGLE-2 diagram stage two): the tree tokens' keys and values sit in
       the target's cache right after the prefix, in flat order; query i sees
       every prefix row and tree row j iff mask[i, j] is set.
+  R15 relaxed acceptance (the SGLang variant in [P2]'s closing notes: target
+      probabilities and a probability threshold decide acceptance, and only
+      when every candidate of a level fails is one rejection-sampling draw
+      made there for the bonus): at node x, p = softmax(target logits / T);
+      x's children are tried in flat order and the walk descends to the first
+      child c with p(c) >= threshold.  When none passes (or x is a leaf) the
+      bonus is drawn from the residual: p with x's children removed and the
+      rest renormalised (rejection sampling with the rejected candidates as
+      point-mass proposals), by inverse CDF over token ids with one uniform
+      u in [0, 1) supplied per sequence.  If the children hold all of p's
+      mass the draw is from p itself.
 
 Parity pins: every function below is pinned by a CPU test (tests/
 test_oracle_*.py) against brute force, closed forms, special cases or the
@@ -87,6 +98,7 @@ __all__ = [
     "attend_row", "draft_rows", "finish_rows", "lm_logits", "lm_tail", "level_one",
     "level_step_forward", "level_step_tail", "rerank", "build_tree", "verify_greedy",
     "draft_extend", "run_round", "RoundResult", "NEAR_TIE", "tree_verify_attention",
+    "target_probs", "sample_residual", "verify_relaxed",
 ]
 
 NEAR_TIE = 1e-3  # a selection whose margin (log domain) is below this is "near-tie"
@@ -440,6 +452,60 @@ def verify_greedy(target_logits: np.ndarray, tokens: np.ndarray, parents: np.nda
         if not child:
             return path, len(path), best, margins
         node = child[0]
+        path.append(node)
+
+
+def target_probs(row: np.ndarray, temperature: float) -> np.ndarray:
+    """Target distribution at a tree node: softmax(logits / T) in fp64 (R15)."""
+    z = np.asarray(row, dtype=np.float64) / float(temperature)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def sample_residual(p: np.ndarray, removed: Sequence[int], u: float):
+    """One rejection-sampling draw at a node whose candidates `removed` were all
+    rejected ([P1] §6.2: resample from the normalised positive part of the
+    target minus the proposal; with point-mass proposals on the candidates that
+    is p with those tokens taken out, renormalised; R15).  Inverse CDF over
+    token ids: the smallest id x whose cumulative residual probability exceeds
+    u.  Returns (token, margin): the distance of u from the nearer end of the
+    drawn token's CDF interval (normalised units)."""
+    r = np.array(p, dtype=np.float64)
+    r[list(removed)] = 0.0
+    if not r.sum() > 0.0:  # the candidates held all the mass: draw from p
+        r = np.array(p, dtype=np.float64)
+    c = np.cumsum(r) / r.sum()
+    x = int(np.searchsorted(c, u, side="right"))
+    x = min(x, int(np.nonzero(r)[0][-1]))  # u at the very top: the last token with mass
+    lo = c[x - 1] if x > 0 else 0.0
+    return x, float(min(u - lo, c[x] - u))
+
+
+def verify_relaxed(target_logits: np.ndarray, tokens: np.ndarray, parents: np.ndarray,
+                   temperature: float, threshold: float, u: float):
+    """Relaxed acceptance walk (R15; [P2] closing notes on SGLang).  From the
+    root, descend to the first child in flat order whose target probability is
+    at least `threshold`; at the stop, draw the bonus from the residual with
+    the uniform u.  target_logits [m, V].  Returns (path of flat indices from
+    the root, accept_len = len(path), bonus, margins): |p(c) - threshold| for
+    every child tried, then the draw's margin."""
+    m = len(tokens)
+    node, path, margins = 0, [0], []
+    while True:
+        p = target_probs(target_logits[node], temperature)
+        kids = [c for c in range(m) if parents[c] == node and c != node]
+        nxt = None
+        for c in kids:
+            pc = float(p[int(tokens[c])])
+            margins.append(abs(pc - threshold))
+            if pc >= threshold:
+                nxt = c
+                break
+        if nxt is None:
+            bonus, mg = sample_residual(p, [int(tokens[c]) for c in kids], u)
+            margins.append(mg)
+            return path, len(path), bonus, margins
+        node = nxt
         path.append(node)
 
 

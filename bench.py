@@ -212,6 +212,47 @@ def tree_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
             "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}
 
 
+def relaxed_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
+    """Relaxed acceptance walk at the round's shape (temperature 1, threshold
+    0.1) on the tree the round just built and the round's target logits.
+    Timed like the tree-verify attention; bytes = every tree row's target
+    logits (the softmax statistics of all m rows are taken in parallel before
+    the walk) plus one sixteenth of the stop row, scanned again for the
+    residual draw."""
+    gen = torch.Generator(device=r.device)
+    gen.manual_seed(2)
+    uni = torch.rand(cfg.B, generator=gen, device=r.device, dtype=torch.float32)
+    call = lambda: r.verify_relaxed(1.0, 0.1, uni, stream=stream)
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            call()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * replays)
+    alen = r.accept_len.cpu().numpy()
+    nbytes = cfg.B * cfg.m * cfg.V * 4 + cfg.B * (-(-cfg.V // 16)) * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "k_relaxed_stats + k_verify_relaxed", "bound": "hbm", "us_per_call": round(us, 2),
+            "accept_len": [int(a) for a in alen], "bytes_per_call": nbytes,
+            "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "temperature": 1.0, "threshold": 0.1,
+            "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +408,7 @@ def main() -> int:
                      "traffic": traffic},
     }
     out["tree_verify_attention"] = tree_verify(torch, L, r, cfg, stream)
+    out["relaxed_verify"] = relaxed_verify(torch, L, r, cfg, stream)
     if not args.no_batched:
         out["mfma_batched_lmhead"] = batched_lmhead(torch, L, dev, stream)
     if not args.no_cpu_baseline:

@@ -99,6 +99,11 @@ def lib() -> ctypes.CDLL:
                                                   c_void_p, c_void_p, c_void_p, c_void_p]),
             "eagle_verify_greedy": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+            "eagle_verify_relaxed_scratch_bytes": (c_size_t, [P(EagleTreeCfg)]),
+            "eagle_verify_relaxed": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
+                                               c_void_p, c_float, c_float, c_void_p,
+                                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                               c_void_p]),
             "eagle_draft_extend": (c_int32, [P(EagleDims), P(EagleWeights), P(EagleTreeCfg),
                                              P(EagleSeqState), c_void_p, c_void_p, c_void_p,
                                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -222,6 +227,19 @@ def eagle_verify_greedy(cfg, vocab, target_logits, tokens, parents, accept_len, 
     _check(lib().eagle_verify_greedy(ctypes.byref(cfg), vocab, _ptr(target_logits), _ptr(tokens),
                                      _ptr(parents), _ptr(accept_len), _ptr(accept_path),
                                      _ptr(bonus), _stream(stream)), "eagle_verify_greedy")
+
+
+def eagle_verify_relaxed_scratch_bytes(cfg) -> int:
+    return int(lib().eagle_verify_relaxed_scratch_bytes(ctypes.byref(cfg)))
+
+
+def eagle_verify_relaxed(cfg, vocab, target_logits, tokens, parents, temperature, threshold,
+                         uniforms, accept_len, accept_path, bonus, scratch, stream=None) -> None:
+    _check(lib().eagle_verify_relaxed(ctypes.byref(cfg), vocab, _ptr(target_logits), _ptr(tokens),
+                                      _ptr(parents), float(temperature), float(threshold),
+                                      _ptr(uniforms), _ptr(accept_len), _ptr(accept_path),
+                                      _ptr(bonus), _ptr(scratch), _nbytes(scratch),
+                                      _stream(stream)), "eagle_verify_relaxed")
 
 
 def eagle_draft_extend(dims, weights, cfg, state, true_feat, tokens, accept_len, accept_path, bonus,

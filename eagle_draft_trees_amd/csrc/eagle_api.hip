@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "skinny_core.h"
 
@@ -516,6 +517,35 @@ int eagle_verify_greedy(const eagle_tree_cfg* cfg, int32_t vocab, const float* t
   return hip_ok(launch_verify(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, tokens, parents,
                               accept_len, accept_path, bonus, (hipStream_t)stream),
                 "verify");
+}
+
+size_t eagle_verify_relaxed_scratch_bytes(const eagle_tree_cfg* cfg) {
+  if (check_cfg(nullptr, cfg)) return 0;
+  return verify_relaxed_scratch_bytes(cfg->batch, cfg->m);
+}
+
+int eagle_verify_relaxed(const eagle_tree_cfg* cfg, int32_t vocab, const float* target_logits,
+                         const int32_t* tokens, const int32_t* parents, float temperature,
+                         float threshold, const float* uniforms, int32_t* accept_len,
+                         int32_t* accept_path, int32_t* bonus, void* scratch, size_t scratch_bytes,
+                         void* stream) {
+  int r;
+  if ((r = check_cfg(nullptr, cfg))) return r;
+  if (vocab < 1) return fail(EAGLE_ERR_SHAPE, "vocab %d", vocab);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(EAGLE_ERR_ARG, "temperature %g (positive, finite)", (double)temperature);
+  if (!std::isfinite(threshold)) return fail(EAGLE_ERR_ARG, "threshold is not finite");
+  if (!target_logits || !tokens || !parents || !uniforms || !accept_len || !accept_path || !bonus ||
+      !scratch)
+    return fail(EAGLE_ERR_ARG, "verify_relaxed: NULL pointer");
+  if ((uintptr_t)scratch % 8) return fail(EAGLE_ERR_ARG, "scratch not 8-byte aligned");
+  const size_t need = verify_relaxed_scratch_bytes(cfg->batch, cfg->m);
+  if (scratch_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "scratch %zu < %zu bytes", scratch_bytes, need);
+  if ((long)cfg->batch * cfg->m > 65535) return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", cfg->batch * cfg->m);
+  return hip_ok(launch_verify_relaxed(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, tokens, parents,
+                                      temperature, threshold, uniforms, scratch, accept_len, accept_path,
+                                      bonus, (hipStream_t)stream),
+                "verify_relaxed");
 }
 
 int eagle_draft_extend(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,

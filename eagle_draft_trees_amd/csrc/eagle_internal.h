@@ -443,6 +443,11 @@ hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, 
 hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
                          const int32_t* parents, int32_t* alen, int32_t* apath, int32_t* bonus,
                          hipStream_t s);
+hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
+                                 const int32_t* parents, float temperature, float threshold,
+                                 const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
+                                 int32_t* bonus, hipStream_t s);
+size_t verify_relaxed_scratch_bytes(int B, int m);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // one matrix W [N][K] (row-major) into the packed tile layout; pair_hd > 0:
 // q/k/v row grouping of rotation pairs for head_dim pair_hd

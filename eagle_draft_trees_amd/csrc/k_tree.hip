@@ -373,6 +373,287 @@ __global__ void __launch_bounds__(1024) k_verify(int m, int D, int V, const floa
   if (tid <= D) apath[(size_t)b * (D + 1) + tid] = tid < len ? path[tid] : -1;
 }
 
+// Relaxed acceptance walk ([P2] closing notes on SGLang's verification: the
+// target's probabilities and a probability threshold decide acceptance, and
+// one rejection-sampling draw at the level where every candidate fails gives
+// the bonus).  At node x, p = softmax(logits[x] / T); x's children are tried
+// in flat order and the walk descends to the first with p(c) >= threshold.
+// At the stop, the bonus is drawn by inverse CDF (smallest id whose
+// cumulative residual mass exceeds u * total) from p with x's children
+// removed; from p itself if they held all of its mass.
+//
+// Two launches.  k_relaxed_stats spreads the softmax statistics of every
+// tree row over the chip: workgroup (segment s, row) reduces ids
+// [s*SEGV, (s+1)*SEGV) of the row to (max, sum of exp(z - max)), z = l / T,
+// reading 256 consecutive ids per wave instruction pair.  k_verify_relaxed
+// (one workgroup per sequence) then walks: a visited node's statistics are
+// its 16 segment pairs combined in segment order, and the children (flat
+// slots 0..m-1, i.e. wave 0) are tested with one ballot.  At the stop, each
+// segment's residual mass is its mass minus the removed children that fall
+// in it; the segment holding u * total is found in segment order and only
+// that segment (about V/16 ids) is scanned in id order: contiguous chunks
+// per thread, a wave-wide scan, the waves chained in order, every bound the
+// same sum wherever it is formed.
+constexpr int RS_SEG = 16;     // segments per row
+constexpr int RS_T = 256;      // threads of a statistics workgroup
+constexpr int RS_U = 8;        // loads in flight per thread
+constexpr int RV_T = 1024;
+constexpr int RV_W = RV_T / WAVE;
+
+__global__ void __launch_bounds__(RS_T) k_relaxed_stats(int V, const float* tl, float temperature,
+                                                        float2* stats) {
+#pragma clang fp contract(off)
+  __shared__ float s_m[RS_T / WAVE], s_s[RS_T / WAVE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sg = blockIdx.x, row = blockIdx.y;
+  const int SEGV = (V + RS_SEG - 1) / RS_SEG;
+  const int a0 = min(V, sg * SEGV), a1 = min(V, a0 + SEGV);
+  const float* r = tl + (size_t)row * V;
+  const float invT = 1.0f / temperature;
+  float mx = -INFINITY, sm = 0.f;
+  for (int x0 = a0 + tid; x0 < a1; x0 += RS_T * RS_U) {
+    float z[RS_U];
+#pragma unroll
+    for (int q = 0; q < RS_U; ++q) {  // unconditional loads from clamped ids: all in flight at once
+      const int x = x0 + q * RS_T;
+      const float l = r[min(x, a1 - 1)];
+      z[q] = x < a1 ? l * invT : -INFINITY;
+    }
+    float bm = mx;
+#pragma unroll
+    for (int q = 0; q < RS_U; ++q) bm = z[q] > bm ? z[q] : bm;  // -inf and NaN never win
+    if (bm > mx) {
+      sm = mx == -INFINITY ? 0.f : sm * expf(mx - bm);
+      mx = bm;
+    }
+#pragma unroll
+    for (int q = 0; q < RS_U; ++q)
+      if (z[q] > -INFINITY) sm += expf(z[q] - mx);
+  }
+  const float wm = wave_max_dpp(mx);
+  const float ws = wave_sum_dpp(mx == -INFINITY ? 0.f : sm * expf(mx - wm));
+  if (lane == 0) {
+    s_m[wave] = wm;
+    s_s[wave] = ws;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float M = s_m[0];
+    for (int w = 1; w < RS_T / WAVE; ++w) M = fmaxf(M, s_m[w]);
+    float S = 0.f;
+    for (int w = 0; w < RS_T / WAVE; ++w) S += s_m[w] == -INFINITY ? 0.f : s_s[w] * expf(s_m[w] - M);
+    stats[(size_t)row * RS_SEG + sg] = make_float2(M, S);
+  }
+}
+
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const float t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, const float* tl,
+                                                         const int32_t* tokens, const int32_t* parents,
+                                                         float temperature, float thr, const float* uniforms,
+                                                         const float2* stats, int32_t* alen, int32_t* apath,
+                                                         int32_t* bonus) {
+  // no fused multiply-adds: z = l / T and each exp(z - M) are formed the same
+  // way here as in the statistics kernel
+#pragma clang fp contract(off)
+  __shared__ float s_seg[RS_SEG], s_res[RS_SEG];
+  __shared__ float s_ws[RV_W];
+  __shared__ float s_M, s_local;
+  __shared__ int s_kid[EAGLE_MAX_TREE], s_kseg[EAGLE_MAX_TREE];
+  __shared__ float s_ke[EAGLE_MAX_TREE];
+  __shared__ int s_nk, s_len, s_node, s_pick, s_seg_pick, s_excl, s_last;
+  __shared__ int path[EAGLE_MAX_DEPTH + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+  const int SEGV = (V + RS_SEG - 1) / RS_SEG;
+  const float invT = 1.0f / temperature;
+  float u = uniforms[b];
+  u = u >= 0.f ? (u < 1.f ? u : 0.99999994f) : 0.f;  // into [0, 1); NaN -> 0
+
+  // ---- the walk, in wave 0 alone: lane j holds flat slot j (m <= 64).  Per
+  // visited node one round trip: lanes 0..15 load its segment statistics and
+  // every child lane loads its token's logit, together; M and S are wave
+  // reductions in a fixed order; one ballot gives the first passing child.
+  if (wave == 0) {
+    const bool inm = lane < m;
+    const int par = inm ? parents[(size_t)b * m + lane] : -2;
+    const int tok = inm ? tokens[(size_t)b * m + lane] : -1;
+    const bool inr = tok >= 0 && tok < V;
+    int node = 0, len = 1;
+    if (lane == 0) path[0] = 0;
+    for (;;) {
+      const float* row = tl + ((size_t)b * m + node) * V;
+      const bool kid = inm && lane != node && par == node;
+      const float2 sp = stats[((size_t)b * m + node) * RS_SEG + (lane & (RS_SEG - 1))];
+      const float l = row[(kid && inr) ? tok : 0];
+      const float sm_ = lane < RS_SEG ? sp.x : -INFINITY;
+      const float M = wave_max_dpp(sm_);
+      const float seg = (lane < RS_SEG && sp.x > -INFINITY) ? sp.y * expf(sp.x - M) : 0.f;
+      const float S = wave_sum_dpp(seg);
+      const float z = (kid && inr) ? l * invT : -INFINITY;
+      const float e = z > -INFINITY ? expf(z - M) : 0.f;
+      const float pc = e / S;
+      const unsigned long long kb = __ballot(kid);
+      const unsigned long long pb = __ballot(kid && inr && pc >= thr && len <= D);
+      if (!pb) {  // the stop: what the residual draw needs
+        if (lane < RS_SEG) s_seg[lane] = seg;
+        if (kid) {
+          const int slot = __popcll(kb & ((1ull << lane) - 1ull));
+          s_kid[slot] = inr ? tok : -1;
+          s_kseg[slot] = inr ? tok / SEGV : -1;
+          s_ke[slot] = e;
+        }
+        if (lane == 0) {
+          s_M = M;
+          s_nk = __popcll(kb);
+          s_len = len;
+          s_node = node;
+        }
+        break;
+      }
+      const int c = __ffsll((long long)pb) - 1;
+      if (lane == 0) path[len] = c;
+      node = c;
+      ++len;
+    }
+  }
+  __syncthreads();
+
+  // ---- the bonus: residual draw at the stop node.  Segment masses less the
+  // removed children (flat order), the segment holding u * total, then an
+  // id-order scan of that segment alone.
+  const int node = s_node, len = s_len;
+  const float* row = tl + ((size_t)b * m + node) * V;
+  const float M = s_M;
+  const int nk = s_nk;
+  if (tid < RS_SEG) {  // segment tid's mass less its removed children, in flat order
+    float r = s_seg[tid];
+    for (int k = 0; k < nk; ++k)
+      if (s_kseg[k] == tid) r -= s_ke[k];
+    s_res[tid] = r > 0.f ? r : 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float res[RS_SEG];
+    float tot = 0.f;
+    for (int sg = 0; sg < RS_SEG; ++sg) {
+      res[sg] = s_res[sg];
+      tot += res[sg];
+    }
+    int excl = 1;
+    if (!(tot > 0.f)) {  // the children held all the mass: draw from p
+      excl = 0;
+      tot = 0.f;
+      for (int sg = 0; sg < RS_SEG; ++sg) {
+        res[sg] = s_seg[sg];
+        tot += res[sg];
+      }
+    }
+    float target = u * tot;
+    if (!(target < tot)) target = nextafterf(tot, 0.f);
+    int pick = -1, last = -1;
+    float cum = 0.f;
+    for (int sg = 0; sg < RS_SEG; ++sg) {
+      if (res[sg] > 0.f) {
+        if (pick < 0 && target < cum + res[sg]) {
+          pick = sg;
+          s_local = target - cum;
+        }
+        last = sg;
+      }
+      cum += res[sg];
+    }
+    if (pick < 0) {  // rounding at the very top: the last segment with mass, at its end
+      pick = last;
+      s_local = last >= 0 ? nextafterf(res[last], 0.f) : 0.f;
+    }
+    s_seg_pick = pick;
+    s_excl = excl;
+    s_pick = -1;
+    s_last = -1;
+  }
+  __syncthreads();
+  const int sg = s_seg_pick;
+  if (sg >= 0) {
+    const bool excl = s_excl != 0;
+    const float local = s_local;
+    const int a0 = min(V, sg * SEGV), a1 = min(V, a0 + SEGV);
+    const int CH = (a1 - a0 + RV_T - 1) / RV_T;  // ids per thread, contiguous
+    const int x0 = min(a1, a0 + tid * CH), x1 = min(a1, x0 + CH);
+    auto mass = [&](int x, float l) {
+      const float z = l * invT;
+      bool out = !(z > -INFINITY);
+      if (excl)
+        for (int k = 0; k < nk; ++k) out = out || s_kid[k] == x;
+      return out ? 0.f : expf(z - M);
+    };
+    // the chunk's logits, four unconditional loads from clamped ids at a time
+    constexpr int CB = 4;
+    float w = 0.f;
+    for (int xb = x0; xb < x1; xb += CB) {
+      float lv[CB];
+#pragma unroll
+      for (int q = 0; q < CB; ++q) lv[q] = row[min(xb + q, x1 - 1)];
+#pragma unroll
+      for (int q = 0; q < CB; ++q)
+        if (xb + q < x1) w += mass(xb + q, lv[q]);
+    }
+    // chunk bounds: lo = (earlier waves) + (earlier lanes), hi = lo + own,
+    // each formed as the same sum as the neighbouring chunk's bound
+    const float wi = wave_incl_scan(w, lane);
+    const float wprev = __shfl_up(wi, 1);
+    if (lane == WAVE - 1) s_ws[wave] = wi;
+    __syncthreads();
+    float base = 0.f, tot = 0.f;
+    for (int v = 0; v < RV_W; ++v) {
+      if (v == wave) base = tot;
+      tot = tot + s_ws[v];
+    }
+    const float lo = base + (lane > 0 ? wprev : 0.f), hi = base + wi;
+    if (w > 0.f) {
+      atomicMax(&s_last, tid);
+      if (lo <= local && local < hi) {
+        const float rem = local - lo;
+        float acc = 0.f;
+        int pick = -1, lastx = -1;
+        for (int xb = x0; xb < x1 && pick < 0; xb += CB) {
+          float lv[CB];
+#pragma unroll
+          for (int q = 0; q < CB; ++q) lv[q] = row[min(xb + q, x1 - 1)];
+#pragma unroll
+          for (int q = 0; q < CB; ++q) {
+            if (xb + q >= x1 || pick >= 0) continue;
+            const float e = mass(xb + q, lv[q]);
+            if (e > 0.f) lastx = xb + q;
+            if (e > 0.f && rem < acc + e) pick = xb + q;
+            else acc += e;
+          }
+        }
+        s_pick = pick >= 0 ? pick : lastx;
+      }
+    }
+    __syncthreads();
+    if (s_pick < 0 && tid == s_last) {  // the segment's scan came out below the target: its last id with mass
+      int lastx = -1;
+      for (int x = x0; x < x1; ++x)
+        if (mass(x, row[x]) > 0.f) lastx = x;
+      s_pick = lastx;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    alen[b] = len;
+    bonus[b] = s_pick >= 0 ? s_pick : 0;
+  }
+  if (tid <= D) apath[(size_t)b * (D + 1) + tid] = tid < len ? path[tid] : -1;
+}
+
 __global__ void k_zero(uint4* p, size_t n16) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
     p[i] = make_uint4(0, 0, 0, 0);
@@ -401,6 +682,19 @@ hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int3
                      bonus);
   return hipGetLastError();
 }
+
+hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
+                                 const int32_t* parents, float temperature, float threshold,
+                                 const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
+                                 int32_t* bonus, hipStream_t s) {
+  float2* st = (float2*)scratch;
+  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m), dim3(RS_T), 0, s, V, tl, temperature, st);
+  hipLaunchKernelGGL(k_verify_relaxed, dim3(B), dim3(RV_T), 0, s, m, D, V, tl, tokens, parents, temperature,
+                     threshold, uniforms, (const float2*)st, alen, apath, bonus);
+  return hipGetLastError();
+}
+
+size_t verify_relaxed_scratch_bytes(int B, int m) { return (size_t)B * m * RS_SEG * sizeof(float2); }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   const size_t n16 = bytes / 16;

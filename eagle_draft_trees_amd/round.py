@@ -106,6 +106,16 @@ class DraftRound:
         L.eagle_verify_greedy(self.tcfg, self.cfg.V, tl, self.tokens, self.parents,
                               self.accept_len, self.accept_path, self.bonus, stream)
 
+    def verify_relaxed(self, temperature: float, threshold: float, uniforms: torch.Tensor,
+                       target_logits: Optional[torch.Tensor] = None, stream=None) -> None:
+        tl = self.target_logits if target_logits is None else target_logits
+        if getattr(self, "_rv_scratch", None) is None:
+            self._rv_scratch = torch.empty(L.eagle_verify_relaxed_scratch_bytes(self.tcfg),
+                                           dtype=torch.uint8, device=self.device)
+        L.eagle_verify_relaxed(self.tcfg, self.cfg.V, tl, self.tokens, self.parents, temperature,
+                               threshold, uniforms, self.accept_len, self.accept_path, self.bonus,
+                               self._rv_scratch, stream)
+
     def extend(self, true_feat: Optional[torch.Tensor] = None, stream=None) -> None:
         tf = self.true_feat if true_feat is None else true_feat
         L.eagle_draft_extend(self.dims, self.wts, self.tcfg, self.state, tf, self.tokens,

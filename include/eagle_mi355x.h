@@ -8,6 +8,8 @@
  *   eagle_rerank_build_tree               top m-1 of every candidate + the root,
  *                                         flattened, ancestor-only mask, positions
  *   eagle_verify_greedy                   greedy longest-accepted-path walk
+ *   eagle_verify_relaxed                  threshold acceptance on the target's
+ *                                         probabilities, residual draw for the bonus
  *   eagle_draft_extend                    draft forward over the accepted path with
  *                                         the target's true features, KV append
  *
@@ -264,6 +266,32 @@ int eagle_rerank_build_tree(const eagle_dims *dims, const eagle_tree_cfg *cfg,
 int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
                         const int32_t *tokens, const int32_t *parents, int32_t *accept_len,
                         int32_t *accept_path, int32_t *bonus, void *stream);
+
+/* Relaxed acceptance ([P2] closing notes on SGLang's verification: the
+ * target's probabilities and a probability threshold decide whether a token
+ * is accepted; only when every candidate of a level fails is one
+ * rejection-sampling draw made there, for the bonus token).  From the root:
+ * p = softmax(target_logits[node] / temperature) in fp32; the node's children
+ * are tried in flat order and the walk descends to the first child c with
+ * p(c) >= threshold.  When none passes (or the node has no children, or the
+ * path already holds depth+1 nodes) the bonus is drawn from p with the
+ * node's children removed and the rest renormalised: the smallest token id
+ * whose cumulative residual mass exceeds u * (residual total), u =
+ * uniforms[b] clamped into [0, 1); if the children held all of p's mass the
+ * draw is from p itself.  Inputs as for eagle_verify_greedy, plus
+ * temperature (> 0, finite), threshold (finite; <= 0 accepts every first
+ * child, > 1 none) and uniforms [batch] fp32 (device; the caller's random
+ * numbers, one per sequence).  scratch: device buffer of at least
+ * eagle_verify_relaxed_scratch_bytes(cfg) bytes, 8-byte aligned, owned by the
+ * caller and overwritten (the per-segment softmax statistics of every tree
+ * row).  Outputs as for eagle_verify_greedy.  Logits of -inf carry no
+ * probability.  batch*m at most 65535. */
+size_t eagle_verify_relaxed_scratch_bytes(const eagle_tree_cfg *cfg);   /* 0 if cfg is invalid */
+int eagle_verify_relaxed(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
+                         const int32_t *tokens, const int32_t *parents, float temperature,
+                         float threshold, const float *uniforms, int32_t *accept_len,
+                         int32_t *accept_path, int32_t *bonus, void *scratch, size_t scratch_bytes,
+                         void *stream);
 
 /* Draft extend ([P3] "在 SGLang 里": rerun the draft over the accepted
  * positions with the target's true hidden states, take row accept_len-1 as

@@ -469,7 +469,9 @@ def sample_residual(p: np.ndarray, removed: Sequence[int], u: float):
     is p with those tokens taken out, renormalised; R15).  Inverse CDF over
     token ids: the smallest id x whose cumulative residual probability exceeds
     u.  Returns (token, margin): the distance of u from the nearer end of the
-    drawn token's CDF interval (normalised units)."""
+    drawn token's CDF interval (normalised units) that another token lies
+    beyond; the ends of [0, 1) have none, so the first and last tokens with
+    mass get an infinite margin on that side."""
     r = np.array(p, dtype=np.float64)
     r[list(removed)] = 0.0
     if not r.sum() > 0.0:  # the candidates held all the mass: draw from p
@@ -477,8 +479,10 @@ def sample_residual(p: np.ndarray, removed: Sequence[int], u: float):
     c = np.cumsum(r) / r.sum()
     x = int(np.searchsorted(c, u, side="right"))
     x = min(x, int(np.nonzero(r)[0][-1]))  # u at the very top: the last token with mass
-    lo = c[x - 1] if x > 0 else 0.0
-    return x, float(min(u - lo, c[x] - u))
+    nz = np.nonzero(r)[0]
+    lo_m = u - c[x - 1] if x > int(nz[0]) else math.inf
+    hi_m = c[x] - u if x < int(nz[-1]) else math.inf
+    return x, float(min(lo_m, hi_m))
 
 
 def verify_relaxed(target_logits: np.ndarray, tokens: np.ndarray, parents: np.ndarray,

@@ -90,6 +90,24 @@ def test_entry_points_reject_bad_arguments_before_launch():
     _expect(L.EAGLE_ERR_SHAPE, lambda: L._check(
         lib.eagle_verify_greedy(ctypes.byref(tc), 0, fake, fake, fake, fake, fake, fake, None),
         "verify"))
+    need = lib.eagle_verify_relaxed_scratch_bytes(ctypes.byref(tc))
+    assert need == tc.batch * tc.m * 16 * 8
+
+    def relaxed(vocab=4096, T=1.0, thr=0.1, uni=fake, scr=fake, scr_bytes=need):
+        return L._check(lib.eagle_verify_relaxed(ctypes.byref(tc), vocab, fake, fake, fake, T, thr,
+                                                 uni, fake, fake, fake, scr, scr_bytes, None),
+                        "relaxed")
+
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(T=0.0))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(T=-1.0))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(T=float("inf")))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(T=float("nan")))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(thr=float("nan")))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(uni=None))
+    _expect(L.EAGLE_ERR_SHAPE, lambda: relaxed(vocab=0))
+    _expect(L.EAGLE_ERR_WORKSPACE, lambda: relaxed(scr_bytes=need - 8))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(scr=None))
+    _expect(L.EAGLE_ERR_ARG, lambda: relaxed(scr=fake + 4))  # misaligned
     _expect(L.EAGLE_ERR_ARG, lambda: L._check(
         lib.eagle_draft_extend(ctypes.byref(dims), ctypes.byref(w), ctypes.byref(tc),
                                ctypes.byref(st), None, fake, fake, fake, fake, fake, n, None),

@@ -132,13 +132,19 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
   v = max(v, dpp_bcast31(v, 0u));
   return (unsigned)__builtin_amdgcn_readlane(v, 63);
 }
-// maximum 64-bit key over the wave (every lane gets it), from two 32-bit
-// reductions: the high words, then the low words of the lanes that hold the
-// highest high word
+// maximum 64-bit key over the wave (every lane gets it): the highest high
+// word by a 32-bit reduction; when one lane holds it (the usual case for
+// keys led by a float value) its low word is read from that lane, otherwise
+// a second reduction takes the highest low word among the lanes that tie
 __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
   const unsigned hi = (unsigned)(k >> 32);
   const unsigned mh = wave_max_u32(hi);
-  const unsigned ml = wave_max_u32(hi == mh ? (unsigned)k : 0u);
+  const unsigned long long tie = __ballot(hi == mh);
+  unsigned ml;
+  if (__popcll(tie) == 1)
+    ml = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)k, __ffsll((long long)tie) - 1);
+  else
+    ml = wave_max_u32(hi == mh ? (unsigned)k : 0u);
   return ((unsigned long long)mh << 32) | ml;
 }
 

@@ -102,6 +102,10 @@ _add(TreeConfig("deep_bf16", 16, "bf16", 2, 256, 4, 2, 64, 512, 2048, 20, 90, 5,
 # more than 64 LM-head rows (80 at level 1, 160 after): the tiled batched
 # LM-head GEMM; a vocabulary that ends inside a 128-column block
 _add(TreeConfig("batch_bf16", 17, "bf16", 80, 256, 4, 2, 64, 512, 3000, 8, 40, 3, 2, 6))
+# a chain shorter than depth+1 (topk 1, m = 3 < D + 1 = 5): the extend's rows
+# per sequence are limited by m, and a whole-tree path reaches that limit, on
+# the weight-streaming kernels (3 sequences x 3 rows)
+_add(TreeConfig("short_f32", 18, "f32", 3, 256, 4, 4, 64, 688, 4096, 64, 64, 4, 1, 3))
 
 
 def config_by_name(name: str) -> TreeConfig:

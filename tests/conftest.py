@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 _CONFIG_ORDER = ["tiny", "tiny_bf16", "ragged_f32", "ragged_bf16", "hd128_bf16", "chain_small",
-                 "wide_bf16", "deep_bf16", "batch_bf16", "7b", "13b", "70b", "chain"]
+                 "wide_bf16", "deep_bf16", "batch_bf16", "short_f32", "7b", "13b", "70b", "chain"]
 
 
 def pytest_collection_modifyitems(session, config, items):

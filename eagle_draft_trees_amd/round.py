@@ -72,6 +72,10 @@ class DraftRound:
             raise L.EagleError(L.EAGLE_ERR_SHAPE, "eagle_workspace_bytes", L.eagle_last_error())
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         L.eagle_workspace_init(self.dims, self.tcfg, self.ws)
+        # per-segment softmax statistics of the relaxed verify (allocated here,
+        # so that a call captured into a graph allocates nothing)
+        self._rv_scratch = torch.empty(L.eagle_verify_relaxed_scratch_bytes(self.tcfg),
+                                       dtype=torch.uint8, device=dev)
 
     def reset_state(self, inputs: Dict[str, object]) -> None:
         """Reload the sequence state from host arrays and zero the workspace."""
@@ -109,9 +113,6 @@ class DraftRound:
     def verify_relaxed(self, temperature: float, threshold: float, uniforms: torch.Tensor,
                        target_logits: Optional[torch.Tensor] = None, stream=None) -> None:
         tl = self.target_logits if target_logits is None else target_logits
-        if getattr(self, "_rv_scratch", None) is None:
-            self._rv_scratch = torch.empty(L.eagle_verify_relaxed_scratch_bytes(self.tcfg),
-                                           dtype=torch.uint8, device=self.device)
         L.eagle_verify_relaxed(self.tcfg, self.cfg.V, tl, self.tokens, self.parents, temperature,
                                threshold, uniforms, self.accept_len, self.accept_path, self.bonus,
                                self._rv_scratch, stream)

@@ -285,7 +285,8 @@ int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *t
  * eagle_verify_relaxed_scratch_bytes(cfg) bytes, 8-byte aligned, owned by the
  * caller and overwritten (the per-segment softmax statistics of every tree
  * row).  Outputs as for eagle_verify_greedy.  Logits of -inf carry no
- * probability.  batch*m at most 65535. */
+ * probability; a stop row whose logits are all -inf (no distribution) gives
+ * bonus 0.  batch*m at most 65535. */
 size_t eagle_verify_relaxed_scratch_bytes(const eagle_tree_cfg *cfg);   /* 0 if cfg is invalid */
 int eagle_verify_relaxed(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
                          const int32_t *tokens, const int32_t *parents, float temperature,

@@ -295,16 +295,18 @@ __device__ __forceinline__ const T* wtile_base(const void* w, int nks, int t, in
   return (const T*)w + (size_t)t * nks * wtile_elems<T>() + lane * El<T>::PER16;
 }
 
-// The SwiGLU activations (the down projection's X) are stored in the same
-// lane order as the A operand: rows in groups of 16, element (r, k) of the
-// [rows][K] matrix at (((r/16) * nks + k/KSTEP) * 64 + 16 * g + r%16) * PER16
-// + k%PER16 with g = (k%KSTEP)/PER16, so that one 16-row k-step of X is one
-// contiguous kilobyte.
+// The SwiGLU activations (the down projection's X) are stored in blocks of
+// 16 rows x one k-step (one contiguous kilobyte), row-major inside a block:
+// element (r, k) of the [rows][K] matrix at ((r/16) * nks + k/KSTEP) * 16 *
+// KSTEP + (r%16) * KSTEP + k%KSTEP.  A lane's A-operand piece (row i, 16
+// bytes) is one aligned 16-byte load, and the rows of a block that lie past
+// the real rows fill whole cache lines at its end, which a reader that
+// points those lanes at the last real row never fetches.
 template <typename T>
 __host__ __device__ __forceinline__ size_t xpk_index(int r, int k, int nks) {
-  constexpr int KS = El<T>::KSTEP, PER = El<T>::PER16;
-  const int s = k / KS, kk = k - s * KS, g = kk / PER, e = kk - g * PER;
-  return (((size_t)(r >> 4) * nks + s) * 64 + g * 16 + (r & 15)) * PER + e;
+  constexpr int KS = El<T>::KSTEP;
+  const int s = k / KS;
+  return (((size_t)(r >> 4) * nks + s) * 16 + (r & 15)) * KS + (k - s * KS);
 }
 
 // q/k/v tiles are numbered over the heads in the order [q heads | k heads |

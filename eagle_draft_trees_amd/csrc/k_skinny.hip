@@ -101,8 +101,9 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
     }
     x1 = (const T*)a.embed + (size_t)clamp_tok(tok, a.V, a.err) * a.d;
     kswitch = a.d;
-  } else if (OP == OP_DOWN) {  // packed activations: this lane's piece of k-step 0 (row c)
-    x0 = (const T*)a.act + lane * El<T>::PER16;
+  } else if (OP == OP_DOWN) {  // packed activations: this lane's piece of k-step 0 (row c;
+    // rows past M read row 0, so the block's padding lines are never fetched)
+    x0 = (const T*)a.act + (size_t)xr * KS + g * El<T>::PER16;
     x1 = x0;
   } else {
     const T* xb = (OP == OP_QKV) ? (const T*)a.x0b : (OP == OP_O) ? (const T*)a.attn : (const T*)a.yg;

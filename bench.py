@@ -160,7 +160,7 @@ def batched_lmhead(torch, L, dev, stream, rows=512, vocab=128256, d=4096, reps=1
     torch.cuda.synchronize()
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
     tflops = 2.0 * rows * vocab * d / (ms * 1e-3) / 1e12
-    return {"kernel": "k_lmgemm (batched LM-head GEMM + per-slab softmax/top-k; bf16, rows > 64)",
+    return {"kernel": "k_lg_xpack + k_lmgemm (feature rows into fragment order, then the batched LM-head GEMM + per-slab softmax/top-k; bf16, rows > 64)",
             "rows": rows, "vocab": vocab, "d": d, "bound": "mfma",
             "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(ms * 1e3, 1),

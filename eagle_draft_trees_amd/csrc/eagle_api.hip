@@ -181,6 +181,8 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   const size_t lp = std::max(plan_lm(B, d, k).part_floats, plan_lm(rows_lv, d, k).part_floats);
   L.lmpart = take(lp * 4);
   L.lmres = take((size_t)std::max(B, rows_lv) * 2 * k * 4);
+  // the batched LM head's input rows in fragment order (16 rows x 32 k per KB)
+  L.xpk = take(d.dtype == EAGLE_BF16 ? (size_t)cdiv(std::max(B, rows_lv), 16) * 16 * cdiv(d.d, 32) * 32 * 2 : 0);
   // (tree verify: m rows per sequence)
   const size_t ap = std::max({plan_attn(MODE_LEVEL, k, d, c, B).part_floats,
                               plan_attn(MODE_EXTEND, re, d, c, B).part_floats,
@@ -316,7 +318,7 @@ static RoundArgs make_args(const eagle_dims& d, const eagle_tree_cfg& c, const e
   a.attn = base + L.attn; a.yf = (float*)(base + L.yf); a.yg = base + L.yg;
   a.rstd = (float*)(base + L.rstd); a.ssq = (float*)(base + L.ssq); a.act = base + L.act;
   a.gpart = (float*)(base + L.gpart); a.lmpart = (float*)(base + L.lmpart);
-  a.lmres = (float*)(base + L.lmres); a.apart = (float*)(base + L.apart);
+  a.lmres = (float*)(base + L.lmres); a.apart = (float*)(base + L.apart); a.xpk = base + L.xpk;
   a.pool_n = L.pool_n;
   return a;
 }

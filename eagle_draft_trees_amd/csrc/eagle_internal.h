@@ -180,7 +180,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 struct WsLayout {
   size_t err, cnt, pool, frontier, feat, tk, tv, ext_h;
   size_t x0f, x0b, q, attn, yf, yg, rstd, ssq, act;
-  size_t gpart, lmpart, lmres, apart;
+  size_t gpart, lmpart, lmres, apart, xpk;
   size_t total;
   int rows_max, pool_n;
 };
@@ -267,6 +267,7 @@ struct RoundArgs {
   float *rstd, *ssq;
   void* act;
   float *gpart, *lmpart, *lmres, *apart;
+  void* xpk;  // batched LM head: its input rows in MFMA fragment order
   int pool_n;
 };
 

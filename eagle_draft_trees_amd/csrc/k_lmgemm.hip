@@ -13,9 +13,12 @@
 //    once per 512 rows and each feature fragment is reused four times;
 //  * per k-step of 32, the 512 feature rows (32 KB) and the 128 weight rows
 //    (8 KB) are staged in LDS in MFMA-fragment order (one kilobyte per 16x32
-//    fragment, lane l's 16 bytes at l*16: the packed weight tiles are already
-//    in that order), so every operand read is one conflict-free 16-byte LDS
-//    read per lane;
+//    fragment, lane l's 16 bytes at l*16), so every operand read is one
+//    conflict-free 16-byte LDS read per lane.  The packed weight tiles are
+//    already in that order, and k_lg_xpack first writes the feature rows in it
+//    (k past K zeroed, rows past M repeating row M-1), so every global load of
+//    either operand is one contiguous kilobyte per wave instead of 16 rows'
+//    half cache lines;
 //  * two LDS buffers and two register stages: the global loads of step s+2
 //    are in flight while step s computes, one barrier per step;
 //  * epilogue: a wave's 64 columns are one 64-column slab of the same record
@@ -41,6 +44,20 @@ static_assert(LG_WB * WAVE == LG_THREADS, "one weight piece per thread per step"
 
 size_t lmgemm_lds_bytes() { return (size_t)(2 * LG_STAGE > LG_EPI ? 2 * LG_STAGE : LG_EPI); }
 
+// The feature rows [M][K] (row-major bf16, K a multiple of 8) in fragment
+// order: block (group, s) = rows 16*group.. x k 32*s.., lane l = 16g + i's 16
+// bytes (row 16*group + i, k 32*s + 8g..) at l*16.  One wave per block.
+__global__ void __launch_bounds__(256) k_lg_xpack(const bf16_t* x, int M, int K, int nks, int nblocks,
+                                                  bf16_t* xpk) {
+  const int blk = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (blk >= nblocks) return;
+  const int grp = blk / nks, s = blk - grp * nks;
+  const int row = min(16 * grp + (lane & 15), M - 1), k = 32 * s + 8 * (lane >> 4);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (k < K) v = ld16(x + (size_t)row * K + k);
+  *(uint4*)(xpk + (size_t)blk * 512 + lane * 8) = v;
+}
+
 __global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, int level) {
   typedef bf16_t T;
   constexpr int KS = El<T>::KSTEP;  // 32
@@ -52,37 +69,30 @@ __global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, in
   const int K = a.d, kk_ = a.k;
   const int nks = (K + KS - 1) / KS;
   const int ntile = (a.V + 15) / 16;
-  const T* xbase = (level == 1) ? (const T*)a.root_feat
-                                : (const T*)a.feat + (size_t)(level - 1) * a.B * kk_ * K;
-
   // ---- staging sources: thread tid fills lane (tid % 64) of feature
-  // fragments tid/64 + 8u (u < 4) and of weight fragment tid/64
-  const int fl = lane, fg = fl >> 4, fi = fl & 15;
+  // fragments tid/64 + 8u (u < 4) and of weight fragment tid/64; both come
+  // from fragment-ordered buffers (a group past the last reads the last)
+  const int ngrp = (p.M + 15) / 16;
   const T* xsrc[LG_XP];
 #pragma unroll
   for (int u = 0; u < LG_XP; ++u) {
-    const int mt = (tid >> 6) + LG_W * u;
-    const int row = min(zg * LG_ROWS + 16 * mt + fi, p.M - 1);  // rows past M: row M-1 (never stored)
-    xsrc[u] = xbase + (size_t)row * K + 8 * fg;
+    const int grp = min(zg * (LG_ROWS / 16) + (tid >> 6) + LG_W * u, ngrp - 1);
+    xsrc[u] = (const T*)a.xpk + (size_t)grp * nks * wtile_elems<T>() + lane * El<T>::PER16;
   }
   const T* wsrc = wtile_base<T>(a.lm_head, nks, min(LG_WB * blk + (tid >> 6), ntile - 1), lane);
-  const int klast = K - 8;
   typedef uint4 Stage[LG_XP + 1];
-  // loads are unconditional from clamped addresses; feature pieces past K are
-  // zeroed when stored (the wait for the data belongs there)
+  // loads are unconditional from clamped addresses
   auto gload = [&](Stage& r, int s) __attribute__((always_inline)) {
     s = min(s, nks - 1);  // past the last step: repeats it (stored, never read)
-    const int k = s * KS + 8 * fg;
 #pragma unroll
-    for (int u = 0; u < LG_XP; ++u) r[u] = ld16(xsrc[u] + (min(k, klast) - 8 * fg));
+    for (int u = 0; u < LG_XP; ++u) r[u] = ld16(xsrc[u] + (size_t)s * wtile_elems<T>());
     r[LG_XP] = ld16w(wsrc + (size_t)s * wtile_elems<T>());
   };
   auto lstore = [&](const Stage& r, int buf, int s) __attribute__((always_inline)) {
+    (void)s;
     unsigned char* b = lds + buf * LG_STAGE;
-    const bool kin = s * KS + 8 * fg < K;
 #pragma unroll
-    for (int u = 0; u < LG_XP; ++u)
-      *(uint4*)(b + (size_t)((tid >> 6) + LG_W * u) * 1024 + lane * 16) = mask4(r[u], kin);
+    for (int u = 0; u < LG_XP; ++u) *(uint4*)(b + (size_t)((tid >> 6) + LG_W * u) * 1024 + lane * 16) = r[u];
     *(uint4*)(b + (size_t)(LG_XB + (tid >> 6)) * 1024 + lane * 16) = r[LG_XP];
   };
 
@@ -206,10 +216,21 @@ __global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, in
 
 hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
                          hipEvent_t e1) {
+  // the feature rows into fragment order, then the GEMM (with events, the
+  // first stamps the pack's start and the second the GEMM's end)
+  const int K = a.d, nks = (K + 31) / 32, nblocks = (p.M + 15) / 16 * nks;
+  const bf16_t* x = level == 1 ? (const bf16_t*)a.root_feat
+                               : (const bf16_t*)a.feat + (size_t)(level - 1) * a.B * a.k * K;
+  const dim3 pgrid((nblocks + 3) / 4);
+  if (e0)
+    hipExtLaunchKernelGGL(k_lg_xpack, pgrid, dim3(256), 0u, s, e0, nullptr, 0u, x, p.M, K, nks, nblocks,
+                          (bf16_t*)a.xpk);
+  else
+    hipLaunchKernelGGL(k_lg_xpack, pgrid, dim3(256), 0, s, x, p.M, K, nks, nblocks, (bf16_t*)a.xpk);
   const dim3 grid((a.V + LG_COLS - 1) / LG_COLS, 1, p.zg), block(LG_THREADS);
   const size_t lds = lmgemm_lds_bytes();
-  if (e0 || e1)
-    hipExtLaunchKernelGGL(k_lmgemm, grid, block, (uint32_t)lds, s, e0, e1, 0u, a, p, level);
+  if (e1)
+    hipExtLaunchKernelGGL(k_lmgemm, grid, block, (uint32_t)lds, s, nullptr, e1, 0u, a, p, level);
   else
     hipLaunchKernelGGL(k_lmgemm, grid, block, lds, s, a, p, level);
   return hipGetLastError();

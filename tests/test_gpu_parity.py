@@ -290,18 +290,36 @@ def test_verify_walk(name):
 
 @pytest.mark.parametrize("name", FAST + FULL)
 def test_extend(name):
+    _extend_case(name, "random")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_bf16", "hd128_bf16", "7b", "70b"])
+def test_extend_full_length(name):
+    """accept_len = min(m, depth+1), the most the extend forwards per sequence,
+    with the accepted path set directly to flat nodes 0, 1, 2, ... (the extend
+    reads only the path, its tokens and the bonus), so that every extend row,
+    the last included, carries real inputs and the last is the next root."""
+    _extend_case(name, "full")
+
+
+def _extend_case(name, plant):
     import torch
     cfg, inp, r, model, seqs = get(name)
-    say(f"[extend] {name}")
+    say(f"[extend:{plant}] {name}")
     orc = _oracle_pool(cfg, inp, model, seqs)
     trees = _trees(cfg, orc)
     TL = _plant(cfg, inp, trees, orc.seqs, p=0.9)
     _upload_tree(r, trees, orc.seqs)
     al, ap, bo = (r.accept_len.cpu().numpy(), r.accept_path.cpu().numpy(), r.bonus.cpu().numpy())
     ores = {}
+    rng = np.random.default_rng(23)
     for b in orc.seqs:
         tr = trees[b][0]
-        path, alen, bonus, _ = O.verify_greedy(TL[b].astype(np.float64), tr.tokens, tr.parents)
+        if plant == "full":
+            alen = min(cfg.m, cfg.D + 1)
+            path, bonus = list(range(alen)), int(rng.integers(0, cfg.V))
+        else:
+            path, alen, bonus, _ = O.verify_greedy(TL[b].astype(np.float64), tr.tokens, tr.parents)
         al[b], bo[b] = alen, bonus
         ap[b] = path + [-1] * (cfg.D + 1 - alen)
         ores[b] = (path, alen, bonus)

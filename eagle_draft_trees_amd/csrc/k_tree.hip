@@ -503,11 +503,18 @@ __global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, co
       const unsigned long long pb = __ballot(kid && inr && pc >= thr && len <= D);
       if (!pb) {  // the stop: what the residual draw needs
         if (lane < RS_SEG) s_seg[lane] = seg;
+        // a token that an earlier child already carries is removed once:
+        // its mass is subtracted from its segment only by the first
+        bool dup = false;
+        for (unsigned long long rest = kb; rest; rest &= rest - 1ull) {  // the children, in flat order
+          const int j = __ffsll((long long)rest) - 1;
+          dup = dup || (j < lane && __builtin_amdgcn_readlane(tok, j) == tok);
+        }
         if (kid) {
           const int slot = __popcll(kb & ((1ull << lane) - 1ull));
           s_kid[slot] = inr ? tok : -1;
           s_kseg[slot] = inr ? tok / SEGV : -1;
-          s_ke[slot] = e;
+          s_ke[slot] = dup ? 0.f : e;
         }
         if (lane == 0) {
           s_M = M;

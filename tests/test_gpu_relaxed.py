@@ -169,6 +169,15 @@ def test_relaxed_edge_cases():
     for uu in (0.05, 0.25, 0.55, 0.95):
         g = _run(1, m2, 3, V2, 1.0, 0.9, t2, p2, l2, np.array([uu], np.float32))
         _check(f"all-children u={uu}", 1, m2, 3, V2, 1.0, 0.9, t2, p2, l2, np.array([uu], np.float32), g)
+    # siblings carrying the same token (not a rerank output, but accepted by
+    # the ABI): the token is removed from the residual once
+    t4 = np.array([[3, 7, 7, 9, 7]], dtype=np.int64)
+    p4 = np.array([[-1, 0, 0, 0, 1]], dtype=np.int64)
+    l4 = (rng.standard_normal((1, 5, 40)) * 0.3).astype(np.float32)
+    for uu in (0.1, 0.45, 0.8):
+        g = _run(1, 5, 3, 40, 1.0, 0.9, t4, p4, l4, np.array([uu], np.float32))
+        _check(f"duplicate siblings u={uu}", 1, 5, 3, 40, 1.0, 0.9, t4, p4, l4, np.array([uu], np.float32), g)
+        assert g[2][0] not in (7, 9)
     # two nodes: root and one child
     t3 = np.array([[5, 9]], dtype=np.int64)
     p3 = np.array([[-1, 0]], dtype=np.int64)

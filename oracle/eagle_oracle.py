@@ -77,6 +77,14 @@ Readings of what the pages leave open (each also listed in the design doc):
       point-mass proposals), by inverse CDF over token ids with one uniform
       u in [0, 1) supplied per sequence.  If the children hold all of p's
       mass the draw is from p itself.
+  R16 static tree (EAGLE-1 / Medusa, [P1] §10.1: a fixed-shape tree with a
+      fixed number of candidates per level, its shape set once for every
+      input; [P3]: EAGLE-1 drafts on one static tree): a template of k slots
+      per depth.  Depth 1 is the root's top-k in rank order; slot j of depth
+      L >= 2 is the child of rank rank[L][j] (in the parent's top-k order) of
+      slot parent[L][j] of depth L-1.  The draft forward, LM head and top-k
+      are those of the dynamic tree; the tree is every template node, root
+      first, then depth-major, then slot order (its first m nodes).
 
 Parity pins: every function below is pinned by a CPU test (tests/
 test_oracle_*.py) against brute force, closed forms, special cases or the
@@ -98,7 +106,8 @@ __all__ = [
     "attend_row", "draft_rows", "finish_rows", "lm_logits", "lm_tail", "level_one",
     "level_step_forward", "level_step_tail", "rerank", "build_tree", "verify_greedy",
     "draft_extend", "run_round", "RoundResult", "NEAR_TIE", "tree_verify_attention",
-    "target_probs", "sample_residual", "verify_relaxed",
+    "target_probs", "sample_residual", "verify_relaxed", "level_step_tail_static",
+    "build_static_tree",
 ]
 
 NEAR_TIE = 1e-3  # a selection whose margin (log domain) is below this is "near-tie"
@@ -367,6 +376,62 @@ def level_step_tail(model: Model, level: int, frontier: List[FrontierNode],
     sc = [pool[i].score for i in cand[:k + 1]]
     sel_margin = min((sc[i] - sc[i + 1] for i in range(len(sc) - 1)), default=math.inf)
     return nxt, tails, sel_margin
+
+
+def level_step_tail_static(model: Model, level: int, frontier: List[FrontierNode],
+                           h_rows: np.ndarray, pool: List[PoolEntry], k: int,
+                           parent: Sequence[int], rank: Sequence[int]):
+    """Tail of level >= 2 on a static tree (R16; [P1] §10.1): each frontier
+    node's top-k children are scored and pooled exactly as in the dynamic
+    tail, in (frontier slot, child rank) order; the next frontier's slot j is
+    the child of rank rank[j] of slot parent[j], whatever its score."""
+    base = len(pool)
+    assert base == k + (level - 2) * k * k
+    tails = []
+    for j, x in enumerate(frontier):
+        ids, logp, margin = lm_tail(model, h_rows[j], k)
+        tails.append(margin)
+        for t, lp in zip(ids, logp):
+            pool.append(PoolEntry(x.score + float(lp), float(lp), int(t), x.pool_idx, level, j))
+    nxt = []
+    for j2 in range(k):
+        pj, rk = int(parent[j2]), int(rank[j2])
+        if not (0 <= pj < k and 0 <= rk < k):
+            raise ValueError("template slot out of range")
+        i = base + pj * k + rk
+        e = pool[i]
+        nxt.append(FrontierNode(e.token, e.score, i, pj, frontier[pj].anc + (j2,)))
+    return nxt, tails
+
+
+def build_static_tree(frontiers: Sequence[Sequence[FrontierNode]], root_token: int, P: int,
+                      m: int) -> "Tree":
+    """Flatten a static tree (R16): the root, then depth 1..D, each in slot
+    order; node (L, j) has flat index 1 + (L-1)*k + j and its parent is the
+    root (L = 1) or slot pslot of depth L-1.  Positions P-1+depth ([P1] §12
+    item 5), ancestor-or-self mask.  The first m nodes are kept (parents
+    precede children, so the kept set is ancestor-closed)."""
+    k = len(frontiers[0])
+    n = min(m, 1 + len(frontiers) * k)
+    tokens = np.empty(n, dtype=np.int64)
+    parents = np.empty(n, dtype=np.int64)
+    depth = np.empty(n, dtype=np.int64)
+    logscore = np.zeros(n, dtype=np.float64)
+    tokens[0], parents[0], depth[0] = root_token, -1, 0
+    for f in range(1, n):
+        L, j = 1 + (f - 1) // k, (f - 1) % k
+        x = frontiers[L - 1][j]
+        tokens[f], depth[f], logscore[f] = x.token, L, x.score
+        parents[f] = 0 if L == 1 else 1 + (L - 2) * k + x.pslot
+    mask = np.zeros((n, n), dtype=np.uint8)
+    for f in range(n):
+        a = f
+        while a != -1:
+            mask[f, a] = 1
+            a = parents[a]
+    pool_idx = np.array([-1] + [frontiers[(f - 1) // k][(f - 1) % k].pool_idx for f in range(1, n)],
+                        dtype=np.int64)
+    return Tree(tokens, parents, depth, P - 1 + depth, mask, logscore, pool_idx)
 
 
 # --------------------------------------------------------------------------- rerank, build

@@ -253,6 +253,41 @@ def relaxed_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
             "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}
 
 
+def static_round(torch, r, cfg, stream, saved_plen, rounds=50) -> dict:
+    """A whole round on a static tree at the round's shape: the template's
+    slot j of every depth >= 2 is the best child (rank 0) of slot j, i.e. the
+    root's k children each extended greedily, m = min(1 + D*k, m) nodes.
+    Captured and timed like the dynamic round."""
+    k, D = cfg.k, cfg.D
+    tm = torch.zeros(D, k, 2, dtype=torch.int32)
+    tm[:, :, 0] = torch.arange(k, dtype=torch.int32)
+    tmpl = tm.to(r.device)
+
+    def one():
+        r.run_static_round(tmpl, stream=stream)
+        torch.add(saved_plen, 0, out=r.prefix_len)
+
+    with torch.cuda.stream(stream):
+        one()
+    torch.cuda.synchronize()
+    per = 10
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(per):
+            one()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(rounds // per):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return {"rounds_per_s": round(rounds / el, 1), "ms_per_round": round(el * 1e3 / rounds, 4),
+            "template": "slot j of every depth >= 2 = rank-0 child of slot j (k greedy chains)",
+            "timing": f"{rounds} rounds from a graph of {per}, wall clock"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -409,6 +444,8 @@ def main() -> int:
     }
     out["tree_verify_attention"] = tree_verify(torch, L, r, cfg, stream)
     out["relaxed_verify"] = relaxed_verify(torch, L, r, cfg, stream)
+    if 1 + cfg.D * cfg.k >= cfg.m:
+        out["static_round"] = static_round(torch, r, cfg, stream, saved_plen)
     if not args.no_batched:
         out["mfma_batched_lmhead"] = batched_lmhead(torch, L, dev, stream)
     if not args.no_cpu_baseline:

@@ -97,6 +97,12 @@ def lib() -> ctypes.CDLL:
             "eagle_rerank_build_tree": (c_int32, [P(EagleDims), P(EagleTreeCfg), P(EagleSeqState),
                                                   c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
                                                   c_void_p, c_void_p, c_void_p, c_void_p]),
+            "eagle_draft_level_static": (c_int32, [P(EagleDims), P(EagleWeights), P(EagleTreeCfg),
+                                                   P(EagleSeqState), c_int32, c_int32, c_void_p,
+                                                   c_void_p, c_size_t, c_void_p]),
+            "eagle_build_static_tree": (c_int32, [P(EagleDims), P(EagleTreeCfg), P(EagleSeqState),
+                                                  c_void_p, c_size_t, c_void_p, c_void_p, c_void_p,
+                                                  c_void_p, c_void_p, c_void_p, c_void_p]),
             "eagle_verify_greedy": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
             "eagle_verify_relaxed_scratch_bytes": (c_size_t, [P(EagleTreeCfg)]),
@@ -220,6 +226,22 @@ def eagle_rerank_build_tree(dims, cfg, state, ws, tokens, parents, depth=None, p
                                          _ptr(depth), _ptr(positions), _ptr(mask),
                                          _ptr(node_logscore), _stream(stream)),
            "eagle_rerank_build_tree")
+
+
+def eagle_draft_level_static(dims, weights, cfg, state, level, flags, tmpl, ws, stream=None) -> None:
+    _check(lib().eagle_draft_level_static(ctypes.byref(dims), ctypes.byref(weights),
+                                          ctypes.byref(cfg), ctypes.byref(state), level, flags,
+                                          _ptr(tmpl), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "eagle_draft_level_static")
+
+
+def eagle_build_static_tree(dims, cfg, state, ws, tokens, parents, depth=None, positions=None,
+                            mask=None, node_logscore=None, stream=None) -> None:
+    _check(lib().eagle_build_static_tree(ctypes.byref(dims), ctypes.byref(cfg), ctypes.byref(state),
+                                         _ptr(ws), _nbytes(ws), _ptr(tokens), _ptr(parents),
+                                         _ptr(depth), _ptr(positions), _ptr(mask),
+                                         _ptr(node_logscore), _stream(stream)),
+           "eagle_build_static_tree")
 
 
 def eagle_verify_greedy(cfg, vocab, target_logits, tokens, parents, accept_len, accept_path, bonus,

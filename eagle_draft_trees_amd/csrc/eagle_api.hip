@@ -427,7 +427,8 @@ int eagle_workspace_init(const eagle_dims* dims, const eagle_tree_cfg* cfg, void
 
 static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
                        const eagle_seq_state* state, int32_t level, int32_t flags, void* ws,
-                       size_t ws_bytes, hipEvent_t e0, hipEvent_t e1, void* stream) {
+                       size_t ws_bytes, hipEvent_t e0, hipEvent_t e1, void* stream,
+                       const int32_t* tmpl = nullptr) {
   int r;
   if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
     return r;
@@ -439,6 +440,7 @@ static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eag
   if ((r = check_weights(w, tail_only)) || (r = check_state(state))) return r;
   const hipStream_t s = (hipStream_t)stream;
   RoundArgs a = make_args(*dims, *cfg, w, state, ws);
+  a.tmpl = tmpl;
   if (level == 1) {
     a.rows = cfg->batch;
     const LmPlan pl = plan_lm(cfg->batch, *dims, cfg->topk);
@@ -469,6 +471,31 @@ int eagle_draft_level_timed(const eagle_dims* dims, const eagle_weights* w,
                             void* stop_event, void* stream) {
   return draft_level(dims, w, cfg, state, level, flags, ws, ws_bytes, (hipEvent_t)start_event,
                      (hipEvent_t)stop_event, stream);
+}
+
+int eagle_draft_level_static(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
+                             const eagle_seq_state* state, int32_t level, int32_t flags,
+                             const int32_t* tmpl, void* ws, size_t ws_bytes, void* stream) {
+  if (!tmpl) return fail(EAGLE_ERR_ARG, "template is NULL");
+  return draft_level(dims, w, cfg, state, level, flags, ws, ws_bytes, nullptr, nullptr, stream, tmpl);
+}
+
+int eagle_build_static_tree(const eagle_dims* dims, const eagle_tree_cfg* cfg,
+                            const eagle_seq_state* state, void* ws, size_t ws_bytes, int32_t* tokens,
+                            int32_t* parents, int32_t* depth, int32_t* positions, uint8_t* mask,
+                            float* node_logscore, void* stream) {
+  int r;
+  if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
+    return r;
+  if ((r = check_state(state))) return r;
+  if (!tokens || !parents) return fail(EAGLE_ERR_ARG, "tokens/parents is NULL");
+  if (cfg->m > 1 + cfg->depth * cfg->topk)
+    return fail(EAGLE_ERR_SHAPE, "m %d > 1 + depth*topk = %d (the static tree's size)", cfg->m,
+                1 + cfg->depth * cfg->topk);
+  RoundArgs a = make_args(*dims, *cfg, nullptr, state, ws);
+  return hip_ok(launch_static_build(a, tokens, parents, depth, positions, mask, node_logscore,
+                                    (hipStream_t)stream),
+                "static build");
 }
 
 int eagle_tree_verify_attention(const eagle_dims* dims, const eagle_tree_cfg* cfg, const float* q,

@@ -262,6 +262,7 @@ struct RoundArgs {
   float* q;
   void* attn;
   const uint8_t* vmask;  // tree verify: the [B][m][m] ancestor-or-self mask
+  const int32_t* tmpl;   // static tree: [D][k] (parent slot, child rank) per slot; null = dynamic
   float* yf;
   void* yg;
   float *rstd, *ssq;
@@ -457,6 +458,8 @@ hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, co
                                  const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
                                  int32_t* bonus, hipStream_t s);
 size_t verify_relaxed_scratch_bytes(int B, int m);
+hipError_t launch_static_build(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
+                               int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // one matrix W [N][K] (row-major) into the packed tile layout; pair_hd > 0:
 // q/k/v row grouping of rotation pairs for head_dim pair_hd

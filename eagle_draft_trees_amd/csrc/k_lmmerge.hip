@@ -14,7 +14,8 @@
 // the root's k children into the pool and frontier; for level L >= 2 the
 // workgroup scores the k*k children (parent score + log p), appends all of
 // them to the pool in (frontier slot, rank) order and keeps the best k by
-// (score desc, pool index asc) as the next frontier.
+// (score desc, pool index asc) as the next frontier; on a static tree the
+// next frontier's slots are instead the template's (parent slot, rank) picks.
 #include <float.h>
 #include <limits.h>
 
@@ -217,23 +218,38 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
       pool[pbase + c] = eagle_pool_entry{s, lp, id, ppi[j], level, j};
     }
   }
-  unsigned long long mine = 0ull;  // lane jn: the jn-th kept child
-  for (int jn = 0; jn < kk_; ++jn) {
-    unsigned long long bk = 0ull;
+  // lane jn: the jn-th kept child (candidate index cw = parent slot * k +
+  // rank, score csc); -1 for a slot left as it was (fewer than k candidates,
+  // impossible as k*k >= k)
+  int cw = -1;
+  float csc = 0.f;
+  if (a.tmpl) {
+    // static tree ([P1] §10.1): slot jn is the child of rank tmpl[.][jn][1]
+    // of slot tmpl[.][jn][0], whatever its score (entries clamped into range)
+    if (lane < kk_) {
+      const int* tp = a.tmpl + ((size_t)(level - 1) * kk_ + lane) * 2;
+      const int pj = clamp_slot(tp[0], kk_), rk = clamp_slot(tp[1], kk_);
+      cw = pj * kk_ + rk;
+      csc = psc[pj] + sres[pj * 2 * kk_ + kk_ + rk];  // the same sum as the candidate's key
+    }
+  } else {
+    unsigned long long mine = 0ull;
+    for (int jn = 0; jn < kk_; ++jn) {
+      unsigned long long bk = 0ull;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bk = key[t] > bk ? key[t] : bk;
-    const unsigned long long win = wave_max_key(bk);
+      for (int t = 0; t < 4; ++t) bk = key[t] > bk ? key[t] : bk;
+      const unsigned long long win = wave_max_key(bk);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) key[t] = key[t] == win ? 0ull : key[t];
-    if (lane == jn) mine = win;
+      for (int t = 0; t < 4; ++t) key[t] = key[t] == win ? 0ull : key[t];
+      if (lane == jn) mine = win;
+    }
+    cw = mine ? argkey_id(mine) : -1;
+    csc = mine ? argkey_value(mine) : 0.f;
   }
-  // a slot with no child (fewer than k candidates, impossible as k*k >= k)
-  // is left as it was
-  const int cw = mine ? argkey_id(mine) : -1;
-  if (lane < kk_ && mine) {
+  if (lane < kk_ && cw >= 0) {
     const int j = cw / kk_;
     fnew[lane].token = __float_as_int(sres[j * 2 * kk_ + (cw - j * kk_)]);
-    fnew[lane].score = argkey_value(mine);
+    fnew[lane].score = csc;
     fnew[lane].pool_idx = pbase + cw;
     fnew[lane].pslot = j;
   }

@@ -311,6 +311,57 @@ __global__ void __launch_bounds__(WAVE) k_rerank_wave(RoundArgs a, int32_t* toke
   }
 }
 
+// Static tree build ([P1] §10.1: EAGLE-1 and Medusa draft on a tree of fixed
+// shape): the tree is every template node, read straight from the frontier
+// records the levels wrote.  Node (depth L, slot j) has flat index
+// 1 + (L-1)*k + j; its parent is the root (L = 1) or slot pslot of depth L-1,
+// and its ancestors are the slots its record lists for depths 1..L.  One wave
+// per sequence, lane f builds flat node f (the first m nodes).
+__global__ void __launch_bounds__(WAVE) k_static_build(RoundArgs a, int32_t* tokens, int32_t* parents,
+                                                       int32_t* depth, int32_t* positions, uint8_t* mask,
+                                                       float* logscore) {
+  const int b = blockIdx.x, f = threadIdx.x, k = a.k, m = a.m;
+  if (f >= m) return;
+  const int P = clamp_prefix(a.prefix_len[b], a);
+  int tok, par, dep;
+  float sc;
+  unsigned long long anc = 1ull;  // the root
+  if (f == 0) {
+    tok = clamp_tok(a.root_token[b], a.V, a.err);
+    par = -1;
+    dep = 0;
+    sc = 0.f;
+  } else {
+    dep = 1 + (f - 1) / k;
+    const int j = (f - 1) - (dep - 1) * k;
+    const eagle_frontier_node& nd = a.frontier[((size_t)dep * a.B + b) * k + j];
+    tok = nd.token;
+    sc = nd.score;
+    par = dep == 1 ? 0 : 1 + (dep - 2) * k + clamp_slot(nd.pslot, k);
+    for (int e = 1; e <= dep; ++e) {  // ancestors at depths 1..dep, then self
+      const int af = 1 + (e - 1) * k + clamp_slot(nd.anc[e - 1], k);
+      if (af < m) anc |= 1ull << af;
+    }
+    anc |= 1ull << f;
+  }
+  tokens[(size_t)b * m + f] = tok;
+  parents[(size_t)b * m + f] = par;
+  if (depth) depth[(size_t)b * m + f] = dep;
+  if (positions) positions[(size_t)b * m + f] = P - 1 + dep;
+  if (logscore) logscore[(size_t)b * m + f] = sc;
+  if (mask) {
+    uint8_t* row = mask + ((size_t)b * m + f) * m;
+    for (int c = 0; c < m; ++c) row[c] = (uint8_t)((anc >> c) & 1ull);
+  }
+}
+
+hipError_t launch_static_build(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
+                               int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s) {
+  hipLaunchKernelGGL(k_static_build, dim3(a.B), dim3(WAVE), 0, s, a, tokens, parents, depth, positions, mask,
+                     logscore);
+  return hipGetLastError();
+}
+
 // Greedy verify, one workgroup (16 waves) per sequence.  [P4] EAGLE-2 diagram:
 // accept the longest consistent path from the root and back off to the last
 // accepted node; the target's choice there is the bonus token.

@@ -100,6 +100,16 @@ class DraftRound:
         L.eagle_draft_level_timed(self.dims, self.wts, self.tcfg, self.state, level, flags,
                                   self.ws, start_event, stop_event, stream)
 
+    def level_static(self, level: int, tmpl: torch.Tensor, flags: int = L.EAGLE_LEVEL_FULL,
+                     stream=None) -> None:
+        L.eagle_draft_level_static(self.dims, self.wts, self.tcfg, self.state, level, flags, tmpl,
+                                   self.ws, stream)
+
+    def build_static(self, stream=None) -> None:
+        L.eagle_build_static_tree(self.dims, self.tcfg, self.state, self.ws, self.tokens,
+                                  self.parents, self.depth, self.positions, self.mask,
+                                  self.logscore, stream)
+
     def rerank(self, stream=None) -> None:
         L.eagle_rerank_build_tree(self.dims, self.tcfg, self.state, self.ws, self.tokens,
                                   self.parents, self.depth, self.positions, self.mask,
@@ -121,6 +131,16 @@ class DraftRound:
         tf = self.true_feat if true_feat is None else true_feat
         L.eagle_draft_extend(self.dims, self.wts, self.tcfg, self.state, tf, self.tokens,
                              self.accept_len, self.accept_path, self.bonus, self.ws, stream)
+
+    def run_static_round(self, tmpl: torch.Tensor, stream=None) -> None:
+        """A round on a static tree: the template's levels, the static build,
+        greedy verify and the extend."""
+        self.level(1, stream=stream)
+        for level in range(2, self.cfg.D + 1):
+            self.level_static(level, tmpl, stream=stream)
+        self.build_static(stream)
+        self.verify(stream=stream)
+        self.extend(stream=stream)
 
     def draft(self, stream=None) -> None:
         for level in range(1, self.cfg.D + 1):

@@ -7,6 +7,8 @@
  *                                         LM head, softmax, top-k, k*k -> k select
  *   eagle_rerank_build_tree               top m-1 of every candidate + the root,
  *                                         flattened, ancestor-only mask, positions
+ *   eagle_draft_level_static,             a static (fixed-shape) tree instead: the
+ *   eagle_build_static_tree               template picks each level's children
  *   eagle_verify_greedy                   greedy longest-accepted-path walk
  *   eagle_verify_relaxed                  threshold acceptance on the target's
  *                                         probabilities, residual draw for the bonus
@@ -240,6 +242,30 @@ int eagle_tree_verify_attention(const eagle_dims *dims, const eagle_tree_cfg *cf
                                 const void *k_cache, const void *v_cache, const int32_t *prefix_len,
                                 const uint8_t *mask, void *out, void *ws, size_t ws_bytes,
                                 void *stream);
+
+/* Static draft tree ([P1] §10.1: EAGLE-1 and Medusa draft on a tree of fixed
+ * shape, a fixed number of candidates per level, chosen once for every
+ * input).  The tree is a template of topk slots per depth: depth 1 is the
+ * root's top-k in rank order; slot j of depth L >= 2 is the child of rank
+ * tmpl[L-1][j][1] (in its parent's top-k order, logit desc, id asc) of slot
+ * tmpl[L-1][j][0] of depth L-1, whatever its score.
+ * eagle_draft_level_static is eagle_draft_level with that selection in place
+ * of the k*k -> k select (the draft forward, LM head, softmax, top-k and the
+ * pool are unchanged).  tmpl: device int32 [depth][topk][2] (row 0 unused),
+ * entries clamped into 0..topk-1; the pairs of one depth should be distinct.
+ * Level 1 ignores tmpl.  eagle_build_static_tree then writes the tree from
+ * the frontiers the levels left in ws: root first, then depth-major, then
+ * slot order (node (L, j) at flat index 1 + (L-1)*topk + j), the first m
+ * nodes (m <= 1 + depth*topk); outputs as for eagle_rerank_build_tree
+ * (node_logscore = the node's path score). */
+int eagle_draft_level_static(const eagle_dims *dims, const eagle_weights *w,
+                             const eagle_tree_cfg *cfg, const eagle_seq_state *state,
+                             int32_t level, int32_t flags, const int32_t *tmpl, void *ws,
+                             size_t ws_bytes, void *stream);
+int eagle_build_static_tree(const eagle_dims *dims, const eagle_tree_cfg *cfg,
+                            const eagle_seq_state *state, void *ws, size_t ws_bytes,
+                            int32_t *tokens, int32_t *parents, int32_t *depth, int32_t *positions,
+                            uint8_t *mask, float *node_logscore, void *stream);
 
 /* Rerank and build ([P1] §10.3 rerank; [P3] organize_draft_results and
  * build_tree_kernel_efficient; [P4] EAGLE-2 diagram).  Per sequence: the best

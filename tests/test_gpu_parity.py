@@ -186,6 +186,74 @@ def test_level_forward_then_tail(name, level):
     say(f"  tail {name} level {level}: {near} near-tie rows")
 
 
+# ------------------------------------------------------------------ static tree
+
+STATIC = ["tiny", "ragged_f32", "hd128_bf16", "wide_bf16", "7b"]
+
+
+@pytest.mark.parametrize("name", STATIC)
+def test_static_tree(name):
+    """Static (fixed-shape) tree, reading R16: per level, the oracle's
+    frontier and random features are seeded and the template's tail-only
+    level runs (children and the template-picked frontier compared); then all
+    the oracle's static frontiers are seeded and the built tree is compared
+    exactly."""
+    import torch
+    from eagle_draft_trees_amd import _lib as L
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[static] {name}")
+    orc = oracle_for(cfg, inp, model, seqs)
+    orc.level1()
+    k, D, B, d = cfg.k, cfg.D, cfg.B, cfg.d
+    es = 2 if cfg.dtype == "bf16" else 4
+    rng = np.random.default_rng(31)
+    tm = np.zeros((D, k, 2), dtype=np.int32)
+    for lv in range(2, D + 1):
+        pairs = rng.choice(k * k, size=k, replace=False)
+        tm[lv - 1, :, 0], tm[lv - 1, :, 1] = pairs // k, pairs % k
+    tmpl = torch.from_numpy(tm).to(r.device)
+    near = 0
+    for level in range(2, D + 1):
+        depth = level - 1
+        h = {b: quant(rng.normal(size=(k, d)), cfg.dtype) for b in orc.seqs}
+        orc.quantize_scores()
+        seed_workspace(r, orc, upto_depth=depth)
+        for b in orc.seqs:
+            for j in range(k):
+                r.ws_write(L.WS_FEAT, store(h[b][j], cfg.dtype), (((depth * B) + b) * k + j) * d * es)
+        sync()
+        r.level_static(level, tmpl, L.EAGLE_LEVEL_TAIL_ONLY)
+        sync()
+        for b in orc.seqs:
+            F, tails = O.level_step_tail_static(orc.model, level, orc.F[b][-1], h[b], orc.pool[b], k,
+                                                tm[level - 1, :, 0], tm[level - 1, :, 1])
+            orc.F[b].append(F)
+            orc.tail_margin[b] += tails
+        gp, gf = gpu_pool(r), gpu_frontier(r, level)
+        base = k + (level - 2) * k * k
+        for b in orc.seqs:
+            n = _check_children(cfg, gp[b], orc.pool[b][base:base + k * k], base, orc.tail_margin[b][-k:], True)
+            near += n
+            if n == 0:
+                _check_frontier(gf[b], orc.F[b][-1])
+                assert np.allclose(gf[b]["score"][:k], [x.score for x in orc.F[b][-1]], atol=SCORE_TOL, rtol=0)
+    orc.quantize_scores()
+    seed_workspace(r, orc, upto_depth=D)
+    sync()
+    r.build_static()
+    sync()
+    tok, par = r.tokens.cpu().numpy(), r.parents.cpu().numpy()
+    dep, pos = r.depth.cpu().numpy(), r.positions.cpu().numpy()
+    msk, lsc = r.mask.cpu().numpy(), r.logscore.cpu().numpy()
+    for b in orc.seqs:
+        tr = O.build_static_tree(orc.F[b], orc.st[b].root_token, orc.st[b].P, cfg.m)
+        assert list(tok[b]) == list(tr.tokens) and list(par[b]) == list(tr.parents)
+        assert list(dep[b]) == list(tr.depth) and list(pos[b]) == list(tr.positions)
+        assert np.array_equal(msk[b], tr.mask)
+        assert np.allclose(lsc[b], tr.logscore, atol=SCORE_TOL, rtol=0)
+    say(f"  static {name}: levels 2..{D} ({near} near-tie rows), tree of {cfg.m} nodes")
+
+
 # ------------------------------------------------------------------ rerank, verify, extend
 
 def _oracle_pool(cfg, inp, model, seqs, seed=5):

@@ -77,6 +77,15 @@ Readings of what the pages leave open (each also listed in the design doc):
       point-mass proposals), by inverse CDF over token ids with one uniform
       u in [0, 1) supplied per sequence.  If the children hold all of p's
       mass the draw is from p itself.
+  R17 strict verification by recursive rejection sampling ([P1] §6.2): at
+      node x, p = softmax(target logits / T) and q = softmax(draft logits / T)
+      (the draft's distribution at x, supplied by the caller as logits at
+      every tree node); x's children are tried in flat order, child c
+      accepted iff u_c * q(t_c) <= p(t_c), i.e. u_c <= min(1, p/q) (u_c the
+      uniform of flat node c); after each rejection p <- norm(max(0, p - q));
+      when every child is rejected (or x is a leaf) the bonus is drawn from
+      the current p by inverse CDF with the sequence's last uniform.  If
+      max(0, p - q) has no mass, p is kept.
   R16 static tree (EAGLE-1 / Medusa, [P1] §10.1: a fixed-shape tree with a
       fixed number of candidates per level, its shape set once for every
       input; [P3]: EAGLE-1 drafts on one static tree): a template of k slots
@@ -107,7 +116,7 @@ __all__ = [
     "level_step_forward", "level_step_tail", "rerank", "build_tree", "verify_greedy",
     "draft_extend", "run_round", "RoundResult", "NEAR_TIE", "tree_verify_attention",
     "target_probs", "sample_residual", "verify_relaxed", "level_step_tail_static",
-    "build_static_tree",
+    "build_static_tree", "verify_rejection",
 ]
 
 NEAR_TIE = 1e-3  # a selection whose margin (log domain) is below this is "near-tie"
@@ -572,6 +581,37 @@ def verify_relaxed(target_logits: np.ndarray, tokens: np.ndarray, parents: np.nd
                 break
         if nxt is None:
             bonus, mg = sample_residual(p, [int(tokens[c]) for c in kids], u)
+            margins.append(mg)
+            return path, len(path), bonus, margins
+        node = nxt
+        path.append(node)
+
+
+def verify_rejection(target_logits: np.ndarray, draft_logits: np.ndarray, tokens: np.ndarray,
+                     parents: np.ndarray, temperature: float, u: Sequence[float]):
+    """Recursive rejection sampling over the tree ([P1] §6.2: accept t-hat iff
+    r <= min(1, p(t-hat)/q(t-hat)), otherwise resample from
+    norm(max(0, p - q)), node by node; R17).  target_logits, draft_logits
+    [m, V]; u [m + 1]: u[c] decides child c, u[m] draws the bonus.  Returns
+    (path of flat indices from the root, accept_len, bonus, margins):
+    |u_c * q(t_c) - p(t_c)| for every child tried, then the draw's margin."""
+    m = len(tokens)
+    node, path, margins = 0, [0], []
+    while True:
+        p = target_probs(target_logits[node], temperature)
+        q = target_probs(draft_logits[node], temperature)
+        nxt = None
+        for c in [c for c in range(m) if parents[c] == node and c != node]:
+            t = int(tokens[c])
+            margins.append(abs(u[c] * q[t] - p[t]))
+            if u[c] * q[t] <= p[t]:
+                nxt = c
+                break
+            r = np.maximum(p - q, 0.0)
+            if r.sum() > 0.0:
+                p = r / r.sum()
+        if nxt is None:
+            bonus, mg = sample_residual(p, [], u[m])
             margins.append(mg)
             return path, len(path), bonus, margins
         node = nxt

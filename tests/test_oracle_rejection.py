@@ -1,0 +1,124 @@
+"""CPU pins of the oracle's recursive rejection sampling (reading R17).
+
+[P1] §6.2 states that the scheme leaves the target distribution exactly
+unchanged.  Here that is checked on the oracle itself: with one or two
+children drawn i.i.d. from the draft distribution q (every token pair
+enumerated with its probability), the first emitted token, measured by
+calling the oracle over grids of uniforms, is distributed as p.  Also: q = p
+accepts every child (the first draft token is always accepted, [P1] §7.1), a
+draft with no mass where the target has any rejects everything, and the
+temperature scales both logits.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import eagle_oracle as O
+
+N = 2000
+GRID = (np.arange(N) + 0.5) / N
+HI = 1.0 - 0.25 / N  # above every grid point: a rejection wherever one is possible
+
+
+def _first_token(tl, dl, tokens, parents, T, u):
+    path, alen, bonus, _ = O.verify_rejection(tl, dl, tokens, parents, T, u)
+    return int(tokens[path[1]]) if alen > 1 else bonus
+
+
+def _frac(values):
+    return float(np.mean(values))
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_one_child_drawn_from_q_is_lossless(seed):
+    rng = np.random.default_rng(seed)
+    V, T = 6, 1.0
+    tl = rng.normal(size=(2, V)) * 1.5
+    dl = rng.normal(size=(2, V)) * 1.5
+    p, q = O.target_probs(tl[0], T), O.target_probs(dl[0], T)
+    parents = np.array([-1, 0])
+    out = np.zeros(V)
+    for t1 in range(V):
+        tokens = np.array([0, t1])
+        u = np.array([0.0, 0.0, 0.0])
+        acc = []
+        for x in GRID:
+            u[1] = x
+            acc.append(_first_token(tl, dl, tokens, parents, T, u) == t1 and
+                       O.verify_rejection(tl, dl, tokens, parents, T, u)[1] == 2)
+        f1 = _frac(acc)
+        draws = np.zeros(V)
+        u[1] = HI
+        for x in GRID:
+            u[2] = x
+            draws[_first_token(tl, dl, tokens, parents, T, u)] += 1.0 / N
+        out[t1] += q[t1] * f1
+        out += q[t1] * (1.0 - f1) * draws
+    assert np.allclose(out, p, atol=4.0 / N)
+
+
+def test_two_children_drawn_iid_from_q_are_lossless():
+    rng = np.random.default_rng(9)
+    V, T = 4, 0.8
+    tl = rng.normal(size=(3, V)) * 1.5
+    dl = rng.normal(size=(3, V)) * 1.5
+    p, q = O.target_probs(tl[0], T), O.target_probs(dl[0], T)
+    parents = np.array([-1, 0, 0])
+    out = np.zeros(V)
+    for t1, t2 in itertools.product(range(V), repeat=2):
+        tokens = np.array([0, t1, t2])
+        u = np.zeros(4)
+        f1 = _frac([O.verify_rejection(tl, dl, tokens, parents, T, np.array([0, x, 0, 0]))[0][1:2] == [1]
+                    for x in GRID])
+        f2 = _frac([O.verify_rejection(tl, dl, tokens, parents, T, np.array([0, HI, x, 0]))[0][1:2] == [2]
+                    for x in GRID])
+        draws = np.zeros(V)
+        for x in GRID:
+            u[:] = [0, HI, HI, x]
+            path, alen, bonus, _ = O.verify_rejection(tl, dl, tokens, parents, T, u)
+            if alen == 1:
+                draws[bonus] += 1.0 / N
+        w = q[t1] * q[t2]
+        out[t1] += w * f1
+        out[t2] += w * (1 - f1) * f2
+        if f2 < 1.0:
+            out += w * (1 - f1) * draws
+    assert np.allclose(out, p, atol=6.0 / N)
+
+
+def test_draft_equal_to_target_accepts_every_first_child():
+    rng = np.random.default_rng(4)
+    m, V = 9, 10
+    parents = np.array([-1, 0, 0, 1, 1, 2, 3, 3, 6])
+    tokens = rng.integers(0, V, size=m)
+    tl = rng.normal(size=(m, V))
+    for u_val in (0.0, 0.5, HI):
+        path, alen, _, _ = O.verify_rejection(tl, tl.copy(), tokens, parents, 1.3, np.full(m + 1, u_val))
+        assert path == [0, 1, 3, 6, 8] and alen == 5
+
+
+def test_draft_without_target_mass_rejects_everything():
+    """q lives on tokens 0..2 where p is zero: every child is rejected, the
+    residual max(0, p - q) is p itself and the bonus is drawn from p."""
+    V = 6
+    tl = np.log(np.array([[1e-300, 1e-300, 1e-300, 0.2, 0.3, 0.5]] * 3))
+    dl = np.log(np.array([[0.5, 0.3, 0.2, 1e-300, 1e-300, 1e-300]] * 3))
+    tokens = np.array([4, 0, 2])
+    parents = np.array([-1, 0, 0])
+    for x, want in ((0.1, 3), (0.3, 4), (0.9, 5)):
+        path, alen, bonus, _ = O.verify_rejection(tl, dl, tokens, parents, 1.0, np.array([0.0, 0.5, 0.5, x]))
+        assert path == [0] and bonus == want
+
+
+def test_temperature_divides_both_logits():
+    rng = np.random.default_rng(6)
+    m, V, T = 6, 8, 2.5
+    parents = np.array([-1, 0, 0, 1, 2, 2])
+    tokens = rng.integers(0, V, size=m)
+    tl, dl = rng.normal(size=(m, V)) * 2, rng.normal(size=(m, V)) * 2
+    for s in range(5):
+        u = np.random.default_rng(s).random(m + 1)
+        a = O.verify_rejection(tl, dl, tokens, parents, T, u)
+        b = O.verify_rejection(tl / T, dl / T, tokens, parents, 1.0, u)
+        assert a[:3] == b[:3]

@@ -105,6 +105,10 @@ def lib() -> ctypes.CDLL:
                                                   c_void_p, c_void_p, c_void_p, c_void_p]),
             "eagle_verify_greedy": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+            "eagle_verify_rejection_scratch_bytes": (c_size_t, [P(EagleTreeCfg), c_int32]),
+            "eagle_verify_rejection": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
             "eagle_verify_relaxed_scratch_bytes": (c_size_t, [P(EagleTreeCfg)]),
             "eagle_verify_relaxed": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                                c_void_p, c_float, c_float, c_void_p,
@@ -249,6 +253,19 @@ def eagle_verify_greedy(cfg, vocab, target_logits, tokens, parents, accept_len, 
     _check(lib().eagle_verify_greedy(ctypes.byref(cfg), vocab, _ptr(target_logits), _ptr(tokens),
                                      _ptr(parents), _ptr(accept_len), _ptr(accept_path),
                                      _ptr(bonus), _stream(stream)), "eagle_verify_greedy")
+
+
+def eagle_verify_rejection_scratch_bytes(cfg, vocab) -> int:
+    return int(lib().eagle_verify_rejection_scratch_bytes(ctypes.byref(cfg), vocab))
+
+
+def eagle_verify_rejection(cfg, vocab, target_logits, draft_logits, tokens, parents, temperature,
+                           uniforms, accept_len, accept_path, bonus, scratch, stream=None) -> None:
+    _check(lib().eagle_verify_rejection(ctypes.byref(cfg), vocab, _ptr(target_logits),
+                                        _ptr(draft_logits), _ptr(tokens), _ptr(parents),
+                                        float(temperature), _ptr(uniforms), _ptr(accept_len),
+                                        _ptr(accept_path), _ptr(bonus), _ptr(scratch),
+                                        _nbytes(scratch), _stream(stream)), "eagle_verify_rejection")
 
 
 def eagle_verify_relaxed_scratch_bytes(cfg) -> int:

@@ -548,6 +548,33 @@ int eagle_verify_greedy(const eagle_tree_cfg* cfg, int32_t vocab, const float* t
                 "verify");
 }
 
+size_t eagle_verify_rejection_scratch_bytes(const eagle_tree_cfg* cfg, int32_t vocab) {
+  if (check_cfg(nullptr, cfg) || vocab < 1) return 0;
+  return (size_t)cfg->batch * vocab * sizeof(float);
+}
+
+int eagle_verify_rejection(const eagle_tree_cfg* cfg, int32_t vocab, const float* target_logits,
+                           const float* draft_logits, const int32_t* tokens, const int32_t* parents,
+                           float temperature, const float* uniforms, int32_t* accept_len,
+                           int32_t* accept_path, int32_t* bonus, void* scratch, size_t scratch_bytes,
+                           void* stream) {
+  int r;
+  if ((r = check_cfg(nullptr, cfg))) return r;
+  if (vocab < 1) return fail(EAGLE_ERR_SHAPE, "vocab %d", vocab);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(EAGLE_ERR_ARG, "temperature %g (positive, finite)", (double)temperature);
+  if (!target_logits || !draft_logits || !tokens || !parents || !uniforms || !accept_len || !accept_path ||
+      !bonus || !scratch)
+    return fail(EAGLE_ERR_ARG, "verify_rejection: NULL pointer");
+  if ((uintptr_t)scratch % 4) return fail(EAGLE_ERR_ARG, "scratch not 4-byte aligned");
+  const size_t need = (size_t)cfg->batch * vocab * sizeof(float);
+  if (scratch_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "scratch %zu < %zu bytes", scratch_bytes, need);
+  return hip_ok(launch_verify_rejection(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, draft_logits,
+                                        tokens, parents, temperature, uniforms, scratch, accept_len,
+                                        accept_path, bonus, (hipStream_t)stream),
+                "verify_rejection");
+}
+
 size_t eagle_verify_relaxed_scratch_bytes(const eagle_tree_cfg* cfg) {
   if (check_cfg(nullptr, cfg)) return 0;
   return verify_relaxed_scratch_bytes(cfg->batch, cfg->m);

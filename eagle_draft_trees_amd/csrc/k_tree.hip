@@ -311,6 +311,250 @@ __global__ void __launch_bounds__(WAVE) k_rerank_wave(RoundArgs a, int32_t* toke
   }
 }
 
+// inclusive prefix sum over the wave's lanes (a fixed order)
+__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const float t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Strict verification by recursive rejection sampling ([P1] §6.2: accept a
+// drafted token t iff u <= min(1, p(t)/q(t)), otherwise resample from
+// norm(max(0, p - q)), node by node).  p and q are the target's and the
+// draft's softmax(logits / T) at the current node.  Children are tried in
+// flat order, child c accepted iff u_c * q(t_c) <= p(t_c); after a rejection
+// p becomes norm(max(0, p - q)) (kept when that has no mass); when every
+// child is rejected the bonus is drawn from the current p by inverse CDF
+// with the sequence's last uniform.
+//
+// One workgroup per sequence.  Per visited node one pass over both rows gives
+// the softmax statistics (strided, coalesced, eight loads in flight per
+// thread, combined in a fixed order).  Until its first rejection a node's p
+// is the row's formula; a rejection costs two passes over the vocabulary (the
+// positive part's mass, then, if it has any, the residual itself into the
+// caller's scratch row, the current p being scratch / Z).  The draw scans
+// contiguous id chunks per thread in id order, every chunk bound the same sum
+// wherever it is formed.
+constexpr int RJ_T = 1024;
+constexpr int RJ_W = RJ_T / WAVE;
+constexpr int RJ_U = 8;
+
+// block-wide sum in a fixed order (waves, then their partials in wave order);
+// every thread gets it
+__device__ __forceinline__ float rj_block_sum(float v, float* sbuf, int tid) {
+  const float w = wave_sum_dpp(v);
+  __syncthreads();
+  if ((tid & 63) == 0) sbuf[tid >> 6] = w;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < RJ_W; ++i) t += sbuf[i];
+  return t;
+}
+
+__global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, const float* tl, const float* dl,
+                                                           const int32_t* tokens, const int32_t* parents,
+                                                           float temperature, const float* uniforms,
+                                                           float* scratch, int32_t* alen, int32_t* apath,
+                                                           int32_t* bonus) {
+#pragma clang fp contract(off)
+  __shared__ float s_m[2][RJ_W], s_s[2][RJ_W], s_red[RJ_W];
+  __shared__ float s_stat[4];  // Mp, Sp, Mq, Sq
+  __shared__ int s_kid[EAGLE_MAX_TREE], s_ktok[EAGLE_MAX_TREE];
+  __shared__ int s_nk, s_pick, s_last;
+  __shared__ int path[EAGLE_MAX_DEPTH + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+  const float invT = 1.0f / temperature;
+  const float* ub = uniforms + (size_t)b * (m + 1);
+  float* pr = scratch + (size_t)b * V;  // the current residual (unnormalised), once materialised
+  int node = 0, len = 1;
+  if (tid == 0) path[0] = 0;
+  bool mat = false;  // the current p lives in pr (divided by pz)
+  float pz = 1.f, Mp = 0.f, Sp = 1.f, Mq = 0.f, Sq = 1.f;
+  auto pcur = [&](int x, const float* rp) -> float {
+    if (mat) return pr[x] / pz;
+    const float z = rp[x] * invT;
+    return z > -INFINITY ? expf(z - Mp) / Sp : 0.f;
+  };
+  auto qval = [&](int x, const float* rq) -> float {
+    const float z = rq[x] * invT;
+    return z > -INFINITY ? expf(z - Mq) / Sq : 0.f;
+  };
+  const float* rp = tl;
+  const float* rq = dl;
+  for (;;) {
+    rp = tl + ((size_t)b * m + node) * V;
+    rq = dl + ((size_t)b * m + node) * V;
+    mat = false;
+    // ---- softmax statistics of both rows
+    float mx[2] = {-INFINITY, -INFINITY}, sm[2] = {0.f, 0.f};
+    for (int x0 = tid; x0 < V; x0 += RJ_T * RJ_U) {
+      float zp[RJ_U], zq[RJ_U];
+#pragma unroll
+      for (int u = 0; u < RJ_U; ++u) {
+        const int x = min(x0 + u * RJ_T, V - 1);
+        const float lp = rp[x], lq = rq[x];
+        const bool in = x0 + u * RJ_T < V;
+        zp[u] = in ? lp * invT : -INFINITY;
+        zq[u] = in ? lq * invT : -INFINITY;
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float* z = r == 0 ? zp : zq;
+        float bm = mx[r];
+#pragma unroll
+        for (int u = 0; u < RJ_U; ++u) bm = z[u] > bm ? z[u] : bm;
+        if (bm > mx[r]) {
+          sm[r] = mx[r] == -INFINITY ? 0.f : sm[r] * expf(mx[r] - bm);
+          mx[r] = bm;
+        }
+#pragma unroll
+        for (int u = 0; u < RJ_U; ++u)
+          if (z[u] > -INFINITY) sm[r] += expf(z[u] - mx[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const float wm = wave_max_dpp(mx[r]);
+      const float ws = wave_sum_dpp(mx[r] == -INFINITY ? 0.f : sm[r] * expf(mx[r] - wm));
+      if (lane == 0) {
+        s_m[r][wave] = wm;
+        s_s[r][wave] = ws;
+      }
+    }
+    // the node's children (flat slots < m <= 64: wave 0), in flat order
+    if (wave == 0) {
+      const bool kid = lane < m && lane != node && parents[(size_t)b * m + lane] == node;
+      const int tok = kid ? tokens[(size_t)b * m + lane] : 0;
+      const unsigned long long kb = __ballot(kid);
+      if (kid) {
+        const int slot = __popcll(kb & ((1ull << lane) - 1ull));
+        s_kid[slot] = lane;
+        s_ktok[slot] = tok;
+      }
+      if (lane == 0) s_nk = len <= D ? __popcll(kb) : 0;  // a path of depth+1 nodes is not extended
+    }
+    __syncthreads();
+    if (tid < 2) {
+      float M = s_m[tid][0];
+      for (int w = 1; w < RJ_W; ++w) M = fmaxf(M, s_m[tid][w]);
+      float S = 0.f;
+      for (int w = 0; w < RJ_W; ++w) S += s_m[tid][w] == -INFINITY ? 0.f : s_s[tid][w] * expf(s_m[tid][w] - M);
+      s_stat[2 * tid] = M;
+      s_stat[2 * tid + 1] = S;
+    }
+    __syncthreads();
+    Mp = s_stat[0];
+    Sp = s_stat[1];
+    Mq = s_stat[2];
+    Sq = s_stat[3];
+    const int nk = s_nk;
+    int next = -1;
+    for (int j = 0; j < nk; ++j) {  // uniform loop: every thread takes the same decisions
+      const int c = s_kid[j], t = s_ktok[j];
+      const bool inr = t >= 0 && t < V;
+      const float pc = inr ? pcur(t, rp) : 0.f, qc = inr ? qval(t, rq) : 0.f;
+      if (inr && ub[c] * qc <= pc) {
+        next = c;
+        break;
+      }
+      // rejected: p <- norm(max(0, p - q)), kept when that has no mass
+      float part = 0.f;
+      for (int x = tid; x < V; x += RJ_T) {
+        const float r = pcur(x, rp) - qval(x, rq);
+        part += r > 0.f ? r : 0.f;
+      }
+      const float Z = rj_block_sum(part, s_red, tid);
+      if (Z > 0.f) {
+        __syncthreads();  // every thread has read the old residual
+        for (int x = tid; x < V; x += RJ_T) {
+          const float r = pcur(x, rp) - qval(x, rq);
+          pr[x] = r > 0.f ? r : 0.f;  // a thread rewrites only the ids it read
+        }
+        __syncthreads();
+        mat = true;
+        pz = Z;
+      }
+    }
+    if (next < 0) break;
+    if (tid == 0) path[len] = next;
+    node = next;
+    ++len;
+    __syncthreads();
+  }
+
+  // ---- the bonus: inverse CDF of the current p, contiguous id chunks in order
+  const float ubonus = ub[m] >= 0.f ? (ub[m] < 1.f ? ub[m] : 0.99999994f) : 0.f;
+  const int CH = (V + RJ_T - 1) / RJ_T;
+  const int x0 = min(V, tid * CH), x1 = min(V, x0 + CH);
+  auto weight = [&](int x) -> float {  // unnormalised mass of id x
+    if (mat) return pr[x];
+    const float z = rp[x] * invT;
+    return z > -INFINITY ? expf(z - Mp) : 0.f;
+  };
+  float w = 0.f;
+  for (int x = x0; x < x1; ++x) w += weight(x);
+  const float wi = wave_incl_scan(w, lane);
+  const float wprev = __shfl_up(wi, 1);
+  __syncthreads();
+  if (lane == WAVE - 1) s_red[wave] = wi;
+  if (tid == 0) {
+    s_pick = -1;
+    s_last = -1;
+  }
+  __syncthreads();
+  float base = 0.f, tot = 0.f;
+  for (int v = 0; v < RJ_W; ++v) {
+    if (v == wave) base = tot;
+    tot = tot + s_red[v];
+  }
+  const float lo = base + (lane > 0 ? wprev : 0.f), hi = base + wi;
+  float target = ubonus * tot;
+  if (!(target < tot)) target = nextafterf(tot, 0.f);
+  if (w > 0.f) {
+    atomicMax(&s_last, tid);
+    if (lo <= target && target < hi) {
+      const float rem = target - lo;
+      float acc = 0.f;
+      int pick = -1, lastx = -1;
+      for (int x = x0; x < x1; ++x) {
+        const float e = weight(x);
+        if (e > 0.f) lastx = x;
+        if (e > 0.f && rem < acc + e) {
+          pick = x;
+          break;
+        }
+        acc += e;
+      }
+      s_pick = pick >= 0 ? pick : lastx;
+    }
+  }
+  __syncthreads();
+  if (s_pick < 0 && tid == s_last) {  // the chunk's scan came out below the target: its last id with mass
+    int lastx = -1;
+    for (int x = x0; x < x1; ++x)
+      if (weight(x) > 0.f) lastx = x;
+    s_pick = lastx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    alen[b] = len;
+    bonus[b] = s_pick >= 0 ? s_pick : 0;
+  }
+  if (tid <= D) apath[(size_t)b * (D + 1) + tid] = tid < len ? path[tid] : -1;
+}
+
+hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, const float* dl,
+                                   const int32_t* tokens, const int32_t* parents, float temperature,
+                                   const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
+                                   int32_t* bonus, hipStream_t s) {
+  hipLaunchKernelGGL(k_verify_rejection, dim3(B), dim3(RJ_T), 0, s, m, D, V, tl, dl, tokens, parents, temperature,
+                     uniforms, (float*)scratch, alen, apath, bonus);
+  return hipGetLastError();
+}
+
 // Static tree build ([P1] §10.1: EAGLE-1 and Medusa draft on a tree of fixed
 // shape): the tree is every template node, read straight from the frontier
 // records the levels wrote.  Node (depth L, slot j) has flat index
@@ -495,15 +739,6 @@ __global__ void __launch_bounds__(RS_T) k_relaxed_stats(int V, const float* tl, 
     for (int w = 0; w < RS_T / WAVE; ++w) S += s_m[w] == -INFINITY ? 0.f : s_s[w] * expf(s_m[w] - M);
     stats[(size_t)row * RS_SEG + sg] = make_float2(M, S);
   }
-}
-
-__device__ __forceinline__ float wave_incl_scan(float v, int lane) {
-#pragma unroll
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const float t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
 }
 
 __global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, const float* tl,

@@ -10,6 +10,7 @@
  *   eagle_draft_level_static,             a static (fixed-shape) tree instead: the
  *   eagle_build_static_tree               template picks each level's children
  *   eagle_verify_greedy                   greedy longest-accepted-path walk
+ *   eagle_verify_rejection                recursive rejection sampling (lossless)
  *   eagle_verify_relaxed                  threshold acceptance on the target's
  *                                         probabilities, residual draw for the bonus
  *   eagle_draft_extend                    draft forward over the accepted path with
@@ -292,6 +293,29 @@ int eagle_rerank_build_tree(const eagle_dims *dims, const eagle_tree_cfg *cfg,
 int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
                         const int32_t *tokens, const int32_t *parents, int32_t *accept_len,
                         int32_t *accept_path, int32_t *bonus, void *stream);
+
+/* Strict verification by recursive rejection sampling ([P1] §6.2: accept a
+ * drafted token t iff u <= min(1, p(t)/q(t)), otherwise resample from
+ * norm(max(0, p - q)), node by node; the result is distributed exactly as the
+ * target).  p = softmax(target_logits[node] / temperature) and q =
+ * softmax(draft_logits[node] / temperature), both [batch][m][vocab] fp32 (the
+ * draft's logits at every flat tree node, kept by the caller; rows of leaves
+ * are not read).  From the root, the node's children are tried in flat order,
+ * child c accepted iff uniforms[b][c] * q(t_c) <= p(t_c); after each
+ * rejection p <- norm(max(0, p - q)) (kept when that has no mass); when every
+ * child is rejected (or the node is a leaf, or the path already holds depth+1
+ * nodes) the bonus is the smallest id whose cumulative p exceeds
+ * uniforms[b][m] (clamped into [0, 1)).  uniforms: device fp32
+ * [batch][m+1], the caller's random numbers.  scratch: device buffer of at
+ * least eagle_verify_rejection_scratch_bytes(cfg, vocab) bytes (one residual
+ * row per sequence), owned by the caller and overwritten.  Outputs as for
+ * eagle_verify_greedy. */
+size_t eagle_verify_rejection_scratch_bytes(const eagle_tree_cfg *cfg, int32_t vocab);
+int eagle_verify_rejection(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
+                           const float *draft_logits, const int32_t *tokens,
+                           const int32_t *parents, float temperature, const float *uniforms,
+                           int32_t *accept_len, int32_t *accept_path, int32_t *bonus,
+                           void *scratch, size_t scratch_bytes, void *stream);
 
 /* Relaxed acceptance ([P2] closing notes on SGLang's verification: the
  * target's probabilities and a probability threshold decide whether a token

@@ -253,6 +253,46 @@ def relaxed_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
             "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}
 
 
+def rejection_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
+    """Strict recursive rejection sampling at the round's shape (temperature
+    1) on the tree the round just built: target logits the round's, draft
+    logits those plus N(0, 0.3^2) noise (a draft close to the target), random
+    uniforms.  Timed like the tree-verify attention."""
+    gen = torch.Generator(device=r.device)
+    gen.manual_seed(3)
+    dl = r.target_logits + 0.3 * torch.randn(r.target_logits.shape, generator=gen, device=r.device)
+    uni = torch.rand(cfg.B, cfg.m + 1, generator=gen, device=r.device, dtype=torch.float32)
+    scr = torch.empty(L.eagle_verify_rejection_scratch_bytes(r.tcfg, cfg.V), dtype=torch.uint8,
+                      device=r.device)
+    call = lambda: L.eagle_verify_rejection(r.tcfg, cfg.V, r.target_logits, dl, r.tokens, r.parents,
+                                            1.0, uni, r.accept_len, r.accept_path, r.bonus, scr,
+                                            stream)
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            call()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * replays)
+    return {"kernel": "k_relaxed_stats x2 + k_verify_rejection", "bound": "latency", "us_per_call": round(us, 2),
+            "accept_len": [int(a) for a in r.accept_len.cpu().numpy()], "temperature": 1.0,
+            "draft": "target logits + N(0, 0.3^2)",
+            "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}
+
+
 def static_round(torch, r, cfg, stream, saved_plen, rounds=50) -> dict:
     """A whole round on a static tree at the round's shape: the template's
     slot j of every depth >= 2 is the best child (rank 0) of slot j, i.e. the
@@ -444,6 +484,7 @@ def main() -> int:
     }
     out["tree_verify_attention"] = tree_verify(torch, L, r, cfg, stream)
     out["relaxed_verify"] = relaxed_verify(torch, L, r, cfg, stream)
+    out["rejection_verify"] = rejection_verify(torch, L, r, cfg, stream)
     if 1 + cfg.D * cfg.k >= cfg.m:
         out["static_round"] = static_round(torch, r, cfg, stream, saved_plen)
     if not args.no_batched:

@@ -550,7 +550,7 @@ int eagle_verify_greedy(const eagle_tree_cfg* cfg, int32_t vocab, const float* t
 
 size_t eagle_verify_rejection_scratch_bytes(const eagle_tree_cfg* cfg, int32_t vocab) {
   if (check_cfg(nullptr, cfg) || vocab < 1) return 0;
-  return (size_t)cfg->batch * vocab * sizeof(float);
+  return verify_rejection_scratch_bytes(cfg->batch, cfg->m);
 }
 
 int eagle_verify_rejection(const eagle_tree_cfg* cfg, int32_t vocab, const float* target_logits,
@@ -566,8 +566,8 @@ int eagle_verify_rejection(const eagle_tree_cfg* cfg, int32_t vocab, const float
   if (!target_logits || !draft_logits || !tokens || !parents || !uniforms || !accept_len || !accept_path ||
       !bonus || !scratch)
     return fail(EAGLE_ERR_ARG, "verify_rejection: NULL pointer");
-  if ((uintptr_t)scratch % 4) return fail(EAGLE_ERR_ARG, "scratch not 4-byte aligned");
-  const size_t need = (size_t)cfg->batch * vocab * sizeof(float);
+  if ((uintptr_t)scratch % 8) return fail(EAGLE_ERR_ARG, "scratch not 8-byte aligned");
+  const size_t need = verify_rejection_scratch_bytes(cfg->batch, cfg->m);
   if (scratch_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "scratch %zu < %zu bytes", scratch_bytes, need);
   return hip_ok(launch_verify_rejection(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, draft_logits,
                                         tokens, parents, temperature, uniforms, scratch, accept_len,

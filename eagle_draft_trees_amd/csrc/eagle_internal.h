@@ -462,6 +462,7 @@ hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, 
                                    const int32_t* tokens, const int32_t* parents, float temperature,
                                    const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
                                    int32_t* bonus, hipStream_t s);
+size_t verify_rejection_scratch_bytes(int B, int m);
 hipError_t launch_static_build(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
                                int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);

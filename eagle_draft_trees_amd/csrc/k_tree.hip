@@ -321,240 +321,6 @@ __device__ __forceinline__ float wave_incl_scan(float v, int lane) {
   return v;
 }
 
-// Strict verification by recursive rejection sampling ([P1] §6.2: accept a
-// drafted token t iff u <= min(1, p(t)/q(t)), otherwise resample from
-// norm(max(0, p - q)), node by node).  p and q are the target's and the
-// draft's softmax(logits / T) at the current node.  Children are tried in
-// flat order, child c accepted iff u_c * q(t_c) <= p(t_c); after a rejection
-// p becomes norm(max(0, p - q)) (kept when that has no mass); when every
-// child is rejected the bonus is drawn from the current p by inverse CDF
-// with the sequence's last uniform.
-//
-// One workgroup per sequence.  Per visited node one pass over both rows gives
-// the softmax statistics (strided, coalesced, eight loads in flight per
-// thread, combined in a fixed order).  Until its first rejection a node's p
-// is the row's formula; a rejection costs two passes over the vocabulary (the
-// positive part's mass, then, if it has any, the residual itself into the
-// caller's scratch row, the current p being scratch / Z).  The draw scans
-// contiguous id chunks per thread in id order, every chunk bound the same sum
-// wherever it is formed.
-constexpr int RJ_T = 1024;
-constexpr int RJ_W = RJ_T / WAVE;
-constexpr int RJ_U = 8;
-
-// block-wide sum in a fixed order (waves, then their partials in wave order);
-// every thread gets it
-__device__ __forceinline__ float rj_block_sum(float v, float* sbuf, int tid) {
-  const float w = wave_sum_dpp(v);
-  __syncthreads();
-  if ((tid & 63) == 0) sbuf[tid >> 6] = w;
-  __syncthreads();
-  float t = 0.f;
-  for (int i = 0; i < RJ_W; ++i) t += sbuf[i];
-  return t;
-}
-
-__global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, const float* tl, const float* dl,
-                                                           const int32_t* tokens, const int32_t* parents,
-                                                           float temperature, const float* uniforms,
-                                                           float* scratch, int32_t* alen, int32_t* apath,
-                                                           int32_t* bonus) {
-#pragma clang fp contract(off)
-  __shared__ float s_m[2][RJ_W], s_s[2][RJ_W], s_red[RJ_W];
-  __shared__ float s_stat[4];  // Mp, Sp, Mq, Sq
-  __shared__ int s_kid[EAGLE_MAX_TREE], s_ktok[EAGLE_MAX_TREE];
-  __shared__ int s_nk, s_pick, s_last;
-  __shared__ int path[EAGLE_MAX_DEPTH + 1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
-  const float invT = 1.0f / temperature;
-  const float* ub = uniforms + (size_t)b * (m + 1);
-  float* pr = scratch + (size_t)b * V;  // the current residual (unnormalised), once materialised
-  int node = 0, len = 1;
-  if (tid == 0) path[0] = 0;
-  bool mat = false;  // the current p lives in pr (divided by pz)
-  float pz = 1.f, Mp = 0.f, Sp = 1.f, Mq = 0.f, Sq = 1.f;
-  auto pcur = [&](int x, const float* rp) -> float {
-    if (mat) return pr[x] / pz;
-    const float z = rp[x] * invT;
-    return z > -INFINITY ? expf(z - Mp) / Sp : 0.f;
-  };
-  auto qval = [&](int x, const float* rq) -> float {
-    const float z = rq[x] * invT;
-    return z > -INFINITY ? expf(z - Mq) / Sq : 0.f;
-  };
-  const float* rp = tl;
-  const float* rq = dl;
-  for (;;) {
-    rp = tl + ((size_t)b * m + node) * V;
-    rq = dl + ((size_t)b * m + node) * V;
-    mat = false;
-    // ---- softmax statistics of both rows
-    float mx[2] = {-INFINITY, -INFINITY}, sm[2] = {0.f, 0.f};
-    for (int x0 = tid; x0 < V; x0 += RJ_T * RJ_U) {
-      float zp[RJ_U], zq[RJ_U];
-#pragma unroll
-      for (int u = 0; u < RJ_U; ++u) {
-        const int x = min(x0 + u * RJ_T, V - 1);
-        const float lp = rp[x], lq = rq[x];
-        const bool in = x0 + u * RJ_T < V;
-        zp[u] = in ? lp * invT : -INFINITY;
-        zq[u] = in ? lq * invT : -INFINITY;
-      }
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float* z = r == 0 ? zp : zq;
-        float bm = mx[r];
-#pragma unroll
-        for (int u = 0; u < RJ_U; ++u) bm = z[u] > bm ? z[u] : bm;
-        if (bm > mx[r]) {
-          sm[r] = mx[r] == -INFINITY ? 0.f : sm[r] * expf(mx[r] - bm);
-          mx[r] = bm;
-        }
-#pragma unroll
-        for (int u = 0; u < RJ_U; ++u)
-          if (z[u] > -INFINITY) sm[r] += expf(z[u] - mx[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const float wm = wave_max_dpp(mx[r]);
-      const float ws = wave_sum_dpp(mx[r] == -INFINITY ? 0.f : sm[r] * expf(mx[r] - wm));
-      if (lane == 0) {
-        s_m[r][wave] = wm;
-        s_s[r][wave] = ws;
-      }
-    }
-    // the node's children (flat slots < m <= 64: wave 0), in flat order
-    if (wave == 0) {
-      const bool kid = lane < m && lane != node && parents[(size_t)b * m + lane] == node;
-      const int tok = kid ? tokens[(size_t)b * m + lane] : 0;
-      const unsigned long long kb = __ballot(kid);
-      if (kid) {
-        const int slot = __popcll(kb & ((1ull << lane) - 1ull));
-        s_kid[slot] = lane;
-        s_ktok[slot] = tok;
-      }
-      if (lane == 0) s_nk = len <= D ? __popcll(kb) : 0;  // a path of depth+1 nodes is not extended
-    }
-    __syncthreads();
-    if (tid < 2) {
-      float M = s_m[tid][0];
-      for (int w = 1; w < RJ_W; ++w) M = fmaxf(M, s_m[tid][w]);
-      float S = 0.f;
-      for (int w = 0; w < RJ_W; ++w) S += s_m[tid][w] == -INFINITY ? 0.f : s_s[tid][w] * expf(s_m[tid][w] - M);
-      s_stat[2 * tid] = M;
-      s_stat[2 * tid + 1] = S;
-    }
-    __syncthreads();
-    Mp = s_stat[0];
-    Sp = s_stat[1];
-    Mq = s_stat[2];
-    Sq = s_stat[3];
-    const int nk = s_nk;
-    int next = -1;
-    for (int j = 0; j < nk; ++j) {  // uniform loop: every thread takes the same decisions
-      const int c = s_kid[j], t = s_ktok[j];
-      const bool inr = t >= 0 && t < V;
-      const float pc = inr ? pcur(t, rp) : 0.f, qc = inr ? qval(t, rq) : 0.f;
-      if (inr && ub[c] * qc <= pc) {
-        next = c;
-        break;
-      }
-      // rejected: p <- norm(max(0, p - q)), kept when that has no mass
-      float part = 0.f;
-      for (int x = tid; x < V; x += RJ_T) {
-        const float r = pcur(x, rp) - qval(x, rq);
-        part += r > 0.f ? r : 0.f;
-      }
-      const float Z = rj_block_sum(part, s_red, tid);
-      if (Z > 0.f) {
-        __syncthreads();  // every thread has read the old residual
-        for (int x = tid; x < V; x += RJ_T) {
-          const float r = pcur(x, rp) - qval(x, rq);
-          pr[x] = r > 0.f ? r : 0.f;  // a thread rewrites only the ids it read
-        }
-        __syncthreads();
-        mat = true;
-        pz = Z;
-      }
-    }
-    if (next < 0) break;
-    if (tid == 0) path[len] = next;
-    node = next;
-    ++len;
-    __syncthreads();
-  }
-
-  // ---- the bonus: inverse CDF of the current p, contiguous id chunks in order
-  const float ubonus = ub[m] >= 0.f ? (ub[m] < 1.f ? ub[m] : 0.99999994f) : 0.f;
-  const int CH = (V + RJ_T - 1) / RJ_T;
-  const int x0 = min(V, tid * CH), x1 = min(V, x0 + CH);
-  auto weight = [&](int x) -> float {  // unnormalised mass of id x
-    if (mat) return pr[x];
-    const float z = rp[x] * invT;
-    return z > -INFINITY ? expf(z - Mp) : 0.f;
-  };
-  float w = 0.f;
-  for (int x = x0; x < x1; ++x) w += weight(x);
-  const float wi = wave_incl_scan(w, lane);
-  const float wprev = __shfl_up(wi, 1);
-  __syncthreads();
-  if (lane == WAVE - 1) s_red[wave] = wi;
-  if (tid == 0) {
-    s_pick = -1;
-    s_last = -1;
-  }
-  __syncthreads();
-  float base = 0.f, tot = 0.f;
-  for (int v = 0; v < RJ_W; ++v) {
-    if (v == wave) base = tot;
-    tot = tot + s_red[v];
-  }
-  const float lo = base + (lane > 0 ? wprev : 0.f), hi = base + wi;
-  float target = ubonus * tot;
-  if (!(target < tot)) target = nextafterf(tot, 0.f);
-  if (w > 0.f) {
-    atomicMax(&s_last, tid);
-    if (lo <= target && target < hi) {
-      const float rem = target - lo;
-      float acc = 0.f;
-      int pick = -1, lastx = -1;
-      for (int x = x0; x < x1; ++x) {
-        const float e = weight(x);
-        if (e > 0.f) lastx = x;
-        if (e > 0.f && rem < acc + e) {
-          pick = x;
-          break;
-        }
-        acc += e;
-      }
-      s_pick = pick >= 0 ? pick : lastx;
-    }
-  }
-  __syncthreads();
-  if (s_pick < 0 && tid == s_last) {  // the chunk's scan came out below the target: its last id with mass
-    int lastx = -1;
-    for (int x = x0; x < x1; ++x)
-      if (weight(x) > 0.f) lastx = x;
-    s_pick = lastx;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    alen[b] = len;
-    bonus[b] = s_pick >= 0 ? s_pick : 0;
-  }
-  if (tid <= D) apath[(size_t)b * (D + 1) + tid] = tid < len ? path[tid] : -1;
-}
-
-hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, const float* dl,
-                                   const int32_t* tokens, const int32_t* parents, float temperature,
-                                   const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
-                                   int32_t* bonus, hipStream_t s) {
-  hipLaunchKernelGGL(k_verify_rejection, dim3(B), dim3(RJ_T), 0, s, m, D, V, tl, dl, tokens, parents, temperature,
-                     uniforms, (float*)scratch, alen, apath, bonus);
-  return hipGetLastError();
-}
-
 // Static tree build ([P1] §10.1: EAGLE-1 and Medusa draft on a tree of fixed
 // shape): the tree is every template node, read straight from the frontier
 // records the levels wrote.  Node (depth L, slot j) has flat index
@@ -988,6 +754,244 @@ hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, co
 }
 
 size_t verify_relaxed_scratch_bytes(int B, int m) { return (size_t)B * m * RS_SEG * sizeof(float2); }
+
+// Strict verification by recursive rejection sampling ([P1] §6.2: accept a
+// drafted token t iff u <= min(1, p(t)/q(t)), otherwise resample from
+// norm(max(0, p - q)), node by node).  p and q are the target's and the
+// draft's softmax(logits / T) at the current node.  Children are tried in
+// flat order, child c accepted iff u_c * q(t_c) <= p(t_c); after a rejection
+// p becomes norm(max(0, p - q)) (kept when that has no mass); when every
+// child is rejected the bonus is drawn from the current p by inverse CDF
+// with the sequence's last uniform.
+//
+// The residual after any number of rejections at a node has a closed form.
+// Start from c = 0, N = 1; on a rejection set c' = c + N and
+// N' = sum_x max(0, p(x) - c' q(x)); if N' > 0 then (c, N) = (c', N').  The
+// current p is then max(0, p - c q) / N: by induction, since q >= 0,
+// max(0, max(0, p - c q)/N - q) = max(0, p - (c + N) q) / N, whose mass is
+// N'/N.  So a rejection costs one pass over the two rows and writes nothing.
+//
+// Three launches.  k_relaxed_stats, once on the target's rows and once on
+// the draft's, reduces every row to per-segment (max, sum) over the chip.
+// k_verify_rejection (one workgroup per sequence) walks: wave 0 holds the
+// tree (lane = flat slot), combines the node's segment statistics and forms
+// p and q at each child's token with one load per lane; the workgroup tries
+// the children in flat order, each rejection one pass over both rows
+// (strided, eight clamped loads per row in flight per thread, summed in a
+// fixed order).  The draw scans contiguous id chunks per thread in id order,
+// every chunk bound the same sum wherever it is formed.
+constexpr int RJ_T = 1024;
+constexpr int RJ_W = RJ_T / WAVE;
+constexpr int RJ_U = 8;
+
+// block-wide sum in a fixed order (waves, then their partials in wave order);
+// every thread gets it
+__device__ __forceinline__ float rj_block_sum(float v, float* sbuf, int tid) {
+  const float w = wave_sum_dpp(v);
+  __syncthreads();
+  if ((tid & 63) == 0) sbuf[tid >> 6] = w;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < RJ_W; ++i) t += sbuf[i];
+  return t;
+}
+
+__global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, const float* tl, const float* dl,
+                                                           const int32_t* tokens, const int32_t* parents,
+                                                           float temperature, const float* uniforms,
+                                                           const float2* stp, const float2* stq, int32_t* alen,
+                                                           int32_t* apath, int32_t* bonus) {
+  // no fused multiply-adds: p - c q and each exp(z - M) are formed the same
+  // way wherever they appear
+#pragma clang fp contract(off)
+  __shared__ float s_red[RJ_W];
+  __shared__ float s_stat[4];  // Mp, Sp, Mq, Sq of the current node
+  __shared__ int s_kid[EAGLE_MAX_TREE], s_kok[EAGLE_MAX_TREE];
+  __shared__ float s_kp[EAGLE_MAX_TREE], s_kq[EAGLE_MAX_TREE];
+  __shared__ int s_nk, s_pick, s_last;
+  __shared__ int path[EAGLE_MAX_DEPTH + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
+  const float invT = 1.0f / temperature;
+  const float* ub = uniforms + (size_t)b * (m + 1);
+  const bool inm = wave == 0 && lane < m;
+  const int par = inm ? parents[(size_t)b * m + lane] : -2;
+  const int tok = inm ? tokens[(size_t)b * m + lane] : -1;
+  const bool inr = tok >= 0 && tok < V;
+  int node = 0, len = 1;
+  if (tid == 0) path[0] = 0;
+  float Mp = 0.f, Sp = 1.f, Mq = 0.f, Sq = 1.f, c = 0.f, N = 1.f;
+  auto pv = [&](float l) -> float {
+    const float z = l * invT;
+    return z > -INFINITY ? expf(z - Mp) / Sp : 0.f;
+  };
+  auto qv = [&](float l) -> float {
+    const float z = l * invT;
+    return z > -INFINITY ? expf(z - Mq) / Sq : 0.f;
+  };
+  const float* rp = tl;
+  const float* rq = dl;
+  for (;;) {
+    rp = tl + ((size_t)b * m + node) * V;
+    rq = dl + ((size_t)b * m + node) * V;
+    if (wave == 0) {
+      const bool kid = inm && lane != node && par == node;
+      const size_t si = ((size_t)b * m + node) * RS_SEG + (lane & (RS_SEG - 1));
+      const float2 sp = stp[si], sq = stq[si];
+      const float lp = rp[(kid && inr) ? tok : 0], lq = rq[(kid && inr) ? tok : 0];
+      const float MP = wave_max_dpp(lane < RS_SEG ? sp.x : -INFINITY);
+      const float MQ = wave_max_dpp(lane < RS_SEG ? sq.x : -INFINITY);
+      const float SP = wave_sum_dpp((lane < RS_SEG && sp.x > -INFINITY) ? sp.y * expf(sp.x - MP) : 0.f);
+      const float SQ = wave_sum_dpp((lane < RS_SEG && sq.x > -INFINITY) ? sq.y * expf(sq.x - MQ) : 0.f);
+      const unsigned long long kb = __ballot(kid);
+      if (kid) {
+        const int slot = __popcll(kb & ((1ull << lane) - 1ull));
+        const float zp = lp * invT, zq = lq * invT;
+        s_kid[slot] = lane;
+        s_kok[slot] = inr;
+        s_kp[slot] = (inr && zp > -INFINITY) ? expf(zp - MP) / SP : 0.f;
+        s_kq[slot] = (inr && zq > -INFINITY) ? expf(zq - MQ) / SQ : 0.f;
+      }
+      if (lane == 0) {
+        s_nk = len <= D ? __popcll(kb) : 0;  // a path of depth+1 nodes is not extended
+        s_stat[0] = MP;
+        s_stat[1] = SP;
+        s_stat[2] = MQ;
+        s_stat[3] = SQ;
+      }
+    }
+    __syncthreads();
+    Mp = s_stat[0];
+    Sp = s_stat[1];
+    Mq = s_stat[2];
+    Sq = s_stat[3];
+    c = 0.f;
+    N = 1.f;
+    const int nk = s_nk;
+    int next = -1;
+    for (int j = 0; j < nk; ++j) {  // uniform loop: every thread takes the same decisions
+      const float pc = s_kp[j], qc = s_kq[j];
+      const float dc = pc - c * qc;
+      const float rc = (dc > 0.f ? dc : 0.f) / N;
+      if (s_kok[j] && ub[s_kid[j]] * qc <= rc) {
+        next = s_kid[j];
+        break;
+      }
+      // rejected: the mass of max(0, p - (c + N) q)
+      const float cn = c + N;
+      float part = 0.f;
+      for (int x0 = tid; x0 < V; x0 += RJ_T * RJ_U) {
+        float lp[RJ_U], lq[RJ_U];
+#pragma unroll
+        for (int u = 0; u < RJ_U; ++u) {  // unconditional loads from clamped ids: all in flight at once
+          const int x = min(x0 + u * RJ_T, V - 1);
+          lp[u] = rp[x];
+          lq[u] = rq[x];
+        }
+#pragma unroll
+        for (int u = 0; u < RJ_U; ++u) {
+          const float r = pv(lp[u]) - cn * qv(lq[u]);
+          part += (x0 + u * RJ_T < V && r > 0.f) ? r : 0.f;
+        }
+      }
+      const float Nn = rj_block_sum(part, s_red, tid);
+      if (Nn > 0.f) {
+        c = cn;
+        N = Nn;
+      }
+    }
+    if (next < 0) break;
+    if (tid == 0) path[len] = next;
+    node = next;
+    ++len;
+    __syncthreads();  // s_kid, s_kp, s_kq, s_stat are rewritten for the next node
+  }
+
+  // ---- the bonus: inverse CDF of the current p, contiguous id chunks in order
+  const float ubonus = ub[m] >= 0.f ? (ub[m] < 1.f ? ub[m] : 0.99999994f) : 0.f;
+  const int CH = (V + RJ_T - 1) / RJ_T;
+  const int x0 = min(V, tid * CH), x1 = min(V, x0 + CH);
+  const bool useq = c > 0.f;  // uniform
+  auto weight = [&](float lp, float lq) -> float {  // mass of an id, up to the factor 1/N
+    const float d = pv(lp) - (useq ? c * qv(lq) : 0.f);
+    return d > 0.f ? d : 0.f;
+  };
+  float w = 0.f;
+  for (int xa = x0; xa < x1; xa += RJ_U) {
+    float lp[RJ_U], lq[RJ_U];
+#pragma unroll
+    for (int u = 0; u < RJ_U; ++u) {
+      const int x = min(xa + u, V - 1);
+      lp[u] = rp[x];
+      lq[u] = useq ? rq[x] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < RJ_U; ++u)
+      if (xa + u < x1) w += weight(lp[u], lq[u]);
+  }
+  const float wi = wave_incl_scan(w, lane);
+  const float wprev = __shfl_up(wi, 1);
+  __syncthreads();
+  if (lane == WAVE - 1) s_red[wave] = wi;
+  if (tid == 0) {
+    s_pick = -1;
+    s_last = -1;
+  }
+  __syncthreads();
+  float base = 0.f, tot = 0.f;
+  for (int v = 0; v < RJ_W; ++v) {
+    if (v == wave) base = tot;
+    tot = tot + s_red[v];
+  }
+  const float lo = base + (lane > 0 ? wprev : 0.f), hi = base + wi;
+  float target = ubonus * tot;
+  if (!(target < tot)) target = nextafterf(tot, 0.f);
+  if (w > 0.f) {
+    atomicMax(&s_last, tid);
+    if (lo <= target && target < hi) {
+      const float rem = target - lo;
+      float acc = 0.f;
+      int pick = -1, lastx = -1;
+      for (int x = x0; x < x1; ++x) {
+        const float e = weight(rp[x], useq ? rq[x] : 0.f);
+        if (e > 0.f) lastx = x;
+        if (e > 0.f && rem < acc + e) {
+          pick = x;
+          break;
+        }
+        acc += e;
+      }
+      s_pick = pick >= 0 ? pick : lastx;
+    }
+  }
+  __syncthreads();
+  if (s_pick < 0 && tid == s_last) {  // the chunk's scan came out below the target: its last id with mass
+    int lastx = -1;
+    for (int x = x0; x < x1; ++x)
+      if (weight(rp[x], useq ? rq[x] : 0.f) > 0.f) lastx = x;
+    s_pick = lastx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    alen[b] = len;
+    bonus[b] = s_pick >= 0 ? s_pick : 0;
+  }
+  if (tid <= D) apath[(size_t)b * (D + 1) + tid] = tid < len ? path[tid] : -1;
+}
+
+hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, const float* dl,
+                                   const int32_t* tokens, const int32_t* parents, float temperature,
+                                   const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
+                                   int32_t* bonus, hipStream_t s) {
+  float2* stp = (float2*)scratch;
+  float2* stq = stp + (size_t)B * m * RS_SEG;
+  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m), dim3(RS_T), 0, s, V, tl, temperature, stp);
+  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m), dim3(RS_T), 0, s, V, dl, temperature, stq);
+  hipLaunchKernelGGL(k_verify_rejection, dim3(B), dim3(RJ_T), 0, s, m, D, V, tl, dl, tokens, parents, temperature,
+                     uniforms, (const float2*)stp, (const float2*)stq, alen, apath, bonus);
+  return hipGetLastError();
+}
+
+size_t verify_rejection_scratch_bytes(int B, int m) { return 2 * (size_t)B * m * RS_SEG * sizeof(float2); }
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   const size_t n16 = bytes / 16;

@@ -299,16 +299,17 @@ int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *t
  * norm(max(0, p - q)), node by node; the result is distributed exactly as the
  * target).  p = softmax(target_logits[node] / temperature) and q =
  * softmax(draft_logits[node] / temperature), both [batch][m][vocab] fp32 (the
- * draft's logits at every flat tree node, kept by the caller; rows of leaves
- * are not read).  From the root, the node's children are tried in flat order,
+ * draft's logits at every flat tree node, kept by the caller; every row is
+ * read).  From the root, the node's children are tried in flat order,
  * child c accepted iff uniforms[b][c] * q(t_c) <= p(t_c); after each
  * rejection p <- norm(max(0, p - q)) (kept when that has no mass); when every
  * child is rejected (or the node is a leaf, or the path already holds depth+1
  * nodes) the bonus is the smallest id whose cumulative p exceeds
  * uniforms[b][m] (clamped into [0, 1)).  uniforms: device fp32
  * [batch][m+1], the caller's random numbers.  scratch: device buffer of at
- * least eagle_verify_rejection_scratch_bytes(cfg, vocab) bytes (one residual
- * row per sequence), owned by the caller and overwritten.  Outputs as for
+ * least eagle_verify_rejection_scratch_bytes(cfg, vocab) bytes, 8-byte
+ * aligned (softmax statistics of every row, per id range), owned by the caller
+ * and overwritten.  Outputs as for
  * eagle_verify_greedy. */
 size_t eagle_verify_rejection_scratch_bytes(const eagle_tree_cfg *cfg, int32_t vocab);
 int eagle_verify_rejection(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,

@@ -122,3 +122,28 @@ def test_temperature_divides_both_logits():
         a = O.verify_rejection(tl, dl, tokens, parents, T, u)
         b = O.verify_rejection(tl / T, dl / T, tokens, parents, 1.0, u)
         assert a[:3] == b[:3]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_residual_closed_form(seed):
+    """The GPU walk keeps the residual after j rejections at a node as
+    max(0, p - c q) / N, with c <- c + N and N <- sum max(0, p - c q) on each
+    rejection (kept when that sum is 0).  Held here to the residual as [P1]
+    §6.2 defines it, norm(max(0, r - q)) applied j times, in fp64."""
+    rng = np.random.default_rng(seed)
+    V = 50
+    p = O.target_probs(rng.normal(size=V) * 2, 1.0)
+    q = O.target_probs(rng.normal(size=V) * 2, 1.0)
+    if seed == 3:
+        q[:10] = 0.0  # the draft misses part of the target's support
+        q /= q.sum()
+    r, c, N = p.copy(), 0.0, 1.0
+    for _ in range(12):
+        d = np.maximum(0.0, r - q)
+        if d.sum() > 0:
+            r = d / d.sum()
+        cn = c + N
+        Nn = np.maximum(0.0, p - cn * q).sum()
+        if Nn > 0:
+            c, N = cn, Nn
+        assert np.allclose(np.maximum(0.0, p - c * q) / N, r, rtol=1e-9, atol=1e-12)

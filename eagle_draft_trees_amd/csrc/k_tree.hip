@@ -807,7 +807,7 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
   __shared__ float s_red[RJ_W];
   __shared__ float s_stat[4];  // Mp, Sp, Mq, Sq of the current node
   __shared__ int s_kid[EAGLE_MAX_TREE], s_kok[EAGLE_MAX_TREE];
-  __shared__ float s_kp[EAGLE_MAX_TREE], s_kq[EAGLE_MAX_TREE];
+  __shared__ float s_kp[EAGLE_MAX_TREE], s_kq[EAGLE_MAX_TREE], s_ku[EAGLE_MAX_TREE];
   __shared__ int s_nk, s_pick, s_last;
   __shared__ int path[EAGLE_MAX_DEPTH + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
@@ -816,6 +816,7 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
   const bool inm = wave == 0 && lane < m;
   const int par = inm ? parents[(size_t)b * m + lane] : -2;
   const int tok = inm ? tokens[(size_t)b * m + lane] : -1;
+  const float uk = inm ? ub[lane] : 1.f;  // the lane's node's uniform, used if it is tried
   const bool inr = tok >= 0 && tok < V;
   int node = 0, len = 1;
   if (tid == 0) path[0] = 0;
@@ -848,6 +849,7 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
         const float zp = lp * invT, zq = lq * invT;
         s_kid[slot] = lane;
         s_kok[slot] = inr;
+        s_ku[slot] = uk;
         s_kp[slot] = (inr && zp > -INFINITY) ? expf(zp - MP) / SP : 0.f;
         s_kq[slot] = (inr && zq > -INFINITY) ? expf(zq - MQ) / SQ : 0.f;
       }
@@ -872,7 +874,7 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
       const float pc = s_kp[j], qc = s_kq[j];
       const float dc = pc - c * qc;
       const float rc = (dc > 0.f ? dc : 0.f) / N;
-      if (s_kok[j] && ub[s_kid[j]] * qc <= rc) {
+      if (s_kok[j] && s_ku[j] * qc <= rc) {
         next = s_kid[j];
         break;
       }
@@ -948,17 +950,28 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
   if (w > 0.f) {
     atomicMax(&s_last, tid);
     if (lo <= target && target < hi) {
+      // the chunk again, in the same order and the same sums, eight loads in
+      // flight; acc and lastx stop at the pick
       const float rem = target - lo;
       float acc = 0.f;
       int pick = -1, lastx = -1;
-      for (int x = x0; x < x1; ++x) {
-        const float e = weight(rp[x], useq ? rq[x] : 0.f);
-        if (e > 0.f) lastx = x;
-        if (e > 0.f && rem < acc + e) {
-          pick = x;
-          break;
+      for (int xa = x0; xa < x1 && pick < 0; xa += RJ_U) {
+        float lp[RJ_U], lq[RJ_U];
+#pragma unroll
+        for (int u = 0; u < RJ_U; ++u) {
+          const int x = min(xa + u, V - 1);
+          lp[u] = rp[x];
+          lq[u] = useq ? rq[x] : 0.f;
         }
-        acc += e;
+#pragma unroll
+        for (int u = 0; u < RJ_U; ++u) {
+          if (xa + u < x1 && pick < 0) {
+            const float e = weight(lp[u], lq[u]);
+            if (e > 0.f) lastx = xa + u;
+            if (e > 0.f && rem < acc + e) pick = xa + u;
+            else acc += e;
+          }
+        }
       }
       s_pick = pick >= 0 ? pick : lastx;
     }
@@ -966,8 +979,18 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
   __syncthreads();
   if (s_pick < 0 && tid == s_last) {  // the chunk's scan came out below the target: its last id with mass
     int lastx = -1;
-    for (int x = x0; x < x1; ++x)
-      if (weight(rp[x], useq ? rq[x] : 0.f) > 0.f) lastx = x;
+    for (int xa = x0; xa < x1; xa += RJ_U) {
+      float lp[RJ_U], lq[RJ_U];
+#pragma unroll
+      for (int u = 0; u < RJ_U; ++u) {
+        const int x = min(xa + u, V - 1);
+        lp[u] = rp[x];
+        lq[u] = useq ? rq[x] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < RJ_U; ++u)
+        if (xa + u < x1 && weight(lp[u], lq[u]) > 0.f) lastx = xa + u;
+    }
     s_pick = lastx;
   }
   __syncthreads();

@@ -287,7 +287,7 @@ def rejection_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
         e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * replays)
-    return {"kernel": "k_relaxed_stats x2 + k_verify_rejection", "bound": "latency", "us_per_call": round(us, 2),
+    return {"kernel": "k_relaxed_stats (both arrays) + k_verify_rejection", "bound": "latency", "us_per_call": round(us, 2),
             "accept_len": [int(a) for a in r.accept_len.cpu().numpy()], "temperature": 1.0,
             "draft": "target logits + N(0, 0.3^2)",
             "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}

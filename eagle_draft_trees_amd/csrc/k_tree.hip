@@ -461,15 +461,17 @@ constexpr int RS_U = 8;        // loads in flight per thread
 constexpr int RV_T = 1024;
 constexpr int RV_W = RV_T / WAVE;
 
-__global__ void __launch_bounds__(RS_T) k_relaxed_stats(int V, const float* tl, float temperature,
-                                                        float2* stats) {
+// blockIdx.z picks the array: 0 = (tl, stats), 1 = (tl2, stats2)
+__global__ void __launch_bounds__(RS_T) k_relaxed_stats(int V, const float* tl, float2* stats, const float* tl2,
+                                                        float2* stats2, float temperature) {
 #pragma clang fp contract(off)
   __shared__ float s_m[RS_T / WAVE], s_s[RS_T / WAVE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sg = blockIdx.x, row = blockIdx.y;
   const int SEGV = (V + RS_SEG - 1) / RS_SEG;
   const int a0 = min(V, sg * SEGV), a1 = min(V, a0 + SEGV);
-  const float* r = tl + (size_t)row * V;
+  const float* r = (blockIdx.z == 0 ? tl : tl2) + (size_t)row * V;
+  float2* out = blockIdx.z == 0 ? stats : stats2;
   const float invT = 1.0f / temperature;
   float mx = -INFINITY, sm = 0.f;
   for (int x0 = a0 + tid; x0 < a1; x0 += RS_T * RS_U) {
@@ -503,7 +505,7 @@ __global__ void __launch_bounds__(RS_T) k_relaxed_stats(int V, const float* tl, 
     for (int w = 1; w < RS_T / WAVE; ++w) M = fmaxf(M, s_m[w]);
     float S = 0.f;
     for (int w = 0; w < RS_T / WAVE; ++w) S += s_m[w] == -INFINITY ? 0.f : s_s[w] * expf(s_m[w] - M);
-    stats[(size_t)row * RS_SEG + sg] = make_float2(M, S);
+    out[(size_t)row * RS_SEG + sg] = make_float2(M, S);
   }
 }
 
@@ -747,7 +749,7 @@ hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, co
                                  const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
                                  int32_t* bonus, hipStream_t s) {
   float2* st = (float2*)scratch;
-  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m), dim3(RS_T), 0, s, V, tl, temperature, st);
+  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m, 1), dim3(RS_T), 0, s, V, tl, st, tl, st, temperature);
   hipLaunchKernelGGL(k_verify_relaxed, dim3(B), dim3(RV_T), 0, s, m, D, V, tl, tokens, parents, temperature,
                      threshold, uniforms, (const float2*)st, alen, apath, bonus);
   return hipGetLastError();
@@ -771,8 +773,8 @@ size_t verify_relaxed_scratch_bytes(int B, int m) { return (size_t)B * m * RS_SE
 // max(0, max(0, p - c q)/N - q) = max(0, p - (c + N) q) / N, whose mass is
 // N'/N.  So a rejection costs one pass over the two rows and writes nothing.
 //
-// Three launches.  k_relaxed_stats, once on the target's rows and once on
-// the draft's, reduces every row to per-segment (max, sum) over the chip.
+// Two launches.  k_relaxed_stats (grid z = 2: the target's rows and the
+// draft's) reduces every row to per-segment (max, sum) over the chip.
 // k_verify_rejection (one workgroup per sequence) walks: wave 0 holds the
 // tree (lane = flat slot), combines the node's segment statistics and forms
 // p and q at each child's token with one load per lane; the workgroup tries
@@ -1007,8 +1009,7 @@ hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, 
                                    int32_t* bonus, hipStream_t s) {
   float2* stp = (float2*)scratch;
   float2* stq = stp + (size_t)B * m * RS_SEG;
-  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m), dim3(RS_T), 0, s, V, tl, temperature, stp);
-  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m), dim3(RS_T), 0, s, V, dl, temperature, stq);
+  hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m, 2), dim3(RS_T), 0, s, V, tl, stp, dl, stq, temperature);
   hipLaunchKernelGGL(k_verify_rejection, dim3(B), dim3(RJ_T), 0, s, m, D, V, tl, dl, tokens, parents, temperature,
                      uniforms, (const float2*)stp, (const float2*)stq, alen, apath, bonus);
   return hipGetLastError();

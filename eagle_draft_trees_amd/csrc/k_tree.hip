@@ -822,14 +822,16 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
   const bool inr = tok >= 0 && tok < V;
   int node = 0, len = 1;
   if (tid == 0) path[0] = 0;
-  float Mp = 0.f, Sp = 1.f, Mq = 0.f, Sq = 1.f, c = 0.f, N = 1.f;
+  // p(x) = exp(z - Mp) * (1 / Sp): one reciprocal per node instead of a
+  // division per id in every pass
+  float Mp = 0.f, rSp = 1.f, Mq = 0.f, rSq = 1.f, c = 0.f, N = 1.f;
   auto pv = [&](float l) -> float {
     const float z = l * invT;
-    return z > -INFINITY ? expf(z - Mp) / Sp : 0.f;
+    return z > -INFINITY ? expf(z - Mp) * rSp : 0.f;
   };
   auto qv = [&](float l) -> float {
     const float z = l * invT;
-    return z > -INFINITY ? expf(z - Mq) / Sq : 0.f;
+    return z > -INFINITY ? expf(z - Mq) * rSq : 0.f;
   };
   const float* rp = tl;
   const float* rq = dl;
@@ -852,8 +854,8 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
         s_kid[slot] = lane;
         s_kok[slot] = inr;
         s_ku[slot] = uk;
-        s_kp[slot] = (inr && zp > -INFINITY) ? expf(zp - MP) / SP : 0.f;
-        s_kq[slot] = (inr && zq > -INFINITY) ? expf(zq - MQ) / SQ : 0.f;
+        s_kp[slot] = (inr && zp > -INFINITY) ? expf(zp - MP) * (1.0f / SP) : 0.f;
+        s_kq[slot] = (inr && zq > -INFINITY) ? expf(zq - MQ) * (1.0f / SQ) : 0.f;
       }
       if (lane == 0) {
         s_nk = len <= D ? __popcll(kb) : 0;  // a path of depth+1 nodes is not extended
@@ -865,9 +867,9 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
     }
     __syncthreads();
     Mp = s_stat[0];
-    Sp = s_stat[1];
+    rSp = 1.0f / s_stat[1];
     Mq = s_stat[2];
-    Sq = s_stat[3];
+    rSq = 1.0f / s_stat[3];
     c = 0.f;
     N = 1.f;
     const int nk = s_nk;

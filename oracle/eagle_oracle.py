@@ -41,7 +41,7 @@ What one round computes (readings where the pages are silent are marked R#):
     target's true features and appends the draft KV ([P3] "在 SGLang 里";
     [P2] Core Idea; [P1] §6.2 and §12 item 3).
 
-Readings of what the pages leave open (each also listed in the design doc):
+Readings of what the pages leave open:
   R1  round = level-1 tail + (D-1) forwards + rerank/build + verify + extend.
   R2  shift direction: the feature is paired with the NEXT token's embedding
       ([P1] §4.1, [P3]); [P4]'s "e_{t-1}" is read as garbled.

@@ -9,7 +9,7 @@ the prefix length is restored on the device so every round has the same
 shape, while the root feature and root token advance (the extend writes
 them).
 
-Prints one JSON line (rank 0).  With --gpus N > 1 it exits: this build
+Prints one JSON line (rank 0).  With --gpus N > 1 it exits: the benchmark
 measures one GPU.
 """
 from __future__ import annotations
@@ -344,7 +344,7 @@ def main() -> int:
                     help="only launch the LM-head kernel this many times (counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(the path would shard by sequence with no per-round communication)",
               file=sys.stderr)
         return 2

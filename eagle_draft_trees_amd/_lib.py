@@ -26,10 +26,12 @@ EAGLE_BF16 = 1
 EAGLE_LEVEL_FULL = 0
 EAGLE_LEVEL_TAIL_ONLY = 1
 EAGLE_LEVEL_LMHEAD_ONLY = 2
+EAGLE_LEVEL_FULL_FC = 3
 EAGLE_MAX_DEPTH = 16
 EAGLE_PACKED_WEIGHTS = 0x45505731
 
-WS_ERROR, WS_POOL, WS_FRONTIER, WS_FEAT, WS_TREE_K, WS_TREE_V, WS_EXT_H = range(7)
+(WS_ERROR, WS_POOL, WS_FRONTIER, WS_FEAT, WS_TREE_K, WS_TREE_V, WS_EXT_H, WS_X0, WS_ATTN,
+ WS_Y) = range(10)
 
 
 class EagleError(RuntimeError):
@@ -49,7 +51,8 @@ WEIGHT_NAMES = ("fc_w", "fc_b", "wq", "wk", "wv", "wo", "post_norm", "w_gate", "
 
 
 class EagleWeights(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in WEIGHT_NAMES] + [("packed", c_int32)]
+    _fields_ = ([(n, c_void_p) for n in WEIGHT_NAMES] + [("tok_proj", c_void_p)]
+                + [("packed", c_int32)])
 
 
 class EagleTreeCfg(ctypes.Structure):

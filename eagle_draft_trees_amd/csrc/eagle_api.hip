@@ -36,7 +36,7 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   p.M = M;
   p.nw = 1;
   switch (op) {
-    case OP_FC: p.N = d.d; p.K = 2 * d.d; break;
+    case OP_FC: p.N = d.d; p.K = d.d; break;  // the feature half (the token half is tabulated)
     case OP_QKV: p.N = (d.n_heads + 2 * d.n_kv_heads) * d.head_dim; p.K = d.d; break;
     case OP_O: p.N = d.d; p.K = d.n_heads * d.head_dim; break;
     case OP_GATEUP: p.N = d.ffn; p.K = d.d; p.nw = 2; break;
@@ -100,6 +100,23 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
 
 static inline bool use_skinny(int mode, int rows) {
   return (mode == MODE_LEVEL || mode == MODE_EXTEND) && rows <= 16;
+}
+
+// FC hand-over (levels of at most 16 rows): level L's merge launch computes
+// the FC of level L+1.  Returns false when the configuration keeps the FC in
+// each level's own call.  *fp: the FC plan over the M rows of level L (B at
+// level 1, B*k after), its waves raised to cover the merge's.
+static bool handover_plan(const eagle_dims& d, const eagle_tree_cfg& c, int level, SkPlan* fp) {
+  const int R = c.batch * c.topk;
+  if (R > 16) return false;
+  const int M = level == 1 ? c.batch : R;
+  SkPlan p = plan_skinny(OP_FC, M, d);
+  const int mwaves = level == 1 ? 1 : c.topk;  // merge waves of the launch
+  const int ksw = std::max(p.KSW, cdiv(mwaves, p.CT));
+  if (p.CT * ksw > SK_MAXW) return false;
+  p.KSW = ksw;
+  if (fp) *fp = p;
+  return true;
 }
 
 LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
@@ -246,24 +263,27 @@ static int check_ws(const eagle_dims* d, const eagle_tree_cfg* c, const void* ws
   return EAGLE_OK;
 }
 
-// the nine streamed matrices: rows N, inputs K, q/k/v pair grouping
+// the nine streamed matrices: rows N, inputs K (source rows ld apart), q/k/v
+// pair grouping.  Only the feature half of fc_w (its first d columns) is
+// streamed; its token half enters through the token-projection table.
 struct PackMat {
   const void* eagle_weights::*field;
   const char* name;
-  int N, K, pair_hd;
+  int N, K, ld, pair_hd;
 };
 static void pack_mats(const eagle_dims& d, PackMat (&m)[9]) {
   const int hq = d.n_heads * d.head_dim, hk = d.n_kv_heads * d.head_dim;
-  m[0] = {&eagle_weights::fc_w, "fc_w", d.d, 2 * d.d, 0};
-  m[1] = {&eagle_weights::wq, "wq", hq, d.d, d.head_dim};
-  m[2] = {&eagle_weights::wk, "wk", hk, d.d, d.head_dim};
-  m[3] = {&eagle_weights::wv, "wv", hk, d.d, d.head_dim};
-  m[4] = {&eagle_weights::wo, "wo", d.d, hq, 0};
-  m[5] = {&eagle_weights::w_gate, "w_gate", d.ffn, d.d, 0};
-  m[6] = {&eagle_weights::w_up, "w_up", d.ffn, d.d, 0};
-  m[7] = {&eagle_weights::w_down, "w_down", d.d, d.ffn, 0};
-  m[8] = {&eagle_weights::lm_head, "lm_head", d.vocab, d.d, 0};
+  m[0] = {&eagle_weights::fc_w, "fc_w", d.d, d.d, 2 * d.d, 0};
+  m[1] = {&eagle_weights::wq, "wq", hq, d.d, d.d, d.head_dim};
+  m[2] = {&eagle_weights::wk, "wk", hk, d.d, d.d, d.head_dim};
+  m[3] = {&eagle_weights::wv, "wv", hk, d.d, d.d, d.head_dim};
+  m[4] = {&eagle_weights::wo, "wo", d.d, hq, hq, 0};
+  m[5] = {&eagle_weights::w_gate, "w_gate", d.ffn, d.d, d.d, 0};
+  m[6] = {&eagle_weights::w_up, "w_up", d.ffn, d.d, d.d, 0};
+  m[7] = {&eagle_weights::w_down, "w_down", d.d, d.ffn, d.ffn, 0};
+  m[8] = {&eagle_weights::lm_head, "lm_head", d.vocab, d.d, d.d, 0};
 }
+static size_t tokproj_bytes(const eagle_dims& d) { return (size_t)d.vocab * d.d * 4; }
 static size_t packed_mat_bytes(int N, int K, int es) {
   const int ks = es == 2 ? 32 : 16;
   return (size_t)cdiv(N, 16) * 16 * ((size_t)cdiv(K, ks) * ks) * es;
@@ -276,10 +296,10 @@ static int check_weights(const eagle_weights* w, bool tail_only) {
   if (!w->lm_head) return fail(EAGLE_ERR_ARG, "weight lm_head is NULL");
   if (tail_only) return EAGLE_OK;
   const void* need[] = {w->fc_w, w->fc_b, w->wq, w->wk, w->wv, w->wo, w->post_norm,
-                        w->w_gate, w->w_up, w->w_down, w->embed};
+                        w->w_gate, w->w_up, w->w_down, w->embed, w->tok_proj};
   const char* names[] = {"fc_w", "fc_b", "wq", "wk", "wv", "wo", "post_norm",
-                         "w_gate", "w_up", "w_down", "embed"};
-  for (int i = 0; i < 11; ++i)
+                         "w_gate", "w_up", "w_down", "embed", "tok_proj"};
+  for (int i = 0; i < 12; ++i)
     if (!need[i]) return fail(EAGLE_ERR_ARG, "weight %s is NULL", names[i]);
   return EAGLE_OK;
 }
@@ -301,7 +321,7 @@ static RoundArgs make_args(const eagle_dims& d, const eagle_tree_cfg& c, const e
   if (w) {
     a.fc_w = w->fc_w; a.fc_b = w->fc_b; a.wq = w->wq; a.wk = w->wk; a.wv = w->wv; a.wo = w->wo;
     a.post_norm = w->post_norm; a.w_gate = w->w_gate; a.w_up = w->w_up; a.w_down = w->w_down;
-    a.embed = w->embed; a.lm_head = w->lm_head;
+    a.embed = w->embed; a.lm_head = w->lm_head; a.tok_proj = (const float*)w->tok_proj;
   }
   if (st) {
     a.k_cache = st->k_cache; a.v_cache = st->v_cache; a.prefix_len = st->prefix_len;
@@ -329,10 +349,12 @@ static int hip_ok(hipError_t e, const char* what) {
 }
 
 // draft layer over `rows` rows (frontier or extend): FC, QKV+RoPE+KV, attention,
-// O+residual+norm stats, gate/up+SwiGLU, down+residual
-static int run_layer(RoundArgs a, const eagle_dims& d, const eagle_tree_cfg& c, hipStream_t s) {
+// O+residual+norm stats, gate/up+SwiGLU, down+residual.  skip_fc: x0 is
+// already in the workspace (the previous level's FC hand-over).
+static int run_layer(RoundArgs a, const eagle_dims& d, const eagle_tree_cfg& c, hipStream_t s,
+                     bool skip_fc = false) {
   static const char* names[] = {"fc", "qkv", "o", "gateup", "down"};
-  for (int op = OP_FC; op <= OP_DOWN; ++op) {
+  for (int op = skip_fc ? OP_QKV : OP_FC; op <= OP_DOWN; ++op) {
     if (op == OP_O) {
       const AttnPlan pa = plan_attn(a.mode, a.RS, d, c, a.B);
       int r = hip_ok(launch_attn(a, pa, s), "attention launch");
@@ -382,7 +404,7 @@ size_t eagle_packed_weights_bytes(const eagle_dims* dims) {
   pack_mats(*dims, m);
   size_t total = 0;
   for (const PackMat& x : m) total += align256(packed_mat_bytes(x.N, x.K, (int)elem_size(*dims)));
-  return total;
+  return total + align256(tokproj_bytes(*dims));
 }
 
 int eagle_pack_weights(const eagle_dims* dims, const eagle_weights* src, void* dst, size_t dst_bytes,
@@ -402,16 +424,22 @@ int eagle_pack_weights(const eagle_dims* dims, const eagle_weights* src, void* d
     if ((uintptr_t)p % 16) return fail(EAGLE_ERR_ARG, "weight %s not 16-byte aligned", x.name);
   }
   if (!src->fc_b || !src->post_norm || !src->embed) return fail(EAGLE_ERR_ARG, "fc_b, post_norm or embed is NULL");
+  if ((uintptr_t)src->embed % 16) return fail(EAGLE_ERR_ARG, "embed not 16-byte aligned");
   const int es = (int)elem_size(*dims);
   eagle_weights o = *src;
   size_t off = 0;
   for (const PackMat& x : m) {
     unsigned char* d = (unsigned char*)dst + off;
-    if ((r = hip_ok(launch_pack(src->*(x.field), d, x.N, x.K, es, x.pair_hd, (hipStream_t)stream), "pack")))
+    if ((r = hip_ok(launch_pack(src->*(x.field), d, x.N, x.K, x.ld, es, x.pair_hd, (hipStream_t)stream), "pack")))
       return r;
     o.*(x.field) = d;
     off += align256(packed_mat_bytes(x.N, x.K, es));
   }
+  float* tp = (float*)((unsigned char*)dst + off);
+  if ((r = hip_ok(launch_tokproj(src->embed, src->fc_w, tp, dims->vocab, dims->d, es, (hipStream_t)stream),
+                  "token projection")))
+    return r;
+  o.tok_proj = tp;
   o.packed = EAGLE_PACKED_WEIGHTS;
   *out = o;
   return EAGLE_OK;
@@ -432,12 +460,17 @@ static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eag
   int r;
   if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
     return r;
-  if (flags != EAGLE_LEVEL_FULL && flags != EAGLE_LEVEL_TAIL_ONLY && flags != EAGLE_LEVEL_LMHEAD_ONLY)
+  if (flags != EAGLE_LEVEL_FULL && flags != EAGLE_LEVEL_TAIL_ONLY && flags != EAGLE_LEVEL_LMHEAD_ONLY &&
+      flags != EAGLE_LEVEL_FULL_FC)
     return fail(EAGLE_ERR_ARG, "flags %d", flags);
   if (level < 1 || level > cfg->depth) return fail(EAGLE_ERR_ARG, "level %d (1..%d)", level, cfg->depth);
   const bool lm_only = flags == EAGLE_LEVEL_LMHEAD_ONLY;
-  const bool tail_only = level == 1 || flags != EAGLE_LEVEL_FULL;
-  if ((r = check_weights(w, tail_only)) || (r = check_state(state))) return r;
+  const bool full = flags == EAGLE_LEVEL_FULL || flags == EAGLE_LEVEL_FULL_FC;
+  const bool tail_only = level == 1 || !full;
+  // the merge of this call also forms the next level's FC input (hand-over)
+  SkPlan fp{};
+  const bool handover = level < cfg->depth && handover_plan(*dims, *cfg, level, &fp);
+  if ((r = check_weights(w, tail_only && !handover)) || (r = check_state(state))) return r;
   const hipStream_t s = (hipStream_t)stream;
   RoundArgs a = make_args(*dims, *cfg, w, state, ws);
   a.tmpl = tmpl;
@@ -446,17 +479,20 @@ static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eag
     const LmPlan pl = plan_lm(cfg->batch, *dims, cfg->topk);
     if ((r = hip_ok(launch_lmhead(a, pl, 1, s, e0, e1), "lm head"))) return r;
     if (lm_only) return EAGLE_OK;
-    return hip_ok(launch_lmmerge(a, pl, 1, s), "lm merge");
+    return hip_ok(launch_lmmerge(a, pl, 1, s, handover ? &fp : nullptr), "lm merge");
   }
   a.mode = MODE_LEVEL;
   a.depth = level - 1;
   a.rows = cfg->batch * cfg->topk;
   a.RS = cfg->topk;
-  if (!tail_only && (r = run_layer(a, *dims, *cfg, s))) return r;
+  // x0 of this level was formed by the previous level's hand-over, unless the
+  // caller asks for it here
+  const bool have_x0 = flags == EAGLE_LEVEL_FULL && handover_plan(*dims, *cfg, level - 1, nullptr);
+  if (!tail_only && (r = run_layer(a, *dims, *cfg, s, have_x0))) return r;
   const LmPlan pl = plan_lm(a.rows, *dims, cfg->topk);
   if ((r = hip_ok(launch_lmhead(a, pl, level, s, e0, e1), "lm head"))) return r;
   if (lm_only) return EAGLE_OK;
-  return hip_ok(launch_lmmerge(a, pl, level, s), "lm merge");
+  return hip_ok(launch_lmmerge(a, pl, level, s, handover ? &fp : nullptr), "lm merge");
 }
 
 int eagle_draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,
@@ -644,6 +680,9 @@ int eagle_ws_view(const eagle_dims* dims, const eagle_tree_cfg* cfg, const void*
     case EAGLE_WS_TREE_K: off = L.tk; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
     case EAGLE_WS_TREE_V: off = L.tv; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
     case EAGLE_WS_EXT_H: off = L.ext_h; n = B * ext_rows((int)m, (int)D) * dims->d * es; break;
+    case EAGLE_WS_X0: off = L.x0f; n = (size_t)L.rows_max * dims->d * 4; break;
+    case EAGLE_WS_ATTN: off = L.attn; n = (size_t)L.rows_max * dims->n_heads * dims->head_dim * es; break;
+    case EAGLE_WS_Y: off = L.yf; n = (size_t)L.rows_max * dims->d * 4; break;
     default: return fail(EAGLE_ERR_ARG, "ws_view: region %d", what);
   }
   *ptr = (char*)ws + off;

@@ -26,7 +26,7 @@ constexpr int GW_FIN_THREADS = 1024;        // split-sum workgroup: one (column 
 
 enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
 enum Mode { MODE_LEVEL = 0, MODE_EXTEND = 1, MODE_VERIFY = 2 };  // verify: target-side tree attention
-enum ErrBits { ERR_TOKEN = 1, ERR_PREFIX = 2 };
+enum ErrBits { ERR_TOKEN = 1, ERR_PREFIX = 2, ERR_SYNC = 4 };
 
 // ------------------------------------------------------------------ elements
 
@@ -243,6 +243,7 @@ struct RoundArgs {
   int rows, RS;     // total rows, rows per sequence
   // weights
   const void *fc_w, *fc_b, *wq, *wk, *wv, *wo, *post_norm, *w_gate, *w_up, *w_down, *embed, *lm_head;
+  const float* tok_proj;  // [V][d]: the token half of the FC per vocabulary entry
   // state
   void *k_cache, *v_cache;
   int* prefix_len;
@@ -367,6 +368,22 @@ __device__ __forceinline__ void ext_row_src(const RoundArgs& a, int row, const T
   tok = i < last ? a.tokens[(size_t)b * a.m + clamp_slot(path[i + 1], a.m)] : a.bonus[b];
 }
 
+// Token of FC row `row` (a frontier node's own token at a level; the next
+// path token or the bonus in the extend), clamped into the vocabulary: the
+// row's token half of the FC is tok_proj[token].
+template <typename T>
+__device__ __forceinline__ int fc_row_token(const RoundArgs& a, int row) {
+  int tok;
+  if (a.mode == MODE_LEVEL) {
+    const int b = row / a.k, j = row - b * a.k;
+    tok = a.frontier[((size_t)a.depth * a.B + b) * a.k + j].token;
+  } else {
+    const T* f;
+    ext_row_src<T>(a, row, f, tok);
+  }
+  return clamp_tok(tok, a.V, a.err);
+}
+
 // Extend: the sequence state advances (the prefix grows by the accepted
 // length, the bonus becomes the next root token).  Called by one workgroup
 // of a launch that reads neither field.
@@ -446,7 +463,11 @@ __device__ __forceinline__ float* slab_field(float* lmpart, int row, int blk, co
 }
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
-hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s);
+// handover (may be null): the FC hand-over of the next level rides along in
+// the merge's launch (the FC plan over this level's rows; its CT * KSW waves
+// are the launch's block size)
+hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
+                          const SkPlan* handover = nullptr);
 hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s);
 hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
                          int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);
@@ -466,8 +487,11 @@ size_t verify_rejection_scratch_bytes(int B, int m);
 hipError_t launch_static_build(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
                                int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
-// one matrix W [N][K] (row-major) into the packed tile layout; pair_hd > 0:
-// q/k/v row grouping of rotation pairs for head_dim pair_hd
-hipError_t launch_pack(const void* src, void* dst, int N, int K, int es, int pair_hd, hipStream_t s);
+// one matrix W [N][K] (row-major, rows ld elements apart) into the packed
+// tile layout; pair_hd > 0: q/k/v row grouping of rotation pairs for head_dim pair_hd
+hipError_t launch_pack(const void* src, void* dst, int N, int K, int ld, int es, int pair_hd, hipStream_t s);
+// token-projection table: tp[v][n] = sum_k embed[v][k] * fc_w[n][d + k] (fp32),
+// from the row-major embed [V][d] and fc_w [d][2d]
+hipError_t launch_tokproj(const void* embed, const void* fc_w, float* tp, int V, int d, int es, hipStream_t s);
 
 }  // namespace eg

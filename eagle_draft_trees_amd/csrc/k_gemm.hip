@@ -18,8 +18,9 @@
 //
 // Fused steps (draft head of [P1] "EAGLE 推测解码为什么比 Medusa 快？" §4.1 and
 // [P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里"):
-//   FC      X = [parent feature || embed[token]] gathered on the fly (no
-//           concatenated copy); epilogue + bias -> x0 (fp32 residual, dtype copy)
+//   FC      X = the parent (level) or true (extend) feature, gathered on the
+//           fly, against the feature half of W_fc; epilogue + the row token's
+//           token-projection entry + bias -> x0 (fp32 residual, dtype copy)
 //   QKV     epilogue applies RoPE at the row's tree position to q and k
 //           ([P1] §12 item 5: positions shared per level) and writes k, v
 //           straight into the in-tree slot (levels) or the prefix cache (extend)
@@ -81,11 +82,14 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
   static_assert(OP != OP_O || CTW == 4, "the O launch keeps 64-column blocks");
 #define TILE(w, r, c) tile[((w) * ROWS + (r)) * 65 + (c)]
   const int rows_here = min(ROWS, p.M - zg * 64);
-  if (OP == OP_FC) {
+  if (OP == OP_FC) {  // + the token half: the row's token-projection table entry
+    __shared__ int s_tok[ROWS];
+    if (tid < rows_here) s_tok[tid] = fc_row_token<T>(a, zg * 64 + tid);
+    __syncthreads();
     for (int idx = tid; idx < rows_here * BW; idx += (int)blockDim.x) {
       const int mr = idx / BW, c = idx % BW, nn = blk * BW + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
-      const float v = TILE(0, mr, c) + El<T>::ld((const T*)a.fc_b, nn);
+      const float v = TILE(0, mr, c) + a.tok_proj[(size_t)s_tok[mr] * a.d + nn] + El<T>::ld((const T*)a.fc_b, nn);
       a.x0f[(size_t)row * a.d + nn] = v;
       El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
     }
@@ -198,7 +202,7 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
   // two X chunks [ROWS][KC] (double buffer); then the K-slice partials; then
   // the output tile
   extern __shared__ __attribute__((aligned(16))) unsigned char xs[];
-  __shared__ const T* rsrc[2][ROWS];  // FC: the two sources of each row
+  __shared__ const T* rsrc[ROWS];  // FC: the source row of each row
   __shared__ float s_rstd[ROWS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -233,28 +237,24 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
   if (OP == OP_DOWN && a.mode == MODE_EXTEND && blk == 0 && split == 0 && zg == 0)
     ext_advance_state(a, tid, THREADS);
 
-  // ---- FC rows: [parent feature || embed[token]] gathered on the fly; rows
-  // past M take row 0's sources
+  // ---- FC rows: the parent (level) or true (extend) feature, gathered on the
+  // fly; rows past M take row 0's source
   if (OP == OP_FC && tid < ROWS) {
     const int row0 = zg * 64 + tid;
     const bool ok = row0 < p.M;
     const int row = ok ? row0 : zg * 64;  // row 0 of the group always exists
     const T* s0;
-    int tok;
     if (a.mode == MODE_LEVEL) {
       const int b = row / a.k, j = row % a.k;
       const eagle_frontier_node& nd = a.frontier[((size_t)a.depth * a.B + b) * a.k + j];
-      tok = nd.token;
       if (a.depth == 1) s0 = (const T*)a.root_feat + (size_t)b * a.d;
       else s0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
     } else {
+      int tok;
       ext_row_src<T>(a, row, s0, tok);
     }
-    tok = clamp_tok(tok, a.V, a.err);
-    rsrc[0][tid] = s0;
-    rsrc[1][tid] = (const T*)a.embed + (size_t)tok * a.d;  // read with k - d
+    rsrc[tid] = s0;
   }
-  const int kswitch = (OP == OP_FC) ? a.d : K;
   const int k0 = split * p.Kc;
   const int kn = min(K, k0 + p.Kc) - k0;  // this split's K range [k0, k0 + kn)
   const int nb = (kn + KC - 1) / KC;      // its chunks
@@ -307,8 +307,7 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
       const int k = min(k0 + b * KC + pc * PER, klast);
       const T* src;
       if (OP == OP_FC) {
-        const bool lo = k < kswitch;
-        src = rsrc[lo ? 0 : 1][r] + (lo ? k : k - kswitch);  // one LDS read, index selected
+        src = rsrc[r] + k;
       } else if (OP == OP_DOWN) {
         const int row = zg * 64 + r;
         src = (const T*)a.act + xpk_index<T>(row < ((p.M + 15) & ~15) ? row : zg * 64 + (r & 15), k, nks);

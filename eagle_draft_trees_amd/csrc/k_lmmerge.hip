@@ -21,7 +21,7 @@
 
 #include <algorithm>
 
-#include "eagle_internal.h"
+#include "skinny_core.h"
 
 namespace eg {
 
@@ -35,9 +35,24 @@ namespace eg {
 // in LDS (long vocabularies).
 constexpr int MG_LDS = 64 * 1024;  // slab head keys of the rows in flight (NH == 0)
 
+// Publication of a merge workgroup's results to the FC hand-over workgroups of
+// the same launch: wave 0 alone wrote the pool and frontier records they
+// read; its stores complete, one release at agent scope (the hand-over
+// workgroups may sit on other XCDs, whose L2s are not coherent with this
+// one), then the count of published sequences goes up.
+__device__ __forceinline__ void publish_merge(int* ready) {
+  __builtin_amdgcn_s_waitcnt(0);
+  if ((threadIdx.x & 63) == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// mwv: waves that take rows (the block may hold more, which only pass the
+// barriers); pub: publish for FC hand-over workgroups when done
 template <int NH>
-__global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan p, int level) {
-  extern __shared__ unsigned long long hk[];                  // NH == 0: [waves][nblk] slab head keys
+__device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, int level, int b, int mwv,
+                                           unsigned long long* hk, bool pub) {
   __shared__ float sres[EAGLE_MAX_TOPK * 2 * EAGLE_MAX_TOPK];  // per row: k id bits, k log p
   __shared__ int sanc[EAGLE_MAX_TOPK * EAGLE_MAX_DEPTH];
   __shared__ float psc[EAGLE_MAX_TOPK];
@@ -46,8 +61,8 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwv = (int)(blockDim.x >> 6);
-  const int b = blockIdx.x, kk_ = a.k, nblk = p.nblk, rec = p.rec;
+  const int nwv = mwv;
+  const int kk_ = a.k, nblk = p.nblk, rec = p.rec;
   const int swidth = p.sk ? p.CT * 16 : 64;  // vocabulary columns per slab
   const int rows = level == 1 ? 1 : kk_;
   const int row0 = level == 1 ? b : b * kk_;
@@ -71,7 +86,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
   }
 
   unsigned long long* hkw = hk + (size_t)wave * nblk;
-  for (int r = wave; r < rows; r += nwv) {
+  for (int r = wave; r < rows && wave < nwv; r += nwv) {
     const int row = row0 + r;
     const float* base = a.lmpart + (size_t)row * nblk * rec;
     // log-sum-exp over the slabs and the slab head keys; NL slabs per lane are
@@ -181,7 +196,10 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
       fnew[lane] = nd;
     }
   }
-  if (level == 1) return;
+  if (level == 1) {  // one row per sequence: wave 0 wrote its pool and frontier
+    if (pub && wave == 0) publish_merge(a.cnt);
+    return;
+  }
 
   // ---- expansion and select (levels >= 2): wave 0 scores the k*k children
   // (parent score + log p), appends all of them to the pool in (frontier
@@ -262,22 +280,150 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan 
       fnew[jn].anc[i] = i < level - 1 ? sanc[j * EAGLE_MAX_DEPTH + i] : (i == level - 1 ? jn : 0);
     }
   }
+  if (pub) publish_merge(a.cnt);
 }
 
-hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s) {
+// FC hand-over ([P1] §4.1 input equation: the next level's row is [feature of
+// the parent || embedding of the node's token]).  While the merge workgroups
+// of the launch pick the next frontier (latency-bound: one workgroup per
+// sequence), these workgroups stream the feature half of W_fc over all of this
+// level's rows -- every one of them can be a parent -- and keep the products
+// on chip.  Once every merge has published, each forms the next rows' x0 =
+// W_fc[:, :d] h(parent) + tok_proj[token] + fc_b for its columns, so the next
+// level starts at q/k/v.  The wait is bounded: a workgroup that gives up
+// flags ERR_SYNC and proceeds (it never hangs).  The merge workgroups have
+// the lowest block indices, so they are dispatched before any of these.
+constexpr int HANDOVER_SPINS = 1 << 17;
+template <typename T>
+__device__ __forceinline__ void fc_handover(const RoundArgs& a, const SkPlan& fp, int level, int nseq, int wg,
+                                            unsigned char* dyn) {
+  constexpr int KS = El<T>::KSTEP;
+  constexpr int BU = 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwv = (int)(blockDim.x >> 6);  // == fp.CT * fp.KSW
+  const int ct = wave % fp.CT, ks = wave / fp.CT;
+  const int t = wg * fp.CT + ct;
+  const int c = lane & 15, g = lane >> 4;
+  const int K = a.d, nks = (K + KS - 1) / KS;
+  const T* const wr[1] = {wtile_base<T>(a.fc_w, nks, t < fp.ntile ? t : 0, lane)};
+  // this level's rows: the root features (level 1) or the level's features
+  const T* xs = level == 1 ? (const T*)a.root_feat : (const T*)a.feat + (size_t)(level - 1) * a.B * a.k * K;
+  const T* x0 = xs + (size_t)(c < fp.M ? c : 0) * K;  // rows past M repeat row 0 (unused)
+  const int s0k = (int)((long)ks * nks / fp.KSW), s1k = (int)((long)(ks + 1) * nks / fp.KSW);
+  const int nbu = ((nks + fp.KSW - 1) / fp.KSW + BU - 1) / BU;
+  f32x4_t acc[1];
+  sk_stream<T, 1, BU, false>(wr, x0, x0, K, K, s0k, s1k, nbu, dyn, acc);
+
+  // K slices meet in LDS; the products [tile][row][column] stay there
+  f32x4_t* red = (f32x4_t*)dyn;
+  float* fs = (float*)(dyn + (size_t)nwv * WAVE * sizeof(f32x4_t));
+  red[wave * WAVE + lane] = acc[0];
+  __syncthreads();
+  if (ks == 0) {
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < fp.KSW; ++s) v += red[(s * fp.CT + ct) * WAVE + lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fs[(ct * 16 + 4 * g + r) * 16 + c] = v[r];
+  }
+
+  // wait until every merge of the launch has published the next frontier
+  __shared__ int s_tok[16], s_prow[16];
+  if (tid == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(a.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nseq) {
+      if (++spins > HANDOVER_SPINS) {
+        atomicOr(a.err, ERR_SYNC);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  const int R = a.B * a.k;  // the next level's rows (at most 16)
+  if (tid < R) {
+    const int b = tid / a.k, jn = tid - b * a.k;
+    eagle_frontier_node* nd = a.frontier + ((size_t)level * a.B + b) * a.k + jn;
+    const int tok = __hip_atomic_load(&nd->token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int ps = __hip_atomic_load(&nd->pslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_tok[tid] = clamp_tok(tok, a.V, a.err);
+    s_prow[tid] = level == 1 ? b : b * a.k + clamp_slot(ps, a.k);
+  }
+  __syncthreads();
+  // every hand-over workgroup has passed its wait once `seen` counts them all:
+  // the last one leaves both counters at zero for the next launch
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(a.cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == fp.nwg - 1) {
+      __hip_atomic_store(a.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const int W = fp.CT * 16;
+  for (int idx = tid; idx < R * W; idx += (int)blockDim.x) {
+    const int row = idx / W, cc = idx - row * W, tl = cc >> 4, col = cc & 15;
+    const int n = (wg * fp.CT + tl) * 16 + col;
+    if (n >= a.d) continue;
+    const float x = fs[(tl * 16 + s_prow[row]) * 16 + col] + a.tok_proj[(size_t)s_tok[row] * a.d + n] +
+                    El<T>::ld((const T*)a.fc_b, n);
+    a.x0f[(size_t)row * a.d + n] = x;
+    El<T>::st((T*)a.x0b, (size_t)row * a.d + n, x);
+  }
+}
+
+// merge workgroups (blocks 0..nseq-1) and, with FUSE, the FC hand-over
+// workgroups of the next level after them
+template <int NH, typename T, bool FUSE>
+__global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmmerge(RoundArgs a, LmPlan p, SkPlan fp, int level, int nseq,
+                                                           int mwv) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  const int blk = blockIdx.x;
+  if (!FUSE || blk < nseq) {
+    merge_body<NH>(a, p, level, blk, mwv, (unsigned long long*)dyn, FUSE);
+    return;
+  }
+  fc_handover<T>(a, fp, level, nseq, blk - nseq, dyn);
+}
+
+// The merge's launch.  fp.nwg > 0: the FC hand-over of the next level rides
+// along (fp is the FC plan over this level's rows with CT * KSW waves, the
+// block size of the launch).
+template <int NH, typename T>
+static void launch_merge_t(const RoundArgs& a, const LmPlan& p, const SkPlan& fp, int level, int nseq, int mwv,
+                           size_t lds, hipStream_t s) {
+  const int rows = level == 1 ? 1 : a.k;
+  if (fp.nwg > 0) {
+    const int nwv = fp.CT * fp.KSW;
+    const size_t fl = (size_t)nwv * WAVE * sizeof(f32x4_t) + (size_t)fp.CT * 256 * sizeof(float);
+    hipLaunchKernelGGL((k_lmmerge<NH, T, true>), dim3(nseq + fp.nwg), dim3(nwv * WAVE), lds > fl ? lds : fl, s, a,
+                       p, fp, level, nseq, NH == 0 ? mwv : nwv);
+  } else {
+    const int nwv = NH == 0 ? mwv : rows;
+    hipLaunchKernelGGL((k_lmmerge<NH, T, false>), dim3(nseq), dim3(nwv * WAVE), lds, s, a, p, fp, level, nseq, nwv);
+  }
+}
+
+template <typename T>
+static hipError_t launch_merge_dt(const RoundArgs& a, const LmPlan& p, const SkPlan& fp, int level, hipStream_t s) {
   const int rows = level == 1 ? 1 : a.k;
   const int nseq = level == 1 ? p.M : p.M / a.k;
   if (p.nblk <= 4 * WAVE) {
-    hipLaunchKernelGGL(k_lmmerge<4>, dim3(nseq), dim3(rows * WAVE), 0, s, a, p, level);
+    launch_merge_t<4, T>(a, p, fp, level, nseq, rows, 0, s);
   } else if (p.nblk <= 8 * WAVE) {
-    hipLaunchKernelGGL(k_lmmerge<8>, dim3(nseq), dim3(rows * WAVE), 0, s, a, p, level);
+    launch_merge_t<8, T>(a, p, fp, level, nseq, rows, 0, s);
   } else {
     const int fit = MG_LDS / (p.nblk * (int)sizeof(unsigned long long));
     const int nwv = std::max(1, std::min(rows, fit));
-    hipLaunchKernelGGL(k_lmmerge<0>, dim3(nseq), dim3(nwv * WAVE), (size_t)nwv * p.nblk * sizeof(unsigned long long),
-                       s, a, p, level);
+    launch_merge_t<0, T>(a, p, fp, level, nseq, nwv, (size_t)nwv * p.nblk * sizeof(unsigned long long), s);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, const SkPlan* handover) {
+  SkPlan none{};
+  const SkPlan& fp = handover ? *handover : none;
+  return a.dtype == EAGLE_BF16 ? launch_merge_dt<bf16_t>(a, p, fp, level, s) : launch_merge_dt<float>(a, p, fp, level, s);
 }
 
 }  // namespace eg

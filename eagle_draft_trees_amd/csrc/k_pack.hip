@@ -4,7 +4,8 @@
 // contiguous kilobyte.  q/k/v matrices group their rows by RoPE pairs (tile j
 // of a head: rows 8j..8j+7 and hd/2+8j..hd/2+8j+7) so that the rotation in
 // the QKV epilogues pairs columns within a lane's tile.  Rows and K past the
-// matrix are zero.
+// matrix are zero.  The source rows are `ld` elements apart (ld >= K: the
+// FC's feature half is the first d columns of the [d][2d] fc_w).
 #include <algorithm>
 
 #include "eagle_internal.h"
@@ -13,7 +14,7 @@ namespace eg {
 
 template <int ES>
 __global__ void __launch_bounds__(256) k_pack(const unsigned char* src, unsigned char* dst, int N, int K,
-                                              int pair_hd, long total) {
+                                              int ld, int pair_hd, long total) {
   constexpr int KS = ES == 2 ? 32 : 16, PER = 16 / ES;
   const int nks = (K + KS - 1) / KS;
   for (long p = (long)blockIdx.x * blockDim.x + threadIdx.x; p < total; p += (long)gridDim.x * blockDim.x) {
@@ -29,21 +30,21 @@ __global__ void __launch_bounds__(256) k_pack(const unsigned char* src, unsigned
     }
     const int k = s * KS + g * PER;  // K is a multiple of 8: a piece is wholly in or out
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r < N && k < K) v = *(const uint4*)(src + ((size_t)r * K + k) * ES);
+    if (r < N && k < K) v = *(const uint4*)(src + ((size_t)r * ld + k) * ES);
     *(uint4*)(dst + (size_t)p * 16) = v;
   }
 }
 
-hipError_t launch_pack(const void* src, void* dst, int N, int K, int es, int pair_hd, hipStream_t s) {
+hipError_t launch_pack(const void* src, void* dst, int N, int K, int ld, int es, int pair_hd, hipStream_t s) {
   const int ks = es == 2 ? 32 : 16;
   const long total = (long)((N + 15) / 16) * ((K + ks - 1) / ks) * 64;
   const int blocks = (int)std::min<long>((total + 255) / 256, 8192);
   if (es == 2)
     hipLaunchKernelGGL(k_pack<2>, dim3(blocks), dim3(256), 0, s, (const unsigned char*)src, (unsigned char*)dst, N, K,
-                       pair_hd, total);
+                       ld, pair_hd, total);
   else
     hipLaunchKernelGGL(k_pack<4>, dim3(blocks), dim3(256), 0, s, (const unsigned char*)src, (unsigned char*)dst, N, K,
-                       pair_hd, total);
+                       ld, pair_hd, total);
   return hipGetLastError();
 }
 

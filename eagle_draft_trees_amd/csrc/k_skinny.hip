@@ -83,11 +83,14 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   }
 
   // ---- this lane's X row: row c (rows past M repeat row 0; discarded).  The
-  // FC gathers [parent feature || embed[token]] without a concatenated copy.
+  // FC streams the feature half of W_fc over the gathered parent (level) or
+  // true (extend) feature; the token half is the row's token-projection
+  // table entry, added in the epilogue.
   const int xr = c < p.M ? c : 0;
   const T* x0;
   const T* x1;
-  int kswitch = K;
+  const int kswitch = K;
+  __shared__ int s_tok[16];
   if (OP == OP_FC) {
     int tok;
     if (a.mode == MODE_LEVEL) {
@@ -96,11 +99,11 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
       tok = nd.token;
       if (a.depth == 1) x0 = (const T*)a.root_feat + (size_t)b * a.d;
       else x0 = (const T*)a.feat + (((size_t)(a.depth - 1) * a.B + b) * a.k + clamp_slot(nd.pslot, a.k)) * a.d;
-    } else {  // extend: [true feature of the path node || embedding of the next token]
+    } else {  // extend: the true feature of the path node and the next token
       ext_row_src<T>(a, xr, x0, tok);
     }
-    x1 = (const T*)a.embed + (size_t)clamp_tok(tok, a.V, a.err) * a.d;
-    kswitch = a.d;
+    x1 = x0;
+    if (tid < 16) s_tok[tid] = clamp_tok(tok, a.V, a.err);  // wave 0, lane = row c
   } else if (OP == OP_DOWN) {  // packed activations: this lane's piece of k-step 0 (row c;
     // rows past M read row 0, so the block's padding lines are never fetched)
     x0 = (const T*)a.act + (size_t)xr * KS + g * El<T>::PER16;
@@ -161,7 +164,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
         if (row >= p.M) continue;
-        const float x = v[0][r] + bias;
+        const float x = v[0][r] + a.tok_proj[(size_t)s_tok[row] * a.d + n] + bias;
         a.x0f[(size_t)row * a.d + n] = x;
         El<T>::st((T*)a.x0b, (size_t)row * a.d + n, x);
       }

@@ -90,13 +90,15 @@ typedef struct {
  *   fc_b [d];  wq [H*hd][d];  wk, wv [Hkv*hd][d];  wo [d][H*hd];
  *   post_norm [d] (RMSNorm gain);  w_gate, w_up [ffn][d];  w_down [d][ffn];
  *   embed [vocab][d] and lm_head [vocab][d]: the target's, shared and frozen.
- * The drafting calls stream the nine matrices fc_w, wq, wk, wv, wo, w_gate,
- * w_up, w_down and lm_head once per pass and take them in the packed layout
+ * The drafting calls stream wq, wk, wv, wo, w_gate, w_up, w_down, lm_head and
+ * the feature half of fc_w once per pass and take them in the packed layout
  * that eagle_pack_weights writes (packed == EAGLE_PACKED_WEIGHTS); fc_b,
- * post_norm and embed stay row-major.  `packed` is 0 for row-major sources. */
+ * post_norm and embed stay row-major.  `packed` is 0 for row-major sources,
+ * whose tok_proj is ignored. */
 typedef struct {
     const void *fc_w, *fc_b, *wq, *wk, *wv, *wo, *post_norm, *w_gate, *w_up, *w_down;
     const void *embed, *lm_head;
+    const void *tok_proj;        /* packed only: fp32 [vocab][d], see eagle_pack_weights */
     int32_t packed;
 } eagle_weights;
 
@@ -154,13 +156,22 @@ typedef struct {
  * are padded with zeros to whole tiles.  wq, wk, wv tiles hold 8 RoPE pairs of
  * one head: tile j of a head holds its rows 8j..8j+7 and hd/2+8j..hd/2+8j+7,
  * so that the rotation stays within a lane's columns; every other matrix's
- * tile t holds rows 16t..16t+15.
- * eagle_packed_weights_bytes: bytes of the packed buffer (each matrix at a
- * 256-byte-aligned offset); 0 if dims are invalid.
+ * tile t holds rows 16t..16t+15.  Only the feature half of fc_w (its columns
+ * 0..d-1, as a [d][d] matrix) is packed.  The token half enters through the
+ * token-projection table tok_proj [vocab][d] fp32, tok_proj[v] = fc_w[:, d:2d]
+ * * embed[v] (fp32 sums of the exact products), written here: the FC of a
+ * row [f || e(t)] is W_fc[:, :d] f + tok_proj[t] + fc_b ([P1] §4.1 input
+ * equation; the product of a matrix with a concatenation is the sum of its
+ * column blocks' products), so the drafting calls read one table row per row
+ * instead of streaming the token half of fc_w.
+ * eagle_packed_weights_bytes: bytes of the packed buffer (each matrix and
+ * the table at a 256-byte-aligned offset); 0 if dims are invalid.
  * eagle_pack_weights: src holds the row-major matrices (src->packed == 0);
  * dst is device memory of at least that many bytes, 256-byte aligned, owned
  * by the caller and left untouched by the drafting calls.  Fills *out with
  * pointers into dst (and src's fc_b, post_norm, embed) and sets out->packed.
+ * src's matrices are read by kernels on `stream`: keep them until that work
+ * is done.
  * Returns EAGLE_ERR_ARG on NULL pointers or a misaligned dst,
  * EAGLE_ERR_WORKSPACE if dst_bytes is too small; launches on `stream`. */
 size_t eagle_packed_weights_bytes(const eagle_dims *dims);
@@ -185,6 +196,8 @@ int eagle_workspace_init(const eagle_dims *dims, const eagle_tree_cfg *cfg, void
                                      frontier are NOT updated, so a level run this way
                                      must be run again with FULL or TAIL_ONLY before
                                      the round continues */
+#define EAGLE_LEVEL_FULL_FC 3     /* level >= 2: FULL, and compute this level's FC input
+                                     x0 in this call (see "FC hand-over" below) */
 
 /* One tree level ([P1] §10.3 expansion; [P3] select_top_k_tokens).
  * level 1: LM head + softmax + top-k on root_feat; the k children of each
@@ -202,7 +215,15 @@ int eagle_workspace_init(const eagle_dims *dims, const eagle_tree_cfg *cfg, void
  *   pool in (frontier slot, rank) order, and the best k by (score desc, pool
  *   index asc) form frontier depth L.
  * Levels must run 1, 2, ..., depth in order within a round.  w: packed
- * weights (eagle_pack_weights; EAGLE_ERR_ARG otherwise). */
+ * weights (eagle_pack_weights; EAGLE_ERR_ARG otherwise).
+ * FC hand-over: when batch * topk <= 16, the FC input of level L+1 (x0 of the
+ * next frontier) is computed by level L's call (FULL or TAIL_ONLY, L < depth):
+ * its LM-head merge launch also streams the feature half of the FC over level
+ * L's rows, and once the next frontier is chosen forms x0 = W_fc[:, :d] h(parent)
+ * + tok_proj[token] + fc_b.  Level L+1 (FULL) then starts at q/k/v.  A caller
+ * that writes the frontier or the features of the parents into the workspace
+ * itself runs level L+1 with EAGLE_LEVEL_FULL_FC, which computes x0 in that
+ * call.  With batch * topk > 16 every FULL level computes its own FC. */
 int eagle_draft_level(const eagle_dims *dims, const eagle_weights *w,
                       const eagle_tree_cfg *cfg, const eagle_seq_state *state,
                       int32_t level, int32_t flags, void *ws, size_t ws_bytes,
@@ -370,13 +391,20 @@ const char *eagle_last_error(void);   /* thread-local text of the last failure *
 
 /* Workspace regions, for tests and debugging. */
 typedef enum {
-    EAGLE_WS_ERROR = 0,     /* int32[4]; [0] bit 0: token id clamped, bit 1: prefix_len clamped */
+    EAGLE_WS_ERROR = 0,     /* int32[4]; [0] bit 0: token id clamped, bit 1: prefix_len clamped,
+                               bit 2: a bounded wait of the FC hand-over gave up (never
+                               expected; the next level's input is then not valid) */
     EAGLE_WS_POOL = 1,      /* eagle_pool_entry [batch][pool]                        */
     EAGLE_WS_FRONTIER = 2,  /* eagle_frontier_node [depth+1][batch][topk] (by depth)  */
     EAGLE_WS_FEAT = 3,      /* dtype [depth][batch][topk][d]: features of frontier nodes */
     EAGLE_WS_TREE_K = 4,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree keys (post-RoPE) */
     EAGLE_WS_TREE_V = 5,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree values    */
-    EAGLE_WS_EXT_H = 6      /* dtype [batch][min(m, depth+1)][d]: extend output features */
+    EAGLE_WS_EXT_H = 6,     /* dtype [batch][min(m, depth+1)][d]: extend output features */
+    /* the last layer pass's intermediates (a level's or the extend's rows, R of them:
+       batch*topk, batch*min(m, depth+1) or batch), row-major over the first R rows */
+    EAGLE_WS_X0 = 7,        /* fp32 [R][d]: FC output x0 (after the bias)            */
+    EAGLE_WS_ATTN = 8,      /* dtype [R][n_heads*head_dim]: attention output          */
+    EAGLE_WS_Y = 9          /* fp32 [R][d]: x0 + o-projection (the post-attention stream) */
 } eagle_ws_region;
 
 int eagle_ws_view(const eagle_dims *dims, const eagle_tree_cfg *cfg, const void *ws,

@@ -266,12 +266,16 @@ def draft_rows(model: Model, feats: np.ndarray, tokens: Sequence[int],
     return x0, q, k, v
 
 
-def finish_rows(model: Model, x0: np.ndarray, attn: np.ndarray) -> np.ndarray:
+def finish_rows(model: Model, x0: np.ndarray, attn: np.ndarray,
+                parts: Optional[dict] = None) -> np.ndarray:
     """Rest of the Llama decoder layer: output projection with the residual
     on x0, post-attention RMSNorm, SwiGLU MLP with its residual.  No final
-    norm ([P3]).  Returns the predicted feature rows [R, d]."""
+    norm ([P3]).  Returns the predicted feature rows [R, d]; ``parts`` (if
+    given) receives the post-attention stream y."""
     c = model.cfg
     y = x0 + model.linear("wo", attn)
+    if parts is not None:
+        parts["y"] = y
     z = rms_norm(y, model.w("post_norm"), c.rms_eps)
     a = silu(model.linear("w_gate", z)) * model.linear("w_up", z)
     return y + model.linear("w_down", a)
@@ -336,11 +340,13 @@ def _visible_kv(st: SeqState, intree: Dict[Tuple[int, int], Tuple[np.ndarray, np
 def level_step_forward(model: Model, st: SeqState, level: int,
                        frontier: List[FrontierNode],
                        feats: Dict[Tuple[int, int], np.ndarray],
-                       intree: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]]):
+                       intree: Dict[Tuple[int, int], Tuple[np.ndarray, np.ndarray]],
+                       parts: Optional[dict] = None):
     """Draft forward of level ``level`` >= 2 over the frontier of depth
     level-1.  Node x's row pairs its parent's draft feature with x's own
     token and sits at position P-1+depth(x) (R8).  Writes in-tree K/V for
-    slot (level-1, j) and the predicted features feats[(level-1, j)]."""
+    slot (level-1, j) and the predicted features feats[(level-1, j)].
+    ``parts`` (if given) receives the rows' intermediates x0, attn and y."""
     c = model.cfg
     depth = level - 1
     pf = np.stack([st.root_feat if depth == 1 else feats[(depth - 1, x.pslot)]
@@ -352,7 +358,9 @@ def level_step_forward(model: Model, st: SeqState, level: int,
         intree[(depth, j)] = (kn[j], vn[j])
     attn = np.stack([attend_row(q[j], *_visible_kv(st, intree, x))
                      for j, x in enumerate(frontier)])
-    h = finish_rows(model, x0, attn)
+    if parts is not None:
+        parts["x0"], parts["attn"] = x0, attn
+    h = finish_rows(model, x0, attn, parts)
     for j in range(len(frontier)):
         feats[(depth, j)] = h[j]
     return h

@@ -86,9 +86,15 @@ class OracleSeqs:
             self.pool[b], self.F[b] = pool, [F]
             self.tail_margin[b] += mg["tail"]
 
-    def forward(self, level: int) -> Dict[int, np.ndarray]:
+    def forward(self, level: int, parts: Optional[Dict[int, dict]] = None) -> Dict[int, np.ndarray]:
+        """Level forward of every sequence; ``parts[b]`` (if given) receives the
+        rows' intermediates (x0, attn, y)."""
+        if parts is not None:
+            for b in self.seqs:
+                parts[b] = {}
         return {b: O.level_step_forward(self.model, self.st[b], level, self.F[b][-1],
-                                        self.feats[b], self.intree[b]) for b in self.seqs}
+                                        self.feats[b], self.intree[b],
+                                        None if parts is None else parts[b]) for b in self.seqs}
 
     def tail(self, level: int, h: Dict[int, np.ndarray]):
         for b in self.seqs:
@@ -182,6 +188,23 @@ def gpu_feats(r, depth: int) -> np.ndarray:
     cfg = r.cfg
     t = r.ws_typed(L.WS_FEAT).view(cfg.D, cfg.B, cfg.k, cfg.d)[depth]
     return to_host(t)
+
+
+def gpu_rows(r, what: int, width: int) -> np.ndarray:
+    """The first rows of a row-major intermediate region (EAGLE_WS_X0 / Y are
+    fp32, EAGLE_WS_ATTN the config dtype) as fp64 [rows][width]."""
+    from eagle_draft_trees_amd import _lib as L
+    import torch
+    t = r.ws_region(what)
+    t = t.view(torch.float32) if what in (L.WS_X0, L.WS_Y) else t.view(
+        torch.bfloat16 if r.cfg.dtype == "bf16" else torch.float32)
+    return to_host(t).reshape(-1, width)
+
+
+def handover(cfg) -> bool:
+    """True when a level's merge launch forms the next level's FC input (at most
+    16 rows per level)."""
+    return cfg.B * cfg.k <= 16
 
 
 def gpu_tree_kv(r):

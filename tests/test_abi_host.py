@@ -123,7 +123,7 @@ def test_ws_view_regions_are_inside_the_workspace():
     n = L.eagle_workspace_bytes(dims, tc)
     base = 1 << 40
     spans = []
-    for what in range(7):
+    for what in range(10):
         p, sz = ctypes.c_void_p(), ctypes.c_size_t()
         assert L.lib().eagle_ws_view(ctypes.byref(dims), ctypes.byref(tc), base, what,
                                      ctypes.byref(p), ctypes.byref(sz)) == 0
@@ -138,8 +138,10 @@ def test_ws_view_regions_are_inside_the_workspace():
 def _packed_bytes_formula(d, H, Hkv, hd, F, V, es):
     ks = 32 if es == 2 else 16
     cd = lambda a, b: -(-a // b)
-    mats = [(d, 2 * d), (H * hd, d), (Hkv * hd, d), (Hkv * hd, d), (d, H * hd), (F, d), (F, d), (d, F), (V, d)]
-    return sum(cd(cd(n, 16) * 16 * cd(k, ks) * ks * es, 256) * 256 for n, k in mats)
+    # the FC's feature half [d][d] is packed; its token half is the fp32 table [V][d]
+    mats = [(d, d), (H * hd, d), (Hkv * hd, d), (Hkv * hd, d), (d, H * hd), (F, d), (F, d), (d, F), (V, d)]
+    return (sum(cd(cd(n, 16) * 16 * cd(k, ks) * ks * es, 256) * 256 for n, k in mats)
+            + cd(V * d * 4, 256) * 256)
 
 
 def test_packed_weights_bytes_and_pack_validation():
@@ -162,7 +164,8 @@ def test_packed_weights_bytes_and_pack_validation():
     _expect(L.EAGLE_ERR_ARG, lambda: pack(dst=None))
     _expect(L.EAGLE_ERR_ARG, lambda: pack(dst=fake + 16))               # misaligned
     _expect(L.EAGLE_ERR_WORKSPACE, lambda: pack(n=need - 1))
-    _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 12), L.EAGLE_PACKED_WEIGHTS)))
+    _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 12),
+                                                             packed=L.EAGLE_PACKED_WEIGHTS)))
     _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 2 + [0] + [fake] * 9))))
     assert "wq" in L.eagle_last_error()
     _expect(L.EAGLE_ERR_ARG, lambda: pack(src_=L.EagleWeights(*([fake] * 2 + [fake + 8] + [fake] * 9))))

@@ -22,8 +22,8 @@ import pytest
 import synth
 from oracle import eagle_oracle as O
 from tests._gpu import (FEAT_TOL, HAVE_GPU, NEAR, PROB_TOL, SCORE_TOL, OracleSeqs, gpu_feats,
-                        gpu_frontier, gpu_pool, gpu_tree_kv, pool_records, quant, rel_l2,
-                        say, seed_workspace, store, to_host)
+                        gpu_frontier, gpu_pool, gpu_rows, gpu_tree_kv, handover, pool_records,
+                        quant, rel_l2, say, seed_workspace, store, to_host)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not HAVE_GPU, reason="needs a GPU")]
@@ -109,21 +109,35 @@ def test_level1_tail(name):
     orc.level1()
     gp, gf = gpu_pool(r), gpu_frontier(r, 1)
     near = 0
+    clear = []
     for b in orc.seqs:
         n = _check_children(cfg, gp[b], orc.pool[b], 0, orc.tail_margin[b], True)
         near += n
         if n == 0:
             _check_frontier(gf[b], orc.F[b][0])
+            clear.append(b)
     say(f"  level1 {name}: {len(orc.seqs)} sequences, {near} near-tie rows")
+    if handover(cfg):
+        # level 1's merge launch formed level 2's FC input: each depth-1 node's
+        # row is [root feature || e(its token)] ([P1] §4.1)
+        from eagle_draft_trees_amd import _lib as L
+        gx0 = gpu_rows(r, L.WS_X0, cfg.d)
+        worst = 0.0
+        for b in clear:
+            F = orc.F[b][0]
+            x0_o = O.draft_rows(orc.model, np.stack([orc.st[b].root_feat] * len(F)),
+                                [x.token for x in F], [0] * len(F))[0]
+            for j in range(cfg.k):
+                e = rel_l2(gx0[b * cfg.k + j], x0_o[j])
+                worst = max(worst, e)
+                assert e <= FEAT_TOL["f32"], (b, j, e)
+        say(f"  FC hand-over {name} level 1: {len(clear)} sequences, worst x0 rel L2 {worst:.2e}")
 
 
 # ------------------------------------------------------------------ levels >= 2
 
 def _levels_for(name):
-    cfg = synth.config_by_name(name)
-    if name in FULL:
-        return [2] + ([3] if name in ("7b", "chain") else [])
-    return list(range(2, cfg.D + 1))
+    return list(range(2, synth.config_by_name(name).D + 1))
 
 
 @pytest.mark.parametrize("name,level", [(n, L) for n in FAST + FULL for L in _levels_for(n)])
@@ -142,14 +156,18 @@ def test_level_forward_then_tail(name, level):
     orc.quantize_scores()
     seed_workspace(r, orc, upto_depth=level - 1)
     sync()
-    r.level(level, L.EAGLE_LEVEL_FULL)
+    # the workspace was written here, so this level forms its own FC input
+    r.level(level, L.EAGLE_LEVEL_FULL_FC)
     sync()
-    h_o = orc.forward(level)  # the same (rounded) stage inputs
+    parts = {}
+    h_o = orc.forward(level, parts)  # the same (rounded) stage inputs
     depth = level - 1
     gfeat = gpu_feats(r, depth)
     gtk, gtv = gpu_tree_kv(r)
+    g_mid = {"x0": gpu_rows(r, L.WS_X0, cfg.d), "attn": gpu_rows(r, L.WS_ATTN, cfg.H * cfg.hd),
+             "y": gpu_rows(r, L.WS_Y, cfg.d)}
     tol = FEAT_TOL[cfg.dtype]
-    worst = 0.0
+    worst, mid = 0.0, {key: 0.0 for key in g_mid}
     for b in orc.seqs:
         for j in range(cfg.k):
             e = rel_l2(gfeat[b, j], h_o[b][j])
@@ -158,7 +176,10 @@ def test_level_forward_then_tail(name, level):
             ok, ov = orc.intree[b][(depth, j)]
             assert rel_l2(gtk[b, depth, j], ok) <= tol
             assert rel_l2(gtv[b, depth, j], ov) <= tol
-    say(f"  forward {name} level {level}: worst feature rel L2 {worst:.2e} (tol {tol})")
+            for key, g in g_mid.items():   # per-intermediate errors, reported
+                mid[key] = max(mid[key], rel_l2(g[b * cfg.k + j], parts[b][key][j]))
+    say(f"  forward {name} level {level}: worst feature rel L2 {worst:.2e} (tol {tol}); "
+        f"intermediates x0 {mid['x0']:.2e}, attention {mid['attn']:.2e}, y {mid['y']:.2e}")
 
     # tail-only stage on the oracle's features, rounded as the GPU stores them
     orc.quantize_state(depth)
@@ -175,6 +196,7 @@ def test_level_forward_then_tail(name, level):
     gp, gf = gpu_pool(r), gpu_frontier(r, level)
     base = cfg.k + (level - 2) * cfg.k * cfg.k
     near = 0
+    clear = []
     for b in orc.seqs:
         tails = orc.tail_margin[b][-cfg.k:]
         n = _check_children(cfg, gp[b], orc.pool[b][base:base + cfg.k * cfg.k], base, tails, True)
@@ -183,7 +205,23 @@ def test_level_forward_then_tail(name, level):
             _check_frontier(gf[b], orc.F[b][-1])
             assert np.allclose(gf[b]["score"][:cfg.k], [x.score for x in orc.F[b][-1]],
                                atol=SCORE_TOL, rtol=0)
+            clear.append(b)
     say(f"  tail {name} level {level}: {near} near-tie rows")
+    if handover(cfg) and level < cfg.D:
+        # the merge launch also formed the next level's FC input from the seeded
+        # features and the frontier it chose: x0 of each next-frontier node x is
+        # FC([feature of x's parent || e(token of x)]) ([P1] §4.1)
+        gx0 = gpu_rows(r, L.WS_X0, cfg.d)
+        worst = 0.0
+        for b in clear:
+            F = orc.F[b][-1]
+            pf = np.stack([orc.feats[b][(depth, x.pslot)] for x in F])
+            x0_o = O.draft_rows(orc.model, pf, [x.token for x in F], [0] * len(F))[0]
+            for j in range(cfg.k):
+                e = rel_l2(gx0[b * cfg.k + j], x0_o[j])
+                worst = max(worst, e)
+                assert e <= FEAT_TOL["f32"], (b, j, e)
+        say(f"  FC hand-over {name} level {level}: {len(clear)} sequences, worst x0 rel L2 {worst:.2e}")
 
 
 # ------------------------------------------------------------------ static tree

@@ -112,6 +112,10 @@ def lib() -> ctypes.CDLL:
             "eagle_verify_rejection": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                                  c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+            "eagle_verify_rejection_topk": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
+                                                      c_void_p, c_float, c_void_p, c_void_p,
+                                                      c_void_p, c_void_p, c_void_p, c_size_t,
+                                                      c_void_p]),
             "eagle_verify_relaxed_scratch_bytes": (c_size_t, [P(EagleTreeCfg)]),
             "eagle_verify_relaxed": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                                c_void_p, c_float, c_float, c_void_p,
@@ -269,6 +273,15 @@ def eagle_verify_rejection(cfg, vocab, target_logits, draft_logits, tokens, pare
                                         float(temperature), _ptr(uniforms), _ptr(accept_len),
                                         _ptr(accept_path), _ptr(bonus), _ptr(scratch),
                                         _nbytes(scratch), _stream(stream)), "eagle_verify_rejection")
+
+
+def eagle_verify_rejection_topk(cfg, vocab, target_logits, tokens, parents, temperature, uniforms,
+                                accept_len, accept_path, bonus, scratch, stream=None) -> None:
+    _check(lib().eagle_verify_rejection_topk(ctypes.byref(cfg), vocab, _ptr(target_logits),
+                                             _ptr(tokens), _ptr(parents), float(temperature),
+                                             _ptr(uniforms), _ptr(accept_len), _ptr(accept_path),
+                                             _ptr(bonus), _ptr(scratch), _nbytes(scratch),
+                                             _stream(stream)), "eagle_verify_rejection_topk")
 
 
 def eagle_verify_relaxed_scratch_bytes(cfg) -> int:

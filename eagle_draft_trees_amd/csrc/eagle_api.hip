@@ -46,7 +46,8 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   p.zg = cdiv(M, 64);
   p.ct = 4;
   p.nblk = cdiv(p.N, 64);
-  const int kc = gemm_kc(p.nw, (int)elem_size(d));
+  p.hl = op == OP_QKV && d.dtype == EAGLE_BF16;
+  const int kc = gemm_kc(p.nw, (int)elem_size(d), p.hl);
   // K is split across workgroups only when the column blocks alone leave
   // more than half of the compute units idle; a split keeps two chunks or more
   const int base = p.nblk * p.zg;
@@ -85,8 +86,10 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   const int nw = op == OP_GATEUP ? 2 : 1;
   // one column tile per workgroup: all 16 waves split K (every CU busy);
   // several tiles: fewer, longer K slices (at least 32 k-steps) stream better
-  p.KSW = p.CT == 1 ? std::max(1, std::min(SK_MAXW, nks / 8))
-                    : std::max(1, std::min(SK_MAXW / p.CT, nks / 32));
+  const int maxw = op == OP_QKV ? SK_QKVW : SK_MAXW;
+  p.CT = std::min(p.CT, maxw);
+  p.KSW = p.CT == 1 ? std::max(1, std::min(maxw, nks / 8))
+                    : std::max(1, std::min(maxw / p.CT, nks / 32));
   p.nwg = cdiv(p.ntile, p.CT);
   p.nps = 0;
   // the X tile is staged in LDS when it fits and is shared by at least two
@@ -94,7 +97,10 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   // (not the FC, whose X rows are gathered from two sources)
   // (not the down projection either: its X, the SwiGLU activations, is stored
   // packed, one contiguous kilobyte per k-step, and is read from L2 directly)
-  p.xlds = op != OP_FC && op != OP_DOWN && p.CT * nw >= 2 && sk_xtile_bytes(p.K, (int)elem_size(d)) <= SK_XLDS_MAX;
+  // (the bf16 q/k/v projection stages both parts of x0, in two K phases)
+  const size_t xt = op == OP_QKV && d.dtype == EAGLE_BF16 ? sk_hl_tile_bytes(p.K, 2)
+                                                          : sk_xtile_bytes(p.K, (int)elem_size(d));
+  p.xlds = op != OP_FC && op != OP_DOWN && p.CT * nw >= 2 && xt <= SK_XLDS_MAX;
   return p;
 }
 
@@ -178,12 +184,15 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   L.pool = take((size_t)B * L.pool_n * sizeof(eagle_pool_entry));
   L.frontier = take((size_t)(D + 1) * B * k * sizeof(eagle_frontier_node));
   L.feat = take((size_t)D * B * k * d.d * es);
-  const size_t kvt = (size_t)B * D * k * d.n_kv_heads * d.head_dim * es;
+  // in-tree K/V in fp32: their scores reach the thousands at deep levels,
+  // where a bf16 rounding of a key moves the softmax
+  const size_t kvt = (size_t)B * D * k * d.n_kv_heads * d.head_dim * 4;
   L.tk = take(kvt);
   L.tv = take(kvt);
   L.ext_h = take((size_t)rows_ex * d.d * es);
   L.x0f = take(R * d.d * 4);
   L.x0b = take(R * d.d * es);
+  L.x0l = take(R * d.d * es);
   L.q = take(R * HD * 4);
   L.attn = take(R * HD * es);
   L.yf = take(R * d.d * 4);
@@ -334,7 +343,7 @@ static RoundArgs make_args(const eagle_dims& d, const eagle_tree_cfg& c, const e
   a.pool = (eagle_pool_entry*)(base + L.pool);
   a.frontier = (eagle_frontier_node*)(base + L.frontier);
   a.feat = base + L.feat; a.tk = base + L.tk; a.tv = base + L.tv; a.ext_h = base + L.ext_h;
-  a.x0f = (float*)(base + L.x0f); a.x0b = base + L.x0b; a.q = (float*)(base + L.q);
+  a.x0f = (float*)(base + L.x0f); a.x0b = base + L.x0b; a.x0l = base + L.x0l; a.q = (float*)(base + L.q);
   a.attn = base + L.attn; a.yf = (float*)(base + L.yf); a.yg = base + L.yg;
   a.rstd = (float*)(base + L.rstd); a.ssq = (float*)(base + L.ssq); a.act = base + L.act;
   a.gpart = (float*)(base + L.gpart); a.lmpart = (float*)(base + L.lmpart);
@@ -605,10 +614,32 @@ int eagle_verify_rejection(const eagle_tree_cfg* cfg, int32_t vocab, const float
   if ((uintptr_t)scratch % 8) return fail(EAGLE_ERR_ARG, "scratch not 8-byte aligned");
   const size_t need = verify_rejection_scratch_bytes(cfg->batch, cfg->m);
   if (scratch_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "scratch %zu < %zu bytes", scratch_bytes, need);
+  if ((long)cfg->batch * cfg->m > 65535) return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", cfg->batch * cfg->m);
   return hip_ok(launch_verify_rejection(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, draft_logits,
                                         tokens, parents, temperature, uniforms, scratch, accept_len,
                                         accept_path, bonus, (hipStream_t)stream),
                 "verify_rejection");
+}
+
+int eagle_verify_rejection_topk(const eagle_tree_cfg* cfg, int32_t vocab, const float* target_logits,
+                                const int32_t* tokens, const int32_t* parents, float temperature,
+                                const float* uniforms, int32_t* accept_len, int32_t* accept_path, int32_t* bonus,
+                                void* scratch, size_t scratch_bytes, void* stream) {
+  int r;
+  if ((r = check_cfg(nullptr, cfg))) return r;
+  if (vocab < 1) return fail(EAGLE_ERR_SHAPE, "vocab %d", vocab);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(EAGLE_ERR_ARG, "temperature %g (positive, finite)", (double)temperature);
+  if (!target_logits || !tokens || !parents || !uniforms || !accept_len || !accept_path || !bonus || !scratch)
+    return fail(EAGLE_ERR_ARG, "verify_rejection_topk: NULL pointer");
+  if ((uintptr_t)scratch % 8) return fail(EAGLE_ERR_ARG, "scratch not 8-byte aligned");
+  const size_t need = verify_relaxed_scratch_bytes(cfg->batch, cfg->m);
+  if (scratch_bytes < need) return fail(EAGLE_ERR_WORKSPACE, "scratch %zu < %zu bytes", scratch_bytes, need);
+  if ((long)cfg->batch * cfg->m > 65535) return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d too large", cfg->batch * cfg->m);
+  return hip_ok(launch_verify_relaxed(cfg->batch, cfg->m, cfg->depth, vocab, target_logits, tokens, parents,
+                                      temperature, 0.f, uniforms, scratch, accept_len, accept_path, bonus,
+                                      (hipStream_t)stream, true),
+                "verify_rejection_topk");
 }
 
 size_t eagle_verify_relaxed_scratch_bytes(const eagle_tree_cfg* cfg) {
@@ -677,8 +708,8 @@ int eagle_ws_view(const eagle_dims* dims, const eagle_tree_cfg* cfg, const void*
     case EAGLE_WS_POOL: off = L.pool; n = B * L.pool_n * sizeof(eagle_pool_entry); break;
     case EAGLE_WS_FRONTIER: off = L.frontier; n = (D + 1) * B * k * sizeof(eagle_frontier_node); break;
     case EAGLE_WS_FEAT: off = L.feat; n = D * B * k * dims->d * es; break;
-    case EAGLE_WS_TREE_K: off = L.tk; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
-    case EAGLE_WS_TREE_V: off = L.tv; n = B * D * k * dims->n_kv_heads * dims->head_dim * es; break;
+    case EAGLE_WS_TREE_K: off = L.tk; n = B * D * k * dims->n_kv_heads * dims->head_dim * 4; break;
+    case EAGLE_WS_TREE_V: off = L.tv; n = B * D * k * dims->n_kv_heads * dims->head_dim * 4; break;
     case EAGLE_WS_EXT_H: off = L.ext_h; n = B * ext_rows((int)m, (int)D) * dims->d * es; break;
     case EAGLE_WS_X0: off = L.x0f; n = (size_t)L.rows_max * dims->d * 4; break;
     case EAGLE_WS_ATTN: off = L.attn; n = (size_t)L.rows_max * dims->n_heads * dims->head_dim * es; break;

@@ -20,8 +20,10 @@ constexpr int GRID_CNT = NCNT - 1;
 constexpr int GEMM_MAXS = 64;    // split-K ways at most
 constexpr int GW_KSW = 4;                   // layer GEMM workgroup: 4 column tiles x GW_KSW K slices
 constexpr int GW_THREADS = 4 * GW_KSW * 64;
-// k-steps per wave per X chunk: four with one weight stream, two with two
-__host__ __device__ constexpr int gw_bu(int nw) { return nw == 2 ? 2 : 4; }
+// k-steps per wave per X chunk: four with one weight stream, two with two or
+// with X in two parts (hl: the bf16 q/k/v projection's x0 = hi + lo, whose two
+// chunks share the LDS)
+__host__ __device__ constexpr int gw_bu(int nw, bool hl = false) { return (nw == 2 || hl) ? 2 : 4; }
 constexpr int GW_FIN_THREADS = 1024;        // split-sum workgroup: one (column tile, m-tile, lane) per thread
 
 enum Op { OP_FC = 0, OP_QKV = 1, OP_O = 2, OP_GATEUP = 3, OP_DOWN = 4 };
@@ -179,7 +181,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 
 struct WsLayout {
   size_t err, cnt, pool, frontier, feat, tk, tv, ext_h;
-  size_t x0f, x0b, q, attn, yf, yg, rstd, ssq, act;
+  size_t x0f, x0b, x0l, q, attn, yf, yg, rstd, ssq, act;
   size_t gpart, lmpart, lmres, apart, xpk;
   size_t total;
   int rows_max, pool_n;
@@ -187,17 +189,18 @@ struct WsLayout {
 
 struct GemmPlan {
   int M, N, K, nw, mt, zg, nblk, S, Kc;
+  int hl;              // X in two bf16 parts (the bf16 q/k/v projection)
   int ct;              // column tiles per workgroup (3 or 4; 4 whenever K is split)
   int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
   size_t part_floats;  // split-K partial floats (0 when S == 1)
 };
 // K elements of one X chunk of a layer GEMM (the GW_KSW slices' k-steps)
-inline int gemm_kc(int nw, int es) { return GW_KSW * gw_bu(nw) * (es == 2 ? 32 : 16); }
+inline int gemm_kc(int nw, int es, bool hl = false) { return GW_KSW * gw_bu(nw, hl) * (es == 2 ? 32 : 16); }
 // dynamic LDS of a layer GEMM workgroup: two X chunks, then the K-slice
 // partials, then the output tile and the RMSNorm partials
 inline size_t gemm_lds_bytes(const GemmPlan& p, int es) {
   const size_t rows = (size_t)p.mt * 16;
-  const size_t xt = 2 * rows * ((size_t)gemm_kc(p.nw, es) * es + 16);
+  const size_t xt = (p.hl ? 4 : 2) * rows * ((size_t)gemm_kc(p.nw, es, p.hl) * es + 16);
   const size_t red = (size_t)(GW_KSW - 1) * 4 * p.nw * p.mt * 64 * 16;
   const size_t tile = (size_t)p.nw * rows * 65 * 4 + rows * 16 * 4;
   return xt > red ? (xt > tile ? xt : tile) : (red > tile ? red : tile);
@@ -206,6 +209,7 @@ inline size_t gemm_lds_bytes(const GemmPlan& p, int es) {
 // Level GEMM with at most 16 rows: CT column tiles of 16 per workgroup, K split
 // over KSW waves per tile (CT * KSW <= SK_MAXW waves), nwg workgroups.
 constexpr int SK_MAXW = 16;
+constexpr int SK_QKVW = 12;  // waves of a q/k/v projection workgroup at most
 struct SkPlan {
   int M, N, K, ntile, CT, KSW, nwg;
   int nps;   // gate/up: RMSNorm partial sums per row written by the O launch
@@ -260,6 +264,7 @@ struct RoundArgs {
   void *feat, *tk, *tv, *ext_h;
   float* x0f;
   void* x0b;
+  void* x0l;  // bf16: the low part of x0, bf16(x0 - bf16(x0))
   float* q;
   void* attn;
   const uint8_t* vmask;  // tree verify: the [B][m][m] ancestor-or-self mask
@@ -395,6 +400,18 @@ __device__ __forceinline__ void ext_advance_state(const RoundArgs& a, int tid, i
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
+
+// x0 element idx of the layer's rows: fp32 (the residual), the dtype copy and,
+// for bf16, the low part that the q/k/v projection adds back
+template <typename T>
+__device__ __forceinline__ void st_x0(const RoundArgs& a, size_t idx, float x) {
+  a.x0f[idx] = x;
+  El<T>::st((T*)a.x0b, idx, x);
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t h = f2bf(x);
+    ((bf16_t*)a.x0l)[idx] = (bf16_t)f2bf(x - bf2f(h));
+  }
+}
 // 16-byte load from a pointer known to be global memory (for pointers that
 // were themselves read from LDS, whose address space the compiler cannot infer)
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -474,10 +491,11 @@ hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, 
 hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
                          const int32_t* parents, int32_t* alen, int32_t* apath, int32_t* bonus,
                          hipStream_t s);
+// topk: the deterministic-candidate rejection walk (uniforms [B][m+1], no threshold)
 hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
                                  const int32_t* parents, float temperature, float threshold,
                                  const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
-                                 int32_t* bonus, hipStream_t s);
+                                 int32_t* bonus, hipStream_t s, bool topk = false);
 size_t verify_relaxed_scratch_bytes(int B, int m);
 hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, const float* dl,
                                    const int32_t* tokens, const int32_t* parents, float temperature,

@@ -171,10 +171,11 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
 
   // the first chunk's K/V loads go out now, ahead of the query setup
   typedef typename VV::raw vraw;
+  const int cl = sizeof(T) == 2 ? min(c1, cp) : c1;  // end of the ping-pong range
   const int vcol = VV::col(lane);
   auto load = [&](uint4 (&kr)[NKS], vraw (&vr)[NV], int c) __attribute__((always_inline)) {
-    c = min(c, c1 - 1);  // past the split's last chunk: repeat it (unused)
-    if (c < cp) {  // consecutive prefix rows; the last chunk's tail repeats row Pv-1
+    c = min(c, cl - 1);  // past the range's last chunk: repeat it (unused)
+    if (sizeof(T) == 2 || c < cp) {  // consecutive prefix rows; the last chunk's tail repeats row Pv-1
       const int r0 = c * AT_C, rmax = Pv - 1 - r0;
       const T* kp = Kp + (size_t)(r0 + min(q, rmax)) * rs;
 #pragma unroll
@@ -190,11 +191,12 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     }
   };
 
-  // this wave's chunks: c0+w, c0+w+AT_W, ... below c1 (a wave-uniform count);
-  // the first is in flight before the query setup
+  // this wave's chunks: c0+w, c0+w+AT_W, ... below cl (a wave-uniform count);
+  // the first is in flight before the query setup.  bf16: cl ends the prefix
+  // chunks, and the wave's in-tree chunks (same stride) follow one by one.
   uint4 ka[NKS], kb[NKS];
   vraw va[NV], vb[NV];
-  const int nmine = __builtin_amdgcn_readfirstlane(c0 + w < c1 ? (c1 - 1 - c0 - w) / AT_W + 1 : 0);
+  const int nmine = __builtin_amdgcn_readfirstlane(c0 + w < cl ? (cl - 1 - c0 - w) / AT_W + 1 : 0);
   if (nmine >= 1) load(ka, va, c0 + w);
 
   // ---- this lane's query operand (query q0+q, dims of k-step s for lane group g),
@@ -265,14 +267,10 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[i][e] = 0.f;
 
-  auto chunk = [&](const uint4 (&kr)[NKS], const vraw (&vr)[NV], int c) __attribute__((always_inline)) {
-    // scores: lane (g, q) gets S^T[4g + r][q], r = 0..3
-    f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      st = mma16(kr[s], qh[s], st, T());
-      if constexpr (sizeof(T) == 2) st = mma16(kr[s], ql[s], st, T());
-    }
+  // masking and the online-softmax update of one chunk's scores: lane (g, q)
+  // holds S^T[4g + r][q]; returns this chunk's rescale of the running output
+  // and the lane's four probabilities
+  auto smax = [&](const f32x4_t& st, int c, float& al, float (&pr4)[4]) __attribute__((always_inline)) {
     float sc[4];
     float cmax = -INFINITY;
 #pragma unroll
@@ -297,8 +295,8 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
     const float mnew = fmaxf(m, cmax);
-    const float al = (m == -INFINITY) ? 0.f : expf(m - mnew);
-    float pr4[4], ps = 0.f;
+    al = (m == -INFINITY) ? 0.f : expf(m - mnew);
+    float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       pr4[r] = sc[r] == -INFINITY ? 0.f : expf(sc[r] - mnew);
@@ -308,18 +306,35 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     ps += __shfl_xor(ps, 32);
     l = l * al + ps;
     m = mnew;
-    if constexpr (MFPV) {
-      // lane (g, q) holds query q's probabilities of keys 4g..4g+3: the B
-      // operand of the 16x16x16 product as it stands.  A high and a low bf16
-      // part keep about 16 bits of each probability; V is exact in bf16.
-      uint32_t h[4], lo[4];
+  };
+  // lane (g, q) holds query q's probabilities of keys 4g..4g+3: the B operand
+  // of the 16x16x16 P.V product as it stands; a high and a low bf16 part keep
+  // about 16 bits of each probability
+  auto psplit = [&](const float (&pr4)[4], uint2& bh, uint2& bl) __attribute__((always_inline)) {
+    uint32_t h[4], lo[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        h[r] = f2bf(pr4[r]);
-        lo[r] = f2bf(pr4[r] - bf2f(h[r]));
-      }
-      const uint2 bh = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-      const uint2 bl = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+    for (int r = 0; r < 4; ++r) {
+      h[r] = f2bf(pr4[r]);
+      lo[r] = f2bf(pr4[r] - bf2f(h[r]));
+    }
+    bh = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    bl = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+  };
+
+  auto chunk = [&](const uint4 (&kr)[NKS], const vraw (&vr)[NV], int c) __attribute__((always_inline)) {
+    // scores: lane (g, q) gets S^T[4g + r][q], r = 0..3
+    f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      st = mma16(kr[s], qh[s], st, T());
+      if constexpr (sizeof(T) == 2) st = mma16(kr[s], ql[s], st, T());
+    }
+    float al, pr4[4];
+    smax(st, c, al, pr4);
+    if constexpr (MFPV) {
+      // V is exact in bf16
+      uint2 bh, bl;
+      psplit(pr4, bh, bl);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const uint2 av = make_uint2(VV::el(vr[0], t) | (VV::el(vr[1], t) << 16),
@@ -363,6 +378,81 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     }
   };
 
+  // bf16: an in-tree chunk.  The in-tree K/V are fp32; each is split into a
+  // high and a low bf16 part, and the products keep the three significant
+  // terms (hi.hi, hi.lo, lo.hi) of both the scores and P.V.
+  auto tchunk = [&](int c) __attribute__((always_inline)) {
+    const float* KtF = (const float*)a.tk;
+    const float* VtF = (const float*)a.tv;
+    auto trow = [&](const float* tree, int i) __attribute__((always_inline)) -> const float* {
+      int t = (c - cp) * AT_C + i;
+      t = t < ntree ? t : 0;
+      const int dep = t / a.k + 1, slot = t - (dep - 1) * a.k;
+      return tree + ((((size_t)b * a.D + dep) * a.k + slot) * a.Hkv + kvh) * HD;
+    };
+    auto split8 = [&](const float4& x0, const float4& x1, uint4& hi, uint4& lo) __attribute__((always_inline)) {
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t h0 = f2bf(x[2 * e]), h1 = f2bf(x[2 * e + 1]);
+        hw[e] = h0 | (h1 << 16);
+        lw[e] = f2bf(x[2 * e] - bf2f(h0)) | (f2bf(x[2 * e + 1] - bf2f(h1)) << 16);
+      }
+      hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    };
+    // loads first: the key row of lane column q, and V rows 4g..4g+3 at the lane's NT columns
+    const float* kp = trow(KtF, q);
+    float4 kx[NKS][2];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      kx[s][0] = *(const float4*)(kp + s * KS + g * PER);
+      kx[s][1] = *(const float4*)(kp + s * KS + g * PER + 4);
+    }
+    float vx[4][NT];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* vp = trow(VtF, 4 * g + u) + vcol;
+#pragma unroll
+      for (int t = 0; t < NT; t += 4) {
+        const float4 f = *(const float4*)(vp + t);
+        vx[u][t] = f.x;
+        vx[u][t + 1] = f.y;
+        vx[u][t + 2] = f.z;
+        vx[u][t + 3] = f.w;
+      }
+    }
+    f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      uint4 kh, kl;
+      split8(kx[s][0], kx[s][1], kh, kl);
+      st = mma16(kh, qh[s], st, T());
+      st = mma16(kh, ql[s], st, T());
+      st = mma16(kl, qh[s], st, T());
+    }
+    float al, pr4[4];
+    smax(st, c, al, pr4);
+    uint2 bh, bl;
+    psplit(pr4, bh, bl);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      uint32_t vh[4], vl[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        vh[u] = f2bf(vx[u][t]);
+        vl[u] = f2bf(vx[u][t] - bf2f(vh[u]));
+      }
+      const uint2 ah = make_uint2(vh[0] | (vh[1] << 16), vh[2] | (vh[3] << 16));
+      const uint2 alo = make_uint2(vl[0] | (vl[1] << 16), vl[2] | (vl[3] << 16));
+      f32x4_t o = accm[t] * al;
+      o = mma16k16(ah, bh, o);
+      o = mma16k16(ah, bl, o);
+      accm[t] = mma16k16(alo, bh, o);
+    }
+  };
+
   if (nmine == 1) {
     // a single chunk (short prefixes, or many key splits): nothing to prefetch
     chunk(ka, va, c0 + w);
@@ -373,12 +463,16 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
       load(kb, vb, c + AT_W);
       __builtin_amdgcn_sched_barrier(0);
       chunk(ka, va, c);
-      if (c + AT_W >= c1) break;
+      if (c + AT_W >= cl) break;
       load(ka, va, c + 2 * AT_W);
       __builtin_amdgcn_sched_barrier(0);
       chunk(kb, vb, c + AT_W);
-      if (c + 2 * AT_W >= c1) break;
+      if (c + 2 * AT_W >= cl) break;
     }
+  }
+  if constexpr (sizeof(T) == 2) {  // this wave's in-tree chunks, c ≡ c0 + w (mod AT_W)
+    const int f = max(c0, cp);
+    for (int c = f + ((c0 + w - f) % AT_W + AT_W) % AT_W; c < c1; c += AT_W) tchunk(c);
   }
 
   // ---- combine the waves' partial results in wave order

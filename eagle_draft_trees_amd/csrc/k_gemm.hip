@@ -21,9 +21,10 @@
 //   FC      X = the parent (level) or true (extend) feature, gathered on the
 //           fly, against the feature half of W_fc; epilogue + the row token's
 //           token-projection entry + bias -> x0 (fp32 residual, dtype copy)
-//   QKV     epilogue applies RoPE at the row's tree position to q and k
-//           ([P1] §12 item 5: positions shared per level) and writes k, v
-//           straight into the in-tree slot (levels) or the prefix cache (extend)
+//   QKV     x0 taken as two bf16 parts (bf16); epilogue applies RoPE at the
+//           row's tree position to q and k ([P1] §12 item 5: positions shared
+//           per level) and writes k, v straight into the in-tree slot (levels,
+//           fp32) or the prefix cache (extend)
 //   O       epilogue adds the residual x0, keeps y, emits y*gain for the MLP
 //           and per-block sums of squares (each gate/up workgroup sums them
 //           into the RMSNorm 1/rms of its rows)
@@ -90,8 +91,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       const int mr = idx / BW, c = idx % BW, nn = blk * BW + c, row = zg * 64 + mr;
       if (nn >= p.N) continue;
       const float v = TILE(0, mr, c) + a.tok_proj[(size_t)s_tok[mr] * a.d + nn] + El<T>::ld((const T*)a.fc_b, nn);
-      a.x0f[(size_t)row * a.d + nn] = v;
-      El<T>::st((T*)a.x0b, (size_t)row * a.d + nn, v);
+      st_x0<T>(a, (size_t)row * a.d + nn, v);
     }
   } else if (OP == OP_QKV) {
     // the block's tiles are tiles CTW*blk .. CTW*blk+CTW-1 (hd/16 tiles per
@@ -132,17 +132,17 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       } else {
         const bool isk = head < hq + hk;
         const int kvh = isk ? head - hq : head - hq - hk;
-        T* dst;
-        if (a.mode == MODE_LEVEL) {
-          T* base = (T*)(isk ? a.tk : a.tv);
-          dst = base + ((((size_t)b * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd;
+        if (a.mode == MODE_LEVEL) {  // in-tree K/V are kept in fp32 (workspace)
+          float* dst = (float*)(isk ? a.tk : a.tv) + ((((size_t)b * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd;
+          dst[fi] = lo;
+          dst[fi + half] = hi;
         } else {
           T* base = (T*)(isk ? a.k_cache : a.v_cache);
           const int P = clamp_prefix(a.prefix_len[b], a);
-          dst = base + (((size_t)b * a.max_prefix + P + slot) * a.Hkv + kvh) * a.hd;
+          T* dst = base + (((size_t)b * a.max_prefix + P + slot) * a.Hkv + kvh) * a.hd;
+          El<T>::st(dst, fi, lo);
+          El<T>::st(dst, fi + half, hi);
         }
-        El<T>::st(dst, fi, lo);
-        El<T>::st(dst, fi + half, hi);
       }
     }
   } else if (OP == OP_O) {
@@ -193,7 +193,9 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
   constexpr int PER = El<T>::PER16;
   constexpr int ES = (int)sizeof(T);
   constexpr int ROWS = MT * 16;
-  constexpr int BU = gw_bu(NW);              // k-steps per wave per chunk
+  constexpr bool HL = OP == OP_QKV && sizeof(T) == 2;  // x0 as two bf16 parts, two chunks per buffer
+  constexpr int NPART = HL ? 2 : 1;
+  constexpr int BU = gw_bu(NW, HL);          // k-steps per wave per chunk
   constexpr int KC = GW_KSW * BU * KS;       // chunk of K: every slice's k-steps
   constexpr int XST = KC * ES + 16;          // LDS row stride: an m-tile's 16 rows on different banks
   constexpr int XBUF = ROWS * XST;           // one X chunk
@@ -299,7 +301,9 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
       pc = i % NPC;
     }
   };
-  auto xload = [&](uint4 (&xr)[XP], int b) __attribute__((always_inline)) {
+  // (HL: part 1 is x0's low part, its pieces at the same places of the
+  // buffer's second chunk)
+  auto xload = [&](uint4 (&xr)[NPART][XP], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < XP; ++q) {
       int r, pc;
@@ -315,30 +319,35 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
         const int row = zg * 64 + r;
         src = xsrc + (size_t)(row < p.M ? row : zg * 64) * K + k;
       }
-      xr[q] = ld16g(src);
+      xr[0][q] = ld16g(src);
+      if constexpr (HL) xr[NPART - 1][q] = ld16g((const T*)a.x0l + (src - xsrc));
     }
   };
   // unconditional stores: a slot past the chunk repeats the last piece (same
   // value, same place), so no load is sunk into a branch of its own
-  auto xstore = [&](const uint4 (&xr)[XP], int buf) __attribute__((always_inline)) {
+  auto xstore = [&](const uint4 (&xr)[NPART][XP], int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < XP; ++q) {
       int r, pc;
       xpiece(q, r, pc);
-      *(uint4*)(xs + buf * XBUF + r * XST + pc * 16) = xr[q];
+#pragma unroll
+      for (int h = 0; h < NPART; ++h) *(uint4*)(xs + (buf * NPART + h) * XBUF + r * XST + pc * 16) = xr[h][q];
     }
   };
   auto comp = [&](const uint4 (&wbuf)[BU][NW], int b, int buf) __attribute__((always_inline)) {
-    const unsigned char* xrow = xs + buf * XBUF + c * XST;
+    const unsigned char* xrow = xs + buf * NPART * XBUF + c * XST;
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int kc = (ks * BU + u) * KS + g * PER;  // offset in the chunk
       const bool kin = b * KC + kc < kn;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 xf = mask4(*(const uint4*)(xrow + mt * 16 * XST + kc * ES), kin);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wbuf[u][w], acc[w][mt], T());
+        for (int h = 0; h < NPART; ++h) {
+          const uint4 xf = mask4(*(const uint4*)(xrow + h * XBUF + mt * 16 * XST + kc * ES), kin);
+#pragma unroll
+          for (int w = 0; w < NW; ++w) acc[w][mt] = mma16(xf, wbuf[u][w], acc[w][mt], T());
+        }
       }
     }
   };
@@ -348,7 +357,7 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
   // other LDS buffer) and weights are in flight; chunk b+2's loads are issued
   // after chunk b's MFMAs, and one barrier per chunk hands the X buffers over.
   // Loads past the last chunk read clamped in-range addresses and are unused.
-  uint4 xr[XP];
+  uint4 xr[NPART][XP];
   uint4 wa[BU][NW], wb[BU][NW];
   // (scheduling barriers keep the prologue's loads in the loop's order: X
   // chunk, then that chunk's weights)

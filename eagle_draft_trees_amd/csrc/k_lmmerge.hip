@@ -367,8 +367,7 @@ __device__ __forceinline__ void fc_handover(const RoundArgs& a, const SkPlan& fp
     if (n >= a.d) continue;
     const float x = fs[(tl * 16 + s_prow[row]) * 16 + col] + a.tok_proj[(size_t)s_tok[row] * a.d + n] +
                     El<T>::ld((const T*)a.fc_b, n);
-    a.x0f[(size_t)row * a.d + n] = x;
-    El<T>::st((T*)a.x0b, (size_t)row * a.d + n, x);
+    st_x0<T>(a, (size_t)row * a.d + n, x);
   }
 }
 

@@ -45,8 +45,10 @@ __device__ __forceinline__ int sk_col(int op, int t, int c, int hd) {
 
 // XL: X staged once in LDS (when its 16 rows fit) instead of loaded from L2
 // at every k-step; the weight loop then issues only weight loads.
+// (the q/k/v projection runs at most SK_QKVW waves: its two-part X staging
+// needs the registers)
 template <typename T, int OP, bool XL>
-__global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p) {
+__global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_skinny(RoundArgs a, SkPlan p) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;  // weight streams per wave (gate and up)
   constexpr int KS = El<T>::KSTEP;
   constexpr int BU = (NW == 2) ? (XL ? 3 : 2) : 4;  // k-steps per load batch (registers permitting)
@@ -130,7 +132,12 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[NW];
   const int nbu = ((nks + p.KSW - 1) / p.KSW + BU - 1) / BU;
-  sk_stream<T, NW, BU, XL, OP == OP_DOWN>(wr, x0, x1, kswitch, K, s0k, s1k, nbu, dyn, acc, x0 - (size_t)xr * K, p.M);
+  if constexpr (OP == OP_QKV && sizeof(T) == 2) {  // x0 as its two bf16 parts
+    sk_stream_hl<T, BU, XL>(wr[0], (const T*)a.x0b, (const T*)a.x0l, K, ks, p.KSW, dyn, acc[0], p.M);
+  } else {
+    sk_stream<T, NW, BU, XL, OP == OP_DOWN>(wr, x0, x1, kswitch, K, s0k, s1k, nbu, dyn, acc, x0 - (size_t)xr * K,
+                                            p.M);
+  }
 
   // ---- K slices meet in LDS; wave (ct, slice 0) sums them in slice order
   if (XL) __syncthreads();  // every wave is done reading the X tile it overwrites
@@ -165,8 +172,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
         const int row = 4 * g + r;
         if (row >= p.M) continue;
         const float x = v[0][r] + a.tok_proj[(size_t)s_tok[row] * a.d + n] + bias;
-        a.x0f[(size_t)row * a.d + n] = x;
-        El<T>::st((T*)a.x0b, (size_t)row * a.d + n, x);
+        st_x0<T>(a, (size_t)row * a.d + n, x);
       }
     }
   } else if (OP == OP_QKV) {
@@ -204,8 +210,8 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_skinny(RoundArgs a, SkPlan p
         } else {
           const bool isk = head < a.H + a.Hkv;
           const int kvh = isk ? head - a.H : head - a.H - a.Hkv;
-          if (lv)
-            El<T>::st((T*)(isk ? a.tk : a.tv), ((((size_t)bb * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd + idx, val);
+          if (lv)  // in-tree K/V are kept in fp32 (workspace)
+            ((float*)(isk ? a.tk : a.tv))[((((size_t)bb * a.D + a.depth) * a.k + slot) * a.Hkv + kvh) * a.hd + idx] = val;
           else
             El<T>::st((T*)(isk ? a.k_cache : a.v_cache), (((size_t)bb * a.max_prefix + P + slot) * a.Hkv + kvh) * a.hd + idx, val);
         }
@@ -278,7 +284,7 @@ static void launch_sk_op(const RoundArgs& a, const SkPlan& p, hipStream_t s) {
   const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
   const size_t red = (size_t)WAVE * p.CT * p.KSW * NW * sizeof(f32x4_t);
   if (p.xlds && OP != OP_DOWN) {  // the down projection's X is packed, never staged
-    const size_t xb = sk_xtile_bytes(p.K, (int)sizeof(T));
+    const size_t xb = OP == OP_QKV && sizeof(T) == 2 ? sk_hl_tile_bytes(p.K, 2) : sk_xtile_bytes(p.K, (int)sizeof(T));
     hipLaunchKernelGGL((k_skinny<T, OP, OP != OP_DOWN>), grid, block, xb > red ? xb : red, s, a, p);
   } else {
     hipLaunchKernelGGL((k_skinny<T, OP, false>), grid, block, red, s, a, p);

@@ -509,6 +509,15 @@ __global__ void __launch_bounds__(RS_T) k_relaxed_stats(int V, const float* tl, 
   }
 }
 
+// TOPK: strict rejection sampling of deterministic candidates (the draft's
+// top-k children are a fixed list, not draws from q): each child is a
+// point-mass proposal, accepted iff u_c * (mass left) <= p(t_c), i.e. u_c <=
+// the residual's probability of t_c; a rejected token leaves the residual
+// (removed and renormalised).  The bonus is the same residual draw as the
+// relaxed walk's.  uniforms [B][m+1]: u[c] decides flat node c, u[m] draws.
+__device__ __forceinline__ float clamp_u(float u) { return u >= 0.f ? (u < 1.f ? u : 0.99999994f) : 0.f; }
+
+template <bool TOPK>
 __global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, const float* tl,
                                                          const int32_t* tokens, const int32_t* parents,
                                                          float temperature, float thr, const float* uniforms,
@@ -527,8 +536,7 @@ __global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, co
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, b = blockIdx.x;
   const int SEGV = (V + RS_SEG - 1) / RS_SEG;
   const float invT = 1.0f / temperature;
-  float u = uniforms[b];
-  u = u >= 0.f ? (u < 1.f ? u : 0.99999994f) : 0.f;  // into [0, 1); NaN -> 0
+  const float u = clamp_u(TOPK ? uniforms[(size_t)b * (m + 1) + m] : uniforms[b]);  // into [0, 1); NaN -> 0
 
   // ---- the walk, in wave 0 alone: lane j holds flat slot j (m <= 64).  Per
   // visited node one round trip: lanes 0..15 load its segment statistics and
@@ -539,6 +547,7 @@ __global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, co
     const int par = inm ? parents[(size_t)b * m + lane] : -2;
     const int tok = inm ? tokens[(size_t)b * m + lane] : -1;
     const bool inr = tok >= 0 && tok < V;
+    const float uk = (TOPK && inm) ? clamp_u(uniforms[(size_t)b * (m + 1) + lane]) : 0.f;
     int node = 0, len = 1;
     if (lane == 0) path[0] = 0;
     for (;;) {
@@ -552,18 +561,29 @@ __global__ void __launch_bounds__(RV_T) k_verify_relaxed(int m, int D, int V, co
       const float S = wave_sum_dpp(seg);
       const float z = (kid && inr) ? l * invT : -INFINITY;
       const float e = z > -INFINITY ? expf(z - M) : 0.f;
-      const float pc = e / S;
       const unsigned long long kb = __ballot(kid);
-      const unsigned long long pb = __ballot(kid && inr && pc >= thr && len <= D);
+      // a token that an earlier child already carries is removed once: its
+      // mass leaves the residual only with the first
+      bool dup = false;
+      for (unsigned long long rest = kb; rest; rest &= rest - 1ull) {  // the children, in flat order
+        const int j = __ffsll((long long)rest) - 1;
+        dup = dup || (j < lane && __builtin_amdgcn_readlane(tok, j) == tok);
+      }
+      bool pass;
+      if (TOPK) {
+        // the mass left when this child is tried: S less the earlier children's
+        // (distinct) tokens; accept iff u_c * left <= e_c (> 0)
+        const float ee = (kid && inr && !dup) ? e : 0.f;
+        const float incl = wave_incl_scan(ee, lane);
+        const float excl = __shfl_up(incl, 1);
+        const float left = S - (lane > 0 ? excl : 0.f);
+        pass = kid && ee > 0.f && uk * (left > 0.f ? left : 0.f) <= ee && len <= D;
+      } else {
+        pass = kid && inr && e / S >= thr && len <= D;
+      }
+      const unsigned long long pb = __ballot(pass);
       if (!pb) {  // the stop: what the residual draw needs
         if (lane < RS_SEG) s_seg[lane] = seg;
-        // a token that an earlier child already carries is removed once:
-        // its mass is subtracted from its segment only by the first
-        bool dup = false;
-        for (unsigned long long rest = kb; rest; rest &= rest - 1ull) {  // the children, in flat order
-          const int j = __ffsll((long long)rest) - 1;
-          dup = dup || (j < lane && __builtin_amdgcn_readlane(tok, j) == tok);
-        }
         if (kid) {
           const int slot = __popcll(kb & ((1ull << lane) - 1ull));
           s_kid[slot] = inr ? tok : -1;
@@ -747,11 +767,15 @@ hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int3
 hipError_t launch_verify_relaxed(int B, int m, int D, int V, const float* tl, const int32_t* tokens,
                                  const int32_t* parents, float temperature, float threshold,
                                  const float* uniforms, void* scratch, int32_t* alen, int32_t* apath,
-                                 int32_t* bonus, hipStream_t s) {
+                                 int32_t* bonus, hipStream_t s, bool topk) {
   float2* st = (float2*)scratch;
   hipLaunchKernelGGL(k_relaxed_stats, dim3(RS_SEG, B * m, 1), dim3(RS_T), 0, s, V, tl, st, tl, st, temperature);
-  hipLaunchKernelGGL(k_verify_relaxed, dim3(B), dim3(RV_T), 0, s, m, D, V, tl, tokens, parents, temperature,
-                     threshold, uniforms, (const float2*)st, alen, apath, bonus);
+  if (topk)
+    hipLaunchKernelGGL(k_verify_relaxed<true>, dim3(B), dim3(RV_T), 0, s, m, D, V, tl, tokens, parents, temperature,
+                       threshold, uniforms, (const float2*)st, alen, apath, bonus);
+  else
+    hipLaunchKernelGGL(k_verify_relaxed<false>, dim3(B), dim3(RV_T), 0, s, m, D, V, tl, tokens, parents,
+                       temperature, threshold, uniforms, (const float2*)st, alen, apath, bonus);
   return hipGetLastError();
 }
 
@@ -878,7 +902,9 @@ __global__ void __launch_bounds__(RJ_T) k_verify_rejection(int m, int D, int V, 
       const float pc = s_kp[j], qc = s_kq[j];
       const float dc = pc - c * qc;
       const float rc = (dc > 0.f ? dc : 0.f) / N;
-      if (s_kok[j] && s_ku[j] * qc <= rc) {
+      // a token the residual gives no mass is never accepted (also when q
+      // underflows to 0 at a low temperature: 0 <= 0 would pass)
+      if (s_kok[j] && rc > 0.f && s_ku[j] * qc <= rc) {
         next = s_kid[j];
         break;
       }

@@ -137,4 +137,146 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
 // Bytes of X tile staged by sk_stream<XL = true>.
 __host__ __device__ inline size_t sk_xtile_bytes(int K, int es) { return (size_t)16 * ((size_t)K * es + 16); }
 
+// The q/k/v projection's input x0 carried as two bf16 parts, x0 = hi + lo
+// (hi = bf16(x0), lo = bf16(x0 - hi): about 16 mantissa bits), the A operand
+// taken twice per weight fragment.  At the tree's deeper levels the scores
+// q.k of a row's own and ancestor keys reach the thousands (the residual
+// stream grows level by level at these weights), and one bf16 rounding of x0
+// there moves the output by more than bf16 activations elsewhere do; the
+// second MFMA per fragment costs nothing at a weight-streaming shape.
+//
+// XL: the M rows of both parts are staged in LDS in two K phases (the hi rows
+// at tile rows 0..15, the lo rows at 16..31, each phase's k-steps H0 = the
+// larger half, row stride H0*KS*ES + 16 bytes): phase p covers k-steps
+// [p*H0, p*H0 + Hp), split over the KSW waves of a column tile like the whole
+// range is in sk_stream.  At the phase boundary the block restages the tile.
+// Otherwise each lane loads its
+// two 16-byte X pieces per k-step from L2.  K must be a whole number of
+// k-steps.  Every thread of the block calls this.
+__host__ __device__ inline int sk_hl_half(int K, int ks) { return ((K / ks) + 1) / 2; }
+__host__ __device__ inline size_t sk_hl_tile_bytes(int K, int es) {
+  const int KS = es == 2 ? 32 : 16;
+  return (size_t)32 * ((size_t)sk_hl_half(K, KS) * KS * es + 16);
+}
+
+// xh, xl: row 0 of the two parts ([M][K] row-major each).
+template <typename T, int BU, bool XL>
+__device__ __forceinline__ void sk_stream_hl(const T* wr, const T* xh, const T* xl, int K, int ks, int KSW,
+                                             unsigned char* dyn, f32x4_t& acc, int M) {
+  constexpr int KS = El<T>::KSTEP;
+  constexpr int PER = El<T>::PER16;
+  constexpr int ES = (int)sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const size_t xro = (size_t)(c < M ? c : 0) * K;  // this lane's row (rows past M read row 0, discarded)
+  const int nks = K / KS;
+  const int H0 = sk_hl_half(K, KS), H1 = nks - H0;
+  const int XST = H0 * KS * ES + 16;
+  // this wave's k-steps in each phase
+  const int a0 = ks * H0 / KSW, e0 = (ks + 1) * H0 / KSW;
+  const int a1 = H0 + ks * H1 / KSW, e1 = H0 + (ks + 1) * H1 / KSW;
+  // batches per phase, the same in every wave; even and at least two, so that
+  // the phase boundary falls between two loop iterations
+  const int nbh = max(2, (((H0 + KSW - 1) / KSW + BU - 1) / BU + 1) & ~1);
+  const int nb = 2 * nbh;
+  acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // k-step of batch b, element u, and whether it is in the wave's range
+  auto kstep = [&](int b, int u, bool& in) __attribute__((always_inline)) {
+    const int ph = b >= nbh, s = (ph ? a1 : a0) + (b - ph * nbh) * BU + u;
+    in = s < (ph ? e1 : e0);
+    return s;
+  };
+  auto load = [&](uint4 (&wb)[BU], uint4 (&xb)[BU][2], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      bool in;
+      const int st = min(kstep(b, u, in), nks - 1);
+      wb[u] = ld16w(wr + (size_t)st * wtile_elems<T>());
+      if (!XL) {
+        const size_t o = xro + (size_t)st * KS + g * PER;
+        xb[u][0] = ld16(xh + o);
+        xb[u][1] = ld16(xl + o);
+      }
+    }
+  };
+  auto comp = [&](const uint4 (&wb)[BU], const uint4 (&xb)[BU][2], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      bool in;
+      const int s = kstep(b, u, in);
+      uint4 vh, vl;
+      if (XL) {
+        const int ph = b >= nbh;
+        const int sl = min(max(s - ph * H0, 0), H0 - 1);  // a slot outside the phase: clamped, masked below
+        const int off = sl * KS * ES + g * 16;
+        vh = *(const uint4*)(dyn + c * XST + off);
+        vl = *(const uint4*)(dyn + (16 + c) * XST + off);
+      } else {
+        vh = xb[u][0];
+        vl = xb[u][1];
+      }
+      acc = mma16(mask4(vh, in), wb[u], acc, T());
+      acc = mma16(mask4(vl, in), wb[u], acc, T());
+    }
+  };
+  // phase p of both parts into LDS: M rows x Hp k-steps, 16-byte pieces, in
+  // passes of SPT pieces per thread (one pass at the 7B shape).  Keeping the
+  // next phase's pieces in registers across the phase was measured slower than
+  // restaging at the boundary, so the restage is synchronous.
+  constexpr int SPT = 7;
+  const int nt = (int)blockDim.x;
+  auto stage = [&](int ph) __attribute__((always_inline)) {
+    const int npc = (ph ? H1 : H0) * KS / PER, tot = 2 * M * npc;
+    for (int i0 = (int)threadIdx.x; i0 < tot; i0 += nt * SPT) {
+      uint4 v[SPT];
+      int dst[SPT];
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) {  // a slot past the end repeats the last piece (same value, same place)
+        const int i = min(i0 + u * nt, tot - 1), q = i / npc, pc = i - q * npc;
+        const int part = q >= M, r = q - part * M;
+        v[u] = ld16((part ? xl : xh) + (size_t)r * K + (size_t)ph * H0 * KS + pc * PER);
+        dst[u] = (part * 16 + r) * XST + pc * 16;
+      }
+#pragma unroll
+      for (int u = 0; u < SPT; ++u) *(uint4*)(dyn + dst[u]) = v[u];
+    }
+  };
+  uint4 wa[BU], wbf[BU], xa[BU][2], xbf[BU][2];
+  load(wa, xa, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(wbf, xbf, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (XL) {
+    stage(0);
+    __syncthreads();
+  }
+  // phase 0, then the restage (every wave done with phase 0's tile), then phase 1
+  int b = 0;
+  for (; b + 2 <= nbh; b += 2) {
+    comp(wa, xa, b);
+    load(wa, xa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbf, xbf, b + 1);
+    load(wbf, xbf, b + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (XL) {
+    __syncthreads();
+    stage(1);
+    __syncthreads();
+  }
+  for (; b + 2 < nb; b += 2) {
+    comp(wa, xa, b);
+    load(wa, xa, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbf, xbf, b + 1);
+    load(wbf, xbf, b + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+  }
+  if (b < nb) comp(wa, xa, b);
+  if (b + 1 < nb) comp(wbf, xbf, b + 1);
+}
+
 }  // namespace eg

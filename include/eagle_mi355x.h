@@ -10,7 +10,10 @@
  *   eagle_draft_level_static,             a static (fixed-shape) tree instead: the
  *   eagle_build_static_tree               template picks each level's children
  *   eagle_verify_greedy                   greedy longest-accepted-path walk
- *   eagle_verify_rejection                recursive rejection sampling (lossless)
+ *   eagle_verify_rejection                recursive rejection sampling of sampled
+ *                                         children (lossless for i.i.d. draws)
+ *   eagle_verify_rejection_topk           the same for deterministic (top-k or
+ *                                         template) children (lossless)
  *   eagle_verify_relaxed                  threshold acceptance on the target's
  *                                         probabilities, residual draw for the bonus
  *   eagle_draft_extend                    draft forward over the accepted path with
@@ -317,13 +320,20 @@ int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *t
 
 /* Strict verification by recursive rejection sampling ([P1] §6.2: accept a
  * drafted token t iff u <= min(1, p(t)/q(t)), otherwise resample from
- * norm(max(0, p - q)), node by node; the result is distributed exactly as the
- * target).  p = softmax(target_logits[node] / temperature) and q =
+ * norm(max(0, p - q)), node by node).  Precondition for losslessness: the
+ * children of each node were drawn independently from q at that node (a
+ * sampled tree).  The result is then distributed exactly as the target.  The
+ * trees this library builds are deterministic (EAGLE-2's top-k, or a static
+ * template): verify those with eagle_verify_rejection_topk below, for which
+ * this call's output is NOT distributed as the target (a single child t with
+ * q(t) = p(t) = 0.5 is always emitted, not half of the time).
+ * p = softmax(target_logits[node] / temperature) and q =
  * softmax(draft_logits[node] / temperature), both [batch][m][vocab] fp32 (the
  * draft's logits at every flat tree node, kept by the caller; every row is
  * read).  From the root, the node's children are tried in flat order,
- * child c accepted iff uniforms[b][c] * q(t_c) <= p(t_c); after each
- * rejection p <- norm(max(0, p - q)) (kept when that has no mass); when every
+ * child c accepted iff p(t_c) > 0 and uniforms[b][c] * q(t_c) <= p(t_c)
+ * (a token the current p gives no mass is never accepted, whatever q is);
+ * after each rejection p <- norm(max(0, p - q)) (kept when that has no mass); when every
  * child is rejected (or the node is a leaf, or the path already holds depth+1
  * nodes) the bonus is the smallest id whose cumulative p exceeds
  * uniforms[b][m] (clamped into [0, 1)).  uniforms: device fp32
@@ -331,13 +341,35 @@ int eagle_verify_greedy(const eagle_tree_cfg *cfg, int32_t vocab, const float *t
  * least eagle_verify_rejection_scratch_bytes(cfg, vocab) bytes, 8-byte
  * aligned (softmax statistics of every row, per id range), owned by the caller
  * and overwritten.  Outputs as for
- * eagle_verify_greedy. */
+ * eagle_verify_greedy.  batch*m at most 65535. */
 size_t eagle_verify_rejection_scratch_bytes(const eagle_tree_cfg *cfg, int32_t vocab);
 int eagle_verify_rejection(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
                            const float *draft_logits, const int32_t *tokens,
                            const int32_t *parents, float temperature, const float *uniforms,
                            int32_t *accept_len, int32_t *accept_path, int32_t *bonus,
                            void *scratch, size_t scratch_bytes, void *stream);
+
+/* Strict rejection sampling of deterministic candidates ([P1] §6.2, with
+ * each drafted child taken as a point-mass proposal: the draft's top-k
+ * children, or a static template's, are a fixed list and not draws from q).
+ * p = softmax(target_logits[node] / temperature).  From the root, the node's
+ * children are tried in flat order: child c is accepted iff
+ * uniforms[b][c] * (1 - mass of the tokens of the children tried before it)
+ * <= p(t_c) and p(t_c) > 0, i.e. with the probability the current residual
+ * (p with the rejected tokens removed, renormalised) gives t_c; a token that
+ * an earlier sibling already carries is rejected.  When every child is
+ * rejected (or the node is a leaf, or the path already holds depth+1 nodes)
+ * the bonus is drawn from that residual (p with the node's children removed;
+ * p itself if they held all the mass) by inverse CDF with uniforms[b][m]: the
+ * emitted token is distributed exactly as the target for any fixed list of
+ * candidates.  Same arguments as eagle_verify_relaxed (its scratch size too),
+ * without the threshold, and uniforms [batch][m+1] as for
+ * eagle_verify_rejection.  Outputs as for eagle_verify_greedy.  batch*m at
+ * most 65535. */
+int eagle_verify_rejection_topk(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
+                                const int32_t *tokens, const int32_t *parents, float temperature,
+                                const float *uniforms, int32_t *accept_len, int32_t *accept_path,
+                                int32_t *bonus, void *scratch, size_t scratch_bytes, void *stream);
 
 /* Relaxed acceptance ([P2] closing notes on SGLang's verification: the
  * target's probabilities and a probability threshold decide whether a token
@@ -397,8 +429,8 @@ typedef enum {
     EAGLE_WS_POOL = 1,      /* eagle_pool_entry [batch][pool]                        */
     EAGLE_WS_FRONTIER = 2,  /* eagle_frontier_node [depth+1][batch][topk] (by depth)  */
     EAGLE_WS_FEAT = 3,      /* dtype [depth][batch][topk][d]: features of frontier nodes */
-    EAGLE_WS_TREE_K = 4,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree keys (post-RoPE) */
-    EAGLE_WS_TREE_V = 5,    /* dtype [batch][depth][topk][Hkv][hd]: in-tree values    */
+    EAGLE_WS_TREE_K = 4,    /* fp32 [batch][depth][topk][Hkv][hd]: in-tree keys (post-RoPE) */
+    EAGLE_WS_TREE_V = 5,    /* fp32 [batch][depth][topk][Hkv][hd]: in-tree values     */
     EAGLE_WS_EXT_H = 6,     /* dtype [batch][min(m, depth+1)][d]: extend output features */
     /* the last layer pass's intermediates (a level's or the extend's rows, R of them:
        batch*topk, batch*min(m, depth+1) or batch), row-major over the first R rows */

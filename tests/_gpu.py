@@ -112,10 +112,10 @@ class OracleSeqs:
             for key in list(self.feats[b]):
                 if key[0] == depth:
                     self.feats[b][key] = quant(self.feats[b][key], dt)
-            for key in list(self.intree[b]):
+            for key in list(self.intree[b]):   # the GPU keeps in-tree K/V in fp32
                 if key[0] == depth:
                     kk, vv = self.intree[b][key]
-                    self.intree[b][key] = (quant(kk, dt), quant(vv, dt))
+                    self.intree[b][key] = (quant(kk, "f32"), quant(vv, "f32"))
 
     def quantize_scores(self):
         for b in self.seqs:
@@ -163,9 +163,9 @@ def seed_workspace(r, orc: OracleSeqs, upto_depth: int, with_pool: bool = True):
                 r.ws_write(L.WS_FEAT, store(h, cfg.dtype), (((depth * B) + b) * k + slot) * d * es)
         for (depth, slot), (kk, vv) in orc.intree[b].items():
             if depth < upto_depth:
-                off = (((b * D) + depth) * k + slot) * kvrow * es
-                r.ws_write(L.WS_TREE_K, store(kk.reshape(-1), cfg.dtype), off)
-                r.ws_write(L.WS_TREE_V, store(vv.reshape(-1), cfg.dtype), off)
+                off = (((b * D) + depth) * k + slot) * kvrow * 4
+                r.ws_write(L.WS_TREE_K, store(kk.reshape(-1), "f32"), off)
+                r.ws_write(L.WS_TREE_V, store(vv.reshape(-1), "f32"), off)
         if with_pool and orc.pool[b]:
             r.ws_write(L.WS_POOL, pool_records(orc.pool[b]),
                        b * cfg.pool_size * L.POOL_DTYPE.itemsize)
@@ -211,5 +211,6 @@ def gpu_tree_kv(r):
     from eagle_draft_trees_amd import _lib as L
     cfg = r.cfg
     shp = (cfg.B, cfg.D, cfg.k, cfg.Hkv, cfg.hd)
-    return (to_host(r.ws_typed(L.WS_TREE_K).view(*shp)),
-            to_host(r.ws_typed(L.WS_TREE_V).view(*shp)))
+    import torch
+    return (to_host(r.ws_region(L.WS_TREE_K).view(torch.float32).view(*shp)),
+            to_host(r.ws_region(L.WS_TREE_V).view(torch.float32).view(*shp)))

@@ -81,11 +81,23 @@ Readings of what the pages leave open:
       node x, p = softmax(target logits / T) and q = softmax(draft logits / T)
       (the draft's distribution at x, supplied by the caller as logits at
       every tree node); x's children are tried in flat order, child c
-      accepted iff u_c * q(t_c) <= p(t_c), i.e. u_c <= min(1, p/q) (u_c the
-      uniform of flat node c); after each rejection p <- norm(max(0, p - q));
-      when every child is rejected (or x is a leaf) the bonus is drawn from
-      the current p by inverse CDF with the sequence's last uniform.  If
-      max(0, p - q) has no mass, p is kept.
+      accepted iff p(t_c) > 0 and u_c * q(t_c) <= p(t_c), i.e. u_c <=
+      min(1, p/q) (u_c the uniform of flat node c; a token without target
+      mass is never accepted, whatever q is); after each rejection
+      p <- norm(max(0, p - q)); when every child is rejected (or x is a leaf)
+      the bonus is drawn from the current p by inverse CDF with the
+      sequence's last uniform.  If max(0, p - q) has no mass, p is kept.
+      Lossless when the children were drawn from q (a sampled tree).
+  R18 strict verification of deterministic candidates ([P1] §6.2 read with
+      each drafted child as a point-mass proposal, since EAGLE-2's top-k
+      children and a static template's are a fixed list, not draws from q;
+      accepting a point mass at t with probability min(1, p(t)/1) and
+      resampling from norm(max(0, p - delta_t)) is the same rule): at node x
+      the children are tried in flat order, child c accepted iff u_c <= r(t_c)
+      with r = p less the tokens rejected so far, renormalised; a rejection
+      removes t_c from r; at the stop the bonus is drawn from r by inverse CDF
+      (p with x's children removed, as in R15's draw).  R17's rule is kept for
+      trees whose children were sampled from q.
   R16 static tree (EAGLE-1 / Medusa, [P1] §10.1: a fixed-shape tree with a
       fixed number of candidates per level, its shape set once for every
       input; [P3]: EAGLE-1 drafts on one static tree): a template of k slots
@@ -116,7 +128,7 @@ __all__ = [
     "level_step_forward", "level_step_tail", "rerank", "build_tree", "verify_greedy",
     "draft_extend", "run_round", "RoundResult", "NEAR_TIE", "tree_verify_attention",
     "target_probs", "sample_residual", "verify_relaxed", "level_step_tail_static",
-    "build_static_tree", "verify_rejection",
+    "build_static_tree", "verify_rejection", "verify_rejection_topk",
 ]
 
 NEAR_TIE = 1e-3  # a selection whose margin (log domain) is below this is "near-tie"
@@ -595,14 +607,24 @@ def verify_relaxed(target_logits: np.ndarray, tokens: np.ndarray, parents: np.nd
         path.append(node)
 
 
+def _rel_margin(a: float, b: float) -> float:
+    """Distance of the comparison a <= b from flipping, relative to the larger
+    side; 0 where both sides are below fp32's normal range."""
+    hi = max(a, b)
+    return abs(a - b) / hi if hi >= 1e-30 else 0.0
+
+
 def verify_rejection(target_logits: np.ndarray, draft_logits: np.ndarray, tokens: np.ndarray,
                      parents: np.ndarray, temperature: float, u: Sequence[float]):
     """Recursive rejection sampling over the tree ([P1] §6.2: accept t-hat iff
     r <= min(1, p(t-hat)/q(t-hat)), otherwise resample from
-    norm(max(0, p - q)), node by node; R17).  target_logits, draft_logits
+    norm(max(0, p - q)), node by node; R17).  A token the current p gives no
+    mass is never accepted (min(1, 0/q) = 0, also where q is 0).  Lossless when
+    each child was drawn from q at its parent.  target_logits, draft_logits
     [m, V]; u [m + 1]: u[c] decides child c, u[m] draws the bonus.  Returns
-    (path of flat indices from the root, accept_len, bonus, margins):
-    |u_c * q(t_c) - p(t_c)| for every child tried, then the draw's margin."""
+    (path of flat indices from the root, accept_len, bonus, margins): for every
+    child tried |u_c q(t_c) - p(t_c)| relative to the larger side (infinite
+    where p(t_c) is 0), then the draw's margin."""
     m = len(tokens)
     node, path, margins = 0, [0], []
     while True:
@@ -611,8 +633,8 @@ def verify_rejection(target_logits: np.ndarray, draft_logits: np.ndarray, tokens
         nxt = None
         for c in [c for c in range(m) if parents[c] == node and c != node]:
             t = int(tokens[c])
-            margins.append(abs(u[c] * q[t] - p[t]))
-            if u[c] * q[t] <= p[t]:
+            margins.append(_rel_margin(u[c] * q[t], p[t]) if p[t] > 0.0 else math.inf)
+            if p[t] > 0.0 and u[c] * q[t] <= p[t]:
                 nxt = c
                 break
             r = np.maximum(p - q, 0.0)
@@ -620,6 +642,47 @@ def verify_rejection(target_logits: np.ndarray, draft_logits: np.ndarray, tokens
                 p = r / r.sum()
         if nxt is None:
             bonus, mg = sample_residual(p, [], u[m])
+            margins.append(mg)
+            return path, len(path), bonus, margins
+        node = nxt
+        path.append(node)
+
+
+def verify_rejection_topk(target_logits: np.ndarray, tokens: np.ndarray, parents: np.ndarray,
+                          temperature: float, u: Sequence[float]):
+    """Rejection sampling of deterministic candidates (R18; [P1] §6.2 with each
+    drafted child a point-mass proposal: the draft's top-k children are a fixed
+    list, not draws from q).  At node x, p = softmax(target logits / T); the
+    children are tried in flat order, child c accepted iff its token still has
+    mass r(t_c) > 0 in the residual r = p with the rejected tokens removed and
+    renormalised, and u_c <= r(t_c); a rejected token leaves r.  When every
+    child is rejected (or x is a leaf) the bonus is drawn from r, i.e. p with
+    x's children removed (sample_residual).  The emitted token is distributed
+    as p for any fixed candidate list.  target_logits [m, V]; u [m + 1]: u[c]
+    decides child c, u[m] draws the bonus.  Returns (path, accept_len, bonus,
+    margins): for every child tried |u_c * left - p(t_c)| relative to the
+    larger side (left = the residual's unnormalised mass; infinite for a token
+    already removed), then the draw's margin."""
+    m = len(tokens)
+    node, path, margins = 0, [0], []
+    while True:
+        p = target_probs(target_logits[node], temperature)
+        kids = [c for c in range(m) if parents[c] == node and c != node]
+        keep = np.ones(p.size, dtype=bool)  # tokens still in the residual
+        nxt = None
+        for c in kids:
+            t = int(tokens[c])
+            left = float(p[keep].sum())
+            if not keep[t] or not p[t] > 0.0:
+                margins.append(math.inf)
+            else:
+                margins.append(_rel_margin(u[c] * left, p[t]))
+                if u[c] * left <= p[t]:
+                    nxt = c
+                    break
+            keep[t] = False
+        if nxt is None:
+            bonus, mg = sample_residual(p, [int(tokens[c]) for c in kids], u[m])
             margins.append(mg)
             return path, len(path), bonus, margins
         node = nxt

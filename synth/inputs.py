@@ -25,8 +25,10 @@ round-to-nearest-even when the config is bf16.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
@@ -181,23 +183,35 @@ def make_inputs(cfg: TreeConfig, seed: int = 0, *, with_weights: bool = True,
     bf = cfg.dtype == "bf16"
     d, V, F = cfg.d, cfg.V, cfg.F
     out: Dict[str, object] = {"cfg": cfg, "seed": seed}
+    # every tensor has its own stream, so they are drawn in parallel threads
+    # (numpy's generators release the interpreter lock while filling arrays);
+    # the values do not depend on the order
+    jobs: Dict[str, object] = {}
+
+    def normal(name, shape, scale):
+        jobs[name] = lambda: _normal(_rng(seed, cfg, name), shape, scale, bf)
+
     if with_weights:
-        out["fc_w"] = _normal(_rng(seed, cfg, "fc_w"), (d, 2 * d), 0.02, bf)
-        out["fc_b"] = _normal(_rng(seed, cfg, "fc_b"), (d,), 0.02, bf)
-        out["wq"] = _normal(_rng(seed, cfg, "wq"), (cfg.H * cfg.hd, d), 0.02, bf)
-        out["wk"] = _normal(_rng(seed, cfg, "wk"), (cfg.Hkv * cfg.hd, d), 0.02, bf)
-        out["wv"] = _normal(_rng(seed, cfg, "wv"), (cfg.Hkv * cfg.hd, d), 0.02, bf)
-        out["wo"] = _normal(_rng(seed, cfg, "wo"), (d, cfg.H * cfg.hd), 0.02, bf)
-        if cfg.norm_gain_noise:
-            g = 1.0 + _normal(_rng(seed, cfg, "post_norm"), (d,), 0.1, False)
-        else:
-            g = np.ones((d,), dtype=np.float32)
-        out["post_norm"] = bf16_bits(g) if bf else g.astype(np.float32)
-        out["w_gate"] = _normal(_rng(seed, cfg, "w_gate"), (F, d), 0.02, bf)
-        out["w_up"] = _normal(_rng(seed, cfg, "w_up"), (F, d), 0.02, bf)
-        out["w_down"] = _normal(_rng(seed, cfg, "w_down"), (d, F), 0.02, bf)
-        out["embed"] = _normal(_rng(seed, cfg, "embed"), (V, d), 0.02, bf)
-        out["lm_head"] = _normal(_rng(seed, cfg, "lm_head"), (V, d), 3.0 / math.sqrt(d), bf)
+        normal("fc_w", (d, 2 * d), 0.02)
+        normal("fc_b", (d,), 0.02)
+        normal("wq", (cfg.H * cfg.hd, d), 0.02)
+        normal("wk", (cfg.Hkv * cfg.hd, d), 0.02)
+        normal("wv", (cfg.Hkv * cfg.hd, d), 0.02)
+        normal("wo", (d, cfg.H * cfg.hd), 0.02)
+
+        def gain():
+            if cfg.norm_gain_noise:
+                g = 1.0 + _normal(_rng(seed, cfg, "post_norm"), (d,), 0.1, False)
+            else:
+                g = np.ones((d,), dtype=np.float32)
+            return bf16_bits(g) if bf else g.astype(np.float32)
+
+        jobs["post_norm"] = gain
+        normal("w_gate", (F, d), 0.02)
+        normal("w_up", (F, d), 0.02)
+        normal("w_down", (d, F), 0.02)
+        normal("embed", (V, d), 0.02)
+        normal("lm_head", (V, d), 3.0 / math.sqrt(d))
     if with_state:
         B, P = cfg.B, cfg.max_prefix
         rp = _rng(seed, cfg, "prefix_len")
@@ -205,25 +219,34 @@ def make_inputs(cfg: TreeConfig, seed: int = 0, *, with_weights: bool = True,
         if cfg.name.startswith("ragged") and B >= 1:
             plen[0] = 1  # a sequence whose only prefix row is the root row
         out["prefix_len"] = plen
-        kc = np.zeros((B, P, cfg.Hkv, cfg.hd), dtype=np.uint16 if bf else np.float32)
-        vc = np.zeros_like(kc)
-        rk, rv = _rng(seed, cfg, "k_cache"), _rng(seed, cfg, "v_cache")
         keep = set(range(B)) if only_seqs is None else set(int(b) for b in only_seqs)
-        for b in range(B):
-            # draw every sequence in order so that only_seqs reproduces the same values
-            n = int(plen[b])
-            if b in keep:
-                kc[b, :n] = _normal(rk, (n, cfg.Hkv, cfg.hd), 1.0, bf)
-                vc[b, :n] = _normal(rv, (n, cfg.Hkv, cfg.hd), 1.0, bf)
-            else:
-                rk.standard_normal((n, cfg.Hkv * cfg.hd), dtype=np.float32)
-                rv.standard_normal((n, cfg.Hkv * cfg.hd), dtype=np.float32)
-        out["k_cache"], out["v_cache"] = kc, vc
-        out["root_feat"] = _normal(_rng(seed, cfg, "root_feat"), (B, d), 1.0, bf)
-        out["root_token"] = _rng(seed, cfg, "root_token").integers(
+
+        def cache(name):
+            c = np.zeros((B, P, cfg.Hkv, cfg.hd), dtype=np.uint16 if bf else np.float32)
+            r = _rng(seed, cfg, name)
+            for b in range(B):
+                # draw every sequence in order so that only_seqs reproduces the same values
+                n = int(plen[b])
+                if b in keep:
+                    c[b, :n] = _normal(r, (n, cfg.Hkv, cfg.hd), 1.0, bf)
+                else:
+                    r.standard_normal((n, cfg.Hkv * cfg.hd), dtype=np.float32)
+            return c
+
+        jobs["k_cache"] = lambda: cache("k_cache")
+        jobs["v_cache"] = lambda: cache("v_cache")
+        normal("root_feat", (B, d), 1.0)
+        jobs["root_token"] = lambda: _rng(seed, cfg, "root_token").integers(
             0, V, size=B, dtype=np.int64).astype(np.int32)
     if with_round:
-        out["true_feat"] = _normal(_rng(seed, cfg, "true_feat"), (cfg.B, cfg.m, d), 1.0, bf)
-        out["target_logits"] = _normal(_rng(seed, cfg, "target_logits"),
-                                       (cfg.B, cfg.m, V), 3.0, False)
+        normal("true_feat", (cfg.B, cfg.m, d), 1.0)
+        jobs["target_logits"] = lambda: _normal(_rng(seed, cfg, "target_logits"),
+                                                (cfg.B, cfg.m, V), 3.0, False)
+    # the largest draws first, so that they start at once
+    order = sorted(jobs, key=lambda n: n not in ("k_cache", "v_cache", "embed", "lm_head", "w_gate",
+                                                  "w_up", "w_down"))
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        futs = {n: ex.submit(jobs[n]) for n in order}
+        for n, f in futs.items():
+            out[n] = f.result()
     return out

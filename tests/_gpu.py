@@ -27,7 +27,26 @@ except Exception:  # pragma: no cover
 NEAR = O.NEAR_TIE
 FEAT_TOL = {"f32": 1e-4, "bf16": 2e-2}   # relative L2 of feature rows
 PROB_TOL = 1e-3                           # |delta| of top-k child probabilities
-SCORE_TOL = 1e-3                          # |delta| of node log-scores
+SCORE_TOL = 1e-3                          # |delta| of node log-scores (see score_tol)
+
+
+def score_tol(d: int, lscale: float) -> float:
+    """Tolerance of a node log-score whose row's logits reach |lscale|.
+
+    A log-score is the parent's score plus log p = logit - logsumexp, the
+    logits being fp32 sums over d products, accumulated in d/32 MFMA steps.
+    Their rounding grows with the logits' magnitude: about sqrt(d/32) *
+    2^-24 * |logit| per logit (0.5 ulp per step, random signs), two logits
+    per log p, with a factor two of headroom.  The contract's 1e-3 (a
+    relative 1e-3 on the probability products) holds on top of that; it
+    dominates at ordinary logit scales, while the deep levels of the
+    synthetic 70B-shaped workload reach |logits| of 2000."""
+    return SCORE_TOL + 4.0 * math.sqrt(d / 32.0) * 2.0 ** -24 * abs(lscale)
+
+
+def logit_scale(model, h: np.ndarray) -> np.ndarray:
+    """max |logit| of each feature row under the oracle's LM head."""
+    return np.abs(O.lm_logits(model, np.atleast_2d(h))).max(axis=1)
 
 
 def say(msg: str) -> None:

@@ -9,7 +9,9 @@ in fp32 and the oracle in fp64; a sequence whose decisions all have margins
 above 1e-5 (|u q(t) - p(t)| for every child tried, the draw's distance from
 its CDF interval ends; p - q cancels but keeps fp32's relative error of about
 1e-6, which renormalising by its mass preserves) must match exactly, closer
-ones are checked for validity only.
+ones are checked for validity only.  Margins are relative (|u q - p| over the
+larger side), so decisions between tiny probabilities at low temperatures
+are compared like any other.
 """
 from __future__ import annotations
 
@@ -92,6 +94,9 @@ CASES = [  # name, B, m, D, V, T, draft noise
     ("hot", 4, 12, 5, 515, 2.0, 1.0),
     ("7b_shape", 2, 60, 6, 32000, 1.0, 0.3),
     ("far_draft", 3, 10, 4, 777, 1.0, 3.0),
+    # a low temperature: q and p underflow to 0 for most tokens in fp32, and a
+    # child without target mass must still be rejected
+    ("cold", 4, 12, 5, 2048, 0.02, 0.3),
 ]
 
 

@@ -1,4 +1,4 @@
-"""CPU pins of the oracle's recursive rejection sampling (reading R17).
+"""CPU pins of the oracle's recursive rejection sampling (readings R17, R18).
 
 [P1] §6.2 states that the scheme leaves the target distribution exactly
 unchanged.  Here that is checked on the oracle itself: with one or two
@@ -7,7 +7,11 @@ enumerated with its probability), the first emitted token, measured by
 calling the oracle over grids of uniforms, is distributed as p.  Also: q = p
 accepts every child (the first draft token is always accepted, [P1] §7.1), a
 draft with no mass where the target has any rejects everything, and the
-temperature scales both logits.
+temperature scales both logits.  R18 (the same rule with each fixed
+candidate a point-mass proposal): the first emitted token is distributed as
+p for fixed candidate lists over nested grids of uniforms, duplicates are
+never accepted, the all-rejected draw is the residual draw, and at T -> 0
+the walk is the greedy walk.
 """
 import itertools
 
@@ -147,3 +151,102 @@ def test_residual_closed_form(seed):
         if Nn > 0:
             c, N = cn, Nn
         assert np.allclose(np.maximum(0.0, p - c * q) / N, r, rtol=1e-9, atol=1e-12)
+
+
+def test_token_without_target_mass_is_never_accepted():
+    """min(1, p/q) is 0 where p(t) is 0: such a child is rejected even with
+    u = 0 and a draft probability that is 0 too (at a low temperature both
+    can vanish; 0 <= 0 must not accept)."""
+    V = 5
+    tl = np.array([[0.0, 0.0, -np.inf, 10.0, 0.0]] * 2)
+    dl = np.array([[10.0, -np.inf, -np.inf, 0.0, 0.0]] * 2)
+    tokens, parents = np.array([0, 2]), np.array([-1, 0])
+    for T in (1.0, 0.05):
+        path, alen, bonus, margins = O.verify_rejection(tl, dl, tokens, parents, T, np.zeros(3))
+        assert path == [0] and alen == 1 and margins[0] == np.inf
+
+
+# ------------------------------------------------------------------ R18: deterministic candidates
+
+def _first_token_topk(tl, tokens, parents, T, u):
+    path, alen, bonus, _ = O.verify_rejection_topk(tl, tokens, parents, T, u)
+    return int(tokens[path[1]]) if alen > 1 else bonus
+
+
+@pytest.mark.parametrize("kids", [(3,), (1, 4), (5, 0, 2), (2, 2)])
+def test_fixed_candidates_are_lossless(kids):
+    """[P1] §6.2's guarantee for a fixed candidate list (EAGLE-2's top-k
+    children are not draws from q): over a grid of every child's uniform and
+    the bonus uniform, the first emitted token is distributed as p.  The
+    children's uniforms are walked in nested grids (a later child's only
+    matters where the earlier ones rejected), the bonus's over a grid."""
+    rng = np.random.default_rng(sum(kids) + 10 * len(kids))
+    V, T, n = 6, 0.9, 400
+    grid = (np.arange(n) + 0.5) / n
+    m = 1 + len(kids)
+    tl = rng.normal(size=(m, V)) * 1.5
+    p = O.target_probs(tl[0], T)
+    tokens = np.array([0] + list(kids))
+    parents = np.array([-1] + [0] * len(kids))
+    out = np.zeros(V)
+
+    def walk(c, u, weight):
+        # child c decides: the grid fraction that accepts it, then deeper
+        if c == m:
+            draws = np.zeros(V)
+            for x in grid:
+                u[m] = x
+                draws[_first_token_topk(tl, tokens, parents, T, u)] += 1.0 / n
+            out[:] += weight * draws
+            return
+        acc = 0.0
+        for x in grid:
+            u[c] = x
+            path, alen, _, _ = O.verify_rejection_topk(tl, tokens, parents, T, u)
+            acc += (alen > 1 and path[1] == c) / n
+        out[int(tokens[c])] += weight * acc
+        u[c] = 1.0 - 0.25 / n  # above every grid point: child c rejected
+        if acc < 1.0:
+            walk(c + 1, u, weight * (1.0 - acc))
+
+    walk(1, np.zeros(m + 1), 1.0)
+    assert np.allclose(out, p, atol=2.0 * len(kids) / n)
+
+
+def test_fixed_candidates_duplicate_and_draw():
+    """A token an earlier sibling already carries is never accepted; when
+    every child is rejected the bonus is the residual draw with the children
+    removed (sample_residual)."""
+    rng = np.random.default_rng(3)
+    V, T = 7, 1.0
+    tl = rng.normal(size=(4, V))
+    tokens, parents = np.array([0, 3, 3, 5]), np.array([-1, 0, 0, 0])
+    p = O.target_probs(tl[0], T)
+    for ub in (0.1, 0.5, 0.93):
+        u = np.array([0.0, 0.999, 0.0, 0.999, ub])  # child 1 and 3 rejected; 2 duplicates 1
+        path, alen, bonus, margins = O.verify_rejection_topk(tl, tokens, parents, T, u)
+        assert path == [0] and margins[1] == np.inf
+        assert bonus == O.sample_residual(p, [3, 3, 5], ub)[0]
+    # a child is accepted with the residual probability: p(t)/(1 - mass removed)
+    r = p[5] / (1.0 - p[3])
+    for x, want in ((r * 0.999, [0, 3]), (r * 1.001, [0])):
+        path = O.verify_rejection_topk(tl, tokens, parents, T, np.array([0.0, 0.999, 0.0, x, 0.5]))[0]
+        assert path == want
+
+
+def test_fixed_candidates_equal_target_greedy_at_low_temperature():
+    """As T -> 0 the residual puts all mass on the argmax: the walk descends
+    exactly where the greedy walk does (its first child carrying the argmax)."""
+    rng = np.random.default_rng(8)
+    m, V = 9, 12
+    parents = np.array([-1, 0, 0, 1, 1, 2, 3, 3, 6])
+    tl = rng.normal(size=(m, V)) * 3
+    tokens = rng.integers(0, V, size=m)
+    for node in range(m):  # plant: some node's child carries the argmax
+        kids = [c for c in range(m) if parents[c] == node]
+        if kids and rng.random() < 0.8:
+            tokens[kids[-1]] = int(np.argmax(tl[node]))
+    u = np.random.default_rng(1).random(m + 1) * 0.98
+    a = O.verify_rejection_topk(tl, tokens, parents, 1e-3, u)
+    g = O.verify_greedy(tl, tokens, parents)
+    assert a[0] == g[0] and a[2] == g[2]

@@ -28,6 +28,7 @@ EAGLE_LEVEL_TAIL_ONLY = 1
 EAGLE_LEVEL_LMHEAD_ONLY = 2
 EAGLE_LEVEL_FULL_FC = 3
 EAGLE_MAX_DEPTH = 16
+EAGLE_NOALLOC_MAX_ROWS = 4096
 EAGLE_PACKED_WEIGHTS = 0x45505731
 
 (WS_ERROR, WS_POOL, WS_FRONTIER, WS_FEAT, WS_TREE_K, WS_TREE_V, WS_EXT_H, WS_X0, WS_ATTN,
@@ -116,6 +117,10 @@ def lib() -> ctypes.CDLL:
                                                       c_void_p, c_float, c_void_p, c_void_p,
                                                       c_void_p, c_void_p, c_void_p, c_size_t,
                                                       c_void_p]),
+            "eagle_verify_rejection_topk_noalloc": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p,
+                                                              c_void_p, c_void_p, c_float, c_void_p,
+                                                              c_void_p, c_void_p, c_void_p,
+                                                              c_void_p]),
             "eagle_verify_relaxed_scratch_bytes": (c_size_t, [P(EagleTreeCfg)]),
             "eagle_verify_relaxed": (c_int32, [P(EagleTreeCfg), c_int32, c_void_p, c_void_p,
                                                c_void_p, c_float, c_float, c_void_p,
@@ -282,6 +287,15 @@ def eagle_verify_rejection_topk(cfg, vocab, target_logits, tokens, parents, temp
                                              _ptr(uniforms), _ptr(accept_len), _ptr(accept_path),
                                              _ptr(bonus), _ptr(scratch), _nbytes(scratch),
                                              _stream(stream)), "eagle_verify_rejection_topk")
+
+
+def eagle_verify_rejection_topk_noalloc(cfg, vocab, target_logits, tokens, parents, temperature,
+                                        uniforms, accept_len, accept_path, bonus, stream=None) -> None:
+    _check(lib().eagle_verify_rejection_topk_noalloc(ctypes.byref(cfg), vocab, _ptr(target_logits),
+                                                     _ptr(tokens), _ptr(parents), float(temperature),
+                                                     _ptr(uniforms), _ptr(accept_len),
+                                                     _ptr(accept_path), _ptr(bonus), _stream(stream)),
+           "eagle_verify_rejection_topk_noalloc")
 
 
 def eagle_verify_relaxed_scratch_bytes(cfg) -> int:

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "skinny_core.h"
 
@@ -640,6 +641,59 @@ int eagle_verify_rejection_topk(const eagle_tree_cfg* cfg, int32_t vocab, const 
                                       temperature, 0.f, uniforms, scratch, accept_len, accept_path, bonus,
                                       (hipStream_t)stream, true),
                 "verify_rejection_topk");
+}
+
+// ---- eagle_verify_rejection_topk_noalloc: the scratch lives in a file-scope
+// device array (each device holds its own copy for the life of the process).
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is taken once per device with hipGetSymbolAddress and only
+// that address is passed to kernels.
+#define NOALLOC_SCRATCH_BYTES ((size_t)EAGLE_NOALLOC_MAX_ROWS * 16 * 8)
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+static std::mutex g_noalloc_mu;
+static void* g_noalloc_ptr[64];  // per device ordinal
+
+// the current device's address of `scratch` (null on failure, with the message set)
+static void* noalloc_scratch() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(EAGLE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    fail(EAGLE_ERR_UNSUPPORTED, "device ordinal %d (0..63)", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(EAGLE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_noalloc_ptr[dev] = ptr;
+  }
+  return g_noalloc_ptr[dev];
+}
+
+int eagle_verify_rejection_topk_noalloc(const eagle_tree_cfg* cfg, int32_t vocab, const float* target_logits,
+                                        const int32_t* tokens, const int32_t* parents, float temperature,
+                                        const float* uniforms, int32_t* accept_len, int32_t* accept_path,
+                                        int32_t* bonus, void* stream) {
+  int r;
+  if ((r = check_cfg(nullptr, cfg))) return r;
+  if ((long)cfg->batch * cfg->m > EAGLE_NOALLOC_MAX_ROWS)
+    return fail(EAGLE_ERR_UNSUPPORTED, "batch*m %d above the no-allocation limit %d", cfg->batch * cfg->m,
+                EAGLE_NOALLOC_MAX_ROWS);
+  const size_t need = verify_relaxed_scratch_bytes(cfg->batch, cfg->m);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(EAGLE_ERR_UNSUPPORTED, "scratch %zu above %zu bytes", need, NOALLOC_SCRATCH_BYTES);
+  void* ptr = noalloc_scratch();
+  if (!ptr) return EAGLE_ERR_HIP;
+  return eagle_verify_rejection_topk(cfg, vocab, target_logits, tokens, parents, temperature, uniforms, accept_len,
+                                     accept_path, bonus, ptr, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t eagle_verify_relaxed_scratch_bytes(const eagle_tree_cfg* cfg) {

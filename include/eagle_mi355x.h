@@ -371,6 +371,26 @@ int eagle_verify_rejection_topk(const eagle_tree_cfg *cfg, int32_t vocab, const 
                                 const float *uniforms, int32_t *accept_len, int32_t *accept_path,
                                 int32_t *bonus, void *scratch, size_t scratch_bytes, void *stream);
 
+/* eagle_verify_rejection_topk for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call without the scratch argument.  Its per-segment softmax
+ * statistics live in a device array inside the library, of
+ * EAGLE_NOALLOC_MAX_ROWS * 128 bytes (512 KB) on each device it runs on, kept
+ * until the process ends; the call allocates nothing (no hipMalloc or
+ * allocating library routine).  batch * m must be at most
+ * EAGLE_NOALLOC_MAX_ROWS, else EAGLE_ERR_UNSUPPORTED.  The array is found on
+ * the calling thread's current device, which must be the stream's.  Every
+ * call on a device shares that device's array: calls that overlap on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller.  Nothing in it needs to start at zero (every statistic is written
+ * before it is read).  Errors and outputs as for eagle_verify_rejection_topk,
+ * plus EAGLE_ERR_HIP if the array's address cannot be obtained. */
+#define EAGLE_NOALLOC_MAX_ROWS 4096
+int eagle_verify_rejection_topk_noalloc(const eagle_tree_cfg *cfg, int32_t vocab, const float *target_logits,
+                                        const int32_t *tokens, const int32_t *parents, float temperature,
+                                        const float *uniforms, int32_t *accept_len, int32_t *accept_path,
+                                        int32_t *bonus, void *stream);
+
 /* Relaxed acceptance ([P2] closing notes on SGLang's verification: the
  * target's probabilities and a probability threshold decide whether a token
  * is accepted; only when every candidate of a level fails is one

@@ -81,40 +81,52 @@ def stored_traffic(workload: str):
         return None
 
 
-def cpu_baseline(cfg, inp, budget_s: float) -> dict:
-    """The fp64 oracle, as it stands, on this host's cores: whole rounds of the
-    same workload until about budget_s seconds of work."""
-    import numpy as np
-    from oracle import eagle_oracle as O
+def blas_info() -> dict:
+    """The BLAS library NumPy runs on and its thread count."""
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
-                    default=1)
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
     except Exception:
-        cores = os.cpu_count() or 1
+        info = []
+    if not info:
+        return {"vendor": "unknown", "threads": os.cpu_count() or 1}
+    i = info[0]
+    return {"vendor": f"{i.get('internal_api', '?')} {i.get('version', '')}".strip(),
+            "threads": int(i.get("num_threads", 1))}
+
+
+def cpu_baseline(cfg, inp, budget_s: float) -> dict:
+    """The fp64 oracle, as it stands, on this host's cores: whole rounds of the
+    same workload until about budget_s seconds of work.  A batch is sampled by
+    sequence (one sequence-round at a time, in order); the rate is scaled to
+    the whole batch and then labelled extrapolated."""
+    import numpy as np
+    from oracle import eagle_oracle as O
+    blas = blas_info()
     model = O.Model(cfg, inp)
     W = lambda a: O.widen(a, cfg.dtype)
-    seqs = list(range(cfg.B))
-    tf = W(inp["true_feat"])
-    TL = inp["target_logits"].astype(np.float64)
     # widen the weights once, outside the timed region
     for n in ("fc_w", "wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "lm_head"):
         if model.raw[n].size <= model._CACHE_LIMIT:
             model.w(n)
-    rounds, t0 = 0, time.perf_counter()
+    done, t0 = 0, time.perf_counter()
     while True:
-        for b in seqs:
-            st = O.SeqState(W(inp["k_cache"][b]), W(inp["v_cache"][b]), int(inp["prefix_len"][b]),
-                            W(inp["root_feat"][b]), int(inp["root_token"][b]))
-            O.run_round(model, st, tf[b], TL[b])
-        rounds += 1
+        b = done % cfg.B
+        st = O.SeqState(W(inp["k_cache"][b]), W(inp["v_cache"][b]), int(inp["prefix_len"][b]),
+                        W(inp["root_feat"][b]), int(inp["root_token"][b]))
+        O.run_round(model, st, W(inp["true_feat"][b]), inp["target_logits"][b].astype(np.float64))
+        done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or rounds >= 50:
+        if el >= budget_s or done >= 50 * cfg.B:
             break
-    return {"value": rounds / el, "unit": "rounds/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rounds} whole round(s) of the same workload ({cfg.B} sequence(s)), "
-                      f"{el:.1f} s, fp64 NumPy"}
+    rounds = done / cfg.B
+    out = {"value": rounds / el, "unit": "rounds/s", "cores": blas["threads"], "kind": "oracle",
+           "blas": blas["vendor"], "blas_threads": blas["threads"], "host_cpus": os.cpu_count(),
+           "sample": f"{done} sequence-round(s) of the same workload ({cfg.B} sequence(s) per round), "
+                     f"{el:.1f} s, fp64 NumPy"}
+    if done % cfg.B:
+        out["extrapolated"] = True
+    return out
 
 
 def batched_lmhead(torch, L, dev, stream, rows=512, vocab=128256, d=4096, reps=10) -> dict:
@@ -328,6 +340,216 @@ def static_round(torch, r, cfg, stream, saved_plen, rounds=50) -> dict:
             "timing": f"{rounds} rounds from a graph of {per}, wall clock"}
 
 
+def rejection_topk_verify(torch, L, r, cfg, stream, reps=50, replays=10) -> dict:
+    """Rejection sampling of deterministic candidates (the draft's top-k
+    children as point-mass proposals) at the round's shape, on the tree the
+    round just built and the round's target logits, random uniforms.  Timed
+    like the tree-verify attention."""
+    gen = torch.Generator(device=r.device)
+    gen.manual_seed(4)
+    uni = torch.rand(cfg.B, cfg.m + 1, generator=gen, device=r.device, dtype=torch.float32)
+    call = lambda: L.eagle_verify_rejection_topk(r.tcfg, cfg.V, r.target_logits, r.tokens, r.parents, 1.0, uni,
+                                                 r.accept_len, r.accept_path, r.bonus, r._rv_scratch, stream)
+    us = _graph_time(torch, call, stream, reps, replays)
+    return {"kernel": "k_relaxed_stats + k_verify_relaxed<topk>", "bound": "latency", "us_per_call": round(us, 2),
+            "accept_len": [int(a) for a in r.accept_len.cpu().numpy()], "temperature": 1.0,
+            "timing": f"HIP events around {replays} replays of a graph of {reps} back-to-back calls"}
+
+
+def _graph_time(torch, call, stream, reps, replays) -> float:
+    """Microseconds per call: `reps` calls captured in a graph, two untimed
+    replays, then `replays` replays between two HIP events on `stream`."""
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(reps):
+            call()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * replays)
+
+
+def copy_bandwidth(torch, dev, stream, nbytes=1 << 30, reps=10) -> dict:
+    """Device copy rate: a 1 GiB buffer copied `reps` times between HIP events;
+    read plus written bytes over the time."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    gbps = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbps": round(gbps, 1), "bytes_copied": nbytes, "timing": f"{reps} copies of 1 GiB between HIP events"}
+
+
+def measure_rounds(torch, r, stream, steps, warmup, graph=True) -> dict:
+    """Whole rounds on the synthetic batch: R consecutive rounds per HIP graph
+    (R the largest divisor of the step count up to 10; every round runs
+    whole, and one graph launch's host latency is paid per R rounds), warm-up,
+    then exactly `steps` rounds between two synchronisations (the wall-clock
+    rate), each replay also bracketed by HIP events (the per-round spread).
+    Between rounds the prefix length is restored on the device so that every
+    round has the same shape; the root feature and token advance."""
+    import numpy as np
+    saved_plen = r.prefix_len.clone()
+
+    def one_round():
+        r.run_round(stream=stream)
+        torch.add(saved_plen, 0, out=r.prefix_len)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        one_round()   # eager round: loads code objects, checks the path runs
+    torch.cuda.synchronize()
+    per = max(q for q in range(1, 11) if steps % q == 0) if graph else 1
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(per):
+                one_round()
+        torch.cuda.synchronize()
+        run = g.replay
+    else:
+        def run():
+            one_round()
+    for _ in range(-(-warmup // per)):
+        with torch.cuda.stream(stream):
+            run()
+    torch.cuda.synchronize()
+    n = steps // per
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for e0, e1 in ev:
+            e0.record(stream)
+            run()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    per_round = np.array([e0.elapsed_time(e1) / per for e0, e1 in ev])
+    out = {"rounds_per_s": steps / el, "ms_per_round": el * 1e3 / steps, "rounds_per_graph": per,
+           "replays": n, "saved_plen": saved_plen}
+    if n >= 1:
+        out["round_ms"] = {"p10": round(float(np.percentile(per_round, 10)), 4),
+                           "median": round(float(np.median(per_round)), 4),
+                           "p90": round(float(np.percentile(per_round, 90)), 4),
+                           "timing": f"HIP events around each of {n} graph replays of {per} rounds"}
+    return out
+
+
+def lmhead_roofline(torch, L, r, cfg, stream, steps, scrub) -> dict:
+    """The dominant kernel, the LM-head GEMM with its fused per-slab softmax
+    and top-k, timed live on the stream it runs on: a LMHEAD_ONLY level call
+    launches exactly that one kernel, and the timed variant has the kernel's
+    own dispatch stamp a pair of HIP events at its start and end.  A second
+    pair of ordinary events, queued around the same call, shows what queue
+    markers add.  Between launches a 512 MiB read (a reduction, outside the
+    events) evicts the 256 MB memory-side Infinity Cache, which would
+    otherwise keep part of the LM head warm across back-to-back launches;
+    inside a round the layer weights stream through it in between.  A read,
+    not a copy: a copy's dirty lines would be written back during the timed
+    launch."""
+    import numpy as np
+    scrub_out = torch.empty((), dtype=torch.float32, device=r.device)
+    n_lm = max(5, steps // 5) * (cfg.D - 1)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_lm)]
+    with torch.cuda.stream(stream):
+        for q in ev:            # torch creates events on their first record
+            for e in q:
+                e.record(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i, (m0, k0, k1, m1) in enumerate(ev):
+            torch.sum(scrub, dim=0, out=scrub_out)
+            m0.record(stream)
+            r.level_timed(2 + i % (cfg.D - 1), L.EAGLE_LEVEL_LMHEAD_ONLY, k0, k1, stream=stream)
+            m1.record(stream)
+    torch.cuda.synchronize()
+    lm_ms = float(np.mean([k0.elapsed_time(k1) for _, k0, k1, _ in ev]))
+    lm_marker_ms = float(np.mean([m0.elapsed_time(m1) for m0, _, _, m1 in ev]))
+    es = 2 if cfg.dtype == "bf16" else 4
+    nbytes = es * cfg.V * cfg.d
+    rows = cfg.B * cfg.k
+    gbps = nbytes / (lm_ms * 1e-3) / 1e9
+    kernel = ("k_lmskinny" if rows <= 16 else "k_lmhead" if rows <= 64 or cfg.dtype != "bf16" else
+              "k_lg_xpack + k_lmgemm")
+    return {"kernel": f"{kernel} (LM-head GEMM + per-slab softmax/top-k, {rows} rows)",
+            "scope": "the round's dominant kernel (the largest share of a round's time)",
+            "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(lm_ms * 1e3, 2),
+            "timing": f"{n_lm} launches, HIP events stamped by the kernel's dispatch "
+                      f"(hipExtLaunchKernel); queued marker events around the same launches: "
+                      f"{lm_marker_ms * 1e3:.2f} us",
+            "bytes_per_launch": int(nbytes),
+            "mfma_frac": round(2.0 * rows * cfg.V * cfg.d / (lm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def workload_name(cfg) -> str:
+    return (f"EAGLE-2 draft round, {cfg.name}-shaped draft head, {cfg.dtype}, batch {cfg.B}, "
+            f"d {cfg.d}, heads {cfg.H}/{cfg.Hkv}x{cfg.hd}, ffn {cfg.F}, vocab {cfg.V}, "
+            f"prefix {cfg.P_lo}-{cfg.P_hi}, depth {cfg.D}, topk {cfg.k}, m {cfg.m}")
+
+
+def round_hbm(cfg, rounds_s, copy_gbps) -> dict:
+    ab = algorithmic_bytes(cfg)
+    nbytes = ab["layer_weights"] + ab["lm_head"] + ab["prefix_kv"] + ab["verify_rows"]
+    gbps = nbytes * rounds_s / 1e9
+    out = {"algorithmic_bytes": int(nbytes), "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+           "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    if copy_gbps:
+        out["copy_gbps"] = copy_gbps
+        out["frac_of_copy"] = round(gbps / copy_gbps, 4)
+    return out
+
+
+def other_config(torch, L, name, dev, stream, seed, steps, warmup, cpu_budget, copy_gbps, scrub) -> dict:
+    """One more workload of the benchmark table: rounds/s, tree tokens/s, the
+    round's share of the HBM roofline, the LM head's roofline, and the oracle
+    on a sample of its sequences."""
+    import synth
+    from eagle_draft_trees_amd.round import DraftRound
+    cfg = synth.config_by_name(name)
+    inp = synth.make_inputs(cfg, seed=seed)
+    r = DraftRound(cfg, inp, dev)
+    m = measure_rounds(torch, r, stream, steps, warmup)
+    out = {"workload": workload_name(cfg), "rounds_per_s": round(m["rounds_per_s"], 2),
+           "ms_per_round": round(m["ms_per_round"], 4), "round_ms": m.get("round_ms"),
+           "rounds_timed": steps, "rounds_per_graph": m["rounds_per_graph"],
+           "tree_tokens_per_s": round(m["rounds_per_s"] * cfg.B * cfg.m, 1)}
+    if cfg.dtype == "bf16":
+        out["round_hbm"] = round_hbm(cfg, m["rounds_per_s"], copy_gbps)
+        out["lmhead_roofline"] = lmhead_roofline(torch, L, r, cfg, stream, steps, scrub)
+    else:
+        out["note"] = ("fp32 and about 12 MB of weights: the round lives in the 256 MB Infinity Cache and "
+                       "is bound by launch latency, not HBM")
+    del r
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, cpu_budget)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +562,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the batched LM-head GEMM measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads of the table (13b, 70b, chain, tiny)")
+    ap.add_argument("--configs-cpu-budget", type=float, default=8.0)
     ap.add_argument("--lmhead-only", type=int, default=0,
                     help="only launch the LM-head kernel this many times (counter runs)")
     args = ap.parse_args()
@@ -349,7 +574,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import synth
@@ -357,14 +581,11 @@ def main() -> int:
     from eagle_draft_trees_amd.round import DraftRound
 
     cfg = synth.config_by_name(args.config)
-    # KV room for one extend per round: the prefix length is restored each round
     inp = synth.make_inputs(cfg, seed=args.seed)
     dev = torch.device("cuda:0")
     r = DraftRound(cfg, inp, "cuda:0")
     stream = torch.cuda.Stream(device=dev)
-    workload = (f"EAGLE-2 draft round, {cfg.name}-shaped draft head, {cfg.dtype}, batch {cfg.B}, "
-                f"d {cfg.d}, heads {cfg.H}/{cfg.Hkv}x{cfg.hd}, ffn {cfg.F}, vocab {cfg.V}, "
-                f"prefix {cfg.P_lo}-{cfg.P_hi}, depth {cfg.D}, topk {cfg.k}, m {cfg.m}")
+    workload = workload_name(cfg)
 
     if args.lmhead_only:
         # counter runs: a copy of known size (calibration), then the LM head alone
@@ -381,77 +602,12 @@ def main() -> int:
         print(json.dumps({"lmhead_only": args.lmhead_only, "copy_bytes": src.numel()}))
         return 0
 
-    saved_plen = r.prefix_len.clone()
-
-    def one_round():
-        r.run_round(stream=stream)
-        torch.add(saved_plen, 0, out=r.prefix_len)
-
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        one_round()   # eager round: loads code objects, checks the path runs
-    torch.cuda.synchronize()
-    # R consecutive rounds per graph (R the largest divisor of the step count up
-    # to 10): every round still runs whole, and one graph launch's host latency
-    # is paid per R rounds instead of per round
-    per = max(r_ for r_ in range(1, 11) if args.steps % r_ == 0) if not args.no_graph else 1
-    if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for _ in range(per):
-                one_round()
-        torch.cuda.synchronize()
-        run = g.replay
-    else:
-        def run():
-            with torch.cuda.stream(stream):
-                one_round()
-
-    for _ in range(-(-args.warmup // per)):
-        run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps // per):
-        run()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms = el * 1e3 / args.steps
-    rounds_s = args.steps / el
-
-    # dominant kernel (the LM-head GEMM with its fused per-slab softmax and
-    # top-k), timed live on the stream it runs on: a LMHEAD_ONLY level call
-    # launches exactly that one kernel, and the timed variant has the kernel's
-    # own dispatch stamp a pair of HIP events at its start and end.  A second
-    # pair of ordinary events, queued around the same call, shows what queue
-    # markers add.
-    # Between launches a 512 MiB read (a reduction, outside the events) evicts
-    # the 256 MB memory-side Infinity Cache, which would otherwise keep part of
-    # the 262 MB LM head warm across back-to-back launches; inside a round the
-    # layer weights stream through it in between.  A read, not a copy: a
-    # copy's dirty lines would be written back during the timed launch.
+    m = measure_rounds(torch, r, stream, args.steps, args.warmup, graph=not args.no_graph)
+    rounds_s = m["rounds_per_s"]
     scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    scrub_out = torch.empty((), dtype=torch.float32, device=dev)
-    n_lm = max(5, args.steps // 5) * (cfg.D - 1)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_lm)]
-    with torch.cuda.stream(stream):
-        for q in ev:            # torch creates events on their first record
-            for e in q:
-                e.record(stream)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for i, (m0, k0, k1, m1) in enumerate(ev):
-            torch.sum(scrub, dim=0, out=scrub_out)
-            m0.record(stream)
-            r.level_timed(2 + i % (cfg.D - 1), L.EAGLE_LEVEL_LMHEAD_ONLY, k0, k1, stream=stream)
-            m1.record(stream)
-    torch.cuda.synchronize()
-    lm_ms = float(np.mean([k0.elapsed_time(k1) for _, k0, k1, _ in ev]))
-    lm_marker_ms = float(np.mean([m0.elapsed_time(m1) for m0, _, _, m1 in ev]))
-    ab = algorithmic_bytes(cfg)
-    lm_gbps = ab["lm_head_per_launch"] / (lm_ms * 1e-3) / 1e9
-    traffic = stored_traffic(workload)
-    round_bytes = ab["layer_weights"] + ab["lm_head"] + ab["prefix_kv"] + ab["verify_rows"]
-    round_gbps = round_bytes * rounds_s / 1e9
+    roof = lmhead_roofline(torch, L, r, cfg, stream, args.steps, scrub)
+    roof["traffic"] = stored_traffic(workload)
+    copy = copy_bandwidth(torch, dev, stream)
 
     out = {
         "metric": "EAGLE-2 draft-tree rounds/s + tree tokens/s at 7B shape; % HBM roofline",
@@ -460,7 +616,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(m["ms_per_round"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -468,29 +624,36 @@ def main() -> int:
         "data": "synthetic (seeded; weights N(0,0.02^2), LM head N(0,1)*3/sqrt(d), features N(0,1), "
                 "target logits N(0,9))",
         "config": {"workload": workload, "batch": cfg.B, "tree_tokens_per_round": cfg.B * cfg.m,
-                   "graph": not args.no_graph, "rounds_per_graph": per},
+                   "graph": not args.no_graph, "rounds_per_graph": m["rounds_per_graph"]},
         "tree_tokens_per_s": round(rounds_s * cfg.B * cfg.m, 1),
-        "round_hbm": {"algorithmic_bytes": int(round_bytes), "achieved": round(round_gbps, 1),
-                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(round_gbps / HBM_PEAK_GBPS, 4)},
-        "roofline": {"kernel": "k_lmskinny (LM-head GEMM + per-slab softmax/top-k)",
-                     "bound": "hbm", "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
-                     "avg_launch_us": round(lm_ms * 1e3, 2),
-                     "timing": f"{n_lm} launches, HIP events stamped by the kernel's dispatch "
-                               f"(hipExtLaunchKernel); queued marker events around the same "
-                               f"launches: {lm_marker_ms * 1e3:.2f} us",
-                     "bytes_per_launch": int(ab["lm_head_per_launch"]),
-                     "traffic": traffic},
+        "round_ms": m.get("round_ms"),
+        "round_hbm": round_hbm(cfg, rounds_s, copy["gbps"]),
+        "roofline": roof,
+        "hbm_copy": copy,
     }
     out["tree_verify_attention"] = tree_verify(torch, L, r, cfg, stream)
     out["relaxed_verify"] = relaxed_verify(torch, L, r, cfg, stream)
     out["rejection_verify"] = rejection_verify(torch, L, r, cfg, stream)
+    out["rejection_topk_verify"] = rejection_topk_verify(torch, L, r, cfg, stream)
     if 1 + cfg.D * cfg.k >= cfg.m:
-        out["static_round"] = static_round(torch, r, cfg, stream, saved_plen)
+        out["static_round"] = static_round(torch, r, cfg, stream, m["saved_plen"])
+    del r
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_batched:
         out["mfma_batched_lmhead"] = batched_lmhead(torch, L, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    if not args.no_configs:
+        others = {}
+        for name in ("tiny", "13b", "70b", "chain"):
+            if name == args.config:
+                continue
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            others[name] = other_config(torch, L, name, dev, stream, args.seed, 20, 5,
+                                        0.0 if args.no_cpu_baseline else args.configs_cpu_budget,
+                                        copy["gbps"], scrub)
+        out["configs"] = others
     print(json.dumps(out), flush=True)
     return 0
 

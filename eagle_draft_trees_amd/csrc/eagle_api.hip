@@ -109,15 +109,40 @@ static inline bool use_skinny(int mode, int rows) {
   return (mode == MODE_LEVEL || mode == MODE_EXTEND) && rows <= 16;
 }
 
+// compute units of the current device (cached per device ordinal; 256 when
+// the query fails)
+static int device_cus() {
+  static std::mutex mu;
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cus[dev]) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
 // FC hand-over (levels of at most 16 rows): level L's merge launch computes
 // the FC of level L+1.  Returns false when the configuration keeps the FC in
 // each level's own call.  *fp: the FC plan over the M rows of level L (B at
-// level 1, B*k after), its waves raised to cover the merge's.
+// level 1, B*k after), its waves raised to cover the merge's.  Its workgroups
+// wait for the merges, so all of them and the merges must be resident at
+// once: one workgroup per compute unit at most (a workgroup of that many
+// waves fills one), more column tiles per workgroup where needed.
 static bool handover_plan(const eagle_dims& d, const eagle_tree_cfg& c, int level, SkPlan* fp) {
   const int R = c.batch * c.topk;
   if (R > 16) return false;
   const int M = level == 1 ? c.batch : R;
   SkPlan p = plan_skinny(OP_FC, M, d);
+  const int nseq = c.batch, ncu = device_cus();
+  if (nseq + p.nwg > ncu) {
+    while (p.CT < SK_MAXW && nseq + cdiv(p.ntile, p.CT) > ncu) ++p.CT;
+    p.KSW = SK_MAXW / p.CT;  // every wave the compute unit holds: the K slices stay short
+    p.nwg = cdiv(p.ntile, p.CT);
+    if (nseq + p.nwg > ncu) return false;
+  }
   const int mwaves = level == 1 ? 1 : c.topk;  // merge waves of the launch
   const int ksw = std::max(p.KSW, cdiv(mwaves, p.CT));
   if (p.CT * ksw > SK_MAXW) return false;

@@ -17,6 +17,9 @@ constexpr int WAVE = 64;
 constexpr int BLOCK = 256;       // four waves
 constexpr int NCNT = 1 << 16;    // last-block counters in the workspace
 constexpr int GRID_CNT = NCNT - 1;
+// FC hand-over: counter 1 counts the workgroups that have read the mailbox,
+// whose 16 64-bit entries sit at counters CNT_MBOX..CNT_MBOX+31
+constexpr int CNT_MBOX = 128;
 constexpr int GEMM_MAXS = 64;    // split-K ways at most
 constexpr int GW_KSW = 4;                   // layer GEMM workgroup: 4 column tiles x GW_KSW K slices
 constexpr int GW_THREADS = 4 * GW_KSW * 64;
@@ -148,6 +151,82 @@ __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k)
   else
     ml = wave_max_u32(hi == mh ? (unsigned)k : 0u);
   return ((unsigned long long)mh << 32) | ml;
+}
+
+// The k largest of the wave's 64-bit keys (N per lane, unique, 0 = empty),
+// sorted: lane j < k receives the j-th largest, 0 past the number of keys.
+// k <= 16.  Instead of k dependent rounds of a wave argmax:
+//  1. threshold: each lane's largest key; the k-th largest of those 64 lane
+//     maxima (ranked by counting against all of them, read back from LDS) is
+//     a key with at least k - 1 keys above it, so every key of the top k is
+//     at or above it (with fewer than k non-empty lanes, every key counts);
+//  2. the keys at or above the threshold -- at most k*N, from the lanes whose
+//     maximum ranked below k -- are packed into LDS;
+//  3. each packed key is ranked by counting the packed keys above it, and the
+//     first k are placed at their rank.
+// `sh`: 128 words of LDS owned by the wave.
+__device__ __forceinline__ unsigned lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+template <int N>
+__device__ __forceinline__ unsigned long long wave_topk(const unsigned long long (&key)[N], int k,
+                                                        unsigned long long* sh) {
+  static_assert(N <= 4, "at most 4 keys per lane (k*N <= 64 packed keys)");
+  const int lane = (int)lane_id();
+  unsigned long long lm = key[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) lm = key[e] > lm ? key[e] : lm;
+  sh[lane] = lm;
+  __builtin_amdgcn_wave_barrier();
+  int r = 0;  // rank of this lane's maximum among the lane maxima
+#pragma unroll
+  for (int i = 0; i < WAVE; i += 8) {  // four 16-byte broadcast reads in flight at a time
+    ulonglong2 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *(const ulonglong2*)(sh + i + 2 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r += (v[j].x > lm ? 1 : 0) + (v[j].y > lm ? 1 : 0);
+    asm volatile("" : "+v"(r)::"memory");  // this batch is used before the next is read
+  }
+  const unsigned long long nzl = __ballot(lm != 0ull);
+  const int nl = __popcll(nzl);
+  unsigned long long tau = 1ull;  // fewer than k non-empty lanes: every key
+  if (nl >= k) {
+    const unsigned long long at = __ballot(lm != 0ull && r == k - 1);
+    const int l = __ffsll((long long)at) - 1;
+    tau = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(lm >> 32), l) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)lm, l);
+  }
+  // pack the keys >= tau into sh[64..64+nc)
+  int nc = 0;
+  unsigned long long* pk = sh + WAVE;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const bool in = key[e] != 0ull && key[e] >= tau;
+    const unsigned long long m = __ballot(in);
+    if (in) pk[nc + __popcll(m & ((1ull << lane) - 1ull))] = key[e];
+    nc += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // rank the packed keys (nc <= 64): lane l holds packed key l
+  const unsigned long long c = lane < nc ? pk[lane] : 0ull;
+  int rk = 0;
+  for (int i = 0; i < nc; i += 8) {  // pk[nc..i+7] (within pk[0..63]) may be stale: masked
+    ulonglong2 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *(const ulonglong2*)(pk + i + 2 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      rk += ((i + 2 * j < nc && v[j].x > c) ? 1 : 0) + ((i + 2 * j + 1 < nc && v[j].y > c) ? 1 : 0);
+    asm volatile("" : "+v"(rk)::"memory");
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < nc && rk < k) sh[rk] = c;
+  __builtin_amdgcn_wave_barrier();
+  const unsigned long long out = lane < min(k, nc) ? sh[lane] : 0ull;
+  __builtin_amdgcn_wave_barrier();
+  return out;
 }
 
 __device__ __forceinline__ float wave_sum_dpp(float v) {

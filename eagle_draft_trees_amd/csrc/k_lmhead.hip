@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
 // tiles (one slab of CT*16 columns) and splits K over KSW waves per tile; X
 // (the rows' features) is staged in LDS when it fits.  The slab's logits meet
 // in LDS and one wave per row reduces them to the slab record (max, sum exp,
-// top-k by (logit desc, id asc) from k rounds of a 64-bit key argmax).
+// top-k by (logit desc, id asc) from a wave top-k over 64-bit keys).
 template <typename T, bool XL>
 __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan p, int level) {
   constexpr int KS = El<T>::KSTEP;
@@ -207,6 +207,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
   __syncthreads();
 
   // one wave per row: up to four columns per lane
+  __shared__ __attribute__((aligned(16))) unsigned long long s_tk[SK_MAXW][2 * WAVE];  // wave_topk scratch
   const int col0 = blockIdx.x * ncol;
   for (int row = wave; row < p.M; row += nwv) {
     float x[4];
@@ -229,17 +230,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
       rec[0] = mx;
       rec[p.nblk] = se;
     }
-    unsigned long long mine = 0ull;  // lane r: the r-th entry
-    for (int r = 0; r < kk_; ++r) {
-      unsigned long long best = 0ull;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) best = key[u] > best ? key[u] : best;
-      const unsigned long long win = wave_max_key(best);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (key[u] == win) key[u] = 0ull;  // keys are unique: one owner
-      if (lane == r) mine = win;
-    }
+    const unsigned long long mine = wave_topk<4>(key, kk_, s_tk[wave]);  // lane r: the r-th entry
     if (lane < kk_) {
       rec[(2 + lane) * p.nblk] = mine ? argkey_value(mine) : -INFINITY;
       rec[(2 + kk_ + lane) * p.nblk] = __int_as_float(mine ? argkey_id(mine) : -1);

@@ -28,24 +28,28 @@ namespace eg {
 // Merge of the slab records, one workgroup per sequence and one wave per row.
 // Each slab's list is sorted, so the row's top-k lies in the k slabs whose
 // heads are the k largest (any other slab has k heads above all its entries):
-// k argmax rounds over the slab heads pick those slabs, k more over their k*k
-// entries give the row's top-k.  All rows of a sequence meet in the same
+// a wave top-k over the slab heads picks those slabs (k argmax rounds when
+// the heads do not fit four per lane), another over their k*k entries gives
+// the row's top-k.  All rows of a sequence meet in the same
 // workgroup, so the expansion that follows needs no cross-workgroup election.
 // NH > 0: each lane keeps its (at most NH) slab heads in registers; NH == 0:
 // in LDS (long vocabularies).
 constexpr int MG_LDS = 64 * 1024;  // slab head keys of the rows in flight (NH == 0)
 
-// Publication of a merge workgroup's results to the FC hand-over workgroups of
-// the same launch: wave 0 alone wrote the pool and frontier records they
-// read; its stores complete, one release at agent scope (the hand-over
-// workgroups may sit on other XCDs, whose L2s are not coherent with this
-// one), then the count of published sequences goes up.
-__device__ __forceinline__ void publish_merge(int* ready) {
-  __builtin_amdgcn_s_waitcnt(0);
-  if ((threadIdx.x & 63) == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+// Publication of the next level's rows to the FC hand-over workgroups of the
+// same launch: one 64-bit mailbox entry per next-level row, (parent row + 1)
+// in the high word and (token + 1) in the low word, so that 0 means "not yet
+// written".  Each entry is a single agent-scope atomic store (it is written
+// through to where the hand-over workgroups, possibly on other XCDs, read it
+// with agent-scope atomic loads), and it carries everything they need: the
+// pool and frontier records are for the next launches, which the kernel
+// boundary orders.  The entry goes out as soon as the row's child is chosen.
+__device__ __forceinline__ unsigned long long* mailbox(const RoundArgs& a) {
+  return (unsigned long long*)(a.cnt + CNT_MBOX);
+}
+__device__ __forceinline__ void post_row(const RoundArgs& a, int row, int prow, int tok) {
+  const unsigned long long e = ((unsigned long long)(uint32_t)(prow + 1) << 32) | (uint32_t)(tok + 1);
+  __hip_atomic_store(mailbox(a) + row, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // mwv: waves that take rows (the block may hold more, which only pass the
@@ -57,6 +61,7 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
   __shared__ int sanc[EAGLE_MAX_TOPK * EAGLE_MAX_DEPTH];
   __shared__ float psc[EAGLE_MAX_TOPK];
   __shared__ int ppi[EAGLE_MAX_TOPK];
+  __shared__ __attribute__((aligned(16))) unsigned long long s_tk[SK_MAXW][2 * WAVE];  // wave_topk scratch
   constexpr int NL = NH > 0 ? NH : 4;  // slabs per lane per load batch
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -131,22 +136,28 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
     // the k slabs with the largest heads (a head's slab follows from its
     // token id): lane j ends up holding the j-th
     int mysel = 0, nsel = 0;
-    for (; nsel < kk_; ++nsel) {
-      const unsigned long long win = wave_max_key(best);
-      if (win == 0ull) break;
-      if (lane == nsel) mysel = argkey_id(win) / swidth;
-      if (NH > 0) {
-        best = 0ull;
+    if constexpr (NH == 4) {
+      const unsigned long long w = wave_topk<4>(hkey, kk_, s_tk[wave]);
+      nsel = __popcll(__ballot(w != 0ull));
+      mysel = w ? argkey_id(w) / swidth : 0;
+    } else {
+      for (; nsel < kk_; ++nsel) {
+        const unsigned long long win = wave_max_key(best);
+        if (win == 0ull) break;
+        if (lane == nsel) mysel = argkey_id(win) / swidth;
+        if (NH > 0) {
+          best = 0ull;
 #pragma unroll
-        for (int u = 0; u < (NH > 0 ? NH : 1); ++u) {
-          hkey[u] = hkey[u] == win ? 0ull : hkey[u];  // keys are unique: one owner
-          best = hkey[u] > best ? hkey[u] : best;
-        }
-      } else if (best == win) {  // the owner's next head: the best of its slabs below win
-        best = 0ull;
-        for (int bb = lane; bb < nblk; bb += WAVE) {
-          const unsigned long long kv = hkw[bb];
-          best = (kv < win && kv > best) ? kv : best;
+          for (int u = 0; u < (NH > 0 ? NH : 1); ++u) {
+            hkey[u] = hkey[u] == win ? 0ull : hkey[u];  // keys are unique: one owner
+            best = hkey[u] > best ? hkey[u] : best;
+          }
+        } else if (best == win) {  // the owner's next head: the best of its slabs below win
+          best = 0ull;
+          for (int bb = lane; bb < nblk; bb += WAVE) {
+            const unsigned long long kv = hkw[bb];
+            best = (kv < win && kv > best) ? kv : best;
+          }
         }
       }
     }
@@ -163,16 +174,7 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
         key[t] = id < 0 ? 0ull : argkey(rc[(2 + e) * nblk], id);
       }
     }
-    unsigned long long mine = 0ull;  // lane q: the row's q-th entry
-    for (int q = 0; q < kk_; ++q) {
-      unsigned long long bk = 0ull;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bk = key[t] > bk ? key[t] : bk;
-      const unsigned long long win = wave_max_key(bk);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) key[t] = key[t] == win ? 0ull : key[t];
-      if (lane == q) mine = win;
-    }
+    const unsigned long long mine = wave_topk<4>(key, kk_, s_tk[wave]);  // lane q: the row's q-th entry
     const int myid = mine ? argkey_id(mine) : 0;
     const float lp = (mine ? argkey_value(mine) : -INFINITY) - lse;
     if (lane < kk_) {
@@ -182,6 +184,7 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
       sres[r * 2 * kk_ + lane] = __int_as_float(myid);
       sres[r * 2 * kk_ + kk_ + lane] = lp;
     }
+    if (level == 1 && pub && lane < kk_) post_row(a, b * kk_ + lane, b, myid);
     if (level == 1 && lane < kk_) {  // the root's k children: pool and frontier
       eagle_pool_entry* pool = a.pool + (size_t)b * a.pool_n;
       eagle_frontier_node* fnew = a.frontier + ((size_t)1 * a.B + b) * kk_;
@@ -196,10 +199,7 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
       fnew[lane] = nd;
     }
   }
-  if (level == 1) {  // one row per sequence: wave 0 wrote its pool and frontier
-    if (pub && wave == 0) publish_merge(a.cnt);
-    return;
-  }
+  if (level == 1) return;  // one row per sequence: its wave wrote the pool and frontier
 
   // ---- expansion and select (levels >= 2): wave 0 scores the k*k children
   // (parent score + log p), appends all of them to the pool in (frontier
@@ -251,18 +251,13 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
       csc = psc[pj] + sres[pj * 2 * kk_ + kk_ + rk];  // the same sum as the candidate's key
     }
   } else {
-    unsigned long long mine = 0ull;
-    for (int jn = 0; jn < kk_; ++jn) {
-      unsigned long long bk = 0ull;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bk = key[t] > bk ? key[t] : bk;
-      const unsigned long long win = wave_max_key(bk);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) key[t] = key[t] == win ? 0ull : key[t];
-      if (lane == jn) mine = win;
-    }
+    const unsigned long long mine = wave_topk<4>(key, kk_, s_tk[0]);
     cw = mine ? argkey_id(mine) : -1;
     csc = mine ? argkey_value(mine) : 0.f;
+  }
+  if (pub && lane < kk_) {  // (cw < 0 cannot happen: k*k >= k candidates)
+    const int j = cw >= 0 ? cw / kk_ : 0;
+    post_row(a, b * kk_ + lane, b * kk_ + j, cw >= 0 ? __float_as_int(sres[j * 2 * kk_ + (cw - j * kk_)]) : 0);
   }
   if (lane < kk_ && cw >= 0) {
     const int j = cw / kk_;
@@ -280,7 +275,6 @@ __device__ __forceinline__ void merge_body(const RoundArgs& a, const LmPlan& p, 
       fnew[jn].anc[i] = i < level - 1 ? sanc[j * EAGLE_MAX_DEPTH + i] : (i == level - 1 ? jn : 0);
     }
   }
-  if (pub) publish_merge(a.cnt);
 }
 
 // FC hand-over ([P1] §4.1 input equation: the next level's row is [feature of
@@ -327,36 +321,35 @@ __device__ __forceinline__ void fc_handover(const RoundArgs& a, const SkPlan& fp
     for (int r = 0; r < 4; ++r) fs[(ct * 16 + 4 * g + r) * 16 + c] = v[r];
   }
 
-  // wait until every merge of the launch has published the next frontier
+  // wait until the mailbox holds every next-level row (wave 0: lane r polls
+  // entry r), then take the rows' parent and token from it
   __shared__ int s_tok[16], s_prow[16];
-  if (tid == 0) {
-    int spins = 0;
-    while (__hip_atomic_load(a.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nseq) {
-      if (++spins > HANDOVER_SPINS) {
-        atomicOr(a.err, ERR_SYNC);
+  const int R = a.B * a.k;  // the next level's rows (at most 16)
+  if (wave == 0) {
+    unsigned long long e = 0ull;
+    for (int spins = 0;; ++spins) {
+      if (lane < R) e = __hip_atomic_load(mailbox(a) + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__ballot(lane < R && e == 0ull) == 0ull) break;
+      if (spins > HANDOVER_SPINS) {
+        if (lane == 0) atomicOr(a.err, ERR_SYNC);
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (lane < R) {
+      const int b = lane / a.k;
+      const int prow = (int)(uint32_t)(e >> 32) - 1, tok = (int)(uint32_t)e - 1;
+      s_tok[lane] = clamp_tok(tok, a.V, a.err);
+      s_prow[lane] = level == 1 ? b : b * a.k + clamp_slot(prow - b * a.k, a.k);
+    }
   }
   __syncthreads();
-  const int R = a.B * a.k;  // the next level's rows (at most 16)
-  if (tid < R) {
-    const int b = tid / a.k, jn = tid - b * a.k;
-    eagle_frontier_node* nd = a.frontier + ((size_t)level * a.B + b) * a.k + jn;
-    const int tok = __hip_atomic_load(&nd->token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int ps = __hip_atomic_load(&nd->pslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_tok[tid] = clamp_tok(tok, a.V, a.err);
-    s_prow[tid] = level == 1 ? b : b * a.k + clamp_slot(ps, a.k);
-  }
-  __syncthreads();
-  // every hand-over workgroup has passed its wait once `seen` counts them all:
-  // the last one leaves both counters at zero for the next launch
+  // every hand-over workgroup has read the mailbox once `seen` counts them
+  // all: the last one clears the entries and the count for the next launch
   if (tid == 0) {
     const int prev = __hip_atomic_fetch_add(a.cnt + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == fp.nwg - 1) {
-      __hip_atomic_store(a.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int r = 0; r < R; ++r) __hip_atomic_store(mailbox(a) + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

@@ -140,50 +140,61 @@ __global__ void __launch_bounds__(BLOCK) k_rerank(RoundArgs a, int32_t* tokens, 
   }
 }
 
-// Bitonic sort, descending, of a wave's 64*KPL keys held in registers:
-// element i = lane*KPL + j is key[j] of lane `lane`.  A compare-exchange at
-// stride below KPL is inside a lane's registers; a larger one pairs lane with
-// lane ^ (stride/KPL) through lane shuffles.  No LDS and no barriers.
-template <int KPL>
-__device__ __forceinline__ void wave_sort_desc(unsigned long long (&key)[KPL], int lane) {
-  constexpr int N = 64 * KPL;
+// The kk-th largest of the wave's unique 64-bit keys (N per lane, 0 = empty;
+// 1 <= kk <= their number): exactly kk keys are >= the result.  Found bit by
+// bit, most significant first: the high word is the largest h with at least
+// kk high words >= h, each step counting N ballots on the scalar unit; the low
+// word only matters under ties of the high word, and is then the smallest low
+// word among the tied keys (all of them taken) or found the same way.
+template <int N>
+__device__ __forceinline__ unsigned long long wave_kth_key(const unsigned long long (&key)[N], int kk) {
+  uint32_t hi[N], lo[N];
 #pragma unroll
-  for (int size = 2; size <= N; size <<= 1) {
+  for (int j = 0; j < N; ++j) {
+    hi[j] = (uint32_t)(key[j] >> 32);
+    lo[j] = (uint32_t)key[j];
+  }
+  uint32_t hp = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t t = hp | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= KPL) {
-        const int lm = stride / KPL;
-        const bool lo = (lane & lm) == 0;  // the lower element of its pair
+    for (int j = 0; j < N; ++j) cnt += __popcll(__ballot(hi[j] >= t));
+    if (cnt >= kk) hp = t;
+  }
+  int cgt = 0, ceq = 0;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const bool desc = ((lane * KPL + j) & size) == 0;
-          const unsigned long long x = key[j];
-          const unsigned long long y =
-              ((unsigned long long)(unsigned)__shfl_xor((int)(unsigned)(x >> 32), lm) << 32) |
-              (unsigned long long)(unsigned)__shfl_xor((int)(unsigned)x, lm);
-          key[j] = (x > y) == (lo == desc) ? x : y;  // a descending pair's lower element keeps the max
-        }
-      } else {
+  for (int j = 0; j < N; ++j) {
+    cgt += __popcll(__ballot(hi[j] > hp));
+    ceq += __popcll(__ballot(hi[j] == hp && key[j] != 0ull));
+  }
+  const int need = kk - cgt;  // 1..ceq of the keys with high word hp
+  uint32_t lp = 0u;
+  if (need == ceq) {
+    lp = 0xFFFFFFFFu;
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          if (j & stride) continue;
-          const int jj = j | stride;
-          const bool desc = ((lane * KPL + j) & size) == 0;
-          const unsigned long long x = key[j], y = key[jj];
-          const bool sw = (x < y) == desc;
-          key[j] = sw ? y : x;
-          key[jj] = sw ? x : y;
-        }
-      }
+    for (int j = 0; j < N; ++j) lp = min(lp, (hi[j] == hp && key[j] != 0ull) ? lo[j] : 0xFFFFFFFFu);
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) lp = min(lp, (uint32_t)__shfl_xor((int)lp, o));
+  } else {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t t = lp | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < N; ++j) cnt += __popcll(__ballot(hi[j] == hp && lo[j] >= t));
+      if (cnt >= need) lp = t;
     }
   }
+  return ((unsigned long long)hp << 32) | lp;
 }
 
 // The same rerank and build in one wave per sequence, for pools of at most
-// 64*KPL entries: the pool is copied to LDS once, its keys are sorted in
-// registers (wave_sort_desc), and one lane per kept node does the flatten
-// (depth by depth, its rank among the kept nodes of its depth by (parent's
-// flat index, pool index)) and its mask row.  Results are those of k_rerank.
+// 64*KPL entries: the pool is copied to LDS once, the (m-1)-th largest key is
+// found by a bitwise search over the keys in registers (wave_kth_key), the
+// keys at or above it are the kept nodes (their order does not matter: the
+// flatten orders them), and one lane per kept node does the flatten (depth by
+// depth, its rank among the kept nodes of its depth by (parent's flat index,
+// pool index)) and its mask row.  Results are those of k_rerank.
 template <int KPL>
 __global__ void __launch_bounds__(WAVE) k_rerank_wave(RoundArgs a, int32_t* tokens, int32_t* parents,
                                                       int32_t* depth, int32_t* positions, uint8_t* mask,
@@ -215,22 +226,38 @@ __global__ void __launch_bounds__(WAVE) k_rerank_wave(RoundArgs a, int32_t* toke
 
   // keys (score desc, depth asc, index asc) as unsigned integers; padding is 0
   unsigned long long key[KPL];
+  {
+    float sc[KPL];
+    int dp[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int e = lane * KPL + j;
-    key[j] = 0ull;
-    if (e < n) {
-      uint32_t u = __float_as_uint(sp[e].score);
+    for (int j = 0; j < KPL; ++j) {  // every LDS read in flight before any is used
+      const int e = min(lane * KPL + j, n - 1);
+      sc[j] = sp[e].score;
+      dp[j] = sp[e].depth;
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int e = lane * KPL + j;
+      uint32_t u = __float_as_uint(sc[j]);
       u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-      key[j] = ((unsigned long long)u << 32) | ((unsigned long long)(255 - (sp[e].depth & 255)) << 24) |
-               (unsigned long long)(0xFFFFFF - e);
+      key[j] = e < n ? ((unsigned long long)u << 32) | ((unsigned long long)(255 - (dp[j] & 255)) << 24) |
+                           (unsigned long long)(0xFFFFFF - e)
+                     : 0ull;
     }
   }
-  wave_sort_desc<KPL>(key, lane);
+  {  // the kept set: the ns largest keys (ns <= n), packed into sel[] in any order
+    const unsigned long long tau = wave_kth_key<KPL>(key, ns);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base = 0;
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int i = lane * KPL + j;
-    if (i < ns) sel[i] = 0xFFFFFF - (int)(key[j] & 0xFFFFFFull);
+    for (int j = 0; j < KPL; ++j) {
+      const bool in = key[j] != 0ull && key[j] >= tau;
+      const unsigned long long msk = __ballot(in);
+      const int pos = base + __popcll(msk & below);
+      if (in && pos < ns) sel[pos] = 0xFFFFFF - (int)(key[j] & 0xFFFFFFull);  // (keys are unique: pos < ns)
+      base += __popcll(msk);
+    }
   }
   __syncthreads();
 
@@ -251,11 +278,13 @@ __global__ void __launch_bounds__(WAVE) k_rerank_wave(RoundArgs a, int32_t* toke
     sk2[lane] = k2;
     __syncthreads();
     int rank = 0;
+    uint4 qv[WAVE / 4];  // all sixteen broadcast reads in flight before any is used
 #pragma unroll
-    for (int u = 0; u < WAVE; u += 4) {
-      const uint4 q = *(const uint4*)&sk2[u];
-      rank += (q.x < k2 ? 1 : 0) + (q.y < k2 ? 1 : 0) + (q.z < k2 ? 1 : 0) + (q.w < k2 ? 1 : 0);
-    }
+    for (int u = 0; u < WAVE / 4; ++u) qv[u] = *(const uint4*)&sk2[4 * u];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < WAVE / 4; ++u)
+      rank += (qv[u].x < k2 ? 1 : 0) + (qv[u].y < k2 ? 1 : 0) + (qv[u].z < k2 ? 1 : 0) + (qv[u].w < k2 ? 1 : 0);
     if (mine) flat_of[e] = (short)(base + rank);
     base += __popcll(__ballot(mine));
     __syncthreads();

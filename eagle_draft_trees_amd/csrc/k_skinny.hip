@@ -128,6 +128,24 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       sqv[u] = a.ssq[(size_t)min(qj + u * QJ, p.nps - 1) * a.rows + min(qrow, p.M - 1)];
   }
 
+  // ---- the epilogue's own inputs, loaded now so that their latency hides
+  // behind the weight stream: O the residual x0 and the norm gain, down the
+  // residual y, q/k/v the prefix length of each row's sequence (for RoPE)
+  float pre[4] = {0.f, 0.f, 0.f, 0.f};
+  float gain = 0.f;
+  int pre_p[4] = {0, 0, 0, 0};
+  if (OP == OP_O || OP == OP_DOWN) {
+    const float* res = OP == OP_O ? a.x0f : a.yf;
+    const int nn = nv ? n : 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pre[r] = res[(size_t)min(4 * g + r, p.M - 1) * a.d + nn];
+    if (OP == OP_O) gain = El<T>::ld((const T*)a.post_norm, nn);
+  }
+  if (OP == OP_QKV) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pre_p[r] = a.prefix_len[min(4 * g + r, p.M - 1) / a.RS];
+  }
+
   // ---- this wave's K slice: k-steps [s0k, s1k)
   const int s0k = (int)((long)ks * nks / p.KSW), s1k = (int)((long)(ks + 1) * nks / p.KSW);
   f32x4_t acc[NW];
@@ -158,10 +176,22 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
   f32x4_t v[NW];
 #pragma unroll
   for (int w = 0; w < NW; ++w) v[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (fin)
-    for (int s = 0; s < p.KSW; ++s)
+  if (fin) {  // the first MS slices' reads in flight together (a slot past KSW repeats the last, unused)
+    constexpr int MS = NW == 2 ? 8 : (OP == OP_QKV ? SK_QKVW : SK_MAXW);
+    f32x4_t rv[MS][NW];
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) rv[s][w] = red[((min(s, p.KSW - 1) * p.CT + ct) * NW + w) * WAVE + lane];
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (s < p.KSW) v[w] += rv[s][w];  // slice order
+    for (int s = MS; s < p.KSW; ++s)
 #pragma unroll
       for (int w = 0; w < NW; ++w) v[w] += red[((s * p.CT + ct) * NW + w) * WAVE + lane];
+  }
 
   // ---- epilogues; lane holds rows 4g..4g+3 of column n
   if (OP == OP_FC) {
@@ -193,7 +223,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
         // the sequence at position P+i, appended to the prefix cache
         const bool lv = a.mode == MODE_LEVEL;
         const int bb = row / a.RS, slot = row - bb * a.RS;
-        const int P = clamp_prefix(a.prefix_len[bb], a);
+        const int P = clamp_prefix(pre_p[r], a);
         if (rot) {
           const int pos = lv ? P - 1 + a.depth : P + slot;
           double sd, cd;
@@ -220,12 +250,11 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
   } else if (OP == OP_O) {
     float sq[4] = {0.f, 0.f, 0.f, 0.f};
     if (fin) {
-      const float gain = nv ? El<T>::ld((const T*)a.post_norm, n) : 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
         if (!nv || row >= p.M) continue;
-        const float y = v[0][r] + a.x0f[(size_t)row * a.d + n];
+        const float y = v[0][r] + pre[r];
         a.yf[(size_t)row * a.d + n] = y;
         El<T>::st((T*)a.yg, (size_t)row * a.d + n, y * gain);
         sq[r] = y * y;
@@ -263,7 +292,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
         if (row >= p.M) continue;
-        const float h = v[0][r] + a.yf[(size_t)row * a.d + n];
+        const float h = v[0][r] + pre[r];
         if (a.mode == MODE_LEVEL) {
           El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + n, h);
         } else {  // extend: row alen-1 of a sequence is its next root feature

@@ -212,6 +212,8 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       const int fi = 8 * j + (low ? c : c - 8);  // frequency index within the half
       const bool rot = head < a.H + a.Hkv;
       const double inv = pow((double)a.theta, -2.0 * (double)fi / (double)a.hd);
+      int lastpos = INT_MIN;  // rows of one position (a level's rows of one sequence) share the angle
+      double sd = 0.0, cd = 1.0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float own = v[0][r];
@@ -226,8 +228,10 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
         const int P = clamp_prefix(pre_p[r], a);
         if (rot) {
           const int pos = lv ? P - 1 + a.depth : P + slot;
-          double sd, cd;
-          sincos((double)pos * inv, &sd, &cd);
+          if (pos != lastpos) {
+            sincos((double)pos * inv, &sd, &cd);
+            lastpos = pos;
+          }
           const float cs = (float)cd, sn = (float)sd;
           const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;
           lo = nlo;

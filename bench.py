@@ -567,6 +567,10 @@ def main() -> int:
     ap.add_argument("--configs-cpu-budget", type=float, default=8.0)
     ap.add_argument("--lmhead-only", type=int, default=0,
                     help="only launch the LM-head kernel this many times (counter runs)")
+    ap.add_argument("--rounds-only", type=int, default=0,
+                    help="only run this many eager rounds after the calibration copies (counter runs)")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="only the batched LM-head GEMM measurement (counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -580,9 +584,12 @@ def main() -> int:
     from eagle_draft_trees_amd import _lib as L
     from eagle_draft_trees_amd.round import DraftRound
 
+    dev = torch.device("cuda:0")
+    if args.batched_only:
+        print(json.dumps(batched_lmhead(torch, L, dev, torch.cuda.Stream(device=dev))), flush=True)
+        return 0
     cfg = synth.config_by_name(args.config)
     inp = synth.make_inputs(cfg, seed=args.seed)
-    dev = torch.device("cuda:0")
     r = DraftRound(cfg, inp, "cuda:0")
     stream = torch.cuda.Stream(device=dev)
     workload = workload_name(cfg)
@@ -600,6 +607,22 @@ def main() -> int:
                 r.level(2, L.EAGLE_LEVEL_LMHEAD_ONLY, stream=stream)
         torch.cuda.synchronize()
         print(json.dumps({"lmhead_only": args.lmhead_only, "copy_bytes": src.numel()}))
+        return 0
+
+    if args.rounds_only:
+        # counter runs: a copy of known size (calibration), then whole rounds, one by one
+        src = torch.empty(64 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        saved = r.prefix_len.clone()
+        with torch.cuda.stream(stream):
+            for _ in range(args.rounds_only):
+                r.run_round(stream=stream)
+                torch.add(saved, 0, out=r.prefix_len)
+        torch.cuda.synchronize()
+        print(json.dumps({"rounds_only": args.rounds_only, "copy_bytes": src.numel(), "workload": workload}))
         return 0
 
     m = measure_rounds(torch, r, stream, args.steps, args.warmup, graph=not args.no_graph)

@@ -112,7 +112,13 @@ test_oracle_*.py) against brute force, closed forms, special cases or the
 pages' worked numbers.  The layer's absolute values at random weights have
 no printed example on the pages; they are pinned through special cases
 (zeroed sublayers, identity FC, single-key attention, library attention
-under an equivalent mask) rather than end to end.
+under an equivalent mask) rather than end to end.  The level forward
+(level_step_forward: R8's position P-1+depth and the visible keys prefix,
+ancestors and self) is pinned two ways in tests/test_oracle_level.py: at
+topk = 1 the levels over a chain equal one causal pass of the layer over
+the same rows (draft_extend, itself pinned to library causal attention),
+and at any topk the level rows equal a library layer under a mask built in
+the test from the pool's parent links.
 """
 from __future__ import annotations
 

@@ -240,6 +240,7 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
                               plan_attn(MODE_EXTEND, re, d, c, B).part_floats,
                               plan_attn(MODE_EXTEND, m, d, c, B).part_floats});
   L.apart = take(ap * 4);
+  L.rope = take((size_t)d.head_dim / 2 * sizeof(double));
   L.total = off;
   return L;
 }
@@ -374,6 +375,7 @@ static RoundArgs make_args(const eagle_dims& d, const eagle_tree_cfg& c, const e
   a.rstd = (float*)(base + L.rstd); a.ssq = (float*)(base + L.ssq); a.act = base + L.act;
   a.gpart = (float*)(base + L.gpart); a.lmpart = (float*)(base + L.lmpart);
   a.lmres = (float*)(base + L.lmres); a.apart = (float*)(base + L.apart); a.xpk = base + L.xpk;
+  a.rope = (const double*)(base + L.rope);
   a.pool_n = L.pool_n;
   return a;
 }
@@ -485,7 +487,10 @@ int eagle_workspace_init(const eagle_dims* dims, const eagle_tree_cfg* cfg, void
   int r;
   if ((r = check_dims(dims)) || (r = check_cfg(dims, cfg)) || (r = check_ws(dims, cfg, ws, ws_bytes)))
     return r;
-  return hip_ok(launch_zero(ws, plan_ws(*dims, *cfg).total, (hipStream_t)stream), "zero fill");
+  const WsLayout L = plan_ws(*dims, *cfg);
+  if ((r = hip_ok(launch_zero(ws, L.total, (hipStream_t)stream), "zero fill"))) return r;
+  return hip_ok(launch_rope_table((double*)((char*)ws + L.rope), dims->head_dim, dims->rope_theta,
+                                  (hipStream_t)stream), "rope table");
 }
 
 static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eagle_tree_cfg* cfg,

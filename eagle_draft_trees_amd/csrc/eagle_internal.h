@@ -261,7 +261,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 struct WsLayout {
   size_t err, cnt, pool, frontier, feat, tk, tv, ext_h;
   size_t x0f, x0b, x0l, q, attn, yf, yg, rstd, ssq, act;
-  size_t gpart, lmpart, lmres, apart, xpk;
+  size_t gpart, lmpart, lmres, apart, xpk, rope;
   size_t total;
   int rows_max, pool_n;
 };
@@ -353,6 +353,7 @@ struct RoundArgs {
   float *rstd, *ssq;
   void* act;
   float *gpart, *lmpart, *lmres, *apart;
+  const double* rope;  // [hd/2]: theta^(-2i/hd) in fp64, written at workspace init
   void* xpk;  // batched LM head: its input rows in MFMA fragment order
   int pool_n;
 };
@@ -565,6 +566,7 @@ hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStre
 hipError_t launch_lmmerge(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
                           const SkPlan* handover = nullptr);
 hipError_t launch_attn(const RoundArgs& a, const AttnPlan& p, hipStream_t s);
+hipError_t launch_rope_table(double* t, int hd, float theta, hipStream_t s);
 hipError_t launch_rerank(const RoundArgs& a, int32_t* tokens, int32_t* parents, int32_t* depth,
                          int32_t* positions, uint8_t* mask, float* logscore, hipStream_t s);
 hipError_t launch_verify(int B, int m, int D, int V, const float* tl, const int32_t* tokens,

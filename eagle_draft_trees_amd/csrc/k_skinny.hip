@@ -57,7 +57,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
   // partial sums [wave][NW][64] once every wave is done with X
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
   f32x4_t* red = (f32x4_t*)dyn;
-  __shared__ float s_ssq[SK_MAXW][16];
+  __shared__ __attribute__((aligned(16))) float s_ssq[SK_MAXW][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ct = wave % p.CT, ks = wave / p.CT;
@@ -141,9 +141,12 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
     for (int r = 0; r < 4; ++r) pre[r] = res[(size_t)min(4 * g + r, p.M - 1) * a.d + nn];
     if (OP == OP_O) gain = El<T>::ld((const T*)a.post_norm, nn);
   }
+  double inv = 0.0;  // q/k/v: this lane's RoPE frequency
   if (OP == OP_QKV) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) pre_p[r] = a.prefix_len[min(4 * g + r, p.M - 1) / a.RS];
+    const int tt = tv ? t : 0, per = a.hd / 16, j = tt - (tt / per) * per;
+    inv = a.rope[8 * j + (c < 8 ? c : c - 8)];
   }
 
   // ---- this wave's K slice: k-steps [s0k, s1k)
@@ -211,9 +214,8 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       const bool low = c < 8;
       const int fi = 8 * j + (low ? c : c - 8);  // frequency index within the half
       const bool rot = head < a.H + a.Hkv;
-      const double inv = pow((double)a.theta, -2.0 * (double)fi / (double)a.hd);
       int lastpos = INT_MIN;  // rows of one position (a level's rows of one sequence) share the angle
-      double sd = 0.0, cd = 1.0;
+      float sn = 0.f, cs = 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float own = v[0][r];
@@ -229,10 +231,13 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
         if (rot) {
           const int pos = lv ? P - 1 + a.depth : P + slot;
           if (pos != lastpos) {
-            sincos((double)pos * inv, &sd, &cd);
+            // the angle pos * theta^(-2i/hd) in fp64, reduced to [-pi, pi] in fp64, then
+            // its sine and cosine in fp32 (the rotation is applied in fp32)
+            const double ang = (double)pos * inv;
+            const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+            sincosf((float)red, &sn, &cs);
             lastpos = pos;
           }
-          const float cs = (float)cd, sn = (float)sd;
           const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;
           lo = nlo;
           hi = nhi;
@@ -279,12 +284,27 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
     }
   } else if (OP == OP_GATEUP) {
     if (fin && nv) {
+      // the rows' sums of squares: every wave's four (rows 4g..4g+3) read together,
+      // then added in wave order
+      const int nwv = (int)(blockDim.x >> 6);
+      float4 sw[SK_MAXW];
+#pragma unroll
+      for (int w = 0; w < SK_MAXW; ++w) sw[w] = *(const float4*)&s_ssq[min(w, nwv - 1)][4 * g];
+      asm volatile("" ::: "memory");
+      float ssr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < SK_MAXW; ++w)
+        if (w < nwv) {
+          ssr[0] += sw[w].x;
+          ssr[1] += sw[w].y;
+          ssr[2] += sw[w].z;
+          ssr[3] += sw[w].w;
+        }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
         if (row >= p.M) continue;
-        float ss = 0.f;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) ss += s_ssq[w][row];
+        const float ss = ssr[r];
         const float rs = 1.0f / sqrtf(ss / (float)a.d + a.eps);
         const float gg = v[0][r] * rs, uu = v[NW - 1][r] * rs;
         El<T>::st((T*)a.act, xpk_index<T>(row, n, (a.F + KS - 1) / KS), gg / (1.0f + expf(-gg)) * uu);

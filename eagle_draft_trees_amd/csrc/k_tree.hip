@@ -1074,6 +1074,18 @@ hipError_t launch_verify_rejection(int B, int m, int D, int V, const float* tl, 
 
 size_t verify_rejection_scratch_bytes(int B, int m) { return 2 * (size_t)B * m * RS_SEG * sizeof(float2); }
 
+// RoPE frequencies theta^(-2i/hd), i < hd/2, in fp64 ([P1] §12 item 5 positions;
+// reading R8: theta and rotate-half pairs), once per workspace
+__global__ void k_rope_table(double* t, int half, double theta, int hd) {
+  const int i = (int)threadIdx.x;
+  if (i < half) t[i] = pow(theta, -2.0 * (double)i / (double)hd);
+}
+
+hipError_t launch_rope_table(double* t, int hd, float theta, hipStream_t s) {
+  hipLaunchKernelGGL(k_rope_table, dim3(1), dim3(WAVE * 2), 0, s, t, hd / 2, (double)theta, hd);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   const size_t n16 = bytes / 16;
   const int blocks = (int)(n16 / BLOCK + 1 < 4096 ? n16 / BLOCK + 1 : 4096);

@@ -184,8 +184,9 @@ int eagle_pack_weights(const eagle_dims *dims, const eagle_weights *src, void *d
 /* Bytes of workspace for (dims, cfg); 0 if they are invalid. */
 size_t eagle_workspace_bytes(const eagle_dims *dims, const eagle_tree_cfg *cfg);
 
-/* Zero the workspace (counters and error word must start at zero).  Call once
- * after allocating it; every kernel leaves its counters at zero again. */
+/* Zero the workspace (counters and error word must start at zero) and write
+ * the RoPE frequency table (theta^(-2i/hd) in fp64) it holds.  Call once after
+ * allocating it; every kernel leaves its counters at zero again. */
 int eagle_workspace_init(const eagle_dims *dims, const eagle_tree_cfg *cfg, void *ws,
                          size_t ws_bytes, void *stream);
 

@@ -175,7 +175,10 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
     if (lane < 16) s_ssq[wave][lane] = s;
   }
   __syncthreads();
-  const bool fin = ks == 0;
+  // the epilogue is spread over the tile's first waves: wave ks (< 4) finishes
+  // the rows 4g+r with r % KSW == ks of every lane group (all four when KSW is 1)
+  const bool fin = ks < 4;
+  auto mine = [&](int r) __attribute__((always_inline)) { return r % p.KSW == ks; };
   f32x4_t v[NW];
 #pragma unroll
   for (int w = 0; w < NW; ++w) v[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -203,7 +206,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
-        if (row >= p.M) continue;
+        if (!mine(r) || row >= p.M) continue;
         const float x = v[0][r] + a.tok_proj[(size_t)s_tok[row] * a.d + n] + bias;
         st_x0<T>(a, (size_t)row * a.d + n, x);
       }
@@ -218,6 +221,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       float sn = 0.f, cs = 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        if (!mine(r)) continue;  // wave-uniform
         const float own = v[0][r];
         const float other = __shfl_xor(own, 8);
         const int row = 4 * g + r;
@@ -262,7 +266,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
-        if (!nv || row >= p.M) continue;
+        if (!mine(r) || !nv || row >= p.M) continue;
         const float y = v[0][r] + pre[r];
         a.yf[(size_t)row * a.d + n] = y;
         El<T>::st((T*)a.yg, (size_t)row * a.d + n, y * gain);
@@ -271,6 +275,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       // sum over the tile's 16 columns (the 16 lanes of one DPP row)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        if (!mine(r)) continue;  // wave-uniform
 #pragma unroll
         for (int st = 0; st < 4; ++st) sq[r] += __uint_as_float(dpp_u32(__float_as_uint(sq[r]), st));
         if (c == 0) s_ssq[ct][4 * g + r] = sq[r];
@@ -303,7 +308,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
-        if (row >= p.M) continue;
+        if (!mine(r) || row >= p.M) continue;
         const float ss = ssr[r];
         const float rs = 1.0f / sqrtf(ss / (float)a.d + a.eps);
         const float gg = v[0][r] * rs, uu = v[NW - 1][r] * rs;
@@ -315,7 +320,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
-        if (row >= p.M) continue;
+        if (!mine(r) || row >= p.M) continue;
         const float h = v[0][r] + pre[r];
         if (a.mode == MODE_LEVEL) {
           El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + n, h);

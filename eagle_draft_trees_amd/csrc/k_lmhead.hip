@@ -14,6 +14,8 @@
 #include <hip/hip_ext.h>
 #include <float.h>
 
+#include <type_traits>
+
 #include "skinny_core.h"
 
 namespace eg {
@@ -209,33 +211,41 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
   // one wave per row: up to four columns per lane
   __shared__ __attribute__((aligned(16))) unsigned long long s_tk[SK_MAXW][2 * WAVE];  // wave_topk scratch
   const int col0 = blockIdx.x * ncol;
-  for (int row = wave; row < p.M; row += nwv) {
-    float x[4];
-    unsigned long long key[4];
-    float mx = -INFINITY;
+  // (NC = columns per lane: two for slabs of up to 128 columns, else four)
+  auto epi = [&](auto ncl) __attribute__((always_inline)) {
+    constexpr int NC = decltype(ncl)::value;
+    for (int row = wave; row < p.M; row += nwv) {
+      float x[NC];
+      unsigned long long key[NC];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = lane + 64 * u;
-      x[u] = j < ncol ? lg[row * LW + j] : -INFINITY;
-      key[u] = x[u] == -INFINITY ? 0ull : argkey(x[u], col0 + j);
-      mx = fmaxf(mx, x[u]);
-    }
-    mx = wave_max_dpp(mx);
-    float se = 0.f;
+      for (int u = 0; u < NC; ++u) {
+        const int j = lane + 64 * u;
+        x[u] = j < ncol ? lg[row * LW + j] : -INFINITY;
+        key[u] = x[u] == -INFINITY ? 0ull : argkey(x[u], col0 + j);
+        mx = fmaxf(mx, x[u]);
+      }
+      mx = wave_max_dpp(mx);
+      float se = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) se += x[u] == -INFINITY ? 0.f : expf(x[u] - mx);
-    se = wave_sum_dpp(se);
-    float* rec = slab_field(a.lmpart, row, blockIdx.x, p);  // field f at rec[f * nblk]
-    if (lane == 0) {
-      rec[0] = mx;
-      rec[p.nblk] = se;
+      for (int u = 0; u < NC; ++u) se += x[u] == -INFINITY ? 0.f : expf(x[u] - mx);
+      se = wave_sum_dpp(se);
+      float* rec = slab_field(a.lmpart, row, blockIdx.x, p);  // field f at rec[f * nblk]
+      if (lane == 0) {
+        rec[0] = mx;
+        rec[p.nblk] = se;
+      }
+      const unsigned long long mine = wave_topk<NC>(key, kk_, s_tk[wave]);  // lane r: the r-th entry
+      if (lane < kk_) {
+        rec[(2 + lane) * p.nblk] = mine ? argkey_value(mine) : -INFINITY;
+        rec[(2 + kk_ + lane) * p.nblk] = __int_as_float(mine ? argkey_id(mine) : -1);
+      }
     }
-    const unsigned long long mine = wave_topk<4>(key, kk_, s_tk[wave]);  // lane r: the r-th entry
-    if (lane < kk_) {
-      rec[(2 + lane) * p.nblk] = mine ? argkey_value(mine) : -INFINITY;
-      rec[(2 + kk_ + lane) * p.nblk] = __int_as_float(mine ? argkey_id(mine) : -1);
-    }
-  }
+  };
+  if (ncol <= 128)
+    epi(std::integral_constant<int, 2>());
+  else
+    epi(std::integral_constant<int, 4>());
 }
 
 // Launch through hipExtLaunchKernel when events are given (they then mark the

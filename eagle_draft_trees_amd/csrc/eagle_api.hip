@@ -166,8 +166,8 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
     p.xlds = p.CT >= 2 && sk_xtile_bytes(d.d, (int)elem_size(d)) <= SK_XLDS_MAX;
   } else {
     p.nblk = cdiv(d.vocab, 64);
-    p.big = d.dtype == EAGLE_BF16 && M > 64;
-    if (p.big) p.zg = cdiv(M, 512);
+    p.big = d.dtype == EAGLE_BF16 && M > 64 && d.d % 128 == 0;
+    if (p.big) p.zg = cdiv(M, lmgemm_rows());
   }
   p.rec = 2 + 2 * topk;
   p.part_floats = (size_t)M * p.nblk * p.rec;

@@ -298,7 +298,7 @@ struct SkPlan {
 struct LmPlan {
   int M, mt, zg, nblk, rec;  // rec = floats per (row, slab) partial; nblk = slabs
   int sk, CT, KSW, xlds;     // sk: streaming-core kernel (M <= 16), CT tiles x KSW waves
-  int big;                   // bf16 and more than 64 rows: the tiled GEMM (k_lmgemm), zg groups of 512 rows
+  int big;                   // bf16, more than 64 rows, d a multiple of 128: the tiled GEMM (k_lmgemm), zg row tiles
   size_t part_floats;
 };
 
@@ -548,6 +548,7 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 // launchers (return a hipError_t)
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
+int lmgemm_rows();  // rows per k_lmgemm tile
 hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
                          hipEvent_t e1);
 // e0/e1 (may be null): events stamped at the LM-head kernel's own start and end

@@ -7,23 +7,29 @@
 // once) the product stops being a weight stream and becomes a dense
 // contraction, so it is tiled for operand reuse:
 //
-//  * a workgroup owns 512 rows x 128 vocabulary columns; each of its eight
+//  * a workgroup owns 256 rows x 256 vocabulary columns; each of its eight
 //    waves owns 128 rows x 64 columns (8 x 4 tiles of v_mfma_f32_16x16x32_bf16,
-//    128 fp32 accumulators per lane), so each weight tile is read from HBM
-//    once per 512 rows and each feature fragment is reused four times;
-//  * per k-step of 32, the 512 feature rows (32 KB) and the 128 weight rows
-//    (8 KB) are staged in LDS in MFMA-fragment order (one kilobyte per 16x32
-//    fragment, lane l's 16 bytes at l*16), so every operand read is one
-//    conflict-free 16-byte LDS read per lane.  The packed weight tiles are
-//    already in that order, and k_lg_xpack first writes the feature rows in it
-//    (k past K zeroed, rows past M repeating row M-1), so every global load of
-//    either operand is one contiguous kilobyte per wave instead of 16 rows'
-//    half cache lines;
-//  * two LDS buffers and two register stages: the global loads of step s+2
-//    are in flight while step s computes, one barrier per step;
+//    128 fp32 accumulators per lane), so one 64-column slab per wave;
+//  * operands move from memory straight into LDS (global_load_lds_dwordx4:
+//    lane l's 16 bytes land at l*16, which is the MFMA fragment order that the
+//    packed weight tiles and the k_lg_xpack feature pack already have), one
+//    kilobyte fragment per wave instruction and no staging registers.  Four
+//    stage buffers of one k-step of 32 (32 KB each); a step's loads are issued
+//    three steps ahead, every wave issuing four of its 32 fragments;
+//  * the eight waves run as two groups of four (one wave of each group per
+//    SIMD) offset by half a step: while one group issues its sixteen MFMA
+//    fragments' worth of LDS reads and next loads, the other runs its 32
+//    MFMAs, so the matrix core of every SIMD always has a wave feeding it.
+//    Each half step ends in a workgroup barrier; each wave waits for its own
+//    loads (a fixed count: the loads past the last step repeat it into
+//    buffers that are not read again) and its LDS reads before it;
+//  * blocks are numbered so that each XCD (blocks b, b+8, ...) takes a
+//    contiguous run of tiles, the row tiles of one column block adjacent, so
+//    that a weight tile is fetched from memory once and re-read from that
+//    XCD's L2;
 //  * epilogue: a wave's 64 columns are one 64-column slab of the same record
 //    layout as the other LM-head kernels (max, sum exp, top-k logits, ids),
-//    one lane per row over a column-major LDS tile.
+//    one lane per row over a column-major LDS tile in the stage buffers.
 #include <hip/hip_ext.h>
 
 #include "eagle_internal.h"
@@ -32,17 +38,20 @@ namespace eg {
 
 constexpr int LG_W = 8;                 // waves per workgroup
 constexpr int LG_THREADS = LG_W * WAVE;
-constexpr int LG_ROWS = 512;            // rows per z-group: 4 row groups of 128
-constexpr int LG_COLS = 128;            // columns per workgroup: 2 column groups of 64
-constexpr int LG_XB = LG_ROWS / 16;     // feature fragments per k-step
-constexpr int LG_WB = LG_COLS / 16;     // weight fragments per k-step
-constexpr int LG_STAGE = (LG_XB + LG_WB) * 1024;   // bytes of one staged k-step
-constexpr int LG_XP = LG_XB * WAVE / LG_THREADS;    // feature pieces per thread per step (4)
-constexpr int LG_TP = 64 + 4;           // epilogue tile: padded rows per column
-constexpr int LG_EPI = LG_W * 64 * LG_TP * 4;      // epilogue tile bytes (64 rows per pass)
-static_assert(LG_WB * WAVE == LG_THREADS, "one weight piece per thread per step");
+constexpr int LG_ROWS = 256;            // rows per workgroup: 2 row groups of 128
+constexpr int LG_COLS = 256;            // columns per workgroup: 4 slabs of 64
+constexpr int LG_FR = (LG_ROWS + LG_COLS) / 16;   // 1 KB fragments per k-step (32)
+constexpr int LG_DMA = LG_FR / LG_W;              // fragments each wave loads per k-step (4)
+static_assert(LG_FR * 1024 == 32768 && LG_DMA == 4, "stage layout");
+// Four stage buffers, separate objects so that the compiler can tell the
+// loads into one from the LDS reads of another (it then adds no waits of its
+// own between them)
+__shared__ __attribute__((aligned(1024))) uint4 lg_s0[2048];
+__shared__ __attribute__((aligned(1024))) uint4 lg_s1[2048];
+__shared__ __attribute__((aligned(1024))) uint4 lg_s2[2048];
+__shared__ __attribute__((aligned(1024))) uint4 lg_s3[2048];
 
-size_t lmgemm_lds_bytes() { return (size_t)(2 * LG_STAGE > LG_EPI ? 2 * LG_STAGE : LG_EPI); }
+int lmgemm_rows() { return LG_ROWS; }
 
 // The feature rows [M][K] (row-major bf16, K a multiple of 8) in fragment
 // order: block (group, s) = rows 16*group.. x k 32*s.., lane l = 16g + i's 16
@@ -58,133 +67,140 @@ __global__ void __launch_bounds__(256) k_lg_xpack(const bf16_t* x, int M, int K,
   *(uint4*)(xpk + (size_t)blk * 512 + lane * 8) = v;
 }
 
-__global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, int level) {
+// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): vmcnt(8) alone, and vmcnt(8) with lgkmcnt(0)
+constexpr int LG_WAIT_VM8 = 8 | (7 << 4) | (15 << 8);
+constexpr int LG_WAIT_VM8_LGKM0 = 8 | (7 << 4);
+constexpr int LG_WAIT_ALL = 0;
+
+__global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, int level, int per_xcd) {
   typedef bf16_t T;
-  constexpr int KS = El<T>::KSTEP;  // 32
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 3, wn = wave >> 2;  // 128-row group, 64-column group
-  const int blk = blockIdx.x, zg = blockIdx.z;
+  const bool first = wave < 4;              // group that runs half a step ahead
+  const int wm = wave & 1, wn = wave >> 1;  // 128-row group, 64-column slab
   const int K = a.d, kk_ = a.k;
-  const int nks = (K + KS - 1) / KS;
-  const int ntile = (a.V + 15) / 16;
-  // ---- staging sources: thread tid fills lane (tid % 64) of feature
-  // fragments tid/64 + 8u (u < 4) and of weight fragment tid/64; both come
-  // from fragment-ordered buffers (a group past the last reads the last)
-  const int ngrp = (p.M + 15) / 16;
-  const T* xsrc[LG_XP];
-#pragma unroll
-  for (int u = 0; u < LG_XP; ++u) {
-    const int grp = min(zg * (LG_ROWS / 16) + (tid >> 6) + LG_W * u, ngrp - 1);
-    xsrc[u] = (const T*)a.xpk + (size_t)grp * nks * wtile_elems<T>() + lane * El<T>::PER16;
-  }
-  const T* wsrc = wtile_base<T>(a.lm_head, nks, min(LG_WB * blk + (tid >> 6), ntile - 1), lane);
-  typedef uint4 Stage[LG_XP + 1];
-  // loads are unconditional from clamped addresses
-  auto gload = [&](Stage& r, int s) __attribute__((always_inline)) {
-    s = min(s, nks - 1);  // past the last step: repeats it (stored, never read)
-#pragma unroll
-    for (int u = 0; u < LG_XP; ++u) r[u] = ld16(xsrc[u] + (size_t)s * wtile_elems<T>());
-    r[LG_XP] = ld16w(wsrc + (size_t)s * wtile_elems<T>());
-  };
-  auto lstore = [&](const Stage& r, int buf, int s) __attribute__((always_inline)) {
-    (void)s;
-    unsigned char* b = lds + buf * LG_STAGE;
-#pragma unroll
-    for (int u = 0; u < LG_XP; ++u) *(uint4*)(b + (size_t)((tid >> 6) + LG_W * u) * 1024 + lane * 16) = r[u];
-    *(uint4*)(b + (size_t)(LG_XB + (tid >> 6)) * 1024 + lane * 16) = r[LG_XP];
-  };
+  const int nks = K / 32;                   // a multiple of 4 (the plan checks)
+  const int ngrp = (p.M + 15) / 16, ntile = (a.V + 15) / 16;
+  const int ncb = (a.V + LG_COLS - 1) / LG_COLS, ntiles = ncb * p.zg;
+  // block b runs on XCD b % 8; XCD x takes tiles x*per_xcd .. (row tiles of
+  // a column block adjacent); the blocks past the last tile end here
+  const int j = blockIdx.x >> 3, lin = (blockIdx.x & 7) * per_xcd + j;
+  if (j >= per_xcd || lin >= ntiles) return;
+  const int cb = lin / p.zg, rb = lin - cb * p.zg;
 
+  // this wave's fragments 4*wave .. 4*wave+3 of every k-step: 0..15 the
+  // feature groups of the row tile, 16..31 the weight tiles of the column
+  // block (a group or tile past the last repeats the last)
+  const T* src[LG_DMA];
+#pragma unroll
+  for (int u = 0; u < LG_DMA; ++u) {
+    const int f = LG_DMA * wave + u;
+    src[u] = f < 16 ? (const T*)a.xpk + (size_t)min(rb * 16 + f, ngrp - 1) * nks * wtile_elems<T>() + lane * 8
+                    : wtile_base<T>(a.lm_head, nks, min(cb * 16 + f - 16, ntile - 1), lane);
+  }
+  auto dma = [&](uint4* buf, int s) __attribute__((always_inline)) {
+    s = min(s, nks - 1);
+#pragma unroll
+    for (int u = 0; u < LG_DMA; ++u)
+      __builtin_amdgcn_global_load_lds((const void*)(src[u] + (size_t)s * wtile_elems<T>()),
+                                       (__attribute__((address_space(3))) void*)(buf + (LG_DMA * wave + u) * WAVE),
+                                       16, 0, 0);
+  };
   f32x4_t acc[8][4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[j][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const unsigned char* b = lds + buf * LG_STAGE;
-    uint4 wf[4];
+    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 xa[8], wb[4];
+  auto rd = [&](const uint4* buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wf[q] = *(const uint4*)(b + (size_t)(LG_XB + wn * 4 + q) * 1024 + lane * 16);
+    for (int q = 0; q < 4; ++q) wb[q] = buf[(16 + 4 * wn + q) * WAVE + lane];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 xf = *(const uint4*)(b + (size_t)(wm * 8 + j) * 1024 + lane * 16);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[j][q] = mma16(xf, wf[q], acc[j][q], T());
-    }
+    for (int i = 0; i < 8; ++i) xa[i] = buf[(8 * wm + i) * WAVE + lane];
   };
+  auto comp = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[i][q] = mma16(xa[i], wb[q], acc[i][q], T());
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Step t: read buffer t%4 and issue step t+3's loads into buffer (t+3)%4
+  // (last read at step t-1, by the second group, before the barrier that
+  // precedes this half step), wait for step t+1's loads (the two later steps
+  // stay in flight) and the reads, barrier, MFMAs, barrier.  The first group
+  // reads step t while the second computes step t-1 and vice versa.
+  // (no branches inside the unrolled body: the compiler's wait analysis then
+  // keeps the loads in flight across the LDS reads)
+#define LG_STEP(BUF, NEXT, t)                       \
+  __builtin_amdgcn_sched_barrier(0);                \
+  rd(BUF);                                          \
+  __builtin_amdgcn_sched_barrier(0);                \
+  dma(NEXT, (t) + 3);                               \
+  __builtin_amdgcn_s_waitcnt(LG_WAIT_VM8_LGKM0);    \
+  __builtin_amdgcn_sched_barrier(0);                \
+  __builtin_amdgcn_s_barrier();                     \
+  __builtin_amdgcn_sched_barrier(0);                \
+  comp();                                           \
+  __builtin_amdgcn_sched_barrier(0);                \
+  __builtin_amdgcn_s_waitcnt(LG_WAIT_VM8);          \
+  __builtin_amdgcn_s_barrier();
 
-  // ---- k-steps: buffers alternate; the loads two steps ahead stay in flight
-  // (straight-line body over two steps, last one or two peeled, so that the
-  // compiler's wait counts stay exact)
-  // (scheduling barriers keep each phase where it is written: the compiler
-  // would otherwise sink the loads to the end of the body and hoist the next
-  // LDS store right behind them)
-  Stage ra, rb;
-  gload(ra, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  gload(rb, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  lstore(ra, 0, 0);
+  dma(lg_s0, 0);
+  dma(lg_s1, 1);
+  dma(lg_s2, 2);
+  __builtin_amdgcn_s_waitcnt(LG_WAIT_VM8);
+  __builtin_amdgcn_s_barrier();
+  if (!first) __builtin_amdgcn_s_barrier();  // the second group starts half a step later
+  for (int t = 0; t < nks; t += 4) {
+    LG_STEP(lg_s0, lg_s3, t)
+    LG_STEP(lg_s1, lg_s0, t + 1)
+    LG_STEP(lg_s2, lg_s1, t + 2)
+    LG_STEP(lg_s3, lg_s2, t + 3)
+  }
+#undef LG_STEP
+  if (first) __builtin_amdgcn_s_barrier();   // (the same barrier count in both groups)
+  __builtin_amdgcn_s_waitcnt(LG_WAIT_ALL);   // the repeated loads past the last step
   __syncthreads();
-  gload(ra, 2);
-  __builtin_amdgcn_sched_barrier(0);
-  int s = 0;
-  for (; s + 2 < nks; s += 2) {
-    compute(0);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(rb, 1, s + 1);
-    __syncthreads();
-    gload(rb, s + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(ra, 0, s + 2);
-    __syncthreads();
-    gload(ra, s + 4);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  compute(0);
-  if (s + 1 < nks) {
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(rb, 1, s + 1);
-    __syncthreads();
-    compute(1);
-  }
-  __syncthreads();  // every wave is done with the staging buffers
 
   // ---- epilogue, two passes of 64 rows per wave: the wave's 64 x 64 block
-  // goes to its LDS tile column-major (rows padded), then lane r reduces row r
-  // of the pass over the slab's 64 columns
-  float* tile = (float*)lds + (size_t)wave * 64 * LG_TP;
+  // goes column-major to a 16 KB tile (half of a stage buffer), row r of
+  // column c at c*64 + (r ^ 4*(c%16)) (float4 stores of 16 columns spread
+  // over the banks, reads of one column by 64 lanes a permutation of one
+  // 64-float run); lane r then reduces row r of the pass over the 64 columns
+  uint4* tb = (wave >> 1) == 0 ? lg_s0 : (wave >> 1) == 1 ? lg_s1 : (wave >> 1) == 2 ? lg_s2 : lg_s3;
+  float* tile = (float*)tb + (wave & 1) * 64 * 64;
   const int c = lane & 15, g = lane >> 4;
-  const int slab = blk * 2 + wn;
+  const int slab = cb * 4 + wn;
   const int cbase = slab * 64;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int j = pass * 4 + jj;
+      const int i = pass * 4 + jj;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col = 16 * q + c;
-        *(float4*)(tile + (size_t)col * LG_TP + 16 * jj + 4 * g) =
-            make_float4(acc[j][q][0], acc[j][q][1], acc[j][q][2], acc[j][q][3]);
+        *(float4*)(tile + col * 64 + ((16 * jj + 4 * g) ^ (4 * c))) =
+            make_float4(acc[i][q][0], acc[i][q][1], acc[i][q][2], acc[i][q][3]);
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const int row = zg * LG_ROWS + wm * 128 + pass * 64 + lane;
+    const int row = rb * LG_ROWS + wm * 128 + pass * 64 + lane;
     // the row's 64 logits into registers once (columns past V: -inf)
     float v[64];
 #pragma unroll
-    for (int col = 0; col < 64; ++col) v[col] = cbase + col < a.V ? tile[(size_t)col * LG_TP + lane] : -INFINITY;
+    for (int col = 0; col < 64; ++col)
+      v[col] = cbase + col < a.V ? tile[col * 64 + (lane ^ (4 * (col & 15)))] : -INFINITY;
     float mx = -INFINITY;
 #pragma unroll
     for (int col = 0; col < 64; ++col) mx = fmaxf(mx, v[col]);
     float se = 0.f;
 #pragma unroll
     for (int col = 0; col < 64; ++col) se += v[col] == -INFINITY ? 0.f : expf(v[col] - mx);
-    if (row < p.M && slab < p.nblk) {  // (the second half of the last block may lie past V)
+    if (row < p.M && slab < p.nblk) {  // (the last column block may reach past V)
       float* rec = slab_field(a.lmpart, row, slab, p);  // field f at rec[f * nblk]
       rec[0] = mx;
       rec[p.nblk] = se;
@@ -227,12 +243,12 @@ hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStre
                           (bf16_t*)a.xpk);
   else
     hipLaunchKernelGGL(k_lg_xpack, pgrid, dim3(256), 0, s, x, p.M, K, nks, nblocks, (bf16_t*)a.xpk);
-  const dim3 grid((a.V + LG_COLS - 1) / LG_COLS, 1, p.zg), block(LG_THREADS);
-  const size_t lds = lmgemm_lds_bytes();
+  const int ntiles = (a.V + LG_COLS - 1) / LG_COLS * p.zg, per_xcd = (ntiles + 7) / 8;
+  const dim3 grid(per_xcd * 8), block(LG_THREADS);
   if (e1)
-    hipExtLaunchKernelGGL(k_lmgemm, grid, block, (uint32_t)lds, s, nullptr, e1, 0u, a, p, level);
+    hipExtLaunchKernelGGL(k_lmgemm, grid, block, 0u, s, nullptr, e1, 0u, a, p, level, per_xcd);
   else
-    hipLaunchKernelGGL(k_lmgemm, grid, block, lds, s, a, p, level);
+    hipLaunchKernelGGL(k_lmgemm, grid, block, 0, s, a, p, level, per_xcd);
   return hipGetLastError();
 }
 

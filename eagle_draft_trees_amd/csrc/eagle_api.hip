@@ -70,6 +70,29 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   p.S = cdiv(p.K, p.Kc);
   p.nps = op == OP_GATEUP ? cdiv(d.d, 64) : 0;
   p.part_floats = p.S > 1 ? (size_t)p.nblk * p.zg * p.S * 4 * p.nw * p.mt * 256 : 0;
+  // Many rows (bf16): 256 x 256 MFMA tiles (gate/up: 128 output columns of
+  // gate and up), K split into ranges of whole 4-step groups until the tiles
+  // about fill the 256 compute units; the partials always go through
+  // k_gemm_fin, which runs the epilogue.  Taken unless the split ranges
+  // would be short (under 32 k-steps): their fp32 partials then cost more
+  // than the skinny path's weight re-reads (o and fc at 512 rows x d 4096).
+  if (d.dtype == EAGLE_BF16 && M > 128 && p.K % 128 == 0) {
+    const int nsx = (p.hl ? 2 : 1) * p.K / 32;
+    const int tiles = cdiv(p.N, op == OP_GATEUP ? 128 : 256) * cdiv(M, 256);
+    const int S = std::max(1, std::min({256 / tiles, nsx / 16, GEMM_MAXS}));
+    const int tks = cdiv(cdiv(nsx, S), 4) * 4;
+    if (S == 1 || tks >= 32) {
+      p.tiled = 1;
+      p.tks = tks;
+      p.S = cdiv(nsx, tks);
+      p.Kc = tks * 32;
+      p.mt = 4;
+      p.zg = cdiv(M, 64);
+      p.ct = 4;
+      p.nblk = cdiv(p.N, 64);
+      p.part_floats = (size_t)p.nblk * p.zg * p.S * 4 * p.nw * p.mt * 256;
+    }
+  }
   return p;
 }
 
@@ -234,7 +257,8 @@ WsLayout plan_ws(const eagle_dims& d, const eagle_tree_cfg& c) {
   L.lmpart = take(lp * 4);
   L.lmres = take((size_t)std::max(B, rows_lv) * 2 * k * 4);
   // the batched LM head's input rows in fragment order (16 rows x 32 k per KB)
-  L.xpk = take(d.dtype == EAGLE_BF16 ? (size_t)cdiv(std::max(B, rows_lv), 16) * 16 * cdiv(d.d, 32) * 32 * 2 : 0);
+  // and the tiled layer GEMMs' X (q/k/v: x0's two parts, 2d)
+  L.xpk = take(d.dtype == EAGLE_BF16 ? (size_t)cdiv(std::max(B, (int)R), 16) * 16 * cdiv(2 * d.d, 32) * 32 * 2 : 0);
   // (tree verify: m rows per sequence)
   const size_t ap = std::max({plan_attn(MODE_LEVEL, k, d, c, B).part_floats,
                               plan_attn(MODE_EXTEND, re, d, c, B).part_floats,

@@ -271,7 +271,9 @@ struct GemmPlan {
   int hl;              // X in two bf16 parts (the bf16 q/k/v projection)
   int ct;              // column tiles per workgroup (3 or 4; 4 whenever K is split)
   int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
-  size_t part_floats;  // split-K partial floats (0 when S == 1)
+  size_t part_floats;  // split-K partial floats (0 when S == 1 on the skinny path)
+  int tiled;           // bf16, more than 128 rows, K a multiple of 128: k_gemm_tiled, then k_gemm_fin
+  int tks;             // tiled: X k-steps per split (a multiple of 4)
 };
 // K elements of one X chunk of a layer GEMM (the GW_KSW slices' k-steps)
 inline int gemm_kc(int nw, int es, bool hl = false) { return GW_KSW * gw_bu(nw, hl) * (es == 2 ? 32 : 16); }
@@ -479,6 +481,15 @@ __device__ __forceinline__ void ext_advance_state(const RoundArgs& a, int tid, i
   }
 }
 
+// Sine and cosine of the RoPE angle pos * inv (inv = theta^(-2i/hd) from the
+// workspace's fp64 table): the angle in fp64, reduced to [-pi, pi] in fp64,
+// then its sine and cosine in fp32 (the rotation itself is applied in fp32)
+__device__ __forceinline__ void rope_sincos(int pos, double inv, float& sn, float& cs) {
+  const double ang = (double)pos * inv;
+  const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+  sincosf((float)red, &sn, &cs);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *(const uint4*)p; }
 
 // x0 element idx of the layer's rows: fp32 (the residual), the dtype copy and,
@@ -549,6 +560,7 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
 int lmgemm_rows();  // rows per k_lmgemm tile
+hipError_t launch_gemm_tiled(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
                          hipEvent_t e1);
 // e0/e1 (may be null): events stamped at the LM-head kernel's own start and end

@@ -117,10 +117,8 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
         pos = clamp_prefix(a.prefix_len[b], a) + slot;
       }
       if (head < hq + hk) {  // q or k: rotate the (fi, fi+half) pair
-        const double inv = pow((double)a.theta, -2.0 * (double)fi / (double)a.hd);
-        double sd, cd;
-        sincos((double)pos * inv, &sd, &cd);
-        const float cs = (float)cd, sn = (float)sd;
+        float sn, cs;
+        rope_sincos(pos, a.rope[fi], sn, cs);
         const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;
         lo = nlo;
         hi = nhi;
@@ -501,6 +499,14 @@ static void launch_main(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
 
 template <typename T, int OP>
 static hipError_t launch_op(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
+  if (p.tiled) {  // many rows: the tiled MFMA GEMM writes partials, k_gemm_fin finishes
+    if (sizeof(T) != 2 || p.mt != 4) return hipErrorInvalidValue;
+    const hipError_t e = launch_gemm_tiled(OP, a, p, s);
+    if (e != hipSuccess) return e;
+    if (OP == OP_GATEUP && p.S == 1) return hipSuccess;  // epilogue in the tiled launch
+    hipLaunchKernelGGL((k_gemm_fin<T, OP, 4>), dim3(p.nblk, 1, p.zg), dim3(GW_FIN_THREADS), 0, s, a, p);
+    return hipGetLastError();
+  }
   if constexpr (OP != OP_O) {
     if (p.ct == 3) {
       if (p.S != 1) return hipErrorInvalidValue;  // three-tile blocks are never split

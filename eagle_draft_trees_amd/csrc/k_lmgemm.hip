@@ -10,19 +10,10 @@
 //  * a workgroup owns 256 rows x 256 vocabulary columns; each of its eight
 //    waves owns 128 rows x 64 columns (8 x 4 tiles of v_mfma_f32_16x16x32_bf16,
 //    128 fp32 accumulators per lane), so one 64-column slab per wave;
-//  * operands move from memory straight into LDS (global_load_lds_dwordx4:
-//    lane l's 16 bytes land at l*16, which is the MFMA fragment order that the
-//    packed weight tiles and the k_lg_xpack feature pack already have), one
-//    kilobyte fragment per wave instruction and no staging registers.  Four
-//    stage buffers of one k-step of 32 (32 KB each); a step's loads are issued
-//    three steps ahead, every wave issuing four of its 32 fragments;
-//  * the eight waves run as two groups of four (one wave of each group per
-//    SIMD) offset by half a step: while one group issues its sixteen MFMA
-//    fragments' worth of LDS reads and next loads, the other runs its 32
-//    MFMAs, so the matrix core of every SIMD always has a wave feeding it.
-//    Each half step ends in a workgroup barrier; each wave waits for its own
-//    loads (a fixed count: the loads past the last step repeat it into
-//    buffers that are not read again) and its LDS reads before it;
+//  * the main loop is the ping-pong MFMA core of the tiled GEMMs
+//    (mfma_pingpong.h): operands straight from memory into four LDS stage
+//    buffers, two wave groups offset by half a k-step so that every SIMD's
+//    matrix core always has a wave feeding it;
 //  * blocks are numbered so that each XCD (blocks b, b+8, ...) takes a
 //    contiguous run of tiles, the row tiles of one column block adjacent, so
 //    that a weight tile is fetched from memory once and re-read from that
@@ -32,24 +23,12 @@
 //    one lane per row over a column-major LDS tile in the stage buffers.
 #include <hip/hip_ext.h>
 
-#include "eagle_internal.h"
+#include "mfma_pingpong.h"
 
 namespace eg {
 
-constexpr int LG_W = 8;                 // waves per workgroup
-constexpr int LG_THREADS = LG_W * WAVE;
-constexpr int LG_ROWS = 256;            // rows per workgroup: 2 row groups of 128
-constexpr int LG_COLS = 256;            // columns per workgroup: 4 slabs of 64
-constexpr int LG_FR = (LG_ROWS + LG_COLS) / 16;   // 1 KB fragments per k-step (32)
-constexpr int LG_DMA = LG_FR / LG_W;              // fragments each wave loads per k-step (4)
-static_assert(LG_FR * 1024 == 32768 && LG_DMA == 4, "stage layout");
-// Four stage buffers, separate objects so that the compiler can tell the
-// loads into one from the LDS reads of another (it then adds no waits of its
-// own between them)
-__shared__ __attribute__((aligned(1024))) uint4 lg_s0[2048];
-__shared__ __attribute__((aligned(1024))) uint4 lg_s1[2048];
-__shared__ __attribute__((aligned(1024))) uint4 lg_s2[2048];
-__shared__ __attribute__((aligned(1024))) uint4 lg_s3[2048];
+constexpr int LG_ROWS = PP_TM;   // rows per workgroup: 2 row groups of 128
+constexpr int LG_COLS = PP_TN;   // columns per workgroup: 4 slabs of 64
 
 int lmgemm_rows() { return LG_ROWS; }
 
@@ -67,17 +46,10 @@ __global__ void __launch_bounds__(256) k_lg_xpack(const bf16_t* x, int M, int K,
   *(uint4*)(xpk + (size_t)blk * 512 + lane * 8) = v;
 }
 
-// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8): vmcnt(8) alone, and vmcnt(8) with lgkmcnt(0)
-constexpr int LG_WAIT_VM8 = 8 | (7 << 4) | (15 << 8);
-constexpr int LG_WAIT_VM8_LGKM0 = 8 | (7 << 4);
-constexpr int LG_WAIT_ALL = 0;
-
-__global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, int level, int per_xcd) {
+__global__ void __launch_bounds__(PP_THREADS) k_lmgemm(RoundArgs a, LmPlan p, int level, int per_xcd) {
   typedef bf16_t T;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool first = wave < 4;              // group that runs half a step ahead
   const int wm = wave & 1, wn = wave >> 1;  // 128-row group, 64-column slab
   const int K = a.d, kk_ = a.k;
   const int nks = K / 32;                   // a multiple of 4 (the plan checks)
@@ -92,86 +64,22 @@ __global__ void __launch_bounds__(LG_THREADS) k_lmgemm(RoundArgs a, LmPlan p, in
   // this wave's fragments 4*wave .. 4*wave+3 of every k-step: 0..15 the
   // feature groups of the row tile, 16..31 the weight tiles of the column
   // block (a group or tile past the last repeats the last)
-  const T* src[LG_DMA];
+  const T* src[PP_DMA];
 #pragma unroll
-  for (int u = 0; u < LG_DMA; ++u) {
-    const int f = LG_DMA * wave + u;
+  for (int u = 0; u < PP_DMA; ++u) {
+    const int f = PP_DMA * wave + u;
     src[u] = f < 16 ? (const T*)a.xpk + (size_t)min(rb * 16 + f, ngrp - 1) * nks * wtile_elems<T>() + lane * 8
                     : wtile_base<T>(a.lm_head, nks, min(cb * 16 + f - 16, ntile - 1), lane);
   }
-  auto dma = [&](uint4* buf, int s) __attribute__((always_inline)) {
-    s = min(s, nks - 1);
-#pragma unroll
-    for (int u = 0; u < LG_DMA; ++u)
-      __builtin_amdgcn_global_load_lds((const void*)(src[u] + (size_t)s * wtile_elems<T>()),
-                                       (__attribute__((address_space(3))) void*)(buf + (LG_DMA * wave + u) * WAVE),
-                                       16, 0, 0);
-  };
   f32x4_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 xa[8], wb[4];
-  auto rd = [&](const uint4* buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wb[q] = buf[(16 + 4 * wn + q) * WAVE + lane];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xa[i] = buf[(8 * wm + i) * WAVE + lane];
-  };
-  auto comp = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][q] = mma16(xa[i], wb[q], acc[i][q], T());
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // Step t: read buffer t%4 and issue step t+3's loads into buffer (t+3)%4
-  // (last read at step t-1, by the second group, before the barrier that
-  // precedes this half step), wait for step t+1's loads (the two later steps
-  // stay in flight) and the reads, barrier, MFMAs, barrier.  The first group
-  // reads step t while the second computes step t-1 and vice versa.
-  // (no branches inside the unrolled body: the compiler's wait analysis then
-  // keeps the loads in flight across the LDS reads)
-#define LG_STEP(BUF, NEXT, t)                       \
-  __builtin_amdgcn_sched_barrier(0);                \
-  rd(BUF);                                          \
-  __builtin_amdgcn_sched_barrier(0);                \
-  dma(NEXT, (t) + 3);                               \
-  __builtin_amdgcn_s_waitcnt(LG_WAIT_VM8_LGKM0);    \
-  __builtin_amdgcn_sched_barrier(0);                \
-  __builtin_amdgcn_s_barrier();                     \
-  __builtin_amdgcn_sched_barrier(0);                \
-  comp();                                           \
-  __builtin_amdgcn_sched_barrier(0);                \
-  __builtin_amdgcn_s_waitcnt(LG_WAIT_VM8);          \
-  __builtin_amdgcn_s_barrier();
-
-  dma(lg_s0, 0);
-  dma(lg_s1, 1);
-  dma(lg_s2, 2);
-  __builtin_amdgcn_s_waitcnt(LG_WAIT_VM8);
-  __builtin_amdgcn_s_barrier();
-  if (!first) __builtin_amdgcn_s_barrier();  // the second group starts half a step later
-  for (int t = 0; t < nks; t += 4) {
-    LG_STEP(lg_s0, lg_s3, t)
-    LG_STEP(lg_s1, lg_s0, t + 1)
-    LG_STEP(lg_s2, lg_s1, t + 2)
-    LG_STEP(lg_s3, lg_s2, t + 3)
-  }
-#undef LG_STEP
-  if (first) __builtin_amdgcn_s_barrier();   // (the same barrier count in both groups)
-  __builtin_amdgcn_s_waitcnt(LG_WAIT_ALL);   // the repeated loads past the last step
-  __syncthreads();
+  pp_main(nks, [&](int u, int s) -> const void* { return src[u] + (size_t)s * wtile_elems<T>(); }, acc);
 
   // ---- epilogue, two passes of 64 rows per wave: the wave's 64 x 64 block
   // goes column-major to a 16 KB tile (half of a stage buffer), row r of
   // column c at c*64 + (r ^ 4*(c%16)) (float4 stores of 16 columns spread
   // over the banks, reads of one column by 64 lanes a permutation of one
   // 64-float run); lane r then reduces row r of the pass over the 64 columns
-  uint4* tb = (wave >> 1) == 0 ? lg_s0 : (wave >> 1) == 1 ? lg_s1 : (wave >> 1) == 2 ? lg_s2 : lg_s3;
-  float* tile = (float*)tb + (wave & 1) * 64 * 64;
+  float* tile = pp_scratch(wave >> 1, wave & 1);
   const int c = lane & 15, g = lane >> 4;
   const int slab = cb * 4 + wn;
   const int cbase = slab * 64;
@@ -244,7 +152,7 @@ hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStre
   else
     hipLaunchKernelGGL(k_lg_xpack, pgrid, dim3(256), 0, s, x, p.M, K, nks, nblocks, (bf16_t*)a.xpk);
   const int ntiles = (a.V + LG_COLS - 1) / LG_COLS * p.zg, per_xcd = (ntiles + 7) / 8;
-  const dim3 grid(per_xcd * 8), block(LG_THREADS);
+  const dim3 grid(per_xcd * 8), block(PP_THREADS);
   if (e1)
     hipExtLaunchKernelGGL(k_lmgemm, grid, block, 0u, s, nullptr, e1, 0u, a, p, level, per_xcd);
   else

@@ -235,11 +235,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
         if (rot) {
           const int pos = lv ? P - 1 + a.depth : P + slot;
           if (pos != lastpos) {
-            // the angle pos * theta^(-2i/hd) in fp64, reduced to [-pi, pi] in fp64, then
-            // its sine and cosine in fp32 (the rotation is applied in fp32)
-            const double ang = (double)pos * inv;
-            const double red = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
-            sincosf((float)red, &sn, &cs);
+            rope_sincos(pos, inv, sn, cs);
             lastpos = pos;
           }
           const float nlo = lo * cs - hi * sn, nhi = hi * cs + lo * sn;

@@ -191,6 +191,13 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
     p.nblk = cdiv(d.vocab, 64);
     p.big = d.dtype == EAGLE_BF16 && M > 64 && d.d % 128 == 0;
     if (p.big) p.zg = cdiv(M, lmgemm_rows());
+    // 17..64 rows: the streaming kernel, 128 * nq columns per workgroup with
+    // nq the smallest that keeps the workgroups to about one per compute unit
+    // (k-steps a multiple of the loop's unroll: 8 with nq 1, else 4)
+    if (d.dtype == EAGLE_BF16 && M <= 64 && d.d % 128 == 0) {
+      p.nq = std::min(4, std::max(1, cdiv(cdiv(d.vocab, 16), 8 * 256)));
+      if (p.nq == 1 && d.d % 256) p.nq = 2;
+    }
   }
   p.rec = 2 + 2 * topk;
   p.part_floats = (size_t)M * p.nblk * p.rec;

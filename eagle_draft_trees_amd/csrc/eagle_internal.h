@@ -301,6 +301,7 @@ struct LmPlan {
   int M, mt, zg, nblk, rec;  // rec = floats per (row, slab) partial; nblk = slabs
   int sk, CT, KSW, xlds;     // sk: streaming-core kernel (M <= 16), CT tiles x KSW waves
   int big;                   // bf16, more than 64 rows, d a multiple of 128: the tiled GEMM (k_lmgemm), zg row tiles
+  int nq;                    // bf16, 17..64 rows, d a multiple of 128: k_lmrows with nq 16-column tiles per wave
   size_t part_floats;
 };
 
@@ -561,6 +562,8 @@ hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
 int lmgemm_rows();  // rows per k_lmgemm tile
 hipError_t launch_gemm_tiled(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
+hipError_t launch_lmrows(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
+                         hipEvent_t e1);
 hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
                          hipEvent_t e1);
 // e0/e1 (may be null): events stamped at the LM-head kernel's own start and end
@@ -570,6 +573,44 @@ hipError_t launch_lmgemm(const RoundArgs& a, const LmPlan& p, int level, hipStre
 // field of every slab is contiguous.  Returns the address of field 0.
 __device__ __forceinline__ float* slab_field(float* lmpart, int row, int blk, const LmPlan& p) {
   return lmpart + (size_t)row * p.rec * p.nblk + blk;
+}
+// One row's record of one 64-column slab, from the row's 64 logits in
+// registers (columns past the vocabulary at -inf): max, sum of exp(v - max),
+// and the top-k by (logit desc, id asc).  Pass r takes the best column below
+// the previous pick in that order; scanning columns upward, a strictly
+// greater value wins, so the lowest column of equal values is taken.
+__device__ __forceinline__ void lm_slab_record(const RoundArgs& a, const LmPlan& p, const float (&v)[64], int row,
+                                               int slab, int cbase) {
+  const int kk_ = a.k;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int col = 0; col < 64; ++col) mx = fmaxf(mx, v[col]);
+  float se = 0.f;
+#pragma unroll
+  for (int col = 0; col < 64; ++col) se += v[col] == -INFINITY ? 0.f : expf(v[col] - mx);
+  if (row < p.M && slab < p.nblk) {
+    float* rec = slab_field(a.lmpart, row, slab, p);  // field f at rec[f * nblk]
+    rec[0] = mx;
+    rec[p.nblk] = se;
+    float pv = INFINITY;
+    int pc = -1;
+    for (int r = 0; r < kk_; ++r) {
+      float bv = -INFINITY;
+      int bc = -1;
+#pragma unroll
+      for (int col = 0; col < 64; ++col) {
+        const bool below = v[col] < pv || (v[col] == pv && col > pc);
+        if (below && v[col] > bv) {
+          bv = v[col];
+          bc = col;
+        }
+      }
+      rec[(2 + r) * p.nblk] = bc >= 0 ? bv : -INFINITY;
+      rec[(2 + kk_ + r) * p.nblk] = __int_as_float(bc >= 0 ? cbase + bc : -1);
+      pv = bc >= 0 ? bv : -INFINITY;
+      pc = bc >= 0 ? bc : 64;
+    }
+  }
 }
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
                          hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);

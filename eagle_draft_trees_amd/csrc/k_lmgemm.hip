@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(PP_THREADS) k_lmgemm(RoundArgs a, LmPlan p, in
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;  // 128-row group, 64-column slab
-  const int K = a.d, kk_ = a.k;
+  const int K = a.d;
   const int nks = K / 32;                   // a multiple of 4 (the plan checks)
   const int ngrp = (p.M + 15) / 16, ntile = (a.V + 15) / 16;
   const int ncb = (a.V + LG_COLS - 1) / LG_COLS, ntiles = ncb * p.zg;
@@ -102,38 +102,7 @@ __global__ void __launch_bounds__(PP_THREADS) k_lmgemm(RoundArgs a, LmPlan p, in
 #pragma unroll
     for (int col = 0; col < 64; ++col)
       v[col] = cbase + col < a.V ? tile[col * 64 + (lane ^ (4 * (col & 15)))] : -INFINITY;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int col = 0; col < 64; ++col) mx = fmaxf(mx, v[col]);
-    float se = 0.f;
-#pragma unroll
-    for (int col = 0; col < 64; ++col) se += v[col] == -INFINITY ? 0.f : expf(v[col] - mx);
-    if (row < p.M && slab < p.nblk) {  // (the last column block may reach past V)
-      float* rec = slab_field(a.lmpart, row, slab, p);  // field f at rec[f * nblk]
-      rec[0] = mx;
-      rec[p.nblk] = se;
-      // top-k by (logit desc, id asc): pass r takes the best column below the
-      // previous pick in that order; scanning columns upward, a strictly
-      // greater value wins, so the lowest column of equal values is taken
-      float pv = INFINITY;
-      int pc = -1;
-      for (int r = 0; r < kk_; ++r) {
-        float bv = -INFINITY;
-        int bc = -1;
-#pragma unroll
-        for (int col = 0; col < 64; ++col) {
-          const bool below = v[col] < pv || (v[col] == pv && col > pc);
-          if (below && v[col] > bv) {
-            bv = v[col];
-            bc = col;
-          }
-        }
-        rec[(2 + r) * p.nblk] = bc >= 0 ? bv : -INFINITY;
-        rec[(2 + kk_ + r) * p.nblk] = __int_as_float(bc >= 0 ? cbase + bc : -1);
-        pv = bc >= 0 ? bv : -INFINITY;
-        pc = bc >= 0 ? bc : 64;
-      }
-    }
+    lm_slab_record(a, p, v, row, slab, cbase);
     __builtin_amdgcn_wave_barrier();  // the tile is rewritten by the next pass
   }
 }

@@ -290,6 +290,7 @@ static hipError_t launch_lmsk_t(const RoundArgs& a, const LmPlan& p, int level, 
 hipError_t launch_lmhead(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
                          hipEvent_t e0, hipEvent_t e1) {
   if (p.big) return launch_lmgemm(a, p, level, s, e0, e1);
+  if (p.nq) return launch_lmrows(a, p, level, s, e0, e1);
   if (p.sk)
     return a.dtype == EAGLE_BF16 ? launch_lmsk_t<bf16_t>(a, p, level, s, e0, e1)
                                  : launch_lmsk_t<float>(a, p, level, s, e0, e1);

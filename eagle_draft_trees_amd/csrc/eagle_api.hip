@@ -93,6 +93,38 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
       p.part_floats = (size_t)p.nblk * p.zg * p.S * 4 * p.nw * p.mt * 256;
     }
   }
+  // 17..64 rows (bf16), FC, O and down: the streaming kernel, 128*nq
+  // columns per workgroup, nq the smallest that keeps the column blocks to
+  // about one workgroup per compute unit; when they number under 128, K split
+  // so that the workgroups about fill the compute units.  Partials go through
+  // k_gemm_fin, which runs the epilogue.  q/k/v and gate/up stay on k_gemm:
+  // they need no split there (so no finishing launch), and at one weight tile
+  // per wave the streaming kernel's row-gathered X loads cost as much as
+  // the split saves (measured at 40 and 64 rows, d 4096-8192).
+  if (!p.tiled && d.dtype == EAGLE_BF16 && M >= 17 && M <= 64 && p.K % 256 == 0 &&
+      (op == OP_FC || op == OP_O || op == OP_DOWN)) {
+    const bool xs2 = op == OP_QKV && p.hl;  // q/k/v: two X sets, at most two tiles per wave
+    const int ntile = cdiv(p.N, 16), nks = p.K / 32;
+    const int nwg1 = cdiv(ntile, 8 / p.nw);
+    int nq = 1, S = 1;
+    if (nwg1 >= 128) {
+      nq = std::min(xs2 ? 2 : 4, cdiv(nwg1, 256));
+      if (nq == 3) nq = 4;
+    } else {
+      S = std::max(1, std::min(256 / nwg1, nks / 16));
+    }
+    const int U = (nq == 1 && !xs2) ? 8 : 4;  // k-steps per loop iteration
+    p.rows = 1;
+    p.nq = nq;
+    p.tks = cdiv(cdiv(nks, S), U) * U;
+    p.S = cdiv(nks, p.tks);
+    p.Kc = p.tks * 32;
+    p.mt = cdiv(M, 16);
+    p.zg = 1;
+    p.ct = 4;
+    p.nblk = cdiv(p.N, 64);
+    p.part_floats = (size_t)p.nblk * p.S * 4 * p.nw * p.mt * 256;
+  }
   return p;
 }
 
@@ -193,10 +225,13 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
     if (p.big) p.zg = cdiv(M, lmgemm_rows());
     // 17..64 rows: the streaming kernel, 128 * nq columns per workgroup with
     // nq the smallest that keeps the workgroups to about one per compute unit
-    // (k-steps a multiple of the loop's unroll: 8 with nq 1, else 4)
+    // (k-steps a multiple of the loop's unroll, 4).  With one weight tile per
+    // wave (vocabularies up to 32768) k_lmhead stays: there the streaming
+    // kernel's row-gathered X loads are as many as its weight loads and it
+    // measured slower at 40 rows x d 8192 (145 vs 107 us).
     if (d.dtype == EAGLE_BF16 && M <= 64 && d.d % 128 == 0) {
-      p.nq = std::min(4, std::max(1, cdiv(cdiv(d.vocab, 16), 8 * 256)));
-      if (p.nq == 1 && d.d % 256) p.nq = 2;
+      const int nq = std::min(4, cdiv(cdiv(d.vocab, 16), 8 * 256));
+      if (nq >= 2) p.nq = nq;
     }
   }
   p.rec = 2 + 2 * topk;

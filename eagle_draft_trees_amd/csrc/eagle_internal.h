@@ -273,7 +273,9 @@ struct GemmPlan {
   int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
   size_t part_floats;  // split-K partial floats (0 when S == 1 on the skinny path)
   int tiled;           // bf16, more than 128 rows, K a multiple of 128: k_gemm_tiled, then k_gemm_fin
-  int tks;             // tiled: X k-steps per split (a multiple of 4)
+  int tks;             // tiled / rows: k-steps per split (a multiple of the main loop's unroll)
+  int rows;            // bf16, 17..64 rows, K a multiple of 256: k_gemm_rows, then k_gemm_fin
+  int nq;              // rows: 16-column weight tiles per wave
 };
 // K elements of one X chunk of a layer GEMM (the GW_KSW slices' k-steps)
 inline int gemm_kc(int nw, int es, bool hl = false) { return GW_KSW * gw_bu(nw, hl) * (es == 2 ? 32 : 16); }
@@ -561,6 +563,7 @@ __device__ __forceinline__ void block_argmax(float& v, int& id, float* sv, int* 
 hipError_t launch_gemm(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_skinny(int op, const RoundArgs& a, const SkPlan& p, hipStream_t s);
 int lmgemm_rows();  // rows per k_lmgemm tile
+hipError_t launch_gemm_rows(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_gemm_tiled(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s);
 hipError_t launch_lmrows(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s, hipEvent_t e0,
                          hipEvent_t e1);

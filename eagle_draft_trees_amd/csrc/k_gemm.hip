@@ -499,6 +499,18 @@ static void launch_main(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
 
 template <typename T, int OP>
 static hipError_t launch_op(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
+  if (p.rows) {  // 17..64 rows: the streaming GEMM writes partials, k_gemm_fin finishes
+    if (sizeof(T) != 2) return hipErrorInvalidValue;
+    const hipError_t e = launch_gemm_rows(OP, a, p, s);
+    if (e != hipSuccess) return e;
+    switch (p.mt) {
+      case 1: hipLaunchKernelGGL((k_gemm_fin<T, OP, 1>), dim3(p.nblk), dim3(GW_FIN_THREADS), 0, s, a, p); break;
+      case 2: hipLaunchKernelGGL((k_gemm_fin<T, OP, 2>), dim3(p.nblk), dim3(GW_FIN_THREADS), 0, s, a, p); break;
+      case 3: hipLaunchKernelGGL((k_gemm_fin<T, OP, 3>), dim3(p.nblk), dim3(GW_FIN_THREADS), 0, s, a, p); break;
+      default: hipLaunchKernelGGL((k_gemm_fin<T, OP, 4>), dim3(p.nblk), dim3(GW_FIN_THREADS), 0, s, a, p); break;
+    }
+    return hipGetLastError();
+  }
   if (p.tiled) {  // many rows: the tiled MFMA GEMM writes partials, k_gemm_fin finishes
     if (sizeof(T) != 2 || p.mt != 4) return hipErrorInvalidValue;
     const hipError_t e = launch_gemm_tiled(OP, a, p, s);

@@ -103,17 +103,16 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   // the split saves (measured at 40 and 64 rows, d 4096-8192).
   if (!p.tiled && d.dtype == EAGLE_BF16 && M >= 17 && M <= 64 && p.K % 256 == 0 &&
       (op == OP_FC || op == OP_O || op == OP_DOWN)) {
-    const bool xs2 = op == OP_QKV && p.hl;  // q/k/v: two X sets, at most two tiles per wave
     const int ntile = cdiv(p.N, 16), nks = p.K / 32;
-    const int nwg1 = cdiv(ntile, 8 / p.nw);
+    const int nwg1 = cdiv(ntile, 8);
     int nq = 1, S = 1;
     if (nwg1 >= 128) {
-      nq = std::min(xs2 ? 2 : 4, cdiv(nwg1, 256));
+      nq = std::min(4, cdiv(nwg1, 256));
       if (nq == 3) nq = 4;
     } else {
       S = std::max(1, std::min(256 / nwg1, nks / 16));
     }
-    const int U = (nq == 1 && !xs2) ? 8 : 4;  // k-steps per loop iteration
+    const int U = nq == 1 ? 8 : 4;  // k-steps per loop iteration
     p.rows = 1;
     p.nq = nq;
     p.tks = cdiv(cdiv(nks, S), U) * U;
@@ -123,7 +122,7 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
     p.zg = 1;
     p.ct = 4;
     p.nblk = cdiv(p.N, 64);
-    p.part_floats = (size_t)p.nblk * p.S * 4 * p.nw * p.mt * 256;
+    p.part_floats = (size_t)p.nblk * p.S * 4 * p.mt * 256;
   }
   return p;
 }

@@ -18,9 +18,6 @@
 //  * with one weight tile per wave (NQ = 1) a stage holds two k-steps (8 X
 //    and 16 weight fragments, 24 KB: three loads per wave, no repeats), so a
 //    barrier covers two k-steps and the loads run six k-steps ahead;
-//  * with two X sets (XS = 2: the q/k/v projection's x0 as a high and a low
-//    bf16 part, both against the same weights) a stage holds 8 X and 8*NQ
-//    weight fragments (NQ <= 2), NQ+1 loads per wave, no repeats;
 //  * each stage t: wait for its loads and the previous stage's LDS reads,
 //    one workgroup barrier, issue the loads of stage t+3 into the buffer
 //    stage t-1 used, read the X fragments and the wave's weight fragments,
@@ -43,14 +40,14 @@ static __shared__ __attribute__((aligned(1024))) uint4 ps_s0[PS_STAGE];
 static __shared__ __attribute__((aligned(1024))) uint4 ps_s1[PS_STAGE];
 static __shared__ __attribute__((aligned(1024))) uint4 ps_s2[PS_STAGE];
 static __shared__ __attribute__((aligned(1024))) uint4 ps_s3[PS_STAGE];
-constexpr int PS_STAGE1 = 24 * 64;  // uint4 per stage buffer with NQ = 1 (two k-steps) or two X sets: 24 KB
+constexpr int PS_STAGE1 = 24 * 64;  // uint4 per stage buffer with NQ = 1 (two k-steps, 24 KB)
 static __shared__ __attribute__((aligned(1024))) uint4 ps_t0[PS_STAGE1];
 static __shared__ __attribute__((aligned(1024))) uint4 ps_t1[PS_STAGE1];
 static __shared__ __attribute__((aligned(1024))) uint4 ps_t2[PS_STAGE1];
 static __shared__ __attribute__((aligned(1024))) uint4 ps_t3[PS_STAGE1];
 
 // k-steps per unrolled loop body (four stage buffers)
-template <int NQ, int XS = 1> constexpr int ps_unroll() { return NQ == 1 && XS == 1 ? 8 : 4; }
+template <int NQ> constexpr int ps_unroll() { return NQ == 1 ? 8 : 4; }
 
 // s_waitcnt immediate (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8) of vmcnt(n) with lgkmcnt(0)
@@ -62,10 +59,9 @@ __host__ __device__ constexpr int ps_wait_vm_lgkm0(int n) { return (n & 15) | ((
 // srcw(q, s): this lane's 16 bytes of the wave's weight tile q at step s.
 // Every wave of the workgroup must call it; it ends with the loads drained
 // and a workgroup barrier, the stage buffers free for the caller.
-template <int NQ, int XS = 1, typename SrcX, typename SrcW>
+template <int NQ, typename SrcX, typename SrcW>
 __device__ __forceinline__ void ps_main(int nsteps, const SrcX& srcx, const SrcW& srcw, f32x4_t (&acc)[4][NQ]) {
   static_assert(NQ >= 1 && NQ <= PS_MAXQ, "weight tiles per wave");
-  static_assert(XS == 1 || (XS == 2 && NQ <= 2), "two X sets: at most two weight tiles per wave");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto lds = [](uint4* p) __attribute__((always_inline)) { return (__attribute__((address_space(3))) void*)p; };
@@ -85,43 +81,7 @@ __device__ __forceinline__ void ps_main(int nsteps, const SrcX& srcx, const SrcW
   dma(NEXT, (t) + 3);                         \
   __builtin_amdgcn_sched_barrier(0);          \
   step(BUF);
-  if constexpr (XS == 2) {
-    // two X sets (x = x_hi + x_lo): X fragment (wave % 4) of set wave / 4 at
-    // slot `wave` (srcx(s) gives each wave its own set), the wave's weight
-    // tiles at slots 8 + NQ*wave + q; every X fragment meets every weight
-    // fragment of the step
-    constexpr int WAIT = ps_wait_vm_lgkm0(2 * (NQ + 1));
-    auto dma = [&](uint4* buf, int s) __attribute__((always_inline)) {
-      s = min(s, nsteps - 1);  // past the last step: repeats it into a buffer not read again
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        __builtin_amdgcn_global_load_lds(srcw(q, s), lds(buf + (8 + NQ * wave + q) * WAVE), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(srcx(s), lds(buf + wave * WAVE), 16, 0, 0);
-    };
-    auto step = [&](const uint4* buf) __attribute__((always_inline)) {
-      uint4 xa[8], wb[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) wb[q] = buf[(8 + NQ * wave + q) * WAVE + lane];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xa[i] = buf[i * WAVE + lane];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          acc[mt][q] = mma16(xa[mt], wb[q], acc[mt][q], bf16_t());
-          acc[mt][q] = mma16(xa[4 + mt], wb[q], acc[mt][q], bf16_t());
-        }
-    };
-    dma(ps_t0, 0);
-    dma(ps_t1, 1);
-    dma(ps_t2, 2);
-    for (int t = 0; t < nsteps; t += 4) {
-      PS_STEP(ps_t0, ps_t3, t)
-      PS_STEP(ps_t1, ps_t0, t + 1)
-      PS_STEP(ps_t2, ps_t1, t + 2)
-      PS_STEP(ps_t3, ps_t2, t + 3)
-    }
-  } else if constexpr (NQ == 1) {
+  if constexpr (NQ == 1) {
     // a stage is k-steps 2t, 2t+1: X fragment (wave % 4) of k-step 2t + wave/4
     // at slot `wave`, the wave's weight tile of k-step 2t + kk at slot
     // 8 + 8 kk + wave

@@ -116,11 +116,18 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int q = lane & 15, g = lane >> 4;
-  // split-major block order: consecutive blocks (which land on different
-  // XCDs) take the splits of one tile, so each XCD reads whole cache rows
-  // (every head of a row range) instead of one head's 256-byte slice of rows
-  const int split = blockIdx.x % p.nsplit, wg = blockIdx.x / p.nsplit;
-  const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
+  // Block order.  Group gi = (sequence, KV head, split), split-major:
+  // consecutive groups (which land on different XCDs) take the splits of one
+  // KV head, so each XCD reads whole cache rows (every head of a row range)
+  // instead of one head's 256-byte slice of rows.  Block b runs on XCD b % 8;
+  // the query tiles of one group (GQA: several query heads share a KV head)
+  // are blocks b, b+8, ... on that one XCD, so they read its K/V through that
+  // XCD's L2 instead of once per XCD.  Blocks past the last group end here.
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int gi = (jx / p.nqt) * 8 + xcd, qt = jx % p.nqt;
+  if (gi >= a.B * a.Hkv * p.nsplit) return;
+  const int split = gi % p.nsplit, bk = gi / p.nsplit, kvh = bk % a.Hkv, b = bk / a.Hkv;
+  const int wg = bk * p.nqt + qt;
   const int q0 = qt * AT_Q;
   const int P = clamp_prefix(a.prefix_len[b], a);
   const bool level = a.mode == MODE_LEVEL, verify = a.mode == MODE_VERIFY;
@@ -593,8 +600,8 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPla
 
 template <typename T, int HD>
 static hipError_t launch_attn_t(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
-  const int tiles = a.B * a.Hkv * p.nqt;
-  hipLaunchKernelGGL((k_attn<T, HD>), dim3(tiles * p.nsplit), dim3(AT_W * WAVE), 0, s, a, p);
+  const int tiles = a.B * a.Hkv * p.nqt, groups = a.B * a.Hkv * p.nsplit;
+  hipLaunchKernelGGL((k_attn<T, HD>), dim3((groups + 7) / 8 * 8 * p.nqt), dim3(AT_W * WAVE), 0, s, a, p);
   if (p.nsplit > 1) hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(tiles), dim3(AT_W * WAVE), 0, s, a, p);
   return hipGetLastError();
 }

@@ -93,16 +93,17 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
       p.part_floats = (size_t)p.nblk * p.zg * p.S * 4 * p.nw * p.mt * 256;
     }
   }
-  // 17..64 rows (bf16), FC, O and down: the streaming kernel, 128*nq
-  // columns per workgroup, nq the smallest that keeps the column blocks to
-  // about one workgroup per compute unit; when they number under 128, K split
-  // so that the workgroups about fill the compute units.  Partials go through
-  // k_gemm_fin, which runs the epilogue.  q/k/v and gate/up stay on k_gemm:
-  // they need no split there (so no finishing launch), and at one weight tile
-  // per wave the streaming kernel's row-gathered X loads cost as much as
-  // the split saves (measured at 40 and 64 rows, d 4096-8192).
+  // 17..64 rows (bf16), O and down, and FC where k_gemm would split K: the
+  // streaming kernel, 128*nq columns per workgroup, nq the smallest that
+  // keeps the column blocks to about one workgroup per compute unit; when they
+  // number under 128, K split so that the workgroups about fill the compute
+  // units.  Partials go through k_gemm_fin, which runs the epilogue.  q/k/v,
+  // gate/up and an unsplit FC stay on k_gemm: there they need no finishing
+  // launch, and at one weight tile per wave the streaming kernel's
+  // row-gathered X loads cost about what its split saves (measured at 40 and
+  // 64 rows, d 4096-8192).
   if (!p.tiled && d.dtype == EAGLE_BF16 && M >= 17 && M <= 64 && p.K % 256 == 0 &&
-      (op == OP_FC || op == OP_O || op == OP_DOWN)) {
+      (op == OP_O || op == OP_DOWN || (op == OP_FC && p.S > 1))) {
     const int ntile = cdiv(p.N, 16), nks = p.K / 32;
     const int nwg1 = cdiv(ntile, 8);
     int nq = 1, S = 1;

@@ -457,6 +457,22 @@ def measure_rounds(torch, r, stream, steps, warmup, graph=True) -> dict:
     return out
 
 
+def lm_kernel_name(cfg, rows) -> str:
+    """The LM-head kernel the library's plan takes for `rows` rows: up to 16
+    the skinny streaming kernel; bf16 with d a multiple of 128, the batched
+    MFMA GEMM above 64 rows and, from 17 to 64 rows, the streaming MFMA
+    kernel when the vocabulary gives each wave at least two 16-column weight
+    tiles (more than 32768 columns); else k_lmhead."""
+    if rows <= 16:
+        return "k_lmskinny"
+    tiled = cfg.dtype == "bf16" and cfg.d % 128 == 0
+    if tiled and rows > 64:
+        return "k_lg_xpack + k_lmgemm"
+    if tiled and -(-cfg.V // 16) > 8 * 256:
+        return "k_lmrows"
+    return "k_lmhead"
+
+
 def lmhead_roofline(torch, L, r, cfg, stream, steps, scrub) -> dict:
     """The dominant kernel, the LM-head GEMM with its fused per-slab softmax
     and top-k, timed live on the stream it runs on: a LMHEAD_ONLY level call
@@ -491,10 +507,8 @@ def lmhead_roofline(torch, L, r, cfg, stream, steps, scrub) -> dict:
     nbytes = es * cfg.V * cfg.d
     rows = cfg.B * cfg.k
     gbps = nbytes / (lm_ms * 1e-3) / 1e9
-    kernel = ("k_lmskinny" if rows <= 16 else "k_lmhead" if rows <= 64 or cfg.dtype != "bf16" else
-              "k_lg_xpack + k_lmgemm")
-    return {"kernel": f"{kernel} (LM-head GEMM + per-slab softmax/top-k, {rows} rows)",
-            "scope": "the round's dominant kernel (the largest share of a round's time)",
+    return {"kernel": f"{lm_kernel_name(cfg, rows)} (LM-head GEMM + per-slab softmax/top-k, {rows} rows)",
+            "scope": "the LM-head GEMM (the largest share of the 7B-shaped round's time)",
             "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(lm_ms * 1e3, 2),
             "timing": f"{n_lm} launches, HIP events stamped by the kernel's dispatch "

@@ -76,7 +76,7 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
   // k_gemm_fin, which runs the epilogue.  Taken unless the split ranges
   // would be short (under 32 k-steps): their fp32 partials then cost more
   // than the skinny path's weight re-reads (o and fc at 512 rows x d 4096).
-  if (d.dtype == EAGLE_BF16 && M > 128 && p.K % 128 == 0) {
+  if (d.dtype == EAGLE_BF16 && M > 64 && p.K % 128 == 0) {
     const int nsx = (p.hl ? 2 : 1) * p.K / 32;
     const int tiles = cdiv(p.N, op == OP_GATEUP ? 128 : 256) * cdiv(M, 256);
     const int S = std::max(1, std::min({256 / tiles, nsx / 16, GEMM_MAXS}));

@@ -272,7 +272,7 @@ struct GemmPlan {
   int ct;              // column tiles per workgroup (3 or 4; 4 whenever K is split)
   int nps;             // gate/up: RMSNorm partial sums per row written by the O launch
   size_t part_floats;  // split-K partial floats (0 when S == 1 on the skinny path)
-  int tiled;           // bf16, more than 128 rows, K a multiple of 128: k_gemm_tiled, then k_gemm_fin
+  int tiled;           // bf16, more than 64 rows, K a multiple of 128: k_gemm_tiled, then k_gemm_fin
   int tks;             // tiled / rows: k-steps per split (a multiple of the main loop's unroll)
   int rows;            // bf16, 17..64 rows, K a multiple of 256: k_gemm_rows, then k_gemm_fin
   int nq;              // rows: 16-column weight tiles per wave

@@ -1,4 +1,4 @@
-// Layer GEMMs of many rows (bf16, more than 128 rows: the extend of a large
+// Layer GEMMs of many rows (bf16, more than 64 rows: the extend of a large
 // batch, or a wide frontier) on the tiled MFMA core.
 //
 // [P3] zdszero.github.io spec_medusa_eagle, "在 SGLang 里": the draft extend

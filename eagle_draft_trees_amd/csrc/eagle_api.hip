@@ -111,7 +111,7 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
       nq = std::min(4, cdiv(nwg1, 256));
       if (nq == 3) nq = 4;
     } else {
-      S = std::max(1, std::min(256 / nwg1, nks / 16));
+      S = std::max(1, std::min({256 / nwg1, nks / 16, GEMM_MAXS}));
     }
     const int U = nq == 1 ? 8 : 4;  // k-steps per loop iteration
     p.rows = 1;

@@ -7,10 +7,10 @@
 //
 // k_lmhead (one launch over the vocabulary): four waves per workgroup each
 // stream 16 LM-head rows against the M feature rows (MFMA, A operand from
-// LDS, X staged in K chunks, the next weight loads issued before the current
-// MFMAs); the 64-column logit tile goes to LDS and each row's slab is reduced
-// to (max, sum exp) and its top-k (logit desc, id asc).  Logits never leave
-// the chip.
+// LDS, X staged in K chunks with the next chunk's loads in flight during the
+// current chunk, the next weight loads issued before the current MFMAs); the
+// 64-column logit tile goes to LDS and each row's slab is reduced to (max,
+// sum exp) and its top-k (logit desc, id asc).  Logits never leave the chip.
 #include <hip/hip_ext.h>
 #include <float.h>
 
@@ -107,12 +107,14 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   __syncthreads();
   int it = 0;
   for (int kc = 0; kc < K; kc += KCH) {
-    if (kc > 0) {  // next X chunk: drains the pipeline once per chunk
+    if (kc > 0) {  // this chunk's X, loaded during the previous chunk, into LDS
       __syncthreads();
-      stage_load(kc);
       stage_store();
       __syncthreads();
     }
+    // the next chunk's X in flight during this chunk's MFMAs (older than the
+    // weight loads issued meanwhile, so storing it waits for it alone)
+    if (kc + KCH < K) stage_load(kc + KCH);
     const int itend = min(nit, (kc + KCH) / (U * KS));
     for (; it + 1 < itend; it += 2) {
       wload(wb, it + 1);

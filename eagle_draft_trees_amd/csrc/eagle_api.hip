@@ -253,6 +253,10 @@ AttnPlan plan_attn(int mode, int RS, const eagle_dims& d, const eagle_tree_cfg& 
   const int chunks = cdiv(keys, 16);
   p.nsplit = std::max(1, std::min({8, cdiv(256, tiles), std::max(1, chunks / 4)}));
   p.part_floats = p.nsplit > 1 ? (size_t)tiles * p.nsplit * 16 * (d.head_dim + 4) : 0;
+  // four-wave workgroups (three per compute unit) when the launch fits in one
+  // such round but not in one of eight-wave workgroups
+  const int wgs = tiles * p.nsplit;
+  p.waves = wgs > 256 && wgs <= 768 ? 4 : 8;
   return p;
 }
 

@@ -310,6 +310,7 @@ struct LmPlan {
 struct AttnPlan {
   int RS, g, nq, nqt;  // rows per sequence, GQA group, queries per KV head, 16-query tiles
   int nsplit;          // key splits per tile (partials merged by a second kernel when > 1)
+  int waves;           // waves per workgroup: 4 (three workgroups per CU) or 8 (one)
   size_t part_floats;  // split partials
 };
 

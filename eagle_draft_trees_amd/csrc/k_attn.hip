@@ -14,8 +14,8 @@
 // row j iff mask[i][j] is set.
 //
 // One workgroup per (sequence, KV head, tile of 16 queries); the queries of a
-// tile are (row, head of the GQA group) pairs.  Its eight waves split the keys
-// in chunks of 16: the prefix rows first, then (levels) every in-tree slot of
+// tile are (row, head of the GQA group) pairs.  Its waves split the keys in
+// chunks of 16: the prefix rows first, then (levels) every in-tree slot of
 // depths 1..L as extra keys, masked per query to that query's ancestors and
 // itself.  Per chunk a wave
 //   * computes the 16x16 score tile S^T = K Q^T on MFMA (bf16: q split into a
@@ -28,11 +28,20 @@
 // The next chunk's K and V loads are in flight while a chunk computes.  The
 // waves' partial (max, sum, output) meet in LDS and are combined in wave order
 // (deterministic); there is no cross-workgroup step.  Scores 1/sqrt(hd) q.k.
+//
+// A workgroup has four or eight waves.  Every wave uses the same query operand,
+// which sits in LDS and is read there at each chunk: held in registers it
+// would take 32 per lane (bf16 hd 128) and leave room for only one workgroup
+// per compute unit.  Four waves then fit three workgroups per compute unit,
+// which pays when the launch has a few hundred workgroups (they all run at
+// once instead of in rounds); eight waves keep more keys in flight per
+// workgroup where the launch has one workgroup per compute unit or fewer, or
+// many rounds of them.
 #include "eagle_internal.h"
 
 namespace eg {
 
-constexpr int AT_W = 8;       // waves per workgroup
+constexpr int AT_MW = 4;      // waves per workgroup of the split merge
 constexpr int AT_Q = 16;      // queries per workgroup (one MFMA tile)
 constexpr int AT_C = 16;      // keys per chunk
 constexpr int AT_MAXS = 8;    // key splits of one query tile at most
@@ -94,8 +103,8 @@ __device__ __forceinline__ f32x4_t mma16k16(uint2 a, uint2 b, f32x4_t c) {
                                                    __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
 }
 
-template <typename T, int HD>
-__global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
+template <typename T, int HD, int W>
+__global__ void __launch_bounds__(W * WAVE, W == 4 ? 3 : 2) k_attn(RoundArgs a, AttnPlan p) {
   constexpr int KS = El<T>::KSTEP;
   constexpr int PER = El<T>::PER16;
   constexpr int NKS = HD / KS;   // MFMA k-steps over the head dimension
@@ -105,13 +114,16 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   constexpr int OP = HD + 4;     // padded LDS row of a wave's partial output
   typedef AtV<T, HD> VV;
   constexpr int NV = VV::N;
-  __shared__ __attribute__((aligned(16))) float sP[AT_W][AT_Q][AT_C];  // fp32: this chunk's probabilities, per wave
-  __shared__ float sAl[AT_W][AT_Q];            // fp32: this chunk's rescale of the running output
-  __shared__ float sM[AT_W][AT_Q], sL[AT_W][AT_Q];
-  __shared__ __attribute__((aligned(16))) float sO[AT_W][AT_Q][OP];
+  __shared__ __attribute__((aligned(16))) float sP[W][AT_Q][AT_C];  // fp32: this chunk's probabilities, per wave
+  __shared__ float sAl[W][AT_Q];            // fp32: this chunk's rescale of the running output
+  __shared__ float sM[W][AT_Q], sL[W][AT_Q];
+  __shared__ __attribute__((aligned(16))) float sO[W][AT_Q][OP];
   __shared__ int sLim[AT_Q];
   __shared__ int sAnc[AT_Q][EAGLE_MAX_DEPTH];
   __shared__ uint8_t sMb[AT_Q][EAGLE_MAX_TREE];  // tree verify: the queries' mask rows
+  // the query operand (its high and low parts) of every lane, the same for
+  // every wave: read from LDS at each use instead of held in registers
+  __shared__ __attribute__((aligned(16))) uint4 sQ[2][NKS][WAVE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -198,19 +210,18 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     }
   };
 
-  // this wave's chunks: c0+w, c0+w+AT_W, ... below cl (a wave-uniform count);
+  // this wave's chunks: c0+w, c0+w+W, ... below cl (a wave-uniform count);
   // the first is in flight before the query setup.  bf16: cl ends the prefix
   // chunks, and the wave's in-tree chunks (same stride) follow one by one.
   uint4 ka[NKS], kb[NKS];
   vraw va[NV], vb[NV];
-  const int nmine = __builtin_amdgcn_readfirstlane(c0 + w < cl ? (cl - 1 - c0 - w) / AT_W + 1 : 0);
+  const int nmine = __builtin_amdgcn_readfirstlane(c0 + w < cl ? (cl - 1 - c0 - w) / W + 1 : 0);
   if (nmine >= 1) load(ka, va, c0 + w);
 
   // ---- this lane's query operand (query q0+q, dims of k-step s for lane group g),
   // pre-scaled by 1/sqrt(hd); bf16 keeps a high and a low part
   const float scale = rsqrtf((float)HD);
-  uint4 qh[NKS], ql[NKS];
-  {
+  if (w == 0) {
     const int gq = min(q0 + q, p.nq - 1);
     const bool qv = q0 + q < p.nq;
     const int row = b * p.RS + gq / p.g, head = kvh * p.g + gq % p.g;
@@ -240,19 +251,19 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
           hw[e] = h0 | (h1 << 16);
           lw[e] = l0 | (l1 << 16);
         }
-        qh[s] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        ql[s] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        sQ[0][s][lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        sQ[1][s][lane] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       } else {
-        qh[s] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+        sQ[0][s][lane] = make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
                            __float_as_uint(x[3]));
-        ql[s] = make_uint4(0, 0, 0, 0);
+        sQ[1][s][lane] = make_uint4(0, 0, 0, 0);
       }
     }
   }
   // tree verify: the tile's mask rows, one byte per thread (padding queries
   // see no tree row)
   if (verify) {
-    for (int idx = tid; idx < AT_Q * a.m; idx += AT_W * WAVE) {
+    for (int idx = tid; idx < AT_Q * a.m; idx += W * WAVE) {
       const int qq = idx / a.m, j = idx - qq * a.m, gq = q0 + qq;
       const int row = min(gq, p.nq - 1) / p.g;
       sMb[qq][j] = gq < p.nq ? a.vmask[((size_t)b * a.m + row) * a.m + j] : (uint8_t)0;
@@ -328,13 +339,22 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     bl = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   };
 
+  // the query operand in LDS, read through a lane index the compiler must
+  // treat as new at every chunk (so that it reads LDS there rather than keep
+  // the operand in registers across the loop)
+  auto qlane = [&]() __attribute__((always_inline)) {
+    int ql = lane;
+    asm volatile("" : "+v"(ql));
+    return ql;
+  };
   auto chunk = [&](const uint4 (&kr)[NKS], const vraw (&vr)[NV], int c) __attribute__((always_inline)) {
+    const int ql = qlane();
     // scores: lane (g, q) gets S^T[4g + r][q], r = 0..3
     f32x4_t st = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      st = mma16(kr[s], qh[s], st, T());
-      if constexpr (sizeof(T) == 2) st = mma16(kr[s], ql[s], st, T());
+      st = mma16(kr[s], sQ[0][s][ql], st, T());
+      if constexpr (sizeof(T) == 2) st = mma16(kr[s], sQ[1][s][ql], st, T());
     }
     float al, pr4[4];
     smax(st, c, al, pr4);
@@ -389,6 +409,7 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   // high and a low bf16 part, and the products keep the three significant
   // terms (hi.hi, hi.lo, lo.hi) of both the scores and P.V.
   auto tchunk = [&](int c) __attribute__((always_inline)) {
+    const int ql = qlane();
     const float* KtF = (const float*)a.tk;
     const float* VtF = (const float*)a.tv;
     auto trow = [&](const float* tree, int i) __attribute__((always_inline)) -> const float* {
@@ -435,9 +456,10 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
     for (int s = 0; s < NKS; ++s) {
       uint4 kh, kl;
       split8(kx[s][0], kx[s][1], kh, kl);
-      st = mma16(kh, qh[s], st, T());
-      st = mma16(kh, ql[s], st, T());
-      st = mma16(kl, qh[s], st, T());
+      const uint4 qhs = sQ[0][s][ql], qls = sQ[1][s][ql];
+      st = mma16(kh, qhs, st, T());
+      st = mma16(kh, qls, st, T());
+      st = mma16(kl, qhs, st, T());
     }
     float al, pr4[4];
     smax(st, c, al, pr4);
@@ -466,20 +488,20 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   } else if (nmine > 1) {
     // two in flight (ping-pong register sets; a load past the wave's last
     // chunk repeats the split's last chunk and is unused)
-    for (int c = c0 + w;; c += 2 * AT_W) {
-      load(kb, vb, c + AT_W);
+    for (int c = c0 + w;; c += 2 * W) {
+      load(kb, vb, c + W);
       __builtin_amdgcn_sched_barrier(0);
       chunk(ka, va, c);
-      if (c + AT_W >= cl) break;
-      load(ka, va, c + 2 * AT_W);
+      if (c + W >= cl) break;
+      load(ka, va, c + 2 * W);
       __builtin_amdgcn_sched_barrier(0);
-      chunk(kb, vb, c + AT_W);
-      if (c + 2 * AT_W >= cl) break;
+      chunk(kb, vb, c + W);
+      if (c + 2 * W >= cl) break;
     }
   }
-  if constexpr (sizeof(T) == 2) {  // this wave's in-tree chunks, c ≡ c0 + w (mod AT_W)
+  if constexpr (sizeof(T) == 2) {  // this wave's in-tree chunks, c ≡ c0 + w (mod W)
     const int f = max(c0, cp);
-    for (int c = f + ((c0 + w - f) % AT_W + AT_W) % AT_W; c < c1; c += AT_W) tchunk(c);
+    for (int c = f + ((c0 + w - f) % W + W) % W; c < c1; c += W) tchunk(c);
   }
 
   // ---- combine the waves' partial results in wave order
@@ -503,20 +525,20 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
   }
   __syncthreads();
   {
-    // 32 threads per query: each weighs the waves itself (max over waves that
+    // W*WAVE/AT_Q threads per query: each weighs the waves itself (max over waves that
     // saw a key, then exp(m_w - M)) and sums its DPT columns in wave order
-    constexpr int TPQ = AT_W * WAVE / AT_Q;
+    constexpr int TPQ = W * WAVE / AT_Q;
     constexpr int DPT = HD / TPQ;
     const int i = tid / TPQ, d0 = (tid % TPQ) * DPT, gq = q0 + i;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < AT_W; ++ww)
+    for (int ww = 0; ww < W; ++ww)
       if (sL[ww][i] > 0.f) M = fmaxf(M, sM[ww][i]);
     float L = 0.f, O[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e) O[e] = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < AT_W; ++ww) {
+    for (int ww = 0; ww < W; ++ww) {
       const float lw = sL[ww][i];
       const float wt = lw > 0.f ? expf(sM[ww][i] - M) : 0.f;
       L += lw * wt;
@@ -548,8 +570,8 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn(RoundArgs a, AttnPlan p) {
 // order: softmax-weighted sum of the splits' unnormalised outputs.  Every load
 // is issued up front (clamped, masked), so the kernel waits once.
 template <typename T, int HD>
-__global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPlan p) {
-  constexpr int PT = AT_Q * HD / (AT_W * WAVE);  // outputs per thread
+__global__ void __launch_bounds__(AT_MW * WAVE) k_attn_merge(RoundArgs a, AttnPlan p) {
+  constexpr int PT = AT_Q * HD / (AT_MW * WAVE);  // outputs per thread
   __shared__ float sW[AT_MAXS][AT_Q], sInv[AT_Q];
   const int tid = threadIdx.x, wg = blockIdx.x;
   const int qt = wg % p.nqt, bk = wg / p.nqt, kvh = bk % a.Hkv, b = bk / a.Hkv;
@@ -559,7 +581,7 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPla
   float ov[PT][AT_MAXS];
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
-    const int idx = tid + u * AT_W * WAVE, i = idx / HD, dd = idx - i * HD;
+    const int idx = tid + u * AT_MW * WAVE, i = idx / HD, dd = idx - i * HD;
 #pragma unroll
     for (int s = 0; s < AT_MAXS; ++s)
       ov[u][s] = part[((size_t)min(s, ns - 1) * AT_Q + i) * (HD + 4) + dd];
@@ -588,7 +610,7 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPla
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
-    const int idx = tid + u * AT_W * WAVE, i = idx / HD, dd = idx - i * HD, gq = q0 + i;
+    const int idx = tid + u * AT_MW * WAVE, i = idx / HD, dd = idx - i * HD, gq = q0 + i;
     float O = 0.f;
 #pragma unroll
     for (int s = 0; s < AT_MAXS; ++s) O += sW[s][i] * ov[u][s];  // weight 0 past ns
@@ -601,8 +623,14 @@ __global__ void __launch_bounds__(AT_W * WAVE) k_attn_merge(RoundArgs a, AttnPla
 template <typename T, int HD>
 static hipError_t launch_attn_t(const RoundArgs& a, const AttnPlan& p, hipStream_t s) {
   const int tiles = a.B * a.Hkv * p.nqt, groups = a.B * a.Hkv * p.nsplit;
-  hipLaunchKernelGGL((k_attn<T, HD>), dim3((groups + 7) / 8 * 8 * p.nqt), dim3(AT_W * WAVE), 0, s, a, p);
-  if (p.nsplit > 1) hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(tiles), dim3(AT_W * WAVE), 0, s, a, p);
+  const dim3 grid((groups + 7) / 8 * 8 * p.nqt);
+  if (p.waves == 4)
+    hipLaunchKernelGGL((k_attn<T, HD, 4>), grid, dim3(4 * WAVE), 0, s, a, p);
+  else if (p.waves == 8)
+    hipLaunchKernelGGL((k_attn<T, HD, 8>), grid, dim3(8 * WAVE), 0, s, a, p);
+  else
+    return hipErrorInvalidValue;
+  if (p.nsplit > 1) hipLaunchKernelGGL((k_attn_merge<T, HD>), dim3(tiles), dim3(AT_MW * WAVE), 0, s, a, p);
   return hipGetLastError();
 }
 

@@ -225,13 +225,14 @@ LmPlan plan_lm(int M, const eagle_dims& d, int topk) {
     if (p.big) p.zg = cdiv(M, lmgemm_rows());
     // 17..64 rows: the streaming kernel, 128 * nq columns per workgroup with
     // nq the smallest that keeps the workgroups to about one per compute unit
-    // (k-steps a multiple of the loop's unroll, 4).  With one weight tile per
-    // wave (vocabularies up to 32768) k_lmhead stays: there the streaming
-    // kernel's row-gathered X loads are as many as its weight loads and it
-    // measured slower at 40 rows x d 8192 (145 vs 107 us).
+    // (k-steps a multiple of the loop's unroll).  With one weight tile per wave
+    // (vocabularies up to 32768) only above 48 rows: there every one of the
+    // four 16-row MFMA tiles is in use and it beat k_lmhead (13B shape, 64 rows
+    // x d 5120, X packed by the down epilogue: 82 vs 93 us); at 40 rows x d
+    // 8192 it measured slower (146-152 vs 106 us).
     if (d.dtype == EAGLE_BF16 && M <= 64 && d.d % 128 == 0) {
       const int nq = std::min(4, cdiv(cdiv(d.vocab, 16), 8 * 256));
-      if (nq >= 2) p.nq = nq;
+      if ((nq >= 2 || M > 48) && d.d % (32 * (nq == 1 ? 8 : 4)) == 0) p.nq = nq;
     }
   }
   p.rec = 2 + 2 * topk;
@@ -598,8 +599,9 @@ static int draft_level(const eagle_dims* dims, const eagle_weights* w, const eag
   // x0 of this level was formed by the previous level's hand-over, unless the
   // caller asks for it here
   const bool have_x0 = flags == EAGLE_LEVEL_FULL && handover_plan(*dims, *cfg, level - 1, nullptr);
-  if (!tail_only && (r = run_layer(a, *dims, *cfg, s, have_x0))) return r;
   const LmPlan pl = plan_lm(a.rows, *dims, cfg->topk);
+  a.lm_px = !tail_only && pl.nq > 0;  // the layer runs here: its down epilogue packs the LM head's X
+  if (!tail_only && (r = run_layer(a, *dims, *cfg, s, have_x0))) return r;
   if ((r = hip_ok(launch_lmhead(a, pl, level, s, e0, e1), "lm head"))) return r;
   if (lm_only) return EAGLE_OK;
   return hip_ok(launch_lmmerge(a, pl, level, s, handover ? &fp : nullptr), "lm merge");

@@ -173,6 +173,7 @@ __device__ __forceinline__ void gemm_epilogue(const RoundArgs& a, const GemmPlan
       const float h = TILE(0, mr, c) + a.yf[(size_t)row * a.d + nn];
       if (a.mode == MODE_LEVEL) {
         El<T>::st((T*)a.feat, ((size_t)a.depth * a.B * a.k + row) * a.d + nn, h);
+        if (a.lm_px) El<T>::st((T*)a.xpk, xpk_index<T>(row, nn, a.d / El<T>::KSTEP), h);
       } else {
         El<T>::st((T*)a.ext_h, (size_t)row * a.d + nn, h);
         const int b = row / a.RS, i = row % a.RS;

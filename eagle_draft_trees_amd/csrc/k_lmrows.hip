@@ -13,10 +13,12 @@
 //    about one per compute unit: each weight byte is read once, and the
 //    features (read from L2 by every workgroup) are a fraction 4 / (8 NQ) of
 //    the weight bytes;
-//  * the feature rows are read in place (row-major): lane l of an X fragment
-//    reads 16 bytes of row l%16, the rows past M repeat row M-1 (packing them
-//    into fragment order first took a launch of its own and saved less than
-//    that launch costs);
+//  * the feature rows: at levels 2 and up, the level's down epilogue has
+//    also written them in fragment order (one kilobyte per 16 rows x 32 k), so
+//    a fragment is one contiguous load; at level 1 (the caller's root
+//    features) they are read in place, lane l of an X fragment reading 16
+//    bytes of row l%16, rows past M repeating row M-1 (a packing launch of its
+//    own would cost more than it saves there);
 //  * epilogue: the 64 x 128*NQ logits go column-major to LDS (64-column
 //    slabs, row r of column c at c*64 + (r XOR 4*(c%16)): the float4 stores of
 //    16 columns spread over the banks, a column's read by 64 lanes is a
@@ -37,18 +39,28 @@ __global__ void __launch_bounds__(PS_THREADS) k_lmrows(RoundArgs a, LmPlan p, in
   const int K = a.d, nks = K / 32;  // a multiple of ps_unroll<NQ>() (the plan checks)
   const int ntile = (a.V + 15) / 16;
   const int t0 = blockIdx.x * 8 * NQ;  // the block's first 16-column tile
-  const T* xbase = (level == 1) ? (const T*)a.root_feat
-                                : (const T*)a.feat + (size_t)(level - 1) * a.B * a.k * K;
-  // X fragment (wave % 4): row 16*(wave%4) + l%16 (rows past M repeat row
-  // M-1), k 8*(l/16) of the step; the wave's weight tiles NQ*wave + q (a tile
-  // past the last repeats the last)
-  const T* xsrc = xbase + (size_t)min(16 * (wave & 3) + (lane & 15), p.M - 1) * K + 8 * (lane >> 4);
+  // X fragment (wave % 4): row 16*(wave%4) + l%16, k 8*(l/16) of the step.
+  // Packed (levels whose down epilogue wrote xpk in this call): one kilobyte
+  // per fragment, the fragments of 16-row groups past the last repeat it (rows
+  // past M within a group hold other data, and only give rows that are never
+  // recorded).  In place: rows past M repeat row M-1.  The wave's weight tiles
+  // NQ*wave + q (a tile past the last repeats the last).
+  const T* xsrc;
+  size_t xstep = 32;
+  if (level >= 2 && a.lm_px) {
+    xsrc = (const T*)a.xpk + (size_t)min(wave & 3, (p.M - 1) >> 4) * nks * 512 + lane * 8;
+    xstep = 512;
+  } else {
+    const T* xbase = (level == 1) ? (const T*)a.root_feat
+                                  : (const T*)a.feat + (size_t)(level - 1) * a.B * a.k * K;
+    xsrc = xbase + (size_t)min(16 * (wave & 3) + (lane & 15), p.M - 1) * K + 8 * (lane >> 4);
+  }
   const T* wsrc[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) wsrc[q] = wtile_base<T>(a.lm_head, nks, min(t0 + NQ * wave + q, ntile - 1), lane);
   f32x4_t acc[4][NQ];
   ps_main<NQ>(
-      nks, [&](int s) -> const void* { return xsrc + 32 * s; },
+      nks, [&](int s) -> const void* { return xsrc + xstep * s; },
       [&](int q, int s) -> const void* { return wsrc[q] + (size_t)s * wtile_elems<T>(); }, acc);
 
   // logits into the slab tiles

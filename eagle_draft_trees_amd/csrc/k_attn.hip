@@ -482,22 +482,24 @@ __global__ void __launch_bounds__(W * WAVE, W == 4 ? 3 : 2) k_attn(RoundArgs a, 
     }
   };
 
-  if (nmine == 1) {
-    // a single chunk (short prefixes, or many key splits): nothing to prefetch
-    chunk(ka, va, c0 + w);
-  } else if (nmine > 1) {
-    // two in flight (ping-pong register sets; a load past the wave's last
-    // chunk repeats the split's last chunk and is unused)
-    for (int c = c0 + w;; c += 2 * W) {
+  // two chunks in flight (ping-pong register sets).  The loop body is
+  // branch-free with a wave-uniform trip count, so that the wait for a set's
+  // loads sits at its first use (an exit between the halves made the compiler
+  // wait for the other set before issuing the next loads).  A load past the
+  // wave's last chunk repeats the range's last chunk: unused, or taken by the
+  // odd chunk after the loop.
+  {
+    int c = c0 + w;
+    const int npair = nmine >> 1;
+    for (int i = 0; i < npair; ++i, c += 2 * W) {
       load(kb, vb, c + W);
       __builtin_amdgcn_sched_barrier(0);
       chunk(ka, va, c);
-      if (c + W >= cl) break;
       load(ka, va, c + 2 * W);
       __builtin_amdgcn_sched_barrier(0);
       chunk(kb, vb, c + W);
-      if (c + 2 * W >= cl) break;
     }
+    if (nmine & 1) chunk(ka, va, c);
   }
   if constexpr (sizeof(T) == 2) {  // this wave's in-tree chunks, c ≡ c0 + w (mod W)
     const int f = max(c0, cp);

@@ -116,8 +116,10 @@ GemmPlan plan_gemm(int op, int M, const eagle_dims& d) {
     const int U = nq == 1 ? 8 : 4;  // k-steps per loop iteration
     p.rows = 1;
     p.nq = nq;
-    p.tks = cdiv(cdiv(nks, S), U) * U;
-    p.S = cdiv(nks, p.tks);
+    // the kernel deals the K range's nks/U iterations over the S splits as
+    // evenly as whole iterations allow
+    p.S = std::min(S, nks / U);
+    p.tks = cdiv(nks / U, p.S) * U;  // the longest split
     p.Kc = p.tks * 32;
     p.mt = cdiv(M, 16);
     p.zg = 1;

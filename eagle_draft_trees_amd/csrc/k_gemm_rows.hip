@@ -16,8 +16,9 @@
 //    the op's activation rows (the FC's gathered parent / true feature rows,
 //    the attention output for O, the packed SwiGLU activations for down);
 //    rows past M repeat row M-1;
-//  * K is split across workgroups (ranges of whole loop iterations) where
-//    the column blocks alone would leave compute units idle;
+//  * K is split across workgroups (ranges of whole loop iterations, as even
+//    as whole iterations allow) where the column blocks alone would leave
+//    compute units idle;
 //  * the workgroups write fp32 partials in the split layout of the skinny
 //    GEMMs, and k_gemm_fin sums them in split order (deterministic) and runs
 //    the op's fused epilogue, the same code as on the skinny path.
@@ -34,7 +35,11 @@ __global__ void __launch_bounds__(PS_THREADS) k_gemm_rows(RoundArgs a, GemmPlan 
   const int K = p.K, nks = K / 32;
   const int ntile = (p.N + 15) / 16;
   const int split = blockIdx.x % p.S, cb = blockIdx.x / p.S;
-  const int s0 = split * p.tks, ns = min(nks - s0, p.tks);  // a multiple of the loop's unroll
+  // this split's k-steps: the K range in units of the loop's unroll, dealt
+  // as evenly as whole units allow (the first units % S splits one more)
+  constexpr int U = ps_unroll<NQ>();
+  const int units = nks / U, uq = units / p.S, ur = units - uq * p.S;
+  const int s0 = (split * uq + min(split, ur)) * U, ns = (uq + (split < ur ? 1 : 0)) * U;
   // down, extend: the sequence state advances here (the prefix grows by the
   // accepted length, the bonus token becomes the next root); nothing in this
   // launch or its finishing launch reads either field
@@ -105,7 +110,9 @@ static hipError_t launch_rows_op(const RoundArgs& a, const GemmPlan& p, hipStrea
 }
 
 hipError_t launch_gemm_rows(int op, const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
-  if (a.dtype != EAGLE_BF16 || p.M < 1 || p.M > 64 || p.zg != 1 || p.K % 256 || p.tks < 1) return hipErrorInvalidValue;
+  if (a.dtype != EAGLE_BF16 || p.M < 1 || p.M > 64 || p.zg != 1 || p.K % 256 || p.S < 1 ||
+      p.S > p.K / (32 * (p.nq == 1 ? 8 : 4)))
+    return hipErrorInvalidValue;
   switch (op) {
     case OP_FC: return launch_rows_op<OP_FC>(a, p, s);
     case OP_O: return launch_rows_op<OP_O>(a, p, s);

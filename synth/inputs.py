@@ -110,8 +110,9 @@ _add(TreeConfig("batch_bf16", 17, "bf16", 80, 256, 4, 2, 64, 512, 3000, 8, 40, 3
 _add(TreeConfig("short_f32", 18, "f32", 3, 256, 4, 4, 64, 688, 4096, 64, 64, 4, 1, 3))
 # 64 level rows (16 sequences x top-4) over a small vocabulary: the streaming
 # LM head with one weight tile per wave, its features packed by the down
-# epilogue; a vocabulary that ends inside a 16-column tile
-_add(TreeConfig("rows64_bf16", 21, "bf16", 16, 256, 4, 2, 64, 512, 3001, 8, 60, 4, 4, 12))
+# epilogue; a vocabulary that ends inside a 16-column tile; at d 1280 the FC
+# and O split K into uneven ranges (5 loop iterations over 2 workgroups)
+_add(TreeConfig("rows64_bf16", 21, "bf16", 16, 1280, 10, 5, 128, 512, 3001, 8, 60, 4, 4, 12))
 # 320 (sequence, KV head) query tiles: the attention's four-wave workgroups
 # (three per compute unit), bf16 at hd 128 and fp32 at hd 64
 _add(TreeConfig("heads_bf16", 19, "bf16", 40, 1024, 8, 8, 128, 512, 2000, 8, 70, 4, 3, 9))

@@ -462,13 +462,16 @@ def lm_kernel_name(cfg, rows) -> str:
     the skinny streaming kernel; bf16 with d a multiple of 128, the batched
     MFMA GEMM above 64 rows and, from 17 to 64 rows, the streaming MFMA
     kernel when the vocabulary gives each wave at least two 16-column weight
-    tiles (more than 32768 columns); else k_lmhead."""
+    tiles (more than 32768 columns), or at 49 to 64 rows with d a multiple of
+    256; else k_lmhead."""
     if rows <= 16:
         return "k_lmskinny"
     tiled = cfg.dtype == "bf16" and cfg.d % 128 == 0
     if tiled and rows > 64:
         return "k_lg_xpack + k_lmgemm"
     if tiled and -(-cfg.V // 16) > 8 * 256:
+        return "k_lmrows"
+    if tiled and rows > 48 and cfg.d % 256 == 0:
         return "k_lmrows"
     return "k_lmhead"
 
@@ -507,8 +510,14 @@ def lmhead_roofline(torch, L, r, cfg, stream, steps, scrub) -> dict:
     nbytes = es * cfg.V * cfg.d
     rows = cfg.B * cfg.k
     gbps = nbytes / (lm_ms * 1e-3) / 1e9
-    return {"kernel": f"{lm_kernel_name(cfg, rows)} (LM-head GEMM + per-slab softmax/top-k, {rows} rows)",
-            "scope": "the LM-head GEMM (the largest share of the 7B-shaped round's time)",
+    kname = lm_kernel_name(cfg, rows)
+    scope = "the LM-head GEMM (the largest share of the 7B-shaped round's time)"
+    if kname == "k_lmrows":
+        scope += ("; an LM-head-only call has no down projection to pack its X, so these launches "
+                  "read the features in place, where the round's levels read the copy the down "
+                  "epilogue writes in MFMA fragment order")
+    return {"kernel": f"{kname} (LM-head GEMM + per-slab softmax/top-k, {rows} rows)",
+            "scope": scope,
             "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(lm_ms * 1e3, 2),
             "timing": f"{n_lm} launches, HIP events stamped by the kernel's dispatch "

@@ -113,6 +113,10 @@ _add(TreeConfig("short_f32", 18, "f32", 3, 256, 4, 4, 64, 688, 4096, 64, 64, 4, 
 # epilogue; a vocabulary that ends inside a 16-column tile; at d 1280 the FC
 # and O split K into uneven ranges (5 loop iterations over 2 workgroups)
 _add(TreeConfig("rows64_bf16", 21, "bf16", 16, 1280, 10, 5, 128, 512, 3001, 8, 60, 4, 4, 12))
+# the deepest tree the library takes (depth 16: every ancestor slot of a
+# frontier record in use, 17 verify and extend rows per sequence)
+_add(TreeConfig("deep16_f32", 22, "f32", 2, 256, 4, 2, 64, 512, 1000, 5, 60, 16, 2, 32))
+_add(TreeConfig("deep16_bf16", 23, "bf16", 2, 256, 4, 2, 64, 512, 1000, 5, 60, 16, 2, 32))
 # 320 (sequence, KV head) query tiles: the attention's four-wave workgroups
 # (three per compute unit), bf16 at hd 128 and fp32 at hd 64
 _add(TreeConfig("heads_bf16", 19, "bf16", 40, 1024, 8, 8, 128, 512, 2000, 8, 70, 4, 3, 9))

@@ -30,7 +30,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not HAVE_GPU, reason="needs a GPU")]
 
 FAST = ["tiny", "tiny_bf16", "ragged_f32", "ragged_bf16", "hd128_bf16", "chain_small", "wide_bf16",
-        "deep_bf16", "batch_bf16", "short_f32", "heads_bf16", "heads_f32", "rows64_bf16"]
+        "deep_bf16", "batch_bf16", "short_f32", "heads_bf16", "heads_f32", "rows64_bf16", "deep16_f32", "deep16_bf16"]
 FULL = ["7b", "13b", "70b", "chain"]
 # sequences the oracle checks at full size (the GPU runs the whole batch)
 SAMPLE = {"13b": [0, 7, 15], "70b": [0, 3], "chain": [0, 31, 63]}

@@ -777,3 +777,31 @@ def test_out_of_range_token_is_clamped_and_flagged():
     err = r.ws_region(0).view(torch.int32)[0].item()
     assert err & 1, err
     assert int(r.tokens[1, 0]) == cfg.V - 1
+
+
+def test_out_of_range_prefix_is_clamped_and_flagged():
+    """A prefix length that leaves no room for the round's rows (above
+    max_prefix - m) or that is not positive is clamped to the nearest valid
+    one and flagged (error word bit 1); the round still completes, every
+    drafted token is a vocabulary id, and the extend advances from the clamped
+    length."""
+    import torch
+    cfg, inp, r, model, seqs = get("ragged_f32")
+    say("[data errors] prefix lengths out of range, ragged_f32")
+    hi = cfg.max_prefix - cfg.m
+    r.ws_region(0).zero_()
+    r.prefix_len[0] = 0
+    r.prefix_len[2] = cfg.max_prefix
+    p1 = int(r.prefix_len[1])
+    sync()
+    r.run_round()
+    sync()
+    err = r.ws_region(0).view(torch.int32)[0].item()
+    assert err & 2, err
+    toks = r.tokens.cpu().numpy()
+    assert ((toks >= 0) & (toks < cfg.V)).all()
+    alen = [int(x) for x in r.accept_len.cpu()]
+    rows = min(cfg.m, cfg.D + 1)
+    assert all(1 <= x <= rows for x in alen), alen
+    plen = [int(x) for x in r.prefix_len.cpu()]
+    assert plen == [1 + alen[0], p1 + alen[1], hi + alen[2]], (plen, alen, hi)

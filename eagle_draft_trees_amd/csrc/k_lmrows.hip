@@ -19,6 +19,7 @@
 //    features) they are read in place, lane l of an X fragment reading 16
 //    bytes of row l%16, rows past M repeating row M-1 (a packing launch of its
 //    own would cost more than it saves there);
+//  * XCD x (blocks x, x+8, ...) takes a contiguous run of column blocks;
 //  * epilogue: the 64 x 128*NQ logits go column-major to LDS (64-column
 //    slabs, row r of column c at c*64 + (r XOR 4*(c%16)): the float4 stores of
 //    16 columns spread over the banks, a column's read by 64 lanes is a
@@ -38,7 +39,12 @@ __global__ void __launch_bounds__(PS_THREADS) k_lmrows(RoundArgs a, LmPlan p, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.d, nks = K / 32;  // a multiple of ps_unroll<NQ>() (the plan checks)
   const int ntile = (a.V + 15) / 16;
-  const int t0 = blockIdx.x * 8 * NQ;  // the block's first 16-column tile
+  // column block of this workgroup: XCD x (blocks x, x+8, ...) takes a
+  // contiguous run of column blocks
+  const int nblk = (ntile + 8 * NQ - 1) / (8 * NQ), per = (nblk + 7) / 8;
+  const int cbk = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (cbk >= nblk) return;
+  const int t0 = cbk * 8 * NQ;  // the block's first 16-column tile
   // X fragment (wave % 4): row 16*(wave%4) + l%16, k 8*(l/16) of the step.
   // Packed (levels whose down epilogue wrote xpk in this call): one kilobyte
   // per fragment, the fragments of 16-row groups past the last repeat it (rows
@@ -78,7 +84,7 @@ __global__ void __launch_bounds__(PS_THREADS) k_lmrows(RoundArgs a, LmPlan p, in
   __syncthreads();
   // slab j of the block: wave j, lane = row
   if (wave < 2 * NQ) {
-    const int slab = blockIdx.x * 2 * NQ + wave, cbase = slab * 64;
+    const int slab = cbk * 2 * NQ + wave, cbase = slab * 64;
     const float* tile = ps_slab<NQ>(wave);
     float v[64];
 #pragma unroll
@@ -92,7 +98,8 @@ hipError_t launch_lmrows(const RoundArgs& a, const LmPlan& p, int level, hipStre
                          hipEvent_t e1) {
   if (a.dtype != EAGLE_BF16 || a.d % (32 * (p.nq == 1 ? 8 : 4)) || p.M > 64 || p.M < 1) return hipErrorInvalidValue;
   const int ntile = (a.V + 15) / 16;
-  const dim3 grid((ntile + 8 * p.nq - 1) / (8 * p.nq)), block(PS_THREADS);
+  const int nblk = (ntile + 8 * p.nq - 1) / (8 * p.nq);
+  const dim3 grid((nblk + 7) / 8 * 8), block(PS_THREADS);
   auto go = [&](auto kern) {
     if (e0 || e1)
       hipExtLaunchKernelGGL(kern, grid, block, 0u, s, e0, e1, 0u, a, p, level);

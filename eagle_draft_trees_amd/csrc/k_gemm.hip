@@ -210,7 +210,13 @@ __global__ void __launch_bounds__(CTW * GW_KSW * 64) k_gemm(RoundArgs a, GemmPla
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ct = wave % CTW, ks = wave / CTW;  // column tile, K slice (of GW_KSW)
   const int c = lane & 15, g = lane >> 4;
-  const int blk = blockIdx.x, split = blockIdx.y, zg = blockIdx.z;
+  // workgroup -> (column block, split, row group): XCD x (blocks x, x+8,
+  // ...) takes a contiguous run, the row groups (which read the same
+  // weights) and the splits of one column block adjacent
+  const int nbz = p.nblk * p.S * p.zg, bpx = (nbz + 7) / 8;
+  const int lb = (int)(blockIdx.x & 7) * bpx + (int)(blockIdx.x >> 3);
+  if (lb >= nbz) return;
+  const int zg = lb % p.zg, split = (lb / p.zg) % p.S, blk = lb / (p.zg * p.S);
   const int cl = ct * 16 + c;
   const int K = p.K;
 
@@ -488,7 +494,8 @@ __global__ void __launch_bounds__(GW_FIN_THREADS) k_gemm_fin(RoundArgs a, GemmPl
 
 template <typename T, int OP, int CTW>
 static void launch_main(const RoundArgs& a, const GemmPlan& p, hipStream_t s) {
-  const dim3 grid(p.nblk, p.S, p.zg), block(CTW * GW_KSW * 64);
+  const int nbz = p.nblk * p.S * p.zg;
+  const dim3 grid((nbz + 7) / 8 * 8), block(CTW * GW_KSW * 64);
   const size_t lds = gemm_lds_bytes(p, (int)sizeof(T));
   switch (p.mt) {
     case 1: hipLaunchKernelGGL((k_gemm<T, OP, 1, CTW>), grid, block, lds, s, a, p); break;

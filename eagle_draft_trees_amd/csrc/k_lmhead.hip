@@ -35,7 +35,12 @@ __global__ void __launch_bounds__(BLOCK) k_lmhead(RoundArgs a, LmPlan p, int lev
   __shared__ __attribute__((aligned(16))) unsigned char xs[ROWS * XST];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int blk = blockIdx.x, zg = blockIdx.z;
+  // workgroup -> (slab, row group): XCD x (blocks x, x+8, ...) takes a
+  // contiguous run, the row groups of one slab adjacent
+  const int nbz = p.nblk * p.zg, bpx = (nbz + 7) / 8;
+  const int lb = (int)(blockIdx.x & 7) * bpx + (int)(blockIdx.x >> 3);
+  if (lb >= nbz) return;
+  const int zg = lb % p.zg, blk = lb / p.zg;
   const int K = a.d, kk_ = a.k;
   const int cl = wave * 16 + (lane & 15);
   const int n = blk * 64 + cl;
@@ -177,8 +182,12 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwv = (int)(blockDim.x >> 6);
+  // slab: XCD x (blocks x, x+8, ...) takes a contiguous run
+  const int bpx = (p.nblk + 7) / 8;  // blocks per XCD
+  const int bk = (int)(blockIdx.x & 7) * bpx + (int)(blockIdx.x >> 3);
+  if (bk >= p.nblk) return;
   const int ct = wave % p.CT, ks = wave / p.CT;
-  const int t = blockIdx.x * p.CT + ct;
+  const int t = bk * p.CT + ct;
   const int c = lane & 15, g = lane >> 4;
   const int K = a.d, kk_ = a.k;
   const int n = t * 16 + c;
@@ -212,7 +221,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
 
   // one wave per row: up to four columns per lane
   __shared__ __attribute__((aligned(16))) unsigned long long s_tk[SK_MAXW][2 * WAVE];  // wave_topk scratch
-  const int col0 = blockIdx.x * ncol;
+  const int col0 = bk * ncol;
   // (NC = columns per lane: two for slabs of up to 128 columns, else four)
   auto epi = [&](auto ncl) __attribute__((always_inline)) {
     constexpr int NC = decltype(ncl)::value;
@@ -232,7 +241,7 @@ __global__ void __launch_bounds__(SK_MAXW * WAVE) k_lmskinny(RoundArgs a, LmPlan
 #pragma unroll
       for (int u = 0; u < NC; ++u) se += x[u] == -INFINITY ? 0.f : expf(x[u] - mx);
       se = wave_sum_dpp(se);
-      float* rec = slab_field(a.lmpart, row, blockIdx.x, p);  // field f at rec[f * nblk]
+      float* rec = slab_field(a.lmpart, row, bk, p);  // field f at rec[f * nblk]
       if (lane == 0) {
         rec[0] = mx;
         rec[p.nblk] = se;
@@ -264,7 +273,8 @@ static void lm_launch(void (*k)(A...), dim3 g, dim3 b, size_t sh, hipStream_t s,
 template <typename T>
 static hipError_t launch_lm_t(const RoundArgs& a, const LmPlan& p, int level, hipStream_t s,
                               hipEvent_t e0, hipEvent_t e1) {
-  const dim3 grid(p.nblk, 1, p.zg), block(BLOCK);
+  const int nbz = p.nblk * p.zg;
+  const dim3 grid((nbz + 7) / 8 * 8), block(BLOCK);
   switch (p.mt) {
     case 1: lm_launch(k_lmhead<T, 1>, grid, block, 0, s, e0, e1, a, p, level); break;
     case 2: lm_launch(k_lmhead<T, 2>, grid, block, 0, s, e0, e1, a, p, level); break;
@@ -279,7 +289,7 @@ static hipError_t launch_lmsk_t(const RoundArgs& a, const LmPlan& p, int level, 
                                 hipEvent_t e0, hipEvent_t e1) {
   const int nwv = p.CT * p.KSW;
   const size_t epi = (size_t)nwv * WAVE * sizeof(f32x4_t) + (size_t)16 * (p.CT * 16 + 1) * sizeof(float);
-  const dim3 grid(p.nblk), block(nwv * WAVE);
+  const dim3 grid((p.nblk + 7) / 8 * 8), block(nwv * WAVE);
   if (p.xlds) {
     const size_t xb = sk_xtile_bytes(a.d, (int)sizeof(T));
     lm_launch(k_lmskinny<T, true>, grid, block, xb > epi ? xb : epi, s, e0, e1, a, p, level);

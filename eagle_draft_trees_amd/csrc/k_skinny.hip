@@ -60,8 +60,12 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
   __shared__ __attribute__((aligned(16))) float s_ssq[SK_MAXW][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // column block: XCD x (blocks x, x+8, ...) takes a contiguous run
+  const int bpx = (p.nwg + 7) / 8;  // blocks per XCD
+  const int bk = (int)(blockIdx.x & 7) * bpx + (int)(blockIdx.x >> 3);
+  if (bk >= p.nwg) return;
   const int ct = wave % p.CT, ks = wave / p.CT;
-  const int t = blockIdx.x * p.CT + ct;
+  const int t = bk * p.CT + ct;
   const int c = lane & 15, g = lane >> 4;
   const bool tv = t < p.ntile;
   const int n = sk_col(OP, tv ? t : 0, c, a.hd);
@@ -281,7 +285,7 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
     if (tid < p.M) {
       float s = 0.f;
       for (int q = 0; q < p.CT; ++q) s += s_ssq[q][tid];
-      a.ssq[(size_t)blockIdx.x * a.rows + tid] = s;
+      a.ssq[(size_t)bk * a.rows + tid] = s;
     }
   } else if (OP == OP_GATEUP) {
     if (fin && nv) {
@@ -328,14 +332,14 @@ __global__ void __launch_bounds__((OP == OP_QKV ? SK_QKVW : SK_MAXW) * WAVE) k_s
       }
     }
     // nothing in this launch reads prefix_len or root_token
-    if (a.mode == MODE_EXTEND && blockIdx.x == 0) ext_advance_state(a, tid, (int)blockDim.x);
+    if (a.mode == MODE_EXTEND && bk == 0) ext_advance_state(a, tid, (int)blockDim.x);
   }
 }
 
 template <typename T, int OP>
 static void launch_sk_op(const RoundArgs& a, const SkPlan& p, hipStream_t s) {
   constexpr int NW = (OP == OP_GATEUP) ? 2 : 1;
-  const dim3 grid(p.nwg), block(WAVE * p.CT * p.KSW);
+  const dim3 grid((p.nwg + 7) / 8 * 8), block(WAVE * p.CT * p.KSW);
   const size_t red = (size_t)WAVE * p.CT * p.KSW * NW * sizeof(f32x4_t);
   if (p.xlds && OP != OP_DOWN) {  // the down projection's X is packed, never staged
     const size_t xb = OP == OP_QKV && sizeof(T) == 2 ? sk_hl_tile_bytes(p.K, 2) : sk_xtile_bytes(p.K, (int)sizeof(T));

@@ -7,7 +7,7 @@
 // keeps that stream going and the features off the critical path:
 //  * operands move from memory straight into LDS (global_load_lds_dwordx4:
 //    lane l's 16 bytes land at l*16, one kilobyte MFMA fragment per wave
-//    instruction).  A k-step of 32 is 4 + 8*NQ fragments: the rows' four X
+//    instruction), the weights non-temporal.  A k-step of 32 is 4 + 8*NQ fragments: the rows' four X
 //    fragments and the workgroup's 8*NQ weight tiles;
 //  * four stage buffers of 36 KB, a step's loads issued three steps ahead.
 //    Each wave loads its own NQ weight fragments, and waves 0..3 the four X
@@ -32,6 +32,10 @@
 namespace eg {
 
 constexpr int PS_W = 8;                  // waves per workgroup
+// cache policy of the weight loads: non-temporal (each weight byte is read
+// once per pass; without the hint the stream evicts the prefix K/V and the
+// activations that the next launches re-read)
+constexpr int PS_WNT = 2;
 constexpr int PS_THREADS = PS_W * WAVE;
 constexpr int PS_MAXQ = 4;               // weight tiles per wave at most
 constexpr int PS_STAGE = (4 + 8 * PS_MAXQ) * 64;  // uint4 per stage buffer (36 KB)
@@ -90,8 +94,8 @@ __device__ __forceinline__ void ps_main(int nsteps, const SrcX& srcx, const SrcW
     auto dma = [&](uint4* buf, int t) __attribute__((always_inline)) {
       t = min(t, nst - 1);  // past the last stage: repeats it into a buffer not read again
       __builtin_amdgcn_global_load_lds(srcx(2 * t + (wave >> 2)), lds(buf + wave * WAVE), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(srcw(0, 2 * t), lds(buf + (8 + wave) * WAVE), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(srcw(0, 2 * t + 1), lds(buf + (16 + wave) * WAVE), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(srcw(0, 2 * t), lds(buf + (8 + wave) * WAVE), 16, 0, PS_WNT);
+      __builtin_amdgcn_global_load_lds(srcw(0, 2 * t + 1), lds(buf + (16 + wave) * WAVE), 16, 0, PS_WNT);
     };
     auto step = [&](const uint4* buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -119,7 +123,7 @@ __device__ __forceinline__ void ps_main(int nsteps, const SrcX& srcx, const SrcW
       s = min(s, nsteps - 1);  // past the last step: repeats it into a buffer not read again
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
-        __builtin_amdgcn_global_load_lds(srcw(q, s), lds(buf + (4 + NQ * wave + q) * WAVE), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(srcw(q, s), lds(buf + (4 + NQ * wave + q) * WAVE), 16, 0, PS_WNT);
       // waves 0..3: X fragment `wave`; waves 4..7 repeat their last weight
       // fragment (a wave-uniform select, no branch)
       const bool xw = wave < 4;

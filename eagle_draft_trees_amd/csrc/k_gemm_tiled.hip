@@ -146,16 +146,15 @@ __global__ void __launch_bounds__(PP_THREADS) k_gemm_tiled(RoundArgs a, GemmPlan
   if (OP == OP_DOWN && a.mode == MODE_EXTEND && lin == 0) ext_advance_state(a, tid, PP_THREADS);
   const int s0 = split * p.tks, ns = min(nsx - s0, p.tks);  // this split's X steps (a multiple of 4)
 
-  // this wave's four fragments of a step: waves 0..3 the X groups 4*wave..
-  // of the row tile, waves 4..7 the weight tiles 4*(wave-4).. of the column
-  // block (gate/up: gate tiles, then the same columns' up tiles); a group or
+  // this wave's four fragments of a step: u = 0, 1 the row tile's X group
+  // 2*wave + u, u = 2, 3 the column block's weight tile 2*wave + u - 2
+  // (gate/up: tiles 0..7 gate, 8..15 the same columns' up tiles); a group or
   // tile past the last repeats the last
-  const bool isw = wave >= 4;
   const T* base[PP_DMA];
 #pragma unroll
   for (int u = 0; u < PP_DMA; ++u) {
-    const int f = PP_DMA * (wave & 3) + u;
-    if (!isw) {
+    const int f = 2 * wave + (u & 1);
+    if (u < 2) {
       const int grp = min(rb * 16 + f, ngrp - 1);
       base[u] = OP == OP_DOWN ? (const T*)a.act + (size_t)grp * nks * 512 + (lane & 15) * 32 + (lane >> 4) * 8
                               : (const T*)a.xpk + (size_t)grp * nsx * 512 + lane * 8;
@@ -171,11 +170,11 @@ __global__ void __launch_bounds__(PP_THREADS) k_gemm_tiled(RoundArgs a, GemmPlan
   }
   auto src = [&](int u, int s) __attribute__((always_inline)) -> const void* {
     int st = s0 + s;
-    if (isw && st >= nks) st -= nks;  // q/k/v: the low part's steps reuse the weights
+    if (u >= 2 && st >= nks) st -= nks;  // q/k/v: the low part's steps reuse the weights
     return base[u] + (size_t)st * 512;
   };
   f32x4_t acc[8][4];
-  pp_main(ns, src, acc);
+  pp_main<true>(ns, src, acc);
 
   if constexpr (OP == OP_GATEUP) {
     if (p.S == 1) {  // unsplit: the SwiGLU epilogue here, no partials

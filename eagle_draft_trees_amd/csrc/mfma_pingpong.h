@@ -9,7 +9,8 @@
 //    address of each lane's 16 bytes of its four fragments of a step, so any
 //    source layout whose fragments are gatherable by lane works.
 //  * Four stage buffers of one k-step (32 KB each); a step's loads are issued
-//    three steps ahead, four fragments by each wave.  Loads past the last step
+//    three steps ahead, four fragments by each wave (with MIX two of X and two
+//    of W, the weight loads non-temporal).  Loads past the last step
 //    repeat it into buffers that are not read again, so every wave waits for a
 //    fixed count (vmcnt(8): the two later steps stay in flight).
 //  * The waves run as two groups of four (one wave of each group per SIMD),
@@ -46,22 +47,35 @@ constexpr int PP_WAIT_VM8_LGKM0 = 8 | (7 << 4);
 // (wave & 1, wave >> 1): rows 128*wm + 16*i, columns 64*wn + 16*q of the
 // tile; lane (g, c) of acc[i][q] holds rows 4g..4g+3 and column c).
 // src(u, s) is the address of this lane's 16 bytes of this wave's fragment u
-// (fragment 4*wave + u of the step: 0..15 X, 16..31 W) at step s < nsteps.
+// at step s < nsteps.  MIX: u = 0, 1 the step's X fragment 2*wave + u (of
+// 0..15), u = 2, 3 its W fragment 2*wave + u - 2 (of 0..15; slot 16 + that in
+// the stage buffer); otherwise fragment 4*wave + u of the step (0..15 X,
+// 16..31 W).
 // Every wave of the workgroup must call it; it ends with the loads drained
 // and a workgroup barrier, the stage buffers free for the caller.
-template <typename Src>
+template <bool MIX = false, typename Src>
 __device__ __forceinline__ void pp_main(int nsteps, const Src& src, f32x4_t (&acc)[8][4]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool first = wave < 4;              // group that runs half a step ahead
   const int wm = wave & 1, wn = wave >> 1;
+  // MIX: this wave's fragments u = 0, 1 are X fragments 2*wave + u and
+  // u = 2, 3 W fragments 16 + 2*wave + u - 2, the weight loads non-temporal
+  // (read once per pass); else fragments 4*wave + u (waves 0..3 X, 4..7 W)
   auto dma = [&](uint4* buf, int s) __attribute__((always_inline)) {
     s = min(s, nsteps - 1);
+    auto at = [&](int f) __attribute__((always_inline)) {
+      return (__attribute__((address_space(3))) void*)(buf + f * WAVE);
+    };
+    if constexpr (MIX) {
+      __builtin_amdgcn_global_load_lds(src(0, s), at(2 * wave), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src(1, s), at(2 * wave + 1), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src(2, s), at(16 + 2 * wave), 16, 0, 2);
+      __builtin_amdgcn_global_load_lds(src(3, s), at(17 + 2 * wave), 16, 0, 2);
+    } else {
 #pragma unroll
-    for (int u = 0; u < PP_DMA; ++u)
-      __builtin_amdgcn_global_load_lds(src(u, s),
-                                       (__attribute__((address_space(3))) void*)(buf + (PP_DMA * wave + u) * WAVE),
-                                       16, 0, 0);
+      for (int u = 0; u < PP_DMA; ++u) __builtin_amdgcn_global_load_lds(src(u, s), at(PP_DMA * wave + u), 16, 0, 0);
+    }
   };
 #pragma unroll
   for (int i = 0; i < 8; ++i)

@@ -50,10 +50,14 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
   for (int w = 0; w < NW; ++w) acc[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nkt = (K + KS - 1) / KS;  // k-step tiles of a packed row block
+  // loads past the slice repeat its last k-step (the bytes this lane has just
+  // loaded) rather than read the next slice's, which another wave streams:
+  // with the non-temporal policy those would be fetched from HBM twice
+  const int stmax = min(max(s1k - 1, 0), nkt - 1);
   auto load = [&](uint4 (&wb)[BU][NW], uint4 (&xb)[BU], int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
-      const int st = min(s0k + b * BU + u, nkt - 1);
+      const int st = min(s0k + b * BU + u, stmax);
       const int kc = min(st * KS + g * PER, klast);
 #pragma unroll
       for (int w = 0; w < NW; ++w) wb[u][w] = ld16w(wr[w] + (size_t)st * wtile_elems<T>());
@@ -115,8 +119,8 @@ __device__ __forceinline__ void sk_stream(const T* const (&wr)[NW], const T* x0,
     __builtin_amdgcn_sched_barrier(0);
   }
   // Both buffers stay in flight: each batch's MFMAs are followed by the load
-  // two batches ahead into the same buffer (loads past the slice read clamped
-  // in-row addresses and are unused); the last one or two batches are peeled.
+  // two batches ahead into the same buffer (loads past the slice repeat its
+  // last k-step and are unused); the last one or two batches are peeled.
   int b = 0;
   for (; b + 2 < nb; b += 2) {
     comp(wa, xa, b);

@@ -488,7 +488,7 @@ __global__ void __launch_bounds__(W * WAVE, W == 4 ? 3 : 2) k_attn(RoundArgs a, 
   // wait for the other set before issuing the next loads).  A load past the
   // wave's last chunk repeats the range's last chunk: unused, or taken by the
   // odd chunk after the loop.
-  {
+  if constexpr (sizeof(T) == 2) {
     int c = c0 + w;
     const int npair = nmine >> 1;
     for (int i = 0; i < npair; ++i, c += 2 * W) {
@@ -500,6 +500,21 @@ __global__ void __launch_bounds__(W * WAVE, W == 4 ? 3 : 2) k_attn(RoundArgs a, 
       chunk(kb, vb, c + W);
     }
     if (nmine & 1) chunk(ka, va, c);
+  } else if (nmine == 1) {
+    // fp32 (sixteen V rows per chunk in registers): with the loop above the
+    // compiler spills, so the halves keep their own exits here
+    chunk(ka, va, c0 + w);
+  } else if (nmine > 1) {
+    for (int c = c0 + w;; c += 2 * W) {
+      load(kb, vb, c + W);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(ka, va, c);
+      if (c + W >= cl) break;
+      load(ka, va, c + 2 * W);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(kb, vb, c + W);
+      if (c + 2 * W >= cl) break;
+    }
   }
   if constexpr (sizeof(T) == 2) {  // this wave's in-tree chunks, c ≡ c0 + w (mod W)
     const int f = max(c0, cp);

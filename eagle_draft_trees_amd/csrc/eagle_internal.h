@@ -363,7 +363,7 @@ struct RoundArgs {
   void* xpk;  // batched LM head: its input rows in MFMA fragment order
   int pool_n;
   // levels (bf16, 17..64 rows): the down epilogue also writes the level's
-  // features into xpk in MFMA fragment order (xpk_index, d/32 k-steps) for the
+  // features into xpk in 16-row blocks (xpk_index, d/32 k-steps) for the
   // streaming LM head that follows in the same call
   int lm_px;
 };

@@ -14,8 +14,8 @@
 //    features (read from L2 by every workgroup) are a fraction 4 / (8 NQ) of
 //    the weight bytes;
 //  * the feature rows: at levels 2 and up, the level's down epilogue has
-//    also written them in fragment order (one kilobyte per 16 rows x 32 k), so
-//    a fragment is one contiguous load; at level 1 (the caller's root
+//    also written them in 16-row blocks (one kilobyte per 16 rows x 32 k,
+//    row-major inside a block), so a fragment is one contiguous kilobyte; at level 1 (the caller's root
 //    features) they are read in place, lane l of an X fragment reading 16
 //    bytes of row l%16, rows past M repeating row M-1 (a packing launch of its
 //    own would cost more than it saves there);
@@ -47,14 +47,14 @@ __global__ void __launch_bounds__(PS_THREADS) k_lmrows(RoundArgs a, LmPlan p, in
   const int t0 = cbk * 8 * NQ;  // the block's first 16-column tile
   // X fragment (wave % 4): row 16*(wave%4) + l%16, k 8*(l/16) of the step.
   // Packed (levels whose down epilogue wrote xpk in this call): one kilobyte
-  // per fragment, the fragments of 16-row groups past the last repeat it (rows
-  // past M within a group hold other data, and only give rows that are never
-  // recorded).  In place: rows past M repeat row M-1.  The wave's weight tiles
+  // per 16 rows x 32 k, row-major inside it (xpk_index), the groups past the
+  // last repeat it (rows past M within a group hold other data, and only give
+  // rows that are never recorded).  In place: rows past M repeat row M-1.  The wave's weight tiles
   // NQ*wave + q (a tile past the last repeats the last).
   const T* xsrc;
   size_t xstep = 32;
   if (level >= 2 && a.lm_px) {
-    xsrc = (const T*)a.xpk + (size_t)min(wave & 3, (p.M - 1) >> 4) * nks * 512 + lane * 8;
+    xsrc = (const T*)a.xpk + (size_t)min(wave & 3, (p.M - 1) >> 4) * nks * 512 + (lane & 15) * 32 + 8 * (lane >> 4);
     xstep = 512;
   } else {
     const T* xbase = (level == 1) ? (const T*)a.root_feat

@@ -766,6 +766,32 @@ def test_timed_level_matches_plain(name):
         assert m0.elapsed_time(k0) >= -1e-3 and k1.elapsed_time(m1) >= -1e-3
 
 
+@pytest.mark.parametrize("name", ["rows64_bf16", "13b", "chain"])
+def test_packed_lm_input_matches_in_place(name):
+    """At 17..64 bf16 level rows the streaming LM head reads the level's
+    features from the copy the down projection's epilogue writes in MFMA
+    fragment order; an LM-head-only call (TAIL_ONLY) reads the same features in
+    place.  The two must give bit-identical records: drafting every level in
+    full, then re-running each level's tail on the features it wrote, builds
+    the same tree."""
+    from eagle_draft_trees_amd import _lib as L
+    cfg, inp, r, model, seqs = get(name)
+    say(f"[packed LM input] {name}")
+    outs = lambda: [t.cpu().numpy().copy() for t in (r.tokens, r.parents, r.mask, r.logscore)]
+    r.draft()
+    sync()
+    ref = outs()
+    r.reset_state(inp)
+    r.level(1)
+    for level in range(2, cfg.D + 1):
+        r.level(level)
+        r.level(level, L.EAGLE_LEVEL_TAIL_ONLY)
+    r.rerank()
+    sync()
+    for a, b in zip(ref, outs()):
+        assert np.array_equal(a, b)
+
+
 def test_out_of_range_token_is_clamped_and_flagged():
     import torch
     cfg, inp, r, model, seqs = get("ragged_f32")

@@ -143,11 +143,14 @@ SkPlan plan_skinny(int op, int M, const eagle_dims& d) {
   const int nks = cdiv(p.K, d.dtype == EAGLE_BF16 ? 32 : 16);
   const int nw = op == OP_GATEUP ? 2 : 1;
   // one column tile per workgroup: all 16 waves split K (every CU busy);
-  // several tiles: fewer, longer K slices (at least 32 k-steps) stream better
+  // several tiles: fewer, longer K slices (at least 32 k-steps; gate/up, two
+  // weight streams per wave, at least 25) stream better.  Measured at the
+  // 7B shape's gate/up (3 tiles, 128 k-steps): 5 slices 33.4 us, 4 slices
+  // 34.3; its q/k/v with 5 slices (15 waves) took 25.6 us against 22.0.
   const int maxw = op == OP_QKV ? SK_QKVW : SK_MAXW;
   p.CT = std::min(p.CT, maxw);
   p.KSW = p.CT == 1 ? std::max(1, std::min(maxw, nks / 8))
-                    : std::max(1, std::min(maxw / p.CT, nks / 32));
+                    : std::max(1, std::min(maxw / p.CT, nks / (op == OP_GATEUP ? 25 : 32)));
   p.nwg = cdiv(p.ntile, p.CT);
   p.nps = 0;
   // the X tile is staged in LDS when it fits and is shared by at least two

@@ -521,7 +521,7 @@ def _run_rounds(name, rounds, gate):
     tf = W(inp["true_feat"])
     alive = set(seqs)
     stats = {"match": 0, "compared": 0, "near": 0, "feat": [], "path_differs": 0, "diffs": [],
-             "diverged": [], "lerr": 0.0}
+             "diverged": [], "lerr": 0.0, "cmp": []}
     rng = np.random.default_rng(99)
     for rd in range(rounds):
         trees = {}
@@ -573,6 +573,7 @@ def _run_rounds(name, rounds, gate):
                 ("accept_len", g_al[b] == alen), ("bonus", g_bo[b] == bonus),
                 ("prefix_len", g_plen[b] == P0 + alen)) if not ok]
             same = not diff
+            stats["cmp"].append((min(mmin, min(wm)), same, rd, b))
             # the next root feature is comparable only when the extend consumed the
             # same accepted nodes (indices and tokens) and bonus as the oracle's
             path_same = (g_al[b] == alen and g_bo[b] == bonus
@@ -612,6 +613,9 @@ def test_round_end_to_end_fp32(name):
     assert s["compared"] > 0
 
 
+BF16_GATE = 4.0  # margin factor over the bf16 logit-error estimate above which a round is gated
+
+
 @pytest.mark.parametrize("name", ["tiny_bf16", "ragged_bf16", "hd128_bf16", "wide_bf16", "7b", "13b", "70b",
                                   "chain"])
 def test_round_end_to_end_bf16_reported(name):
@@ -632,6 +636,15 @@ def test_round_end_to_end_bf16_reported(name):
     # path is the same the extend's next root feature must still agree
     assert s["compared"] >= 1
     assert all(f <= FEAT_TOL["bf16"] for f in s["feat"])
+    # where every decision of the round (drafting and the verify walk) clears
+    # the bf16 score-noise scale by a wide factor, the round must be the
+    # oracle's exactly
+    gate = BF16_GATE * s["lerr"]
+    clear = [(mg, same, rd, b) for mg, same, rd, b in s["cmp"] if mg > gate]
+    say(f"    {len(clear)} sequence-round(s) with every margin above {BF16_GATE} x the logit-error "
+        f"estimate ({gate:.2e}): all must match")
+    for mg, same, rd, b in clear:
+        assert same, (name, rd, b, mg, gate)
 
 
 # ------------------------------------------------------------------ determinism, data errors
